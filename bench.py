@@ -1,0 +1,182 @@
+"""Benchmark: PT-block attention core (GIIM + TCM) tokens/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload img2048]
+                    [--no-cpu-baseline] [--breakdown]
+
+A step is one forward of the whole attention core of one PT-DiT block
+(proxy pooling, proxy self-attention, token->proxy cross-attention, window
+attention, shifted-window attention, with all Q/K/V/O projections and
+residuals) over one batch of synthetic input already resident in HBM.
+Prints ONE JSON line.
+
+The dominant kernel's roofline entry times every launch of that kernel inside
+the timed region with HIP events recorded on the launch stream (the library's
+kernel trace). Its HBM traffic comes from rocprofv3 counters stored in
+profiles/traffic.json, and is reported only while the kernel source still
+hashes to the value recorded with the counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+METRIC = "PT-block attention tokens/s + % MFMA-bf16 peak at 2048² (N=16384)"
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
+    """Time the float64 oracle (as it stands) on one full block of the same
+    workload, on this host's cores."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    from synth_inputs import make_all_weights, make_x
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s / 2 or len(times) >= 3:
+            break
+    t = statistics.median(times)
+    return {"value": wl.B * wl.N / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full {wl.name} block(s) ({wl.B}x{wl.N} tokens), float64 NumPy, "
+                      f"median {t:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="img2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this attention core is built and timed on a single "
+              "MI355X; multi-GPU runs are not part of it.", file=sys.stderr)
+        return 2
+
+    import torch
+    import diffusion_transformer_attention_pt_amd as P
+    from diffusion_transformer_attention_pt_amd import _lib
+    from synth_inputs import WORKLOADS, make_all_weights, make_x
+
+    wl = WORKLOADS[args.workload]
+    prec = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(make_x(wl)).to(prec).to(dev)
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift,
+                             make_all_weights(wl), prec=prec, device=dev)
+    flops = blk.flops()
+
+    for _ in range(args.warmup):
+        blk.forward(x)
+    torch.cuda.synchronize()
+
+    # dominant kernel: the Q/K/V projection of the token rows (2 launches per step)
+    dom_cls = _lib.K_GEMM_QKV
+    _lib.trace_enable(dom_cls, 2 * args.steps + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.forward(x)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom_ms = _lib.trace_read(2 * args.steps + 8)
+    _lib.trace_disable()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = wl.B * wl.N / (elapsed / args.steps)
+    tflops = flops["total"] / (elapsed / args.steps) / 1e12
+    peak = PEAK_BF16_TFLOPS if prec == torch.bfloat16 else PEAK_F32_TFLOPS
+
+    rows = wl.B * wl.N
+    dom_flop = 2 * rows * wl.D * 3 * wl.D
+    dom_avg_ms = statistics.mean(dom_ms) if dom_ms else float("nan")
+    dom_tflops = dom_flop / (dom_avg_ms * 1e-3) / 1e12
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath)).get("gemm_qkv_" + wl.name)
+        if rec and rec.get("source_sha") == source_hash(rec.get("sources", [])):
+            traffic = rec.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: batch {wl.B}, grid {wl.F}x{wl.H}x{wl.W} (N={wl.N}), "
+                               f"D={wl.D}, {wl.heads} heads, proxy window {wl.p}, TCM window {wl.win} "
+                               f"shift {wl.shift}",
+                   "batch": wl.B, "tokens": wl.N, "D": wl.D, "heads": wl.heads,
+                   "gflop_per_step": round(flops["total"] / 1e9, 3)},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / peak, 4),
+        "roofline": {"kernel": "gemm_bf16 Q/K/V projection of the token rows "
+                               f"[{rows}x{wl.D}]x[{wl.D}x{3 * wl.D}]",
+                     "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / peak, 4), "traffic": traffic,
+                     "avg_launch_ms": round(dom_avg_ms, 5), "launches": len(dom_ms)},
+    }
+    if args.breakdown:
+        names = {_lib.K_POOL: "pool", _lib.K_GEMM_PROXY: "gemm_proxy", _lib.K_GEMM_Q: "gemm_q",
+                 _lib.K_ATTN_FLASH: "attn_flash", _lib.K_GEMM_OUT: "gemm_out",
+                 _lib.K_GEMM_QKV: "gemm_qkv", _lib.K_ATTN_WINDOW: "attn_window"}
+        br = {}
+        for cls, nm in names.items():
+            _lib.trace_enable(cls, 64)
+            for _ in range(10):
+                blk.forward(x)
+            torch.cuda.synchronize()
+            ms = _lib.trace_read(64)
+            _lib.trace_disable()
+            br[nm] = {"launches_per_step": len(ms) // 10, "avg_ms": round(statistics.mean(ms), 5) if ms else None,
+                      "ms_per_step": round(sum(ms) / 10, 5)}
+        out["breakdown"] = br
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,73 @@
+"""The attention core of one PT-DiT block: GIIM then TCM, as five ABI calls.
+
+Order and residuals follow the Qihoo-T2X reading note, code-correspondence
+excerpt 2 (PT-Block forward) with Eq. GIIM and Eq. TCM of section 3:
+    P  = Averaging(x)                      ptdit_proxy_pool
+    P' = P + SA(P)                         ptdit_proxy_sa
+    x1 = x + CS(x, P')                     ptdit_proxy_xattn
+    x2 = x1 + WSA(x1)                      ptdit_window_sa
+    x3 = x2 + SWSA(x2)                     ptdit_shift_window_sa
+
+With bf16 precision the block input is bf16, the residual stream
+(P, P', x1, x2, x3) is kept in fp32 and every projection reads its operand
+rounded to bf16; with fp32 precision everything is fp32. Buffers and the
+workspace are allocated once, in the constructor; forward() only launches.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import AttnWeights
+
+
+class PTBlockAttention:
+    def __init__(self, B: int, grid: Sequence[int], D: int, heads: int, p: Sequence[int],
+                 win: Sequence[int], shift: Sequence[int], weights: Sequence[dict],
+                 prec: torch.dtype = torch.bfloat16, device="cuda"):
+        self.B = B
+        self.F, self.H, self.W = grid
+        self.D, self.heads = D, heads
+        self.p, self.win, self.shift = tuple(p), tuple(win), tuple(shift)
+        self.prec = prec
+        self.device = torch.device(device)
+        self.N = self.F * self.H * self.W
+        self.M = (self.F // p[0]) * (self.H // p[1]) * (self.W // p[2])
+        self.g = (B, self.F, self.H, self.W, D, heads)
+        self.weights = [AttnWeights.from_dict(w, prec, self.device) for w in weights]
+        stream_dt = torch.float32
+        self.P = torch.empty(B, self.M, D, dtype=stream_dt, device=self.device)
+        self.P2 = torch.empty_like(self.P)
+        self.x1 = torch.empty(B, self.N, D, dtype=stream_dt, device=self.device)
+        self.x2 = torch.empty_like(self.x1)
+        self.x3 = torch.empty_like(self.x1)
+        need = max(
+            _lib.workspace_bytes(_lib.OP_PROXY_SA, (B, 1, 1, self.M, D, heads), self.M, (1, 1, 1), prec),
+            _lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.M, (1, 1, 1), prec),
+            _lib.workspace_bytes(_lib.OP_WINDOW_SA, self.g, 0, self.win, prec),
+        )
+        self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        g, w = self.g, self.weights
+        _lib.proxy_pool(x, g, self.p, out=self.P)
+        _lib.proxy_sa(self.P, self.heads, w[0], residual=True, ws=self.ws, out=self.P2)
+        _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=self.ws, out=self.x1)
+        _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2)
+        _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3)
+        return self.x3
+
+    def intermediates(self) -> Dict[str, torch.Tensor]:
+        return {"P": self.P, "P2": self.P2, "x1": self.x1, "x2": self.x2, "x3": self.x3}
+
+    def flops(self) -> Dict[str, int]:
+        """Algorithmic FLOPs of one forward (2 per multiply-accumulate): the
+        ten projections over real rows plus the four attention cores counted
+        dense over their (padded) windows, queries restricted to real tokens."""
+        B, N, M, D = self.B, self.N, self.M, self.D
+        L = self.win[0] * self.win[1] * self.win[2]
+        proj = B * D * D * ((3 * M + M) + (N + 2 * M + N) + 2 * (3 * N + N))
+        core = B * D * (2 * M * M + 2 * N * M + 2 * (2 * N * L))
+        return {"projection": 2 * proj, "core": 2 * core, "total": 2 * (proj + core)}

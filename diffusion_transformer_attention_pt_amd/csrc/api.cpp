@@ -1,0 +1,420 @@
+// C ABI of the PT-DiT attention core: argument validation, workspace carving
+// and kernel dispatch. Every check runs on the host before the first launch;
+// nothing here allocates device memory or synchronises the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+#include <vector>
+
+#include "../../include/ptdit.h"
+#include "kernels.hpp"
+
+using namespace ptdit;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t esize(ptdit_dtype t) { return t == PTDIT_F32 ? 4 : 2; }
+bool valid_dtype(ptdit_dtype t) { return t == PTDIT_BF16 || t == PTDIT_F32; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ trace
+struct Trace {
+  int cls = -1;
+  int cap = 0;
+  int count = 0;
+  std::vector<hipEvent_t> start, stop;
+} g_trace;
+
+struct TraceScope {
+  hipStream_t s;
+  int slot = -1;
+  TraceScope(int cls, hipStream_t st) : s(st) {
+    if (g_trace.cls == cls && g_trace.count < g_trace.cap) {
+      slot = g_trace.count++;
+      hipEventRecord(g_trace.start[slot], s);
+    }
+  }
+  ~TraceScope() {
+    if (slot >= 0) hipEventRecord(g_trace.stop[slot], s);
+  }
+};
+
+ptdit_status hip_status(hipError_t e) { return e == hipSuccess ? PTDIT_OK : PTDIT_ERR_HIP; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+ptdit_status check_common(int64_t B, int64_t D, int64_t heads) {
+  if (B < 0 || B > 65535 || D <= 0 || heads <= 0 || heads > 65535) return PTDIT_ERR_SHAPE;
+  if (D % heads != 0) return PTDIT_ERR_SHAPE;
+  const int64_t dh = D / heads;
+  if (dh != 72 && dh != 64) return PTDIT_ERR_SHAPE;  // head widths with compiled kernels
+  return PTDIT_OK;
+}
+
+ptdit_status check_io_dtypes(ptdit_dtype prec, ptdit_dtype in_dt, ptdit_dtype out_dt) {
+  if (!valid_dtype(prec) || !valid_dtype(in_dt) || !valid_dtype(out_dt)) return PTDIT_ERR_DTYPE;
+  if (prec == PTDIT_F32 && (in_dt != PTDIT_F32 || out_dt != PTDIT_F32)) return PTDIT_ERR_DTYPE;
+  return PTDIT_OK;
+}
+
+ptdit_status check_weights(const ptdit_attn_w* w) {
+  if (!w || !w->w_qkv || !w->w_o) return PTDIT_ERR_NULL;
+  if (!aligned16(w->w_qkv) || !aligned16(w->w_o) || !aligned16(w->b_qkv) || !aligned16(w->b_o))
+    return PTDIT_ERR_ALIGN;
+  return PTDIT_OK;
+}
+
+ptdit_status check_grid(const ptdit_grid& g) {
+  if (g.F < 0 || g.H < 0 || g.W < 0) return PTDIT_ERR_SHAPE;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  if (N > (int64_t)1 << 30) return PTDIT_ERR_SHAPE;
+  return check_common(g.B, g.D, g.heads);
+}
+
+hipError_t gemm(ptdit_dtype prec, const void* A, ptdit_dtype a_dt, int64_t M, int K, int N,
+                const void* W, const void* bias, const void* R, ptdit_dtype r_dt,
+                void* Y, ptdit_dtype y_dt, bool head_major, int64_t Ntok, int heads, int D,
+                int trace_cls, hipStream_t s) {
+  GemmDesc d;
+  d.A = A; d.a_f32 = a_dt == PTDIT_F32;
+  d.W = W; d.bias = bias;
+  d.R = R; d.r_f32 = r_dt == PTDIT_F32;
+  d.Y = Y; d.y_f32 = y_dt == PTDIT_F32;
+  d.M = M; d.N = N; d.K = K;
+  d.head_major = head_major; d.Ntok = Ntok; d.heads = heads;
+  d.dh = heads > 0 ? D / heads : 0; d.D = D;
+  TraceScope ts(trace_cls, s);
+  return prec == PTDIT_F32 ? launch_gemm_f32(d, s) : launch_gemm_bf16(d, s);
+}
+
+const void* offset_elems(const void* p, int64_t elems, ptdit_dtype dt) {
+  return p ? (const char*)p + elems * (int64_t)esize(dt) : nullptr;
+}
+
+// Window / shifted-window attention shared by both ABI calls.
+ptdit_status window_common(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
+                           ptdit_win3 shift, const ptdit_attn_w* w, int32_t add_residual,
+                           void* out, ptdit_dtype out_dt, void* ws, size_t ws_bytes,
+                           ptdit_dtype prec, hipStream_t stream) {
+  ptdit_status st = check_grid(g);
+  if (st) return st;
+  if ((st = check_io_dtypes(prec, x_dt, out_dt))) return st;
+  if ((st = check_weights(w))) return st;
+  if (win.t <= 0 || win.h <= 0 || win.w <= 0) return PTDIT_ERR_SHAPE;
+  if ((int64_t)win.t * win.h * win.w > 128) return PTDIT_ERR_SHAPE;
+  if (shift.t < 0 || shift.h < 0 || shift.w < 0 || shift.t >= win.t || shift.h >= win.h ||
+      shift.w >= win.w)
+    return PTDIT_ERR_SHAPE;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  const int64_t rows = (int64_t)g.B * N;
+  if (rows == 0) return PTDIT_OK;
+  if (!x || !out) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  const size_t need = ptdit_workspace_bytes(PTDIT_OP_WINDOW_SA, g, 0, win, prec);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  const size_t xb = rows * g.D * esize(x_dt), ob = rows * g.D * esize(out_dt);
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need)) return PTDIT_ERR_ALIAS;
+
+  const int D = g.D;
+  char* wsp = (char*)ws;
+  void* qkv = wsp;
+  void* o = wsp + align_up((size_t)rows * 3 * D * esize(prec));
+  hipError_t e = gemm(prec, x, x_dt, rows, D, 3 * D, w->w_qkv, w->b_qkv, nullptr, prec, qkv, prec,
+                      true, N, g.heads, D, PTDIT_K_GEMM_QKV, stream);
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  WindowDesc wd;
+  wd.QKV = qkv; wd.bias_qkv = w->b_qkv; wd.O = o;
+  wd.B = g.B; wd.F = g.F; wd.H = g.H; wd.W = g.W; wd.D = D; wd.heads = g.heads; wd.dh = D / g.heads;
+  wd.wt = win.t; wd.wh = win.h; wd.ww = win.w;
+  wd.st = shift.t; wd.sh = shift.h; wd.sw = shift.w;
+  wd.Fp = (g.F + win.t - 1) / win.t * win.t;
+  wd.Hp = (g.H + win.h - 1) / win.h * win.h;
+  wd.Wp = (g.W + win.w - 1) / win.w * win.w;
+  wd.scale = 1.0f / std::sqrt((float)wd.dh);
+  {
+    TraceScope ts(PTDIT_K_ATTN_WINDOW, stream);
+    e = launch_window(wd, prec == PTDIT_F32, stream);
+  }
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
+           false, N, g.heads, D, PTDIT_K_GEMM_OUT, stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ptdit_version(void) { return "ptdit-mi355x 0.1 (gfx950)"; }
+
+const char* ptdit_status_str(ptdit_status st) {
+  switch (st) {
+    case PTDIT_OK: return "ok";
+    case PTDIT_ERR_NULL: return "null pointer";
+    case PTDIT_ERR_SHAPE: return "invalid shape";
+    case PTDIT_ERR_DIVISIBILITY: return "proxy window does not divide the grid";
+    case PTDIT_ERR_DTYPE: return "unsupported dtype combination";
+    case PTDIT_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PTDIT_ERR_WORKSPACE: return "workspace missing or too small";
+    case PTDIT_ERR_HIP: return "HIP launch failed";
+    case PTDIT_ERR_ALIAS: return "output overlaps an input or the workspace";
+  }
+  return "unknown status";
+}
+
+size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 win, ptdit_dtype prec) {
+  (void)win;
+  if (!valid_dtype(prec) || g.B < 0 || g.D <= 0 || g.F < 0 || g.H < 0 || g.W < 0) return 0;
+  const size_t es = esize(prec);
+  const size_t B = (size_t)g.B, D = (size_t)g.D;
+  const size_t N = (size_t)g.F * g.H * g.W;
+  switch (op) {
+    case PTDIT_OP_PROXY_SA:
+      if (M < 0) return 0;
+      return align_up(B * 3 * M * D * es) + align_up(B * M * D * es);
+    case PTDIT_OP_PROXY_XATTN:
+      if (M < 0) return 0;
+      return align_up(B * N * D * es) + align_up(B * 2 * M * D * es) + align_up(B * N * D * es);
+    case PTDIT_OP_WINDOW_SA:
+    case PTDIT_OP_SHIFT_WINDOW_SA:
+      return align_up(B * 3 * N * D * es) + align_up(B * N * D * es);
+  }
+  return 0;
+}
+
+ptdit_status ptdit_linear(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in,
+                          int32_t d_out, const void* w, const void* b,
+                          const void* residual, ptdit_dtype r_dt,
+                          void* y, ptdit_dtype y_dt, ptdit_dtype prec, hipStream_t stream) {
+  if (!valid_dtype(prec) || !valid_dtype(x_dt) || !valid_dtype(y_dt) || !valid_dtype(r_dt))
+    return PTDIT_ERR_DTYPE;
+  if (prec == PTDIT_F32 && (x_dt != PTDIT_F32 || y_dt != PTDIT_F32 || (residual && r_dt != PTDIT_F32)))
+    return PTDIT_ERR_DTYPE;
+  if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return PTDIT_ERR_SHAPE;
+  if (rows == 0) return PTDIT_OK;
+  if (!x || !w || !y) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(b) || !aligned16(residual) || !aligned16(y))
+    return PTDIT_ERR_ALIGN;
+  if (overlaps(y, rows * d_out * esize(y_dt), x, rows * d_in * esize(x_dt))) return PTDIT_ERR_ALIAS;
+  hipError_t e = gemm(prec, x, x_dt, rows, d_in, d_out, w, b, residual, r_dt, y, y_dt, false, rows, 1,
+                      d_out, PTDIT_K_GEMM_OUT, stream);
+  return hip_status(e);
+}
+
+ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,
+                              void* proxies, ptdit_dtype out_dt, hipStream_t stream) {
+  if (!valid_dtype(x_dt) || !valid_dtype(out_dt)) return PTDIT_ERR_DTYPE;
+  if (g.B < 0 || g.F < 0 || g.H < 0 || g.W < 0 || g.D <= 0 || g.D % 8) return PTDIT_ERR_SHAPE;
+  if (p.t <= 0 || p.h <= 0 || p.w <= 0) return PTDIT_ERR_SHAPE;
+  if (g.F % p.t || g.H % p.h || g.W % p.w) return PTDIT_ERR_DIVISIBILITY;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  if (N > (int64_t)1 << 30) return PTDIT_ERR_SHAPE;
+  const int64_t M = N / ((int64_t)p.t * p.h * p.w);
+  if ((int64_t)g.B * M > INT32_MAX) return PTDIT_ERR_SHAPE;
+  if ((int64_t)g.B * M == 0) return PTDIT_OK;
+  if (!x || !proxies) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(proxies)) return PTDIT_ERR_ALIGN;
+  if (overlaps(proxies, g.B * M * g.D * esize(out_dt), x, g.B * N * g.D * esize(x_dt)))
+    return PTDIT_ERR_ALIAS;
+  PoolDesc d;
+  d.x = x; d.x_f32 = x_dt == PTDIT_F32;
+  d.out = proxies; d.out_f32 = out_dt == PTDIT_F32;
+  d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D;
+  d.pt = p.t; d.ph = p.h; d.pw = p.w;
+  TraceScope ts(PTDIT_K_POOL, stream);
+  return hip_status(launch_pool(d, stream));
+}
+
+ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, int32_t M,
+                            int32_t D, int32_t heads, const ptdit_attn_w* w,
+                            int32_t add_residual, void* out, ptdit_dtype out_dt,
+                            void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
+  ptdit_status st = check_common(B, D, heads);
+  if (st) return st;
+  if (M < 0) return PTDIT_ERR_SHAPE;
+  if ((st = check_io_dtypes(prec, p_dt, out_dt))) return st;
+  if ((st = check_weights(w))) return st;
+  const int64_t rows = (int64_t)B * M;
+  if (rows == 0) return PTDIT_OK;
+  if (!proxies || !out) return PTDIT_ERR_NULL;
+  if (!aligned16(proxies) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  ptdit_grid g{B, 1, 1, M, D, heads};
+  const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_SA, g, M, ptdit_win3{1, 1, 1}, prec);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  if (overlaps(out, rows * D * esize(out_dt), proxies, rows * D * esize(p_dt)) ||
+      overlaps(out, rows * D * esize(out_dt), ws, need))
+    return PTDIT_ERR_ALIAS;
+
+  const int dh = D / heads;
+  char* wsp = (char*)ws;
+  void* qkv = wsp;
+  void* o = wsp + align_up((size_t)rows * 3 * D * esize(prec));
+  hipError_t e = gemm(prec, proxies, p_dt, rows, D, 3 * D, w->w_qkv, w->b_qkv, nullptr, prec, qkv,
+                      prec, true, M, heads, D, PTDIT_K_GEMM_PROXY, stream);
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  FlashDesc f;
+  const int64_t hs = (int64_t)M * dh, gs = (int64_t)heads * hs;
+  f.Q = qkv; f.q_bs = 3 * gs; f.q_hs = hs;
+  f.K = offset_elems(qkv, gs, prec); f.k_bs = 3 * gs; f.k_hs = hs;
+  f.V = offset_elems(qkv, 2 * gs, prec); f.v_bs = 3 * gs; f.v_hs = hs;
+  f.O = o; f.B = B; f.heads = heads; f.Nq = M; f.Nk = M; f.dh = dh; f.D = D;
+  f.scale = 1.0f / std::sqrt((float)dh);
+  {
+    TraceScope ts(PTDIT_K_ATTN_FLASH, stream);
+    e = launch_flash(f, prec == PTDIT_F32, stream);
+  }
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? proxies : nullptr, p_dt, out,
+           out_dt, false, M, heads, D, PTDIT_K_GEMM_PROXY, stream);
+  return hip_status(e);
+}
+
+ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+                               const void* proxies, ptdit_dtype p_dt, int32_t M,
+                               const ptdit_attn_w* w, int32_t add_residual,
+                               void* out, ptdit_dtype out_dt,
+                               void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
+  ptdit_status st = check_grid(g);
+  if (st) return st;
+  if ((st = check_io_dtypes(prec, x_dt, out_dt))) return st;
+  if (!valid_dtype(p_dt) || (prec == PTDIT_F32 && p_dt != PTDIT_F32)) return PTDIT_ERR_DTYPE;
+  if ((st = check_weights(w))) return st;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  const int64_t rows = (int64_t)g.B * N;
+  if (rows == 0) return PTDIT_OK;
+  if (M <= 0) return PTDIT_ERR_SHAPE;  // softmax over an empty key set is undefined
+  if (!x || !proxies || !out) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(proxies) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_XATTN, g, M, ptdit_win3{1, 1, 1}, prec);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  const size_t ob = rows * g.D * esize(out_dt);
+  if (overlaps(out, ob, x, rows * g.D * esize(x_dt)) ||
+      overlaps(out, ob, proxies, (size_t)g.B * M * g.D * esize(p_dt)) || overlaps(out, ob, ws, need))
+    return PTDIT_ERR_ALIAS;
+
+  const int D = g.D, heads = g.heads, dh = D / heads;
+  const size_t es = esize(prec);
+  char* wsp = (char*)ws;
+  void* q = wsp;
+  void* kv = wsp + align_up((size_t)rows * D * es);
+  void* o = (char*)kv + align_up((size_t)g.B * 2 * M * D * es);
+  // Q = x Wq^T + bq (rows 0..D-1 of w_qkv), head-major [B][1][heads][N][dh]
+  hipError_t e = gemm(prec, x, x_dt, rows, D, D, w->w_qkv, w->b_qkv, nullptr, prec, q, prec, true, N,
+                      heads, D, PTDIT_K_GEMM_Q, stream);
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  // K, V = P' W_{k,v}^T + b_{k,v} (rows D..3D-1), head-major [B][2][heads][M][dh]
+  e = gemm(prec, proxies, p_dt, (int64_t)g.B * M, D, 2 * D, offset_elems(w->w_qkv, (int64_t)D * D, prec),
+           offset_elems(w->b_qkv, D, prec), nullptr, prec, kv, prec, true, M, heads, D,
+           PTDIT_K_GEMM_PROXY, stream);
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  FlashDesc f;
+  const int64_t qhs = N * dh, khs = (int64_t)M * dh;
+  f.Q = q; f.q_bs = heads * qhs; f.q_hs = qhs;
+  f.K = kv; f.k_bs = 2 * heads * khs; f.k_hs = khs;
+  f.V = offset_elems(kv, heads * khs, prec); f.v_bs = 2 * heads * khs; f.v_hs = khs;
+  f.O = o; f.B = g.B; f.heads = heads; f.Nq = (int)N; f.Nk = M; f.dh = dh; f.D = D;
+  f.scale = 1.0f / std::sqrt((float)dh);
+  {
+    TraceScope ts(PTDIT_K_ATTN_FLASH, stream);
+    e = launch_flash(f, prec == PTDIT_F32, stream);
+  }
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
+           false, N, heads, D, PTDIT_K_GEMM_OUT, stream);
+  return hip_status(e);
+}
+
+ptdit_status ptdit_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
+                             const ptdit_attn_w* w, int32_t add_residual,
+                             void* out, ptdit_dtype out_dt,
+                             void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
+  return window_common(x, x_dt, g, win, ptdit_win3{0, 0, 0}, w, add_residual, out, out_dt, ws,
+                       ws_bytes, prec, stream);
+}
+
+ptdit_status ptdit_shift_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+                                   ptdit_win3 win, ptdit_win3 shift,
+                                   const ptdit_attn_w* w, int32_t add_residual,
+                                   void* out, ptdit_dtype out_dt,
+                                   void* ws, size_t ws_bytes, ptdit_dtype prec,
+                                   hipStream_t stream) {
+  return window_common(x, x_dt, g, win, shift, w, add_residual, out, out_dt, ws, ws_bytes, prec,
+                       stream);
+}
+
+ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,
+                          void* y, ptdit_dtype dt, hipStream_t stream) {
+  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+  if (g.B < 0 || g.F < 0 || g.H < 0 || g.W < 0 || g.D <= 0 || g.D % 8) return PTDIT_ERR_SHAPE;
+  if (shift.t < 0 || shift.h < 0 || shift.w < 0) return PTDIT_ERR_SHAPE;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  if (N > (int64_t)1 << 30) return PTDIT_ERR_SHAPE;
+  if (g.B * N == 0) return PTDIT_OK;
+  if (!x || !y) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return PTDIT_ERR_ALIGN;
+  const size_t bytes = g.B * N * g.D * esize(dt);
+  if (overlaps(x, bytes, y, bytes)) return PTDIT_ERR_ALIAS;
+  auto norm = [&](int s, int L) {
+    int r = s % L;
+    if (inverse) r = (L - r) % L;
+    return r;
+  };
+  RollDesc d;
+  d.x = x; d.y = y; d.f32 = dt == PTDIT_F32;
+  d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D;
+  d.st = norm(shift.t, g.F); d.sh = norm(shift.h, g.H); d.sw = norm(shift.w, g.W);
+  TraceScope ts(PTDIT_K_ROLL, stream);
+  return hip_status(launch_roll(d, stream));
+}
+
+ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity) {
+  ptdit_trace_disable();
+  if (capacity <= 0 || kernel_class < 0) return PTDIT_ERR_SHAPE;
+  g_trace.start.resize(capacity);
+  g_trace.stop.resize(capacity);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&g_trace.start[i]) != hipSuccess || hipEventCreate(&g_trace.stop[i]) != hipSuccess) {
+      g_trace.start.resize(i);
+      g_trace.stop.resize(i);
+      ptdit_trace_disable();
+      return PTDIT_ERR_HIP;
+    }
+  }
+  g_trace.cls = kernel_class;
+  g_trace.cap = capacity;
+  g_trace.count = 0;
+  return PTDIT_OK;
+}
+
+int32_t ptdit_trace_read(float* ms, int32_t max) {
+  int n = 0;
+  for (int i = 0; i < g_trace.count && i < max; ++i) {
+    if (hipEventSynchronize(g_trace.stop[i]) != hipSuccess) break;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_trace.start[i], g_trace.stop[i]) != hipSuccess) break;
+    ms[n++] = t;
+  }
+  return n;
+}
+
+void ptdit_trace_disable(void) {
+  for (size_t i = 0; i < g_trace.start.size(); ++i) hipEventDestroy(g_trace.start[i]);
+  for (size_t i = 0; i < g_trace.stop.size(); ++i) hipEventDestroy(g_trace.stop[i]);
+  g_trace.start.clear();
+  g_trace.stop.clear();
+  g_trace.cls = -1;
+  g_trace.cap = 0;
+  g_trace.count = 0;
+}
+
+}  // extern "C"

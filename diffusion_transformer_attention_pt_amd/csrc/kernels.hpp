@@ -1,0 +1,65 @@
+// Host-side launch interface of the PT-DiT attention-core kernels.
+// Internal to the library: api.cpp validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptdit {
+
+// Y = A W^T + bias (+ R). A: [M][K], W: [N][K], bias: [N], R/Y: [M][N].
+// head_major: Y is instead written as [b][N/D groups][heads][Ntok][dh] with
+// row m = b*Ntok + tok and column n = g*D + h*dh + d (no residual then).
+struct GemmDesc {
+  const void* A; int a_f32;
+  const void* W; const void* bias;
+  const void* R; int r_f32;
+  void* Y; int y_f32;
+  int64_t M; int N; int K;
+  int head_major; int64_t Ntok; int heads; int dh; int D;
+};
+hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
+hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32
+
+struct PoolDesc {
+  const void* x; int x_f32;
+  void* out; int out_f32;
+  int B, F, H, W, D;
+  int pt, ph, pw;
+};
+hipError_t launch_pool(const PoolDesc& d, hipStream_t s);
+
+struct RollDesc {
+  const void* x; void* y; int f32;
+  int B, F, H, W, D;
+  int st, sh, sw;  // already reduced mod the extents, sign applied
+};
+hipError_t launch_roll(const RollDesc& d, hipStream_t s);
+
+// softmax(Q K^T * scale) V per (batch, head). Q/K/V head-major:
+// row r of head h in batch b at base + b*bs + h*hs + r*dh. O: [B][Nq][D].
+struct FlashDesc {
+  const void* Q; int64_t q_bs, q_hs;
+  const void* K; int64_t k_bs, k_hs;
+  const void* V; int64_t v_bs, v_hs;
+  void* O;
+  int B, heads, Nq, Nk, dh, D;
+  float scale;
+};
+hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s);
+
+// Window attention on head-major QKV [B][3][heads][Ntok][dh] with the grid
+// zero-padded to (Fp, Hp, Wp), rolled by -shift, partitioned into windows
+// (wt, wh, ww) and masked by region labels. Pad tokens use bias_qkv (or 0).
+struct WindowDesc {
+  const void* QKV; const void* bias_qkv;
+  void* O;
+  int B, F, H, W, D, heads, dh;
+  int wt, wh, ww;
+  int st, sh, sw;
+  int Fp, Hp, Wp;
+  float scale;
+};
+hipError_t launch_window(const WindowDesc& d, int f32, hipStream_t s);
+
+}  // namespace ptdit

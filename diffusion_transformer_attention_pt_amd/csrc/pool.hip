@@ -1,0 +1,220 @@
+// Window-average proxy pooling (GIIM "Averaging") and the stand-alone 3D roll.
+//
+// Both are bandwidth-bound. Every thread owns 8 consecutive channels (one
+// 16-byte bf16 vector) so a row of D channels is read by D/8 neighbouring
+// threads in one coalesced sweep.
+//
+// Pool summation order (fixed, so the result is bit-reproducible): fp32;
+// for each (dt, di) the row sum over dj runs in index order from 0; row sums
+// are added over di in index order; plane sums over dt in index order; then
+// one IEEE fp32 division by P = p_t*p_h*p_w (hipcc's default fp32 division
+// is correctly rounded; this file is built without fast-math).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ptdit {
+
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  __device__ static void load(const uint16_t* p, float* f) { unpack8(*reinterpret_cast<const uint4*>(p), f); }
+  __device__ static void store(uint16_t* p, const float* f) { *reinterpret_cast<uint4*>(p) = pack8(f); }
+};
+template <> struct Vec8<float> {
+  __device__ static void load(const float* p, float* f) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ static void store(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = float4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<float4*>(p + 4) = float4{f[4], f[5], f[6], f[7]};
+  }
+};
+
+struct PoolParams {
+  const void* x;
+  void* out;
+  int B, F, H, W, D;
+  int pt, ph, pw;
+  int FT, HI, WJ;  // proxy grid
+};
+
+constexpr int POOL_CX = 16;   // channel chunks (of 8) per workgroup along x
+constexpr int POOL_MAXR = 64; // max (dt, di) rows held in LDS
+
+// Block (POOL_CX, ny): thread (tx, ty) sums rows r = ty, ty+ny, ... of the
+// window for chunk tx into LDS; thread ty == 0 then adds them in order.
+template <typename TX, typename TO>
+__global__ void __launch_bounds__(1024) pool_kernel(PoolParams p) {
+  __shared__ float part[POOL_MAXR * POOL_CX * 8];
+  const int C = p.D / 8;
+  const int tx = threadIdx.x, ty = threadIdx.y, ny = blockDim.y;
+  const int cx = blockIdx.y * POOL_CX + tx;
+  const int M = p.FT * p.HI * p.WJ;
+  const int bm = blockIdx.x;
+  const int b = bm / M, m = bm - b * M;
+  const int T = m / (p.HI * p.WJ), I = (m / p.WJ) % p.HI, J = m % p.WJ;
+  const int R = p.pt * p.ph;
+  const TX* x = reinterpret_cast<const TX*>(p.x);
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+
+  if (cx < C) {
+    for (int r = ty; r < R; r += ny) {
+      const int dt = r / p.ph, di = r - dt * p.ph;
+      const int t = T * p.pt + dt, i = I * p.ph + di;
+      const TX* src = x + ((int64_t)b * N + ((int64_t)t * p.H + i) * p.W + (int64_t)J * p.pw) * p.D + cx * 8;
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int dj = 0;
+      for (; dj + 4 <= p.pw; dj += 4) {  // four independent loads in flight, adds in order
+        float v0[8], v1[8], v2[8], v3[8];
+        Vec8<TX>::load(src + (int64_t)(dj + 0) * p.D, v0);
+        Vec8<TX>::load(src + (int64_t)(dj + 1) * p.D, v1);
+        Vec8<TX>::load(src + (int64_t)(dj + 2) * p.D, v2);
+        Vec8<TX>::load(src + (int64_t)(dj + 3) * p.D, v3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = (((s[e] + v0[e]) + v1[e]) + v2[e]) + v3[e];
+      }
+      for (; dj < p.pw; ++dj) {
+        float v[8];
+        Vec8<TX>::load(src + (int64_t)dj * p.D, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[(r * POOL_CX + tx) * 8 + e] = s[e];
+    }
+  }
+  __syncthreads();
+  if (ty == 0 && cx < C) {
+    float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < p.pt; ++dt) {
+      float plane[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int di = 0; di < p.ph; ++di) {
+        const int r = dt * p.ph + di;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) plane[e] = plane[e] + part[(r * POOL_CX + tx) * 8 + e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tot[e] = tot[e] + plane[e];
+    }
+    const float P = (float)(p.pt * p.ph * p.pw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot[e] = tot[e] / P;
+    TO* out = reinterpret_cast<TO*>(p.out);
+    Vec8<TO>::store(out + ((int64_t)b * M + m) * p.D + cx * 8, tot);
+  }
+}
+
+// Fallback for windows with more than POOL_MAXR (dt, di) rows: one thread per
+// chunk walks the whole window, same order.
+template <typename TX, typename TO>
+__global__ void __launch_bounds__(256) pool_serial_kernel(PoolParams p) {
+  const int C = p.D / 8;
+  const int M = p.FT * p.HI * p.WJ;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)p.B * M * C) return;
+  const int cx = (int)(gid % C);
+  const int64_t bm = gid / C;
+  const int b = (int)(bm / M), m = (int)(bm % M);
+  const int T = m / (p.HI * p.WJ), I = (m / p.WJ) % p.HI, J = m % p.WJ;
+  const TX* x = reinterpret_cast<const TX*>(p.x);
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < p.pt; ++dt) {
+    float plane[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int di = 0; di < p.ph; ++di) {
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const int t = T * p.pt + dt, i = I * p.ph + di;
+      const TX* src = x + ((int64_t)b * N + ((int64_t)t * p.H + i) * p.W + (int64_t)J * p.pw) * p.D + cx * 8;
+      for (int dj = 0; dj < p.pw; ++dj) {
+        float v[8];
+        Vec8<TX>::load(src + (int64_t)dj * p.D, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) plane[e] = plane[e] + s[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot[e] = tot[e] + plane[e];
+  }
+  const float P = (float)(p.pt * p.ph * p.pw);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tot[e] = tot[e] / P;
+  TO* out = reinterpret_cast<TO*>(p.out);
+  Vec8<TO>::store(out + ((int64_t)b * M + m) * p.D + cx * 8, tot);
+}
+
+template <typename TX, typename TO>
+static hipError_t run_pool(const PoolParams& p, hipStream_t s) {
+  const int C = p.D / 8;
+  const int M = p.FT * p.HI * p.WJ;
+  const int R = p.pt * p.ph;
+  if ((int64_t)p.B * M == 0) return hipSuccess;
+  if (R <= POOL_MAXR) {
+    int ny = R;
+    while (ny * POOL_CX > 1024) ny = (ny + 1) / 2;
+    dim3 grid(p.B * M, (C + POOL_CX - 1) / POOL_CX);
+    hipLaunchKernelGGL((pool_kernel<TX, TO>), grid, dim3(POOL_CX, ny), 0, s, p);
+  } else {
+    const int64_t total = (int64_t)p.B * M * C;
+    hipLaunchKernelGGL((pool_serial_kernel<TX, TO>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const PoolDesc& d, hipStream_t s) {
+  PoolParams p;
+  p.x = d.x; p.out = d.out;
+  p.B = d.B; p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D;
+  p.pt = d.pt; p.ph = d.ph; p.pw = d.pw;
+  p.FT = d.F / d.pt; p.HI = d.H / d.ph; p.WJ = d.W / d.pw;
+  if (d.x_f32) return d.out_f32 ? run_pool<float, float>(p, s) : run_pool<float, uint16_t>(p, s);
+  return d.out_f32 ? run_pool<uint16_t, float>(p, s) : run_pool<uint16_t, uint16_t>(p, s);
+}
+
+// ----------------------------------------------------------------------------
+// 3D cyclic roll: y[t,i,j] = x[(t+st) mod F, (i+sh) mod H, (j+sw) mod W].
+// One thread per 16-byte vector; shifts arrive already in [0, extent).
+// ----------------------------------------------------------------------------
+struct RollParams {
+  const uint4* x;
+  uint4* y;
+  int B, F, H, W;
+  int vec_per_tok;
+  int st, sh, sw;
+};
+
+__global__ void __launch_bounds__(256) roll_kernel(RollParams p) {
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const int64_t total = (int64_t)p.B * N * p.vec_per_tok;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int v = (int)(g % p.vec_per_tok);
+    const int64_t bt = g / p.vec_per_tok;
+    const int64_t b = bt / N, n = bt - b * N;
+    const int j = (int)(n % p.W), i = (int)((n / p.W) % p.H), t = (int)(n / ((int64_t)p.W * p.H));
+    int ts = t + p.st; ts -= ts >= p.F ? p.F : 0;
+    int is = i + p.sh; is -= is >= p.H ? p.H : 0;
+    int js = j + p.sw; js -= js >= p.W ? p.W : 0;
+    const int64_t src = b * N + ((int64_t)ts * p.H + is) * p.W + js;
+    p.y[g] = p.x[src * p.vec_per_tok + v];
+  }
+}
+
+hipError_t launch_roll(const RollDesc& d, hipStream_t s) {
+  RollParams p;
+  p.x = reinterpret_cast<const uint4*>(d.x);
+  p.y = reinterpret_cast<uint4*>(d.y);
+  p.B = d.B; p.F = d.F; p.H = d.H; p.W = d.W;
+  p.vec_per_tok = d.f32 ? d.D / 4 : d.D / 8;
+  p.st = d.st; p.sh = d.sh; p.sw = d.sw;
+  const int64_t total = (int64_t)d.B * d.F * d.H * d.W * p.vec_per_tok;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(roll_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace ptdit

@@ -1,0 +1,231 @@
+/*
+ * ptdit.h -- C ABI of the PT-DiT attention core (GIIM + TCM) for AMD MI355X
+ * (gfx950). Hand-written HIP kernels; no torch types cross this boundary.
+ *
+ * The operations are those of the Qihoo-T2X reading note (page "Qihoo-T2X --
+ * Proxy-Tokenized DiT for Text-to-Any-Task"):
+ *   - section 3 "Method", Eq. GIIM: z_s = CS(z_s, SA(Averaging(z_s))) with
+ *     z_s in R^{N x D} reshaped to f x h x w and one proxy token per
+ *     p_t x p_h x p_w window (window average);
+ *   - section 3 "Method", Eq. TCM: z_hat = WSA(z_s) + z_s,
+ *     z_w = SWSA(z_hat) + z_hat, the shifted windows being a 3D cyclic shift;
+ *   - the code-correspondence section (module table and excerpt 2, PT-Block
+ *     forward) for the call order and residual placement.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Tokens.   x is [B][N][D], N = F*H*W, tokens row-major over (f, h, w);
+ *            channels contiguous.
+ *  Proxies.  [B][M][D], M = (F/p_t)*(H/p_h)*(W/p_w), row-major over the
+ *            window grid (T, I, J).
+ *  Heads.    head h owns channels [h*dh, (h+1)*dh), dh = D/heads; scores are
+ *            scaled by 1/sqrt(dh); no positional term inside the core.
+ *  Weights.  nn.Linear layout, y = x W^T + b. w_qkv is [3D][D]: rows 0..D-1
+ *            are W_q, D..2D-1 W_k, 2D..3D-1 W_v; b_qkv is [3D] or NULL;
+ *            w_o is [D][D]; b_o is [D] or NULL. The single output projection
+ *            of an attention plays the role of to_out followed by
+ *            linear_1_visual (two linear maps compose into one).
+ *  Precision ("prec").
+ *            PTDIT_BF16: weights and biases are bf16; projections and
+ *            attention run on bf16 MFMA with fp32 accumulation; the library's
+ *            intermediates (Q, K, V, attention output) are bf16; softmax
+ *            statistics are fp32. Activation inputs may be bf16 or fp32
+ *            (x_dt), outputs bf16 or fp32 (out_dt); the residual added is the
+ *            input x itself, in its own dtype.
+ *            PTDIT_F32: everything fp32 (fp32 MFMA); x_dt = out_dt = F32.
+ *  Memory.   Every pointer except the stream is a DEVICE pointer, 16-byte
+ *            aligned. The caller allocates and frees all memory, including
+ *            the workspace (size from ptdit_workspace_bytes). The library
+ *            never allocates device memory, never synchronises the stream
+ *            and keeps no state between calls except the optional kernel
+ *            trace (ptdit_trace_*). out must not alias x or the workspace.
+ *  Streams.  All work is enqueued asynchronously on `stream` (0 = default).
+ *  Errors.   Every argument is checked on the host before any launch; on a
+ *            failed check nothing is launched, outputs are untouched and a
+ *            negative ptdit_status is returned. A failed launch returns
+ *            PTDIT_ERR_HIP. ptdit_status_str names a status.
+ */
+#ifndef PTDIT_H
+#define PTDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PTDIT_BF16 = 0, PTDIT_F32 = 1 } ptdit_dtype;
+
+typedef enum {
+  PTDIT_OK = 0,
+  PTDIT_ERR_NULL = -1,          /* a required pointer is NULL */
+  PTDIT_ERR_SHAPE = -2,         /* a size is non-positive, D % heads != 0, dh unsupported ... */
+  PTDIT_ERR_DIVISIBILITY = -3,  /* the proxy window does not divide the grid */
+  PTDIT_ERR_DTYPE = -4,         /* unsupported dtype combination */
+  PTDIT_ERR_ALIGN = -5,         /* a pointer is not 16-byte aligned */
+  PTDIT_ERR_WORKSPACE = -6,     /* workspace missing or smaller than required */
+  PTDIT_ERR_HIP = -7,           /* a kernel launch failed */
+  PTDIT_ERR_ALIAS = -8          /* output overlaps an input or the workspace */
+} ptdit_status;
+
+/* Token grid of one call: batch B, frames F, height H, width W (N = F*H*W),
+ * model width D split into `heads` heads. */
+typedef struct { int32_t B, F, H, W, D, heads; } ptdit_grid;
+
+/* A 3D extent (proxy window, TCM window or shift) along (t, h, w). */
+typedef struct { int32_t t, h, w; } ptdit_win3;
+
+/* Weights of one attention module (layout in the header comment). */
+typedef struct {
+  const void* w_qkv;
+  const void* b_qkv;
+  const void* w_o;
+  const void* b_o;
+} ptdit_attn_w;
+
+/* Operation codes for ptdit_workspace_bytes. */
+typedef enum {
+  PTDIT_OP_PROXY_SA = 0,
+  PTDIT_OP_PROXY_XATTN = 1,
+  PTDIT_OP_WINDOW_SA = 2,
+  PTDIT_OP_SHIFT_WINDOW_SA = 3
+} ptdit_op;
+
+/*
+ * ptdit_linear -- one projection, y = x W^T + b (+ residual).
+ * Source: the Q/K/V/O linear maps inside every attention module of the code
+ * correspondence table (proxy_attn1, pvisual_attn2, linear_1_visual, attn1).
+ *   x        [rows][d_in], dtype x_dt
+ *   w        [d_out][d_in], dtype = prec;  b: [d_out] (prec) or NULL
+ *   residual [rows][d_out], dtype r_dt, or NULL (no residual)
+ *   y        [rows][d_out], dtype y_dt
+ * Requires rows >= 0, d_in and d_out positive multiples of 8.
+ */
+ptdit_status ptdit_linear(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in,
+                          int32_t d_out, const void* w, const void* b,
+                          const void* residual, ptdit_dtype r_dt,
+                          void* y, ptdit_dtype y_dt, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_proxy_pool -- Averaging(z_s) of Eq. GIIM (section 3, "Method"; the
+ * get_proxy_token(..., mode="mean") row of the code-correspondence table).
+ *   x        [B][N][D], dtype x_dt (BF16 or F32)
+ *   proxies  [B][M][D], dtype out_dt (BF16 or F32)
+ * Proxy (T, I, J) is the average of tokens (T*p_t+dt, I*p_h+di, J*p_w+dj).
+ * Arithmetic (fixed, bit-reproducible): fp32 sums; for every (dt, di) the
+ * row sum over dj is taken in index order; row sums are added over di in
+ * index order; plane sums over dt in index order; then one IEEE fp32
+ * division by p_t*p_h*p_w; a bf16 output is rounded to nearest, ties even.
+ * Requires p to divide (F, H, W) (else PTDIT_ERR_DIVISIBILITY), D % 8 == 0.
+ */
+ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,
+                              void* proxies, ptdit_dtype out_dt, hipStream_t stream);
+
+/*
+ * ptdit_proxy_sa -- the proxy self-attention of GIIM (proxy_attn1 in the
+ * code-correspondence table; excerpt 2 adds its input back):
+ *   out = MHA(P, P) (+ P when add_residual != 0).
+ *   proxies  [B][M][D], dtype p_dt;  out [B][M][D], dtype out_dt
+ *   ws       workspace of ptdit_workspace_bytes(PTDIT_OP_PROXY_SA, ...) bytes
+ */
+ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, int32_t M,
+                            int32_t D, int32_t heads, const ptdit_attn_w* w,
+                            int32_t add_residual, void* out, ptdit_dtype out_dt,
+                            void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_proxy_xattn -- CS(z_s, P') of Eq. GIIM (pvisual_attn2 followed by
+ * linear_1_visual): every token is a query, the M attended proxies are keys
+ * and values:  out = MHA(x, P') (+ x when add_residual != 0).
+ *   x        [B][N][D], dtype x_dt;  proxies [B][M][D], dtype p_dt
+ *   out      [B][N][D], dtype out_dt
+ */
+ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+                               const void* proxies, ptdit_dtype p_dt, int32_t M,
+                               const ptdit_attn_w* w, int32_t add_residual,
+                               void* out, ptdit_dtype out_dt,
+                               void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_window_sa -- WSA of Eq. TCM (attn1 on window-grouped tokens):
+ * attention inside each win.t x win.h x win.w window of the grid, the grid
+ * being zero-padded at the high end of every axis to a multiple of the window
+ * (pad tokens are zero vectors, so their keys/values are the biases; their
+ * outputs are dropped):  out = WSA(x) (+ x when add_residual != 0).
+ *   x, out   [B][N][D]
+ * Requires a window of at most 128 tokens, a multiple of 16.
+ */
+ptdit_status ptdit_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
+                             const ptdit_attn_w* w, int32_t add_residual,
+                             void* out, ptdit_dtype out_dt,
+                             void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_shift_window_sa -- SWSA of Eq. TCM (window_shift, window attention,
+ * window_Ishift): the zero-padded grid is rolled by -shift
+ * (z[k] = y[(k + s) mod L] per axis), window attention runs under the
+ * boundary mask, the result is rolled back by +shift and cropped. Mask: per
+ * axis of padded length L, window w, shift s, rolled coordinate k is in
+ * region 0 if k < L-w, 1 if L-w <= k < L-s, 2 otherwise; a query sees a key
+ * only if their regions agree on every axis. No data is moved for the roll:
+ * the kernels address tokens through it.
+ *   out = SWSA(x) (+ x when add_residual != 0); 0 <= shift < win per axis.
+ */
+ptdit_status ptdit_shift_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+                                   ptdit_win3 win, ptdit_win3 shift,
+                                   const ptdit_attn_w* w, int32_t add_residual,
+                                   void* out, ptdit_dtype out_dt,
+                                   void* ws, size_t ws_bytes, ptdit_dtype prec,
+                                   hipStream_t stream);
+
+/*
+ * ptdit_roll3d -- the 3D cyclic shift of window_shift / window_Ishift as a
+ * stand-alone copy (the attention calls never materialise it):
+ * inverse == 0: y[t,i,j] = x[(t+s_t) mod F, (i+s_h) mod H, (j+s_w) mod W];
+ * inverse != 0: y[t,i,j] = x[(t-s_t) mod F, ...]. x, y: [B][N][D], dtype dt;
+ * bit-exact copy. Requires 0 <= shift, D % 8 == 0.
+ */
+ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,
+                          void* y, ptdit_dtype dt, hipStream_t stream);
+
+/* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
+ * ignored for the GIIM ops). Returns 0 for invalid arguments. */
+size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 win,
+                             ptdit_dtype prec);
+
+/* Human-readable name of a status. Never NULL. */
+const char* ptdit_status_str(ptdit_status st);
+
+/* Library version string. */
+const char* ptdit_version(void);
+
+/*
+ * Kernel trace (profiling aid, not thread-safe): after ptdit_trace_enable(k),
+ * every launch of kernel class k (see ptdit_kernel_class) is bracketed by a
+ * pair of HIP events recorded on the launch stream, up to `capacity` launches.
+ * ptdit_trace_read waits for the recorded events and writes up to `max`
+ * durations in milliseconds; it returns the count. ptdit_trace_disable frees
+ * the events. Events are host-side HIP objects; no device memory is used.
+ */
+typedef enum {
+  PTDIT_K_POOL = 0,
+  PTDIT_K_GEMM_QKV = 1,      /* Q/K/V projection of the token rows for window attention */
+  PTDIT_K_GEMM_OUT = 2,      /* output projections of the token rows (+ residual), ptdit_linear */
+  PTDIT_K_ATTN_FLASH = 3,    /* proxy self-attention and cross-attention cores */
+  PTDIT_K_ATTN_WINDOW = 4,   /* window / shifted-window attention cores */
+  PTDIT_K_ROLL = 5,
+  PTDIT_K_GEMM_Q = 6,        /* query projection of the token rows for cross-attention */
+  PTDIT_K_GEMM_PROXY = 7     /* every projection of the proxy rows */
+} ptdit_kernel_class;
+
+ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity);
+int32_t ptdit_trace_read(float* ms, int32_t max);
+void ptdit_trace_disable(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTDIT_H */

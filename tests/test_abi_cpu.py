@@ -1,0 +1,136 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+No kernel runs here (the calls below fail validation first)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth_inputs import WORKLOADS, WORKLOAD_ORDER
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ptdit.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ptdit_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from diffusion_transformer_attention_pt_amd import _lib
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    from diffusion_transformer_attention_pt_amd import _lib
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.ptdit_version()
+    for code in range(-8, 1):
+        s = lib.ptdit_status_str(code)
+        assert s and s != b"unknown status"
+    assert lib.ptdit_status_str(-99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    from diffusion_transformer_attention_pt_amd._lib import Grid, Win3, OP_WINDOW_SA, OP_PROXY_XATTN, OP_PROXY_SA
+    g = Grid(1, 1, 128, 128, 1152, 16)
+    n = lib.ptdit_workspace_bytes(OP_WINDOW_SA, g, 0, Win3(1, 8, 8), 0)
+    assert n == 4 * 16384 * 1152 * 2
+    n = lib.ptdit_workspace_bytes(OP_PROXY_XATTN, g, 256, Win3(1, 1, 1), 1)
+    assert n == (2 * 16384 * 1152 + 2 * 256 * 1152) * 4
+    n = lib.ptdit_workspace_bytes(OP_PROXY_SA, Grid(2, 1, 1, 256, 1152, 16), 256, Win3(1, 1, 1), 0)
+    assert n == 2 * 4 * 256 * 1152 * 2
+    assert lib.ptdit_workspace_bytes(OP_WINDOW_SA, g, 0, Win3(1, 8, 8), 7) == 0
+
+
+def test_host_validation_rejects_before_launch(lib):
+    from diffusion_transformer_attention_pt_amd._lib import AttnW, Grid, Win3
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    g = Grid(1, 1, 16, 16, 1152, 16)
+    # pool: window does not divide the grid
+    assert lib.ptdit_proxy_pool(fake, 0, g, Win3(1, 3, 3), fake, 0, None) == -3
+    # pool: null pointer
+    assert lib.ptdit_proxy_pool(None, 0, g, Win3(1, 2, 2), fake, 0, None) == -1
+    # pool: misaligned
+    assert lib.ptdit_proxy_pool(ctypes.c_void_p((1 << 20) + 2), 0, g, Win3(1, 2, 2), fake, 0, None) == -5
+    # pool: bad dtype, bad D
+    assert lib.ptdit_proxy_pool(fake, 5, g, Win3(1, 2, 2), fake, 0, None) == -4
+    assert lib.ptdit_proxy_pool(fake, 0, Grid(1, 1, 16, 16, 1150, 16), Win3(1, 2, 2), fake, 0, None) == -2
+    w = AttnW(fake.value, None, fake.value, None)
+    # window: head width without kernels, shift >= window, too-large window
+    assert lib.ptdit_window_sa(fake, 0, Grid(1, 1, 16, 16, 1152, 12), Win3(1, 8, 8), ctypes.byref(w), 1,
+                               fake, 0, fake, 1 << 30, 0, None) == -2
+    assert lib.ptdit_shift_window_sa(fake, 0, g, Win3(1, 8, 8), Win3(0, 8, 4), ctypes.byref(w), 1,
+                                     fake, 0, fake, 1 << 30, 0, None) == -2
+    assert lib.ptdit_window_sa(fake, 0, g, Win3(2, 8, 9), ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 0,
+                               None) == -2
+    # window: workspace too small
+    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, ctypes.c_void_p(1 << 40), 0,
+                               fake, 16, 0, None) == -6
+    # window: output aliases the input
+    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, 0,
+                               ctypes.c_void_p(1 << 40), 1 << 30, 0, None) == -8
+    # fp32 precision with bf16 activations
+    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 1,
+                               None) == -4
+    # cross-attention with no proxies
+    assert lib.ptdit_proxy_xattn(fake, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 0,
+                                 None) == -2
+    # null weights
+    assert lib.ptdit_proxy_sa(fake, 0, 1, 256, 1152, 16, None, 1, fake, 0, fake, 1 << 30, 0, None) == -1
+    # linear: d_in not a multiple of 8
+    assert lib.ptdit_linear(fake, 0, 10, 12, 16, fake, None, None, 0, fake, 0, 0, None) == -2
+    # empty inputs are a successful no-op
+    assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
+    assert lib.ptdit_window_sa(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w), 1,
+                               None, 0, None, 0, 0, None) == 0
+    assert lib.ptdit_linear(None, 0, 0, 16, 16, None, None, None, 0, None, 0, 0, None) == 0
+
+
+def test_block_flops_match_oracle_counters():
+    """The FLOP figure the benchmark divides by equals the oracle's counters
+    (projections over real rows; cores dense over windows, real queries)."""
+    from diffusion_transformer_attention_pt_amd.block import PTBlockAttention
+    for name in WORKLOAD_ORDER:
+        wl = WORKLOADS[name]
+        blk = PTBlockAttention.__new__(PTBlockAttention)
+        blk.B, (blk.F, blk.H, blk.W), blk.D, blk.N, blk.M, blk.win = wl.B, wl.grid, wl.D, wl.N, wl.M, wl.win
+        f = blk.flops()
+        pm = O.count_projection_macs(wl.grid, wl.p, wl.win, wl.D, B=wl.B)
+        cm = O.count_core_macs(wl.grid, wl.p, wl.win, wl.D, B=wl.B, real_queries=True)
+        assert f["projection"] == 2 * sum(pm.values())
+        assert f["core"] == 2 * sum(cm.values())
+    wl = WORKLOADS["img2048"]
+    assert abs(PTBlockAttention.flops(_fake(wl))["total"] / 1e9 - 468.24) < 0.01
+
+
+def _fake(wl):
+    from diffusion_transformer_attention_pt_amd.block import PTBlockAttention
+    blk = PTBlockAttention.__new__(PTBlockAttention)
+    blk.B, (blk.F, blk.H, blk.W), blk.D, blk.N, blk.M, blk.win = wl.B, wl.grid, wl.D, wl.N, wl.M, wl.win
+    return blk
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The package must not import the oracle or compute on the CPU."""
+    pkg = os.path.join(ROOT, "diffusion_transformer_attention_pt_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("oracle is", ""), fn
+            assert "import numpy" not in src, fn

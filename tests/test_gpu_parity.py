@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.
+
+Bars: pooling and roll bit-exact; every floating-point result within max-abs
+2e-2 and relative-L2 1e-2 of the oracle (tests/gpu_util.py). Branch outputs
+are compared with the residual off, whole blocks with it on.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import announce, assert_close, dev, host
+from synth_inputs import (WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_weights, make_x, round_bf16,
+                          tiny)
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diffusion_transformer_attention_pt_amd as P
+    P.load()
+    return P
+
+
+def _wl(**kw) -> Workload:
+    base = dict(B=1, F=1, H=24, W=40, D=1152, heads=16, p=(1, 4, 4), win=(1, 8, 8), shift=(0, 4, 4),
+                dtype="bf16", index=7)
+    base.update(kw)
+    return tiny("case", **base)
+
+
+def _grid(wl):
+    return (wl.B, wl.F, wl.H, wl.W, wl.D, wl.heads)
+
+
+def _prec(wl):
+    return BF16 if wl.dtype == "bf16" else F32
+
+
+# ----------------------------------------------------------------------------- pool (bit-exact)
+
+POOL_CASES = [(n, None) for n in WORKLOAD_ORDER] + [
+    ("odd", dict(B=2, F=4, H=6, W=9, D=64, p=(2, 3, 3))),
+    ("serial", dict(B=1, F=2, H=80, W=3, D=1152, p=(2, 40, 1))),
+    ("p111", dict(B=1, F=1, H=5, W=7, D=1152, p=(1, 1, 1))),
+    ("one_proxy", dict(B=3, F=2, H=4, W=4, D=1152, p=(2, 4, 4))),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c[0] for c in POOL_CASES])
+@pytest.mark.parametrize("in_dt,out_dt", [(BF16, BF16), (BF16, F32), (F32, F32), (F32, BF16)])
+def test_pool_bit_exact(P, case, in_dt, out_dt):
+    name, kw = case
+    wl = WORKLOADS[name] if kw is None else _wl(**kw)
+    announce(f"pool {name} {in_dt}->{out_dt} grid={wl.grid} p={wl.p}")
+    x = make_x(wl.scaled(dtype="bf16" if in_dt == BF16 else "f32"), seed=100 + wl.index)
+    got = P.proxy_pool(dev(x, in_dt), _grid(wl), wl.p, out_dtype=out_dt)
+    ref = O.proxy_pool_f32(x, wl.grid, wl.p)
+    if out_dt == BF16:
+        ref = O.round_bf16_rne(ref)
+    g = got.float().cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- roll (bit-exact)
+
+@pytest.mark.parametrize("grid,shift", [((1, 128, 128), (0, 4, 4)), ((16, 30, 45), (1, 4, 4)),
+                                        ((3, 5, 7), (4, 6, 9)), ((2, 8, 8), (0, 0, 0))])
+@pytest.mark.parametrize("dt", [BF16, F32])
+def test_roll_bit_exact(P, grid, shift, dt):
+    announce(f"roll {grid} {shift} {dt}")
+    wl = _wl(F=grid[0], H=grid[1], W=grid[2], D=64)
+    x = make_x(wl.scaled(dtype="bf16" if dt == BF16 else "f32"), seed=5)
+    xd = dev(x, dt)
+    y = P.roll3d(xd, _grid(wl), shift)
+    ref = O.roll3d(x.reshape(1, *grid, 64), shift).reshape(x.shape)
+    assert np.array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
+    back = P.roll3d(y, _grid(wl), shift, inverse=True)
+    assert torch.equal(back, xd)
+
+
+# ----------------------------------------------------------------------------- projections
+
+@pytest.mark.parametrize("rows,din,dout", [(1000, 1152, 3456), (7, 1152, 1152), (4096, 1152, 1152),
+                                           (300, 16, 64), (257, 72, 40)])
+@pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "f32"])
+def test_linear(P, rows, din, dout, mode):
+    announce(f"linear {rows}x{din}->{dout} {mode}")
+    g = np.random.default_rng(rows + din)
+    x = g.standard_normal((rows, din)).astype(np.float32)
+    w = (g.standard_normal((dout, din)) * 0.02).astype(np.float32)
+    b = (g.standard_normal(dout) * 0.02).astype(np.float32)
+    r = g.standard_normal((rows, dout)).astype(np.float32)
+    if mode == "f32":
+        y = P.linear(dev(x, F32), dev(w, F32), dev(b, F32), residual=dev(r, F32), out_dtype=F32)
+        ref = O.linear(x, w, b) + r
+    else:
+        from synth_inputs import round_bf16
+        w, b = round_bf16(w), round_bf16(b)
+        if mode == "bf16":
+            x = round_bf16(x)
+            y = P.linear(dev(x, BF16), dev(w, BF16), dev(b, BF16), out_dtype=F32)
+            ref = O.linear(x, w, b)
+        else:
+            y = P.linear(dev(x, F32), dev(w, BF16), dev(b, BF16), residual=dev(round_bf16(r), BF16),
+                         out_dtype=F32)
+            ref = O.linear(x, w, b) + round_bf16(r)
+    assert_close(host(y), ref, "linear")
+
+
+# ----------------------------------------------------------------------------- attention calls
+
+CALL_CASES = {
+    "bf16_ragged": _wl(),
+    "bf16_video_pad": _wl(F=4, H=13, W=21, p=(1, 13, 7), win=(2, 8, 8), shift=(1, 4, 4)),
+    "bf16_batch2": _wl(B=2, H=16, W=24, p=(1, 2, 2)),
+    "f32_small": _wl(dtype="f32", H=16, W=16, p=(1, 2, 2)),
+    "f32_video_pad": _wl(dtype="f32", F=3, H=10, W=12, p=(1, 5, 4), win=(2, 8, 8), shift=(1, 4, 4)),
+    "bf16_dh64": _wl(D=1024, heads=16, H=16, W=16, p=(1, 4, 4)),
+}
+
+
+def _weights(wl, a, scale=0.02):
+    return make_weights(wl, a, scale=scale)
+
+
+@pytest.mark.parametrize("name", list(CALL_CASES))
+@pytest.mark.parametrize("residual", [False, True])
+def test_calls_vs_oracle(P, name, residual):
+    wl = CALL_CASES[name]
+    prec = _prec(wl)
+    announce(f"calls {name} residual={residual} grid={wl.grid} p={wl.p} win={wl.win} shift={wl.shift}")
+    x = make_x(wl, seed=200 + wl.index)
+    xd = dev(x, prec)
+    ws = [_weights(wl, a) for a in range(4)]
+    aw = [P.AttnWeights.from_dict(w, prec, "cuda") for w in ws]
+    Pm = O.proxy_pool(x, wl.grid, wl.p).astype(np.float32)
+    Pm_in = round_bf16(Pm) if prec == BF16 else Pm  # the proxies as uploaded
+    Pd = dev(Pm_in, prec)
+    out_dt = F32
+    got = P.proxy_sa(Pd, wl.heads, aw[0], residual=residual, out_dtype=out_dt)
+    assert_close(host(got), O.proxy_sa(Pm_in, ws[0], wl.heads, residual), "proxy_sa")
+    got = P.proxy_xattn(xd, _grid(wl), Pd, aw[1], residual=residual, out_dtype=out_dt)
+    assert_close(host(got), O.proxy_xattn(x, Pm_in, ws[1], wl.heads, residual), "proxy_xattn")
+    got = P.window_sa(xd, _grid(wl), wl.win, aw[2], residual=residual, out_dtype=out_dt)
+    assert_close(host(got), O.window_sa(x, wl.grid, wl.win, ws[2], wl.heads, residual), "window_sa")
+    got = P.shift_window_sa(xd, _grid(wl), wl.win, wl.shift, aw[3], residual=residual, out_dtype=out_dt)
+    ref = O.shift_window_sa(x, wl.grid, wl.win, wl.shift, ws[3], wl.heads, residual)
+    assert_close(host(got), ref, "shift_window_sa")
+
+
+def test_peaked_softmax_and_bf16_outputs(P):
+    """Weights x10 make the softmax peaked (exercises the online rescale over
+    key blocks); outputs stored in bf16."""
+    wl = _wl(H=32, W=32, p=(1, 2, 2))  # 256 proxies -> four key blocks
+    announce("peaked softmax")
+    x = make_x(wl, seed=301)
+    ws = [_weights(wl, a, scale=0.06) for a in range(4)]
+    aw = [P.AttnWeights.from_dict(w, BF16, "cuda") for w in ws]
+    Pm = O.proxy_pool(x, wl.grid, wl.p)
+    Pd = dev(Pm, F32)
+    got = P.proxy_xattn(dev(x, BF16), _grid(wl), Pd, aw[1], residual=False, out_dtype=BF16)
+    assert_close(host(got), O.proxy_xattn(x, Pm, ws[1], wl.heads, False), "xattn peaked")
+    got = P.shift_window_sa(dev(x, BF16), _grid(wl), wl.win, wl.shift, aw[3], residual=False,
+                            out_dtype=BF16)
+    assert_close(host(got), O.shift_window_sa(x, wl.grid, wl.win, wl.shift, ws[3], wl.heads, False),
+                 "swsa peaked")
+
+
+@pytest.mark.parametrize("kw", [dict(win=(1, 1, 1), shift=(0, 0, 0)), dict(win=(1, 16, 8), shift=(0, 15, 7)),
+                                dict(H=5, W=6, win=(1, 8, 8), shift=(0, 4, 4), p=(1, 5, 3)),
+                                dict(F=2, H=8, W=8, win=(2, 8, 8), shift=(1, 0, 0), p=(1, 1, 1))],
+                         ids=["one_token", "win128_maxshift", "grid_smaller_than_window", "p111_temporal"])
+def test_window_edge_cases(P, kw):
+    wl = _wl(**kw)
+    announce(f"window edge {kw}")
+    x = make_x(wl, seed=400)
+    ws = _weights(wl, 3)
+    aw = P.AttnWeights.from_dict(ws, BF16, "cuda")
+    got = P.shift_window_sa(dev(x, BF16), _grid(wl), wl.win, wl.shift, aw, residual=False, out_dtype=F32)
+    assert_close(host(got), O.shift_window_sa(x, wl.grid, wl.win, wl.shift, ws, wl.heads, False), "edge")
+
+
+def test_one_proxy_and_many_proxies(P):
+    for kw in (dict(F=2, H=4, W=6, p=(2, 4, 6)), dict(H=20, W=30, p=(1, 1, 1))):
+        wl = _wl(**kw)
+        announce(f"proxies M={wl.M}")
+        x = make_x(wl, seed=500)
+        ws = [_weights(wl, a) for a in range(2)]
+        aw = [P.AttnWeights.from_dict(w, BF16, "cuda") for w in ws]
+        Pm = O.proxy_pool_f32(x, wl.grid, wl.p)
+        P2 = P.proxy_sa(dev(Pm, F32), wl.heads, aw[0], out_dtype=F32)
+        P2o = O.proxy_sa(Pm, ws[0], wl.heads).astype(np.float32)
+        assert_close(host(P2), P2o, "proxy_sa")
+        got = P.proxy_xattn(dev(x, BF16), _grid(wl), dev(P2o, F32), aw[1], residual=False, out_dtype=F32)
+        assert_close(host(got), O.proxy_xattn(x, P2o, ws[1], wl.heads, False), "xattn")
+
+
+def test_error_paths_leave_outputs_untouched(P):
+    wl = _wl()
+    x = dev(make_x(wl, seed=1), BF16)
+    out = torch.full((1, wl.M, wl.D), 7.0, device="cuda")
+    with pytest.raises(P.PtditError) as e:
+        P.proxy_pool(x, _grid(wl), (1, 5, 5), out=out)
+    assert e.value.status == -3
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    aw = P.AttnWeights.from_dict(_weights(wl, 2), BF16, "cuda")
+    o2 = torch.full(x.shape, 3.0, device="cuda")
+    with pytest.raises(P.PtditError):
+        P.shift_window_sa(x, _grid(wl), wl.win, (0, 8, 4), aw, out=o2)
+    import ctypes
+    from diffusion_transformer_attention_pt_amd import _lib
+    tiny_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    cw = aw.c()
+    st = P.load().ptdit_window_sa(x.data_ptr(), 0, _lib.Grid(*_grid(wl)), _lib.Win3(*wl.win), ctypes.byref(cw),
+                                  1, o2.data_ptr(), 1, tiny_ws.data_ptr(), 16, 0, _lib._stream())
+    assert st == -6
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 3.0)
+
+
+def test_empty_batch_is_noop(P):
+    wl = _wl(B=0)
+    x = torch.empty(0, wl.N, wl.D, dtype=BF16, device="cuda")
+    aw = P.AttnWeights.from_dict(_weights(_wl(), 2), BF16, "cuda")
+    y = P.window_sa(x, _grid(wl), wl.win, aw)
+    assert y.shape == x.shape
+    Pp = P.proxy_pool(x, _grid(wl), wl.p)
+    assert Pp.shape[0] == 0
+
+
+# ----------------------------------------------------------------------------- whole block, every workload
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_block_vs_oracle(P, name):
+    wl = WORKLOADS[name]
+    prec = _prec(wl)
+    announce(f"block {name} B={wl.B} grid={wl.grid} p={wl.p} win={wl.win} shift={wl.shift} {wl.dtype}")
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=prec)
+    xd = dev(x, prec)
+    blk.forward(xd)
+    torch.cuda.synchronize()
+    ref = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)
+    inter = blk.intermediates()
+    for k in ("P", "P2", "x1", "x2", "x3"):
+        assert_close(host(inter[k]), ref[k], f"{name}.{k}")
+    # the sum of the four branches alone (input removed) must also meet the bar
+    assert_close(host(inter["x3"]) - x, ref["x3"] - x, f"{name}.branches")
+    # a second forward on the same buffers gives identical bits
+    first = inter["x3"].clone()
+    blk.forward(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(first, blk.x3)
