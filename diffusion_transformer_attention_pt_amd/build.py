@@ -28,6 +28,7 @@ COMMON_FLAGS = [
     "-fno-fast-math", "-ffp-contract=on",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]

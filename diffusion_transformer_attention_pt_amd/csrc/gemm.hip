@@ -12,6 +12,8 @@
 // consecutive OUTPUT COLUMNS of one row: the epilogue adds bias / residual and
 // stores 4 contiguous values per lane, both for row-major outputs and for the
 // head-major Q/K/V layout [b][group][head][token][dh] (dh % 4 == 0).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,7 +48,39 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int ti
   tn = in / gm;
 }
 
-template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN, bool HEADMAJOR>
+// Raw global->register staging of one 16-byte LDS chunk (8 elements of A).
+// fp32 sources keep their 32 raw bytes until the LDS store, so the global
+// loads stay in flight across the MFMAs instead of being waited on for the
+// conversion.
+template <typename TA> struct Stage;
+template <> struct Stage<uint16_t> {
+  uint4 v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ void zero() { v = uint4{0, 0, 0, 0}; }
+  __device__ uint4 bf16() const { return v; }
+};
+template <> struct Stage<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ void zero() { a = b = float4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ uint4 bf16() const {
+    return uint4{pack_bf2(a.x, a.y), pack_bf2(a.z, a.w), pack_bf2(b.x, b.y), pack_bf2(b.z, b.w)};
+  }
+};
+
+// Pipeline (one barrier per 64-wide k step, LDS double buffer, register
+// double buffer of MFMA fragments):
+//   issue global loads of step kt+1 into staging registers
+//   read fragments (kt, k 32..63)            | MFMAs on fragments (kt, k 0..31)
+//   write staging registers to the other LDS buffer; barrier
+//   read fragments (kt+1, k 0..31)           | MFMAs on fragments (kt, k 32..63)
+// A buffer is rewritten one iteration after its last read, and every read of
+// it completed before the barrier that separates the two.
+template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN, bool HEADMAJOR,
+          bool KFULL>
 __global__ void __launch_bounds__(WM* WN * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = WM * WN * 64;
@@ -61,8 +95,9 @@ gemm_bf16_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (p.N + BN - 1) / BN;
+  if ((int)blockIdx.x >= tiles_m * tiles_n) return;  // grid larger than the tile count
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tm, tn);
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
 
@@ -70,36 +105,51 @@ gemm_bf16_kernel(GemmParams p) {
   const int K = p.K;
   const int KT = (K + 63) / 64;
 
-  uint4 ra[ACH], rw[WCH];
+  // Thread t stages chunk c = t % 8 of rows r0 + i * RS (i < ACH for A, i < WCH for W).
+  // Rows past the edge are clamped: loaded but never stored.
+  constexpr int RS = NT / 8;
+  const int r0 = tid >> 3, c8 = (tid & 7) * 8;
+
+  Stage<TA> ra[ACH];
+  Stage<uint16_t> rw[WCH];
   auto gload = [&](int kt) {
+    const int k = kt * 64 + c8;
+    const bool ok = KFULL || k < K;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-      const int q = tid + i * NT, row = q >> 3, c = q & 7;
-      const int k = kt * 64 + c * 8;
-      int64_t gm = m0 + row;
+      int64_t gm = m0 + r0 + i * RS;
       gm = gm < p.M ? gm : p.M - 1;
-      ra[i] = k < K ? load8_as_bf16(A + gm * K + k) : uint4{0, 0, 0, 0};
+      if (ok) ra[i].load(A + gm * K + k);
+      else ra[i].zero();
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int q = tid + i * NT, row = q >> 3, c = q & 7;
-      const int k = kt * 64 + c * 8;
-      int gn = n0 + row;
+      int gn = n0 + r0 + i * RS;
       gn = gn < p.N ? gn : p.N - 1;
-      rw[i] = k < K ? *reinterpret_cast<const uint4*>(p.W + (int64_t)gn * K + k) : uint4{0, 0, 0, 0};
+      if (ok) rw[i].load(p.W + (int64_t)gn * K + k);
+      else rw[i].zero();
     }
   };
   auto lstore = [&](int buf) {
+    const int c = tid & 7;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-      const int q = tid + i * NT, row = q >> 3, c = q & 7;
-      lds[buf][row * 8 + (c ^ (row & 7))] = ra[i];
+      const int row = r0 + i * RS;
+      lds[buf][row * 8 + (c ^ (row & 7))] = ra[i].bf16();
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int q = tid + i * NT, row = q >> 3, c = q & 7;
-      lds[buf][(BM + row) * 8 + (c ^ (row & 7))] = rw[i];
+      const int row = r0 + i * RS;
+      lds[buf][(BM + row) * 8 + (c ^ (row & 7))] = rw[i].bf16();
     }
+  };
+  // fragments of k sub-step kk (0: k 0..31, 1: k 32..63); (row & 7) == (lane & 7)
+  auto lfrag = [&](int buf, int kk, uint4* wf, uint4* xf) {
+    const int sw = (kk * 4 + (lane >> 4)) ^ (lane & 7);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wf[i] = lds[buf][(BM + wn * TN + i * 16 + (lane & 15)) * 8 + sw];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) xf[j] = lds[buf][(wm * TM + j * 16 + (lane & 15)) * 8 + sw];
   };
 
   floatx4 acc[FN][FM];
@@ -107,35 +157,28 @@ gemm_bf16_kernel(GemmParams p) {
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
+  auto mma = [&](const uint4* wf, const uint4* xf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+  };
 
+  uint4 w0[FN], x0[FM], w1[FN], x1[FM];
   gload(0);
   lstore(0);
   __syncthreads();
+  lfrag(0, 0, w0, x0);
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 4 + (lane >> 4);
-      const int sw = c ^ (lane & 7);  // (row & 7) == (lane & 7) for every fragment row
-      uint4 wf[FN], xf[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * TN + i * 16 + (lane & 15);
-        wf[i] = lds[buf][(BM + row) * 8 + sw];
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * TM + j * 16 + (lane & 15);
-        xf[j] = lds[buf][row * 8 + sw];
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+    const bool more = kt + 1 < KT;
+    if (more) gload(kt + 1);
+    lfrag(buf, 1, w1, x1);
+    mma(w0, x0);
+    if (more) lstore(buf ^ 1);
     __syncthreads();
+    if (more) lfrag(buf ^ 1, 0, w0, x0);
+    mma(w1, x1);
   }
 
   // Epilogue: lane holds C[m][n .. n+3].
@@ -173,6 +216,343 @@ gemm_bf16_kernel(GemmParams p) {
       }
     }
   }
+}
+
+// ----------------------------------------------------------------------------
+// Multi-stage variant: global -> LDS directly (global_load_lds_dwordx4), no
+// staging registers, a ring of STAGES k-slices of 32 with STAGES-1 in flight.
+//
+// A DMA instruction moves 64 lanes x 16 bytes into 1 KB of LDS at a
+// wave-uniform base, lane l landing at base + 16*l. The swizzle is therefore
+// applied on the global side: LDS slot (row, p) receives global chunk
+// c = p ^ swz(row), so fragment reads (16 rows, one chunk each) stay
+// conflict-free:
+//   bf16 rows (32 values = 4 chunks):  c = p ^ ((row >> 1) & 3)
+//   fp32 rows (32 values = 8 chunks):  c = p ^ (row & 7); a fragment of 8
+//   values is two chunks, converted to bf16 (v_cvt_pk_bf16_f32) after the read.
+// Per k-slice each wave waits until its own loads for the slice have landed
+// (s_waitcnt vmcnt), then one barrier publishes the slice to all waves and
+// retires every read of the slot about to be refilled.
+// ----------------------------------------------------------------------------
+#define PTDIT_GLDS16(gptr, lptr)                                                                 \
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(gptr),       \
+                                   (void __attribute__((address_space(3)))*)(lptr), 16, 0, 0)
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n must be a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  if constexpr (N == 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (n >= N) wait_vm_lgkm0<N>();
+    else wait_vm_dyn<N - 1>(n);
+  }
+}
+
+// Barrier that orders LDS traffic without draining the in-flight DMA ring
+// (the compiler-level "memory" clobbers keep LDS accesses on their side).
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename TA> struct DmaA;
+template <> struct DmaA<uint16_t> {
+  static constexpr int CPR = 4;  // 16-byte chunks per row per k-slice
+  __device__ static int chunk(int row, int p) { return p ^ ((row >> 1) & 3); }
+  // fragment (row, 8-value group g) -> 8 bf16
+  __device__ static uint4 frag(const uint4* base, int row, int g) {
+    return base[row * 4 + (g ^ ((row >> 1) & 3))];
+  }
+};
+template <> struct DmaA<float> {
+  static constexpr int CPR = 8;
+  __device__ static int chunk(int row, int p) { return p ^ (row & 7); }
+  __device__ static uint4 frag(const uint4* base, int row, int g) {
+    const uint4 lo = base[row * 8 + ((2 * g) ^ (row & 7))];
+    const uint4 hi = base[row * 8 + ((2 * g + 1) ^ (row & 7))];
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    auto cv = [](unsigned a, unsigned b) {
+      return __builtin_bit_cast(unsigned, __builtin_convertvector(f2{__uint_as_float(a), __uint_as_float(b)}, bf2));
+    };
+    return uint4{cv(lo.x, lo.y), cv(lo.z, lo.w), cv(hi.x, hi.y), cv(hi.z, hi.w)};
+  }
+};
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Each ring slot is its own __shared__ array and every slot index is a
+// compile-time constant: the compiler's wait insertion then knows that
+// fragment reads of slot s cannot alias the DMA in flight into other slots,
+// and does not drain the ring before every read.
+template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN, int STAGES, bool HEADMAJOR>
+__global__ void __launch_bounds__(WM* WN * 64, 1)
+gemm_dma_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int CA = DmaA<TA>::CPR;
+  constexpr int SA = BM * CA, SB = BN * 4;      // 16-byte slots per stage
+  constexpr int IA = SA / 64, IB = SB / 64;     // DMA instructions per stage
+  constexpr int IT = IA + IB;
+  constexpr int MAXI = (IT + NW - 1) / NW;      // per wave, upper bound
+  static_assert(SA % 64 == 0 && SB % 64 == 0, "stage must be whole DMA instructions");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+
+  // Epilogue staging: band j = tile rows {wm*TM + j*16 + r}, i.e. WM*16 rows
+  // x BN columns, row pitch padded by 16 bytes. A bf16 band fills one ring
+  // slot, an fp32 band two, so BPP = STAGES (bf16) or STAGES/2 (fp32) bands are
+  // staged per pass.
+  constexpr int EPI_PITCH = BN + 16 / (int)sizeof(TY);           // elements
+  constexpr int EPI_ROWS = WM * 16;
+  constexpr int EPI_ROWS_PER_SLOT = sizeof(TY) == 2 ? EPI_ROWS : EPI_ROWS / 2;
+  constexpr int EPI_SLOT = (EPI_ROWS_PER_SLOT * EPI_PITCH * (int)sizeof(TY) + 15) / 16;  // uint4
+  constexpr int SLOT = (SA + SB) > EPI_SLOT ? (SA + SB) : EPI_SLOT;
+  constexpr int BPP = sizeof(TY) == 2 ? STAGES : STAGES / 2;       // bands per pass
+  static_assert(BPP >= 1, "fp32 staging spans two slots");
+
+  __shared__ uint4 ring0[SLOT];
+  __shared__ uint4 ring1[SLOT];
+  __shared__ uint4 ring2[STAGES > 2 ? SLOT : 1];
+  __shared__ uint4 ring3[STAGES > 3 ? SLOT : 1];
+  auto slot = [&](auto sI) -> uint4* {
+    constexpr int sl = decltype(sI)::value;
+    if constexpr (sl == 0) return ring0;
+    else if constexpr (sl == 1) return ring1;
+    else if constexpr (sl == 2) return ring2;
+    else return ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave % WM, wn = wave / WM;
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (p.N + BN - 1) / BN;
+  if ((int)blockIdx.x >= tiles_m * tiles_n) return;  // grid larger than the tile count
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int K = p.K;
+  const int KT = K / 32;
+
+  // This wave's DMA instructions j = wave + i*NW (i < MAXI). A wave with
+  // fewer than MAXI real instructions repeats its first one (same source,
+  // same LDS bytes), so every wave issues exactly MAXI per slice: the loop
+  // then has no wave-dependent branch and the vmcnt target is a constant.
+  const TA* A = reinterpret_cast<const TA*>(p.A);
+  const char* src[MAXI];
+  int dst[MAXI], stride[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int j0 = wave + i * NW;
+    const int j = j0 < IT ? j0 : wave;
+    if (j < IA) {
+      const int sl = j * 64 + lane, row = sl / CA, pp = sl % CA;
+      int64_t gm = m0 + row;
+      gm = gm < p.M ? gm : p.M - 1;
+      src[i] = reinterpret_cast<const char*>(A + gm * K + DmaA<TA>::chunk(row, pp) * (16 / sizeof(TA)));
+      dst[i] = j * 64;
+      stride[i] = 32 * (int)sizeof(TA);
+    } else {
+      const int sl = (j - IA) * 64 + lane, row = sl / 4, pp = sl % 4;
+      int gn = n0 + row;
+      gn = gn < p.N ? gn : p.N - 1;
+      src[i] = reinterpret_cast<const char*>(p.W + (int64_t)gn * K + (pp ^ ((row >> 1) & 3)) * 8);
+      dst[i] = SA + (j - IA) * 64;
+      stride[i] = 64;
+    }
+  }
+  auto issue = [&](int kt, uint4* st) {
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16(src[i] + kt * stride[i], st + dst[i]);
+  };
+
+  floatx4 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
+
+  // bias of this lane's output columns (4 bf16 per 16-column tile), fetched
+  // early and kept packed; used in the epilogue
+  uint2 biasp[FN];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
+    biasp[i] = (p.bias && n < p.N) ? *reinterpret_cast<const uint2*>(p.bias + n) : uint2{0u, 0u};
+  }
+
+  const int g = lane >> 4, lr = lane & 15;
+  auto compute = [&](const uint4* st) {
+    uint4 wf[FN], xf[FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int row = wn * TN + i * 16 + lr;
+      wf[i] = st[SA + row * 4 + (g ^ ((row >> 1) & 3))];
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, wm * TM + j * 16 + lr, g);
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+  };
+
+  // Prologue: slices 0 .. STAGES-2 in flight (KT >= STAGES-1 is guaranteed by the host).
+  static_for<0, STAGES - 1>([&](auto sI) { issue(decltype(sI)::value, slot(sI)); });
+
+  // Steady state: every slice kt < NMAIN refills the slot freed by slice
+  // kt-1 with slice kt+STAGES-1 (< KT). Branch-free body.
+  const int NMAIN = (KT - STAGES + 1) / STAGES * STAGES;
+  for (int kt0 = 0; kt0 < NMAIN; kt0 += STAGES) {
+    static_for<0, STAGES>([&](auto sI) {
+      constexpr int s = decltype(sI)::value;
+      wait_vm_lgkm0<(STAGES - 2) * MAXI>();
+      ring_barrier();
+      issue(kt0 + s + STAGES - 1, slot(std::integral_constant<int, (s + STAGES - 1) % STAGES>{}));
+      compute(slot(sI));
+    });
+  }
+  // Tail: the last KT - NMAIN (< 2*STAGES-1) slices; slot of slice NMAIN + t is t % STAGES.
+  static_for<0, 2 * STAGES - 2>([&](auto tI) {
+    constexpr int t = decltype(tI)::value;
+    const int kt = NMAIN + t;
+    if (kt < KT) {
+      const int ahead = min(STAGES - 2, KT - 1 - kt);
+      wait_vm_dyn<(STAGES - 2) * MAXI>(ahead * MAXI);
+      ring_barrier();
+      if (kt + STAGES - 1 < KT)
+        issue(kt + STAGES - 1, slot(std::integral_constant<int, (t + STAGES - 1) % STAGES>{}));
+      compute(slot(std::integral_constant<int, t % STAGES>{}));
+    }
+  });
+
+  // Epilogue through LDS: lane holds C[m][n .. n+3]; stage 16-row bands (bias
+  // added, converted to TY), then write whole 16-byte chunks in row order so a
+  // wave's stores cover long contiguous runs (rows of the tile are
+  // consecutive tokens; head-major chunks never straddle a head, dh % 8 == 0).
+  wait_vm_lgkm0<0>();
+  ring_barrier();  // ring drained, every fragment read retired
+  TY* Y = reinterpret_cast<TY*>(p.Y);
+  const TR* R = reinterpret_cast<const TR*>(p.R);
+  constexpr int E = 16 / (int)sizeof(TY);          // elements per 16-byte chunk
+  constexpr int CPRO = BN / E;                     // chunks per staged row
+
+  // Store-phase chunk assignment, fixed across bands: chunk q = tid + i*NT of
+  // a band is staged row sr = q / CPRO, chunk cc = q % CPRO (compile-time
+  // divisors). Column-dependent address parts are computed once here; rows
+  // advance by 16 per band, tracked as (batch, token) without division.
+  constexpr int NQ = (EPI_ROWS * CPRO + NW * 64 - 1) / (NW * 64);
+  int64_t colpart[NQ];
+  int rowbase[NQ];
+  bool qok[NQ];
+  const int64_t b0 = m0 / p.Ntok;            // one division per thread
+  const int64_t t0 = m0 - b0 * p.Ntok;
+  const int G = p.N / p.D;
+  const int64_t bstride = (int64_t)G * p.heads * p.Ntok * p.dh;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = tid + i * NW * 64;
+    const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
+    const int n = n0 + cc * E;
+    qok[i] = q < EPI_ROWS * CPRO && n < p.N;
+    rowbase[i] = (sr / 16) * TM + (sr % 16);
+    if constexpr (HEADMAJOR) {
+      const int gg = n / p.D, hn = n - gg * p.D;
+      const int h = hn / p.dh, d = hn - h * p.dh;
+      colpart[i] = ((int64_t)(gg * p.heads + h) * p.Ntok) * p.dh + d;
+    } else {
+      colpart[i] = n;
+    }
+  }
+
+  // band j lives in slot (j % BPP) [bf16] or slots 2*(j % BPP), 2*(j % BPP)+1 [fp32]
+  auto band_base = [&](auto jI, int sr) -> TY* {
+    constexpr int jj = decltype(jI)::value % BPP;
+    if constexpr (sizeof(TY) == 2) {
+      return reinterpret_cast<TY*>(slot(std::integral_constant<int, jj>{}));
+    } else {
+      return sr < EPI_ROWS_PER_SLOT ? reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj>{}))
+                                    : reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj + 1>{}));
+    }
+  };
+  static_for<0, (FM + BPP - 1) / BPP>([&](auto passI) {
+    constexpr int pass = decltype(passI)::value;
+    // stage bands pass*BPP .. pass*BPP+BPP-1
+    static_for<0, BPP>([&](auto kI) {
+      constexpr int jb = pass * BPP + decltype(kI)::value;
+      if constexpr (jb < FM) {
+        const int sr = wm * 16 + lr;
+        TY* base = band_base(std::integral_constant<int, jb>{}, sr);
+        const int lrow = sr % EPI_ROWS_PER_SLOT;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int c = wn * TN + i * 16 + 4 * (lane >> 4);
+          store4(base + lrow * EPI_PITCH + c, acc[i][jb][0] + __uint_as_float(biasp[i].x << 16),
+                 acc[i][jb][1] + __uint_as_float(biasp[i].x & 0xffff0000u),
+                 acc[i][jb][2] + __uint_as_float(biasp[i].y << 16),
+                 acc[i][jb][3] + __uint_as_float(biasp[i].y & 0xffff0000u));
+        }
+      }
+    });
+    ring_barrier();
+    static_for<0, BPP>([&](auto kI) {
+      constexpr int jb = pass * BPP + decltype(kI)::value;
+      if constexpr (jb < FM) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const int q = tid + i * NW * 64;
+          const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
+          const int rr = rowbase[i] + jb * 16;
+          if (!qok[i] || m0 + rr >= p.M) continue;
+          const TY* sb = band_base(std::integral_constant<int, jb>{}, sr);
+          const uint4 v = *reinterpret_cast<const uint4*>(sb + (sr % EPI_ROWS_PER_SLOT) * EPI_PITCH + cc * E);
+          if constexpr (HEADMAJOR) {
+            int64_t tok = t0 + rr, b = b0;
+            while (tok >= p.Ntok) { tok -= p.Ntok; ++b; }
+            *reinterpret_cast<uint4*>(Y + b * bstride + colpart[i] + tok * p.dh) = v;
+          } else {
+            const int64_t off = (m0 + rr) * p.N + colpart[i];
+            if (R) {
+              if constexpr (sizeof(TY) == 4) {
+                const float4 r = load4f(R + off);
+                float4 o = __builtin_bit_cast(float4, v);
+                o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+                *reinterpret_cast<float4*>(Y + off) = o;
+              } else {
+                float f[8], rv[8];
+                unpack8(v, f);
+                const float4 r0 = load4f(R + off), r1 = load4f(R + off + 4);
+                rv[0] = r0.x; rv[1] = r0.y; rv[2] = r0.z; rv[3] = r0.w;
+                rv[4] = r1.x; rv[5] = r1.y; rv[6] = r1.z; rv[7] = r1.w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] += rv[e];
+                *reinterpret_cast<uint4*>(Y + off) = pack8(f);
+              }
+            } else {
+              *reinterpret_cast<uint4*>(Y + off) = v;
+            }
+          }
+        }
+      }
+    });
+    if constexpr (pass + 1 < (FM + BPP - 1) / BPP) ring_barrier();  // staging reused by the next pass
+  });
 }
 
 // ----------------------------------------------------------------------------
@@ -268,14 +648,35 @@ template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN,
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * (int64_t)((p.N + BN - 1) / BN);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TA, TR, TY, BM, BN, WM, WN, HM>), dim3((unsigned)tiles),
+  if (p.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_bf16_kernel<TA, TR, TY, BM, BN, WM, WN, HM, true>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<TA, TR, TY, BM, BN, WM, WN, HM, false>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN, int S, bool HM>
+static hipError_t run_dma(const GemmParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * (int64_t)((p.N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_dma_kernel<TA, TR, TY, BM, BN, WM, WN, S, HM>), dim3((unsigned)tiles),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
+// Tile choice. Token-row projections (M >= 2048 rows, K a multiple of 32) use
+// the multi-stage DMA kernel with 256x288 tiles: 288 = 4 heads of 72, and
+// D = 1152 = 4 x 288, 3D = 12 x 288, so a 2048^2 image block yields exactly
+// 256 (N = D) or 768 (N = 3D) tiles for 256 CUs. Proxy-row projections and odd
+// shapes use the register-staged kernel.
 template <typename TA, typename TR, typename TY, bool HM>
 static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
-  if (p.M >= 2048) return run_bf16<TA, TR, TY, 256, 192, 2, 2, HM>(p, s);
+  constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
+  if (p.M >= 2048 && p.K % 32 == 0 && p.K / 32 >= STAGES)
+    return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
+  if (p.M >= 1024) return run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s);
   return run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
 }
 
