@@ -77,6 +77,9 @@ def main() -> int:
     ap.add_argument("--workload", default="img2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="before the run, copy a 256 MiB buffer once (a plain copy kernel of known "
+                         "size, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this attention core is built and timed on a single "
@@ -92,6 +95,12 @@ def main() -> int:
     prec = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     x = torch.from_numpy(make_x(wl)).to(prec).to(dev)
     blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift,
                              make_all_weights(wl), prec=prec, device=dev)
