@@ -70,6 +70,25 @@ struct BF16P {
     sm.vt[c * 8 + 6][s] = (uint16_t)(vv.w & 0xffff); sm.vt[c * 8 + 7][s] = (uint16_t)(vv.w >> 16);
   }
 
+  // Stage chunk c of V for key slots 4*kq .. 4*kq+3 (rows may be NULL -> 0),
+  // transposed in registers: each V^T row gets one 8-byte write.
+  template <int KEYS>
+  __device__ static void stage_vquad(Smem<KEYS>& sm, int kq, int c, const T* const* rows) {
+    uint4 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = rows[e] ? *reinterpret_cast<const uint4*>(rows[e] + c * 8) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = (j & 1) * 16;
+      const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&v[0])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&v[1])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&v[2])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&v[3])[j >> 1] >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(&sm.vt[c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    }
+  }
+
   // S^T tile t: rows = keys t*16 .. +16, columns = the wave's 16 queries.
   template <int KEYS>
   __device__ static floatx4 score(const Smem<KEYS>& sm, const QF& q, int t, int lane) {
@@ -229,13 +248,13 @@ __global__ void __launch_bounds__(256) flash_kernel(FlashParams prm) {
       }
     mx = quad_max(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int t = 0; t < NTILE; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = exp2f(sc[t][r] - m_new);
+        const float e = fast_exp2(sc[t][r] - m_new);
         sc[t][r] = e;
         rs += e;
       }
@@ -256,6 +275,359 @@ __global__ void __launch_bounds__(256) flash_kernel(FlashParams prm) {
       const int d = i * 16 + 4 * (lane >> 4);
       if (d < DH) P::store_o(Ob + d, o[i][0] * inv, o[i][1] * inv, o[i][2] * inv, o[i][3] * inv);
     }
+  }
+}
+
+// ---------------------------------------------------------------- flash core, bf16, wide
+// Workgroup = 8 waves x 32 queries (two 16-query tiles per wave) of one
+// (batch, head). Keys stream in blocks of 64 through a double-buffered LDS
+// stage: block b+1 is loaded into registers while block b is computed, then
+// written to the other buffer (one barrier per block). V is transposed in
+// registers four keys at a time, so its LDS writes are 8-byte and
+// conflict-free. Both query tiles of a wave share every K / V^T fragment read.
+constexpr int FW_WAVES = 8, FW_QPW = 32, FW_KB = 64;
+constexpr int FW_Q = FW_WAVES * FW_QPW;
+
+template <int DH>
+__global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_wide(FlashParams prm) {
+  using P = BF16P<DH>;
+  constexpr int NT = FW_WAVES * 64, NKC = P::NKC, NDT = P::NDT, DCH = P::DCH;
+  constexpr int VTP = FW_KB + 4;  // V^T row pitch (elements)
+  __shared__ uint4 ks[2][FW_KB * DCH];
+  __shared__ uint16_t vt[2][NDT * 16][VTP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = lane >> 4, lr = lane & 15;
+  const uint16_t* Qb = reinterpret_cast<const uint16_t*>(prm.Q) + b * prm.q_bs + h * prm.q_hs;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(prm.K) + b * prm.k_bs + h * prm.k_hs;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(prm.V) + b * prm.v_bs + h * prm.v_hs;
+  const int q0 = blockIdx.x * FW_Q + wave * FW_QPW;
+
+  typename P::QF qf[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = q0 + t * 16 + lr;
+    qf[t] = P::load_q(q < prm.Nq ? Qb + (int64_t)q * DH : nullptr, lane);
+  }
+  // zero the padded V^T rows (d >= DH) of both buffers once
+  for (int i = tid; i < 2 * (NDT * 16 - DH) * VTP; i += NT) {
+    const int bb = i / ((NDT * 16 - DH) * VTP), r = i % ((NDT * 16 - DH) * VTP);
+    vt[bb][DH + r / VTP][r % VTP] = 0;
+  }
+
+  // staging work items per block: K chunks (key, c) and V quads (c, key quad)
+  constexpr int KITEMS = FW_KB * DCH, VITEMS = DCH * (FW_KB / 4);
+  constexpr int KPT = (KITEMS + NT - 1) / NT, VPT = (VITEMS + NT - 1) / NT;
+  uint4 kreg[KPT], vreg[VPT][4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int it = tid + i * NT;
+      kreg[i] = uint4{0, 0, 0, 0};
+      if (it < KITEMS) {
+        const int key = it / DCH, c = it % DCH, gk = k0 + key;
+        if (gk < prm.Nk) kreg[i] = *reinterpret_cast<const uint4*>(Kb + (int64_t)gk * DH + c * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int it = tid + i * NT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vreg[i][e] = uint4{0, 0, 0, 0};
+      if (it < VITEMS) {
+        const int c = it / (FW_KB / 4), kq = it % (FW_KB / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gk = k0 + kq * 4 + e;
+          if (gk < prm.Nk) vreg[i][e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)gk * DH + c * 8);
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int it = tid + i * NT;
+      if (it < KITEMS) ks[buf][it] = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int it = tid + i * NT;
+      if (it < VITEMS) {
+        const int c = it / (FW_KB / 4), kq = it % (FW_KB / 4);
+        // row d = 8c + j holds keys kq*4 .. kq*4+3: gather element j of the 4 key vectors
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int sh = (j & 1) * 16;
+          const uint32_t a0 = (w0[j >> 1] >> sh) & 0xffffu, a1 = (w1[j >> 1] >> sh) & 0xffffu;
+          const uint32_t a2 = (w2[j >> 1] >> sh) & 0xffffu, a3 = (w3[j >> 1] >> sh) & 0xffffu;
+          *reinterpret_cast<uint2*>(&vt[buf][c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+        }
+      }
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  floatx4 o[2][NDT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) o[t][i] = zero4();
+
+  const int nblk = (prm.Nk + FW_KB - 1) / FW_KB;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    const int k0 = blk * FW_KB;
+    if (blk + 1 < nblk) gload(k0 + FW_KB);
+    // S^T tiles: 4 key tiles x 2 query tiles, K fragments shared
+    floatx4 sc[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sc[0][kt] = zero4();
+      sc[1][kt] = zero4();
+      const int key = kt * 16 + lr;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int d = kc * 32 + 8 * g;
+        const uint4 kf = d < DH ? ks[buf][key * DCH + d / 8] : uint4{0, 0, 0, 0};
+        sc[0][kt] = mfma_bf16(kf, qf[0].v[kc], sc[0][kt]);
+        sc[1][kt] = mfma_bf16(kf, qf[1].v[kc], sc[1][kt]);
+      }
+    }
+    const bool full = k0 + FW_KB <= prm.Nk;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kt * 16 + 4 * g + r;
+          const float v = (full || key < prm.Nk) ? sc[t][kt][r] * prm.sl2 : -INFINITY;
+          sc[t][kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = quad_max(mx);
+      const float m_new = fmaxf(m_run[t], mx);
+      const float alpha = fast_exp2(m_run[t] - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = fast_exp2(sc[t][kt][r] - m_new);
+          sc[t][kt][r] = e;
+          rs += e;
+        }
+      rs = quad_sum(rs);
+      l_run[t] = l_run[t] * alpha + rs;
+      m_run[t] = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[t][i] *= alpha;
+    }
+    // O^T += V^T P^T, V^T fragments shared by both query tiles
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint4 pf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        pf[t] = uint4{pack_bf2(sc[t][2 * u][0], sc[t][2 * u][1]), pack_bf2(sc[t][2 * u][2], sc[t][2 * u][3]),
+                      pack_bf2(sc[t][2 * u + 1][0], sc[t][2 * u + 1][1]),
+                      pack_bf2(sc[t][2 * u + 1][2], sc[t][2 * u + 1][3])};
+      const int kb = u * 32 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int drow = dt * 16 + lr;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&vt[buf][drow][kb]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&vt[buf][drow][kb + 16]);
+        const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
+        o[0][dt] = mfma_bf16(vf, pf[0], o[0][dt]);
+        o[1][dt] = mfma_bf16(vf, pf[1], o[1][dt]);
+      }
+    }
+    if (blk + 1 < nblk) {
+      lstore(buf ^ 1);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = q0 + t * 16 + lr;
+    if (q < prm.Nq) {
+      const float inv = 1.f / l_run[t];
+      uint16_t* Ob = reinterpret_cast<uint16_t*>(prm.O) + ((int64_t)b * prm.Nq + q) * prm.D + h * DH;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int d = i * 16 + 4 * g;
+        if (d < DH) store4(Ob + d, o[t][i][0] * inv, o[t][i][1] * inv, o[t][i][2] * inv, o[t][i][3] * inv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- flash core, bf16, K/V resident
+// For up to 256 keys (every image workload: 256 proxies). Workgroup = 8 waves
+// bound to one (batch, head) and a contiguous range of queries: K and V^T of
+// that head are staged in LDS once, then the workgroup walks its range in
+// blocks of 256 queries (32 per wave) with the next block's Q fragments
+// loaded while the current block is computed. No barrier inside the loop.
+constexpr int FR_MAXK = 256;
+
+template <int DH>
+__global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams prm, int q_per_wg) {
+  using P = BF16P<DH>;
+  constexpr int NT = FW_WAVES * 64, NKC = P::NKC, NDT = P::NDT, DCH = P::DCH;
+  constexpr int VTP = FR_MAXK + 4;
+  __shared__ uint4 ks[FR_MAXK * DCH];
+  __shared__ uint16_t vt[NDT * 16][VTP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = lane >> 4, lr = lane & 15;
+  const uint16_t* Qb = reinterpret_cast<const uint16_t*>(prm.Q) + b * prm.q_bs + h * prm.q_hs;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(prm.K) + b * prm.k_bs + h * prm.k_hs;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(prm.V) + b * prm.v_bs + h * prm.v_hs;
+  const int nkb = (prm.Nk + FW_KB - 1) / FW_KB;     // 64-key blocks
+  const int qbeg = blockIdx.x * q_per_wg;
+  const int qend = min(prm.Nq, qbeg + q_per_wg);
+
+  auto load_qf = [&](int qblk, typename P::QF* qf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = qblk + wave * FW_QPW + t * 16 + lr;
+      qf[t] = P::load_q(q < qend ? Qb + (int64_t)q * DH : nullptr, lane);
+    }
+  };
+  typename P::QF qf[2], qn[2];
+  load_qf(qbeg, qf);
+
+  // stage K (chunks) and V^T (four keys per item) of all keys, zero beyond Nk
+  for (int it = tid; it < nkb * FW_KB * DCH; it += NT) {
+    const int key = it / DCH, c = it % DCH;
+    ks[it] = key < prm.Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+  }
+  for (int it = tid; it < DCH * (nkb * FW_KB / 4); it += NT) {
+    const int c = it / (nkb * FW_KB / 4), kq = it % (nkb * FW_KB / 4);
+    uint4 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = kq * 4 + e;
+      v[e] = key < prm.Nk ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = (j & 1) * 16;
+      const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&v[0])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&v[1])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&v[2])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&v[3])[j >> 1] >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(&vt[c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    }
+  }
+  for (int i = tid; i < (NDT * 16 - DH) * VTP; i += NT) vt[DH + i / VTP][i % VTP] = 0;
+  __syncthreads();
+
+  for (int qblk = qbeg; qblk < qend; qblk += FW_Q) {
+    if (qblk + FW_Q < qend) load_qf(qblk + FW_Q, qn);
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    floatx4 o[2][NDT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[t][i] = zero4();
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int k0 = kb * FW_KB;
+      floatx4 sc[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sc[0][kt] = zero4();
+        sc[1][kt] = zero4();
+        const int key = k0 + kt * 16 + lr;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const int d = kc * 32 + 8 * g;
+          const uint4 kf = d < DH ? ks[key * DCH + d / 8] : uint4{0, 0, 0, 0};
+          sc[0][kt] = mfma_bf16(kf, qf[0].v[kc], sc[0][kt]);
+          sc[1][kt] = mfma_bf16(kf, qf[1].v[kc], sc[1][kt]);
+        }
+      }
+      const bool full = k0 + FW_KB <= prm.Nk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + kt * 16 + 4 * g + r;
+            const float v = (full || key < prm.Nk) ? sc[t][kt][r] * prm.sl2 : -INFINITY;
+            sc[t][kt][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = quad_max(mx);
+        const float m_new = fmaxf(m_run[t], mx);
+        const float alpha = fast_exp2(m_run[t] - m_new);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(sc[t][kt][r] - m_new);
+            sc[t][kt][r] = e;
+            rs += e;
+          }
+        rs = quad_sum(rs);
+        l_run[t] = l_run[t] * alpha + rs;
+        m_run[t] = m_new;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) o[t][i] *= alpha;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint4 pf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          pf[t] = uint4{pack_bf2(sc[t][2 * u][0], sc[t][2 * u][1]), pack_bf2(sc[t][2 * u][2], sc[t][2 * u][3]),
+                        pack_bf2(sc[t][2 * u + 1][0], sc[t][2 * u + 1][1]),
+                        pack_bf2(sc[t][2 * u + 1][2], sc[t][2 * u + 1][3])};
+        const int kbase = k0 + u * 32 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int drow = dt * 16 + lr;
+          const uint2 lo = *reinterpret_cast<const uint2*>(&vt[drow][kbase]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&vt[drow][kbase + 16]);
+          const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
+          o[0][dt] = mfma_bf16(vf, pf[0], o[0][dt]);
+          o[1][dt] = mfma_bf16(vf, pf[1], o[1][dt]);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = qblk + wave * FW_QPW + t * 16 + lr;
+      if (q < qend) {
+        const float inv = 1.f / l_run[t];
+        uint16_t* Ob = reinterpret_cast<uint16_t*>(prm.O) + ((int64_t)b * prm.Nq + q) * prm.D + h * DH;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+          const int d = i * 16 + 4 * g;
+          if (d < DH) store4(Ob + d, o[t][i][0] * inv, o[t][i][1] * inv, o[t][i][2] * inv, o[t][i][3] * inv);
+        }
+      }
+    }
+    qf[0] = qn[0];
+    qf[1] = qn[1];
   }
 }
 
@@ -285,7 +657,7 @@ __global__ void __launch_bounds__(NTILE * 64) window_kernel(WindowParams prm) {
   constexpr int KEYS = NTILE2 * 16;
   __shared__ typename P::template Smem<KEYS> sm;
   __shared__ int tok_s[KEYS];
-  __shared__ int lab_s[KEYS];
+  __shared__ __attribute__((aligned(16))) int lab_s[KEYS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -321,12 +693,32 @@ __global__ void __launch_bounds__(NTILE * 64) window_kernel(WindowParams prm) {
   const T* bk = bias ? bias + prm.D + h * DH : nullptr;
   const T* bv = bias ? bias + 2 * prm.D + h * DH : nullptr;
 
-  for (int idx = tid; idx < KEYS * P::DCH; idx += NT) {
-    const int s = idx / P::DCH, c = idx - s * P::DCH;
-    const int tok = tok_s[s];
-    const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
-    const T* vr = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
-    P::stage(sm, s, c, kr, vr);
+  if constexpr (P::TPV == 2) {
+    // bf16: K chunk by chunk, V four slots at a time (transposed in registers)
+    for (int idx = tid; idx < KEYS * P::DCH; idx += NT) {
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      const int tok = tok_s[s];
+      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
+      sm.k[s * P::DCH + c] = kr ? *reinterpret_cast<const uint4*>(kr + c * 8) : uint4{0, 0, 0, 0};
+    }
+    for (int idx = tid; idx < P::DCH * (KEYS / 4); idx += NT) {
+      const int c = idx / (KEYS / 4), kq = idx - c * (KEYS / 4);
+      const T* rows[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tok_s[kq * 4 + e];
+        rows[e] = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
+      }
+      P::stage_vquad(sm, kq, c, rows);
+    }
+  } else {
+    for (int idx = tid; idx < KEYS * P::DCH; idx += NT) {
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      const int tok = tok_s[s];
+      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
+      const T* vr = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
+      P::stage(sm, s, c, kr, vr);
+    }
   }
   __syncthreads();
 
@@ -336,16 +728,24 @@ __global__ void __launch_bounds__(NTILE * 64) window_kernel(WindowParams prm) {
   floatx4 sc[NTILE2];
 #pragma unroll
   for (int t = 0; t < NTILE2; ++t) sc[t] = P::score(sm, qf, t, lane);
+  // key slots of this lane: t*16 + 4*(lane/16) + r. Labels are read four at a
+  // time; without a shift every real slot of a window shares one label, so
+  // only the slots past the window need masking.
+  const bool masked = (prm.st | prm.sh | prm.sw) != 0;
   float mx = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < NTILE2; ++t)
+  for (int t = 0; t < NTILE2; ++t) {
+    const int ks0 = t * 16 + 4 * (lane >> 4);
+    const int4 lab4 = *reinterpret_cast<const int4*>(&lab_s[ks0]);
+    const int labs[4] = {lab4.x, lab4.y, lab4.z, lab4.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int ks = t * 16 + 4 * (lane >> 4) + r;
-      const float v = lab_s[ks] == qlab && ks < wsz ? sc[t][r] * prm.sl2 : -INFINITY;
+      const bool ok = ks0 + r < wsz && (!masked || labs[r] == qlab);
+      const float v = ok ? sc[t][r] * prm.sl2 : -INFINITY;
       sc[t][r] = v;
       mx = fmaxf(mx, v);
     }
+  }
   mx = quad_max(mx);
   if (mx == -INFINITY) mx = 0.f;  // slot past the window: keeps the idle column finite
   float rs = 0.f;
@@ -353,7 +753,7 @@ __global__ void __launch_bounds__(NTILE * 64) window_kernel(WindowParams prm) {
   for (int t = 0; t < NTILE2; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = exp2f(sc[t][r] - mx);
+      const float e = fast_exp2(sc[t][r] - mx);
       sc[t][r] = e;
       rs += e;
     }
@@ -389,8 +789,50 @@ static hipError_t run_flash(const FlashDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DH>
+static hipError_t run_flash_wide(const FlashDesc& d, hipStream_t s) {
+  FlashParams p;
+  p.Q = d.Q; p.q_bs = d.q_bs; p.q_hs = d.q_hs;
+  p.K = d.K; p.k_bs = d.k_bs; p.k_hs = d.k_hs;
+  p.V = d.V; p.v_bs = d.v_bs; p.v_hs = d.v_hs;
+  p.O = d.O; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
+  p.sl2 = d.scale * LOG2E;
+  dim3 grid((d.Nq + FW_Q - 1) / FW_Q, d.heads, d.B);
+  hipLaunchKernelGGL((flash_bf16_wide<DH>), grid, dim3(FW_WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DH>
+static hipError_t run_flash_resident(const FlashDesc& d, hipStream_t s) {
+  FlashParams p;
+  p.Q = d.Q; p.q_bs = d.q_bs; p.q_hs = d.q_hs;
+  p.K = d.K; p.k_bs = d.k_bs; p.k_hs = d.k_hs;
+  p.V = d.V; p.v_bs = d.v_bs; p.v_hs = d.v_hs;
+  p.O = d.O; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
+  p.sl2 = d.scale * LOG2E;
+  // about one workgroup per CU: split each (batch, head) query range so that
+  // B * heads * ranges ~ 256, ranges in whole 256-query blocks
+  const int pairs = d.B * d.heads;
+  int ranges = (256 + pairs - 1) / pairs;
+  const int qblocks = (d.Nq + FW_Q - 1) / FW_Q;
+  if (ranges > qblocks) ranges = qblocks;
+  if (ranges < 1) ranges = 1;
+  const int q_per_wg = (qblocks + ranges - 1) / ranges * FW_Q;
+  dim3 grid((d.Nq + q_per_wg - 1) / q_per_wg, d.heads, d.B);
+  hipLaunchKernelGGL((flash_bf16_resident<DH>), grid, dim3(FW_WAVES * 64), 0, s, p, q_per_wg);
+  return hipGetLastError();
+}
+
 hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s) {
   if (d.Nq == 0 || d.B == 0) return hipSuccess;
+  if (!f32 && d.Nq >= 2048 && d.Nk <= FR_MAXK) {
+    if (d.dh == 72) return run_flash_resident<72>(d, s);
+    if (d.dh == 64) return run_flash_resident<64>(d, s);
+  }
+  if (!f32 && d.Nq >= 2048) {
+    if (d.dh == 72) return run_flash_wide<72>(d, s);
+    if (d.dh == 64) return run_flash_wide<64>(d, s);
+  }
   if (d.dh == 72) return f32 ? run_flash<F32P<72>, 72>(d, s) : run_flash<BF16P<72>, 72>(d, s);
   if (d.dh == 64) return f32 ? run_flash<F32P<64>, 64>(d, s) : run_flash<BF16P<64>, 64>(d, s);
   return hipErrorInvalidValue;

@@ -20,8 +20,20 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-// Two floats -> two packed bf16 (low half = a).
-__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+// Two floats -> two packed bf16 (low half = a), software round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_bf2_sw(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+
+// Two floats -> two packed bf16 (low half = a) with the hardware converter
+// (v_cvt_pk_bf16_f32, round to nearest even under the default mode).
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// 2^x on the transcendental unit (v_exp_f32); inputs here are <= 0 and results
+// below the fp32 normal range may flush to zero.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
@@ -34,6 +46,14 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   uint4 r;
   r.x = pack_bf2(f[0], f[1]); r.y = pack_bf2(f[2], f[3]);
   r.z = pack_bf2(f[4], f[5]); r.w = pack_bf2(f[6], f[7]);
+  return r;
+}
+
+// software-RNE variant, for results specified bit-for-bit (window averages)
+__device__ __forceinline__ uint4 pack8_sw(const float* f) {
+  uint4 r;
+  r.x = pack_bf2_sw(f[0], f[1]); r.y = pack_bf2_sw(f[2], f[3]);
+  r.z = pack_bf2_sw(f[4], f[5]); r.w = pack_bf2_sw(f[6], f[7]);
   return r;
 }
 

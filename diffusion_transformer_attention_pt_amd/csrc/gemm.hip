@@ -312,7 +312,7 @@ gemm_dma_kernel(GemmParams p) {
   constexpr int MAXI = (IT + NW - 1) / NW;      // per wave, upper bound
   static_assert(SA % 64 == 0 && SB % 64 == 0, "stage must be whole DMA instructions");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
 
   // Epilogue staging: band j = tile rows {wm*TM + j*16 + r}, i.e. WM*16 rows
   // x BN columns, row pitch padded by 16 bytes. A bf16 band fills one ring
@@ -330,12 +330,20 @@ gemm_dma_kernel(GemmParams p) {
   __shared__ uint4 ring1[SLOT];
   __shared__ uint4 ring2[STAGES > 2 ? SLOT : 1];
   __shared__ uint4 ring3[STAGES > 3 ? SLOT : 1];
+  __shared__ uint4 ring4[STAGES > 4 ? SLOT : 1];
+  __shared__ uint4 ring5[STAGES > 5 ? SLOT : 1];
+  __shared__ uint4 ring6[STAGES > 6 ? SLOT : 1];
+  __shared__ uint4 ring7[STAGES > 7 ? SLOT : 1];
   auto slot = [&](auto sI) -> uint4* {
     constexpr int sl = decltype(sI)::value;
     if constexpr (sl == 0) return ring0;
     else if constexpr (sl == 1) return ring1;
     else if constexpr (sl == 2) return ring2;
-    else return ring3;
+    else if constexpr (sl == 3) return ring3;
+    else if constexpr (sl == 4) return ring4;
+    else if constexpr (sl == 5) return ring5;
+    else if constexpr (sl == 6) return ring6;
+    else return ring7;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -676,6 +684,9 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
   if (p.M >= 2048 && p.K % 32 == 0 && p.K / 32 >= STAGES)
     return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
+  // few rows (proxies): latency-bound, so a small tile with 7 k-slices in flight
+  if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 8)
+    return run_dma<TA, TR, TY, 64, 64, 2, 2, 8, HM>(p, s);
   if (p.M >= 1024) return run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s);
   return run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
 }

@@ -17,7 +17,7 @@ namespace ptdit {
 template <typename T> struct Vec8;
 template <> struct Vec8<uint16_t> {
   __device__ static void load(const uint16_t* p, float* f) { unpack8(*reinterpret_cast<const uint4*>(p), f); }
-  __device__ static void store(uint16_t* p, const float* f) { *reinterpret_cast<uint4*>(p) = pack8(f); }
+  __device__ static void store(uint16_t* p, const float* f) { *reinterpret_cast<uint4*>(p) = pack8_sw(f); }
 };
 template <> struct Vec8<float> {
   __device__ static void load(const float* p, float* f) {
