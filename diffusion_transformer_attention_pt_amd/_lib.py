@@ -69,9 +69,9 @@ def load() -> ctypes.CDLL:
         "ptdit_linear": [vp, i32, i64, i32, i32, vp, vp, vp, i32, vp, i32, i32, vp],
         "ptdit_proxy_pool": [vp, i32, G, W3, vp, i32, vp],
         "ptdit_proxy_sa": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
-        "ptdit_proxy_xattn": [vp, i32, G, vp, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
-        "ptdit_window_sa": [vp, i32, G, W3, AW, i32, vp, i32, vp, sz, i32, vp],
-        "ptdit_shift_window_sa": [vp, i32, G, W3, W3, AW, i32, vp, i32, vp, sz, i32, vp],
+        "ptdit_proxy_xattn": [vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
+        "ptdit_window_sa": [vp, vp, i32, G, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
+        "ptdit_shift_window_sa": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_roll3d": [vp, G, W3, i32, vp, i32, vp],
         "ptdit_workspace_bytes": [i32, G, i32, W3, i32],
         "ptdit_status_str": [i32],
@@ -210,7 +210,9 @@ def proxy_sa(P: torch.Tensor, heads: int, w: AttnWeights, residual: bool = True,
 
 def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnWeights,
                 residual: bool = True, out_dtype: Optional[torch.dtype] = None,
-                ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out_lowp: optional bf16 tensor of out's shape that receives bf16(out)."""
     lib = load()
     M = P2.shape[1]
     if out is None:
@@ -219,40 +221,47 @@ def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnW
     ws = _ws(need, ws, x.device)
     cw = w.c()
     st = lib.ptdit_proxy_xattn(_ptr(x), _dt(x.dtype), Grid(*grid), _ptr(P2), _dt(P2.dtype), M,
-                               ctypes.byref(cw), int(residual), _ptr(out), _dt(out.dtype), _ptr(ws),
-                               ws.numel(), _dt(w.dtype), _stream())
+                               ctypes.byref(cw), int(residual), _ptr(out), _ptr(out_lowp), _dt(out.dtype),
+                               _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
     _check("ptdit_proxy_xattn", st)
     return out
 
 
 def window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], w: AttnWeights,
               residual: bool = True, out_dtype: Optional[torch.dtype] = None,
-              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              x_lowp: Optional[torch.Tensor] = None, out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_lowp: optional bf16 copy of an fp32 x (read by the projection);
+    out_lowp: optional bf16 tensor that receives bf16(out)."""
     lib = load()
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_WINDOW_SA, grid, 0, win, w.dtype)
     ws = _ws(need, ws, x.device)
     cw = w.c()
-    st = lib.ptdit_window_sa(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*win), ctypes.byref(cw),
-                             int(residual), _ptr(out), _dt(out.dtype), _ptr(ws), ws.numel(),
-                             _dt(w.dtype), _stream())
+    st = lib.ptdit_window_sa(_ptr(x), _ptr(x_lowp), _dt(x.dtype), Grid(*grid), Win3(*win),
+                             ctypes.byref(cw), int(residual), _ptr(out), _ptr(out_lowp), _dt(out.dtype),
+                             _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
     _check("ptdit_window_sa", st)
     return out
 
 
 def shift_window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], shift: Sequence[int],
                     w: AttnWeights, residual: bool = True, out_dtype: Optional[torch.dtype] = None,
-                    ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    x_lowp: Optional[torch.Tensor] = None,
+                    out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_lowp / out_lowp as for window_sa."""
     lib = load()
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_SHIFT_WINDOW_SA, grid, 0, win, w.dtype)
     ws = _ws(need, ws, x.device)
     cw = w.c()
-    st = lib.ptdit_shift_window_sa(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*win), Win3(*shift),
-                                   ctypes.byref(cw), int(residual), _ptr(out), _dt(out.dtype),
-                                   _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
+    st = lib.ptdit_shift_window_sa(_ptr(x), _ptr(x_lowp), _dt(x.dtype), Grid(*grid), Win3(*win),
+                                   Win3(*shift), ctypes.byref(cw), int(residual), _ptr(out),
+                                   _ptr(out_lowp), _dt(out.dtype), _ptr(ws), ws.numel(), _dt(w.dtype),
+                                   _stream())
     _check("ptdit_shift_window_sa", st)
     return out
 

@@ -10,7 +10,9 @@ excerpt 2 (PT-Block forward) with Eq. GIIM and Eq. TCM of section 3:
 
 With bf16 precision the block input is bf16, the residual stream
 (P, P', x1, x2, x3) is kept in fp32 and every projection reads its operand
-rounded to bf16; with fp32 precision everything is fp32. Buffers and the
+rounded to bf16; x1 and x2 also get a bf16 copy from the epilogue that
+writes them, which the next call's Q/K/V projection reads (same values,
+half the bytes). With fp32 precision everything is fp32. Buffers and the
 workspace are allocated once, in the constructor; forward() only launches.
 """
 from __future__ import annotations
@@ -43,6 +45,9 @@ class PTBlockAttention:
         self.x1 = torch.empty(B, self.N, D, dtype=stream_dt, device=self.device)
         self.x2 = torch.empty_like(self.x1)
         self.x3 = torch.empty_like(self.x1)
+        lowp = prec == torch.bfloat16
+        self.x1_lowp = torch.empty(B, self.N, D, dtype=torch.bfloat16, device=self.device) if lowp else None
+        self.x2_lowp = torch.empty_like(self.x1_lowp) if lowp else None
         need = max(
             _lib.workspace_bytes(_lib.OP_PROXY_SA, (B, 1, 1, self.M, D, heads), self.M, (1, 1, 1), prec),
             _lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.M, (1, 1, 1), prec),
@@ -54,9 +59,11 @@ class PTBlockAttention:
         g, w = self.g, self.weights
         _lib.proxy_pool(x, g, self.p, out=self.P)
         _lib.proxy_sa(self.P, self.heads, w[0], residual=True, ws=self.ws, out=self.P2)
-        _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=self.ws, out=self.x1)
-        _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2)
-        _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3)
+        _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=self.ws, out=self.x1, out_lowp=self.x1_lowp)
+        _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2,
+                       x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
+        _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3,
+                             x_lowp=self.x2_lowp)
         return self.x3
 
     def intermediates(self) -> Dict[str, torch.Tensor]:

@@ -74,6 +74,14 @@ ptdit_status check_weights(const ptdit_attn_w* w) {
   return PTDIT_OK;
 }
 
+// Optional bf16 copies of fp32 activations (out_lowp written, x_lowp read):
+// only with bf16 precision and an fp32 tensor beside them.
+ptdit_status check_lowp(ptdit_dtype prec, const void* lowp, ptdit_dtype beside_dt) {
+  if (!lowp) return PTDIT_OK;
+  if (prec != PTDIT_BF16 || beside_dt != PTDIT_F32) return PTDIT_ERR_DTYPE;
+  return aligned16(lowp) ? PTDIT_OK : PTDIT_ERR_ALIGN;
+}
+
 ptdit_status check_grid(const ptdit_grid& g) {
   if (g.F < 0 || g.H < 0 || g.W < 0) return PTDIT_ERR_SHAPE;
   const int64_t N = (int64_t)g.F * g.H * g.W;
@@ -84,12 +92,13 @@ ptdit_status check_grid(const ptdit_grid& g) {
 hipError_t gemm(ptdit_dtype prec, const void* A, ptdit_dtype a_dt, int64_t M, int K, int N,
                 const void* W, const void* bias, const void* R, ptdit_dtype r_dt,
                 void* Y, ptdit_dtype y_dt, bool head_major, int64_t Ntok, int heads, int D,
-                int trace_cls, hipStream_t s) {
+                int trace_cls, hipStream_t s, void* Y2 = nullptr) {
   GemmDesc d;
   d.A = A; d.a_f32 = a_dt == PTDIT_F32;
   d.W = W; d.bias = bias;
   d.R = R; d.r_f32 = r_dt == PTDIT_F32;
   d.Y = Y; d.y_f32 = y_dt == PTDIT_F32;
+  d.Y2 = Y2;
   d.M = M; d.N = N; d.K = K;
   d.head_major = head_major; d.Ntok = Ntok; d.heads = heads;
   d.dh = heads > 0 ? D / heads : 0; d.D = D;
@@ -102,10 +111,10 @@ const void* offset_elems(const void* p, int64_t elems, ptdit_dtype dt) {
 }
 
 // Window / shifted-window attention shared by both ABI calls.
-ptdit_status window_common(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
-                           ptdit_win3 shift, const ptdit_attn_w* w, int32_t add_residual,
-                           void* out, ptdit_dtype out_dt, void* ws, size_t ws_bytes,
-                           ptdit_dtype prec, hipStream_t stream) {
+ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
+                           ptdit_win3 win, ptdit_win3 shift, const ptdit_attn_w* w,
+                           int32_t add_residual, void* out, void* out_lowp, ptdit_dtype out_dt,
+                           void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
   ptdit_status st = check_grid(g);
   if (st) return st;
   if ((st = check_io_dtypes(prec, x_dt, out_dt))) return st;
@@ -120,17 +129,22 @@ ptdit_status window_common(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_
   if (rows == 0) return PTDIT_OK;
   if (!x || !out) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  if ((st = check_lowp(prec, x_lowp, x_dt)) || (st = check_lowp(prec, out_lowp, out_dt))) return st;
   const size_t need = ptdit_workspace_bytes(PTDIT_OP_WINDOW_SA, g, 0, win, prec);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
-  const size_t xb = rows * g.D * esize(x_dt), ob = rows * g.D * esize(out_dt);
-  if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need)) return PTDIT_ERR_ALIAS;
+  const size_t xb = rows * g.D * esize(x_dt), ob = rows * g.D * esize(out_dt), lb = rows * g.D * 2;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need) || overlaps(out, ob, x_lowp, lb) ||
+      overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, x_lowp, lb) ||
+      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need))
+    return PTDIT_ERR_ALIAS;
 
   const int D = g.D;
   char* wsp = (char*)ws;
   void* qkv = wsp;
   void* o = wsp + align_up((size_t)rows * 3 * D * esize(prec));
-  hipError_t e = gemm(prec, x, x_dt, rows, D, 3 * D, w->w_qkv, w->b_qkv, nullptr, prec, qkv, prec,
-                      true, N, g.heads, D, PTDIT_K_GEMM_QKV, stream);
+  // the projection reads bf16(x); x_lowp, when given, already holds it
+  hipError_t e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, 3 * D, w->w_qkv,
+                      w->b_qkv, nullptr, prec, qkv, prec, true, N, g.heads, D, PTDIT_K_GEMM_QKV, stream);
   if (e != hipSuccess) return PTDIT_ERR_HIP;
   WindowDesc wd;
   wd.QKV = qkv; wd.bias_qkv = w->b_qkv; wd.O = o;
@@ -147,7 +161,7 @@ ptdit_status window_common(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_
   }
   if (e != hipSuccess) return PTDIT_ERR_HIP;
   e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
-           false, N, g.heads, D, PTDIT_K_GEMM_OUT, stream);
+           false, N, g.heads, D, PTDIT_K_GEMM_OUT, stream, out_lowp);
   return hip_status(e);
 }
 
@@ -282,7 +296,7 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
 ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
                                const void* proxies, ptdit_dtype p_dt, int32_t M,
                                const ptdit_attn_w* w, int32_t add_residual,
-                               void* out, ptdit_dtype out_dt,
+                               void* out, void* out_lowp, ptdit_dtype out_dt,
                                void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
   ptdit_status st = check_grid(g);
   if (st) return st;
@@ -295,11 +309,14 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
   if (M <= 0) return PTDIT_ERR_SHAPE;  // softmax over an empty key set is undefined
   if (!x || !proxies || !out) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(proxies) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  if ((st = check_lowp(prec, out_lowp, out_dt))) return st;
   const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_XATTN, g, M, ptdit_win3{1, 1, 1}, prec);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
-  const size_t ob = rows * g.D * esize(out_dt);
-  if (overlaps(out, ob, x, rows * g.D * esize(x_dt)) ||
-      overlaps(out, ob, proxies, (size_t)g.B * M * g.D * esize(p_dt)) || overlaps(out, ob, ws, need))
+  const size_t ob = rows * g.D * esize(out_dt), lb = rows * g.D * 2;
+  const size_t xb = rows * g.D * esize(x_dt), pb = (size_t)g.B * M * g.D * esize(p_dt);
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, proxies, pb) || overlaps(out, ob, ws, need) ||
+      overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, proxies, pb) ||
+      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need))
     return PTDIT_ERR_ALIAS;
 
   const int D = g.D, heads = g.heads, dh = D / heads;
@@ -330,26 +347,26 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
   }
   if (e != hipSuccess) return PTDIT_ERR_HIP;
   e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
-           false, N, heads, D, PTDIT_K_GEMM_OUT, stream);
+           false, N, heads, D, PTDIT_K_GEMM_OUT, stream, out_lowp);
   return hip_status(e);
 }
 
-ptdit_status ptdit_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
-                             const ptdit_attn_w* w, int32_t add_residual,
-                             void* out, ptdit_dtype out_dt,
+ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
+                             ptdit_win3 win, const ptdit_attn_w* w, int32_t add_residual,
+                             void* out, void* out_lowp, ptdit_dtype out_dt,
                              void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
-  return window_common(x, x_dt, g, win, ptdit_win3{0, 0, 0}, w, add_residual, out, out_dt, ws,
-                       ws_bytes, prec, stream);
+  return window_common(x, x_lowp, x_dt, g, win, ptdit_win3{0, 0, 0}, w, add_residual, out, out_lowp,
+                       out_dt, ws, ws_bytes, prec, stream);
 }
 
-ptdit_status ptdit_shift_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g,
-                                   ptdit_win3 win, ptdit_win3 shift,
+ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt,
+                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift,
                                    const ptdit_attn_w* w, int32_t add_residual,
-                                   void* out, ptdit_dtype out_dt,
+                                   void* out, void* out_lowp, ptdit_dtype out_dt,
                                    void* ws, size_t ws_bytes, ptdit_dtype prec,
                                    hipStream_t stream) {
-  return window_common(x, x_dt, g, win, shift, w, add_residual, out, out_dt, ws, ws_bytes, prec,
-                       stream);
+  return window_common(x, x_lowp, x_dt, g, win, shift, w, add_residual, out, out_lowp, out_dt, ws,
+                       ws_bytes, prec, stream);
 }
 
 ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,

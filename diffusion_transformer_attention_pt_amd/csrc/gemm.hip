@@ -25,6 +25,7 @@ struct GemmParams {
   const uint16_t* bias;
   const void* R;
   void* Y;
+  uint16_t* Y2;  // optional bf16 copy of an fp32 token-major Y (same rounding as A operands)
   int64_t M;
   int N, K;
   int64_t Ntok;
@@ -213,6 +214,8 @@ gemm_bf16_kernel(GemmParams p) {
           v0 += r.x; v1 += r.y; v2 += r.z; v3 += r.w;
         }
         store4(Y + off, v0, v1, v2, v3);
+        if constexpr (sizeof(TY) == 4)
+          if (p.Y2) store4(p.Y2 + off, v0, v1, v2, v3);
       }
     }
   }
@@ -362,32 +365,37 @@ gemm_dma_kernel(GemmParams p) {
   // fewer than MAXI real instructions repeats its first one (same source,
   // same LDS bytes), so every wave issues exactly MAXI per slice: the loop
   // then has no wave-dependent branch and the vmcnt target is a constant.
+  // Addresses are a wave-uniform base (the tile's first A row or W row, in
+  // SGPRs) plus a 32-bit per-lane byte offset, so the DMA takes the
+  // saddr + voffset form and each instruction costs one VGPR.
   const TA* A = reinterpret_cast<const TA*>(p.A);
-  const char* src[MAXI];
-  int dst[MAXI], stride[MAXI];
+  const char* const a_base = reinterpret_cast<const char*>(A + m0 * K);
+  const char* const w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * K);
+  bool is_a[MAXI];
+  uint32_t voff[MAXI];
+  int dst[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int j0 = wave + i * NW;
     const int j = j0 < IT ? j0 : wave;
+    is_a[i] = j < IA;
     if (j < IA) {
       const int sl = j * 64 + lane, row = sl / CA, pp = sl % CA;
-      int64_t gm = m0 + row;
-      gm = gm < p.M ? gm : p.M - 1;
-      src[i] = reinterpret_cast<const char*>(A + gm * K + DmaA<TA>::chunk(row, pp) * (16 / sizeof(TA)));
+      const int r = m0 + row < p.M ? row : (int)(p.M - 1 - m0);
+      voff[i] = (uint32_t)(((int64_t)r * K + DmaA<TA>::chunk(row, pp) * (16 / (int)sizeof(TA))) * (int)sizeof(TA));
       dst[i] = j * 64;
-      stride[i] = 32 * (int)sizeof(TA);
     } else {
       const int sl = (j - IA) * 64 + lane, row = sl / 4, pp = sl % 4;
-      int gn = n0 + row;
-      gn = gn < p.N ? gn : p.N - 1;
-      src[i] = reinterpret_cast<const char*>(p.W + (int64_t)gn * K + (pp ^ ((row >> 1) & 3)) * 8);
+      const int r = n0 + row < p.N ? row : p.N - 1 - n0;
+      voff[i] = (uint32_t)(((int64_t)r * K + (pp ^ ((row >> 1) & 3)) * 8) * 2);
       dst[i] = SA + (j - IA) * 64;
-      stride[i] = 64;
     }
   }
   auto issue = [&](int kt, uint4* st) {
+    const char* const ak = a_base + kt * (32 * (int)sizeof(TA));
+    const char* const wk = w_base + kt * 64;
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16(src[i] + kt * stride[i], st + dst[i]);
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
   };
 
   floatx4 acc[FN][FM];
@@ -536,13 +544,16 @@ gemm_dma_kernel(GemmParams p) {
             *reinterpret_cast<uint4*>(Y + b * bstride + colpart[i] + tok * p.dh) = v;
           } else {
             const int64_t off = (m0 + rr) * p.N + colpart[i];
-            if (R) {
-              if constexpr (sizeof(TY) == 4) {
+            if constexpr (sizeof(TY) == 4) {
+              float4 o = __builtin_bit_cast(float4, v);
+              if (R) {
                 const float4 r = load4f(R + off);
-                float4 o = __builtin_bit_cast(float4, v);
                 o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
-                *reinterpret_cast<float4*>(Y + off) = o;
-              } else {
+              }
+              *reinterpret_cast<float4*>(Y + off) = o;
+              if (p.Y2) store4(p.Y2 + off, o.x, o.y, o.z, o.w);
+            } else if (R) {
+              {
                 float f[8], rv[8];
                 unpack8(v, f);
                 const float4 r0 = load4f(R + off), r1 = load4f(R + off + 4);
@@ -682,6 +693,10 @@ static hipError_t run_dma(const GemmParams& p, hipStream_t s) {
 template <typename TA, typename TR, typename TY, bool HM>
 static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
+  // the DMA kernels address a tile's A / W rows with 32-bit byte offsets
+  const bool off32 = (int64_t)288 * p.K * (int64_t)sizeof(TA) < (int64_t)1 << 31;
+  if (!off32) return p.M >= 1024 ? run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s)
+                                 : run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
   if (p.M >= 2048 && p.K % 32 == 0 && p.K / 32 >= STAGES)
     return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
   // few rows (proxies): latency-bound, so a small tile with 7 k-slices in flight
@@ -705,6 +720,7 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.bias = reinterpret_cast<const uint16_t*>(d.bias);
   p.R = d.R;
   p.Y = d.Y;
+  p.Y2 = reinterpret_cast<uint16_t*>(d.Y2);
   p.M = d.M; p.N = d.N; p.K = d.K;
   p.Ntok = d.Ntok > 0 ? d.Ntok : 1;
   p.heads = d.heads; p.dh = d.dh; p.D = d.D;

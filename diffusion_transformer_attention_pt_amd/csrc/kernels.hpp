@@ -15,6 +15,7 @@ struct GemmDesc {
   const void* W; const void* bias;
   const void* R; int r_f32;
   void* Y; int y_f32;
+  void* Y2;  // optional bf16 copy of Y (token-major fp32 Y only), else nullptr
   int64_t M; int N; int K;
   int head_major; int64_t Ntok; int heads; int dh; int D;
 };

@@ -39,6 +39,18 @@
  *            never allocates device memory, never synchronises the stream
  *            and keeps no state between calls except the optional kernel
  *            trace (ptdit_trace_*). out must not alias x or the workspace.
+ *  Low-precision copies (optional, PTDIT_BF16 precision only).
+ *            out_lowp: a [B][N][D] bf16 buffer that receives bf16(out),
+ *            rounded to nearest even, written by the same epilogue that
+ *            writes an fp32 out. x_lowp: a [B][N][D] bf16 buffer that holds
+ *            bf16(x) of an fp32 x (for example a previous call's out_lowp);
+ *            the Q/K/V projection then reads it instead of rounding x
+ *            itself, which gives bit-identical results, while the residual
+ *            still adds the fp32 x. The library does not verify that x_lowp
+ *            matches x. Either may be NULL. Given with bf16 precision
+ *            beside a bf16 tensor, or with PTDIT_F32 precision, they are
+ *            rejected with PTDIT_ERR_DTYPE; they must not overlap any other
+ *            argument (PTDIT_ERR_ALIAS).
  *  Streams.  All work is enqueued asynchronously on `stream` (0 = default).
  *  Errors.   Every argument is checked on the host before any launch; on a
  *            failed check nothing is launched, outputs are untouched and a
@@ -140,12 +152,12 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
  * linear_1_visual): every token is a query, the M attended proxies are keys
  * and values:  out = MHA(x, P') (+ x when add_residual != 0).
  *   x        [B][N][D], dtype x_dt;  proxies [B][M][D], dtype p_dt
- *   out      [B][N][D], dtype out_dt
+ *   out      [B][N][D], dtype out_dt;  out_lowp: optional bf16 copy of out
  */
 ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
                                const void* proxies, ptdit_dtype p_dt, int32_t M,
                                const ptdit_attn_w* w, int32_t add_residual,
-                               void* out, ptdit_dtype out_dt,
+                               void* out, void* out_lowp, ptdit_dtype out_dt,
                                void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
 
 /*
@@ -154,12 +166,12 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
  * being zero-padded at the high end of every axis to a multiple of the window
  * (pad tokens are zero vectors, so their keys/values are the biases; their
  * outputs are dropped):  out = WSA(x) (+ x when add_residual != 0).
- *   x, out   [B][N][D]
+ *   x, out   [B][N][D];  x_lowp, out_lowp: optional bf16 copies (see above)
  * Requires a window of at most 128 tokens, a multiple of 16.
  */
-ptdit_status ptdit_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 win,
-                             const ptdit_attn_w* w, int32_t add_residual,
-                             void* out, ptdit_dtype out_dt,
+ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
+                             ptdit_win3 win, const ptdit_attn_w* w, int32_t add_residual,
+                             void* out, void* out_lowp, ptdit_dtype out_dt,
                              void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
 
 /*
@@ -173,10 +185,10 @@ ptdit_status ptdit_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdi
  * the kernels address tokens through it.
  *   out = SWSA(x) (+ x when add_residual != 0); 0 <= shift < win per axis.
  */
-ptdit_status ptdit_shift_window_sa(const void* x, ptdit_dtype x_dt, ptdit_grid g,
-                                   ptdit_win3 win, ptdit_win3 shift,
+ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt,
+                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift,
                                    const ptdit_attn_w* w, int32_t add_residual,
-                                   void* out, ptdit_dtype out_dt,
+                                   void* out, void* out_lowp, ptdit_dtype out_dt,
                                    void* ws, size_t ws_bytes, ptdit_dtype prec,
                                    hipStream_t stream);
 

@@ -73,23 +73,44 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.ptdit_proxy_pool(fake, 0, Grid(1, 1, 16, 16, 1150, 16), Win3(1, 2, 2), fake, 0, None) == -2
     w = AttnW(fake.value, None, fake.value, None)
     # window: head width without kernels, shift >= window, too-large window
-    assert lib.ptdit_window_sa(fake, 0, Grid(1, 1, 16, 16, 1152, 12), Win3(1, 8, 8), ctypes.byref(w), 1,
-                               fake, 0, fake, 1 << 30, 0, None) == -2
-    assert lib.ptdit_shift_window_sa(fake, 0, g, Win3(1, 8, 8), Win3(0, 8, 4), ctypes.byref(w), 1,
-                                     fake, 0, fake, 1 << 30, 0, None) == -2
-    assert lib.ptdit_window_sa(fake, 0, g, Win3(2, 8, 9), ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 0,
-                               None) == -2
+    assert lib.ptdit_window_sa(fake, None, 0, Grid(1, 1, 16, 16, 1152, 12), Win3(1, 8, 8), ctypes.byref(w),
+                               1, fake, None, 0, fake, 1 << 30, 0, None) == -2
+    assert lib.ptdit_shift_window_sa(fake, None, 0, g, Win3(1, 8, 8), Win3(0, 8, 4), ctypes.byref(w), 1,
+                                     fake, None, 0, fake, 1 << 30, 0, None) == -2
+    assert lib.ptdit_window_sa(fake, None, 0, g, Win3(2, 8, 9), ctypes.byref(w), 1, fake, None, 0, fake,
+                               1 << 30, 0, None) == -2
     # window: workspace too small
-    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, ctypes.c_void_p(1 << 40), 0,
+    far = ctypes.c_void_p(1 << 40)
+    assert lib.ptdit_window_sa(fake, None, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, far, None, 0,
                                fake, 16, 0, None) == -6
     # window: output aliases the input
-    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, 0,
-                               ctypes.c_void_p(1 << 40), 1 << 30, 0, None) == -8
+    assert lib.ptdit_window_sa(fake, None, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, None, 0,
+                               far, 1 << 30, 0, None) == -8
     # fp32 precision with bf16 activations
-    assert lib.ptdit_window_sa(fake, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 1,
-                               None) == -4
+    assert lib.ptdit_window_sa(fake, None, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, fake, None, 0, fake,
+                               1 << 30, 1, None) == -4
+    # bf16 copies: only beside fp32 tensors, only with bf16 precision, aligned, not aliased
+    x32, o32 = ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42)
+    lo, ws = ctypes.c_void_p(1 << 43), ctypes.c_void_p(1 << 44)
+    ok_args = dict(x=x32, xl=lo, xdt=1, out=o32, ol=None, odt=1, prec=0)
+
+    def win(**kw):
+        a = {**ok_args, **kw}
+        return lib.ptdit_window_sa(a["x"], a["xl"], a["xdt"], g, Win3(1, 8, 8), ctypes.byref(w), 1, a["out"],
+                                   a["ol"], a["odt"], ws, 1 << 30, a["prec"], None)
+    assert win(xdt=0) == -4                                   # x_lowp beside a bf16 x
+    assert win(xl=None, ol=lo, odt=0) == -4                   # out_lowp beside a bf16 out
+    assert win(xl=None, ol=lo, prec=1) == -4                  # fp32 precision
+    assert win(xl=ctypes.c_void_p((1 << 43) + 8)) == -5       # misaligned
+    assert win(xl=None, ol=ctypes.c_void_p((1 << 41) + 4096)) == -8   # out_lowp inside x
+    assert win(ol=lo) == -8                                   # out_lowp is x_lowp
+    assert win(xl=ctypes.c_void_p((1 << 42) + 4096)) == -8    # out inside x_lowp's range
+    assert lib.ptdit_proxy_xattn(x32, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, ctypes.c_void_p(1 << 44),
+                                 1, ctypes.c_void_p(1 << 44), 1 << 30, 0, None) == -8  # out_lowp is the ws
+    assert lib.ptdit_proxy_xattn(x32, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, lo, 0, ws, 1 << 30, 0,
+                                 None) == -4                 # out_lowp beside a bf16 out
     # cross-attention with no proxies
-    assert lib.ptdit_proxy_xattn(fake, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, 0, fake, 1 << 30, 0,
+    assert lib.ptdit_proxy_xattn(fake, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, None, 0, fake, 1 << 30, 0,
                                  None) == -2
     # null weights
     assert lib.ptdit_proxy_sa(fake, 0, 1, 256, 1152, 16, None, 1, fake, 0, fake, 1 << 30, 0, None) == -1
@@ -97,8 +118,8 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.ptdit_linear(fake, 0, 10, 12, 16, fake, None, None, 0, fake, 0, 0, None) == -2
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
-    assert lib.ptdit_window_sa(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w), 1,
-                               None, 0, None, 0, 0, None) == 0
+    assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),
+                               1, None, None, 0, None, 0, 0, None) == 0
     assert lib.ptdit_linear(None, 0, 0, 16, 16, None, None, None, 0, None, 0, 0, None) == 0
 
 

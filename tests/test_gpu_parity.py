@@ -162,6 +162,41 @@ def test_calls_vs_oracle(P, name, residual):
     assert_close(host(got), ref, "shift_window_sa")
 
 
+LOWP_CASES = ["bf16_ragged", "bf16_video_pad", "bf16_dma_ragged", "bf16_dma_video"]
+
+
+@pytest.mark.parametrize("name", LOWP_CASES)
+def test_lowp_copies(P, name):
+    """out_lowp holds bf16(out) bit for bit (round to nearest even, as torch
+    casts); passing x_lowp = bf16(x) beside an fp32 x changes no output bit;
+    asking for out_lowp changes no bit of out."""
+    wl = CALL_CASES[name]
+    announce(f"lowp copies {name} grid={wl.grid} win={wl.win} shift={wl.shift}")
+    x = dev(make_x(wl, seed=250 + wl.index), F32) * 3.0   # an fp32 residual-stream input
+    xl = x.to(BF16)
+    aw = [P.AttnWeights.from_dict(_weights(wl, a), BF16, "cuda") for a in range(4)]
+    Pd = dev(round_bf16(O.proxy_pool(host(x).astype(np.float64), wl.grid, wl.p).astype(np.float32)), BF16)
+    g = _grid(wl)
+
+    def check(plain, out, out_lowp, what):
+        torch.cuda.synchronize()
+        assert torch.equal(plain, out), f"{what}: out changed"
+        assert torch.equal(out_lowp.view(torch.int16), out.to(BF16).view(torch.int16)), f"{what}: out_lowp"
+
+    plain = P.proxy_xattn(x, g, Pd, aw[1], out_dtype=F32)
+    ol = torch.full(x.shape, 7.0, dtype=BF16, device="cuda")
+    out = P.proxy_xattn(x, g, Pd, aw[1], out_dtype=F32, out_lowp=ol)
+    check(plain, out, ol, "proxy_xattn")
+    plain = P.window_sa(x, g, wl.win, aw[2], out_dtype=F32)
+    ol = torch.full(x.shape, 7.0, dtype=BF16, device="cuda")
+    out = P.window_sa(x, g, wl.win, aw[2], out_dtype=F32, x_lowp=xl, out_lowp=ol)
+    check(plain, out, ol, "window_sa")
+    plain = P.shift_window_sa(x, g, wl.win, wl.shift, aw[3], out_dtype=F32)
+    ol = torch.full(x.shape, 7.0, dtype=BF16, device="cuda")
+    out = P.shift_window_sa(x, g, wl.win, wl.shift, aw[3], out_dtype=F32, x_lowp=xl, out_lowp=ol)
+    check(plain, out, ol, "shift_window_sa")
+
+
 def test_peaked_softmax(P):
     """Sharper softmax than the workloads, outputs in fp32.
 
@@ -247,8 +282,9 @@ def test_error_paths_leave_outputs_untouched(P):
     from diffusion_transformer_attention_pt_amd import _lib
     tiny_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     cw = aw.c()
-    st = P.load().ptdit_window_sa(x.data_ptr(), 0, _lib.Grid(*_grid(wl)), _lib.Win3(*wl.win), ctypes.byref(cw),
-                                  1, o2.data_ptr(), 1, tiny_ws.data_ptr(), 16, 0, _lib._stream())
+    st = P.load().ptdit_window_sa(x.data_ptr(), None, 0, _lib.Grid(*_grid(wl)), _lib.Win3(*wl.win),
+                                  ctypes.byref(cw), 1, o2.data_ptr(), None, 1, tiny_ws.data_ptr(), 16, 0,
+                                  _lib._stream())
     assert st == -6
     torch.cuda.synchronize()
     assert torch.all(o2 == 3.0)
@@ -283,6 +319,9 @@ def test_block_vs_oracle(P, name):
         assert_close(host(inter[k]), ref[k], f"{name}.{k}")
     # the sum of the four branches alone (input removed) must also meet the bar
     assert_close(host(inter["x3"]) - x, ref["x3"] - x, f"{name}.branches")
+    if prec == BF16:   # the bf16 copies the next projection reads
+        assert torch.equal(blk.x1_lowp.view(torch.int16), inter["x1"].to(BF16).view(torch.int16))
+        assert torch.equal(blk.x2_lowp.view(torch.int16), inter["x2"].to(BF16).view(torch.int16))
     # a second forward on the same buffers gives identical bits
     first = inter["x3"].clone()
     blk.forward(xd)
