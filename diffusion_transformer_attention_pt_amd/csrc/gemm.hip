@@ -298,6 +298,204 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Per-wave DMA plan of one k-slice of a BM x BN tile: instruction j moves 64
+// 16-byte chunks (A rows for j < IA, W rows after); wave w owns j = w + i*NW.
+// A wave with fewer than MAXI real instructions repeats its first one (same
+// source, same LDS bytes), so every wave issues exactly MAXI per slice: the
+// loops then have no wave-dependent branch and vmcnt targets are constants.
+// Addresses are a wave-uniform base (the tile's first A or W row, in SGPRs)
+// plus a 32-bit per-lane byte offset, so the DMA takes the saddr + voffset
+// form and each instruction holds one VGPR.
+template <typename TA, int BM, int BN, int NW>
+struct DmaPlan {
+  static constexpr int CA = DmaA<TA>::CPR;
+  static constexpr int SA = BM * CA, SB = BN * 4;   // 16-byte slots per stage
+  static constexpr int IA = SA / 64, IB = SB / 64, IT = IA + IB;
+  static constexpr int MAXI = (IT + NW - 1) / NW;  // per wave, upper bound
+  static_assert(SA % 64 == 0 && SB % 64 == 0, "stage must be whole DMA instructions");
+
+  const char* a_base;
+  const char* w_base;
+  bool is_a[MAXI];
+  uint32_t voff[MAXI];
+  int dst[MAXI];
+
+  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
+    const int K = p.K;
+    a_base = reinterpret_cast<const char*>(reinterpret_cast<const TA*>(p.A) + m0 * K);
+    w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * K);
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j0 = wave + i * NW;
+      const int j = j0 < IT ? j0 : wave;
+      is_a[i] = j < IA;
+      if (j < IA) {
+        const int sl = j * 64 + lane, row = sl / CA, pp = sl % CA;
+        const int r = m0 + row < p.M ? row : (int)(p.M - 1 - m0);
+        voff[i] = (uint32_t)(((int64_t)r * K + DmaA<TA>::chunk(row, pp) * (16 / (int)sizeof(TA))) *
+                             (int)sizeof(TA));
+        dst[i] = j * 64;
+      } else {
+        const int sl = (j - IA) * 64 + lane, row = sl / 4, pp = sl % 4;
+        const int r = n0 + row < p.N ? row : p.N - 1 - n0;
+        voff[i] = (uint32_t)(((int64_t)r * K + (pp ^ ((row >> 1) & 3)) * 8) * 2);
+        dst[i] = SA + (j - IA) * 64;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint4* st) const {
+    const char* const ak = a_base + kt * (32 * (int)sizeof(TA));
+    const char* const wk = w_base + kt * 64;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
+  }
+};
+
+// Epilogue staging through the ring: band j = tile rows {wm*TM + j*16 + r},
+// i.e. WM*16 rows x BN columns, row pitch padded by 16 bytes. A bf16 band
+// fills one ring slot, an fp32 band two, so BPP = STAGES (bf16) or STAGES/2
+// (fp32) bands are staged per pass.
+template <typename TY, int BN, int WM, int STAGES>
+struct EpiShape {
+  static constexpr int PITCH = BN + 16 / (int)sizeof(TY);  // elements
+  static constexpr int ROWS = WM * 16;
+  static constexpr int ROWS_PER_SLOT = sizeof(TY) == 2 ? ROWS : ROWS / 2;
+  static constexpr int SLOT = (ROWS_PER_SLOT * PITCH * (int)sizeof(TY) + 15) / 16;  // uint4
+  static constexpr int BPP = sizeof(TY) == 2 ? STAGES : STAGES / 2;
+  static_assert(BPP >= 1, "fp32 staging spans two slots");
+};
+
+// Epilogue through LDS: lane holds C[m][n .. n+3]; stage 16-row bands (bias
+// added, converted to TY), then write whole 16-byte chunks in row order so a
+// wave's stores cover long contiguous runs (rows of the tile are consecutive
+// tokens; head-major chunks never straddle a head, dh % 8 == 0). The ring
+// must be drained (no DMA in flight, every fragment read retired) on entry.
+template <typename TR, typename TY, int BM, int BN, int WM, int WN, int STAGES, bool HEADMAJOR, class SlotFn>
+__device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4 (&acc)[BN / WN / 16][BM / WM / 16],
+                                              const uint2 (&biasp)[BN / WN / 16], SlotFn&& slot, int tid,
+                                              int lane, int wm, int wn, int64_t m0, int n0) {
+  constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  using ES = EpiShape<TY, BN, WM, STAGES>;
+  constexpr int BPP = ES::BPP;
+  TY* Y = reinterpret_cast<TY*>(p.Y);
+  const TR* R = reinterpret_cast<const TR*>(p.R);
+  constexpr int E = 16 / (int)sizeof(TY);          // elements per 16-byte chunk
+  constexpr int CPRO = BN / E;                     // chunks per staged row
+  const int lr = lane & 15;
+
+  // Store-phase chunk assignment, fixed across bands: chunk q = tid + i*NT of
+  // a band is staged row sr = q / CPRO, chunk cc = q % CPRO (compile-time
+  // divisors). Column-dependent address parts are computed once here; rows
+  // advance by 16 per band, tracked as (batch, token) without division.
+  constexpr int NQ = (ES::ROWS * CPRO + NW * 64 - 1) / (NW * 64);
+  int64_t colpart[NQ];
+  int rowbase[NQ];
+  bool qok[NQ];
+  const int64_t b0 = m0 / p.Ntok;            // one division per thread
+  const int64_t t0 = m0 - b0 * p.Ntok;
+  const int G = p.N / p.D;
+  const int64_t bstride = (int64_t)G * p.heads * p.Ntok * p.dh;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = tid + i * NW * 64;
+    const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
+    const int n = n0 + cc * E;
+    qok[i] = q < ES::ROWS * CPRO && n < p.N;
+    rowbase[i] = (sr / 16) * TM + (sr % 16);
+    if constexpr (HEADMAJOR) {
+      const int gg = n / p.D, hn = n - gg * p.D;
+      const int h = hn / p.dh, d = hn - h * p.dh;
+      colpart[i] = ((int64_t)(gg * p.heads + h) * p.Ntok) * p.dh + d;
+    } else {
+      colpart[i] = n;
+    }
+  }
+
+  // band j lives in slot (j % BPP) [bf16] or slots 2*(j % BPP), 2*(j % BPP)+1 [fp32]
+  auto band_base = [&](auto jI, int sr) -> TY* {
+    constexpr int jj = decltype(jI)::value % BPP;
+    if constexpr (sizeof(TY) == 2) {
+      return reinterpret_cast<TY*>(slot(std::integral_constant<int, jj>{}));
+    } else {
+      return sr < ES::ROWS_PER_SLOT ? reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj>{}))
+                                    : reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj + 1>{}));
+    }
+  };
+  static_for<0, (FM + BPP - 1) / BPP>([&](auto passI) {
+    constexpr int pass = decltype(passI)::value;
+    // stage bands pass*BPP .. pass*BPP+BPP-1
+    static_for<0, BPP>([&](auto kI) {
+      constexpr int jb = pass * BPP + decltype(kI)::value;
+      if constexpr (jb < FM) {
+        const int sr = wm * 16 + lr;
+        TY* base = band_base(std::integral_constant<int, jb>{}, sr);
+        const int lrow = sr % ES::ROWS_PER_SLOT;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int c = wn * TN + i * 16 + 4 * (lane >> 4);
+          store4(base + lrow * ES::PITCH + c, acc[i][jb][0] + __uint_as_float(biasp[i].x << 16),
+                 acc[i][jb][1] + __uint_as_float(biasp[i].x & 0xffff0000u),
+                 acc[i][jb][2] + __uint_as_float(biasp[i].y << 16),
+                 acc[i][jb][3] + __uint_as_float(biasp[i].y & 0xffff0000u));
+        }
+      }
+    });
+    ring_barrier();
+    static_for<0, BPP>([&](auto kI) {
+      constexpr int jb = pass * BPP + decltype(kI)::value;
+      if constexpr (jb < FM) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const int q = tid + i * NW * 64;
+          const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
+          const int rr = rowbase[i] + jb * 16;
+          if (!qok[i] || m0 + rr >= p.M) continue;
+          const TY* sb = band_base(std::integral_constant<int, jb>{}, sr);
+          const uint4 v = *reinterpret_cast<const uint4*>(sb + (sr % ES::ROWS_PER_SLOT) * ES::PITCH + cc * E);
+          if constexpr (HEADMAJOR) {
+            int64_t tok = t0 + rr, b = b0;
+            while (tok >= p.Ntok) { tok -= p.Ntok; ++b; }
+            *reinterpret_cast<uint4*>(Y + b * bstride + colpart[i] + tok * p.dh) = v;
+          } else {
+            const int64_t off = (m0 + rr) * p.N + colpart[i];
+            if constexpr (sizeof(TY) == 4) {
+              float4 o = __builtin_bit_cast(float4, v);
+              if (R) {
+                const float4 r = load4f(R + off);
+                o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+              }
+              *reinterpret_cast<float4*>(Y + off) = o;
+              if (p.Y2) store4(p.Y2 + off, o.x, o.y, o.z, o.w);
+            } else if (R) {
+              float f[8], rv[8];
+              unpack8(v, f);
+              const float4 r0 = load4f(R + off), r1 = load4f(R + off + 4);
+              rv[0] = r0.x; rv[1] = r0.y; rv[2] = r0.z; rv[3] = r0.w;
+              rv[4] = r1.x; rv[5] = r1.y; rv[6] = r1.z; rv[7] = r1.w;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) f[e] += rv[e];
+              *reinterpret_cast<uint4*>(Y + off) = pack8(f);
+            } else {
+              *reinterpret_cast<uint4*>(Y + off) = v;
+            }
+          }
+        }
+      }
+    });
+    if constexpr (pass + 1 < (FM + BPP - 1) / BPP) ring_barrier();  // staging reused by the next pass
+  });
+}
+
+// bias of this lane's output columns (4 bf16 per 16-column tile), kept packed
+template <int FN>
+__device__ __forceinline__ void load_bias(const GemmParams& p, int ncol0, int lane, uint2 (&biasp)[FN]) {
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int n = ncol0 + i * 16 + 4 * (lane >> 4);
+    biasp[i] = (p.bias && n < p.N) ? *reinterpret_cast<const uint2*>(p.bias + n) : uint2{0u, 0u};
+  }
+}
+
 // Each ring slot is its own __shared__ array and every slot index is a
 // compile-time constant: the compiler's wait insertion then knows that
 // fragment reads of slot s cannot alias the DMA in flight into other slots,
@@ -308,26 +506,12 @@ gemm_dma_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int CA = DmaA<TA>::CPR;
-  constexpr int SA = BM * CA, SB = BN * 4;      // 16-byte slots per stage
-  constexpr int IA = SA / 64, IB = SB / 64;     // DMA instructions per stage
-  constexpr int IT = IA + IB;
-  constexpr int MAXI = (IT + NW - 1) / NW;      // per wave, upper bound
-  static_assert(SA % 64 == 0 && SB % 64 == 0, "stage must be whole DMA instructions");
+  using DP = DmaPlan<TA, BM, BN, NW>;
+  using ES = EpiShape<TY, BN, WM, STAGES>;
+  constexpr int SA = DP::SA, MAXI = DP::MAXI;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
-
-  // Epilogue staging: band j = tile rows {wm*TM + j*16 + r}, i.e. WM*16 rows
-  // x BN columns, row pitch padded by 16 bytes. A bf16 band fills one ring
-  // slot, an fp32 band two, so BPP = STAGES (bf16) or STAGES/2 (fp32) bands are
-  // staged per pass.
-  constexpr int EPI_PITCH = BN + 16 / (int)sizeof(TY);           // elements
-  constexpr int EPI_ROWS = WM * 16;
-  constexpr int EPI_ROWS_PER_SLOT = sizeof(TY) == 2 ? EPI_ROWS : EPI_ROWS / 2;
-  constexpr int EPI_SLOT = (EPI_ROWS_PER_SLOT * EPI_PITCH * (int)sizeof(TY) + 15) / 16;  // uint4
-  constexpr int SLOT = (SA + SB) > EPI_SLOT ? (SA + SB) : EPI_SLOT;
-  constexpr int BPP = sizeof(TY) == 2 ? STAGES : STAGES / 2;       // bands per pass
-  static_assert(BPP >= 1, "fp32 staging spans two slots");
+  constexpr int SLOT = (DP::SA + DP::SB) > ES::SLOT ? (DP::SA + DP::SB) : ES::SLOT;
 
   __shared__ uint4 ring0[SLOT];
   __shared__ uint4 ring1[SLOT];
@@ -358,60 +542,18 @@ gemm_dma_kernel(GemmParams p) {
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  const int K = p.K;
-  const int KT = K / 32;
+  const int KT = p.K / 32;
 
-  // This wave's DMA instructions j = wave + i*NW (i < MAXI). A wave with
-  // fewer than MAXI real instructions repeats its first one (same source,
-  // same LDS bytes), so every wave issues exactly MAXI per slice: the loop
-  // then has no wave-dependent branch and the vmcnt target is a constant.
-  // Addresses are a wave-uniform base (the tile's first A row or W row, in
-  // SGPRs) plus a 32-bit per-lane byte offset, so the DMA takes the
-  // saddr + voffset form and each instruction costs one VGPR.
-  const TA* A = reinterpret_cast<const TA*>(p.A);
-  const char* const a_base = reinterpret_cast<const char*>(A + m0 * K);
-  const char* const w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * K);
-  bool is_a[MAXI];
-  uint32_t voff[MAXI];
-  int dst[MAXI];
-#pragma unroll
-  for (int i = 0; i < MAXI; ++i) {
-    const int j0 = wave + i * NW;
-    const int j = j0 < IT ? j0 : wave;
-    is_a[i] = j < IA;
-    if (j < IA) {
-      const int sl = j * 64 + lane, row = sl / CA, pp = sl % CA;
-      const int r = m0 + row < p.M ? row : (int)(p.M - 1 - m0);
-      voff[i] = (uint32_t)(((int64_t)r * K + DmaA<TA>::chunk(row, pp) * (16 / (int)sizeof(TA))) * (int)sizeof(TA));
-      dst[i] = j * 64;
-    } else {
-      const int sl = (j - IA) * 64 + lane, row = sl / 4, pp = sl % 4;
-      const int r = n0 + row < p.N ? row : p.N - 1 - n0;
-      voff[i] = (uint32_t)(((int64_t)r * K + (pp ^ ((row >> 1) & 3)) * 8) * 2);
-      dst[i] = SA + (j - IA) * 64;
-    }
-  }
-  auto issue = [&](int kt, uint4* st) {
-    const char* const ak = a_base + kt * (32 * (int)sizeof(TA));
-    const char* const wk = w_base + kt * 64;
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
-  };
+  DP dma;
+  dma.init(p, m0, n0, wave, lane);
 
   floatx4 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
-
-  // bias of this lane's output columns (4 bf16 per 16-column tile), fetched
-  // early and kept packed; used in the epilogue
-  uint2 biasp[FN];
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
-    biasp[i] = (p.bias && n < p.N) ? *reinterpret_cast<const uint2*>(p.bias + n) : uint2{0u, 0u};
-  }
+  uint2 biasp[FN];  // fetched early, used in the epilogue
+  load_bias<FN>(p, n0 + wn * TN, lane, biasp);
 
   const int g = lane >> 4, lr = lane & 15;
   auto compute = [&](const uint4* st) {
@@ -430,7 +572,7 @@ gemm_dma_kernel(GemmParams p) {
   };
 
   // Prologue: slices 0 .. STAGES-2 in flight (KT >= STAGES-1 is guaranteed by the host).
-  static_for<0, STAGES - 1>([&](auto sI) { issue(decltype(sI)::value, slot(sI)); });
+  static_for<0, STAGES - 1>([&](auto sI) { dma.issue(decltype(sI)::value, slot(sI)); });
 
   // Steady state: every slice kt < NMAIN refills the slot freed by slice
   // kt-1 with slice kt+STAGES-1 (< KT). Branch-free body.
@@ -440,7 +582,7 @@ gemm_dma_kernel(GemmParams p) {
       constexpr int s = decltype(sI)::value;
       wait_vm_lgkm0<(STAGES - 2) * MAXI>();
       ring_barrier();
-      issue(kt0 + s + STAGES - 1, slot(std::integral_constant<int, (s + STAGES - 1) % STAGES>{}));
+      dma.issue(kt0 + s + STAGES - 1, slot(std::integral_constant<int, (s + STAGES - 1) % STAGES>{}));
       compute(slot(sI));
     });
   }
@@ -453,125 +595,136 @@ gemm_dma_kernel(GemmParams p) {
       wait_vm_dyn<(STAGES - 2) * MAXI>(ahead * MAXI);
       ring_barrier();
       if (kt + STAGES - 1 < KT)
-        issue(kt + STAGES - 1, slot(std::integral_constant<int, (t + STAGES - 1) % STAGES>{}));
+        dma.issue(kt + STAGES - 1, slot(std::integral_constant<int, (t + STAGES - 1) % STAGES>{}));
       compute(slot(std::integral_constant<int, t % STAGES>{}));
     }
   });
 
-  // Epilogue through LDS: lane holds C[m][n .. n+3]; stage 16-row bands (bias
-  // added, converted to TY), then write whole 16-byte chunks in row order so a
-  // wave's stores cover long contiguous runs (rows of the tile are
-  // consecutive tokens; head-major chunks never straddle a head, dh % 8 == 0).
   wait_vm_lgkm0<0>();
   ring_barrier();  // ring drained, every fragment read retired
-  TY* Y = reinterpret_cast<TY*>(p.Y);
-  const TR* R = reinterpret_cast<const TR*>(p.R);
-  constexpr int E = 16 / (int)sizeof(TY);          // elements per 16-byte chunk
-  constexpr int CPRO = BN / E;                     // chunks per staged row
+  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(p, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
+}
 
-  // Store-phase chunk assignment, fixed across bands: chunk q = tid + i*NT of
-  // a band is staged row sr = q / CPRO, chunk cc = q % CPRO (compile-time
-  // divisors). Column-dependent address parts are computed once here; rows
-  // advance by 16 per band, tracked as (batch, token) without division.
-  constexpr int NQ = (EPI_ROWS * CPRO + NW * 64 - 1) / (NW * 64);
-  int64_t colpart[NQ];
-  int rowbase[NQ];
-  bool qok[NQ];
-  const int64_t b0 = m0 / p.Ntok;            // one division per thread
-  const int64_t t0 = m0 - b0 * p.Ntok;
-  const int G = p.N / p.D;
-  const int64_t bstride = (int64_t)G * p.heads * p.Ntok * p.dh;
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int q = tid + i * NW * 64;
-    const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
-    const int n = n0 + cc * E;
-    qok[i] = q < EPI_ROWS * CPRO && n < p.N;
-    rowbase[i] = (sr / 16) * TM + (sr % 16);
-    if constexpr (HEADMAJOR) {
-      const int gg = n / p.D, hn = n - gg * p.D;
-      const int h = hn / p.dh, d = hn - h * p.dh;
-      colpart[i] = ((int64_t)(gg * p.heads + h) * p.Ntok) * p.dh + d;
-    } else {
-      colpart[i] = n;
-    }
-  }
-
-  // band j lives in slot (j % BPP) [bf16] or slots 2*(j % BPP), 2*(j % BPP)+1 [fp32]
-  auto band_base = [&](auto jI, int sr) -> TY* {
-    constexpr int jj = decltype(jI)::value % BPP;
-    if constexpr (sizeof(TY) == 2) {
-      return reinterpret_cast<TY*>(slot(std::integral_constant<int, jj>{}));
-    } else {
-      return sr < EPI_ROWS_PER_SLOT ? reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj>{}))
-                                    : reinterpret_cast<TY*>(slot(std::integral_constant<int, 2 * jj + 1>{}));
-    }
+// ----------------------------------------------------------------------------
+// Ping-pong variant for the large token-row projections (bf16 A): the same
+// 256 x 288 tile and 8 waves of 64 x 144 as gemm_dma_kernel, but the waves
+// form two groups (W columns 0..143 and 144..287) that run one phase apart.
+// Each SIMD holds one wave of each group, so while one group's waves run
+// their MFMAs the other group's waves read their LDS fragments (and the LDS
+// sees the reads of four waves at a time instead of eight).
+//
+// Every wave runs the same body for slice k:
+//   refill slot (k-1) % 4 with slice k+3;  read slice k's fragments;
+//   wait for slice k+1;  barrier;  MFMAs of slice k;  wait;  barrier
+// Group 1 executes one extra barrier before its first body, group 0 one
+// after its last, which offsets the groups by one phase. Counting barriers
+// from the prologue's (#0): group 0 reads slice k between #2k and #2k+1,
+// group 1 between #2k+1 and #2k+2. Hence slot k-1 is free for both groups
+// from #2k on (group 0 refills after #2k, group 1 after #2k+1), and slice
+// k+1, waited on by every wave before each barrier of its body k, is whole
+// in LDS by #2k+2. Requires KT % 4 == 0 and KT >= 8.
+// ----------------------------------------------------------------------------
+template <typename TR, typename TY, bool HEADMAJOR>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
+  using TA = uint16_t;
+  constexpr int BM = 256, BN = 288, WM = 4, WN = 2, NW = 8, STAGES = 4;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  using DP = DmaPlan<TA, BM, BN, NW>;
+  using ES = EpiShape<TY, BN, WM, STAGES>;
+  constexpr int SA = DP::SA, MAXI = DP::MAXI;
+  constexpr int SLOT = (DP::SA + DP::SB) > ES::SLOT ? (DP::SA + DP::SB) : ES::SLOT;
+  __shared__ uint4 ring0[SLOT];
+  __shared__ uint4 ring1[SLOT];
+  __shared__ uint4 ring2[SLOT];
+  __shared__ uint4 ring3[SLOT];
+  auto slot = [&](auto sI) -> uint4* {
+    constexpr int sl = (decltype(sI)::value % STAGES + STAGES) % STAGES;
+    if constexpr (sl == 0) return ring0;
+    else if constexpr (sl == 1) return ring1;
+    else if constexpr (sl == 2) return ring2;
+    else return ring3;
   };
-  static_for<0, (FM + BPP - 1) / BPP>([&](auto passI) {
-    constexpr int pass = decltype(passI)::value;
-    // stage bands pass*BPP .. pass*BPP+BPP-1
-    static_for<0, BPP>([&](auto kI) {
-      constexpr int jb = pass * BPP + decltype(kI)::value;
-      if constexpr (jb < FM) {
-        const int sr = wm * 16 + lr;
-        TY* base = band_base(std::integral_constant<int, jb>{}, sr);
-        const int lrow = sr % EPI_ROWS_PER_SLOT;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;  // wn is the group
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (p.N + BN - 1) / BN;
+  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int KT = p.K / 32;
+
+  DP dma;
+  dma.init(p, m0, n0, wave, lane);
+  floatx4 acc[FN][FM];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int c = wn * TN + i * 16 + 4 * (lane >> 4);
-          store4(base + lrow * EPI_PITCH + c, acc[i][jb][0] + __uint_as_float(biasp[i].x << 16),
-                 acc[i][jb][1] + __uint_as_float(biasp[i].x & 0xffff0000u),
-                 acc[i][jb][2] + __uint_as_float(biasp[i].y << 16),
-                 acc[i][jb][3] + __uint_as_float(biasp[i].y & 0xffff0000u));
-        }
-      }
-    });
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
+
+  const int g = lane >> 4, lr = lane & 15;
+  uint4 wf[FN], xf[FM];
+  auto read_frags = [&](const uint4* st) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int row = wn * TN + i * 16 + lr;
+      wf[i] = st[SA + row * 4 + (g ^ ((row >> 1) & 3))];
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, wm * TM + j * 16 + lr, g);
+  };
+  auto mfmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+  };
+  // body of slice k (slot t = k % 4); AHEAD: slices allowed in flight once
+  // slice k+1 has landed
+  auto body = [&](auto tI, auto issueI, auto aheadI, int k) {
+    constexpr int t = decltype(tI)::value, AHEAD = decltype(aheadI)::value;
+    if constexpr (decltype(issueI)::value) dma.issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
+    read_frags(slot(std::integral_constant<int, t>{}));
+    wait_vm_lgkm0<AHEAD * MAXI>();
+    __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
-    static_for<0, BPP>([&](auto kI) {
-      constexpr int jb = pass * BPP + decltype(kI)::value;
-      if constexpr (jb < FM) {
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          const int q = tid + i * NW * 64;
-          const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
-          const int rr = rowbase[i] + jb * 16;
-          if (!qok[i] || m0 + rr >= p.M) continue;
-          const TY* sb = band_base(std::integral_constant<int, jb>{}, sr);
-          const uint4 v = *reinterpret_cast<const uint4*>(sb + (sr % EPI_ROWS_PER_SLOT) * EPI_PITCH + cc * E);
-          if constexpr (HEADMAJOR) {
-            int64_t tok = t0 + rr, b = b0;
-            while (tok >= p.Ntok) { tok -= p.Ntok; ++b; }
-            *reinterpret_cast<uint4*>(Y + b * bstride + colpart[i] + tok * p.dh) = v;
-          } else {
-            const int64_t off = (m0 + rr) * p.N + colpart[i];
-            if constexpr (sizeof(TY) == 4) {
-              float4 o = __builtin_bit_cast(float4, v);
-              if (R) {
-                const float4 r = load4f(R + off);
-                o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
-              }
-              *reinterpret_cast<float4*>(Y + off) = o;
-              if (p.Y2) store4(p.Y2 + off, o.x, o.y, o.z, o.w);
-            } else if (R) {
-              {
-                float f[8], rv[8];
-                unpack8(v, f);
-                const float4 r0 = load4f(R + off), r1 = load4f(R + off + 4);
-                rv[0] = r0.x; rv[1] = r0.y; rv[2] = r0.z; rv[3] = r0.w;
-                rv[4] = r1.x; rv[5] = r1.y; rv[6] = r1.z; rv[7] = r1.w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] += rv[e];
-                *reinterpret_cast<uint4*>(Y + off) = pack8(f);
-              }
-            } else {
-              *reinterpret_cast<uint4*>(Y + off) = v;
-            }
-          }
-        }
-      }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas();
+    wait_vm_lgkm0<AHEAD * MAXI>();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Prologue: slices 0..2 in flight, slice 0 landed (barrier #0); group 1
+  // then takes its extra barrier.
+  static_for<0, 3>([&](auto sI) { dma.issue(decltype(sI)::value, slot(sI)); });
+  wait_vm_lgkm0<2 * MAXI>();
+  ring_barrier();
+  if (wn == 1) ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Steady state: bodies k = 0 .. KT-5 (refill slice k+3 < KT - 1).
+  const int NMAIN = KT - 4;
+  for (int k0 = 0; k0 < NMAIN; k0 += 4) {
+    static_for<0, 4>([&](auto tI) {
+      body(tI, std::true_type{}, std::integral_constant<int, 2>{}, k0 + decltype(tI)::value);
     });
-    if constexpr (pass + 1 < (FM + BPP - 1) / BPP) ring_barrier();  // staging reused by the next pass
-  });
+  }
+  // Tail: bodies KT-4 .. KT-1 (only the first refills, with slice KT-1).
+  body(std::integral_constant<int, 0>{}, std::true_type{}, std::integral_constant<int, 2>{}, NMAIN);
+  body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, 1>{}, NMAIN + 1);
+  body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, 0>{}, NMAIN + 2);
+  body(std::integral_constant<int, 3>{}, std::false_type{}, std::integral_constant<int, 0>{}, NMAIN + 3);
+  if (wn == 0) ring_barrier();
+
+  wait_vm_lgkm0<0>();
+  ring_barrier();
+  uint2 biasp[FN];
+  load_bias<FN>(p, n0 + wn * TN, lane, biasp);
+  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(p, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
 }
 
 // ----------------------------------------------------------------------------
@@ -685,11 +838,22 @@ static hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TR, typename TY, bool HM>
+static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
+  if (p.K % 128 != 0 || p.K < 256) return hipErrorInvalidValue;  // KT % 4 == 0, KT >= 8
+  const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM>), dim3((unsigned)tiles), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
 // Tile choice. Token-row projections (M >= 2048 rows, K a multiple of 32) use
-// the multi-stage DMA kernel with 256x288 tiles: 288 = 4 heads of 72, and
-// D = 1152 = 4 x 288, 3D = 12 x 288, so a 2048^2 image block yields exactly
-// 256 (N = D) or 768 (N = 3D) tiles for 256 CUs. Proxy-row projections and odd
-// shapes use the register-staged kernel.
+// 256x288 tiles: 288 = 4 heads of 72, and D = 1152 = 4 x 288, 3D = 12 x 288,
+// so a 2048^2 image block yields exactly 256 (N = D) or 768 (N = 3D) tiles for
+// 256 CUs. With bf16 A and K % 128 == 0 the ping-pong kernel takes them, else
+// the multi-stage ring kernel. Proxy-row projections (few rows) are latency-
+// bound and take a small tile with a deep ring; odd shapes take the
+// register-staged kernel.
 template <typename TA, typename TR, typename TY, bool HM>
 static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
@@ -697,6 +861,9 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   const bool off32 = (int64_t)288 * p.K * (int64_t)sizeof(TA) < (int64_t)1 << 31;
   if (!off32) return p.M >= 1024 ? run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s)
                                  : run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
+  if constexpr (sizeof(TA) == 2) {
+    if (p.M >= 2048 && p.K % 128 == 0 && p.K >= 256) return run_pp<TR, TY, HM>(p, s);
+  }
   if (p.M >= 2048 && p.K % 32 == 0 && p.K / 32 >= STAGES)
     return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
   // few rows (proxies): latency-bound, so a small tile with 7 k-slices in flight

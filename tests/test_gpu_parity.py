@@ -91,7 +91,10 @@ def test_roll_bit_exact(P, grid, shift, dt):
 
 @pytest.mark.parametrize("rows,din,dout", [(1000, 1152, 3456), (7, 1152, 1152), (4096, 1152, 1152),
                                            (300, 16, 64), (257, 72, 40), (2500, 1152, 3456),
-                                           (3000, 1152, 1000), (1500, 1152, 1152), (2048, 96, 288)])
+                                           (3000, 1152, 1000), (1500, 1152, 1152), (2048, 96, 288),
+                                           # >= 2048 rows: K % 128 != 0 takes the ring kernel (33
+                                           # k-slices), K = 256 the ping-pong kernel's minimum
+                                           (2304, 1056, 1152), (2100, 256, 600)])
 @pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "f32"])
 def test_linear(P, rows, din, dout, mode):
     announce(f"linear {rows}x{din}->{dout} {mode}")
