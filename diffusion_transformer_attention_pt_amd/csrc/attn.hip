@@ -474,20 +474,30 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_wide(FlashParams prm
   }
 }
 
-// ---------------------------------------------------------------- flash core, bf16, K/V resident
+// ---------------------------------------------------------------- flash core, bf16, single pass
 // For up to 256 keys (every image workload: 256 proxies). Workgroup = 8 waves
 // bound to one (batch, head) and a contiguous range of queries: K and V^T of
-// that head are staged in LDS once, then the workgroup walks its range in
-// blocks of 256 queries (32 per wave) with the next block's Q fragments
-// loaded while the current block is computed. No barrier inside the loop.
-constexpr int FR_MAXK = 256;
+// that head are staged in LDS once, then each wave walks 32 queries (two
+// 16-query tiles) at a time. All 256 scores of a query fit in the lane
+// registers (16 key tiles x 4), so the softmax is exact in one pass: one
+// max, then exp2(s * c - m * c) with c = scale * log2(e) folded into an FMA,
+// no running rescale. Keys past Nk are staged as zeros and masked to -inf.
+// Fragment loads run one step ahead of their MFMAs (sched_barrier fences
+// keep the scheduler from hoisting all of them, which would not fit in
+// registers); the next query block's Q fragments load into the current
+// block's Q registers once the scores are done. No barrier inside the loop.
+constexpr int FS_MAXK = 256, FS_KT = FS_MAXK / 16;
 
 template <int DH>
-__global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams prm, int q_per_wg) {
+__global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams prm, int q_per_wg) {
   using P = BF16P<DH>;
   constexpr int NT = FW_WAVES * 64, NKC = P::NKC, NDT = P::NDT, DCH = P::DCH;
-  constexpr int VTP = FR_MAXK + 4;
-  __shared__ uint4 ks[FR_MAXK * DCH];
+  constexpr int VTP = FS_MAXK + 4;
+  // With a padded head (72 -> 80 rows of V^T), row DH of V^T is all ones, so
+  // row DH of O^T = V^T P^T is the softmax denominator: the sum of the very
+  // bf16 probabilities the numerator used, accumulated by the MFMA.
+  constexpr bool ONES_ROW = NDT * 16 > DH;
+  __shared__ uint4 ks[FS_MAXK * DCH];
   __shared__ uint16_t vt[NDT * 16][VTP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -496,7 +506,6 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams
   const uint16_t* Qb = reinterpret_cast<const uint16_t*>(prm.Q) + b * prm.q_bs + h * prm.q_hs;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(prm.K) + b * prm.k_bs + h * prm.k_hs;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(prm.V) + b * prm.v_bs + h * prm.v_hs;
-  const int nkb = (prm.Nk + FW_KB - 1) / FW_KB;     // 64-key blocks
   const int qbeg = blockIdx.x * q_per_wg;
   const int qend = min(prm.Nq, qbeg + q_per_wg);
 
@@ -507,16 +516,16 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams
       qf[t] = P::load_q(q < qend ? Qb + (int64_t)q * DH : nullptr, lane);
     }
   };
-  typename P::QF qf[2], qn[2];
+  typename P::QF qf[2];
   load_qf(qbeg, qf);
 
-  // stage K (chunks) and V^T (four keys per item) of all keys, zero beyond Nk
-  for (int it = tid; it < nkb * FW_KB * DCH; it += NT) {
+  // stage K (chunks) and V^T (four keys per item) of all key slots, zero past Nk
+  for (int it = tid; it < FS_MAXK * DCH; it += NT) {
     const int key = it / DCH, c = it % DCH;
     ks[it] = key < prm.Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
   }
-  for (int it = tid; it < DCH * (nkb * FW_KB / 4); it += NT) {
-    const int c = it / (nkb * FW_KB / 4), kq = it % (nkb * FW_KB / 4);
+  for (int it = tid; it < DCH * (FS_MAXK / 4); it += NT) {
+    const int c = it / (FS_MAXK / 4), kq = it % (FS_MAXK / 4);
     uint4 v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -533,91 +542,115 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams
       *reinterpret_cast<uint2*>(&vt[c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
     }
   }
-  for (int i = tid; i < (NDT * 16 - DH) * VTP; i += NT) vt[DH + i / VTP][i % VTP] = 0;
+  for (int i = tid; i < (NDT * 16 - DH) * VTP; i += NT)
+    vt[DH + i / VTP][i % VTP] = (ONES_ROW && i < VTP) ? (uint16_t)0x3f80u : (uint16_t)0;  // bf16 1.0
   __syncthreads();
 
+  const float c2 = prm.sl2;
+  const bool masked = prm.Nk < FS_MAXK;  // uniform
+  auto load_kf = [&](int kt, uint4* kf) {
+    const int key = kt * 16 + lr;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = kc * 32 + 8 * g;
+      kf[kc] = d < DH ? ks[key * DCH + d / 8] : uint4{0, 0, 0, 0};
+    }
+  };
+  auto load_vf = [&](int u, uint4* vf) {
+    const int kbase = u * 32 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int drow = dt * 16 + lr;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&vt[drow][kbase]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&vt[drow][kbase + 16]);
+      vf[dt] = uint4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+
   for (int qblk = qbeg; qblk < qend; qblk += FW_Q) {
-    if (qblk + FW_Q < qend) load_qf(qblk + FW_Q, qn);
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    // S^T for all 256 key slots of both query tiles
+    floatx4 sc[2][FS_KT];
+    uint4 kf[2][NKC];
+    load_kf(0, kf[0]);
+#pragma unroll
+    for (int kt = 0; kt < FS_KT; ++kt) {
+      if (kt + 1 < FS_KT) load_kf(kt + 1, kf[(kt + 1) & 1]);
+      sc[0][kt] = zero4();
+      sc[1][kt] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        sc[0][kt] = mfma_bf16(kf[kt & 1][kc], qf[0].v[kc], sc[0][kt]);
+        sc[1][kt] = mfma_bf16(kf[kt & 1][kc], qf[1].v[kc], sc[1][kt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (qblk + FW_Q < qend) load_qf(qblk + FW_Q, qf);  // next block; scores no longer need qf
+    if (masked) {
+#pragma unroll
+      for (int kt = 0; kt < FS_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt * 16 + 4 * g + r >= prm.Nk) sc[0][kt][r] = sc[1][kt][r] = -INFINITY;
+    }
+
+    // exact softmax numerators and sums; P^T packed to bf16 right away
+    uint32_t pk[2][FS_KT][2];
+    float lsum[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float mx = sc[t][0][0];
+#pragma unroll
+      for (int kt = 0; kt < FS_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[t][kt][r]);
+      const float nmc = -quad_max(mx) * c2;
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < FS_KT; ++kt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = fast_exp2(fmaf(sc[t][kt][r], c2, nmc));
+          if constexpr (!ONES_ROW) rs += e[r];
+        }
+        pk[t][kt][0] = pack_bf2(e[0], e[1]);
+        pk[t][kt][1] = pack_bf2(e[2], e[3]);
+      }
+      if constexpr (!ONES_ROW) lsum[t] = quad_sum(rs);
+    }
+
+    // O^T = V^T P^T over key-tile pairs
     floatx4 o[2][NDT];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < NDT; ++i) o[t][i] = zero4();
-
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int k0 = kb * FW_KB;
-      floatx4 sc[2][4];
+    uint4 vf[2][NDT];
+    load_vf(0, vf[0]);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sc[0][kt] = zero4();
-        sc[1][kt] = zero4();
-        const int key = k0 + kt * 16 + lr;
+    for (int u = 0; u < FS_KT / 2; ++u) {
+      if (u + 1 < FS_KT / 2) load_vf(u + 1, vf[(u + 1) & 1]);
+      const uint4 pf0 = uint4{pk[0][2 * u][0], pk[0][2 * u][1], pk[0][2 * u + 1][0], pk[0][2 * u + 1][1]};
+      const uint4 pf1 = uint4{pk[1][2 * u][0], pk[1][2 * u][1], pk[1][2 * u + 1][0], pk[1][2 * u + 1][1]};
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const int d = kc * 32 + 8 * g;
-          const uint4 kf = d < DH ? ks[key * DCH + d / 8] : uint4{0, 0, 0, 0};
-          sc[0][kt] = mfma_bf16(kf, qf[0].v[kc], sc[0][kt]);
-          sc[1][kt] = mfma_bf16(kf, qf[1].v[kc], sc[1][kt]);
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[0][dt] = mfma_bf16(vf[u & 1][dt], pf0, o[0][dt]);
+        o[1][dt] = mfma_bf16(vf[u & 1][dt], pf1, o[1][dt]);
       }
-      const bool full = k0 + FW_KB <= prm.Nk;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + kt * 16 + 4 * g + r;
-            const float v = (full || key < prm.Nk) ? sc[t][kt][r] * prm.sl2 : -INFINITY;
-            sc[t][kt][r] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = quad_max(mx);
-        const float m_new = fmaxf(m_run[t], mx);
-        const float alpha = fast_exp2(m_run[t] - m_new);
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(sc[t][kt][r] - m_new);
-            sc[t][kt][r] = e;
-            rs += e;
-          }
-        rs = quad_sum(rs);
-        l_run[t] = l_run[t] * alpha + rs;
-        m_run[t] = m_new;
-#pragma unroll
-        for (int i = 0; i < NDT; ++i) o[t][i] *= alpha;
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint4 pf[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          pf[t] = uint4{pack_bf2(sc[t][2 * u][0], sc[t][2 * u][1]), pack_bf2(sc[t][2 * u][2], sc[t][2 * u][3]),
-                        pack_bf2(sc[t][2 * u + 1][0], sc[t][2 * u + 1][1]),
-                        pack_bf2(sc[t][2 * u + 1][2], sc[t][2 * u + 1][3])};
-        const int kbase = k0 + u * 32 + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int drow = dt * 16 + lr;
-          const uint2 lo = *reinterpret_cast<const uint2*>(&vt[drow][kbase]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&vt[drow][kbase + 16]);
-          const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
-          o[0][dt] = mfma_bf16(vf, pf[0], o[0][dt]);
-          o[1][dt] = mfma_bf16(vf, pf[1], o[1][dt]);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
+    if constexpr (ONES_ROW) {
+      // O^T row DH sits in tile DH / 16, element DH % 4 of lane group (DH % 16) / 4
+      constexpr int DT = DH / 16, GR = (DH % 16) / 4, EL = DH % 4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) lsum[t] = __shfl(o[t][DT][EL], GR * 16 + lr);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int q = qblk + wave * FW_QPW + t * 16 + lr;
       if (q < qend) {
-        const float inv = 1.f / l_run[t];
+        const float inv = 1.f / lsum[t];
         uint16_t* Ob = reinterpret_cast<uint16_t*>(prm.O) + ((int64_t)b * prm.Nq + q) * prm.D + h * DH;
 #pragma unroll
         for (int i = 0; i < NDT; ++i) {
@@ -626,8 +659,6 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_resident(FlashParams
         }
       }
     }
-    qf[0] = qn[0];
-    qf[1] = qn[1];
   }
 }
 
@@ -803,7 +834,7 @@ static hipError_t run_flash_wide(const FlashDesc& d, hipStream_t s) {
 }
 
 template <int DH>
-static hipError_t run_flash_resident(const FlashDesc& d, hipStream_t s) {
+static hipError_t run_flash_single(const FlashDesc& d, hipStream_t s) {
   FlashParams p;
   p.Q = d.Q; p.q_bs = d.q_bs; p.q_hs = d.q_hs;
   p.K = d.K; p.k_bs = d.k_bs; p.k_hs = d.k_hs;
@@ -819,15 +850,15 @@ static hipError_t run_flash_resident(const FlashDesc& d, hipStream_t s) {
   if (ranges < 1) ranges = 1;
   const int q_per_wg = (qblocks + ranges - 1) / ranges * FW_Q;
   dim3 grid((d.Nq + q_per_wg - 1) / q_per_wg, d.heads, d.B);
-  hipLaunchKernelGGL((flash_bf16_resident<DH>), grid, dim3(FW_WAVES * 64), 0, s, p, q_per_wg);
+  hipLaunchKernelGGL((flash_bf16_single<DH>), grid, dim3(FW_WAVES * 64), 0, s, p, q_per_wg);
   return hipGetLastError();
 }
 
 hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s) {
   if (d.Nq == 0 || d.B == 0) return hipSuccess;
-  if (!f32 && d.Nq >= 2048 && d.Nk <= FR_MAXK) {
-    if (d.dh == 72) return run_flash_resident<72>(d, s);
-    if (d.dh == 64) return run_flash_resident<64>(d, s);
+  if (!f32 && d.Nq >= 2048 && d.Nk <= FS_MAXK) {
+    if (d.dh == 72) return run_flash_single<72>(d, s);
+    if (d.dh == 64) return run_flash_single<64>(d, s);
   }
   if (!f32 && d.Nq >= 2048) {
     if (d.dh == 72) return run_flash_wide<72>(d, s);
