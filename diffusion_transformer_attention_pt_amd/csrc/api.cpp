@@ -37,11 +37,11 @@ struct TraceScope {
   TraceScope(int cls, hipStream_t st) : s(st) {
     if (g_trace.cls == cls && g_trace.count < g_trace.cap) {
       slot = g_trace.count++;
-      hipEventRecord(g_trace.start[slot], s);
+      (void)hipEventRecord(g_trace.start[slot], s);
     }
   }
   ~TraceScope() {
-    if (slot >= 0) hipEventRecord(g_trace.stop[slot], s);
+    if (slot >= 0) (void)hipEventRecord(g_trace.stop[slot], s);
   }
 };
 
@@ -400,7 +400,9 @@ ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity) {
   g_trace.start.resize(capacity);
   g_trace.stop.resize(capacity);
   for (int i = 0; i < capacity; ++i) {
-    if (hipEventCreate(&g_trace.start[i]) != hipSuccess || hipEventCreate(&g_trace.stop[i]) != hipSuccess) {
+    // no system-scope fence: the events only time work on this device
+    if (hipEventCreateWithFlags(&g_trace.start[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&g_trace.stop[i], hipEventDisableSystemFence) != hipSuccess) {
       g_trace.start.resize(i);
       g_trace.stop.resize(i);
       ptdit_trace_disable();
@@ -425,8 +427,8 @@ int32_t ptdit_trace_read(float* ms, int32_t max) {
 }
 
 void ptdit_trace_disable(void) {
-  for (size_t i = 0; i < g_trace.start.size(); ++i) hipEventDestroy(g_trace.start[i]);
-  for (size_t i = 0; i < g_trace.stop.size(); ++i) hipEventDestroy(g_trace.stop[i]);
+  for (size_t i = 0; i < g_trace.start.size(); ++i) (void)hipEventDestroy(g_trace.start[i]);
+  for (size_t i = 0; i < g_trace.stop.size(); ++i) (void)hipEventDestroy(g_trace.stop[i]);
   g_trace.start.clear();
   g_trace.stop.clear();
   g_trace.cls = -1;
