@@ -266,21 +266,27 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Fragment addressing: a wave reads fragment j of 16 rows at row0 + 16*j,
+// row0 = (wave's first row) + lane % 16, with the wave's first row a multiple
+// of 8. The swizzles below depend on row bits 1..2 (bf16) or 0..2 (fp32),
+// which 16*j never changes, so a lane computes its slot offset once (lofs)
+// and fragment j sits at a constant distance from it: LDS reads then use
+// immediate offsets from one base register per ring slot.
 template <typename TA> struct DmaA;
 template <> struct DmaA<uint16_t> {
   static constexpr int CPR = 4;  // 16-byte chunks per row per k-slice
   __device__ static int chunk(int row, int p) { return p ^ ((row >> 1) & 3); }
-  // fragment (row, 8-value group g) -> 8 bf16
-  __device__ static uint4 frag(const uint4* base, int row, int g) {
-    return base[row * 4 + (g ^ ((row >> 1) & 3))];
-  }
+  __device__ static int lofs(int row0, int g) { return row0 * 4 + (g ^ ((row0 >> 1) & 3)); }
+  // fragment j (rows row0 + 16 j, 8-value group g) -> 8 bf16
+  __device__ static uint4 frag(const uint4* base, int lofs, int j) { return base[lofs + j * 64]; }
 };
 template <> struct DmaA<float> {
   static constexpr int CPR = 8;
   __device__ static int chunk(int row, int p) { return p ^ (row & 7); }
-  __device__ static uint4 frag(const uint4* base, int row, int g) {
-    const uint4 lo = base[row * 8 + ((2 * g) ^ (row & 7))];
-    const uint4 hi = base[row * 8 + ((2 * g + 1) ^ (row & 7))];
+  __device__ static int lofs(int row0, int g) { return row0 * 8 + ((2 * g) ^ (row0 & 7)); }
+  __device__ static uint4 frag(const uint4* base, int lofs, int j) {
+    const uint4 lo = base[lofs + j * 128];
+    const uint4 hi = base[(lofs ^ 1) + j * 128];  // chunk 2g+1 of the same row
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
     typedef float f2 __attribute__((ext_vector_type(2)));
     auto cv = [](unsigned a, unsigned b) {
@@ -385,29 +391,26 @@ __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4
 
   // Store-phase chunk assignment, fixed across bands: chunk q = tid + i*NT of
   // a band is staged row sr = q / CPRO, chunk cc = q % CPRO (compile-time
-  // divisors). Column-dependent address parts are computed once here; rows
-  // advance by 16 per band, tracked as (batch, token) without division.
+  // divisors). Head-major column parts (divisions by runtime sizes) are
+  // computed once here; rows advance by 16 per band, tracked as (batch,
+  // token) without division. Token-major addresses are recomputed per store,
+  // which keeps the registers of the (still live) accumulators free.
   constexpr int NQ = (ES::ROWS * CPRO + NW * 64 - 1) / (NW * 64);
-  int64_t colpart[NQ];
-  int rowbase[NQ];
-  bool qok[NQ];
+  constexpr int NQH = HEADMAJOR ? NQ : 1;
+  int64_t colpart[NQH];
   const int64_t b0 = m0 / p.Ntok;            // one division per thread
   const int64_t t0 = m0 - b0 * p.Ntok;
   const int G = p.N / p.D;
   const int64_t bstride = (int64_t)G * p.heads * p.Ntok * p.dh;
+  if constexpr (HEADMAJOR) {
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int q = tid + i * NW * 64;
-    const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
-    const int n = n0 + cc * E;
-    qok[i] = q < ES::ROWS * CPRO && n < p.N;
-    rowbase[i] = (sr / 16) * TM + (sr % 16);
-    if constexpr (HEADMAJOR) {
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + i * NW * 64;
+      const int cc = q - (q / CPRO) * CPRO;
+      const int n = n0 + cc * E;
       const int gg = n / p.D, hn = n - gg * p.D;
       const int h = hn / p.dh, d = hn - h * p.dh;
       colpart[i] = ((int64_t)(gg * p.heads + h) * p.Ntok) * p.dh + d;
-    } else {
-      colpart[i] = n;
     }
   }
 
@@ -448,16 +451,17 @@ __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4
         for (int i = 0; i < NQ; ++i) {
           const int q = tid + i * NW * 64;
           const int sr = q / CPRO, cc = q - (q / CPRO) * CPRO;
-          const int rr = rowbase[i] + jb * 16;
-          if (!qok[i] || m0 + rr >= p.M) continue;
+          const int rr = (sr / 16) * TM + (sr % 16) + jb * 16;
+          const int n = n0 + cc * E;
+          if (q >= ES::ROWS * CPRO || n >= p.N || m0 + rr >= p.M) continue;
           const TY* sb = band_base(std::integral_constant<int, jb>{}, sr);
           const uint4 v = *reinterpret_cast<const uint4*>(sb + (sr % ES::ROWS_PER_SLOT) * ES::PITCH + cc * E);
           if constexpr (HEADMAJOR) {
             int64_t tok = t0 + rr, b = b0;
             while (tok >= p.Ntok) { tok -= p.Ntok; ++b; }
-            *reinterpret_cast<uint4*>(Y + b * bstride + colpart[i] + tok * p.dh) = v;
+            *reinterpret_cast<uint4*>(Y + b * bstride + colpart[HEADMAJOR ? i : 0] + tok * p.dh) = v;
           } else {
-            const int64_t off = (m0 + rr) * p.N + colpart[i];
+            const int64_t off = (m0 + rr) * p.N + n;
             if constexpr (sizeof(TY) == 4) {
               float4 o = __builtin_bit_cast(float4, v);
               if (R) {
@@ -556,15 +560,15 @@ gemm_dma_kernel(GemmParams p) {
   load_bias<FN>(p, n0 + wn * TN, lane, biasp);
 
   const int g = lane >> 4, lr = lane & 15;
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "fragment rows advance by 16");
+  const int lofs_w = SA + DmaA<uint16_t>::lofs(wn * TN + lr, g);
+  const int lofs_a = DmaA<TA>::lofs(wm * TM + lr, g);
   auto compute = [&](const uint4* st) {
     uint4 wf[FN], xf[FM];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int row = wn * TN + i * 16 + lr;
-      wf[i] = st[SA + row * 4 + (g ^ ((row >> 1) & 3))];
-    }
+    for (int i = 0; i < FN; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, wm * TM + j * 16 + lr, g);
+    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, lofs_a, j);
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -614,21 +618,41 @@ gemm_dma_kernel(GemmParams p) {
 // sees the reads of four waves at a time instead of eight).
 //
 // Every wave runs the same body for slice k:
-//   refill slot (k-1) % 4 with slice k+3;  read slice k's fragments;
-//   wait for slice k+1;  barrier;  MFMAs of slice k;  wait;  barrier
+//   read slice k's fragments;  wait for slice k+1;  barrier;
+//   refill slot (k-1) % 4 with slice k+3;  MFMAs of slice k;  wait;  barrier
 // Group 1 executes one extra barrier before its first body, group 0 one
 // after its last, which offsets the groups by one phase. Counting barriers
 // from the prologue's (#0): group 0 reads slice k between #2k and #2k+1,
 // group 1 between #2k+1 and #2k+2. Hence slot k-1 is free for both groups
-// from #2k on (group 0 refills after #2k, group 1 after #2k+1), and slice
+// from #2k on (group 0 refills after #2k+1, group 1 after #2k+2), and slice
 // k+1, waited on by every wave before each barrier of its body k, is whole
 // in LDS by #2k+2. Requires KT % 4 == 0 and KT >= 8.
+//
+// RKT > 0 (token-major output with a residual, KT == RKT == 36, one slice
+// per accumulator block): the residual is folded into the accumulators
+// during the main loop instead of being read in the epilogue. Each wave owns
+// FN*FM = 36 accumulator blocks of 16x16; body k loads the residual of block
+// k (one 4-value vector per lane) just before its refill and adds it in body
+// k+1, whose first wait (the refill's MAXI operations may stay in flight)
+// has retired it. The prologue loads block 35 between slices 1 and 2, in the
+// same position relative to the refills, so the vmcnt targets stay
+// constants. The loop is unrolled completely so that every block index is a
+// constant. The epilogue then only writes.
 // ----------------------------------------------------------------------------
-template <typename TR, typename TY, bool HEADMAJOR>
+// residual block loaded by steady body k of a wave with nb accumulator blocks
+// (k = -1: the prologue's load); -1: none
+constexpr int pp_rblock(int k, int nb) { return k < 0 ? nb + k : (k < nb - 1 ? k : -1); }
+
+template <typename TR, typename TY, bool HEADMAJOR, int RKT>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
+  constexpr bool RIN = RKT > 0;
+  static_assert(!RIN || RKT == 36, "one k-slice per accumulator block of a 64 x 144 wave tile");
   using TA = uint16_t;
   constexpr int BM = 256, BN = 288, WM = 4, WN = 2, NW = 8, STAGES = 4;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int NB = FN * FM;  // accumulator blocks per wave
+  constexpr int RL = RIN ? 1 : 0;
+  static_assert(!RIN || !HEADMAJOR, "residual only for token-major output");
   using DP = DmaPlan<TA, BM, BN, NW>;
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int SA = DP::SA, MAXI = DP::MAXI;
@@ -654,7 +678,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  const int KT = p.K / 32;
+  const int KT = RIN ? RKT : p.K / 32;
 
   DP dma;
   dma.init(p, m0, n0, wave, lane);
@@ -665,15 +689,14 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
     for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
 
   const int g = lane >> 4, lr = lane & 15;
+  const int lofs_w = SA + DmaA<uint16_t>::lofs(wn * TN + lr, g);
+  const int lofs_a = DmaA<TA>::lofs(wm * TM + lr, g);
   uint4 wf[FN], xf[FM];
   auto read_frags = [&](const uint4* st) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int row = wn * TN + i * 16 + lr;
-      wf[i] = st[SA + row * 4 + (g ^ ((row >> 1) & 3))];
-    }
+    for (int i = 0; i < FN; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, wm * TM + j * 16 + lr, g);
+    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, lofs_a, j);
   };
   auto mfmas = [&]() {
 #pragma unroll
@@ -681,50 +704,114 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
   };
-  // body of slice k (slot t = k % 4); AHEAD: slices allowed in flight once
-  // slice k+1 has landed
-  auto body = [&](auto tI, auto issueI, auto aheadI, int k) {
-    constexpr int t = decltype(tI)::value, AHEAD = decltype(aheadI)::value;
-    if constexpr (decltype(issueI)::value) dma.issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
+
+  // residual of accumulator block b (i = b % FN, j = b / FN): the lane's row
+  // and 4 columns, addressed as a wave-uniform base + the block's uniform
+  // offset + a 32-bit lane offset (full tiles only: M % 256 == 0, N % 288 == 0)
+  using RV = typename std::conditional<sizeof(TR) == 4, float4, uint2>::type;
+  const char* const rbase = reinterpret_cast<const char*>(
+      reinterpret_cast<const TR*>(p.R) + (m0 + wm * TM) * p.N + n0 + wn * TN);
+  const uint32_t rlane = (uint32_t)((lr * p.N + 4 * g) * (int)sizeof(TR));
+  auto rload = [&](auto bI) -> RV {
+    constexpr int b = decltype(bI)::value, i = b % FN, j = b / FN;
+    const int uoff = (j * 16 * p.N + i * 16) * (int)sizeof(TR);
+    return *reinterpret_cast<const RV*>(rbase + uoff + rlane);
+  };
+  auto radd = [&](auto bI, const RV& v) {  // bI: compile-time block
+    constexpr int bb = decltype(bI)::value;
+    float f[4];
+    if constexpr (sizeof(TR) == 4) {
+      f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    } else {
+      f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+      f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[bb % FN][bb / FN][r] += f[r];
+  };
+  RV rbuf;
+
+  // body of slice k (slot t = k % 4). W1 / W2: vm operations allowed in
+  // flight at the two waits; RES: this body takes part in the residual stream.
+  // RES bodies take a compile-time slice index kI (residual blocks
+  // rblock(k-2) added, rblock(k) loaded; -1: none)
+  auto body = [&](auto tI, auto issueI, auto w1I, auto w2I, auto resI, int k, auto kI) {
+    constexpr int t = decltype(tI)::value;
+    constexpr bool RES = RIN && decltype(resI)::value;
     read_frags(slot(std::integral_constant<int, t>{}));
-    wait_vm_lgkm0<AHEAD * MAXI>();
+    wait_vm_lgkm0<decltype(w1I)::value>();
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int KC = decltype(kI)::value;
+    if constexpr (RES) {
+      constexpr int b = pp_rblock(KC - 1, NB);
+      if constexpr (b >= 0) radd(std::integral_constant<int, b>{}, rbuf);
+      constexpr int bn = pp_rblock(KC, NB);
+      if constexpr (bn >= 0) rbuf = rload(std::integral_constant<int, bn>{});
+      // the residual load stays ahead of the refill, so the refill's MAXI
+      // operations are all that may follow it at the next body's first wait
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (decltype(issueI)::value) dma.issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
     mfmas();
-    wait_vm_lgkm0<AHEAD * MAXI>();
+    wait_vm_lgkm0<decltype(w2I)::value>();
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
+  using I0 = std::integral_constant<int, 0>;
 
-  // Prologue: slices 0..2 in flight, slice 0 landed (barrier #0); group 1
-  // then takes its extra barrier.
-  static_for<0, 3>([&](auto sI) { dma.issue(decltype(sI)::value, slot(sI)); });
-  wait_vm_lgkm0<2 * MAXI>();
+  // Prologue: slices 0..2 (and, with RIN, the residual of blocks NB-2 and
+  // NB-1 after slices 1 and 2), slice 0 landed (barrier #0); group 1 then
+  // takes its extra barrier.
+  dma.issue(0, slot(std::integral_constant<int, 0>{}));
+  dma.issue(1, slot(std::integral_constant<int, 1>{}));
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (RIN) rbuf = rload(std::integral_constant<int, pp_rblock(-1, NB)>{});
+  __builtin_amdgcn_sched_barrier(0);
+  dma.issue(2, slot(std::integral_constant<int, 2>{}));
+  wait_vm_lgkm0<2 * MAXI + RL>();
   ring_barrier();
   if (wn == 1) ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
   // Steady state: bodies k = 0 .. KT-5 (refill slice k+3 < KT - 1).
   const int NMAIN = KT - 4;
-  for (int k0 = 0; k0 < NMAIN; k0 += 4) {
-    static_for<0, 4>([&](auto tI) {
-      body(tI, std::true_type{}, std::integral_constant<int, 2>{}, k0 + decltype(tI)::value);
+  using W1 = std::integral_constant<int, MAXI>;
+  using W2 = std::integral_constant<int, 2 * MAXI + RL>;
+  if constexpr (RIN) {
+    static_for<0, RKT - 4>([&](auto kI) {
+      constexpr int k = decltype(kI)::value;
+      body(std::integral_constant<int, k % 4>{}, std::true_type{}, W1{}, W2{}, std::true_type{}, k, kI);
     });
+  } else {
+    for (int k0 = 0; k0 < NMAIN; k0 += 4) {
+      static_for<0, 4>([&](auto tI) {
+        body(tI, std::true_type{}, W1{}, W2{}, std::false_type{}, k0 + decltype(tI)::value, I0{});
+      });
+    }
   }
   // Tail: bodies KT-4 .. KT-1 (only the first refills, with slice KT-1).
-  body(std::integral_constant<int, 0>{}, std::true_type{}, std::integral_constant<int, 2>{}, NMAIN);
-  body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, 1>{}, NMAIN + 1);
-  body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, 0>{}, NMAIN + 2);
-  body(std::integral_constant<int, 3>{}, std::false_type{}, std::integral_constant<int, 0>{}, NMAIN + 3);
+  using RT = std::integral_constant<bool, RIN>;
+  constexpr int NM = RIN ? RKT - 4 : 0;
+  body(std::integral_constant<int, 0>{}, std::true_type{}, W1{}, std::integral_constant<int, 2 * MAXI + RL>{}, RT{},
+       NMAIN, std::integral_constant<int, NM>{});
+  body(std::integral_constant<int, 1>{}, std::false_type{}, W1{}, std::integral_constant<int, MAXI + RL>{}, RT{},
+       NMAIN + 1, std::integral_constant<int, NM + 1>{});
+  body(std::integral_constant<int, 2>{}, std::false_type{}, I0{}, std::integral_constant<int, RL>{}, RT{}, NMAIN + 2,
+       std::integral_constant<int, NM + 2>{});
+  body(std::integral_constant<int, 3>{}, std::false_type{}, I0{}, I0{}, RT{}, NMAIN + 3,
+       std::integral_constant<int, NM + 3>{});
   if (wn == 0) ring_barrier();
 
   wait_vm_lgkm0<0>();
   ring_barrier();
+  GemmParams pe = p;
+  if constexpr (RIN) pe.R = nullptr;  // every block's residual is in the accumulators
   uint2 biasp[FN];
   load_bias<FN>(p, n0 + wn * TN, lane, biasp);
-  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(p, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
+  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(pe, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
 }
 
 // ----------------------------------------------------------------------------
@@ -843,7 +930,14 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 != 0 || p.K < 256) return hipErrorInvalidValue;  // KT % 4 == 0, KT >= 8
   const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM>), dim3((unsigned)tiles), dim3(512), 0, s, p);
+  if constexpr (!HM) {
+    // the model width D = 1152 with whole tiles: residual folded into the main loop
+    if (p.R && p.K == 36 * 32 && p.M % 256 == 0 && p.N % 288 == 0) {
+      hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36>), dim3((unsigned)tiles), dim3(512), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0>), dim3((unsigned)tiles), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

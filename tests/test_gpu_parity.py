@@ -95,8 +95,11 @@ def test_roll_bit_exact(P, grid, shift, dt):
                                            # >= 2048 rows: K % 128 != 0 takes the ring kernel (33
                                            # k-slices), K = 256 the ping-pong kernel's minimum
                                            (2304, 1056, 1152), (2100, 256, 600)])
-@pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "f32"])
+@pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "bf16_res32", "bf16_res16", "f32"])
 def test_linear(P, rows, din, dout, mode):
+    """bf16_res32 / bf16_res16: bf16 x with an fp32 / bf16 residual, the two
+    output projections of the block; whole 256 x 288 tiles at d_in = 1152
+    fold the residual into the main loop, other shapes add it at the end."""
     announce(f"linear {rows}x{din}->{dout} {mode}")
     g = np.random.default_rng(rows + din)
     x = g.standard_normal((rows, din)).astype(np.float32)
@@ -113,6 +116,12 @@ def test_linear(P, rows, din, dout, mode):
             x = round_bf16(x)
             y = P.linear(dev(x, BF16), dev(w, BF16), dev(b, BF16), out_dtype=F32)
             ref = O.linear(x, w, b)
+        elif mode in ("bf16_res32", "bf16_res16"):
+            x = round_bf16(x)
+            r = r * 4.0 if mode == "bf16_res32" else round_bf16(r)
+            rd = dev(r, F32 if mode == "bf16_res32" else BF16)
+            y = P.linear(dev(x, BF16), dev(w, BF16), dev(b, BF16), residual=rd, out_dtype=F32)
+            ref = O.linear(x, w, b) + r
         else:
             y = P.linear(dev(x, F32), dev(w, BF16), dev(b, BF16), residual=dev(round_bf16(r), BF16),
                          out_dtype=F32)
