@@ -158,8 +158,8 @@ def main() -> int:
                    "gflop_per_step": round(flops["total"] / 1e9, 3)},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
-        "roofline": {"kernel": "gemm_bf16 Q/K/V projection of the token rows "
-                               f"[{rows}x{wl.D}]x[{wl.D}x{3 * wl.D}]",
+        "roofline": {"kernel": "gemm_pp_kernel: Q/K/V projection of the token rows "
+                               f"[{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] bf16 -> head-major bf16",
                      "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(dom_avg_ms, 5), "launches": len(dom_ms)},
