@@ -43,10 +43,11 @@ constexpr int POOL_CX = 16;   // channel chunks (of 8) per workgroup along x
 constexpr int POOL_MAXR = 64; // max (dt, di) rows held in LDS
 
 // Block (POOL_CX, ny): thread (tx, ty) sums rows r = ty, ty+ny, ... of the
-// window for chunk tx into LDS; thread ty == 0 then adds them in order.
+// window for chunk tx into LDS; thread ty == 0 then adds them in order. The
+// LDS holds the window's R = p_t * p_h row sums (dynamic size, R * 512 B).
 template <typename TX, typename TO>
 __global__ void __launch_bounds__(1024) pool_kernel(PoolParams p) {
-  __shared__ float part[POOL_MAXR * POOL_CX * 8];
+  extern __shared__ float part[];
   const int C = p.D / 8;
   const int tx = threadIdx.x, ty = threadIdx.y, ny = blockDim.y;
   const int cx = blockIdx.y * POOL_CX + tx;
@@ -65,6 +66,15 @@ __global__ void __launch_bounds__(1024) pool_kernel(PoolParams p) {
       const TX* src = x + ((int64_t)b * N + ((int64_t)t * p.H + i) * p.W + (int64_t)J * p.pw) * p.D + cx * 8;
       float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       int dj = 0;
+      for (; dj + 8 <= p.pw; dj += 8) {  // eight independent loads in flight, adds in order
+        float v[8][8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Vec8<TX>::load(src + (int64_t)(dj + u) * p.D, v[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = s[e] + v[u][e];
+      }
       for (; dj + 4 <= p.pw; dj += 4) {  // four independent loads in flight, adds in order
         float v0[8], v1[8], v2[8], v3[8];
         Vec8<TX>::load(src + (int64_t)(dj + 0) * p.D, v0);
@@ -155,7 +165,8 @@ static hipError_t run_pool(const PoolParams& p, hipStream_t s) {
     int ny = R;
     while (ny * POOL_CX > 1024) ny = (ny + 1) / 2;
     dim3 grid(p.B * M, (C + POOL_CX - 1) / POOL_CX);
-    hipLaunchKernelGGL((pool_kernel<TX, TO>), grid, dim3(POOL_CX, ny), 0, s, p);
+    hipLaunchKernelGGL((pool_kernel<TX, TO>), grid, dim3(POOL_CX, ny), (size_t)R * POOL_CX * 8 * sizeof(float), s,
+                       p);
   } else {
     const int64_t total = (int64_t)p.B * M * C;
     hipLaunchKernelGGL((pool_serial_kernel<TX, TO>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
