@@ -514,7 +514,7 @@ gemm_dma_kernel(GemmParams p) {
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int SA = DP::SA, MAXI = DP::MAXI;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert(STAGES >= 2 && STAGES <= 8, "ring depth");
+  static_assert(STAGES >= 2 && STAGES <= 16, "ring depth");
   constexpr int SLOT = (DP::SA + DP::SB) > ES::SLOT ? (DP::SA + DP::SB) : ES::SLOT;
 
   __shared__ uint4 ring0[SLOT];
@@ -525,6 +525,14 @@ gemm_dma_kernel(GemmParams p) {
   __shared__ uint4 ring5[STAGES > 5 ? SLOT : 1];
   __shared__ uint4 ring6[STAGES > 6 ? SLOT : 1];
   __shared__ uint4 ring7[STAGES > 7 ? SLOT : 1];
+  __shared__ uint4 ring8[STAGES > 8 ? SLOT : 1];
+  __shared__ uint4 ring9[STAGES > 9 ? SLOT : 1];
+  __shared__ uint4 ring10[STAGES > 10 ? SLOT : 1];
+  __shared__ uint4 ring11[STAGES > 11 ? SLOT : 1];
+  __shared__ uint4 ring12[STAGES > 12 ? SLOT : 1];
+  __shared__ uint4 ring13[STAGES > 13 ? SLOT : 1];
+  __shared__ uint4 ring14[STAGES > 14 ? SLOT : 1];
+  __shared__ uint4 ring15[STAGES > 15 ? SLOT : 1];
   auto slot = [&](auto sI) -> uint4* {
     constexpr int sl = decltype(sI)::value;
     if constexpr (sl == 0) return ring0;
@@ -534,7 +542,15 @@ gemm_dma_kernel(GemmParams p) {
     else if constexpr (sl == 4) return ring4;
     else if constexpr (sl == 5) return ring5;
     else if constexpr (sl == 6) return ring6;
-    else return ring7;
+    else if constexpr (sl == 7) return ring7;
+    else if constexpr (sl == 8) return ring8;
+    else if constexpr (sl == 9) return ring9;
+    else if constexpr (sl == 10) return ring10;
+    else if constexpr (sl == 11) return ring11;
+    else if constexpr (sl == 12) return ring12;
+    else if constexpr (sl == 13) return ring13;
+    else if constexpr (sl == 14) return ring14;
+    else return ring15;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -945,9 +961,8 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
 // 256x288 tiles: 288 = 4 heads of 72, and D = 1152 = 4 x 288, 3D = 12 x 288,
 // so a 2048^2 image block yields exactly 256 (N = D) or 768 (N = 3D) tiles for
 // 256 CUs. With bf16 A and K % 128 == 0 the ping-pong kernel takes them, else
-// the multi-stage ring kernel. Proxy-row projections (few rows) are latency-
-// bound and take a small tile with a deep ring; odd shapes take the
-// register-staged kernel.
+// the multi-stage ring kernel. Proxy-row projections (few rows) take a small
+// tile; odd shapes take the register-staged kernel.
 template <typename TA, typename TR, typename TY, bool HM>
 static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
@@ -960,9 +975,10 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   }
   if (p.M >= 2048 && p.K % 32 == 0 && p.K / 32 >= STAGES)
     return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
-  // few rows (proxies): latency-bound, so a small tile with 7 k-slices in flight
-  if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 8)
-    return run_dma<TA, TR, TY, 64, 64, 2, 2, 8, HM>(p, s);
+  // few rows (proxies): a small tile for parallelism; a 4-slot ring measured
+  // faster than 8 or 12 slots here (shorter prologue, same streaming rate)
+  if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 4)
+    return run_dma<TA, TR, TY, 64, 64, 2, 2, 4, HM>(p, s);
   if (p.M >= 1024) return run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s);
   return run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
 }
