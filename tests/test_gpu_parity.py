@@ -277,6 +277,23 @@ def test_one_proxy_and_many_proxies(P):
         assert_close(host(got), O.proxy_xattn(x, P2o, ws[1], wl.heads, False), "xattn")
 
 
+@pytest.mark.parametrize("grid,nk", [((1, 48, 50), 1), ((1, 60, 68), 255), ((1, 48, 50), 256), ((1, 32, 72), 257)],
+                         ids=["one_key", "255_keys", "256_keys", "257_keys"])
+def test_xattn_key_counts(P, grid, nk):
+    """Token queries (>= 2048) against 1, 255, 256 and 257 keys: the single-pass
+    kernel (all keys in registers, slots past Nk masked) up to 256 keys, the
+    online-softmax kernel beyond."""
+    wl = _wl(F=grid[0], H=grid[1], W=grid[2], p=(1, 1, 1))
+    announce(f"xattn keys={nk} queries={wl.N}")
+    x = make_x(wl, seed=600 + nk)
+    rng = np.random.default_rng(700 + nk)
+    prox = round_bf16(rng.standard_normal((1, nk, wl.D)).astype(np.float32))
+    ws = _weights(wl, 1)
+    aw = P.AttnWeights.from_dict(ws, BF16, "cuda")
+    got = P.proxy_xattn(dev(x, BF16), _grid(wl), dev(prox, BF16), aw, residual=False, out_dtype=F32)
+    assert_close(host(got), O.proxy_xattn(x, prox, ws, wl.heads, False), f"xattn {nk} keys")
+
+
 def test_error_paths_leave_outputs_untouched(P):
     wl = _wl()
     x = dev(make_x(wl, seed=1), BF16)
