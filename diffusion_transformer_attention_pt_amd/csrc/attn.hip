@@ -816,6 +816,18 @@ static hipError_t run_flash(const FlashDesc& d, hipStream_t s) {
   p.O = d.O; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
   p.sl2 = d.scale * LOG2E;
   dim3 grid((d.Nq + 63) / 64, d.heads, d.B);
+  // bf16 with at most 256 keys: one key block, staged once (one load latency
+  // instead of one per 64 keys); fp32 blocks would not fit in LDS
+  if constexpr (sizeof(typename P::T) == 2) {
+    if (d.Nk > 128 && d.Nk <= 256) {
+      hipLaunchKernelGGL((flash_kernel<P, DH, 256>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+    if (d.Nk > 64 && d.Nk <= 128) {
+      hipLaunchKernelGGL((flash_kernel<P, DH, 128>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((flash_kernel<P, DH, 64>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
