@@ -634,13 +634,15 @@ gemm_dma_kernel(GemmParams p) {
 // sees the reads of four waves at a time instead of eight).
 //
 // Every wave runs the same body for slice k:
-//   read slice k's fragments;  wait for slice k+1;  barrier;
-//   refill slot (k-1) % 4 with slice k+3;  MFMAs of slice k;  wait;  barrier
+//   refill slot (k-1) % 4 with slice k+3;  read slice k's fragments;
+//   wait for slice k+1;  barrier;  MFMAs of slice k;  wait;  barrier
+// (the refill is issued in the read phase, which waits at the barrier for
+// the other group's MFMAs anyway, so the MFMA phase carries no DMA issue)
 // Group 1 executes one extra barrier before its first body, group 0 one
 // after its last, which offsets the groups by one phase. Counting barriers
 // from the prologue's (#0): group 0 reads slice k between #2k and #2k+1,
 // group 1 between #2k+1 and #2k+2. Hence slot k-1 is free for both groups
-// from #2k on (group 0 refills after #2k+1, group 1 after #2k+2), and slice
+// from #2k on (group 0 refills after #2k, group 1 after #2k+1), and slice
 // k+1, waited on by every wave before each barrier of its body k, is whole
 // in LDS by #2k+2. Requires KT % 4 == 0 and KT >= 8.
 //
@@ -648,12 +650,13 @@ gemm_dma_kernel(GemmParams p) {
 // per accumulator block): the residual is folded into the accumulators
 // during the main loop instead of being read in the epilogue. Each wave owns
 // FN*FM = 36 accumulator blocks of 16x16; body k loads the residual of block
-// k (one 4-value vector per lane) just before its refill and adds it in body
-// k+1, whose first wait (the refill's MAXI operations may stay in flight)
-// has retired it. The prologue loads block 35 between slices 1 and 2, in the
-// same position relative to the refills, so the vmcnt targets stay
-// constants. The loop is unrolled completely so that every block index is a
-// constant. The epilogue then only writes.
+// k (one 4-value vector per lane, into buffer k % 2) just before its refill
+// and adds it in body k+1's MFMA phase, after that body's first wait (two
+// refills and one residual load may stay in flight) has retired it. The
+// prologue loads block 35 between slices 1 and 2, in the same position
+// relative to the refills, so the vmcnt targets stay constants. The loop is
+// unrolled completely so that every block index is a constant. The epilogue
+// then only writes.
 // ----------------------------------------------------------------------------
 // residual block loaded by steady body k of a wave with nb accumulator blocks
 // (k = -1: the prologue's load); -1: none
@@ -745,46 +748,47 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[bb % FN][bb / FN][r] += f[r];
   };
-  RV rbuf;
+  RV rbuf[2];
 
-  // body of slice k (slot t = k % 4). W1 / W2: vm operations allowed in
-  // flight at the two waits; RES: this body takes part in the residual stream.
-  // RES bodies take a compile-time slice index kI (residual blocks
-  // rblock(k-2) added, rblock(k) loaded; -1: none)
-  auto body = [&](auto tI, auto issueI, auto w1I, auto w2I, auto resI, int k, auto kI) {
+  // body of slice k (slot t = k % 4). W: vm operations allowed in flight at
+  // both waits (nothing is issued between them); RES: this body takes part in
+  // the residual stream, with a compile-time slice index kI (block
+  // pp_rblock(k) loaded, pp_rblock(k-1) added; -1: none).
+  auto body = [&](auto tI, auto issueI, auto wI, auto resI, int k, auto kI) {
     constexpr int t = decltype(tI)::value;
     constexpr bool RES = RIN && decltype(resI)::value;
-    read_frags(slot(std::integral_constant<int, t>{}));
-    wait_vm_lgkm0<decltype(w1I)::value>();
-    __builtin_amdgcn_sched_barrier(0);
-    ring_barrier();
-    __builtin_amdgcn_sched_barrier(0);
     constexpr int KC = decltype(kI)::value;
     if constexpr (RES) {
-      constexpr int b = pp_rblock(KC - 1, NB);
-      if constexpr (b >= 0) radd(std::integral_constant<int, b>{}, rbuf);
       constexpr int bn = pp_rblock(KC, NB);
-      if constexpr (bn >= 0) rbuf = rload(std::integral_constant<int, bn>{});
-      // the residual load stays ahead of the refill, so the refill's MAXI
-      // operations are all that may follow it at the next body's first wait
+      if constexpr (bn >= 0) rbuf[KC % 2] = rload(std::integral_constant<int, bn>{});
+      // the residual load stays ahead of the refill
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (decltype(issueI)::value) dma.issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
+    read_frags(slot(std::integral_constant<int, t>{}));
+    wait_vm_lgkm0<decltype(wI)::value>();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RES) {
+      constexpr int b = pp_rblock(KC - 1, NB);
+      if constexpr (b >= 0) radd(std::integral_constant<int, b>{}, rbuf[(KC + 1) % 2]);
+    }
     mfmas();
-    wait_vm_lgkm0<decltype(w2I)::value>();
+    wait_vm_lgkm0<decltype(wI)::value>();
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
   using I0 = std::integral_constant<int, 0>;
 
-  // Prologue: slices 0..2 (and, with RIN, the residual of blocks NB-2 and
-  // NB-1 after slices 1 and 2), slice 0 landed (barrier #0); group 1 then
-  // takes its extra barrier.
+  // Prologue: slices 0..2 (and, with RIN, the residual of block NB-1 after
+  // slice 1, into buffer 1), slice 0 landed (barrier #0); group 1 then takes
+  // its extra barrier.
   dma.issue(0, slot(std::integral_constant<int, 0>{}));
   dma.issue(1, slot(std::integral_constant<int, 1>{}));
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (RIN) rbuf = rload(std::integral_constant<int, pp_rblock(-1, NB)>{});
+  if constexpr (RIN) rbuf[1] = rload(std::integral_constant<int, pp_rblock(-1, NB)>{});
   __builtin_amdgcn_sched_barrier(0);
   dma.issue(2, slot(std::integral_constant<int, 2>{}));
   wait_vm_lgkm0<2 * MAXI + RL>();
@@ -792,33 +796,31 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   if (wn == 1) ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // Steady state: bodies k = 0 .. KT-5 (refill slice k+3 < KT - 1).
+  // Steady state: bodies k = 0 .. KT-5 (refill slice k+3 < KT - 1); at each
+  // wait slices k+2, k+3 (and residual k) may stay in flight.
   const int NMAIN = KT - 4;
-  using W1 = std::integral_constant<int, MAXI>;
-  using W2 = std::integral_constant<int, 2 * MAXI + RL>;
+  using WS = std::integral_constant<int, 2 * MAXI + RL>;
   if constexpr (RIN) {
     static_for<0, RKT - 4>([&](auto kI) {
       constexpr int k = decltype(kI)::value;
-      body(std::integral_constant<int, k % 4>{}, std::true_type{}, W1{}, W2{}, std::true_type{}, k, kI);
+      body(std::integral_constant<int, k % 4>{}, std::true_type{}, WS{}, std::true_type{}, k, kI);
     });
   } else {
     for (int k0 = 0; k0 < NMAIN; k0 += 4) {
       static_for<0, 4>([&](auto tI) {
-        body(tI, std::true_type{}, W1{}, W2{}, std::false_type{}, k0 + decltype(tI)::value, I0{});
+        body(tI, std::true_type{}, WS{}, std::false_type{}, k0 + decltype(tI)::value, I0{});
       });
     }
   }
   // Tail: bodies KT-4 .. KT-1 (only the first refills, with slice KT-1).
   using RT = std::integral_constant<bool, RIN>;
   constexpr int NM = RIN ? RKT - 4 : 0;
-  body(std::integral_constant<int, 0>{}, std::true_type{}, W1{}, std::integral_constant<int, 2 * MAXI + RL>{}, RT{},
-       NMAIN, std::integral_constant<int, NM>{});
-  body(std::integral_constant<int, 1>{}, std::false_type{}, W1{}, std::integral_constant<int, MAXI + RL>{}, RT{},
+  body(std::integral_constant<int, 0>{}, std::true_type{}, WS{}, RT{}, NMAIN, std::integral_constant<int, NM>{});
+  body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, MAXI + RL>{}, RT{},
        NMAIN + 1, std::integral_constant<int, NM + 1>{});
-  body(std::integral_constant<int, 2>{}, std::false_type{}, I0{}, std::integral_constant<int, RL>{}, RT{}, NMAIN + 2,
+  body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, RL>{}, RT{}, NMAIN + 2,
        std::integral_constant<int, NM + 2>{});
-  body(std::integral_constant<int, 3>{}, std::false_type{}, I0{}, I0{}, RT{}, NMAIN + 3,
-       std::integral_constant<int, NM + 3>{});
+  body(std::integral_constant<int, 3>{}, std::false_type{}, I0{}, RT{}, NMAIN + 3, std::integral_constant<int, NM + 3>{});
   if (wn == 0) ring_barrier();
 
   wait_vm_lgkm0<0>();
