@@ -48,9 +48,13 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     import numpy as np  # noqa: F401
     import oracle as O
     from synth_inputs import make_all_weights, make_x
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('threading_layer')})"
     except Exception:
         threads = os.cpu_count() or 1
     x = make_x(wl)
@@ -64,9 +68,26 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
         if time.perf_counter() - t_start > budget_s / 2 or len(times) >= 3:
             break
     t = statistics.median(times)
-    return {"value": wl.B * wl.N / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} full {wl.name} block(s) ({wl.B}x{wl.N} tokens), float64 NumPy, "
-                      f"median {t:.2f} s"}
+    out = {"value": wl.B * wl.N / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{len(times)} full {wl.name} block(s) ({wl.B}x{wl.N} tokens), float64 NumPy, "
+                     f"median {t:.2f} s",
+           "blas": blas, "host_cpus": len(os.sched_getaffinity(0))}
+    # the same oracle on one BLAS thread, on the small fp32 image block
+    # (N=1024), so that per-core speed is visible apart from the core count
+    try:
+        from threadpoolctl import threadpool_limits
+        from synth_inputs import WORKLOADS
+        small = WORKLOADS["img256_f32"]
+        xs, wss = make_x(small), make_all_weights(small)
+        with threadpool_limits(limits=1, user_api="blas"):
+            t0 = time.perf_counter()
+            O.block(xs, small.grid, small.p, small.win, small.shift, wss, small.heads)
+            t1 = time.perf_counter() - t0
+        out["one_thread"] = {"workload": small.name, "tokens": small.B * small.N,
+                             "seconds": round(t1, 3), "tokens_per_s": round(small.B * small.N / t1, 1)}
+    except Exception as e:  # threadpoolctl missing: report the gap, not a number
+        out["one_thread"] = f"not measured: {type(e).__name__}"
+    return out
 
 
 def main() -> int:
@@ -122,6 +143,18 @@ def main() -> int:
     dom_ms = _lib.trace_read(2 * args.steps + 8)
     _lib.trace_disable()
 
+    # per-step distribution: a separate pass, every step bracketed by events
+    # on the launch stream
+    nq = min(args.steps, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nq)]
+    for e0, e1 in evs:
+        e0.record()
+        blk.forward(x)
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    quant = lambda q: per_step[min(len(per_step) - 1, int(q * len(per_step)))]
+
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = wl.B * wl.N / (elapsed / args.steps)
     tflops = flops["total"] / (elapsed / args.steps) / 1e12
@@ -156,6 +189,7 @@ def main() -> int:
                                f"shift {wl.shift}",
                    "batch": wl.B, "tokens": wl.N, "D": wl.D, "heads": wl.heads,
                    "gflop_per_step": round(flops["total"] / 1e9, 3)},
+        "step_ms_p10_p50_p90": [round(quant(0.1), 4), round(quant(0.5), 4), round(quant(0.9), 4)],
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
         "roofline": {"kernel": "gemm_pp_kernel: Q/K/V projection of the token rows "
@@ -168,6 +202,18 @@ def main() -> int:
         names = {_lib.K_POOL: "pool", _lib.K_GEMM_PROXY: "gemm_proxy", _lib.K_GEMM_Q: "gemm_q",
                  _lib.K_ATTN_FLASH: "attn_flash", _lib.K_GEMM_OUT: "gemm_out",
                  _lib.K_GEMM_QKV: "gemm_qkv", _lib.K_ATTN_WINDOW: "attn_window"}
+        # algorithmic work per step of each class: FLOP (MFMA-bound classes) or
+        # HBM bytes (pool, window cores: reads of x / Q,K,V and writes of the result)
+        B, N, M, D = wl.B, wl.N, wl.M, wl.D
+        L = wl.win[0] * wl.win[1] * wl.win[2]
+        es = 2 if prec == torch.bfloat16 else 4
+        work = {"pool": ("GB/s", B * N * D * es + B * M * D * 4),
+                "gemm_proxy": ("TFLOP/s", 2 * B * M * D * 6 * D),
+                "gemm_q": ("TFLOP/s", 2 * B * N * D * D),
+                "attn_flash": ("TFLOP/s", 2 * B * D * (2 * M * M + 2 * N * M)),
+                "gemm_out": ("TFLOP/s", 3 * 2 * B * N * D * D),
+                "gemm_qkv": ("TFLOP/s", 2 * 2 * B * N * D * 3 * D),
+                "attn_window": ("GB/s", 2 * 4 * B * N * D * es)}
         br = {}
         for cls, nm in names.items():
             _lib.trace_enable(cls, 64)
@@ -176,11 +222,38 @@ def main() -> int:
             torch.cuda.synchronize()
             ms = _lib.trace_read(64)
             _lib.trace_disable()
+            step_s = sum(ms) / 10 * 1e-3
+            unit, amount = work[nm]
+            if unit == "GB/s":
+                rate, pk = amount / step_s / 1e9, PEAK_HBM_GBS
+            else:
+                rate, pk = amount / step_s / 1e12, peak
             br[nm] = {"launches_per_step": len(ms) // 10, "avg_ms": round(statistics.mean(ms), 5) if ms else None,
-                      "ms_per_step": round(sum(ms) / 10, 5)}
+                      "ms_per_step": round(sum(ms) / 10, 5), "achieved": round(rate, 1), "unit": unit,
+                      "peak_frac": round(rate / pk, 4)}
+        # cold pooling: rotate copies of x whose total exceeds the 256 MB
+        # last-level cache, so every launch reads x from HBM
+        xbytes = x.numel() * x.element_size()
+        ncopy = max(2, min(64, -(-600_000_000 // xbytes)))
+        xs = [x.clone() for _ in range(ncopy)]
+        reps = 4 * ncopy
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        _lib.proxy_pool(xs[0], blk.g, blk.p, out=blk.P)
+        e0.record()
+        for i in range(reps):
+            _lib.proxy_pool(xs[i % ncopy], blk.g, blk.p, out=blk.P)
+        e1.record()
+        torch.cuda.synchronize()
+        cold_ms = e0.elapsed_time(e1) / reps
+        cold_rate = work["pool"][1] / (cold_ms * 1e-3) / 1e9
+        br["pool_cold"] = {"avg_ms": round(cold_ms, 5), "achieved": round(cold_rate, 1), "unit": "GB/s",
+                           "peak_frac": round(cold_rate / PEAK_HBM_GBS, 4),
+                           "copies": ncopy, "bytes_rotated": ncopy * xbytes}
+        del xs
         out["breakdown"] = br
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"]["gpu_speedup"] = round(tokens_per_s / out["cpu_baseline"]["value"], 1)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

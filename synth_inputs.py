@@ -90,6 +90,28 @@ WORKLOADS: Dict[str, Workload] = {
                         note="N=65536, 256 proxies"),
 }
 WORKLOAD_ORDER: List[str] = ["img256_f32", "img1024", "img2048", "video16x30x45", "img4096"]
+
+# The pages' own video settings, beyond the five above. Video compresses time
+# by p_f = 4 (Qihoo-T2X, section 3, compression ratios); the spatial ratio
+# follows the image schedule for the view size (512 -> (4, 4)).
+#  * the 16x30x45 video grid with p_f = 4: 4x6x9 = 216 proxies;
+#  * multi-view generation read as a pseudo-video of 24 views, each a 512^2
+#    image (32x32 latent tokens after 8x VAE and 2x2 patches): 24x32x32;
+#  * long video, 512^2 x 288 frames, read as 72 latent frames (4x temporal
+#    VAE) of 32x32 tokens: 73,728 tokens, 18x8x8 = 1152 proxies.
+EXTRA_WORKLOADS: Dict[str, Workload] = {
+    "video16x30x45_pf4": Workload("video16x30x45_pf4", 6, B=1, F=16, H=30, W=45, D=1152, heads=16,
+                                  p=(4, 5, 5), win=(2, 8, 8), shift=(1, 4, 4), dtype="bf16",
+                                  note="N=21600, p_f=4: 216 proxies, grid zero-padded to 16x32x48 for TCM"),
+    "mview24x32x32": Workload("mview24x32x32", 8, B=1, F=24, H=32, W=32, D=1152, heads=16,
+                              p=(4, 4, 4), win=(2, 8, 8), shift=(1, 4, 4), dtype="bf16",
+                              note="N=24576 (24 views of 32x32), 384 proxies"),
+    "video72x32x32": Workload("video72x32x32", 9, B=1, F=72, H=32, W=32, D=1152, heads=16,
+                              p=(4, 4, 4), win=(2, 8, 8), shift=(1, 4, 4), dtype="bf16",
+                              note="N=73728 (long video), 1152 proxies"),
+}
+WORKLOADS.update(EXTRA_WORKLOADS)
+ALL_WORKLOADS: List[str] = WORKLOAD_ORDER + list(EXTRA_WORKLOADS)
 HEADLINE = "img2048"
 
 

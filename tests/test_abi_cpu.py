@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synth_inputs import WORKLOADS, WORKLOAD_ORDER
+from synth_inputs import ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ptdit.h")
@@ -127,7 +127,7 @@ def test_block_flops_match_oracle_counters():
     """The FLOP figure the benchmark divides by equals the oracle's counters
     (projections over real rows; cores dense over windows, real queries)."""
     from diffusion_transformer_attention_pt_amd.block import PTBlockAttention
-    for name in WORKLOAD_ORDER:
+    for name in ALL_WORKLOADS:
         wl = WORKLOADS[name]
         blk = PTBlockAttention.__new__(PTBlockAttention)
         blk.B, (blk.F, blk.H, blk.W), blk.D, blk.N, blk.M, blk.win = wl.B, wl.grid, wl.D, wl.N, wl.M, wl.win

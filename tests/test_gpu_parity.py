@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 from gpu_util import announce, assert_close, dev, host
-from synth_inputs import (WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_weights, make_x, round_bf16,
+from synth_inputs import (ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_weights, make_x, round_bf16,
                           tiny)
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,7 @@ def _prec(wl):
 
 # ----------------------------------------------------------------------------- pool (bit-exact)
 
-POOL_CASES = [(n, None) for n in WORKLOAD_ORDER] + [
+POOL_CASES = [(n, None) for n in ALL_WORKLOADS] + [
     ("odd", dict(B=2, F=4, H=6, W=9, D=64, p=(2, 3, 3))),
     ("serial", dict(B=1, F=2, H=80, W=3, D=1152, p=(2, 40, 1))),
     ("p111", dict(B=1, F=1, H=5, W=7, D=1152, p=(1, 1, 1))),
@@ -331,7 +331,7 @@ def test_empty_batch_is_noop(P):
 
 # ----------------------------------------------------------------------------- whole block, every workload
 
-@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", ALL_WORKLOADS)
 def test_block_vs_oracle(P, name):
     wl = WORKLOADS[name]
     prec = _prec(wl)

@@ -25,7 +25,7 @@ import torch
 
 import bruteforce as bf
 import oracle as O
-from synth_inputs import WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_int_x, make_x, tiny
+from synth_inputs import ALL_WORKLOADS, EXTRA_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_int_x, make_x, tiny
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")
 
@@ -352,6 +352,29 @@ def test_compression_schedule_keeps_proxy_count():
     for name in WORKLOAD_ORDER[:3] + ["img4096"]:
         wl = WORKLOADS[name]
         assert wl.M == 256
+
+
+def test_video_workloads_follow_pages_ratios():
+    """The extra video workloads compress time by the pages' fixed p_f and
+    space by the image schedule's ratio for their view size (512^2 views ->
+    32x32 latent tokens under 8x VAE and 2x2 patches)."""
+    facts = json.load(open(GOLDEN))
+    pf = facts["video_temporal_ratio"]["value"]
+    spatial = {res // 16: tuple(p[1:]) for res, p in facts["compression_ratios_image"]["value"]}
+    for name, wl in EXTRA_WORKLOADS.items():
+        assert wl.p[0] == pf, name
+        assert wl.F % pf == 0 and wl.H % wl.p[1] == 0 and wl.W % wl.p[2] == 0, name
+        if wl.H == wl.W:
+            assert tuple(wl.p[1:]) == spatial[wl.H], name
+    # the three proxy counts
+    assert [EXTRA_WORKLOADS[n].M for n in ("video16x30x45_pf4", "mview24x32x32", "video72x32x32")] == \
+        [4 * 6 * 9, 6 * 8 * 8, 18 * 8 * 8]
+    # cost model holds for every workload (pages' complexity paragraph)
+    for name in ALL_WORKLOADS:
+        wl = WORKLOADS[name]
+        c = O.count_core_macs(wl.grid, wl.p, wl.win, wl.D, B=wl.B)
+        P = wl.p[0] * wl.p[1] * wl.p[2]
+        assert c["xattn"] * P == wl.B * 2 * wl.N * wl.N * wl.D
 
 
 def test_projection_macs_img2048():
