@@ -725,16 +725,23 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   };
 
   // residual of accumulator block b (i = b % FN, j = b / FN): the lane's row
-  // and 4 columns, addressed as a wave-uniform base + the block's uniform
-  // offset + a 32-bit lane offset (full tiles only: M % 256 == 0, N % 288 == 0)
+  // and 4 columns, addressed as a wave-uniform base (the tile's first row) +
+  // the block's uniform column offset + a 32-bit lane offset per row block.
+  // Rows past M read row M - 1 (never stored: the epilogue drops them), so a
+  // ragged last row tile needs no branch; columns need N % 288 == 0.
   using RV = typename std::conditional<sizeof(TR) == 4, float4, uint2>::type;
-  const char* const rbase = reinterpret_cast<const char*>(
-      reinterpret_cast<const TR*>(p.R) + (m0 + wm * TM) * p.N + n0 + wn * TN);
-  const uint32_t rlane = (uint32_t)((lr * p.N + 4 * g) * (int)sizeof(TR));
+  const char* const rbase = reinterpret_cast<const char*>(reinterpret_cast<const TR*>(p.R) + m0 * p.N + n0 + wn * TN);
+  uint32_t rlane[RIN ? FM : 1];
+  if constexpr (RIN) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t row = min(m0 + wm * TM + j * 16 + lr, p.M - 1);
+      rlane[j] = (uint32_t)(((int)(row - m0) * p.N + 4 * g) * (int)sizeof(TR));
+    }
+  }
   auto rload = [&](auto bI) -> RV {
     constexpr int b = decltype(bI)::value, i = b % FN, j = b / FN;
-    const int uoff = (j * 16 * p.N + i * 16) * (int)sizeof(TR);
-    return *reinterpret_cast<const RV*>(rbase + uoff + rlane);
+    return *reinterpret_cast<const RV*>(rbase + i * 16 * (int)sizeof(TR) + rlane[j]);
   };
   auto radd = [&](auto bI, const RV& v) {  // bI: compile-time block
     constexpr int bb = decltype(bI)::value;
@@ -949,8 +956,9 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
   if (tiles <= 0) return hipSuccess;
   if constexpr (!HM) {
-    // the model width D = 1152 with whole tiles: residual folded into the main loop
-    if (p.R && p.K == 36 * 32 && p.M % 256 == 0 && p.N % 288 == 0) {
+    // the model width D = 1152 with whole column tiles: residual folded into
+    // the main loop (rows past M of a ragged last row tile are clamped)
+    if (p.R && p.K == 36 * 32 && p.N % 288 == 0) {
       hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36>), dim3((unsigned)tiles), dim3(512), 0, s, p);
       return hipGetLastError();
     }

@@ -94,7 +94,11 @@ def test_roll_bit_exact(P, grid, shift, dt):
                                            (3000, 1152, 1000), (1500, 1152, 1152), (2048, 96, 288),
                                            # >= 2048 rows: K % 128 != 0 takes the ring kernel (33
                                            # k-slices), K = 256 the ping-pong kernel's minimum
-                                           (2304, 1056, 1152), (2100, 256, 600)])
+                                           (2304, 1056, 1152), (2100, 256, 600),
+                                           # residual folded into the main loop with a ragged
+                                           # last row tile (2100 = 8 x 256 + 52; 52 < 64 rows,
+                                           # so three of its four row waves hold no real row)
+                                           (2100, 1152, 1152), (2350, 1152, 2304)])
 @pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "bf16_res32", "bf16_res16", "f32"])
 def test_linear(P, rows, din, dout, mode):
     """bf16_res32 / bf16_res16: bf16 x with an fp32 / bf16 residual, the two
