@@ -662,6 +662,263 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams p
   }
 }
 
+// ---------------------------------------------------------------- flash core, bf16, ping-pong
+// Up to FP_MAXK keys, all resident in LDS (K row-major chunks; V^T with a
+// row of ones at DH, so the softmax denominator is accumulated by the MFMA
+// as row DH of O^T). Keys are taken in blocks of 64 with an online softmax.
+// Each wave owns 64 queries (four 16-query tiles), so every K or V^T
+// fragment read from LDS feeds four MFMAs: with two tiles per wave the
+// fragment reads, not the matrix core, set the pace.
+// The 8 waves form two groups of four, one wave of each per SIMD, that run
+// one phase apart: a wave alternates a VALU phase (softmax of one key block:
+// max, exp2, bf16 pack; O rescaled when some running max grew) and an MFMA
+// phase (P V of that block, then the scores of the next block, possibly of
+// the next query block). Every phase ends at a workgroup barrier, so while
+// one group's softmax occupies a SIMD's VALU the other group's products
+// occupy its matrix core. K/V are read-only after staging: the barriers only
+// keep the two groups in step.
+constexpr int FP_MAXK = 512;
+
+template <int DH>
+constexpr int flash_pp_lds_bytes(int keys) {
+  return keys * (DH / 8) * 16 + ((DH + 15) / 16) * 16 * (keys + 4) * 2;
+}
+
+// FP_QT 16-query tiles per wave, key blocks of FP_KB
+constexpr int PP_QT = 2, PP_KB = 128;
+template <int DH, int FP_QT, int FP_KB>
+__global__ void __launch_bounds__(FW_WAVES * 64, 1) flash_bf16_pp(FlashParams prm, int q_per_wg, int nkb) {
+  constexpr int FP_KT = FP_KB / 16, FP_QPW = 16 * FP_QT, FP_Q = FW_WAVES * FP_QPW;
+  using P = BF16P<DH>;
+  constexpr int NT = FW_WAVES * 64, NDT = P::NDT, DCH = P::DCH;
+  static_assert(NDT * 16 > DH, "the denominator uses the ones row of V^T");
+  extern __shared__ uint4 fp_smem[];
+  const int keys = nkb * FP_KB, vtp = keys + 4;
+  uint4* const ks = fp_smem;                                               // [keys][DCH]
+  uint16_t* const vt = reinterpret_cast<uint16_t*>(fp_smem + keys * DCH);  // [NDT*16][vtp]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = lane >> 4, lr = lane & 15;
+  const uint16_t* Qb = reinterpret_cast<const uint16_t*>(prm.Q) + b * prm.q_bs + h * prm.q_hs;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(prm.K) + b * prm.k_bs + h * prm.k_hs;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(prm.V) + b * prm.v_bs + h * prm.v_hs;
+  const int qbeg = blockIdx.x * q_per_wg;
+  const int qend = min(prm.Nq, qbeg + q_per_wg);
+  const int Nk = prm.Nk;
+
+  // Q fragments: NKF chunks of 32 head dims for the 16x16x32 MFMA, then the
+  // last 8 dims (DH = 32 NKF + 8) for one 16x16x16 MFMA (lane group g holds
+  // dims 32 NKF + 4g .. +3; groups 2, 3 zero)
+  constexpr int NKF = DH / 32;
+  static_assert(DH % 32 == 8, "head dim 32k + 8");
+  struct QFr { uint4 v[NKF]; uint2 tail; };
+  QFr qf[FP_QT];
+  // addresses: a wave-uniform base (the wave's first query row) + a 32-bit
+  // lane offset + a per-tile constant
+  const uint32_t q_lane = (uint32_t)((lr * DH + 8 * g) * 2), q_tail = (uint32_t)((lr * DH + NKF * 32 + 4 * g) * 2);
+  auto load_qf = [&](int qblk) {
+    const int q0 = qblk + wave * FP_QPW;
+    const char* base = reinterpret_cast<const char*>(Qb + (int64_t)q0 * DH);
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      const bool ok = q0 + t * 16 + lr < qend;
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc)
+        qf[t].v[kc] = ok ? *reinterpret_cast<const uint4*>(base + q_lane + (t * 16 * DH + kc * 32) * 2)
+                         : uint4{0, 0, 0, 0};
+      qf[t].tail = ok && g < 2 ? *reinterpret_cast<const uint2*>(base + q_tail + t * 16 * DH * 2) : uint2{0, 0};
+    }
+  };
+  load_qf(qbeg);
+
+  // stage K (chunks) and V^T (four keys per item) of every key slot, zeros
+  // past Nk; row DH of V^T is all ones, rows past it zero
+  for (int it = tid; it < keys * DCH; it += NT) {
+    const int key = it / DCH, c = it % DCH;
+    ks[it] = key < Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+  }
+  for (int it = tid; it < DCH * (keys / 4); it += NT) {
+    const int c = it / (keys / 4), kq = it % (keys / 4);
+    uint4 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = kq * 4 + e;
+      v[e] = key < Nk ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = (j & 1) * 16;
+      const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&v[0])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&v[1])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&v[2])[j >> 1] >> sh) & 0xffffu;
+      const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&v[3])[j >> 1] >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(&vt[(c * 8 + j) * vtp + kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    }
+  }
+  for (int i = tid; i < (NDT * 16 - DH) * vtp; i += NT) vt[DH * vtp + i] = i < vtp ? (uint16_t)0x3f80u : (uint16_t)0;
+  __syncthreads();
+
+  const float c2 = prm.sl2;
+  const bool tail_masked = Nk < keys;  // uniform: only the last key block holds slots past Nk
+
+  floatx4 sc[FP_QT][FP_KT];
+  uint32_t pk[FP_QT][FP_KT][2];
+  floatx4 o[FP_QT][NDT];
+  float m_run[FP_QT];
+
+  auto scores = [&](int kb) {
+    struct KFr { uint4 v[NKF]; uint2 tail; };
+    KFr kf[2];
+    auto load_kf = [&](int kt, KFr& f) {
+      const int key = kb * FP_KB + kt * 16 + lr;
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc) f.v[kc] = ks[key * DCH + kc * 4 + g];
+      f.tail = g < 2 ? reinterpret_cast<const uint2*>(&ks[key * DCH + NKF * 4])[g] : uint2{0, 0};
+    };
+    load_kf(0, kf[0]);
+#pragma unroll
+    for (int kt = 0; kt < FP_KT; ++kt) {
+      if (kt + 1 < FP_KT) load_kf(kt + 1, kf[(kt + 1) & 1]);
+      const KFr& f = kf[kt & 1];
+#pragma unroll
+      for (int t = 0; t < FP_QT; ++t) sc[t][kt] = mfma_bf16_k16(f.tail, qf[t].tail, zero4());
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc)
+#pragma unroll
+        for (int t = 0; t < FP_QT; ++t) sc[t][kt] = mfma_bf16(f.v[kc], qf[t].v[kc], sc[t][kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv = [&](int kb) {
+    uint4 vf[2][NDT];
+    auto load_vf = [&](int u, uint4* f) {
+      const uint16_t* base = vt + lr * vtp + kb * FP_KB + u * 32 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t* row = base + dt * 16 * vtp;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+        f[dt] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+    load_vf(0, vf[0]);
+#pragma unroll
+    for (int u = 0; u < FP_KT / 2; ++u) {
+      if (u + 1 < FP_KT / 2) load_vf(u + 1, vf[(u + 1) & 1]);
+#pragma unroll
+      for (int t = 0; t < FP_QT; ++t) {
+        const uint4 pf = uint4{pk[t][2 * u][0], pk[t][2 * u][1], pk[t][2 * u + 1][0], pk[t][2 * u + 1][1]};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] = mfma_bf16(vf[u & 1][dt], pf, o[t][dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // softmax of key block kb; kb == 0 starts a query block (O is zero)
+  auto softmax = [&](int kb) {
+    if (kb == nkb - 1 && tail_masked) {
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool out = kb * FP_KB + kt * 16 + 4 * g + r >= Nk;
+#pragma unroll
+          for (int t = 0; t < FP_QT; ++t) sc[t][kt][r] = out ? -INFINITY : sc[t][kt][r];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      float mx = sc[t][0][0];
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[t][kt][r]);
+      mx = quad_max(mx);
+      float m_new = mx;
+      if (kb > 0) {
+        m_new = fmaxf(m_run[t], mx);
+        // rescale O only when some query's running max grew
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run[t]) != 0) {
+          const float alpha = fast_exp2((m_run[t] - m_new) * c2);
+#pragma unroll
+          for (int i = 0; i < NDT; ++i) o[t][i] *= alpha;
+        }
+      }
+      m_run[t] = m_new;
+      const float nmc = -m_new * c2;
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = fast_exp2(fmaf(sc[t][kt][r], c2, nmc));
+        pk[t][kt][0] = pack_bf2(e[0], e[1]);
+        pk[t][kt][1] = pack_bf2(e[2], e[3]);
+      }
+    }
+  };
+  auto zero_o = [&]() {
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t)
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[t][i] = zero4();
+  };
+  // O^T row DH (the denominator) sits in tile DH / 16, element DH % 4 of lane group (DH % 16) / 4
+  auto store_o = [&](int qblk) {
+    constexpr int DT = DH / 16, GR = (DH % 16) / 4, EL = DH % 4;
+    const int q0 = qblk + wave * FP_QPW;
+    char* base = reinterpret_cast<char*>(reinterpret_cast<uint16_t*>(prm.O) + ((int64_t)b * prm.Nq + q0) * prm.D + h * DH);
+    const uint32_t o_lane = (uint32_t)((lr * prm.D + 4 * g) * 2);
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      const float lsum = __shfl(o[t][DT][EL], GR * 16 + lr);
+      if (q0 + t * 16 + lr < qend) {
+        const float inv = 1.f / lsum;
+        char* row = base + o_lane + (uint32_t)(t * 16 * prm.D * 2);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+          if (i * 16 + 4 * g < DH)
+            store4(reinterpret_cast<uint16_t*>(row + i * 32), o[t][i][0] * inv, o[t][i][1] * inv, o[t][i][2] * inv,
+                   o[t][i][3] * inv);
+        }
+      }
+    }
+  };
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // group 1 runs one phase behind group 0
+  if (grp == 1) phase_end();
+  scores(0);
+  phase_end();
+  for (int qblk = qbeg; qblk < qend; qblk += FP_Q) {
+    const bool more = qblk + FP_Q < qend;
+    for (int kb = 0; kb < nkb; ++kb) {
+      // VALU phase: softmax of block kb (O starts at zero with block 0)
+      softmax(kb);
+      if (kb == 0) zero_o();
+      if (kb == nkb - 1 && more) load_qf(qblk + FP_Q);  // this query block's scores are done
+      phase_end();
+      // MFMA phase: P V of block kb (then the finished block's output), then
+      // the next scores
+      pv(kb);
+      if (kb + 1 < nkb) {
+        scores(kb + 1);
+      } else {
+        store_o(qblk);
+        if (more) scores(0);
+      }
+      phase_end();
+    }
+  }
+  if (grp == 0) phase_end();
+}
+
 // ---------------------------------------------------------------- window core
 struct WindowParams {
   const void* QKV;       // [B][3][heads][N][dh]
@@ -866,8 +1123,43 @@ static hipError_t run_flash_single(const FlashDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DH, int QT, int KB>
+static hipError_t run_flash_pp(const FlashDesc& d, hipStream_t s) {
+  constexpr int FP_Q = FW_WAVES * 16 * QT;
+  FlashParams p;
+  p.Q = d.Q; p.q_bs = d.q_bs; p.q_hs = d.q_hs;
+  p.K = d.K; p.k_bs = d.k_bs; p.k_hs = d.k_hs;
+  p.V = d.V; p.v_bs = d.v_bs; p.v_hs = d.v_hs;
+  p.O = d.O; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
+  p.sl2 = d.scale * LOG2E;
+  // about one workgroup per CU (the LDS holds every key of one head)
+  const int pairs = d.B * d.heads;
+  int ranges = (256 + pairs - 1) / pairs;
+  const int qblocks = (d.Nq + FP_Q - 1) / FP_Q;
+  if (ranges > qblocks) ranges = qblocks;
+  if (ranges < 1) ranges = 1;
+  const int q_per_wg = (qblocks + ranges - 1) / ranges * FP_Q;
+  dim3 grid((d.Nq + q_per_wg - 1) / q_per_wg, d.heads, d.B);
+  const int nkb = (d.Nk + KB - 1) / KB;
+  const int lds = flash_pp_lds_bytes<DH>(nkb * KB);
+  constexpr int max_lds = flash_pp_lds_bytes<DH>((FP_MAXK + KB - 1) / KB * KB);
+  static_assert(max_lds <= 160 * 1024, "LDS");
+  static bool attr_set = false;  // same value from every thread: a benign race
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_bf16_pp<DH, QT, KB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((flash_bf16_pp<DH, QT, KB>), grid, dim3(FW_WAVES * 64), lds, s, p, q_per_wg, nkb);
+  return hipGetLastError();
+}
+
 hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s) {
   if (d.Nq == 0 || d.B == 0) return hipSuccess;
+  if (!f32 && d.Nq >= 2048 && d.Nk > FS_MAXK && d.Nk <= FP_MAXK) {
+    if (d.dh == 72) return run_flash_pp<72, PP_QT, PP_KB>(d, s);
+  }
   if (!f32 && d.Nq >= 2048 && d.Nk <= FS_MAXK) {
     if (d.dh == 72) return run_flash_single<72>(d, s);
     if (d.dh == 64) return run_flash_single<64>(d, s);

@@ -57,6 +57,15 @@ __device__ __forceinline__ uint4 pack8_sw(const float* f) {
   return r;
 }
 
+// D(16x16, fp32) += A(16x16, bf16) * B(16x16, bf16): lane l supplies A row
+// (l % 16), k = 4*(l / 16) .. +4 and B column (l % 16), the same k range; D as
+// below.
+__device__ __forceinline__ floatx4 mfma_bf16_k16(const uint2& a, const uint2& b, floatx4 c) {
+  typedef short shortx4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c,
+                                                   0, 0, 0);
+}
+
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
 // Lane l supplies A row (l % 16), k = 8*(l / 16) .. +8 and B column (l % 16),
 // the same k range; it receives D rows 4*(l / 16) .. +4 of column (l % 16).

@@ -281,18 +281,26 @@ def test_one_proxy_and_many_proxies(P):
         assert_close(host(got), O.proxy_xattn(x, P2o, ws[1], wl.heads, False), "xattn")
 
 
-@pytest.mark.parametrize("grid,nk", [((1, 48, 50), 1), ((1, 60, 68), 255), ((1, 48, 50), 256), ((1, 32, 72), 257)],
-                         ids=["one_key", "255_keys", "256_keys", "257_keys"])
-def test_xattn_key_counts(P, grid, nk):
-    """Token queries (>= 2048) against 1, 255, 256 and 257 keys: the single-pass
-    kernel (all keys in registers, slots past Nk masked) up to 256 keys, the
-    online-softmax kernel beyond."""
+XATTN_KEYS = [((1, 48, 50), 1, 1.0), ((1, 48, 50), 127, 1.0), ((1, 48, 50), 128, 1.0), ((1, 48, 50), 129, 1.0),
+              ((1, 60, 68), 255, 1.0), ((1, 48, 50), 256, 1.0), ((1, 32, 72), 257, 1.0), ((1, 48, 50), 384, 1.0),
+              ((1, 48, 50), 384, 3.0), ((1, 50, 41), 511, 1.0), ((1, 48, 50), 512, 3.0), ((1, 48, 50), 513, 1.0)]
+
+
+@pytest.mark.parametrize("grid,nk,wscale", XATTN_KEYS,
+                         ids=[f"{nk}_keys" + ("_peaked" if s > 1 else "") for _, nk, s in XATTN_KEYS])
+def test_xattn_key_counts(P, grid, nk, wscale):
+    """Token queries (>= 2048) against 1 .. 513 keys: up to 512 keys every key
+    of a head stays in LDS and key blocks of 128 (the last one partly masked)
+    go through the online softmax; beyond, keys stream through LDS. Weights
+    scaled by 3 (logits x9) give peaked scores whose running max moves between blocks."""
     wl = _wl(F=grid[0], H=grid[1], W=grid[2], p=(1, 1, 1))
-    announce(f"xattn keys={nk} queries={wl.N}")
+    announce(f"xattn keys={nk} queries={wl.N} wscale={wscale}")
     x = make_x(wl, seed=600 + nk)
     rng = np.random.default_rng(700 + nk)
     prox = round_bf16(rng.standard_normal((1, nk, wl.D)).astype(np.float32))
     ws = _weights(wl, 1)
+    if wscale != 1.0:
+        ws = {k: round_bf16(v * np.float32(wscale)) if k in ("wq", "wk") else v for k, v in ws.items()}
     aw = P.AttnWeights.from_dict(ws, BF16, "cuda")
     got = P.proxy_xattn(dev(x, BF16), _grid(wl), dev(prox, BF16), aw, residual=False, out_dtype=F32)
     assert_close(host(got), O.proxy_xattn(x, prox, ws, wl.heads, False), f"xattn {nk} keys")
