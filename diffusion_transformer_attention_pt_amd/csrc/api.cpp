@@ -198,7 +198,9 @@ size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 wi
       return align_up(B * 3 * M * D * es) + align_up(B * M * D * es);
     case PTDIT_OP_PROXY_XATTN:
       if (M < 0) return 0;
-      return align_up(B * N * D * es) + align_up(B * 2 * M * D * es) + align_up(B * N * D * es);
+      // Q, K/V, attention output, and (bf16, more than 512 keys) packed V^T blocks
+      return align_up(B * N * D * es) + align_up(B * 2 * M * D * es) + align_up(B * N * D * es) +
+             (prec == PTDIT_BF16 && g.heads > 0 ? align_up(ptdit::flash_vt_bytes(g.B, g.heads, M)) : 0);
     case PTDIT_OP_WINDOW_SA:
     case PTDIT_OP_SHIFT_WINDOW_SA:
       return align_up(B * 3 * N * D * es) + align_up(B * N * D * es);
@@ -341,6 +343,10 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
   f.V = offset_elems(kv, heads * khs, prec); f.v_bs = 2 * heads * khs; f.v_hs = khs;
   f.O = o; f.B = g.B; f.heads = heads; f.Nq = (int)N; f.Nk = M; f.dh = dh; f.D = D;
   f.scale = 1.0f / std::sqrt((float)dh);
+  if (prec == PTDIT_BF16) {
+    f.vt = (char*)o + align_up((size_t)rows * D * es);
+    f.vt_bytes = flash_vt_bytes(g.B, heads, M);
+  }
   {
     TraceScope ts(PTDIT_K_ATTN_FLASH, stream);
     e = launch_flash(f, prec == PTDIT_F32, stream);

@@ -899,10 +899,11 @@ __global__ void __launch_bounds__(FW_WAVES * 64, 1) flash_bf16_pp(FlashParams pr
   for (int qblk = qbeg; qblk < qend; qblk += FP_Q) {
     const bool more = qblk + FP_Q < qend;
     for (int kb = 0; kb < nkb; ++kb) {
-      // VALU phase: softmax of block kb (O starts at zero with block 0)
+      // VALU phase: (next query block's Q, whose last scores are done,)
+      // softmax of block kb (O starts at zero with block 0)
+      if (kb == nkb - 1 && more) load_qf(qblk + FP_Q);
       softmax(kb);
       if (kb == 0) zero_o();
-      if (kb == nkb - 1 && more) load_qf(qblk + FP_Q);  // this query block's scores are done
       phase_end();
       // MFMA phase: P V of block kb (then the finished block's output), then
       // the next scores
@@ -915,6 +916,283 @@ __global__ void __launch_bounds__(FW_WAVES * 64, 1) flash_bf16_pp(FlashParams pr
       }
       phase_end();
     }
+  }
+  if (grp == 0) phase_end();
+}
+
+// ---------------------------------------------------------------- flash core, bf16, ping-pong, streamed keys
+// More than FP_MAXK keys: the same two-group schedule (PP_QT tiles per wave,
+// key blocks of 128), with K/V streamed through a ring of three LDS buffers.
+// V^T is first packed per (batch, head, key block) into the exact LDS image
+// of one block (80 rows of FPS_VTP elements: DH rows of V^T, the ones row,
+// zero rows; keys past Nk zero), so both K and V^T move with direct
+// global -> LDS DMA and no staging registers. Group 0 issues the DMA of step
+// s + 2 at the end of its MFMA phase s (after that phase's last LDS read);
+// every wave waits for its memory operations at the end of the next VALU
+// phase, which reads no LDS, and the barrier closing that phase publishes the
+// block. Step s's buffer (s mod 3) is read in the four phases starting at
+// phase 2s, so the buffer refilled for step s + 2 (that of step s - 1) is
+// free by then.
+constexpr int FPS_KB = 128, FPS_VTP = FPS_KB + 4;
+constexpr int FPS_VT_CHUNKS = (80 * FPS_VTP * 2 / 16 + 63) / 64 * 64;  // 16-byte chunks per packed block
+
+// vt[b][h][kb] (FPS_VT_CHUNKS chunks): row r, key j at element r * FPS_VTP + j
+template <int DH>
+__global__ void __launch_bounds__(256) vt_pack_kernel(FlashParams prm, uint4* vt, int nkb) {
+  const int h = blockIdx.y, b = blockIdx.z, heads = gridDim.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nkb * FPS_VT_CHUNKS) return;
+  const int kb = idx / FPS_VT_CHUNKS, c = idx % FPS_VT_CHUNKS;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(prm.V) + b * prm.v_bs + h * prm.v_hs;
+  uint16_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int el = c * 8 + j, r = el / FPS_VTP, key = el % FPS_VTP;
+    const int gk = kb * FPS_KB + key;
+    uint16_t v = 0;
+    if (r < DH && key < FPS_KB && gk < prm.Nk) v = Vb[(int64_t)gk * DH + r];
+    else if (r == DH && key < FPS_KB) v = 0x3f80u;  // bf16 1.0
+    e[j] = v;
+  }
+  vt[((int64_t)(b * heads + h) * nkb + kb) * FPS_VT_CHUNKS + c] =
+      uint4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+            e[6] | ((uint32_t)e[7] << 16)};
+}
+
+template <int DH>
+__global__ void __launch_bounds__(FW_WAVES * 64, 1)
+    flash_bf16_pps(FlashParams prm, const uint4* __restrict__ vtp_all, int q_per_wg, int nkb) {
+  constexpr int FP_QT = PP_QT, FP_KB = FPS_KB;
+  constexpr int FP_KT = FP_KB / 16, FP_QPW = 16 * FP_QT, FP_Q = FW_WAVES * FP_QPW;
+  using P = BF16P<DH>;
+  constexpr int NDT = P::NDT, DCH = P::DCH;
+  static_assert(NDT * 16 == 80 && DH < 80, "packed V^T holds 80 rows with the ones row at DH");
+  constexpr int KCH = FP_KB * DCH;             // K chunks per block (rows are contiguous: a linear copy)
+  constexpr int BUFC = KCH + FPS_VT_CHUNKS;    // chunks per ring buffer
+  constexpr int NDMA = BUFC / 64;              // DMA instructions per block
+  static_assert(KCH % 64 == 0 && FPS_VT_CHUNKS % 64 == 0, "whole DMA instructions");
+  constexpr int DMA_PER_WAVE = (NDMA + 3) / 4;  // issued by the four waves of group 0
+  extern __shared__ uint4 fp_smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int h = blockIdx.y, b = blockIdx.z, heads = gridDim.y;
+  const int g = lane >> 4, lr = lane & 15;
+  const uint16_t* Qb = reinterpret_cast<const uint16_t*>(prm.Q) + b * prm.q_bs + h * prm.q_hs;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(prm.K) + b * prm.k_bs + h * prm.k_hs;
+  const uint4* VTb = vtp_all + (int64_t)(b * heads + h) * nkb * FPS_VT_CHUNKS;
+  const int qbeg = blockIdx.x * q_per_wg;
+  const int qend = min(prm.Nq, qbeg + q_per_wg);
+  const int Nk = prm.Nk;
+  const int last_kchunk = Nk * DCH - 1;
+  const int nq = (qend - qbeg + FP_Q - 1) / FP_Q;
+  const int S = nq * nkb;  // steps: (query block, key block)
+
+  // DMA of key block kb into ring buffer buf: instruction j < KCH/64 copies K
+  // chunks (clamped to the last real key), the rest the packed V^T block
+  auto dma = [&](int kb, int buf, int j) {
+    uint4* dst = fp_smem + buf * BUFC + j * 64;
+    if (j < KCH / 64) {
+      const int ch = min(kb * KCH + j * 64 + lane, last_kchunk);
+      PTDIT_GLDS16(reinterpret_cast<const char*>(Kb) + (size_t)ch * 16, dst);
+    } else {
+      PTDIT_GLDS16(VTb + (size_t)kb * FPS_VT_CHUNKS + (j - KCH / 64) * 64 + lane, dst);
+    }
+  };
+  auto dma_block_all = [&](int kb, int buf) {  // all eight waves (prologue)
+    for (int j = wave; j < NDMA; j += FW_WAVES) dma(kb, buf, j);
+  };
+  auto dma_block_g0 = [&](int kb, int buf) {  // group 0 only
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int j = wave + 4 * i;
+      if (j < NDMA) dma(kb, buf, j);
+    }
+  };
+
+  constexpr int NKF = DH / 32;
+  static_assert(DH % 32 == 8, "head dim 32k + 8");
+  struct QFr { uint4 v[NKF]; uint2 tail; };
+  QFr qf[FP_QT];
+  const uint32_t q_lane = (uint32_t)((lr * DH + 8 * g) * 2), q_tail = (uint32_t)((lr * DH + NKF * 32 + 4 * g) * 2);
+  auto load_qf = [&](int qblk) {
+    const int q0 = qblk + wave * FP_QPW;
+    const char* base = reinterpret_cast<const char*>(Qb + (int64_t)q0 * DH);
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      const bool ok = q0 + t * 16 + lr < qend;
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc)
+        qf[t].v[kc] = ok ? *reinterpret_cast<const uint4*>(base + q_lane + (t * 16 * DH + kc * 32) * 2)
+                         : uint4{0, 0, 0, 0};
+      qf[t].tail = ok && g < 2 ? *reinterpret_cast<const uint2*>(base + q_tail + t * 16 * DH * 2) : uint2{0, 0};
+    }
+  };
+
+  // prologue: Q of the first query block, key blocks of steps 0 and 1
+  load_qf(qbeg);
+  dma_block_all(0, 0);
+  if (S > 1) dma_block_all(1 % nkb, 1);
+  wait_vm_lgkm0<0>();
+  __syncthreads();
+
+  const float c2 = prm.sl2;
+  const bool tail_masked = Nk < nkb * FP_KB;
+
+  floatx4 sc[FP_QT][FP_KT];
+  uint32_t pk[FP_QT][FP_KT][2];
+  floatx4 o[FP_QT][NDT];
+  float m_run[FP_QT];
+
+  auto scores = [&](int buf) {
+    const uint4* ks = fp_smem + buf * BUFC;
+    struct KFr { uint4 v[NKF]; uint2 tail; };
+    KFr kf[2];
+    auto load_kf = [&](int kt, KFr& f) {
+      const int key = kt * 16 + lr;
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc) f.v[kc] = ks[key * DCH + kc * 4 + g];
+      f.tail = g < 2 ? reinterpret_cast<const uint2*>(&ks[key * DCH + NKF * 4])[g] : uint2{0, 0};
+    };
+    load_kf(0, kf[0]);
+#pragma unroll
+    for (int kt = 0; kt < FP_KT; ++kt) {
+      if (kt + 1 < FP_KT) load_kf(kt + 1, kf[(kt + 1) & 1]);
+      const KFr& f = kf[kt & 1];
+#pragma unroll
+      for (int t = 0; t < FP_QT; ++t) sc[t][kt] = mfma_bf16_k16(f.tail, qf[t].tail, zero4());
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc)
+#pragma unroll
+        for (int t = 0; t < FP_QT; ++t) sc[t][kt] = mfma_bf16(f.v[kc], qf[t].v[kc], sc[t][kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv = [&](int buf) {
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(fp_smem + buf * BUFC + KCH);
+    uint4 vf[2][NDT];
+    auto load_vf = [&](int u, uint4* f) {
+      const uint16_t* base = vt + lr * FPS_VTP + u * 32 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t* row = base + dt * 16 * FPS_VTP;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+        f[dt] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+    load_vf(0, vf[0]);
+#pragma unroll
+    for (int u = 0; u < FP_KT / 2; ++u) {
+      if (u + 1 < FP_KT / 2) load_vf(u + 1, vf[(u + 1) & 1]);
+#pragma unroll
+      for (int t = 0; t < FP_QT; ++t) {
+        const uint4 pf = uint4{pk[t][2 * u][0], pk[t][2 * u][1], pk[t][2 * u + 1][0], pk[t][2 * u + 1][1]};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] = mfma_bf16(vf[u & 1][dt], pf, o[t][dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto softmax = [&](int kb) {
+    if (kb == nkb - 1 && tail_masked) {
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool out = kb * FP_KB + kt * 16 + 4 * g + r >= Nk;
+#pragma unroll
+          for (int t = 0; t < FP_QT; ++t) sc[t][kt][r] = out ? -INFINITY : sc[t][kt][r];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      float mx = sc[t][0][0];
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[t][kt][r]);
+      mx = quad_max(mx);
+      float m_new = mx;
+      if (kb > 0) {
+        m_new = fmaxf(m_run[t], mx);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run[t]) != 0) {
+          const float alpha = fast_exp2((m_run[t] - m_new) * c2);
+#pragma unroll
+          for (int i = 0; i < NDT; ++i) o[t][i] *= alpha;
+        }
+      }
+      m_run[t] = m_new;
+      const float nmc = -m_new * c2;
+#pragma unroll
+      for (int kt = 0; kt < FP_KT; ++kt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = fast_exp2(fmaf(sc[t][kt][r], c2, nmc));
+        pk[t][kt][0] = pack_bf2(e[0], e[1]);
+        pk[t][kt][1] = pack_bf2(e[2], e[3]);
+      }
+    }
+  };
+  auto zero_o = [&]() {
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t)
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[t][i] = zero4();
+  };
+  auto store_o = [&](int qblk) {
+    constexpr int DT = DH / 16, GR = (DH % 16) / 4, EL = DH % 4;
+    const int q0 = qblk + wave * FP_QPW;
+    char* base = reinterpret_cast<char*>(reinterpret_cast<uint16_t*>(prm.O) + ((int64_t)b * prm.Nq + q0) * prm.D + h * DH);
+    const uint32_t o_lane = (uint32_t)((lr * prm.D + 4 * g) * 2);
+#pragma unroll
+    for (int t = 0; t < FP_QT; ++t) {
+      const float lsum = __shfl(o[t][DT][EL], GR * 16 + lr);
+      if (q0 + t * 16 + lr < qend) {
+        const float inv = 1.f / lsum;
+        char* row = base + o_lane + (uint32_t)(t * 16 * prm.D * 2);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+          if (i * 16 + 4 * g < DH)
+            store4(reinterpret_cast<uint16_t*>(row + i * 32), o[t][i][0] * inv, o[t][i][1] * inv, o[t][i][2] * inv,
+                   o[t][i][3] * inv);
+        }
+      }
+    }
+  };
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // group 1 runs one phase behind group 0
+  if (grp == 1) phase_end();
+  scores(0);
+  phase_end();
+  for (int s = 0; s < S; ++s) {
+    const int qi = s / nkb, kb = s - qi * nkb;
+    const int qblk = qbeg + qi * FP_Q;
+    const bool more = qi + 1 < nq;
+    // VALU phase: (next query block's Q, whose last scores are done,) softmax
+    // of step s; the DMA issued in the last MFMA phase (step s + 1's block)
+    // and the Q loads land before the barrier
+    if (kb == nkb - 1 && more) load_qf(qblk + FP_Q);
+    softmax(kb);
+    if (kb == 0) zero_o();
+    wait_vm_lgkm0<0>();
+    phase_end();
+    // MFMA phase: P V of step s (then the finished block's output), the
+    // scores of step s + 1, then (group 0) the DMA of step s + 2
+    pv(s % 3);
+    if (kb == nkb - 1) store_o(qblk);
+    if (s + 1 < S) scores((s + 1) % 3);
+    if (grp == 0 && s + 2 < S) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma_block_g0((s + 2) % nkb, (s + 2) % 3);
+    }
+    phase_end();
   }
   if (grp == 0) phase_end();
 }
@@ -1155,6 +1433,45 @@ static hipError_t run_flash_pp(const FlashDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DH>
+static hipError_t run_flash_pps(const FlashDesc& d, hipStream_t s) {
+  constexpr int FP_Q = FW_WAVES * 16 * PP_QT;
+  FlashParams p;
+  p.Q = d.Q; p.q_bs = d.q_bs; p.q_hs = d.q_hs;
+  p.K = d.K; p.k_bs = d.k_bs; p.k_hs = d.k_hs;
+  p.V = d.V; p.v_bs = d.v_bs; p.v_hs = d.v_hs;
+  p.O = d.O; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
+  p.sl2 = d.scale * LOG2E;
+  const int nkb = (d.Nk + FPS_KB - 1) / FPS_KB;
+  if (!d.vt || d.vt_bytes < flash_vt_bytes(d.B, d.heads, d.Nk)) return hipErrorInvalidValue;
+  uint4* vt = reinterpret_cast<uint4*>(d.vt);
+  hipLaunchKernelGGL((vt_pack_kernel<DH>), dim3((nkb * FPS_VT_CHUNKS + 255) / 256, d.heads, d.B), dim3(256), 0, s, p,
+                     vt, nkb);
+  const int pairs = d.B * d.heads;
+  int ranges = (256 + pairs - 1) / pairs;
+  const int qblocks = (d.Nq + FP_Q - 1) / FP_Q;
+  if (ranges > qblocks) ranges = qblocks;
+  if (ranges < 1) ranges = 1;
+  const int q_per_wg = (qblocks + ranges - 1) / ranges * FP_Q;
+  dim3 grid((d.Nq + q_per_wg - 1) / q_per_wg, d.heads, d.B);
+  constexpr int lds = 3 * (FPS_KB * DH / 8 + FPS_VT_CHUNKS) * 16;
+  static_assert(lds <= 160 * 1024, "LDS");
+  static bool attr_set = false;  // same value from every thread: a benign race
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_bf16_pps<DH>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((flash_bf16_pps<DH>), grid, dim3(FW_WAVES * 64), lds, s, p, vt, q_per_wg, nkb);
+  return hipGetLastError();
+}
+
+size_t flash_vt_bytes(int B, int heads, int Nk) {
+  if (Nk <= FP_MAXK) return 0;
+  return (size_t)B * heads * ((Nk + FPS_KB - 1) / FPS_KB) * FPS_VT_CHUNKS * 16;
+}
+
 hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s) {
   if (d.Nq == 0 || d.B == 0) return hipSuccess;
   if (!f32 && d.Nq >= 2048 && d.Nk > FS_MAXK && d.Nk <= FP_MAXK) {
@@ -1164,6 +1481,8 @@ hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s) {
     if (d.dh == 72) return run_flash_single<72>(d, s);
     if (d.dh == 64) return run_flash_single<64>(d, s);
   }
+  // more keys: streamed through LDS (needs the packed V^T scratch)
+  if (!f32 && d.Nq >= 2048 && d.dh == 72 && d.vt) return run_flash_pps<72>(d, s);
   if (!f32 && d.Nq >= 2048) {
     if (d.dh == 72) return run_flash_wide<72>(d, s);
     if (d.dh == 64) return run_flash_wide<64>(d, s);

@@ -115,4 +115,18 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 __device__ __forceinline__ float ld1(const uint16_t* p) { return bf2f(*p); }
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 
+// global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane l
+// lands at the wave-uniform LDS address lptr + 16 l.
+#define PTDIT_GLDS16(gptr, lptr)                                                                 \
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(gptr),       \
+                                   (void __attribute__((address_space(3)))*)(lptr), 16, 0, 0)
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n must be a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+
 }  // namespace ptdit

@@ -237,17 +237,7 @@ gemm_bf16_kernel(GemmParams p) {
 // (s_waitcnt vmcnt), then one barrier publishes the slice to all waves and
 // retires every read of the slot about to be refilled.
 // ----------------------------------------------------------------------------
-#define PTDIT_GLDS16(gptr, lptr)                                                                 \
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(gptr),       \
-                                   (void __attribute__((address_space(3)))*)(lptr), 16, 0, 0)
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
-// lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n must be a compile-time constant.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
-}
 template <int N>
 __device__ __forceinline__ void wait_vm_dyn(int n) {
   if constexpr (N == 0) {

@@ -46,8 +46,12 @@ struct FlashDesc {
   void* O;
   int B, heads, Nq, Nk, dh, D;
   float scale;
+  void* vt = nullptr;     // scratch for packed V^T blocks (bf16, more than 512 keys)
+  size_t vt_bytes = 0;
 };
 hipError_t launch_flash(const FlashDesc& d, int f32, hipStream_t s);
+// bytes of FlashDesc::vt that a bf16 launch with Nk keys needs (0: none)
+size_t flash_vt_bytes(int B, int heads, int Nk);
 
 // Window attention on head-major QKV [B][3][heads][Ntok][dh] with the grid
 // zero-padded to (Fp, Hp, Wp), rolled by -shift, partitioned into windows

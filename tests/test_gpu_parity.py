@@ -267,7 +267,10 @@ def test_window_edge_cases(P, kw):
 
 
 def test_one_proxy_and_many_proxies(P):
-    for kw in (dict(F=2, H=4, W=6, p=(2, 4, 6)), dict(H=20, W=30, p=(1, 1, 1))):
+    # 1 proxy; 600 proxies; 2400 proxies (>= 2048 queries on more than 512
+    # keys: proxy self-attention without packed V^T scratch, cross-attention
+    # with keys streamed through LDS)
+    for kw in (dict(F=2, H=4, W=6, p=(2, 4, 6)), dict(H=20, W=30, p=(1, 1, 1)), dict(H=48, W=50, p=(1, 1, 1))):
         wl = _wl(**kw)
         announce(f"proxies M={wl.M}")
         x = make_x(wl, seed=500)
@@ -283,16 +286,21 @@ def test_one_proxy_and_many_proxies(P):
 
 XATTN_KEYS = [((1, 48, 50), 1, 1.0), ((1, 48, 50), 127, 1.0), ((1, 48, 50), 128, 1.0), ((1, 48, 50), 129, 1.0),
               ((1, 60, 68), 255, 1.0), ((1, 48, 50), 256, 1.0), ((1, 32, 72), 257, 1.0), ((1, 48, 50), 384, 1.0),
-              ((1, 48, 50), 384, 3.0), ((1, 50, 41), 511, 1.0), ((1, 48, 50), 512, 3.0), ((1, 48, 50), 513, 1.0)]
+              ((1, 48, 50), 384, 3.0), ((1, 50, 41), 511, 1.0), ((1, 48, 50), 512, 3.0), ((1, 48, 50), 513, 1.0),
+              ((1, 48, 50), 640, 1.0), ((1, 60, 68), 864, 1.0), ((1, 48, 50), 1024, 3.0), ((1, 32, 72), 1152, 1.0),
+              ((1, 48, 50), 1153, 1.0)]
 
 
 @pytest.mark.parametrize("grid,nk,wscale", XATTN_KEYS,
                          ids=[f"{nk}_keys" + ("_peaked" if s > 1 else "") for _, nk, s in XATTN_KEYS])
 def test_xattn_key_counts(P, grid, nk, wscale):
-    """Token queries (>= 2048) against 1 .. 513 keys: up to 512 keys every key
-    of a head stays in LDS and key blocks of 128 (the last one partly masked)
-    go through the online softmax; beyond, keys stream through LDS. Weights
-    scaled by 3 (logits x9) give peaked scores whose running max moves between blocks."""
+    """Token queries (>= 2048) against 1 .. 1153 keys: up to 256 keys in one
+    pass; up to 512 every key of a head stays in LDS and key blocks of 128
+    (the last one partly masked) go through the online softmax; beyond, key
+    blocks stream through a ring of LDS buffers (queries span several query
+    blocks, so the ring wraps over the key blocks more than once). Weights
+    scaled by 3 (logits x9) give peaked scores whose running max moves
+    between blocks."""
     wl = _wl(F=grid[0], H=grid[1], W=grid[2], p=(1, 1, 1))
     announce(f"xattn keys={nk} queries={wl.N} wscale={wscale}")
     x = make_x(wl, seed=600 + nk)
