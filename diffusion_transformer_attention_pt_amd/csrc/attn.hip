@@ -58,11 +58,17 @@ struct BF16P {
       sm.vt[DH + i / (KEYS + 4)][i % (KEYS + 4)] = 0;
   }
 
-  // Stage chunk c (8 channels) of key slot s; NULL rows stage zeros.
+  // Staging of chunk c (8 channels) of key slot s in two steps, so that a
+  // thread's loads for all its chunks are in flight together: load() reads
+  // the K and V chunk (NULL rows give zeros), put() writes them to LDS.
+  struct Raw { uint4 k, v; };
+  __device__ static Raw load(int c, const T* krow, const T* vrow) {
+    return Raw{krow ? *reinterpret_cast<const uint4*>(krow + c * 8) : uint4{0, 0, 0, 0},
+               vrow ? *reinterpret_cast<const uint4*>(vrow + c * 8) : uint4{0, 0, 0, 0}};
+  }
   template <int KEYS>
-  __device__ static void stage(Smem<KEYS>& sm, int s, int c, const T* krow, const T* vrow) {
-    const uint4 kv = krow ? *reinterpret_cast<const uint4*>(krow + c * 8) : uint4{0, 0, 0, 0};
-    const uint4 vv = vrow ? *reinterpret_cast<const uint4*>(vrow + c * 8) : uint4{0, 0, 0, 0};
+  __device__ static void put(Smem<KEYS>& sm, int s, int c, const Raw& r) {
+    const uint4 kv = r.k, vv = r.v;
     sm.k[s * DCH + c] = kv;
     sm.vt[c * 8 + 0][s] = (uint16_t)(vv.x & 0xffff); sm.vt[c * 8 + 1][s] = (uint16_t)(vv.x >> 16);
     sm.vt[c * 8 + 2][s] = (uint16_t)(vv.y & 0xffff); sm.vt[c * 8 + 3][s] = (uint16_t)(vv.y >> 16);
@@ -70,14 +76,10 @@ struct BF16P {
     sm.vt[c * 8 + 6][s] = (uint16_t)(vv.w & 0xffff); sm.vt[c * 8 + 7][s] = (uint16_t)(vv.w >> 16);
   }
 
-  // Stage chunk c of V for key slots 4*kq .. 4*kq+3 (rows may be NULL -> 0),
+  // Write chunk c of V for key slots 4*kq .. 4*kq+3 (already loaded),
   // transposed in registers: each V^T row gets one 8-byte write.
   template <int KEYS>
-  __device__ static void stage_vquad(Smem<KEYS>& sm, int kq, int c, const T* const* rows) {
-    uint4 v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = rows[e] ? *reinterpret_cast<const uint4*>(rows[e] + c * 8) : uint4{0, 0, 0, 0};
+  __device__ static void put_vquad(Smem<KEYS>& sm, int kq, int c, const uint4* v) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sh = (j & 1) * 16;
@@ -152,12 +154,22 @@ struct F32P {
     for (int i = tid; i < PADC * KEYS; i += nt) sm.v[i / PADC][DH + i % PADC] = 0.f;
   }
 
+  struct Raw { float4 k0, k1, v0, v1; };
+  __device__ static Raw load(int c, const T* krow, const T* vrow) {
+    const float4 z = float4{0.f, 0.f, 0.f, 0.f};
+    return Raw{krow ? *reinterpret_cast<const float4*>(krow + c * 8) : z,
+               krow ? *reinterpret_cast<const float4*>(krow + c * 8 + 4) : z,
+               vrow ? *reinterpret_cast<const float4*>(vrow + c * 8) : z,
+               vrow ? *reinterpret_cast<const float4*>(vrow + c * 8 + 4) : z};
+  }
   template <int KEYS>
-  __device__ static void stage(Smem<KEYS>& sm, int s, int c, const T* krow, const T* vrow) {
+  __device__ static void put(Smem<KEYS>& sm, int s, int c, const Raw& r) {
+    const float kk[8] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w, r.k1.x, r.k1.y, r.k1.z, r.k1.w};
+    const float vv[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sm.k[s][c * 8 + e] = krow ? krow[c * 8 + e] : 0.f;
-      sm.v[s][c * 8 + e] = vrow ? vrow[c * 8 + e] : 0.f;
+      sm.k[s][c * 8 + e] = kk[e];
+      sm.v[s][c * 8 + e] = vv[e];
     }
   }
 
@@ -225,12 +237,24 @@ __global__ void __launch_bounds__(256) flash_kernel(FlashParams prm) {
   for (int i = 0; i < P::NDT; ++i) o[i] = zero4();
 
   for (int k0 = 0; k0 < prm.Nk; k0 += KB) {
-    __syncthreads();
-    for (int idx = tid; idx < KB * P::DCH; idx += NT) {
+    // every load of the block first, then the LDS writes (after the barrier
+    // that retires the previous block's reads)
+    constexpr int ITEMS = KB * P::DCH, PER = (ITEMS + NT - 1) / NT;
+    typename P::Raw raw[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
       const int s = idx / P::DCH, c = idx - s * P::DCH;
       const int gk = k0 + s;
-      const bool ok = gk < prm.Nk;
-      P::stage(sm, s, c, ok ? Kb + (int64_t)gk * DH : nullptr, ok ? Vb + (int64_t)gk * DH : nullptr);
+      const bool ok = idx < ITEMS && gk < prm.Nk;
+      raw[i] = P::load(c, ok ? Kb + (int64_t)gk * DH : nullptr, ok ? Vb + (int64_t)gk * DH : nullptr);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      if (idx < ITEMS) P::put(sm, s, c, raw[i]);
     }
     __syncthreads();
     floatx4 sc[NTILE];
@@ -1259,38 +1283,65 @@ __global__ void __launch_bounds__(NTILE * 64) window_kernel(WindowParams prm) {
   const T* bk = bias ? bias + prm.D + h * DH : nullptr;
   const T* bv = bias ? bias + 2 * prm.D + h * DH : nullptr;
 
-  if constexpr (P::TPV == 2) {
-    // bf16: K chunk by chunk, V four slots at a time (transposed in registers)
-    for (int idx = tid; idx < KEYS * P::DCH; idx += NT) {
-      const int s = idx / P::DCH, c = idx - s * P::DCH;
-      const int tok = tok_s[s];
-      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
-      sm.k[s * P::DCH + c] = kr ? *reinterpret_cast<const uint4*>(kr + c * 8) : uint4{0, 0, 0, 0};
-    }
-    for (int idx = tid; idx < P::DCH * (KEYS / 4); idx += NT) {
-      const int c = idx / (KEYS / 4), kq = idx - c * (KEYS / 4);
-      const T* rows[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = tok_s[kq * 4 + e];
-        rows[e] = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
-      }
-      P::stage_vquad(sm, kq, c, rows);
-    }
-  } else {
-    for (int idx = tid; idx < KEYS * P::DCH; idx += NT) {
-      const int s = idx / P::DCH, c = idx - s * P::DCH;
-      const int tok = tok_s[s];
-      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
-      const T* vr = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
-      P::stage(sm, s, c, kr, vr);
-    }
-  }
-  __syncthreads();
-
+  // Every global load of the window (K, V, this lane's query) is issued
+  // before the first LDS write, so the thread waits for one latency.
   const int qs = wave * 16 + (lane & 15);
   const int qtok = tok_s[qs], qlab = lab_s[qs];
+  if constexpr (P::TPV == 2) {
+    // bf16: K chunk by chunk, V four slots at a time (transposed in registers)
+    constexpr int KI = (KEYS * P::DCH + NT - 1) / NT, VI = (P::DCH * (KEYS / 4) + NT - 1) / NT;
+    uint4 kreg[KI], vreg[VI][4];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = tid + i * NT;
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      const int tok = idx < KEYS * P::DCH ? tok_s[s] : -2;
+      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
+      kreg[i] = kr ? *reinterpret_cast<const uint4*>(kr + c * 8) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int idx = tid + i * NT;
+      const int c = idx / (KEYS / 4), kq = idx - c * (KEYS / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = idx < P::DCH * (KEYS / 4) ? tok_s[kq * 4 + e] : -2;
+        const T* vr = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
+        vreg[i][e] = vr ? *reinterpret_cast<const uint4*>(vr + c * 8) : uint4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < KEYS * P::DCH) sm.k[idx] = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int idx = tid + i * NT;
+      const int c = idx / (KEYS / 4), kq = idx - c * (KEYS / 4);
+      if (idx < P::DCH * (KEYS / 4)) P::put_vquad(sm, kq, c, vreg[i]);
+    }
+  } else {
+    constexpr int ITEMS = KEYS * P::DCH, PER = (ITEMS + NT - 1) / NT;
+    typename P::Raw raw[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      const int tok = idx < ITEMS ? tok_s[s] : -2;
+      const T* kr = tok >= 0 ? Kb + (int64_t)tok * DH : (tok == -1 ? bk : nullptr);
+      const T* vr = tok >= 0 ? Vb + (int64_t)tok * DH : (tok == -1 ? bv : nullptr);
+      raw[i] = P::load(c, kr, vr);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int s = idx / P::DCH, c = idx - s * P::DCH;
+      if (idx < ITEMS) P::put(sm, s, c, raw[i]);
+    }
+  }
   const auto qf = P::load_q(qtok >= 0 ? Qb + (int64_t)qtok * DH : nullptr, lane);
+  __syncthreads();
   floatx4 sc[NTILE2];
 #pragma unroll
   for (int t = 0; t < NTILE2; ++t) sc[t] = P::score(sm, qf, t, lane);
