@@ -38,6 +38,12 @@ Readings where the pages are silent (all listed in the design doc):
             window w and shift s the region of coordinate k is 0 if k < L-w,
             1 if L-w <= k < L-s, 2 otherwise; a query sees a key only if their
             regions agree on every axis; excluded pairs get weight exactly 0.
+  R-select  the proxy-extraction ablation's Top-Left and Random proxies (and
+            get_proxy_token's mode "first", code-correspondence excerpt 1)
+            take one token of the window as its proxy: the token at the
+            window-local offset o = (dt*p_h + di)*p_w + dj (row-major inside
+            the window, as R-order), o = 0 for Top-Left, a drawn offset per
+            window for Random; offsets are taken modulo P.
 """
 from __future__ import annotations
 
@@ -46,7 +52,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "linear", "attention", "mha", "proxy_grid", "proxy_pool", "proxy_pool_f32",
+    "linear", "attention", "mha", "proxy_grid", "proxy_pool", "proxy_pool_f32", "proxy_select",
     "round_bf16_rne", "proxy_sa", "proxy_xattn", "pad_grid", "partition",
     "unpartition", "roll3d", "region_labels", "window_sa", "shift_window_sa",
     "block", "count_core_macs", "count_projection_macs",
@@ -140,6 +146,28 @@ def proxy_pool(x: np.ndarray, grid: Grid, p: Sequence[int]) -> np.ndarray:
     FT, HI, WJ = proxy_grid(grid, p)
     xg = x.reshape(B, FT, p[0], HI, p[1], WJ, p[2], D)
     return xg.mean(axis=(2, 4, 6)).reshape(B, FT * HI * WJ, D)
+
+
+def proxy_select(x: np.ndarray, grid: Grid, p: Sequence[int],
+                 offsets: Optional[np.ndarray] = None) -> np.ndarray:
+    """One token per window as its proxy (reading R-select): the alternative
+    to Averaging in the proxy-extraction ablation (section 3, ablation notes).
+
+    x: [B, N, D]; offsets: [B, M] window-local offsets (taken modulo P) or
+    None for every window's top-left token. Returns [B, M, D] (float64 values
+    of the selected tokens, no arithmetic).
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    FT, HI, WJ = proxy_grid(grid, p)
+    P = p[0] * p[1] * p[2]
+    xg = x.reshape(B, FT, p[0], HI, p[1], WJ, p[2], D)
+    # [B, M, P, D]: the window's tokens in row-major (dt, di, dj) order
+    win = xg.transpose(0, 1, 3, 5, 2, 4, 6, 7).reshape(B, FT * HI * WJ, P, D)
+    if offsets is None:
+        return win[:, :, 0, :].copy()
+    o = np.mod(np.asarray(offsets, dtype=np.int64), P).reshape(B, FT * HI * WJ)
+    return np.take_along_axis(win, o[:, :, None, None], axis=2)[:, :, 0, :]
 
 
 def proxy_pool_f32(x: np.ndarray, grid: Grid, p: Sequence[int]) -> np.ndarray:
@@ -316,14 +344,18 @@ def shift_window_sa(x: np.ndarray, grid: Grid, win: Sequence[int], shift: Sequen
 
 def block(x: np.ndarray, grid: Grid, p: Sequence[int], win: Sequence[int],
           shift: Sequence[int], weights: Sequence[Weights], heads: int,
-          pool: str = "f64") -> Dict[str, np.ndarray]:
+          pool: str = "f64", offsets: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """GIIM then TCM, in the order of excerpt 2 (PT-Block forward).
 
     weights = [proxy SA, cross-attention, WSA, SWSA]. pool="f64" uses the
     float64 window mean; pool="bf16" uses the kernel-precision mean rounded to
-    bf16 (what a bf16 proxy tensor holds). Returns every intermediate.
+    bf16 (what a bf16 proxy tensor holds); pool="select" takes one token per
+    window (reading R-select; offsets None: top-left). Returns every
+    intermediate.
     """
-    if pool == "f64":
+    if pool == "select":
+        P = proxy_select(x, grid, p, offsets)
+    elif pool == "f64":
         P = proxy_pool(x, grid, p)
     elif pool == "bf16":
         P = _f64(round_bf16_rne(proxy_pool_f32(x, grid, p)))

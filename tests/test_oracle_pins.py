@@ -102,6 +102,72 @@ def test_pool_f64_bruteforce_and_global_mean():
     np.testing.assert_allclose(got.mean(axis=1), x.mean(axis=1), rtol=0, atol=1e-14)
 
 
+# ----------------------------------------------------------------------------- proxy selection (R-select)
+
+@pytest.mark.parametrize("grid,p", [((4, 6, 9), (2, 3, 3)), ((1, 8, 8), (1, 4, 4)), ((3, 5, 7), (1, 1, 1)),
+                                    ((2, 4, 6), (2, 4, 6))])
+def test_select_is_a_strided_slice(grid, p):
+    """Offset o = (dt*p_h + di)*p_w + dj selects the strided slice
+    x[dt::p_t, di::p_h, dj::p_w] (numpy basic slicing), for every o; o = 0 /
+    None is the top-left token of each window."""
+    rng = np.random.default_rng(11)
+    B, D = 2, 8
+    x = rng.standard_normal((B, int(np.prod(grid)), D))
+    xg = x.reshape(B, *grid, D)
+    M = int(np.prod(O.proxy_grid(grid, p)))
+    np.testing.assert_array_equal(O.proxy_select(x, grid, p),
+                                  xg[:, ::p[0], ::p[1], ::p[2]].reshape(B, M, D))
+    for dt in range(p[0]):
+        for di in range(p[1]):
+            for dj in range(p[2]):
+                o = (dt * p[1] + di) * p[2] + dj
+                got = O.proxy_select(x, grid, p, np.full((B, M), o))
+                np.testing.assert_array_equal(got, xg[:, dt::p[0], di::p[1], dj::p[2]].reshape(B, M, D))
+
+
+def test_select_offsets_per_window_bruteforce_and_mean():
+    """Per-window offsets against a scalar loop over the grid (offsets taken
+    modulo P, negative ones wrap); and the mean over all P offsets of the
+    selections is the window average."""
+    grid, p = (4, 6, 6), (2, 3, 2)
+    rng = np.random.default_rng(12)
+    B, D = 2, 4
+    x = rng.standard_normal((B, int(np.prod(grid)), D))
+    FT, HI, WJ = O.proxy_grid(grid, p)
+    P = p[0] * p[1] * p[2]
+    offs = rng.integers(-2 * P, 3 * P, size=(B, FT * HI * WJ))
+    got = O.proxy_select(x, grid, p, offs)
+    for b in range(B):
+        for T in range(FT):
+            for I in range(HI):
+                for J in range(WJ):
+                    m = (T * HI + I) * WJ + J
+                    o = int(offs[b, m]) % P
+                    dt, rem = divmod(o, p[1] * p[2])
+                    di, dj = divmod(rem, p[2])
+                    n = ((T * p[0] + dt) * grid[1] + I * p[1] + di) * grid[2] + J * p[2] + dj
+                    np.testing.assert_array_equal(got[b, m], x[b, n])
+    M = FT * HI * WJ
+    allsel = sum(O.proxy_select(x, grid, p, np.full((B, M), o)) for o in range(P)) / P
+    np.testing.assert_allclose(allsel, O.proxy_pool(x, grid, p), rtol=1e-12, atol=1e-12)
+
+
+def test_block_with_selected_proxies_matches_bruteforce():
+    """The block with top-left proxies equals the scalar brute force fed the
+    same proxies: pool='select' changes only the proxy extraction."""
+    wl = tiny("sel", B=1, F=2, H=4, W=4, D=8, heads=2, p=(2, 2, 2), win=(2, 4, 4), shift=(1, 2, 2))
+    x = make_x(wl, seed=31)
+    ws = make_all_weights(wl)
+    got = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads, pool="select")
+    P = O.proxy_select(x, wl.grid, wl.p)
+    np.testing.assert_array_equal(got["P"], P)
+    P2 = O.proxy_sa(P, ws[0], wl.heads)
+    x1 = O.proxy_xattn(x, P2, ws[1], wl.heads)
+    np.testing.assert_allclose(got["x1"], x1, rtol=1e-12, atol=1e-12)
+    # and the mean-pooled block differs (the variants are distinct)
+    assert not np.allclose(O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)["x3"], got["x3"])
+
+
 def test_pool_f32_close_to_f64():
     wl = tiny(H=32, W=32, D=64, p=(1, 8, 8))
     x = make_x(wl, seed=12)
