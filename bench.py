@@ -1,7 +1,7 @@
 """Benchmark: PT-block attention core (GIIM + TCM) tokens/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload img2048]
-                    [--no-cpu-baseline] [--breakdown]
+                    [--proxy-mode mean|first|random] [--no-cpu-baseline] [--breakdown]
 
 A step is one forward of the whole attention core of one PT-DiT block
 (proxy pooling, proxy self-attention, token->proxy cross-attention, window
@@ -96,6 +96,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img2048")
+    ap.add_argument("--proxy-mode", default="mean", choices=["mean", "first", "random"],
+                    help="proxy extraction: window average (the default of the method), top-left token, "
+                         "or a drawn token per window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -110,7 +113,7 @@ def main() -> int:
     import torch
     import diffusion_transformer_attention_pt_amd as P
     from diffusion_transformer_attention_pt_amd import _lib
-    from synth_inputs import WORKLOADS, make_all_weights, make_x
+    from synth_inputs import WORKLOADS, make_all_weights, make_proxy_offsets, make_x
 
     wl = WORKLOADS[args.workload]
     prec = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -123,8 +126,10 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     x = torch.from_numpy(make_x(wl)).to(prec).to(dev)
+    offs = torch.from_numpy(make_proxy_offsets(wl)) if args.proxy_mode == "random" else None
     blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift,
-                             make_all_weights(wl), prec=prec, device=dev)
+                             make_all_weights(wl), prec=prec, device=dev, proxy_mode=args.proxy_mode,
+                             proxy_offsets=offs)
     flops = blk.flops()
 
     for _ in range(args.warmup):
@@ -186,7 +191,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {wl.B}, grid {wl.F}x{wl.H}x{wl.W} (N={wl.N}), "
                                f"D={wl.D}, {wl.heads} heads, proxy window {wl.p}, TCM window {wl.win} "
-                               f"shift {wl.shift}",
+                               f"shift {wl.shift}, proxies: {args.proxy_mode}",
                    "batch": wl.B, "tokens": wl.N, "D": wl.D, "heads": wl.heads,
                    "gflop_per_step": round(flops["total"] / 1e9, 3)},
         "step_ms_p10_p50_p90": [round(quant(0.1), 4), round(quant(0.5), 4), round(quant(0.9), 4)],
@@ -207,7 +212,9 @@ def main() -> int:
         B, N, M, D = wl.B, wl.N, wl.M, wl.D
         L = wl.win[0] * wl.win[1] * wl.win[2]
         es = 2 if prec == torch.bfloat16 else 4
-        work = {"pool": ("GB/s", B * N * D * es + B * M * D * 4),
+        # (the selection variants read only the selected tokens)
+        pool_in = B * N * D * es if args.proxy_mode == "mean" else B * M * D * es
+        work = {"pool": ("GB/s", pool_in + B * M * D * 4),
                 "gemm_proxy": ("TFLOP/s", 2 * B * M * D * 6 * D),
                 "gemm_q": ("TFLOP/s", 2 * B * N * D * D),
                 "attn_flash": ("TFLOP/s", 2 * B * D * (2 * M * M + 2 * N * M)),

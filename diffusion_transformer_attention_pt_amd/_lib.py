@@ -25,7 +25,7 @@ STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",
           -7: "PTDIT_ERR_HIP", -8: "PTDIT_ERR_ALIAS"}
 
-EXPORTED = ["ptdit_linear", "ptdit_proxy_pool", "ptdit_proxy_sa", "ptdit_proxy_xattn",
+EXPORTED = ["ptdit_linear", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_xattn",
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
             "ptdit_trace_disable"]
@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "ptdit_linear": [vp, i32, i64, i32, i32, vp, vp, vp, i32, vp, i32, i32, vp],
         "ptdit_proxy_pool": [vp, i32, G, W3, vp, i32, vp],
+        "ptdit_proxy_select": [vp, i32, G, W3, vp, vp, i32, vp],
         "ptdit_proxy_sa": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
         "ptdit_proxy_xattn": [vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_window_sa": [vp, vp, i32, G, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
@@ -175,6 +176,26 @@ def linear(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None,
     st = lib.ptdit_linear(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(b), _ptr(residual),
                           r_dt, _ptr(out), _dt(out.dtype), _dt(w.dtype), _stream())
     _check("ptdit_linear", st)
+    return out
+
+
+def proxy_select(x: torch.Tensor, grid: Sequence[int], p: Sequence[int],
+                 offsets: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grid = (B, F, H, W, D, heads); x [B, N, D] -> proxies [B, M, D], one
+    token per window (offsets: int32 [B, M] window-local offsets, or None for
+    the top-left token)."""
+    lib = load()
+    B, F, H, W, D, _ = grid
+    M = (F // p[0]) * (H // p[1]) * (W // p[2]) if all(p) else 0
+    if offsets is not None:
+        if offsets.dtype != torch.int32 or offsets.numel() != B * M:
+            raise ValueError("offsets must be int32 [B, M]")
+    if out is None:
+        out = torch.empty(B, M, D, dtype=out_dtype or x.dtype, device=x.device)
+    st = lib.ptdit_proxy_select(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*p), _ptr(offsets), _ptr(out),
+                                _dt(out.dtype), _stream())
+    _check("ptdit_proxy_select", st)
     return out
 
 

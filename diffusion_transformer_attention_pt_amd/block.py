@@ -8,6 +8,11 @@ excerpt 2 (PT-Block forward) with Eq. GIIM and Eq. TCM of section 3:
     x2 = x1 + WSA(x1)                      ptdit_window_sa
     x3 = x2 + SWSA(x2)                     ptdit_shift_window_sa
 
+Proxy extraction is the window average by default (proxy_mode="mean");
+"first" takes each window's top-left token and "random" the token at a
+caller-drawn window-local offset (proxy_offsets, int32 [B, M]), the two
+alternatives of the pages' proxy-extraction ablation (ptdit_proxy_select).
+
 With bf16 precision the block input is bf16, the residual stream
 (P, P', x1, x2, x3) is kept in fp32 and every projection reads its operand
 rounded to bf16; x1 and x2 also get a bf16 copy from the epilogue that
@@ -28,13 +33,21 @@ from ._lib import AttnWeights
 class PTBlockAttention:
     def __init__(self, B: int, grid: Sequence[int], D: int, heads: int, p: Sequence[int],
                  win: Sequence[int], shift: Sequence[int], weights: Sequence[dict],
-                 prec: torch.dtype = torch.bfloat16, device="cuda"):
+                 prec: torch.dtype = torch.bfloat16, device="cuda", proxy_mode: str = "mean",
+                 proxy_offsets: Optional[torch.Tensor] = None):
         self.B = B
         self.F, self.H, self.W = grid
         self.D, self.heads = D, heads
         self.p, self.win, self.shift = tuple(p), tuple(win), tuple(shift)
         self.prec = prec
         self.device = torch.device(device)
+        if proxy_mode not in ("mean", "first", "random"):
+            raise ValueError(f"proxy_mode {proxy_mode!r}")
+        if (proxy_mode == "random") != (proxy_offsets is not None):
+            raise ValueError("proxy_offsets go with proxy_mode='random' (and only with it)")
+        self.proxy_mode = proxy_mode
+        self.proxy_offsets = (proxy_offsets.to(device=self.device, dtype=torch.int32).contiguous()
+                              if proxy_offsets is not None else None)
         self.N = self.F * self.H * self.W
         self.M = (self.F // p[0]) * (self.H // p[1]) * (self.W // p[2])
         self.g = (B, self.F, self.H, self.W, D, heads)
@@ -57,7 +70,10 @@ class PTBlockAttention:
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         g, w = self.g, self.weights
-        _lib.proxy_pool(x, g, self.p, out=self.P)
+        if self.proxy_mode == "mean":
+            _lib.proxy_pool(x, g, self.p, out=self.P)
+        else:
+            _lib.proxy_select(x, g, self.p, self.proxy_offsets, out=self.P)
         _lib.proxy_sa(self.P, self.heads, w[0], residual=True, ws=self.ws, out=self.P2)
         _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=self.ws, out=self.x1, out_lowp=self.x1_lowp)
         _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2,

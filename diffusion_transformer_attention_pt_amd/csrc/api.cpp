@@ -251,6 +251,33 @@ ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptd
   return hip_status(launch_pool(d, stream));
 }
 
+ptdit_status ptdit_proxy_select(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,
+                                const int32_t* offsets, void* proxies, ptdit_dtype out_dt,
+                                hipStream_t stream) {
+  if (!valid_dtype(x_dt) || !valid_dtype(out_dt)) return PTDIT_ERR_DTYPE;
+  if (g.B < 0 || g.F < 0 || g.H < 0 || g.W < 0 || g.D <= 0 || g.D % 8) return PTDIT_ERR_SHAPE;
+  if (p.t <= 0 || p.h <= 0 || p.w <= 0) return PTDIT_ERR_SHAPE;
+  if (g.F % p.t || g.H % p.h || g.W % p.w) return PTDIT_ERR_DIVISIBILITY;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  if (N > (int64_t)1 << 30) return PTDIT_ERR_SHAPE;
+  const int64_t M = N / ((int64_t)p.t * p.h * p.w);
+  if ((int64_t)g.B * M > INT32_MAX) return PTDIT_ERR_SHAPE;
+  if ((int64_t)g.B * M == 0) return PTDIT_OK;
+  if (!x || !proxies) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(proxies) || ((uintptr_t)offsets & 3)) return PTDIT_ERR_ALIGN;
+  const size_t pb = g.B * M * g.D * esize(out_dt);
+  if (overlaps(proxies, pb, x, g.B * N * g.D * esize(x_dt)) ||
+      overlaps(proxies, pb, offsets, (size_t)g.B * M * sizeof(int32_t)))
+    return PTDIT_ERR_ALIAS;
+  PoolDesc d;
+  d.x = x; d.x_f32 = x_dt == PTDIT_F32;
+  d.out = proxies; d.out_f32 = out_dt == PTDIT_F32;
+  d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D;
+  d.pt = p.t; d.ph = p.h; d.pw = p.w;
+  TraceScope ts(PTDIT_K_POOL, stream);
+  return hip_status(launch_select(d, offsets, stream));
+}
+
 ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, int32_t M,
                             int32_t D, int32_t heads, const ptdit_attn_w* w,
                             int32_t add_residual, void* out, ptdit_dtype out_dt,

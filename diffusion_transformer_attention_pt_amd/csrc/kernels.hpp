@@ -29,6 +29,8 @@ struct PoolDesc {
   int pt, ph, pw;
 };
 hipError_t launch_pool(const PoolDesc& d, hipStream_t s);
+// one token per window: offsets [B][M] (window-local, taken mod P) or null
+hipError_t launch_select(const PoolDesc& d, const int32_t* offsets, hipStream_t s);
 
 struct RollDesc {
   const void* x; void* y; int f32;

@@ -185,6 +185,54 @@ hipError_t launch_pool(const PoolDesc& d, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
+// Proxy selection: one thread per 8 channels of one proxy copies the chunk of
+// the window token at the proxy's offset (bf16 -> fp32 exact, fp32 -> bf16
+// rounded to nearest even, the same rounding as the pooled proxies).
+// ----------------------------------------------------------------------------
+template <typename TX, typename TO>
+__global__ void __launch_bounds__(256) select_kernel(PoolParams p, const int32_t* offsets) {
+  const int C = p.D / 8;
+  const int M = p.FT * p.HI * p.WJ;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)p.B * M * C) return;
+  const int cx = (int)(gid % C);
+  const int64_t bm = gid / C;
+  const int b = (int)(bm / M), m = (int)(bm % M);
+  const int T = m / (p.HI * p.WJ), I = (m / p.WJ) % p.HI, J = m % p.WJ;
+  const int P = p.pt * p.ph * p.pw;
+  int o = 0;
+  if (offsets) {
+    o = offsets[bm] % P;
+    o += o < 0 ? P : 0;
+  }
+  const int dt = o / (p.ph * p.pw), di = (o / p.pw) % p.ph, dj = o % p.pw;
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const int64_t n = ((int64_t)(T * p.pt + dt) * p.H + (I * p.ph + di)) * p.W + (J * p.pw + dj);
+  float v[8];
+  Vec8<TX>::load(reinterpret_cast<const TX*>(p.x) + ((int64_t)b * N + n) * p.D + cx * 8, v);
+  Vec8<TO>::store(reinterpret_cast<TO*>(p.out) + bm * p.D + cx * 8, v);
+}
+
+hipError_t launch_select(const PoolDesc& d, const int32_t* offsets, hipStream_t s) {
+  PoolParams p;
+  p.x = d.x; p.out = d.out;
+  p.B = d.B; p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D;
+  p.pt = d.pt; p.ph = d.ph; p.pw = d.pw;
+  p.FT = d.F / d.pt; p.HI = d.H / d.ph; p.WJ = d.W / d.pw;
+  const int64_t total = (int64_t)p.B * p.FT * p.HI * p.WJ * (p.D / 8);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (d.x_f32) {
+    if (d.out_f32) hipLaunchKernelGGL((select_kernel<float, float>), grid, dim3(256), 0, s, p, offsets);
+    else hipLaunchKernelGGL((select_kernel<float, uint16_t>), grid, dim3(256), 0, s, p, offsets);
+  } else {
+    if (d.out_f32) hipLaunchKernelGGL((select_kernel<uint16_t, float>), grid, dim3(256), 0, s, p, offsets);
+    else hipLaunchKernelGGL((select_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s, p, offsets);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
 // 3D cyclic roll: y[t,i,j] = x[(t+st) mod F, (i+sh) mod H, (j+sw) mod W].
 // One thread per 16-byte vector; shifts arrive already in [0, extent).
 // ----------------------------------------------------------------------------

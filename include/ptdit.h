@@ -136,6 +136,27 @@ ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptd
                               void* proxies, ptdit_dtype out_dt, hipStream_t stream);
 
 /*
+ * ptdit_proxy_select -- proxy extraction by one token per window instead of
+ * the average: the Top-Left and Random rows of the proxy-extraction ablation
+ * (section 3, ablation notes) and get_proxy_token's mode "first"
+ * (code-correspondence excerpt 1).
+ *   x        [B][N][D], dtype x_dt (BF16 or F32)
+ *   offsets  [B][M] int32 device array, or NULL for every window's top-left
+ *            token. Proxy m = (T, I, J) of batch b is the token
+ *            (T*p_t+dt, I*p_h+di, J*p_w+dj) with window-local offset
+ *            o = (dt*p_h + di)*p_w + dj = offsets[b][m] mod P, P =
+ *            p_t*p_h*p_w (any int32 is accepted; negative values wrap).
+ *            Random proxies pass offsets the caller drew.
+ *   proxies  [B][M][D], dtype out_dt: a copy of the selected tokens (bf16 to
+ *            fp32 exact; fp32 to bf16 rounds to nearest, ties even).
+ * Requires p to divide (F, H, W) (else PTDIT_ERR_DIVISIBILITY), D % 8 == 0.
+ * Caller owns every buffer; proxies must not overlap x or offsets.
+ */
+ptdit_status ptdit_proxy_select(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,
+                                const int32_t* offsets, void* proxies, ptdit_dtype out_dt,
+                                hipStream_t stream);
+
+/*
  * ptdit_proxy_sa -- the proxy self-attention of GIIM (proxy_attn1 in the
  * code-correspondence table; excerpt 2 adds its input back):
  *   out = MHA(P, P) (+ P when add_residual != 0).

@@ -156,6 +156,16 @@ def make_weights(wl: Workload, attn: int, seed_base: int | None = None,
     return out
 
 
+def make_proxy_offsets(wl: Workload, seed: int | None = None) -> np.ndarray:
+    """Window-local token offsets for random proxy extraction, int32 [B, M],
+    uniform over the P = p_t*p_h*p_w tokens of each window (the draws the
+    Random variant makes, passed to both sides as inputs)."""
+    s = 1000 * wl.index + 999 if seed is None else seed
+    g = np.random.Generator(np.random.PCG64(s))
+    P = wl.p[0] * wl.p[1] * wl.p[2]
+    return g.integers(0, P, size=(wl.B, wl.M), dtype=np.int32)
+
+
 def make_all_weights(wl: Workload, **kw) -> List[Dict[str, np.ndarray]]:
     return [make_weights(wl, a, **kw) for a in range(4)]
 

@@ -116,6 +116,16 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.ptdit_proxy_sa(fake, 0, 1, 256, 1152, 16, None, 1, fake, 0, fake, 1 << 30, 0, None) == -1
     # linear: d_in not a multiple of 8
     assert lib.ptdit_linear(fake, 0, 10, 12, 16, fake, None, None, 0, fake, 0, 0, None) == -2
+    # selection: divisibility, dtype, D, nulls, alignment of the offsets, offsets inside the output
+    sel = lib.ptdit_proxy_select
+    assert sel(fake, 0, g, Win3(1, 3, 3), None, fake, 0, None) == -3
+    assert sel(fake, 3, g, Win3(1, 2, 2), None, fake, 0, None) == -4
+    assert sel(fake, 0, Grid(1, 1, 16, 16, 1150, 16), Win3(1, 2, 2), None, fake, 0, None) == -2
+    assert sel(fake, 0, g, Win3(0, 2, 2), None, fake, 0, None) == -2
+    assert sel(None, 0, g, Win3(1, 2, 2), None, fake, 0, None) == -1
+    assert sel(fake, 0, g, Win3(1, 2, 2), ctypes.c_void_p((1 << 41) + 2), far, 0, None) == -5
+    assert sel(fake, 0, g, Win3(1, 2, 2), ctypes.c_void_p((1 << 40) + 64), far, 0, None) == -8
+    assert sel(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, None, 0, None) == 0
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
     assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),

@@ -13,7 +13,8 @@ import torch
 
 import oracle as O
 from gpu_util import announce, assert_close, dev, host
-from synth_inputs import (ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_weights, make_x, round_bf16,
+from synth_inputs import (ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_proxy_offsets,
+                          make_weights, make_x, round_bf16,
                           tiny)
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +69,59 @@ def test_pool_bit_exact(P, case, in_dt, out_dt):
         ref = O.round_bf16_rne(ref)
     g = got.float().cpu().numpy()
     assert np.array_equal(g.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- proxy selection (bit-exact)
+
+SELECT_CASES = ["img256_f32", "img1024", "img2048", "video16x30x45", "video16x30x45_pf4", "mview24x32x32"]
+
+
+@pytest.mark.parametrize("name", SELECT_CASES)
+@pytest.mark.parametrize("in_dt,out_dt", [(BF16, BF16), (BF16, F32), (F32, F32), (F32, BF16)])
+@pytest.mark.parametrize("mode", ["first", "random"])
+def test_select_bit_exact(P, name, in_dt, out_dt, mode):
+    """One token per window: the selected tokens exactly (fp32 -> bf16 rounds
+    to nearest even on both sides). Random offsets include values outside
+    [0, P), negative ones too, which both sides take modulo P."""
+    wl = WORKLOADS[name]
+    announce(f"select {name} {mode} {in_dt}->{out_dt}")
+    x = make_x(wl.scaled(dtype="bf16" if in_dt == BF16 else "f32"), seed=140 + wl.index)
+    offs = None
+    if mode == "random":
+        offs = make_proxy_offsets(wl, seed=150 + wl.index).astype(np.int64)
+        Pn = wl.p[0] * wl.p[1] * wl.p[2]
+        offs[..., ::7] += 3 * Pn
+        offs[..., 3::11] -= 5 * Pn
+        offs = offs.astype(np.int32)
+    got = P.proxy_select(dev(x, in_dt), _grid(wl), wl.p,
+                         None if offs is None else torch.from_numpy(offs).cuda(), out_dtype=out_dt)
+    ref = O.proxy_select(x, wl.grid, wl.p, offs).astype(np.float32)
+    if out_dt == BF16:
+        ref = O.round_bf16_rne(ref)
+    g = got.float().cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("name,mode", [("img1024", "first"), ("img1024", "random"),
+                                       ("video16x30x45_pf4", "random"), ("img256_f32", "first")])
+def test_block_with_selected_proxies(P, name, mode):
+    """The whole block with top-left or random proxies against the oracle's
+    block fed the same offsets."""
+    wl = WORKLOADS[name]
+    prec = _prec(wl)
+    announce(f"block {name} proxies={mode}")
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    offs = make_proxy_offsets(wl) if mode == "random" else None
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=prec,
+                             proxy_mode=mode, proxy_offsets=None if offs is None else torch.from_numpy(offs))
+    blk.forward(dev(x, prec))
+    torch.cuda.synchronize()
+    ref = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads, pool="select", offsets=offs)
+    inter = blk.intermediates()
+    assert np.array_equal(host(inter["P"]), ref["P"].astype(np.float32))
+    for k in ("P2", "x1", "x2", "x3"):
+        assert_close(host(inter[k]), ref[k], f"{name}.{mode}.{k}")
 
 
 # ----------------------------------------------------------------------------- roll (bit-exact)
