@@ -44,6 +44,14 @@ Readings where the pages are silent (all listed in the design doc):
             window-local offset o = (dt*p_h + di)*p_w + dj (row-major inside
             the window, as R-order), o = 0 for Top-Left, a drawn offset per
             window for Random; offsets are taken modulo P.
+  R-text    the text cross-attention after TCM (section 3: PT-Block = GIIM +
+            TCM + text cross-attn + MLP; Figure 3 data flow) is MHA with the
+            tokens as queries and the caption embeddings (already projected to
+            D, outside the block like the patch embedding) as keys/values,
+            plus the residual: the same map as the proxy cross-attention.
+  R-mlp     the MLP is the DiT/PixArt feed-forward: Lin(GELU(Lin(x; W1, b1));
+            W2, b2) with hidden width 4D and the tanh form of GELU, plus the
+            residual. The pages name the MLP and nothing about its shape.
 """
 from __future__ import annotations
 
@@ -55,7 +63,7 @@ __all__ = [
     "linear", "attention", "mha", "proxy_grid", "proxy_pool", "proxy_pool_f32", "proxy_select",
     "round_bf16_rne", "proxy_sa", "proxy_xattn", "pad_grid", "partition",
     "unpartition", "roll3d", "region_labels", "window_sa", "shift_window_sa",
-    "block", "count_core_macs", "count_projection_macs",
+    "block", "count_core_macs", "count_projection_macs", "gelu_tanh", "mlp", "text_xattn",
 ]
 
 Grid = Tuple[int, int, int]
@@ -230,6 +238,28 @@ def proxy_xattn(x: np.ndarray, P2: np.ndarray, w: Weights, heads: int,
     return _f64(x) + y if residual else y
 
 
+def text_xattn(x: np.ndarray, text: np.ndarray, w: Weights, heads: int,
+               residual: bool = True) -> np.ndarray:
+    """Text cross-attention of the PT-Block (reading R-text): tokens are
+    queries, caption embeddings [B, L, D] are keys and values."""
+    y = mha(x, text, w, heads)
+    return _f64(x) + y if residual else y
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """GELU in its tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+    (Hendrycks & Gimpel, the approximation DiT-style MLPs use)."""
+    x = _f64(x)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def mlp(x: np.ndarray, w: Weights, residual: bool = True) -> np.ndarray:
+    """The PT-Block's MLP (reading R-mlp): Lin(GELU(Lin(x; W1, b1)); W2, b2)
+    (+ x). w = {"w1": [H, D], "b1": [H], "w2": [D, H], "b2": [D]}."""
+    y = linear(gelu_tanh(linear(x, w["w1"], w.get("b1"))), w["w2"], w.get("b2"))
+    return _f64(x) + y if residual else y
+
+
 # ----------------------------------------------------------------------------
 # TCM: window attention and shifted-window attention
 # ----------------------------------------------------------------------------
@@ -344,7 +374,9 @@ def shift_window_sa(x: np.ndarray, grid: Grid, win: Sequence[int], shift: Sequen
 
 def block(x: np.ndarray, grid: Grid, p: Sequence[int], win: Sequence[int],
           shift: Sequence[int], weights: Sequence[Weights], heads: int,
-          pool: str = "f64", offsets: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+          pool: str = "f64", offsets: Optional[np.ndarray] = None,
+          text: Optional[np.ndarray] = None, w_text: Optional[Weights] = None,
+          w_mlp: Optional[Weights] = None) -> Dict[str, np.ndarray]:
     """GIIM then TCM, in the order of excerpt 2 (PT-Block forward).
 
     weights = [proxy SA, cross-attention, WSA, SWSA]. pool="f64" uses the
@@ -367,7 +399,12 @@ def block(x: np.ndarray, grid: Grid, p: Sequence[int], win: Sequence[int],
     x1 = proxy_xattn(x, P2, weights[1], heads)
     x2 = window_sa(x1, grid, win, weights[2], heads)
     x3 = shift_window_sa(x2, grid, win, shift, weights[3], heads)
-    return {"P": P, "P2": P2, "x1": x1, "x2": x2, "x3": x3}
+    out = {"P": P, "P2": P2, "x1": x1, "x2": x2, "x3": x3}
+    # the rest of the PT-Block (readings R-text, R-mlp), when given
+    if text is not None:
+        out["x4"] = text_xattn(x3, text, w_text, heads)
+        out["x5"] = mlp(out["x4"], w_mlp)
+    return out
 
 
 def count_core_macs(grid: Grid, p: Sequence[int], win: Sequence[int], D: int,

@@ -156,6 +156,29 @@ def make_weights(wl: Workload, attn: int, seed_base: int | None = None,
     return out
 
 
+TEXT_TOKENS = 120  # caption length of the text cross-attention
+
+
+def make_text(wl: Workload, L: int = TEXT_TOKENS, seed: int | None = None) -> np.ndarray:
+    """Caption embeddings [B, L, D] (already projected to D), N(0, 1)."""
+    s = 1000 * wl.index + 997 if seed is None else seed
+    t = _normal(s, (wl.B, L, wl.D), 1.0)
+    return round_bf16(t) if wl.dtype == "bf16" else t
+
+
+def make_mlp_weights(wl: Workload, hidden: int | None = None, seed_base: int | None = None,
+                     scale: float = 0.02) -> Dict[str, np.ndarray]:
+    """MLP weights: w1 [H, D], b1 [H], w2 [D, H], b2 [D], N(0, scale), H = 4D."""
+    H = 4 * wl.D if hidden is None else hidden
+    base = 1000 * wl.index + 60 if seed_base is None else seed_base
+    shapes = {"w1": (H, wl.D), "b1": (H,), "w2": (wl.D, H), "b2": (wl.D,)}
+    out = {}
+    for j, (name, shape) in enumerate(shapes.items()):
+        v = _normal(base + j, shape, scale)
+        out[name] = round_bf16(v) if wl.dtype == "bf16" else v
+    return out
+
+
 def make_proxy_offsets(wl: Workload, seed: int | None = None) -> np.ndarray:
     """Window-local token offsets for random proxy extraction, int32 [B, M],
     uniform over the P = p_t*p_h*p_w tokens of each window (the draws the

@@ -168,6 +168,67 @@ def test_block_with_selected_proxies_matches_bruteforce():
     assert not np.allclose(O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)["x3"], got["x3"])
 
 
+# ----------------------------------------------------------------------------- text cross-attention and MLP
+
+def test_gelu_tanh_matches_torch_and_identity():
+    """The tanh form against torch's gelu(approximate='tanh') in float64 (a
+    library routine), its odd-part identity gelu(x) - gelu(-x) = x, and its
+    limits."""
+    x = np.linspace(-12, 12, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(x), ref, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(O.gelu_tanh(x) - O.gelu_tanh(-x), x, rtol=0, atol=1e-12)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(O.gelu_tanh(np.array([12.0]))[0] - 12.0) < 1e-12
+    assert abs(O.gelu_tanh(np.array([-12.0]))[0]) < 1e-12
+    # not the erf form: they differ by ~1e-3 around |x| ~ 2
+    erf = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()
+    assert np.max(np.abs(O.gelu_tanh(x) - erf)) > 1e-4
+
+
+def test_mlp_closed_forms_and_scalar_loop():
+    rng = np.random.default_rng(21)
+    B, N, D, H = 2, 5, 8, 32
+    x = rng.standard_normal((B, N, D))
+    w = {"w1": rng.standard_normal((H, D)) * 0.3, "b1": rng.standard_normal(H) * 0.3,
+         "w2": rng.standard_normal((D, H)) * 0.3, "b2": rng.standard_normal(D) * 0.3}
+    # W1 = 0: the hidden layer is the constant gelu(b1)
+    w0 = dict(w, w1=np.zeros((H, D)))
+    const = w["w2"] @ O.gelu_tanh(w["b1"]) + w["b2"]
+    np.testing.assert_allclose(O.mlp(x, w0), x + const, rtol=1e-12, atol=1e-12)
+    # W2 = 0: only b2 and the residual remain
+    np.testing.assert_allclose(O.mlp(x, dict(w, w2=np.zeros((D, H)))), x + w["b2"], rtol=1e-12, atol=1e-12)
+    # scalar loop
+    got = O.mlp(x, w, residual=False)
+    for b in range(B):
+        for n in range(N):
+            h = [w["b1"][k] + sum(w["w1"][k, i] * x[b, n, i] for i in range(D)) for k in range(H)]
+            g = [0.5 * v * (1 + math.tanh(math.sqrt(2 / math.pi) * (v + 0.044715 * v ** 3))) for v in h]
+            for j in range(D):
+                y = w["b2"][j] + sum(w["w2"][j, k] * g[k] for k in range(H))
+                assert abs(got[b, n, j] - y) < 1e-12
+
+
+def test_text_xattn_is_mha_with_caption_keys():
+    """Text cross-attention: uniform over the caption when W_k = 0 (closed
+    form), and the block's x4/x5 follow x3 through text_xattn and mlp."""
+    wl = tiny("txt", B=1, F=1, H=8, W=8, D=16, heads=2, p=(1, 2, 2), win=(1, 4, 4), shift=(0, 2, 2))
+    x = make_x(wl, seed=41)
+    rng = np.random.default_rng(42)
+    text = rng.standard_normal((1, 7, wl.D))
+    wt = make_all_weights(wl)[1]
+    wz = dict(wt, wk=np.zeros_like(wt["wk"]), bk=np.zeros_like(wt["bk"]))
+    v_mean = O.linear(text, wz["wv"], wz["bv"]).mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(O.text_xattn(x, text, wz, wl.heads, residual=False),
+                               np.broadcast_to(O.linear(v_mean, wz["wo"], wz["bo"]), x.shape), rtol=1e-12, atol=1e-12)
+    wm = {"w1": rng.standard_normal((64, wl.D)) * 0.1, "b1": rng.standard_normal(64) * 0.1,
+          "w2": rng.standard_normal((wl.D, 64)) * 0.1, "b2": rng.standard_normal(wl.D) * 0.1}
+    ws = make_all_weights(wl)
+    r = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads, text=text, w_text=wt, w_mlp=wm)
+    np.testing.assert_allclose(r["x4"], O.text_xattn(r["x3"], text, wt, wl.heads), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["x5"], O.mlp(r["x4"], wm), rtol=1e-12, atol=1e-12)
+
+
 def test_pool_f32_close_to_f64():
     wl = tiny(H=32, W=32, D=64, p=(1, 8, 8))
     x = make_x(wl, seed=12)
