@@ -1,7 +1,8 @@
 """Benchmark: PT-block attention core (GIIM + TCM) tokens/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload img2048]
-                    [--proxy-mode mean|first|random] [--no-cpu-baseline] [--breakdown]
+                    [--proxy-mode mean|first|random] [--full-block]
+                    [--no-cpu-baseline] [--breakdown]
 
 A step is one forward of the whole attention core of one PT-DiT block
 (proxy pooling, proxy self-attention, token->proxy cross-attention, window
@@ -99,6 +100,9 @@ def main() -> int:
     ap.add_argument("--proxy-mode", default="mean", choices=["mean", "first", "random"],
                     help="proxy extraction: window average (the default of the method), top-left token, "
                          "or a drawn token per window")
+    ap.add_argument("--full-block", action="store_true",
+                    help="also run the rest of the PT-Block in every step: text cross-attention over 120 "
+                         "caption tokens and the MLP (the default step is the attention core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -113,7 +117,7 @@ def main() -> int:
     import torch
     import diffusion_transformer_attention_pt_amd as P
     from diffusion_transformer_attention_pt_amd import _lib
-    from synth_inputs import WORKLOADS, make_all_weights, make_proxy_offsets, make_x
+    from synth_inputs import WORKLOADS, make_all_weights, make_mlp_weights, make_proxy_offsets, make_text, make_weights, make_x
 
     wl = WORKLOADS[args.workload]
     prec = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -129,7 +133,9 @@ def main() -> int:
     offs = torch.from_numpy(make_proxy_offsets(wl)) if args.proxy_mode == "random" else None
     blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift,
                              make_all_weights(wl), prec=prec, device=dev, proxy_mode=args.proxy_mode,
-                             proxy_offsets=offs)
+                             proxy_offsets=offs,
+                             **(dict(text=make_text(wl), text_weights=make_weights(wl, 4), mlp_weights=make_mlp_weights(wl))
+                                if args.full_block else {}))
     flops = blk.flops()
 
     for _ in range(args.warmup):
@@ -191,7 +197,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {wl.B}, grid {wl.F}x{wl.H}x{wl.W} (N={wl.N}), "
                                f"D={wl.D}, {wl.heads} heads, proxy window {wl.p}, TCM window {wl.win} "
-                               f"shift {wl.shift}, proxies: {args.proxy_mode}",
+                               f"shift {wl.shift}, proxies: {args.proxy_mode}"
+                               + (", with text cross-attention (120 tokens) and MLP (hidden 4D)" if args.full_block else ""),
                    "batch": wl.B, "tokens": wl.N, "D": wl.D, "heads": wl.heads,
                    "gflop_per_step": round(flops["total"] / 1e9, 3)},
         "step_ms_p10_p50_p90": [round(quant(0.1), 4), round(quant(0.5), 4), round(quant(0.9), 4)],
@@ -221,6 +228,13 @@ def main() -> int:
                 "gemm_out": ("TFLOP/s", 3 * 2 * B * N * D * D),
                 "gemm_qkv": ("TFLOP/s", 2 * 2 * B * N * D * 3 * D),
                 "attn_window": ("GB/s", 2 * 4 * B * N * D * es)}
+        if args.full_block:  # the text cross-attention shares the GIIM classes; the MLP has its own
+            T, Hm = blk.L, blk.hidden
+            for k, extra in (("gemm_q", 2 * B * N * D * D), ("gemm_proxy", 2 * B * T * D * 2 * D),
+                             ("attn_flash", 4 * B * N * T * D), ("gemm_out", 2 * B * N * D * D)):
+                work[k] = (work[k][0], work[k][1] + extra)
+            names[_lib.K_GEMM_MLP] = "gemm_mlp"
+            work["gemm_mlp"] = ("TFLOP/s", 4 * B * N * D * Hm)
         br = {}
         for cls, nm in names.items():
             _lib.trace_enable(cls, 64)

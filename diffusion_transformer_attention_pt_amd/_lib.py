@@ -18,14 +18,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libptdit.so")
 
 PTDIT_BF16, PTDIT_F32 = 0, 1
-OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA = 0, 1, 2, 3
-K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY = range(8)
+OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA, OP_MLP = 0, 1, 2, 3, 4
+K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY, K_GEMM_MLP = range(9)
 
 STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT_ERR_DIVISIBILITY",
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",
           -7: "PTDIT_ERR_HIP", -8: "PTDIT_ERR_ALIAS"}
 
-EXPORTED = ["ptdit_linear", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_xattn",
+EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_xattn",
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
             "ptdit_trace_disable"]
@@ -43,6 +43,10 @@ class Win3(ctypes.Structure):
 class AttnW(ctypes.Structure):
     _fields_ = [("w_qkv", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p),
                 ("w_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p)]
+
+
+class MlpW(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
 
 class PtditError(RuntimeError):
@@ -64,11 +68,12 @@ def load() -> ctypes.CDLL:
                            "`python -m diffusion_transformer_attention_pt_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    G, W3, AW = Grid, Win3, ctypes.POINTER(AttnW)
+    G, W3, AW, MW = Grid, Win3, ctypes.POINTER(AttnW), ctypes.POINTER(MlpW)
     sig = {
         "ptdit_linear": [vp, i32, i64, i32, i32, vp, vp, vp, i32, vp, i32, i32, vp],
         "ptdit_proxy_pool": [vp, i32, G, W3, vp, i32, vp],
         "ptdit_proxy_select": [vp, i32, G, W3, vp, vp, i32, vp],
+        "ptdit_mlp": [vp, vp, i32, i64, i32, i32, MW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_proxy_sa": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
         "ptdit_proxy_xattn": [vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_window_sa": [vp, vp, i32, G, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
@@ -148,6 +153,50 @@ class AttnWeights:
 
     def c(self) -> AttnW:
         return AttnW(_ptr(self.w_qkv), _ptr(self.b_qkv), _ptr(self.w_o), _ptr(self.b_o))
+
+
+@dataclass
+class MlpWeights:
+    """Weights of the MLP in the ABI layout: w1 [H, D], b1 [H], w2 [D, H], b2 [D]."""
+    w1: torch.Tensor
+    b1: Optional[torch.Tensor]
+    w2: torch.Tensor
+    b2: Optional[torch.Tensor]
+
+    @staticmethod
+    def from_dict(w: dict, dtype: torch.dtype, device) -> "MlpWeights":
+        t = lambda a: torch.as_tensor(a).to(device=device, dtype=dtype).contiguous()
+        return MlpWeights(t(w["w1"]), t(w["b1"]) if w.get("b1") is not None else None,
+                          t(w["w2"]), t(w["b2"]) if w.get("b2") is not None else None)
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.w1.dtype
+
+    @property
+    def hidden(self) -> int:
+        return self.w1.shape[0]
+
+    def c(self) -> MlpW:
+        return MlpW(_ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2))
+
+
+def mlp(x: torch.Tensor, w: MlpWeights, residual: bool = True, out_dtype: Optional[torch.dtype] = None,
+        ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        x_lowp: Optional[torch.Tensor] = None, out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [..., D] -> Lin(GELU(Lin(x; w1, b1)); w2, b2) (+ x)."""
+    lib = load()
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    need = workspace_bytes(OP_MLP, (rows, 1, 1, 1, D, 1), w.hidden, (1, 1, 1), w.dtype)
+    ws = _ws(need, ws, x.device)
+    cw = w.c()
+    st = lib.ptdit_mlp(_ptr(x), _ptr(x_lowp), _dt(x.dtype), rows, D, w.hidden, ctypes.byref(cw), int(residual),
+                       _ptr(out), _ptr(out_lowp), _dt(out.dtype), _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
+    _check("ptdit_mlp", st)
+    return out
 
 
 def version() -> str:

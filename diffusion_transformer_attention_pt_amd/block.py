@@ -8,6 +8,11 @@ excerpt 2 (PT-Block forward) with Eq. GIIM and Eq. TCM of section 3:
     x2 = x1 + WSA(x1)                      ptdit_window_sa
     x3 = x2 + SWSA(x2)                     ptdit_shift_window_sa
 
+With caption embeddings (text, [B, L, D]) and MLP weights the rest of the
+PT-Block follows (section 3: PT-Block = GIIM + TCM + text cross-attn + MLP):
+    x4 = x3 + MHA(x3, text)                ptdit_proxy_xattn (keys/values: text)
+    x5 = x4 + MLP(x4)                      ptdit_mlp
+
 Proxy extraction is the window average by default (proxy_mode="mean");
 "first" takes each window's top-left token and "random" the token at a
 caller-drawn window-local offset (proxy_offsets, int32 [B, M]), the two
@@ -27,14 +32,15 @@ from typing import Dict, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import AttnWeights
+from ._lib import AttnWeights, MlpWeights
 
 
 class PTBlockAttention:
     def __init__(self, B: int, grid: Sequence[int], D: int, heads: int, p: Sequence[int],
                  win: Sequence[int], shift: Sequence[int], weights: Sequence[dict],
                  prec: torch.dtype = torch.bfloat16, device="cuda", proxy_mode: str = "mean",
-                 proxy_offsets: Optional[torch.Tensor] = None):
+                 proxy_offsets: Optional[torch.Tensor] = None, text: Optional[torch.Tensor] = None,
+                 text_weights: Optional[dict] = None, mlp_weights: Optional[dict] = None):
         self.B = B
         self.F, self.H, self.W = grid
         self.D, self.heads = D, heads
@@ -61,11 +67,26 @@ class PTBlockAttention:
         lowp = prec == torch.bfloat16
         self.x1_lowp = torch.empty(B, self.N, D, dtype=torch.bfloat16, device=self.device) if lowp else None
         self.x2_lowp = torch.empty_like(self.x1_lowp) if lowp else None
-        need = max(
+        if (text is None) != (text_weights is None) or (text is None) != (mlp_weights is None):
+            raise ValueError("text, text_weights and mlp_weights go together")
+        self.full = text is not None
+        need = [
             _lib.workspace_bytes(_lib.OP_PROXY_SA, (B, 1, 1, self.M, D, heads), self.M, (1, 1, 1), prec),
             _lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.M, (1, 1, 1), prec),
             _lib.workspace_bytes(_lib.OP_WINDOW_SA, self.g, 0, self.win, prec),
-        )
+        ]
+        if self.full:
+            self.text = torch.as_tensor(text).to(device=self.device, dtype=prec).contiguous()
+            self.L = self.text.shape[1]
+            self.w_text = AttnWeights.from_dict(text_weights, prec, self.device)
+            self.w_mlp = MlpWeights.from_dict(mlp_weights, prec, self.device)
+            self.hidden = self.w_mlp.hidden
+            self.x4 = torch.empty_like(self.x1)
+            self.x5 = torch.empty_like(self.x1)
+            self.x4_lowp = torch.empty_like(self.x1_lowp) if lowp else None
+            need += [_lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.L, (1, 1, 1), prec),
+                     _lib.workspace_bytes(_lib.OP_MLP, (B * self.N, 1, 1, 1, D, 1), self.hidden, (1, 1, 1), prec)]
+        need = max(need)
         self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
@@ -80,10 +101,18 @@ class PTBlockAttention:
                        x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
         _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3,
                              x_lowp=self.x2_lowp)
-        return self.x3
+        if not self.full:
+            return self.x3
+        _lib.proxy_xattn(self.x3, g, self.text, self.w_text, residual=True, ws=self.ws, out=self.x4,
+                         out_lowp=self.x4_lowp)
+        _lib.mlp(self.x4, self.w_mlp, residual=True, ws=self.ws, out=self.x5, x_lowp=self.x4_lowp)
+        return self.x5
 
     def intermediates(self) -> Dict[str, torch.Tensor]:
-        return {"P": self.P, "P2": self.P2, "x1": self.x1, "x2": self.x2, "x3": self.x3}
+        out = {"P": self.P, "P2": self.P2, "x1": self.x1, "x2": self.x2, "x3": self.x3}
+        if self.full:
+            out.update(x4=self.x4, x5=self.x5)
+        return out
 
     def flops(self) -> Dict[str, int]:
         """Algorithmic FLOPs of one forward (2 per multiply-accumulate): the
@@ -93,4 +122,10 @@ class PTBlockAttention:
         L = self.win[0] * self.win[1] * self.win[2]
         proj = B * D * D * ((3 * M + M) + (N + 2 * M + N) + 2 * (3 * N + N))
         core = B * D * (2 * M * M + 2 * N * M + 2 * (2 * N * L))
-        return {"projection": 2 * proj, "core": 2 * core, "total": 2 * (proj + core)}
+        out = {"projection": 2 * proj, "core": 2 * core, "total": 2 * (proj + core)}
+        if getattr(self, "full", False):
+            T, Hm = self.L, self.hidden
+            text = B * D * (D * (N + 2 * T + N) + 2 * N * T)   # Q, K/V, O maps; Q K^T and P V
+            mlp = B * N * D * Hm * 2
+            out.update(text=2 * text, mlp=2 * mlp, total=out["total"] + 2 * (text + mlp))
+        return out

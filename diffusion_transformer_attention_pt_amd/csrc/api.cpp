@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -92,7 +93,7 @@ ptdit_status check_grid(const ptdit_grid& g) {
 hipError_t gemm(ptdit_dtype prec, const void* A, ptdit_dtype a_dt, int64_t M, int K, int N,
                 const void* W, const void* bias, const void* R, ptdit_dtype r_dt,
                 void* Y, ptdit_dtype y_dt, bool head_major, int64_t Ntok, int heads, int D,
-                int trace_cls, hipStream_t s, void* Y2 = nullptr) {
+                int trace_cls, hipStream_t s, void* Y2 = nullptr, int act = 0) {
   GemmDesc d;
   d.A = A; d.a_f32 = a_dt == PTDIT_F32;
   d.W = W; d.bias = bias;
@@ -102,6 +103,7 @@ hipError_t gemm(ptdit_dtype prec, const void* A, ptdit_dtype a_dt, int64_t M, in
   d.M = M; d.N = N; d.K = K;
   d.head_major = head_major; d.Ntok = Ntok; d.heads = heads;
   d.dh = heads > 0 ? D / heads : 0; d.D = D;
+  d.act = act;
   TraceScope ts(trace_cls, s);
   return prec == PTDIT_F32 ? launch_gemm_f32(d, s) : launch_gemm_bf16(d, s);
 }
@@ -204,6 +206,9 @@ size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 wi
     case PTDIT_OP_WINDOW_SA:
     case PTDIT_OP_SHIFT_WINDOW_SA:
       return align_up(B * 3 * N * D * es) + align_up(B * N * D * es);
+    case PTDIT_OP_MLP:
+      if (M <= 0) return 0;
+      return align_up(B * N * (size_t)M * es);
   }
   return 0;
 }
@@ -249,6 +254,39 @@ ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptd
   d.pt = p.t; d.ph = p.h; d.pw = p.w;
   TraceScope ts(PTDIT_K_POOL, stream);
   return hip_status(launch_pool(d, stream));
+}
+
+ptdit_status ptdit_mlp(const void* x, const void* x_lowp, ptdit_dtype x_dt, int64_t rows, int32_t D,
+                       int32_t hidden, const ptdit_mlp_w* w, int32_t add_residual, void* out,
+                       void* out_lowp, ptdit_dtype out_dt, void* ws, size_t ws_bytes, ptdit_dtype prec,
+                       hipStream_t stream) {
+  ptdit_status st = check_io_dtypes(prec, x_dt, out_dt);
+  if (st) return st;
+  if (rows < 0 || D <= 0 || hidden <= 0 || D % 8 || hidden % 8) return PTDIT_ERR_SHAPE;
+  if (!w || !w->w1 || !w->w2) return PTDIT_ERR_NULL;
+  if (rows == 0) return PTDIT_OK;
+  if (!x || !out) return PTDIT_ERR_NULL;
+  if (x_lowp && (prec != PTDIT_BF16 || x_dt != PTDIT_F32)) return PTDIT_ERR_DTYPE;
+  if ((st = check_lowp(prec, out_lowp, out_dt))) return st;
+  if (!aligned16(x) || !aligned16(x_lowp) || !aligned16(out) || !aligned16(ws) || !aligned16(w->w1) ||
+      !aligned16(w->w2) || !aligned16(w->b1) || !aligned16(w->b2))
+    return PTDIT_ERR_ALIGN;
+  const ptdit_grid g{(int32_t)std::min<int64_t>(rows, INT32_MAX), 1, 1, 1, D, 1};
+  if (rows > INT32_MAX) return PTDIT_ERR_SHAPE;
+  const size_t need = ptdit_workspace_bytes(PTDIT_OP_MLP, g, hidden, ptdit_win3{1, 1, 1}, prec);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  const size_t xb = rows * D * esize(x_dt), ob = rows * D * esize(out_dt), lb = rows * D * 2;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need) || overlaps(out, ob, x_lowp, lb) ||
+      overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, x_lowp, lb) || overlaps(out_lowp, lb, out, ob) ||
+      overlaps(out_lowp, lb, ws, need))
+    return PTDIT_ERR_ALIAS;
+  // h = GELU(x W1^T + b1) into the workspace, then out = h W2^T + b2 (+ x)
+  hipError_t e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, hidden, w->w1, w->b1,
+                      nullptr, prec, ws, prec, false, rows, 1, hidden, PTDIT_K_GEMM_MLP, stream, nullptr, 1);
+  if (e != hipSuccess) return PTDIT_ERR_HIP;
+  e = gemm(prec, ws, prec, rows, hidden, D, w->w2, w->b2, add_residual ? x : nullptr, x_dt, out, out_dt, false,
+           rows, 1, D, PTDIT_K_GEMM_MLP, stream, out_lowp);
+  return hip_status(e);
 }
 
 ptdit_status ptdit_proxy_select(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,

@@ -115,6 +115,13 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 __device__ __forceinline__ float ld1(const uint16_t* p) { return bf2f(*p); }
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 
+// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (Hendrycks &
+// Gimpel's approximation), in fp32 with the device library's tanhf.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.0f + tanhf(u));
+}
+
 // global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane l
 // lands at the wave-uniform LDS address lptr + 16 l.
 #define PTDIT_GLDS16(gptr, lptr)                                                                 \

@@ -30,6 +30,7 @@ struct GemmParams {
   int N, K;
   int64_t Ntok;
   int heads, dh, D;
+  int act;  // 1: GELU after the bias (token-major, no residual)
 };
 
 // XCD-aware tile order: hardware hands block i to XCD (i % 8); re-number so
@@ -200,6 +201,9 @@ gemm_bf16_kernel(GemmParams p) {
       if (m >= p.M) continue;
       float v0 = acc[i][j][0] + b0, v1 = acc[i][j][1] + b1;
       float v2 = acc[i][j][2] + b2, v3 = acc[i][j][3] + b3;
+      if (p.act) {
+        v0 = gelu_tanh(v0); v1 = gelu_tanh(v1); v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+      }
       if constexpr (HEADMAJOR) {
         const int g = n / p.D, hn = n - g * p.D;
         const int h = hn / p.dh, d = hn - h * p.dh;
@@ -426,10 +430,14 @@ __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
           const int c = wn * TN + i * 16 + 4 * (lane >> 4);
-          store4(base + lrow * ES::PITCH + c, acc[i][jb][0] + __uint_as_float(biasp[i].x << 16),
-                 acc[i][jb][1] + __uint_as_float(biasp[i].x & 0xffff0000u),
-                 acc[i][jb][2] + __uint_as_float(biasp[i].y << 16),
-                 acc[i][jb][3] + __uint_as_float(biasp[i].y & 0xffff0000u));
+          float v0 = acc[i][jb][0] + __uint_as_float(biasp[i].x << 16);
+          float v1 = acc[i][jb][1] + __uint_as_float(biasp[i].x & 0xffff0000u);
+          float v2 = acc[i][jb][2] + __uint_as_float(biasp[i].y << 16);
+          float v3 = acc[i][jb][3] + __uint_as_float(biasp[i].y & 0xffff0000u);
+          if (p.act) {
+            v0 = gelu_tanh(v0); v1 = gelu_tanh(v1); v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+          }
+          store4(base + lrow * ES::PITCH + c, v0, v1, v2, v3);
         }
       }
     });
@@ -843,6 +851,7 @@ struct GemmF32Params {
   int N, K;
   int64_t Ntok;
   int heads, dh, D;
+  int act;
 };
 
 template <bool HEADMAJOR>
@@ -896,6 +905,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmF32Params p) {
       if (m >= p.M) continue;
       float v0 = acc[i][j][0] + bv.x, v1 = acc[i][j][1] + bv.y;
       float v2 = acc[i][j][2] + bv.z, v3 = acc[i][j][3] + bv.w;
+      if (p.act) {
+        v0 = gelu_tanh(v0); v1 = gelu_tanh(v1); v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+      }
       if constexpr (HEADMAJOR) {
         const int g = n / p.D, hn = n - g * p.D;
         const int h = hn / p.dh, d = hn - h * p.dh;
@@ -1001,6 +1013,7 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.M = d.M; p.N = d.N; p.K = d.K;
   p.Ntok = d.Ntok > 0 ? d.Ntok : 1;
   p.heads = d.heads; p.dh = d.dh; p.D = d.D;
+  p.act = d.act;
   if (d.a_f32) {
     if (d.y_f32) return pick_r<float, float>(d, p, s);
     return pick_r<float, uint16_t>(d, p, s);
@@ -1019,6 +1032,7 @@ hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s) {
   p.M = d.M; p.N = d.N; p.K = d.K;
   p.Ntok = d.Ntok > 0 ? d.Ntok : 1;
   p.heads = d.heads; p.dh = d.dh; p.D = d.D;
+  p.act = d.act;
   const int64_t tiles = ((p.M + 63) / 64) * (int64_t)((p.N + 63) / 64);
   if (tiles <= 0) return hipSuccess;
   if (d.head_major)

@@ -18,6 +18,7 @@ struct GemmDesc {
   void* Y2;  // optional bf16 copy of Y (token-major fp32 Y only), else nullptr
   int64_t M; int N; int K;
   int head_major; int64_t Ntok; int heads; int dh; int D;
+  int act = 0;  // 1: GELU (tanh form) after the bias; token-major output without residual only
 };
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32

@@ -102,7 +102,8 @@ typedef enum {
   PTDIT_OP_PROXY_SA = 0,
   PTDIT_OP_PROXY_XATTN = 1,
   PTDIT_OP_WINDOW_SA = 2,
-  PTDIT_OP_SHIFT_WINDOW_SA = 3
+  PTDIT_OP_SHIFT_WINDOW_SA = 3,
+  PTDIT_OP_MLP = 4
 } ptdit_op;
 
 /*
@@ -134,6 +135,33 @@ ptdit_status ptdit_linear(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t
  */
 ptdit_status ptdit_proxy_pool(const void* x, ptdit_dtype x_dt, ptdit_grid g, ptdit_win3 p,
                               void* proxies, ptdit_dtype out_dt, hipStream_t stream);
+
+/* MLP weights (nn.Linear layout): w1 [hidden][D], b1 [hidden], w2 [D][hidden],
+ * b2 [D]; biases nullable; dtype as the projections' (bf16 unless prec F32). */
+typedef struct {
+  const void* w1;
+  const void* b1;
+  const void* w2;
+  const void* b2;
+} ptdit_mlp_w;
+
+/*
+ * ptdit_mlp -- the MLP of the PT-Block that follows the text cross-attention
+ * (section 3: PT-Block = GIIM + TCM + text cross-attn + MLP; Figure 3):
+ *   out = Lin(GELU(Lin(x; w1, b1)); w2, b2) (+ x when add_residual != 0),
+ * GELU in its tanh form, 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))),
+ * applied in fp32 to the first map's output before it is stored (bf16 with
+ * PTDIT_BF16 precision, else fp32) in the workspace.
+ *   x        [rows][D], dtype x_dt; x_lowp: optional bf16 copy of an fp32 x
+ *            (read instead of x by the first map, bf16 precision only)
+ *   out      [rows][D], dtype out_dt; out_lowp: optional bf16 copy of out
+ *   ws       ptdit_workspace_bytes(PTDIT_OP_MLP, {rows,1,1,1,D,1}, hidden, ...)
+ * Requires D % 8 == 0, hidden % 8 == 0. Errors as the attention calls.
+ */
+ptdit_status ptdit_mlp(const void* x, const void* x_lowp, ptdit_dtype x_dt, int64_t rows, int32_t D,
+                       int32_t hidden, const ptdit_mlp_w* w, int32_t add_residual, void* out,
+                       void* out_lowp, ptdit_dtype out_dt, void* ws, size_t ws_bytes, ptdit_dtype prec,
+                       hipStream_t stream);
 
 /*
  * ptdit_proxy_select -- proxy extraction by one token per window instead of
@@ -224,7 +252,8 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
                           void* y, ptdit_dtype dt, hipStream_t stream);
 
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
- * ignored for the GIIM ops). Returns 0 for invalid arguments. */
+ * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*
+ * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments. */
 size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 win,
                              ptdit_dtype prec);
 
@@ -250,7 +279,8 @@ typedef enum {
   PTDIT_K_ATTN_WINDOW = 4,   /* window / shifted-window attention cores */
   PTDIT_K_ROLL = 5,
   PTDIT_K_GEMM_Q = 6,        /* query projection of the token rows for cross-attention */
-  PTDIT_K_GEMM_PROXY = 7     /* every projection of the proxy rows */
+  PTDIT_K_GEMM_PROXY = 7,    /* every projection of the proxy rows */
+  PTDIT_K_GEMM_MLP = 8       /* both linear maps of the MLP */
 } ptdit_kernel_class;
 
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity);

@@ -126,6 +126,22 @@ def test_host_validation_rejects_before_launch(lib):
     assert sel(fake, 0, g, Win3(1, 2, 2), ctypes.c_void_p((1 << 41) + 2), far, 0, None) == -5
     assert sel(fake, 0, g, Win3(1, 2, 2), ctypes.c_void_p((1 << 40) + 64), far, 0, None) == -8
     assert sel(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, None, 0, None) == 0
+    # MLP: widths, weights, dtypes, workspace, aliasing; zero rows is a no-op
+    from diffusion_transformer_attention_pt_amd._lib import MlpW
+    mw = MlpW(fake.value, None, fake.value, None)
+    mlp = lambda x, rows, D, H, w, out, ws, wsb, prec=0, xl=None, xdt=0: lib.ptdit_mlp(
+        x, xl, xdt, rows, D, H, w, 1, out, None, xdt, ws, wsb, prec, None)
+    assert mlp(fake, 64, 1150, 4608, ctypes.byref(mw), far, far, 1 << 30) == -2
+    assert mlp(fake, 64, 1152, 4604, ctypes.byref(mw), far, far, 1 << 30) == -2
+    assert mlp(fake, 64, 1152, 4608, None, far, far, 1 << 30) == -1
+    assert mlp(fake, 64, 1152, 4608, ctypes.byref(MlpW(fake.value, None, None, None)), far, far, 1 << 30) == -1
+    assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41), 64) == -6
+    assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), fake, ctypes.c_void_p(1 << 41), 1 << 30) == -8
+    assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41), 1 << 30, prec=1) == -4
+    assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41), 1 << 30,
+               xl=ctypes.c_void_p(1 << 42)) == -4    # x_lowp beside a bf16 x
+    assert mlp(None, 0, 1152, 4608, ctypes.byref(mw), None, None, 0) == 0
+    assert lib.ptdit_workspace_bytes(4, Grid(100, 1, 1, 1, 1152, 1), 4608, Win3(1, 1, 1), 0) >= 100 * 4608 * 2
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
     assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),

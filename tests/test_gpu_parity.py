@@ -13,8 +13,8 @@ import torch
 
 import oracle as O
 from gpu_util import announce, assert_close, dev, host
-from synth_inputs import (ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_proxy_offsets,
-                          make_weights, make_x, round_bf16,
+from synth_inputs import (ALL_WORKLOADS, WORKLOADS, WORKLOAD_ORDER, Workload, make_all_weights, make_mlp_weights,
+                          make_proxy_offsets, make_text, make_weights, make_x, round_bf16,
                           tiny)
 
 pytestmark = pytest.mark.gpu
@@ -122,6 +122,73 @@ def test_block_with_selected_proxies(P, name, mode):
     assert np.array_equal(host(inter["P"]), ref["P"].astype(np.float32))
     for k in ("P2", "x1", "x2", "x3"):
         assert_close(host(inter[k]), ref[k], f"{name}.{mode}.{k}")
+
+
+# ----------------------------------------------------------------------------- text cross-attention + MLP
+
+MLP_CASES = [  # rows, D, hidden, x dtype, precision; the kernel each first map takes
+    (2400, 1152, 4608, "bf16", BF16),    # >= 2048 rows, bf16 A: ping-pong kernel with the GELU epilogue
+    (2100, 1152, 4608, "f32", BF16),     # fp32 A (residual stream): 256x288 ring kernel
+    (300, 1152, 4608, "f32", BF16),      # few rows: 64x64 ring kernel
+    (257, 64, 96, "bf16", BF16),         # odd shapes: register-staged kernel
+    (300, 1152, 2304, "f32", F32),       # fp32 precision
+]
+
+
+@pytest.mark.parametrize("rows,D,H,xdt,prec", MLP_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}_{c[3]}" for c in MLP_CASES])
+@pytest.mark.parametrize("residual", [False, True])
+def test_mlp(P, rows, D, H, xdt, prec, residual):
+    wl = _wl(D=D, dtype="bf16" if prec == BF16 else "f32")
+    announce(f"mlp rows={rows} D={D} H={H} x={xdt} prec={prec} residual={residual}")
+    rng = np.random.default_rng(rows + H)
+    x = rng.standard_normal((rows, D)).astype(np.float32)
+    if xdt == "bf16":
+        x = round_bf16(x)
+    w = make_mlp_weights(wl, hidden=H, seed_base=900 + D)
+    mw = P.MlpWeights.from_dict(w, prec, "cuda")
+    got = P.mlp(dev(x, BF16 if xdt == "bf16" else F32), mw, residual=residual, out_dtype=F32)
+    # the first map reads x rounded to bf16 (bf16 precision), as every projection does
+    xin = round_bf16(x) if prec == BF16 else x
+    ref = O.mlp(xin, w, residual=False) + (x if residual else 0.0)
+    assert_close(host(got), ref, f"mlp {rows}x{D}x{H}")
+
+
+def test_mlp_lowp_copies(P):
+    """x_lowp (bf16 copy of an fp32 x) gives the same result as x itself;
+    out_lowp receives bf16(out)."""
+    wl = _wl()
+    x = np.random.default_rng(5).standard_normal((2304, 1152)).astype(np.float32)
+    w = make_mlp_weights(wl, seed_base=950)
+    mw = P.MlpWeights.from_dict(w, BF16, "cuda")
+    xd = dev(x, F32)
+    plain = P.mlp(xd, mw, out_dtype=F32)
+    ol = torch.full(xd.shape, 7.0, dtype=BF16, device="cuda")
+    got = P.mlp(xd, mw, out_dtype=F32, x_lowp=xd.to(BF16), out_lowp=ol)
+    assert torch.equal(plain, got)
+    assert torch.equal(ol.view(torch.int16), got.to(BF16).view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["img256_f32", "img1024", "img2048"])
+def test_full_block_vs_oracle(P, name):
+    """GIIM, TCM, then the text cross-attention over 120 caption tokens and
+    the MLP (readings R-text, R-mlp) against the oracle's full block."""
+    wl = WORKLOADS[name]
+    prec = _prec(wl)
+    announce(f"full block {name}")
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    text = make_text(wl)
+    wt = make_weights(wl, 4)
+    wm = make_mlp_weights(wl)
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=prec,
+                             text=text, text_weights=wt, mlp_weights=wm)
+    blk.forward(dev(x, prec))
+    torch.cuda.synchronize()
+    ref = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads, text=text, w_text=wt, w_mlp=wm)
+    inter = blk.intermediates()
+    for k in ("x3", "x4", "x5"):
+        assert_close(host(inter[k]), ref[k], f"{name}.{k}")
+    assert_close(host(inter["x5"]) - x, ref["x5"] - x, f"{name}.branches")
 
 
 # ----------------------------------------------------------------------------- roll (bit-exact)
