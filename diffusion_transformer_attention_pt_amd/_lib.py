@@ -75,7 +75,7 @@ def load() -> ctypes.CDLL:
         "ptdit_proxy_select": [vp, i32, G, W3, vp, vp, i32, vp],
         "ptdit_mlp": [vp, vp, i32, i64, i32, i32, MW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_proxy_sa": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
-        "ptdit_proxy_xattn": [vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
+        "ptdit_proxy_xattn": [vp, vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_window_sa": [vp, vp, i32, G, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_shift_window_sa": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_roll3d": [vp, G, W3, i32, vp, i32, vp],
@@ -281,8 +281,9 @@ def proxy_sa(P: torch.Tensor, heads: int, w: AttnWeights, residual: bool = True,
 def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnWeights,
                 residual: bool = True, out_dtype: Optional[torch.dtype] = None,
                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out_lowp: optional bf16 tensor of out's shape that receives bf16(out)."""
+                out_lowp: Optional[torch.Tensor] = None, x_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out_lowp: optional bf16 tensor of out's shape that receives bf16(out);
+    x_lowp: optional bf16 copy of an fp32 x, read by the query projection."""
     lib = load()
     M = P2.shape[1]
     if out is None:
@@ -290,7 +291,7 @@ def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnW
     need = workspace_bytes(OP_PROXY_XATTN, grid, M, (1, 1, 1), w.dtype)
     ws = _ws(need, ws, x.device)
     cw = w.c()
-    st = lib.ptdit_proxy_xattn(_ptr(x), _dt(x.dtype), Grid(*grid), _ptr(P2), _dt(P2.dtype), M,
+    st = lib.ptdit_proxy_xattn(_ptr(x), _ptr(x_lowp), _dt(x.dtype), Grid(*grid), _ptr(P2), _dt(P2.dtype), M,
                                ctypes.byref(cw), int(residual), _ptr(out), _ptr(out_lowp), _dt(out.dtype),
                                _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
     _check("ptdit_proxy_xattn", st)

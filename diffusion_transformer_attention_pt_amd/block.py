@@ -83,6 +83,7 @@ class PTBlockAttention:
             self.hidden = self.w_mlp.hidden
             self.x4 = torch.empty_like(self.x1)
             self.x5 = torch.empty_like(self.x1)
+            self.x3_lowp = torch.empty_like(self.x1_lowp) if lowp else None
             self.x4_lowp = torch.empty_like(self.x1_lowp) if lowp else None
             need += [_lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.L, (1, 1, 1), prec),
                      _lib.workspace_bytes(_lib.OP_MLP, (B * self.N, 1, 1, 1, D, 1), self.hidden, (1, 1, 1), prec)]
@@ -100,11 +101,11 @@ class PTBlockAttention:
         _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2,
                        x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
         _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3,
-                             x_lowp=self.x2_lowp)
+                             x_lowp=self.x2_lowp, out_lowp=self.x3_lowp if self.full else None)
         if not self.full:
             return self.x3
         _lib.proxy_xattn(self.x3, g, self.text, self.w_text, residual=True, ws=self.ws, out=self.x4,
-                         out_lowp=self.x4_lowp)
+                         out_lowp=self.x4_lowp, x_lowp=self.x3_lowp)
         _lib.mlp(self.x4, self.w_mlp, residual=True, ws=self.ws, out=self.x5, x_lowp=self.x4_lowp)
         return self.x5
 

@@ -360,7 +360,7 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
   return hip_status(e);
 }
 
-ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                                const void* proxies, ptdit_dtype p_dt, int32_t M,
                                const ptdit_attn_w* w, int32_t add_residual,
                                void* out, void* out_lowp, ptdit_dtype out_dt,
@@ -377,13 +377,15 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
   if (!x || !proxies || !out) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(proxies) || !aligned16(out) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
   if ((st = check_lowp(prec, out_lowp, out_dt))) return st;
+  if ((st = check_lowp(prec, x_lowp, x_dt))) return st;
   const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_XATTN, g, M, ptdit_win3{1, 1, 1}, prec);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
   const size_t ob = rows * g.D * esize(out_dt), lb = rows * g.D * 2;
   const size_t xb = rows * g.D * esize(x_dt), pb = (size_t)g.B * M * g.D * esize(p_dt);
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, proxies, pb) || overlaps(out, ob, ws, need) ||
       overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, proxies, pb) ||
-      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need))
+      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need) || overlaps(out, ob, x_lowp, lb) ||
+      overlaps(out_lowp, lb, x_lowp, lb))
     return PTDIT_ERR_ALIAS;
 
   const int D = g.D, heads = g.heads, dh = D / heads;
@@ -392,9 +394,10 @@ ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
   void* q = wsp;
   void* kv = wsp + align_up((size_t)rows * D * es);
   void* o = (char*)kv + align_up((size_t)g.B * 2 * M * D * es);
-  // Q = x Wq^T + bq (rows 0..D-1 of w_qkv), head-major [B][1][heads][N][dh]
-  hipError_t e = gemm(prec, x, x_dt, rows, D, D, w->w_qkv, w->b_qkv, nullptr, prec, q, prec, true, N,
-                      heads, D, PTDIT_K_GEMM_Q, stream);
+  // Q = x Wq^T + bq (rows 0..D-1 of w_qkv), head-major [B][1][heads][N][dh];
+  // the projection reads bf16(x), which x_lowp, when given, already holds
+  hipError_t e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, D, w->w_qkv, w->b_qkv,
+                      nullptr, prec, q, prec, true, N, heads, D, PTDIT_K_GEMM_Q, stream);
   if (e != hipSuccess) return PTDIT_ERR_HIP;
   // K, V = P' W_{k,v}^T + b_{k,v} (rows D..3D-1), head-major [B][2][heads][M][dh]
   e = gemm(prec, proxies, p_dt, (int64_t)g.B * M, D, 2 * D, offset_elems(w->w_qkv, (int64_t)D * D, prec),

@@ -515,7 +515,7 @@ constexpr int FS_MAXK = 256, FS_KT = FS_MAXK / 16;
 template <int DH>
 __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams prm, int q_per_wg) {
   using P = BF16P<DH>;
-  constexpr int NT = FW_WAVES * 64, NKC = P::NKC, NDT = P::NDT, DCH = P::DCH;
+  constexpr int NT = FW_WAVES * 64, NDT = P::NDT, DCH = P::DCH;
   constexpr int VTP = FS_MAXK + 4;
   // With a padded head (72 -> 80 rows of V^T), row DH of V^T is all ones, so
   // row DH of O^T = V^T P^T is the softmax denominator: the sum of the very
@@ -533,37 +533,71 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams p
   const int qbeg = blockIdx.x * q_per_wg;
   const int qend = min(prm.Nq, qbeg + q_per_wg);
 
-  auto load_qf = [&](int qblk, typename P::QF* qf) {
+  // Q fragments: NKF chunks of 32 head dims for the 16x16x32 MFMA and, for
+  // DH = 32 NKF + 8, the last 8 dims for one 16x16x16 MFMA (lane group g
+  // holds dims 32 NKF + 4g .. +3; groups 2, 3 zero)
+  constexpr bool TAIL = DH % 32 == 8;
+  constexpr int NKF = DH / 32;
+  static_assert(TAIL || DH % 32 == 0, "head dim 32k or 32k + 8");
+  uint4 qv[2][NKF];
+  uint2 qtl[2];
+  auto load_qf = [&](int qblk) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int q = qblk + wave * FW_QPW + t * 16 + lr;
-      qf[t] = P::load_q(q < qend ? Qb + (int64_t)q * DH : nullptr, lane);
+      const bool ok = q < qend;
+      const uint16_t* row = Qb + (int64_t)q * DH;
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc)
+        qv[t][kc] = ok ? *reinterpret_cast<const uint4*>(row + kc * 32 + 8 * g) : uint4{0, 0, 0, 0};
+      qtl[t] = TAIL && ok && g < 2 ? *reinterpret_cast<const uint2*>(row + NKF * 32 + 4 * g) : uint2{0, 0};
     }
   };
-  typename P::QF qf[2];
-  load_qf(qbeg, qf);
+  load_qf(qbeg);
 
-  // stage K (chunks) and V^T (four keys per item) of all key slots, zero past Nk
-  for (int it = tid; it < FS_MAXK * DCH; it += NT) {
-    const int key = it / DCH, c = it % DCH;
-    ks[it] = key < prm.Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
-  }
-  for (int it = tid; it < DCH * (FS_MAXK / 4); it += NT) {
-    const int c = it / (FS_MAXK / 4), kq = it % (FS_MAXK / 4);
-    uint4 v[4];
+  // stage K (chunks) and V^T (four keys per item) of all key slots, zero past
+  // Nk: every load first, then the LDS writes (one load latency)
+  {
+    constexpr int KI = (FS_MAXK * DCH + NT - 1) / NT, VI = (DCH * (FS_MAXK / 4) + NT - 1) / NT;
+    uint4 kr[KI], vr[VI][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = kq * 4 + e;
-      v[e] = key < prm.Nk ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + i * NT;
+      const int key = it / DCH, c = it % DCH;
+      kr[i] = it < FS_MAXK * DCH && key < prm.Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8)
+                                                 : uint4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sh = (j & 1) * 16;
-      const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&v[0])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&v[1])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&v[2])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&v[3])[j >> 1] >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(&vt[c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      const int c = it / (FS_MAXK / 4), kq = it % (FS_MAXK / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kq * 4 + e;
+        vr[i][e] = it < DCH * (FS_MAXK / 4) && key < prm.Nk
+                       ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8)
+                       : uint4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + i * NT;
+      if (it < FS_MAXK * DCH) ks[it] = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      if (it >= DCH * (FS_MAXK / 4)) continue;
+      const int c = it / (FS_MAXK / 4), kq = it % (FS_MAXK / 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = (j & 1) * 16;
+        const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&vr[i][0])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&vr[i][1])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&vr[i][2])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&vr[i][3])[j >> 1] >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(&vt[c * 8 + j][kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      }
     }
   }
   for (int i = tid; i < (NDT * 16 - DH) * VTP; i += NT)
@@ -572,13 +606,12 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams p
 
   const float c2 = prm.sl2;
   const bool masked = prm.Nk < FS_MAXK;  // uniform
-  auto load_kf = [&](int kt, uint4* kf) {
+  struct KFr { uint4 v[NKF]; uint2 tail; };
+  auto load_kf = [&](int kt, KFr& kf) {
     const int key = kt * 16 + lr;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int d = kc * 32 + 8 * g;
-      kf[kc] = d < DH ? ks[key * DCH + d / 8] : uint4{0, 0, 0, 0};
-    }
+    for (int kc = 0; kc < NKF; ++kc) kf.v[kc] = ks[key * DCH + kc * 4 + g];
+    kf.tail = TAIL && g < 2 ? reinterpret_cast<const uint2*>(&ks[key * DCH + NKF * 4])[g] : uint2{0, 0};
   };
   auto load_vf = [&](int u, uint4* vf) {
     const int kbase = u * 32 + 4 * g;
@@ -594,21 +627,22 @@ __global__ void __launch_bounds__(FW_WAVES * 64) flash_bf16_single(FlashParams p
   for (int qblk = qbeg; qblk < qend; qblk += FW_Q) {
     // S^T for all 256 key slots of both query tiles
     floatx4 sc[2][FS_KT];
-    uint4 kf[2][NKC];
+    KFr kf[2];
     load_kf(0, kf[0]);
 #pragma unroll
     for (int kt = 0; kt < FS_KT; ++kt) {
       if (kt + 1 < FS_KT) load_kf(kt + 1, kf[(kt + 1) & 1]);
-      sc[0][kt] = zero4();
-      sc[1][kt] = zero4();
+      const KFr& f = kf[kt & 1];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        sc[0][kt] = mfma_bf16(kf[kt & 1][kc], qf[0].v[kc], sc[0][kt]);
-        sc[1][kt] = mfma_bf16(kf[kt & 1][kc], qf[1].v[kc], sc[1][kt]);
+      for (int t = 0; t < 2; ++t) sc[t][kt] = TAIL ? mfma_bf16_k16(f.tail, qtl[t], zero4()) : zero4();
+#pragma unroll
+      for (int kc = 0; kc < NKF; ++kc) {
+        sc[0][kt] = mfma_bf16(f.v[kc], qv[0][kc], sc[0][kt]);
+        sc[1][kt] = mfma_bf16(f.v[kc], qv[1][kc], sc[1][kt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (qblk + FW_Q < qend) load_qf(qblk + FW_Q, qf);  // next block; scores no longer need qf
+    if (qblk + FW_Q < qend) load_qf(qblk + FW_Q);  // next block; scores no longer need the Q fragments
     if (masked) {
 #pragma unroll
       for (int kt = 0; kt < FS_KT; ++kt)
@@ -759,27 +793,48 @@ __global__ void __launch_bounds__(FW_WAVES * 64, 1) flash_bf16_pp(FlashParams pr
   load_qf(qbeg);
 
   // stage K (chunks) and V^T (four keys per item) of every key slot, zeros
-  // past Nk; row DH of V^T is all ones, rows past it zero
-  for (int it = tid; it < keys * DCH; it += NT) {
-    const int key = it / DCH, c = it % DCH;
-    ks[it] = key < Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
-  }
-  for (int it = tid; it < DCH * (keys / 4); it += NT) {
-    const int c = it / (keys / 4), kq = it % (keys / 4);
-    uint4 v[4];
+  // past Nk; row DH of V^T is all ones, rows past it zero. Every load first,
+  // then the LDS writes (one load latency).
+  {
+    constexpr int KI = (FP_MAXK * DCH + NT - 1) / NT, VI = (DCH * (FP_MAXK / 4) + NT - 1) / NT;
+    uint4 kr[KI], vr[VI][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = kq * 4 + e;
-      v[e] = key < Nk ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8) : uint4{0, 0, 0, 0};
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + i * NT;
+      const int key = it / DCH, c = it % DCH;
+      kr[i] = it < keys * DCH && key < Nk ? *reinterpret_cast<const uint4*>(Kb + (int64_t)key * DH + c * 8)
+                                          : uint4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sh = (j & 1) * 16;
-      const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&v[0])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&v[1])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&v[2])[j >> 1] >> sh) & 0xffffu;
-      const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&v[3])[j >> 1] >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(&vt[(c * 8 + j) * vtp + kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      const int c = it / (keys / 4), kq = it % (keys / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kq * 4 + e;
+        vr[i][e] = it < DCH * (keys / 4) && key < Nk ? *reinterpret_cast<const uint4*>(Vb + (int64_t)key * DH + c * 8)
+                                                     : uint4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int it = tid + i * NT;
+      if (it < keys * DCH) ks[it] = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int it = tid + i * NT;
+      if (it >= DCH * (keys / 4)) continue;
+      const int c = it / (keys / 4), kq = it % (keys / 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = (j & 1) * 16;
+        const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&vr[i][0])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&vr[i][1])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&vr[i][2])[j >> 1] >> sh) & 0xffffu;
+        const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&vr[i][3])[j >> 1] >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(&vt[(c * 8 + j) * vtp + kq * 4]) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      }
     }
   }
   for (int i = tid; i < (NDT * 16 - DH) * vtp; i += NT) vt[DH * vtp + i] = i < vtp ? (uint16_t)0x3f80u : (uint16_t)0;

@@ -201,9 +201,12 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
  * linear_1_visual): every token is a query, the M attended proxies are keys
  * and values:  out = MHA(x, P') (+ x when add_residual != 0).
  *   x        [B][N][D], dtype x_dt;  proxies [B][M][D], dtype p_dt
+ *   x_lowp   optional bf16 copy of an fp32 x, read by the query projection
  *   out      [B][N][D], dtype out_dt;  out_lowp: optional bf16 copy of out
+ * The same call serves the PT-Block's text cross-attention, with the caption
+ * embeddings [B][L][D] in place of the proxies (M = L).
  */
-ptdit_status ptdit_proxy_xattn(const void* x, ptdit_dtype x_dt, ptdit_grid g,
+ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                                const void* proxies, ptdit_dtype p_dt, int32_t M,
                                const ptdit_attn_w* w, int32_t add_residual,
                                void* out, void* out_lowp, ptdit_dtype out_dt,

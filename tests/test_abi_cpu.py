@@ -105,12 +105,18 @@ def test_host_validation_rejects_before_launch(lib):
     assert win(xl=None, ol=ctypes.c_void_p((1 << 41) + 4096)) == -8   # out_lowp inside x
     assert win(ol=lo) == -8                                   # out_lowp is x_lowp
     assert win(xl=ctypes.c_void_p((1 << 42) + 4096)) == -8    # out inside x_lowp's range
-    assert lib.ptdit_proxy_xattn(x32, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, ctypes.c_void_p(1 << 44),
+    assert lib.ptdit_proxy_xattn(x32, None, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, ctypes.c_void_p(1 << 44),
                                  1, ctypes.c_void_p(1 << 44), 1 << 30, 0, None) == -8  # out_lowp is the ws
-    assert lib.ptdit_proxy_xattn(x32, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, lo, 0, ws, 1 << 30, 0,
+    assert lib.ptdit_proxy_xattn(x32, None, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, lo, 0, ws, 1 << 30, 0,
                                  None) == -4                 # out_lowp beside a bf16 out
+    assert lib.ptdit_proxy_xattn(fake, lo, 0, g, fake, 0, 256, ctypes.byref(w), 1, o32, None, 1, ws, 1 << 30, 0,
+                                 None) == -4                 # x_lowp beside a bf16 x
+    assert lib.ptdit_proxy_xattn(x32, ctypes.c_void_p((1 << 43) + 8), 1, g, fake, 0, 256, ctypes.byref(w), 1,
+                                 o32, None, 1, ws, 1 << 30, 0, None) == -5   # misaligned x_lowp
+    assert lib.ptdit_proxy_xattn(x32, lo, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, lo, 1, ws, 1 << 30, 0,
+                                 None) == -8                 # out_lowp is x_lowp
     # cross-attention with no proxies
-    assert lib.ptdit_proxy_xattn(fake, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, None, 0, fake, 1 << 30, 0,
+    assert lib.ptdit_proxy_xattn(fake, None, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, None, 0, fake, 1 << 30, 0,
                                  None) == -2
     # null weights
     assert lib.ptdit_proxy_sa(fake, 0, 1, 256, 1152, 16, None, 1, fake, 0, fake, 1 << 30, 0, None) == -1

@@ -322,7 +322,7 @@ def test_lowp_copies(P, name):
 
     plain = P.proxy_xattn(x, g, Pd, aw[1], out_dtype=F32)
     ol = torch.full(x.shape, 7.0, dtype=BF16, device="cuda")
-    out = P.proxy_xattn(x, g, Pd, aw[1], out_dtype=F32, out_lowp=ol)
+    out = P.proxy_xattn(x, g, Pd, aw[1], out_dtype=F32, out_lowp=ol, x_lowp=xl)
     check(plain, out, ol, "proxy_xattn")
     plain = P.window_sa(x, g, wl.win, aw[2], out_dtype=F32)
     ol = torch.full(x.shape, 7.0, dtype=BF16, device="cuda")
