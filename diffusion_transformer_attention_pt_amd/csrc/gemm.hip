@@ -854,53 +854,104 @@ struct GemmF32Params {
   int act;
 };
 
-template <bool HEADMAJOR>
+template <bool HEADMAJOR, int BM>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmF32Params p) {
-  constexpr int BM = 64, BN = 64, BK = 16, LD = BK + 1;
-  __shared__ float As[BM * LD];
-  __shared__ float Ws[BN * LD];
+  // BM x 64 tile (BM = 64: 4 waves of 32x32; BM = 32, for few rows: 4 waves
+  // of 32x16), k-slices of 32 through a double-buffered LDS; the global
+  // loads of slice k+2 are issued before slice k is computed (two register
+  // sets), so each load has two slices of MFMA work to land.
+  constexpr int BN = 64, BK = 32, LD = BK + 1;
+  constexpr int WMN = BM / 32, WNN = 4 / WMN;     // waves along m and n
+  constexpr int FN = BN / WNN / 16, FM = 2;       // 16x16 blocks per wave
+  constexpr int RA = BM / 32;                     // A row groups of 32 per thread
+  __shared__ float As[2][BM * LD];
+  __shared__ float Ws[2][BN * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMN, wn = wave / WMN;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  floatx4 acc[2][2];
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
+  floatx4 acc[FN][FM];
+  for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j) acc[i][j] = zero4();
 
-  const int lrow = tid >> 2, lc = (tid & 3) * 4;
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    {
-      int64_t gm = m0 + lrow;
-      gm = gm < p.M ? gm : p.M - 1;
-      int gn = n0 + lrow;
-      gn = gn < p.N ? gn : p.N - 1;
-      const int k = k0 + lc;
-      float4 a = k < p.K ? *reinterpret_cast<const float4*>(p.A + gm * p.K + k) : float4{0, 0, 0, 0};
-      float4 w = k < p.K ? *reinterpret_cast<const float4*>(p.W + (int64_t)gn * p.K + k) : float4{0, 0, 0, 0};
-      As[lrow * LD + lc + 0] = a.x; As[lrow * LD + lc + 1] = a.y;
-      As[lrow * LD + lc + 2] = a.z; As[lrow * LD + lc + 3] = a.w;
-      Ws[lrow * LD + lc + 0] = w.x; Ws[lrow * LD + lc + 1] = w.y;
-      Ws[lrow * LD + lc + 2] = w.z; Ws[lrow * LD + lc + 3] = w.w;
+  // thread t moves rows (t >> 3) + 32 r, columns 4 * (t & 7) .. +3
+  const int lrow = tid >> 3, lc = (tid & 7) * 4;
+  int64_t ga[RA];
+  int64_t gw[2];
+#pragma unroll
+  for (int r = 0; r < RA; ++r) {
+    const int64_t gm = m0 + lrow + 32 * r;
+    ga[r] = (gm < p.M ? gm : p.M - 1) * p.K;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int gn = n0 + lrow + 32 * r;
+    gw[r] = (int64_t)(gn < p.N ? gn : p.N - 1) * p.K;
+  }
+  struct Slice { float4 a[RA], w[2]; };
+  auto gload = [&](int k0, Slice& sl) {
+    const int k = k0 + lc;
+    const bool ok = k < p.K;  // K % 4 == 0: a chunk is in or out as a whole
+#pragma unroll
+    for (int r = 0; r < RA; ++r)
+      sl.a[r] = ok ? *reinterpret_cast<const float4*>(p.A + ga[r] + k) : float4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sl.w[r] = ok ? *reinterpret_cast<const float4*>(p.W + gw[r] + k) : float4{0, 0, 0, 0};
+  };
+  auto lstore = [&](int buf, const Slice& sl) {
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+      float* ad = &As[buf][(lrow + 32 * r) * LD + lc];
+      ad[0] = sl.a[r].x; ad[1] = sl.a[r].y; ad[2] = sl.a[r].z; ad[3] = sl.a[r].w;
     }
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float* wd = &Ws[buf][(lrow + 32 * r) * LD + lc];
+      wd[0] = sl.w[r].x; wd[1] = sl.w[r].y; wd[2] = sl.w[r].z; wd[3] = sl.w[r].w;
+    }
+  };
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kq = 0; kq < BK / 4; ++kq) {
       const int k = kq * 4 + (lane >> 4);
-      float wf[2], xf[2];
-      for (int i = 0; i < 2; ++i) wf[i] = Ws[(wn * 32 + i * 16 + (lane & 15)) * LD + k];
-      for (int j = 0; j < 2; ++j) xf[j] = As[(wm * 32 + j * 16 + (lane & 15)) * LD + k];
-      for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(wf[i], xf[j], acc[i][j]);
+      float wf[FN], xf[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wf[i] = Ws[buf][(wn * FN * 16 + i * 16 + (lane & 15)) * LD + k];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) xf[j] = As[buf][(wm * 32 + j * 16 + (lane & 15)) * LD + k];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_f32(wf[i], xf[j], acc[i][j]);
     }
-    __syncthreads();
+  };
+
+  const int KT = (p.K + BK - 1) / BK;
+  Slice sl[2];
+  gload(0, sl[0]);
+  if (KT > 1) gload(BK, sl[1]);
+  lstore(0, sl[0]);
+  __syncthreads();
+  // slice kt: computed from LDS buffer kt % 2; sl[(kt + 1) % 2] holds slice kt+1
+  for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = kt + u;
+      if (k >= KT) break;
+      if (k + 2 < KT) gload((k + 2) * BK, sl[u]);  // sl[u] (slice k) is already in LDS
+      compute(u);
+      if (k + 1 < KT) lstore(u ^ 1, sl[u ^ 1]);
+      __syncthreads();
+    }
   }
-  for (int i = 0; i < 2; ++i) {
-    const int n = n0 + wn * 32 + i * 16 + 4 * (lane >> 4);
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * FN * 16 + i * 16 + 4 * (lane >> 4);
     if (n >= p.N) continue;
     float4 bv = p.bias ? *reinterpret_cast<const float4*>(p.bias + n) : float4{0, 0, 0, 0};
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < FM; ++j) {
       const int64_t m = m0 + wm * 32 + j * 16 + (lane & 15);
       if (m >= p.M) continue;
       float v0 = acc[i][j][0] + bv.x, v1 = acc[i][j][1] + bv.y;
@@ -1033,12 +1084,20 @@ hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s) {
   p.Ntok = d.Ntok > 0 ? d.Ntok : 1;
   p.heads = d.heads; p.dh = d.dh; p.D = d.D;
   p.act = d.act;
-  const int64_t tiles = ((p.M + 63) / 64) * (int64_t)((p.N + 63) / 64);
+  // 32-row tiles (twice the workgroups) when 64-row tiles would leave fewer
+  // than two workgroups per CU: proxy rows, and the output projections of
+  // short token sequences
+  const bool small = ((p.M + 63) / 64) * (int64_t)((p.N + 63) / 64) < 512;
+  const int bm = small ? 32 : 64;
+  const int64_t tiles = ((p.M + bm - 1) / bm) * (int64_t)((p.N + 63) / 64);
   if (tiles <= 0) return hipSuccess;
-  if (d.head_major)
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, p);
+  if (d.head_major) {
+    if (small) hipLaunchKernelGGL((gemm_f32_kernel<true, 32>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_f32_kernel<true, 64>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  } else {
+    if (small) hipLaunchKernelGGL((gemm_f32_kernel<false, 32>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_f32_kernel<false, 64>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
