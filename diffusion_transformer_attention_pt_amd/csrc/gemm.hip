@@ -252,10 +252,14 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
   }
 }
 
-// Barrier that orders LDS traffic without draining the in-flight DMA ring
-// (the compiler-level "memory" clobbers keep LDS accesses on their side).
+// Barrier that orders LDS traffic without draining the in-flight DMA ring:
+// the wave's own LDS operations complete first (s_waitcnt lgkmcnt(0); this
+// target does not wait for them at s_barrier, and a ds_write of 64 lanes
+// lands in passes of 16), the vector-memory counter is left alone. The
+// compiler-level "memory" clobbers keep LDS accesses on their side.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -1040,8 +1044,11 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
     return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
   // few rows (proxies): a small tile for parallelism; a 4-slot ring measured
   // faster than 8 or 12 slots here (shorter prologue, same streaming rate)
-  if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 4)
+  if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 4) {
+    // 32-row tiles when 64-row tiles would leave under two workgroups per CU
+    if (((p.M + 63) / 64) * (int64_t)((p.N + 63) / 64) < 512) return run_dma<TA, TR, TY, 32, 64, 2, 2, 4, HM>(p, s);
     return run_dma<TA, TR, TY, 64, 64, 2, 2, 4, HM>(p, s);
+  }
   if (p.M >= 1024) return run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s);
   return run_bf16<TA, TR, TY, 64, 64, 2, 2, HM>(p, s);
 }

@@ -219,7 +219,9 @@ def test_roll_bit_exact(P, grid, shift, dt):
                                            # residual folded into the main loop with a ragged
                                            # last row tile (2100 = 8 x 256 + 52; 52 < 64 rows,
                                            # so three of its four row waves hold no real row)
-                                           (2100, 1152, 1152), (2350, 1152, 2304)])
+                                           (2100, 1152, 1152), (2350, 1152, 2304),
+                                           # few rows on 32-row tiles (ragged: 300 = 9 x 32 + 12)
+                                           (300, 1152, 2304)])
 @pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "bf16_res32", "bf16_res16", "f32"])
 def test_linear(P, rows, din, dout, mode):
     """bf16_res32 / bf16_res16: bf16 x with an fp32 / bf16 residual, the two
@@ -252,6 +254,27 @@ def test_linear(P, rows, din, dout, mode):
                          out_dtype=F32)
             ref = O.linear(x, w, b) + round_bf16(r)
     assert_close(host(y), ref, "linear")
+
+
+def test_linear_epilogue_staging_is_ordered(P):
+    """Regression: every wave's LDS writes of the epilogue staging must land
+    before the barrier that lets other waves read them. 512 x 2304 outputs on
+    32-row tiles (several workgroups per CU) exposed a missing wait as a
+    4-row x 16-column block of stale values; repeated launches must agree
+    bit for bit and match the oracle."""
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((512, 1152)).astype(np.float32)
+    w = round_bf16(rng.standard_normal((2304, 1152)).astype(np.float32) * 0.02)
+    b = round_bf16(rng.standard_normal(2304).astype(np.float32) * 0.02)
+    ref = O.linear(round_bf16(x), w, b)
+    wd, bd = dev(w, BF16), dev(b, BF16)
+    for adt in (F32, BF16):
+        xd = dev(x, adt)
+        first = P.linear(xd, wd, bd, out_dtype=F32)
+        assert_close(host(first), ref, "linear 512x2304")
+        for _ in range(20):
+            again = P.linear(xd, wd, bd, out_dtype=F32)
+            assert torch.equal(first, again)
 
 
 # ----------------------------------------------------------------------------- attention calls
