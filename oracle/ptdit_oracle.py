@@ -15,7 +15,7 @@ Proxy-Tokenized DiT for Text-to-Any-Task"), section 3 "Method":
     attention is a cyclic shift, window attention and the inverse shift);
   * the "complexity" paragraph of section 3 for the attention-cost formula.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent (each named below; the tests refer to them by name):
   R-order   tokens are row-major over (f, h, w); proxies row-major over the
             window grid (Figure 2 notes: row-major flattening).
   R-pool32  the window average's kernel precision: float32 sums taken along
