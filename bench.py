@@ -270,7 +270,20 @@ def main() -> int:
         br["pool_cold"] = {"avg_ms": round(cold_ms, 5), "achieved": round(cold_rate, 1), "unit": "GB/s",
                            "peak_frac": round(cold_rate / PEAK_HBM_GBS, 4),
                            "copies": ncopy, "bytes_rotated": ncopy * xbytes}
-        del xs
+        # cold stand-alone roll (the shifted-window attention addresses through
+        # the roll and never materialises it): reads and writes B*N*D elements
+        ys = torch.empty_like(x)
+        _lib.roll3d(xs[0], blk.g, blk.shift, out=ys)
+        e0.record()
+        for i in range(reps):
+            _lib.roll3d(xs[i % ncopy], blk.g, blk.shift, out=ys)
+        e1.record()
+        torch.cuda.synchronize()
+        roll_ms = e0.elapsed_time(e1) / reps
+        roll_rate = 2 * xbytes / (roll_ms * 1e-3) / 1e9
+        br["roll_cold"] = {"avg_ms": round(roll_ms, 5), "achieved": round(roll_rate, 1), "unit": "GB/s",
+                           "peak_frac": round(roll_rate / PEAK_HBM_GBS, 4), "copies": ncopy}
+        del xs, ys
         out["breakdown"] = br
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)

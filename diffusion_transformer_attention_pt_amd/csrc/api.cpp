@@ -451,6 +451,9 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
   const int64_t N = (int64_t)g.F * g.H * g.W;
   if (N > (int64_t)1 << 30) return PTDIT_ERR_SHAPE;
   if (g.B * N == 0) return PTDIT_OK;
+  // the kernel indexes grid rows (b, t, i) and the 16-byte vectors of one row in 32 bits
+  const int64_t vec_per_row = (int64_t)g.W * g.D * esize(dt) / 16;
+  if ((int64_t)g.B * g.F * g.H > INT32_MAX || vec_per_row > INT32_MAX - 1024) return PTDIT_ERR_SHAPE;
   if (!x || !y) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return PTDIT_ERR_ALIGN;
   const size_t bytes = g.B * N * g.D * esize(dt);

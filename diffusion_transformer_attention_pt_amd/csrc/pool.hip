@@ -234,7 +234,12 @@ hipError_t launch_select(const PoolDesc& d, const int32_t* offsets, hipStream_t 
 
 // ----------------------------------------------------------------------------
 // 3D cyclic roll: y[t,i,j] = x[(t+st) mod F, (i+sh) mod H, (j+sw) mod W].
-// One thread per 16-byte vector; shifts arrive already in [0, extent).
+// A roll moves whole grid rows (b, t, i) and rotates the tokens inside a row,
+// so workgroups are laid out per destination row: the source row is one
+// scalar computation per workgroup, and inside the row the source of vector
+// e is e + sw * vec_per_tok, wrapped once by the row length (no division per
+// vector). Each thread moves RU vectors (16 bytes each) with all its loads in
+// flight before the stores.
 // ----------------------------------------------------------------------------
 struct RollParams {
   const uint4* x;
@@ -244,20 +249,40 @@ struct RollParams {
   int st, sh, sw;
 };
 
+constexpr int RU = 4;
+
+__device__ __forceinline__ int roll_src(int e, int shift, int rowlen) {
+  int se = e + shift;
+  return se >= rowlen ? se - rowlen : se;
+}
+
 __global__ void __launch_bounds__(256) roll_kernel(RollParams p) {
-  const int64_t N = (int64_t)p.F * p.H * p.W;
-  const int64_t total = (int64_t)p.B * N * p.vec_per_tok;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int v = (int)(g % p.vec_per_tok);
-    const int64_t bt = g / p.vec_per_tok;
-    const int64_t b = bt / N, n = bt - b * N;
-    const int j = (int)(n % p.W), i = (int)((n / p.W) % p.H), t = (int)(n / ((int64_t)p.W * p.H));
-    int ts = t + p.st; ts -= ts >= p.F ? p.F : 0;
-    int is = i + p.sh; is -= is >= p.H ? p.H : 0;
-    int js = j + p.sw; js -= js >= p.W ? p.W : 0;
-    const int64_t src = b * N + ((int64_t)ts * p.H + is) * p.W + js;
-    p.y[g] = p.x[src * p.vec_per_tok + v];
+  // destination row (b, t, i) = blockIdx.y + gridDim.y * blockIdx.z (the grid
+  // splits rows over two dimensions so that any count fits)
+  const int row = blockIdx.y + gridDim.y * blockIdx.z;
+  if (row >= p.B * p.F * p.H) return;
+  const int i = row % p.H, t = (row / p.H) % p.F, b = row / (p.H * p.F);
+  int ts = t + p.st; ts -= ts >= p.F ? p.F : 0;
+  int is = i + p.sh; is -= is >= p.H ? p.H : 0;
+  const int rowlen = p.W * p.vec_per_tok, shift = p.sw * p.vec_per_tok;
+  const uint4* src = p.x + (int64_t)((b * p.F + ts) * p.H + is) * rowlen;
+  uint4* dst = p.y + (int64_t)row * rowlen;
+  // four 16-byte vectors per lane, all loads issued before any store; the
+  // indices of lanes past the row end are clamped to its last vector so the
+  // loads need no branch, only the stores are predicated
+  const int e = blockIdx.x * (256 * RU) + threadIdx.x, last = rowlen - 1;
+  const uint4 v0 = src[roll_src(min(e, last), shift, rowlen)];
+  const uint4 v1 = src[roll_src(min(e + 256, last), shift, rowlen)];
+  const uint4 v2 = src[roll_src(min(e + 512, last), shift, rowlen)];
+  const uint4 v3 = src[roll_src(min(e + 768, last), shift, rowlen)];
+  if ((blockIdx.x + 1) * (256 * RU) <= rowlen) {
+    // whole chunk inside the row (a workgroup-uniform test): plain stores
+    dst[e] = v0; dst[e + 256] = v1; dst[e + 512] = v2; dst[e + 768] = v3;
+  } else {
+    if (e < rowlen) dst[e] = v0;
+    if (e + 256 < rowlen) dst[e + 256] = v1;
+    if (e + 512 < rowlen) dst[e + 512] = v2;
+    if (e + 768 < rowlen) dst[e + 768] = v3;
   }
 }
 
@@ -268,11 +293,15 @@ hipError_t launch_roll(const RollDesc& d, hipStream_t s) {
   p.B = d.B; p.F = d.F; p.H = d.H; p.W = d.W;
   p.vec_per_tok = d.f32 ? d.D / 4 : d.D / 8;
   p.st = d.st; p.sh = d.sh; p.sw = d.sw;
-  const int64_t total = (int64_t)d.B * d.F * d.H * d.W * p.vec_per_tok;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(roll_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const int64_t rows = (int64_t)d.B * d.F * d.H;
+  const int64_t rowlen = (int64_t)d.W * p.vec_per_tok;
+  if (rows == 0 || rowlen == 0) return hipSuccess;
+  // the kernel indexes rows and in-row vectors in 32 bits
+  if (rows > INT32_MAX || rowlen > INT32_MAX - 1024) return hipErrorInvalidValue;
+  const int64_t gy = rows < 65535 ? rows : 65535, gz = (rows + gy - 1) / gy;
+  if (gz > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((rowlen + 256 * RU - 1) / (256 * RU)), (unsigned)gy, (unsigned)gz);
+  hipLaunchKernelGGL(roll_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -249,7 +249,9 @@ ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtyp
  * stand-alone copy (the attention calls never materialise it):
  * inverse == 0: y[t,i,j] = x[(t+s_t) mod F, (i+s_h) mod H, (j+s_w) mod W];
  * inverse != 0: y[t,i,j] = x[(t-s_t) mod F, ...]. x, y: [B][N][D], dtype dt;
- * bit-exact copy. Requires 0 <= shift, D % 8 == 0.
+ * bit-exact copy. Requires 0 <= shift, D % 8 == 0, F*H*W <= 2^30, B*F*H and
+ * the 16-byte vectors of one grid row (W*D*size/16) below 2^31 - 1024
+ * (PTDIT_ERR_SHAPE otherwise); y must not overlap x (PTDIT_ERR_ALIAS).
  */
 ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,
                           void* y, ptdit_dtype dt, hipStream_t stream);

@@ -148,6 +148,13 @@ def test_host_validation_rejects_before_launch(lib):
                xl=ctypes.c_void_p(1 << 42)) == -4    # x_lowp beside a bf16 x
     assert mlp(None, 0, 1152, 4608, ctypes.byref(mw), None, None, 0) == 0
     assert lib.ptdit_workspace_bytes(4, Grid(100, 1, 1, 1, 1152, 1), 4608, Win3(1, 1, 1), 0) >= 100 * 4608 * 2
+    # roll: negative shift, D % 8, a grid row of 2^31 16-byte vectors (32-bit in-row index),
+    # output inside the input
+    roll = lib.ptdit_roll3d
+    assert roll(fake, g, Win3(0, -1, 0), 0, far, 0, None) == -2
+    assert roll(fake, Grid(1, 1, 16, 16, 1150, 16), Win3(0, 1, 1), 0, far, 0, None) == -2
+    assert roll(fake, Grid(1, 1, 1, 1 << 20, 1 << 14, 16), Win3(0, 0, 1), 0, far, 0, None) == -2
+    assert roll(fake, g, Win3(0, 1, 1), 0, ctypes.c_void_p((1 << 20) + 4096), 0, None) == -8
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
     assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),

@@ -193,16 +193,18 @@ def test_full_block_vs_oracle(P, name):
 
 # ----------------------------------------------------------------------------- roll (bit-exact)
 
-@pytest.mark.parametrize("grid,shift", [((1, 128, 128), (0, 4, 4)), ((16, 30, 45), (1, 4, 4)),
-                                        ((3, 5, 7), (4, 6, 9)), ((2, 8, 8), (0, 0, 0))])
+@pytest.mark.parametrize("grid,shift,B,D", [((1, 128, 128), (0, 4, 4), 1, 64), ((16, 30, 45), (1, 4, 4), 1, 64),
+                                            ((3, 5, 7), (4, 6, 9), 1, 64), ((2, 8, 8), (0, 0, 0), 1, 64),
+                                            # batches; rows longer than one workgroup's span (W*D/8 vectors)
+                                            ((2, 6, 9), (1, 5, 8), 3, 64), ((1, 4, 300), (0, 3, 299), 2, 1152)])
 @pytest.mark.parametrize("dt", [BF16, F32])
-def test_roll_bit_exact(P, grid, shift, dt):
-    announce(f"roll {grid} {shift} {dt}")
-    wl = _wl(F=grid[0], H=grid[1], W=grid[2], D=64)
+def test_roll_bit_exact(P, grid, shift, B, D, dt):
+    announce(f"roll B={B} {grid} {shift} D={D} {dt}")
+    wl = _wl(B=B, F=grid[0], H=grid[1], W=grid[2], D=D)
     x = make_x(wl.scaled(dtype="bf16" if dt == BF16 else "f32"), seed=5)
     xd = dev(x, dt)
     y = P.roll3d(xd, _grid(wl), shift)
-    ref = O.roll3d(x.reshape(1, *grid, 64), shift).reshape(x.shape)
+    ref = O.roll3d(x.reshape(B, *grid, D), shift).reshape(x.shape)
     assert np.array_equal(y.float().cpu().numpy(), ref.astype(np.float32))
     back = P.roll3d(y, _grid(wl), shift, inverse=True)
     assert torch.equal(back, xd)
