@@ -359,6 +359,12 @@ struct DmaPlan {
 // i.e. WM*16 rows x BN columns, row pitch padded by 16 bytes. A bf16 band
 // fills one ring slot, an fp32 band two, so BPP = STAGES (bf16) or STAGES/2
 // (fp32) bands are staged per pass.
+
+typedef unsigned int ntu4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+  ntu4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<ntu4*>(p));
+}
 template <typename TY, int BN, int WM, int STAGES>
 struct EpiShape {
   static constexpr int PITCH = BN + 16 / (int)sizeof(TY);  // elements
@@ -470,7 +476,7 @@ __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4
                 const float4 r = load4f(R + off);
                 o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
               }
-              *reinterpret_cast<float4*>(Y + off) = o;
+              st_nt16(Y + off, __builtin_bit_cast(uint4, o));
               if (p.Y2) store4(p.Y2 + off, o.x, o.y, o.z, o.w);
             } else if (R) {
               float f[8], rv[8];
@@ -743,7 +749,14 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   }
   auto rload = [&](auto bI) -> RV {
     constexpr int b = decltype(bI)::value, i = b % FN, j = b / FN;
-    return *reinterpret_cast<const RV*>(rbase + i * 16 * (int)sizeof(TR) + rlane[j]);
+    const char* ra = rbase + i * 16 * (int)sizeof(TR) + rlane[j];
+    if constexpr (sizeof(TR) == 4) {
+      typedef float ntf4 __attribute__((ext_vector_type(4)));
+      const ntf4 v = __builtin_nontemporal_load(reinterpret_cast<const ntf4*>(ra));
+      return RV{v.x, v.y, v.z, v.w};
+    } else {
+      return *reinterpret_cast<const RV*>(ra);
+    }
   };
   auto radd = [&](auto bI, const RV& v) {  // bI: compile-time block
     constexpr int bb = decltype(bI)::value;

@@ -292,6 +292,10 @@ CALL_CASES = {
     # rows (2400 = 9.4 tiles of 256) and a width that pads to the window
     "bf16_dma_ragged": _wl(H=48, W=50, p=(1, 4, 5)),
     "bf16_dma_video": _wl(F=3, H=30, W=45, p=(1, 5, 5), win=(2, 8, 8), shift=(1, 4, 4)),
+    # 256-row projection tiles that straddle the batch boundary (1600 tokens a
+    # batch), and a head width (64) that does not divide the 288-column tile
+    "bf16_dma_batch2": _wl(B=2, H=40, W=40, p=(1, 4, 4)),
+    "bf16_dma_dh64": _wl(D=1024, heads=16, H=48, W=48, p=(1, 4, 4)),
 }
 
 
