@@ -8,4 +8,7 @@ code with the GPU path (the seeded input generators in synth_inputs.py are the
 only common module, and they hold none of the method's arithmetic).
 """
 from .ptdit_oracle import *  # noqa: F401,F403
-from .ptdit_oracle import __all__  # noqa: F401
+from .ptdit_backward import *  # noqa: F401,F403
+from . import ptdit_backward as _bwd, ptdit_oracle as _fwd
+
+__all__ = list(_fwd.__all__) + list(_bwd.__all__)
