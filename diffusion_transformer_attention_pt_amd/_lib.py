@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libptdit.so")
 
 PTDIT_BF16, PTDIT_F32 = 0, 1
 OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA, OP_MLP = 0, 1, 2, 3, 4
-K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY, K_GEMM_MLP = range(9)
+(K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY, K_GEMM_MLP,
+ K_BWD_WINDOW, K_BWD_DENSE, K_BWD_POOL) = range(12)
 
 STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT_ERR_DIVISIBILITY",
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",
@@ -28,7 +29,8 @@ STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT
 EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_xattn",
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
-            "ptdit_trace_disable"]
+            "ptdit_trace_disable", "ptdit_window_attn_bwd", "ptdit_attn_bwd", "ptdit_attn_bwd_workspace_bytes",
+            "ptdit_proxy_pool_bwd"]
 
 
 class Grid(ctypes.Structure):
@@ -85,12 +87,17 @@ def load() -> ctypes.CDLL:
         "ptdit_trace_enable": [i32, i32],
         "ptdit_trace_read": [ctypes.POINTER(ctypes.c_float), i32],
         "ptdit_trace_disable": [],
+        "ptdit_window_attn_bwd": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
+        "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
+        "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
+        "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = i32
     lib.ptdit_workspace_bytes.restype = sz
+    lib.ptdit_attn_bwd_workspace_bytes.restype = sz
     lib.ptdit_status_str.restype = ctypes.c_char_p
     lib.ptdit_version.restype = ctypes.c_char_p
     lib.ptdit_trace_disable.restype = None
@@ -346,6 +353,74 @@ def roll3d(x: torch.Tensor, grid: Sequence[int], shift: Sequence[int], inverse: 
                           _stream())
     _check("ptdit_roll3d", st)
     return out
+
+
+def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], win: Sequence[int],
+                    shift: Sequence[int] = (0, 0, 0), b_qkv: Optional[torch.Tensor] = None,
+                    d_qkv: Optional[torch.Tensor] = None, d_b_kv: Optional[torch.Tensor] = None):
+    """Backward of the window / shifted-window attention core. qkv [B, 3, heads,
+    N, dh] (the forward's Q/K/V), d_o [B, N, D]. Returns (d_qkv fp32 [B, 3, heads,
+    N, dh], d_b_kv fp32 [2, D]: pad-slot gradients, added to d_b_kv when given)."""
+    lib = load()
+    B, F, H, W, D, heads = grid
+    if d_o.dtype != qkv.dtype or (b_qkv is not None and b_qkv.dtype != qkv.dtype):
+        raise ValueError("qkv, d_o and b_qkv must share one dtype")
+    if d_qkv is None:
+        d_qkv = torch.empty(qkv.shape, dtype=torch.float32, device=qkv.device)
+    if d_b_kv is None:
+        d_b_kv = torch.zeros(2, D, dtype=torch.float32, device=qkv.device)
+    st = lib.ptdit_window_attn_bwd(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid), Win3(*win),
+                                   Win3(*shift), _ptr(d_qkv), _ptr(d_b_kv), _stream())
+    _check("ptdit_window_attn_bwd", st)
+    return d_qkv, d_b_kv
+
+
+def _bhld(t: torch.Tensor, name: str) -> int:
+    """Batch stride (elements) of a [B, heads, L, dh] view whose batch items are contiguous."""
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must live on the GPU")
+    B, h, L, dh = t.shape
+    if t.stride(3) != 1 or t.stride(2) != dh or t.stride(1) != L * dh:
+        raise ValueError(f"{name}: each batch item must be a contiguous [heads, L, dh] block")
+    return t.stride(0)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
+             ws: Optional[torch.Tensor] = None):
+    """Backward of the unmasked attention core (proxy SA, cross-attention).
+    q [B, heads, Nq, dh], k / v [B, heads, Nk, dh] (views into fused buffers
+    allowed), d_o [B, Nq, heads*dh]. Returns fp32 (dq, dk, dv), contiguous."""
+    lib = load()
+    B, heads, Nq, dh = q.shape
+    Nk = k.shape[2]
+    if k.stride(0) != v.stride(0):
+        raise ValueError("k and v must share their batch stride")
+    dq = torch.empty(B, heads, Nq, dh, dtype=torch.float32, device=q.device)
+    dk = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
+    dv = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
+    need = int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh))
+    ws = _ws(need, ws, q.device)
+    if len({q.dtype, k.dtype, v.dtype, d_o.dtype}) != 1:
+        raise ValueError("q, k, v and d_o must share one dtype")
+    q_bs, kv_bs = _bhld(q, "q"), _bhld(k, "k")
+    _bhld(v, "v")
+    st = lib.ptdit_attn_bwd(q.data_ptr(), q_bs, k.data_ptr(), v.data_ptr(), kv_bs, _ptr(d_o), _dt(q.dtype),
+                            B, heads, Nq, Nk, dh, _ptr(dq), heads * Nq * dh, _ptr(dk), _ptr(dv), heads * Nk * dh,
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _check("ptdit_attn_bwd", st)
+    return dq, dk, dv
+
+
+def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int],
+                   d_x: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+    """Backward of the window average: d_x[token] (+)= d_proxies[its proxy] / P (fp32)."""
+    lib = load()
+    B, F, H, W, D, _ = grid
+    if d_x is None:
+        d_x = torch.empty(B, F * H * W, D, dtype=torch.float32, device=d_proxies.device)
+    st = lib.ptdit_proxy_pool_bwd(_ptr(d_proxies), Grid(*grid), Win3(*p), _ptr(d_x), int(accumulate), _stream())
+    _check("ptdit_proxy_pool_bwd", st)
+    return d_x
 
 
 def trace_enable(kernel_class: int, capacity: int) -> None:

@@ -471,6 +471,119 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
   return hip_status(launch_roll(d, stream));
 }
 
+ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv,
+                                   float* d_b_kv, hipStream_t stream) {
+  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+  ptdit_status st = check_grid(g);
+  if (st) return st;
+  if (win.t <= 0 || win.h <= 0 || win.w <= 0) return PTDIT_ERR_SHAPE;
+  if ((int64_t)win.t * win.h * win.w > 128) return PTDIT_ERR_SHAPE;
+  if (shift.t < 0 || shift.h < 0 || shift.w < 0 || shift.t >= win.t || shift.h >= win.h ||
+      shift.w >= win.w)
+    return PTDIT_ERR_SHAPE;
+  const int64_t N = (int64_t)g.F * g.H * g.W, rows = (int64_t)g.B * N;
+  if (rows == 0) return PTDIT_OK;
+  const bool pads = g.F % win.t || g.H % win.h || g.W % win.w;
+  if (!qkv || !d_o || !d_qkv || (pads && !d_b_kv)) return PTDIT_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(d_o) || !aligned16(d_qkv) || !aligned16(b_qkv) || !aligned16(d_b_kv))
+    return PTDIT_ERR_ALIGN;
+  const size_t gb = (size_t)rows * 3 * g.D * 4, bb = (size_t)2 * g.D * 4;
+  if (overlaps(d_qkv, gb, qkv, rows * 3 * g.D * esize(dt)) || overlaps(d_qkv, gb, d_o, rows * g.D * esize(dt)) ||
+      overlaps(d_qkv, gb, b_qkv, 3 * g.D * esize(dt)) || overlaps(d_b_kv, bb, d_qkv, gb) ||
+      overlaps(d_b_kv, bb, qkv, rows * 3 * g.D * esize(dt)) || overlaps(d_b_kv, bb, d_o, rows * g.D * esize(dt)))
+    return PTDIT_ERR_ALIAS;
+  WindowBwdDesc d;
+  d.QKV = qkv; d.bias_qkv = b_qkv; d.dO = d_o; d.dQKV = d_qkv; d.dbias_kv = d_b_kv;
+  d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D; d.heads = g.heads; d.dh = g.D / g.heads;
+  d.wt = win.t; d.wh = win.h; d.ww = win.w;
+  d.st = shift.t; d.sh = shift.h; d.sw = shift.w;
+  d.Fp = (g.F + win.t - 1) / win.t * win.t;
+  d.Hp = (g.H + win.h - 1) / win.h * win.h;
+  d.Wp = (g.W + win.w - 1) / win.w * win.w;
+  d.scale = 1.0f / std::sqrt((float)d.dh);
+  TraceScope ts(PTDIT_K_BWD_WINDOW, stream);
+  return hip_status(launch_window_bwd(d, dt == PTDIT_F32, stream));
+}
+
+namespace {
+constexpr int kBwdQChunk = 1024;  // queries per partial-sum chunk of the key-major kernel
+int bwd_chunks(int Nq) { return Nq <= kBwdQChunk ? 1 : (Nq + kBwdQChunk - 1) / kBwdQChunk; }
+}  // namespace
+
+size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int32_t Nk, int32_t dh) {
+  if (B < 0 || heads <= 0 || Nq < 0 || Nk < 0 || (dh != 64 && dh != 72)) return 0;
+  const int chunks = bwd_chunks(Nq);
+  size_t bytes = align_up((size_t)B * heads * Nq * 3 * 4);
+  if (chunks > 1) bytes += align_up((size_t)chunks * B * heads * Nk * 2 * dh * 4);
+  return bytes < kAlign ? kAlign : bytes;
+}
+
+ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
+                            int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                            int32_t Nq, int32_t Nk, int32_t dh, float* d_q, int64_t dq_bstride, float* d_k,
+                            float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+  if (B < 0 || heads <= 0 || Nq < 0 || Nk < 0 || (dh != 64 && dh != 72)) return PTDIT_ERR_SHAPE;
+  if ((int64_t)B * heads > 65535 || Nq > (1 << 30) || (Nq > 0 && Nk == 0) || bwd_chunks(Nq) > 65535)
+    return PTDIT_ERR_SHAPE;
+  if ((int64_t)B * Nq == 0) return PTDIT_OK;
+  const int64_t hq = (int64_t)heads * Nq * dh, hk = (int64_t)heads * Nk * dh;
+  if (q_bstride < hq || kv_bstride < hk || dq_bstride < hq || dkv_bstride < hk) return PTDIT_ERR_SHAPE;
+  if (!q || !k || !v || !d_o || !d_q || !d_k || !d_v) return PTDIT_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_q) ||
+      !aligned16(d_k) || !aligned16(d_v) || !aligned16(ws))
+    return PTDIT_ERR_ALIGN;
+  const size_t need = ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  const size_t es = esize(dt);
+  const size_t qb = ((B - 1) * q_bstride + hq) * es, kb = ((B - 1) * kv_bstride + hk) * es;
+  const size_t ob = (size_t)B * Nq * heads * dh * es;
+  const size_t dqb = ((B - 1) * dq_bstride + hq) * 4, dkb = ((B - 1) * dkv_bstride + hk) * 4;
+  const void* outs[4] = {d_q, d_k, d_v, ws};
+  const size_t osz[4] = {dqb, dkb, dkb, need};
+  for (int a = 0; a < 4; ++a) {
+    if (overlaps(outs[a], osz[a], q, qb) || overlaps(outs[a], osz[a], k, kb) || overlaps(outs[a], osz[a], v, kb) ||
+        overlaps(outs[a], osz[a], d_o, ob))
+      return PTDIT_ERR_ALIAS;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlaps(outs[a], osz[a], outs[c], osz[c])) return PTDIT_ERR_ALIAS;
+  }
+  DenseBwdDesc d;
+  d.q = q; d.k = k; d.v = v; d.dO = d_o;
+  d.q_bs = q_bstride; d.kv_bs = kv_bstride;
+  d.dq = d_q; d.dk = d_k; d.dv = d_v; d.dq_bs = dq_bstride; d.dkv_bs = dkv_bstride;
+  d.stats = (float*)ws;
+  d.part = (float*)((char*)ws + align_up((size_t)B * heads * Nq * 3 * 4));
+  d.B = B; d.heads = heads; d.Nq = Nq; d.Nk = Nk; d.D = heads * dh; d.dh = dh;
+  d.chunks = bwd_chunks(Nq);
+  d.qchunk = d.chunks == 1 ? Nq : kBwdQChunk;
+  d.scale = 1.0f / std::sqrt((float)dh);
+  TraceScope ts(PTDIT_K_BWD_DENSE, stream);
+  return hip_status(launch_dense_bwd(d, dt == PTDIT_F32, stream));
+}
+
+ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,
+                                  int32_t accumulate, hipStream_t stream) {
+  if (g.B < 0 || g.F < 0 || g.H < 0 || g.W < 0 || g.D <= 0 || g.D % 4) return PTDIT_ERR_SHAPE;
+  if (p.t <= 0 || p.h <= 0 || p.w <= 0) return PTDIT_ERR_SHAPE;
+  if (g.F % p.t || g.H % p.h || g.W % p.w) return PTDIT_ERR_DIVISIBILITY;
+  const int64_t N = (int64_t)g.F * g.H * g.W;
+  if (N > (int64_t)1 << 30 || (int64_t)g.B * N * (g.D / 4) > (int64_t)INT32_MAX * 256) return PTDIT_ERR_SHAPE;
+  if ((int64_t)g.B * N == 0) return PTDIT_OK;
+  if (!d_proxies || !d_x) return PTDIT_ERR_NULL;
+  if (!aligned16(d_proxies) || !aligned16(d_x)) return PTDIT_ERR_ALIGN;
+  const int64_t M = N / ((int64_t)p.t * p.h * p.w);
+  if (overlaps(d_x, g.B * N * g.D * 4, d_proxies, g.B * M * g.D * 4)) return PTDIT_ERR_ALIAS;
+  PoolBwdDesc d;
+  d.dP = d_proxies; d.dx = d_x;
+  d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D;
+  d.pt = p.t; d.ph = p.h; d.pw = p.w;
+  d.accumulate = accumulate != 0;
+  TraceScope ts(PTDIT_K_BWD_POOL, stream);
+  return hip_status(launch_pool_bwd(d, stream));
+}
+
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity) {
   ptdit_trace_disable();
   if (capacity <= 0 || kernel_class < 0) return PTDIT_ERR_SHAPE;

@@ -1,0 +1,542 @@
+// Backward pass of the PT-DiT attention core (Qihoo-T2X reading note,
+// section 3 "Method": Eq. GIIM and Eq. TCM; the pages train the model at
+// 2048^2, section 4). The gradients are those of the forward maps: with
+// S = Q K^T * scale, A = softmax(S) over the allowed keys and O = A V,
+//   dV = A^T dO,  dA = dO V^T,  dS = A * (dA - rowsum(A * dA)),
+//   dQ = dS K * scale,  dK = dS^T Q * scale   (per head).
+// The softmax is recomputed from Q and K (nothing of the forward is kept but
+// its inputs), exactly: every kernel takes the row maximum and sum over all
+// keys before it forms a weight. Arithmetic is fp32; the gradients are fp32.
+//
+//   window_bwd_kernel  WSA / SWSA core: one workgroup per (window, head,
+//                      batch) with the window's Q, K, V, dO in LDS; a
+//                      query-major phase (softmax statistics, dQ) and a
+//                      key-major phase (dK, dV). The roll, padding and
+//                      boundary mask are the forward's addressing; the
+//                      gradient of a pad key/value slot (the bias b_k/b_v)
+//                      is added into d_bias_kv.
+//   dense_bwd_q_kernel proxy SA / cross-attention, query-major: statistics
+//                      and dQ, keys streamed through LDS in 64-key chunks.
+//   dense_bwd_kv_kernel key-major: dK, dV of 64 keys over one chunk of the
+//                      queries (partial sums when the queries are split).
+//   dense_bwd_reduce   fixed-order sum of the partials (deterministic).
+//   pool_bwd_kernel    window average: dx[token] (+)= dP[its proxy] / P.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ptdit {
+
+namespace {
+
+constexpr int BW_NT = 256;  // threads per workgroup of every kernel here
+
+// sum / max over the G consecutive lanes of a group (G = 1, 2, 4, 8)
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int region_of(int k, int L, int w, int s) {
+  return k < L - w ? 0 : (k < L - s ? 1 : 2);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// Window attention backward
+// ----------------------------------------------------------------------------
+struct WindowBwdParams {
+  const void* QKV;       // [B][3][heads][N][dh]
+  const void* bias_qkv;  // [3D] or null (pad keys/values are b_k/b_v, else 0)
+  const void* dO;        // [B][N][D]
+  float* dQKV;           // [B][3][heads][N][dh]
+  float* dbias_kv;       // [2][D], accumulated into; null when nothing pads
+  int F, H, W, D, heads;
+  int wt, wh, ww;
+  int st, sh, sw;
+  int Fp, Hp, Wp;
+  float scale;
+};
+
+template <typename T, int DH, int KEYS>
+__global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
+  constexpr int PI = DH + 1;           // LDS row pitch in floats (odd: rows spread over the banks)
+  constexpr int G = BW_NT / KEYS;      // threads per query (phase 1) and per key (phase 2)
+  constexpr int PER = KEYS / G;        // keys per thread in phase 1
+  __shared__ float qs[KEYS * PI], ks[KEYS * PI], vs[KEYS * PI], gs[KEYS * PI];
+  __shared__ int tok_s[KEYS], lab_s[KEYS];
+  __shared__ float m_s[KEYS], l_s[KEYS], d_s[KEYS];
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int nWh = p.Hp / p.wh, nWw = p.Wp / p.ww;
+  const int Tw = blockIdx.x / (nWh * nWw), Iw = (blockIdx.x / nWw) % nWh, Jw = blockIdx.x % nWw;
+  const int wsz = p.wt * p.wh * p.ww;
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const bool masked = (p.st | p.sh | p.sw) != 0;
+
+  // slot s of the window -> token (-1: pad, -2: past the window), region label
+  for (int s = tid; s < KEYS; s += BW_NT) {
+    int tok = -2, lab = 0;
+    if (s < wsz) {
+      const int a = s / (p.wh * p.ww), c = (s / p.ww) % p.wh, e = s % p.ww;
+      const int rt = Tw * p.wt + a, ri = Iw * p.wh + c, rj = Jw * p.ww + e;
+      int ot = rt + p.st; ot -= ot >= p.Fp ? p.Fp : 0;
+      int oi = ri + p.sh; oi -= oi >= p.Hp ? p.Hp : 0;
+      int oj = rj + p.sw; oj -= oj >= p.Wp ? p.Wp : 0;
+      tok = (ot < p.F && oi < p.H && oj < p.W) ? (ot * p.H + oi) * p.W + oj : -1;
+      lab = region_of(rt, p.Fp, p.wt, p.st) * 9 + region_of(ri, p.Hp, p.wh, p.sh) * 3 +
+            region_of(rj, p.Wp, p.ww, p.sw);
+    }
+    tok_s[s] = tok;
+    lab_s[s] = lab;
+  }
+  __syncthreads();
+
+  const T* base = reinterpret_cast<const T*>(p.QKV);
+  const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
+  const T* Qb = base + (int64_t)b * 3 * gsz + h * hs;
+  const T* Kb = Qb + gsz;
+  const T* Vb = Qb + 2 * gsz;
+  const T* bias = reinterpret_cast<const T*>(p.bias_qkv);
+  const T* dOb = reinterpret_cast<const T*>(p.dO) + (int64_t)b * N * p.D + h * DH;
+  for (int idx = tid; idx < KEYS * DH; idx += BW_NT) {
+    const int s = idx / DH, d = idx - s * DH;
+    const int tok = tok_s[s];
+    float q = 0.f, k = 0.f, v = 0.f, g = 0.f;
+    if (tok >= 0) {
+      q = ld1(Qb + (int64_t)tok * DH + d);
+      k = ld1(Kb + (int64_t)tok * DH + d);
+      v = ld1(Vb + (int64_t)tok * DH + d);
+      g = ld1(dOb + (int64_t)tok * p.D + d);
+    } else if (tok == -1 && bias) {
+      k = ld1(bias + p.D + h * DH + d);
+      v = ld1(bias + 2 * p.D + h * DH + d);
+    }
+    qs[s * PI + d] = q; ks[s * PI + d] = k; vs[s * PI + d] = v; gs[s * PI + d] = g;
+  }
+  __syncthreads();
+
+  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
+  float* dKb = dQb + gsz;
+  float* dVb = dQb + 2 * gsz;
+
+  // Phase 1 (query slot i, keys sub, sub+G, ...): statistics and dQ.
+  {
+    const int i = tid / G, sub = tid % G;
+    const int tq = tok_s[i], lq = lab_s[i];
+    float s[PER], dp[PER];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = sub + u * G;
+      const bool ok = tok_s[j] != -2 && (!masked || lab_s[j] == lq);
+      float a = 0.f, c = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < DH; ++d) {
+        a += qs[i * PI + d] * ks[j * PI + d];
+        c += gs[i * PI + d] * vs[j * PI + d];
+      }
+      s[u] = ok ? a * p.scale : -INFINITY;
+      dp[u] = c;
+      mx = fmaxf(mx, s[u]);
+    }
+    mx = group_max<G>(mx);
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      s[u] = s[u] == -INFINITY ? 0.f : expf(s[u] - mx);
+      l += s[u];
+    }
+    l = group_sum<G>(l);
+    const float rl = 1.f / l;
+    float dsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      s[u] *= rl;  // softmax weight
+      dsum += s[u] * dp[u];
+    }
+    dsum = group_sum<G>(dsum);
+    if (sub == 0) { m_s[i] = mx; l_s[i] = l; d_s[i] = dsum; }
+    // dQ_i = scale * sum_j A_ij (dA_ij - D_i) k_j; each lane sums its keys,
+    // the group adds the parts, lane sub writes dims sub, sub+G, ...
+    for (int d0 = 0; d0 < DH; d0 += G) {
+      float part[G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) part[e] = 0.f;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int j = sub + u * G;
+        const float w = s[u] * (dp[u] - dsum);
+#pragma unroll
+        for (int e = 0; e < G; ++e)
+          if (d0 + e < DH) part[e] += w * ks[j * PI + d0 + e];
+      }
+#pragma unroll
+      for (int e = 0; e < G; ++e) part[e] = group_sum<G>(part[e]);
+      float mine = 0.f;
+#pragma unroll
+      for (int e = 0; e < G; ++e) mine = e == sub ? part[e] : mine;
+      if (tq >= 0 && d0 + sub < DH) dQb[(int64_t)tq * DH + d0 + sub] = mine * p.scale;
+    }
+  }
+  __syncthreads();
+
+  // Phase 2 (key slot j, queries sub, sub+G, ...): dK, dV.
+  {
+    const int j = tid / G, sub = tid % G;
+    const int tk = tok_s[j], lk = lab_s[j];
+    float dk[DH], dv[DH];
+#pragma unroll
+    for (int d = 0; d < DH; ++d) { dk[d] = 0.f; dv[d] = 0.f; }
+    if (tk != -2) {
+      for (int i = sub; i < KEYS; i += G) {
+        // only real queries carry a gradient (pad outputs are cropped)
+        if (tok_s[i] < 0 || (masked && lab_s[i] != lk)) continue;
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int d = 0; d < DH; ++d) {
+          a += qs[i * PI + d] * ks[j * PI + d];
+          c += gs[i * PI + d] * vs[j * PI + d];
+        }
+        const float w = expf(a * p.scale - m_s[i]) / l_s[i];
+        const float ds = w * (c - d_s[i]);
+#pragma unroll
+        for (int d = 0; d < DH; ++d) {
+          dv[d] += w * gs[i * PI + d];
+          dk[d] += ds * qs[i * PI + d];
+        }
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+      dk[d] = group_sum<G>(dk[d]) * p.scale;
+      dv[d] = group_sum<G>(dv[d]);
+    }
+    if (tk >= 0) {
+      for (int d = sub; d < DH; d += G) {
+        float k = 0.f, v = 0.f;
+#pragma unroll
+        for (int e = 0; e < DH; ++e) { k = e == d ? dk[e] : k; v = e == d ? dv[e] : v; }
+        dKb[(int64_t)tk * DH + d] = k;
+        dVb[(int64_t)tk * DH + d] = v;
+      }
+    } else if (tk == -1 && p.dbias_kv) {
+      for (int d = sub; d < DH; d += G) {
+        float k = 0.f, v = 0.f;
+#pragma unroll
+        for (int e = 0; e < DH; ++e) { k = e == d ? dk[e] : k; v = e == d ? dv[e] : v; }
+        atomicAdd(p.dbias_kv + h * DH + d, k);
+        atomicAdd(p.dbias_kv + p.D + h * DH + d, v);
+      }
+    }
+  }
+}
+
+template <typename T, int DH>
+static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
+  WindowBwdParams p;
+  p.QKV = d.QKV; p.bias_qkv = d.bias_qkv; p.dO = d.dO; p.dQKV = d.dQKV; p.dbias_kv = d.dbias_kv;
+  p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D; p.heads = d.heads;
+  p.wt = d.wt; p.wh = d.wh; p.ww = d.ww;
+  p.st = d.st; p.sh = d.sh; p.sw = d.sw;
+  p.Fp = d.Fp; p.Hp = d.Hp; p.Wp = d.Wp;
+  p.scale = d.scale;
+  const int nwin = (d.Fp / d.wt) * (d.Hp / d.wh) * (d.Wp / d.ww);
+  const dim3 grid(nwin, d.heads, d.B);
+  const int wsz = d.wt * d.wh * d.ww;
+  if (wsz <= 64) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 64>), grid, dim3(BW_NT), 0, s, p);
+  else if (wsz <= 128) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 128>), grid, dim3(BW_NT), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_window_bwd(const WindowBwdDesc& d, int f32, hipStream_t s) {
+  if (d.B == 0) return hipSuccess;
+  if (d.dh == 72) return f32 ? pick_window_bwd<float, 72>(d, s) : pick_window_bwd<uint16_t, 72>(d, s);
+  if (d.dh == 64) return f32 ? pick_window_bwd<float, 64>(d, s) : pick_window_bwd<uint16_t, 64>(d, s);
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
+// Dense attention backward (proxy self-attention, cross-attention)
+// ----------------------------------------------------------------------------
+struct DenseBwdParams {
+  const void *q, *k, *v, *dO;
+  int64_t q_bs, kv_bs;   // batch strides (elements) of q and of k / v
+  float *dq, *dk, *dv;
+  int64_t dq_bs, dkv_bs;
+  float* stats;          // [B][heads][Nq][3]: row max, row sum, D = rowsum(A * dA)
+  float* part;           // [chunks][B][heads][Nk][2][dh] when the queries are split
+  int B, heads, Nq, Nk, D, qchunk, chunks;
+  float scale;
+};
+
+constexpr int DB_Q = 64;   // queries per workgroup (query-major kernel)
+constexpr int DB_K = 64;   // keys per LDS chunk / per workgroup (key-major kernel)
+
+// 4 lanes per query; lane sub takes keys sub, sub+4, ... of each 64-key chunk.
+template <typename T, int DH>
+__global__ void __launch_bounds__(BW_NT) dense_bwd_q_kernel(DenseBwdParams p) {
+  constexpr int PI = DH + 1, G = 4, PER = DB_K / G;
+  __shared__ float ks[DB_K * PI], vs[DB_K * PI];
+  const int tid = threadIdx.x, i = blockIdx.x * DB_Q + tid / G, sub = tid % G;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const bool live = i < p.Nq;
+  const T* Q = reinterpret_cast<const T*>(p.q) + b * p.q_bs + ((int64_t)h * p.Nq + (live ? i : 0)) * DH;
+  const T* K = reinterpret_cast<const T*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const T* V = reinterpret_cast<const T*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const T* G0 = reinterpret_cast<const T*>(p.dO) + ((int64_t)b * p.Nq + (live ? i : 0)) * p.D + h * DH;
+  float q[DH], g[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) { q[d] = live ? ld1(Q + d) : 0.f; g[d] = live ? ld1(G0 + d) : 0.f; }
+
+  auto stage = [&](int c0, bool with_v) {
+    __syncthreads();
+    for (int idx = tid; idx < DB_K * DH; idx += BW_NT) {
+      const int j = idx / DH, d = idx - j * DH, key = c0 + j;
+      ks[j * PI + d] = key < p.Nk ? ld1(K + (int64_t)key * DH + d) : 0.f;
+      if (with_v) vs[j * PI + d] = key < p.Nk ? ld1(V + (int64_t)key * DH + d) : 0.f;
+    }
+    __syncthreads();
+  };
+
+  // pass 1: row maximum and sum (online over the chunks)
+  float mx = -INFINITY, l = 0.f;
+  for (int c0 = 0; c0 < p.Nk; c0 += DB_K) {
+    stage(c0, false);
+#pragma unroll 4
+    for (int u = 0; u < PER; ++u) {
+      const int j = sub + u * G;
+      if (c0 + j >= p.Nk) continue;
+      float a = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) a += q[d] * ks[j * PI + d];
+      const float sc = a * p.scale;
+      if (sc > mx) { l = l * expf(mx - sc) + 1.f; mx = sc; }
+      else l += expf(sc - mx);
+    }
+  }
+  {
+    const float m2 = group_max<G>(mx);
+    l = group_sum<G>(mx == -INFINITY ? 0.f : l * expf(mx - m2));
+    mx = m2;
+  }
+  const float rl = 1.f / l;
+  // pass 2: D = sum_j A_ij dA_ij, X = sum_j A_ij dA_ij k_j, Y = sum_j A_ij k_j;
+  // dQ = scale * (X - D * Y)
+  float X[DH], Y[DH], Dl = 0.f;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) { X[d] = 0.f; Y[d] = 0.f; }
+  for (int c0 = 0; c0 < p.Nk; c0 += DB_K) {
+    stage(c0, true);
+    for (int u = 0; u < PER; ++u) {
+      const int j = sub + u * G;
+      if (c0 + j >= p.Nk) continue;
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        a += q[d] * ks[j * PI + d];
+        c += g[d] * vs[j * PI + d];
+      }
+      const float w = expf(a * p.scale - mx) * rl;
+      Dl += w * c;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        X[d] += w * c * ks[j * PI + d];
+        Y[d] += w * ks[j * PI + d];
+      }
+    }
+  }
+  Dl = group_sum<G>(Dl);
+#pragma unroll
+  for (int d = 0; d < DH; ++d) { X[d] = group_sum<G>(X[d]); Y[d] = group_sum<G>(Y[d]); }
+  if (!live) return;
+  float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + i) * DH;
+  for (int d = sub; d < DH; d += G) {
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) { x = e == d ? X[e] : x; y = e == d ? Y[e] : y; }
+    dq[d] = (x - Dl * y) * p.scale;
+  }
+  if (sub == 0) {
+    float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + i) * 3;
+    st[0] = mx; st[1] = l; st[2] = Dl;
+  }
+}
+
+// 4 lanes per key; lane sub takes queries sub, sub+4, ... of each 64-query tile.
+template <typename T, int DH>
+__global__ void __launch_bounds__(BW_NT) dense_bwd_kv_kernel(DenseBwdParams p) {
+  constexpr int PI = DH + 1, G = 4;
+  __shared__ float qs[DB_Q * PI], gs[DB_Q * PI], st[DB_Q * 3];
+  const int tid = threadIdx.x, j = blockIdx.x * DB_K + tid / G, sub = tid % G;
+  const int chunk = blockIdx.y, bh = blockIdx.z, b = bh / p.heads, h = bh - b * p.heads;
+  const bool live = j < p.Nk;
+  const T* K = reinterpret_cast<const T*>(p.k) + b * p.kv_bs + ((int64_t)h * p.Nk + (live ? j : 0)) * DH;
+  const T* V = reinterpret_cast<const T*>(p.v) + b * p.kv_bs + ((int64_t)h * p.Nk + (live ? j : 0)) * DH;
+  const T* Q = reinterpret_cast<const T*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
+  const T* G0 = reinterpret_cast<const T*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
+  const float* S = p.stats + ((int64_t)b * p.heads + h) * p.Nq * 3;
+  float k[DH], v[DH], dk[DH], dv[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    k[d] = live ? ld1(K + d) : 0.f; v[d] = live ? ld1(V + d) : 0.f;
+    dk[d] = 0.f; dv[d] = 0.f;
+  }
+  const int q0 = chunk * p.qchunk, q1 = min(p.Nq, q0 + p.qchunk);
+  for (int t0 = q0; t0 < q1; t0 += DB_Q) {
+    __syncthreads();
+    for (int idx = tid; idx < DB_Q * DH; idx += BW_NT) {
+      const int r = idx / DH, d = idx - r * DH, qi = t0 + r;
+      qs[r * PI + d] = qi < q1 ? ld1(Q + (int64_t)qi * DH + d) : 0.f;
+      gs[r * PI + d] = qi < q1 ? ld1(G0 + (int64_t)qi * p.D + d) : 0.f;
+    }
+    for (int idx = tid; idx < DB_Q * 3; idx += BW_NT) st[idx] = t0 + idx / 3 < q1 ? S[(int64_t)t0 * 3 + idx] : 0.f;
+    __syncthreads();
+    for (int r = sub; r < DB_Q; r += G) {
+      if (t0 + r >= q1) break;
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        a += qs[r * PI + d] * k[d];
+        c += gs[r * PI + d] * v[d];
+      }
+      const float w = expf(a * p.scale - st[r * 3]) / st[r * 3 + 1];
+      const float ds = w * (c - st[r * 3 + 2]);
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        dv[d] += w * gs[r * PI + d];
+        dk[d] += ds * qs[r * PI + d];
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DH; ++d) { dk[d] = group_sum<G>(dk[d]); dv[d] = group_sum<G>(dv[d]); }
+  if (!live) return;
+  for (int d = sub; d < DH; d += G) {
+    float kk = 0.f, vv = 0.f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) { kk = e == d ? dk[e] : kk; vv = e == d ? dv[e] : vv; }
+    if (p.chunks == 1) {
+      p.dk[b * p.dkv_bs + ((int64_t)h * p.Nk + j) * DH + d] = kk * p.scale;
+      p.dv[b * p.dkv_bs + ((int64_t)h * p.Nk + j) * DH + d] = vv;
+    } else {
+      float* pt = p.part + ((((int64_t)chunk * p.B + b) * p.heads + h) * p.Nk + j) * 2 * DH;
+      pt[d] = kk;
+      pt[DH + d] = vv;
+    }
+  }
+}
+
+template <int DH>
+__global__ void __launch_bounds__(BW_NT) dense_bwd_reduce_kernel(DenseBwdParams p) {
+  const int64_t per = (int64_t)p.B * p.heads * p.Nk * DH;
+  const int64_t e = (int64_t)blockIdx.x * BW_NT + threadIdx.x;
+  if (e >= per) return;
+  const int d = (int)(e % DH);
+  const int64_t row = e / DH;  // (b * heads + h) * Nk + j
+  const int64_t b = row / ((int64_t)p.heads * p.Nk), rest = row - b * p.heads * p.Nk;
+  float sk = 0.f, sv = 0.f;
+  for (int c = 0; c < p.chunks; ++c) {  // fixed order
+    const float* pt = p.part + ((int64_t)c * p.B * p.heads * p.Nk + row) * 2 * DH;
+    sk += pt[d];
+    sv += pt[DH + d];
+  }
+  p.dk[b * p.dkv_bs + rest * DH + d] = sk * p.scale;
+  p.dv[b * p.dkv_bs + rest * DH + d] = sv;
+}
+
+template <typename T, int DH>
+static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
+  DenseBwdParams p;
+  p.q = d.q; p.k = d.k; p.v = d.v; p.dO = d.dO;
+  p.q_bs = d.q_bs; p.kv_bs = d.kv_bs;
+  p.dq = d.dq; p.dk = d.dk; p.dv = d.dv; p.dq_bs = d.dq_bs; p.dkv_bs = d.dkv_bs;
+  p.stats = d.stats; p.part = d.part;
+  p.B = d.B; p.heads = d.heads; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
+  p.qchunk = d.qchunk; p.chunks = d.chunks;
+  p.scale = d.scale;
+  hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), dim3((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), dim3(BW_NT), 0, s,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dense_bwd_kv_kernel<T, DH>), dim3((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads),
+                     dim3(BW_NT), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || d.chunks == 1) return e;
+  const int64_t n = (int64_t)d.B * d.heads * d.Nk * DH;
+  hipLaunchKernelGGL((dense_bwd_reduce_kernel<DH>), dim3((unsigned)((n + BW_NT - 1) / BW_NT)), dim3(BW_NT), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_bwd(const DenseBwdDesc& d, int f32, hipStream_t s) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  if (d.dh == 72) return f32 ? run_dense_bwd<float, 72>(d, s) : run_dense_bwd<uint16_t, 72>(d, s);
+  if (d.dh == 64) return f32 ? run_dense_bwd<float, 64>(d, s) : run_dense_bwd<uint16_t, 64>(d, s);
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
+// Window-average backward: dx[b, t] (+)= dP[b, proxy(t)] / P, 4 floats a thread
+// ----------------------------------------------------------------------------
+struct PoolBwdParams {
+  const float* dP;
+  float* dx;
+  int F, H, W, D;
+  int pt, ph, pw;
+  int64_t rows;  // B * N
+  int accumulate;
+  float P;
+};
+
+__global__ void __launch_bounds__(BW_NT) pool_bwd_kernel(PoolBwdParams p) {
+  const int q4 = p.D / 4;
+  const int64_t e = (int64_t)blockIdx.x * BW_NT + threadIdx.x;
+  if (e >= p.rows * q4) return;
+  const int64_t row = e / q4;
+  const int c = (int)(e - row * q4);
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const int64_t b = row / N;
+  const int tok = (int)(row - b * N);
+  const int t = tok / (p.H * p.W), i = (tok / p.W) % p.H, j = tok % p.W;
+  const int nh = p.H / p.ph, nw = p.W / p.pw, M = (p.F / p.pt) * nh * nw;
+  const int m = ((t / p.pt) * nh + i / p.ph) * nw + j / p.pw;
+  const float4 g = *reinterpret_cast<const float4*>(p.dP + ((b * M + m) * p.D) + 4 * c);
+  float4 o{g.x / p.P, g.y / p.P, g.z / p.P, g.w / p.P};
+  float4* dst = reinterpret_cast<float4*>(p.dx + row * p.D + 4 * c);
+  if (p.accumulate) {
+    const float4 a = *dst;
+    o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+  }
+  *dst = o;
+}
+
+hipError_t launch_pool_bwd(const PoolBwdDesc& d, hipStream_t s) {
+  PoolBwdParams p;
+  p.dP = d.dP; p.dx = d.dx;
+  p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D;
+  p.pt = d.pt; p.ph = d.ph; p.pw = d.pw;
+  p.rows = (int64_t)d.B * d.F * d.H * d.W;
+  p.accumulate = d.accumulate;
+  p.P = (float)(d.pt * d.ph * d.pw);
+  const int64_t n = p.rows * (d.D / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_bwd_kernel, dim3((unsigned)((n + BW_NT - 1) / BW_NT)), dim3(BW_NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace ptdit

@@ -70,4 +70,36 @@ struct WindowDesc {
 };
 hipError_t launch_window(const WindowDesc& d, int f32, hipStream_t s);
 
+// Backward pass of the attention core (fp32 gradients).
+struct WindowBwdDesc {
+  const void* QKV; const void* bias_qkv; const void* dO;
+  float* dQKV; float* dbias_kv;
+  int B, F, H, W, D, heads, dh;
+  int wt, wh, ww;
+  int st, sh, sw;
+  int Fp, Hp, Wp;
+  float scale;
+};
+hipError_t launch_window_bwd(const WindowBwdDesc& d, int f32, hipStream_t s);
+
+struct DenseBwdDesc {
+  const void *q, *k, *v, *dO;
+  int64_t q_bs, kv_bs;
+  float *dq, *dk, *dv;
+  int64_t dq_bs, dkv_bs;
+  float* stats;  // [B][heads][Nq][3]
+  float* part;   // [chunks][B][heads][Nk][2][dh] (chunks > 1)
+  int B, heads, Nq, Nk, D, dh, qchunk, chunks;
+  float scale;
+};
+hipError_t launch_dense_bwd(const DenseBwdDesc& d, int f32, hipStream_t s);
+
+struct PoolBwdDesc {
+  const float* dP; float* dx;
+  int B, F, H, W, D;
+  int pt, ph, pw;
+  int accumulate;
+};
+hipError_t launch_pool_bwd(const PoolBwdDesc& d, hipStream_t s);
+
 }  // namespace ptdit

@@ -256,6 +256,65 @@ ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtyp
 ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,
                           void* y, ptdit_dtype dt, hipStream_t stream);
 
+/*
+ * Backward pass of the attention core (Qihoo-T2X reading note, section 3
+ * "Method": the gradients of Eq. GIIM's and Eq. TCM's attentions; the pages
+ * train at 2048^2, section 4). With S = Q K^T / sqrt(dh), A = softmax(S) over
+ * the allowed keys, O = A V and dO = dL/dO: dV = A^T dO, dS = A * (dO V^T -
+ * rowsum(A * dO V^T)), dQ = dS K / sqrt(dh), dK = dS^T Q / sqrt(dh). The
+ * softmax is recomputed from Q and K; nothing of the forward call is needed
+ * but its Q/K/V. Inputs are bf16 or fp32 (dt, all alike); gradients are fp32.
+ * Every output is written (not accumulated) unless stated; errors are
+ * returned before anything is launched.
+ *
+ * ptdit_window_attn_bwd -- the core of ptdit_window_sa (shift 0) or
+ * ptdit_shift_window_sa: the same windows, padding, roll and boundary mask.
+ *   qkv      [B][3][heads][N][dh] device, dt: the Q/K/V of the forward call
+ *            (the projections of x, head-major)
+ *   b_qkv    [3D] device, dt, or NULL: the forward's projection bias; pad
+ *            tokens' keys/values are b_k/b_v (zero when NULL)
+ *   d_o      [B][N][D] device, dt: gradient of the attention output (the
+ *            input of the output projection)
+ *   d_qkv    [B][3][heads][N][dh] device, fp32: dQ, dK, dV of the real tokens
+ *   d_b_kv   [2][D] device, fp32, or NULL: the gradients that reach pad key /
+ *            value slots are ADDED here (d b_k, d b_v); required (else
+ *            PTDIT_ERR_NULL) when the window does not divide the grid
+ *   win, shift as for the forward call (window <= 128 tokens, shift < window).
+ */
+ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv,
+                                   float* d_b_kv, hipStream_t stream);
+
+/*
+ * ptdit_attn_bwd -- the core of ptdit_proxy_sa (queries = keys = proxies) or
+ * ptdit_proxy_xattn (queries = tokens, keys = proxies), unmasked.
+ *   q        batch b at q + b*q_bstride elements: [heads][Nq][dh], dt
+ *   k, v     batch b at k / v + b*kv_bstride: [heads][Nk][dh], dt
+ *            (so the fused [B][3][heads][M][dh] and [B][2][heads][M][dh]
+ *            buffers of the forward calls are addressed in place)
+ *   d_o      [B][Nq][heads*dh] device, dt
+ *   d_q      batch b at d_q + b*dq_bstride: [heads][Nq][dh], fp32
+ *   d_k, d_v batch b at + b*dkv_bstride: [heads][Nk][dh], fp32
+ *   ws       ptdit_attn_bwd_workspace_bytes(...) bytes of device memory
+ *   dh 64 or 72; B*heads <= 65535; every pointer 16-byte aligned; the
+ *   outputs overlap neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS).
+ */
+ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
+                            int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                            int32_t Nq, int32_t Nk, int32_t dh, float* d_q, int64_t dq_bstride, float* d_k,
+                            float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int32_t Nk, int32_t dh);
+
+/*
+ * ptdit_proxy_pool_bwd -- gradient of the window average (Eq. GIIM's
+ * Averaging): every token of a proxy window receives d_proxies[proxy] / P,
+ * P = p_t*p_h*p_w (IEEE fp32 division). d_proxies [B][M][D] fp32, d_x
+ * [B][N][D] fp32 (written, or added to when accumulate != 0); D % 4 == 0.
+ * The gradient of the roll is the inverse roll: ptdit_roll3d(inverse = 1).
+ */
+ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,
+                                  int32_t accumulate, hipStream_t stream);
+
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
  * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*
  * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments. */
@@ -285,7 +344,10 @@ typedef enum {
   PTDIT_K_ROLL = 5,
   PTDIT_K_GEMM_Q = 6,        /* query projection of the token rows for cross-attention */
   PTDIT_K_GEMM_PROXY = 7,    /* every projection of the proxy rows */
-  PTDIT_K_GEMM_MLP = 8       /* both linear maps of the MLP */
+  PTDIT_K_GEMM_MLP = 8,      /* both linear maps of the MLP */
+  PTDIT_K_BWD_WINDOW = 9,    /* window attention backward */
+  PTDIT_K_BWD_DENSE = 10,    /* proxy / cross-attention backward (all three kernels) */
+  PTDIT_K_BWD_POOL = 11      /* window-average backward */
 } ptdit_kernel_class;
 
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity);

@@ -204,3 +204,20 @@ def tiny(name: str = "tiny", *, B=1, F=1, H=8, W=8, D=16, heads=2, p=(1, 2, 2),
     """A small workload for brute-force pins and fast parity cases."""
     return Workload(name, index, B=B, F=F, H=H, W=W, D=D, heads=heads, p=p, win=win,
                     shift=shift, dtype=dtype)
+
+
+def make_attn_grad_inputs(B: int, heads: int, Nq: int, Nk: int, dh: int, seed: int, scale: float = 1.0,
+                          dtype: str = "bf16"):
+    """Inputs of an attention-core backward: q [B, heads, Nq, dh], k, v
+    [B, heads, Nk, dh] (standard normal times `scale` for q and k, so the
+    scores q.k / sqrt(dh) have standard deviation scale^2), and the output
+    gradient d_o [B, Nq, heads*dh] (standard normal). bf16-representable
+    float32 when dtype is "bf16"."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.standard_normal((B, heads, Nq, dh), dtype=np.float32) * scale
+    k = g.standard_normal((B, heads, Nk, dh), dtype=np.float32) * scale
+    v = g.standard_normal((B, heads, Nk, dh), dtype=np.float32)
+    do = g.standard_normal((B, Nq, heads * dh), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v, do = (round_bf16(a) for a in (q, k, v, do))
+    return q, k, v, do

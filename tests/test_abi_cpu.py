@@ -155,6 +155,41 @@ def test_host_validation_rejects_before_launch(lib):
     assert roll(fake, Grid(1, 1, 16, 16, 1150, 16), Win3(0, 1, 1), 0, far, 0, None) == -2
     assert roll(fake, Grid(1, 1, 1, 1 << 20, 1 << 14, 16), Win3(0, 0, 1), 0, far, 0, None) == -2
     assert roll(fake, g, Win3(0, 1, 1), 0, ctypes.c_void_p((1 << 20) + 4096), 0, None) == -8
+    # backward: window core (dtype, head width, window > 128, shift >= window, a padded grid
+    # without d_b_kv, outputs over inputs)
+    wb = lambda qkv, do, dt, gg, wn, sh, dq, db: lib.ptdit_window_attn_bwd(qkv, None, do, dt, gg, wn, sh, dq, db, None)
+    gpad = Grid(1, 1, 20, 20, 1152, 16)
+    d1, d2 = ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42)
+    assert wb(fake, far, 3, g, Win3(1, 8, 8), Win3(0, 4, 4), d1, d2) == -4
+    assert wb(fake, far, 0, Grid(1, 1, 16, 16, 1152, 12), Win3(1, 8, 8), Win3(0, 4, 4), d1, d2) == -2
+    assert wb(fake, far, 0, g, Win3(3, 8, 8), Win3(0, 4, 4), d1, d2) == -2
+    assert wb(fake, far, 0, g, Win3(1, 8, 8), Win3(0, 8, 4), d1, d2) == -2
+    assert wb(fake, far, 0, gpad, Win3(1, 8, 8), Win3(0, 4, 4), d1, None) == -1
+    assert wb(fake, far, 0, g, Win3(1, 8, 8), Win3(0, 4, 4), fake, d2) == -8
+    assert wb(fake, far, 0, g, Win3(1, 8, 8), Win3(0, 4, 4), d1, ctypes.c_void_p((1 << 41) + 64)) == -8
+    assert wb(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), Win3(0, 4, 4), None, None) == 0
+    # backward: dense core
+    ab = lambda B, h, Nq, Nk, dh, qbs, kvbs, ws, wsb, dq=d1: lib.ptdit_attn_bwd(
+        fake, qbs, far, far, kvbs, far, 0, B, h, Nq, Nk, dh, dq, h * Nq * dh, d2, ctypes.c_void_p(1 << 43),
+        h * Nk * dh, ws, wsb, None)
+    wsb = lib.ptdit_attn_bwd_workspace_bytes(1, 16, 2400, 150, 72)
+    assert wsb >= 16 * 2400 * 3 * 4 + 3 * 16 * 150 * 2 * 72 * 4
+    assert lib.ptdit_attn_bwd_workspace_bytes(1, 16, 256, 256, 80) == 0
+    ws4 = ctypes.c_void_p(1 << 44)
+    assert ab(1, 16, 2400, 150, 80, 16 * 2400 * 80, 16 * 150 * 80, ws4, wsb) == -2      # head width
+    assert ab(300, 300, 64, 64, 72, 300 * 64 * 72, 300 * 64 * 72, ws4, 1 << 40) == -2   # B*heads
+    assert ab(1, 16, 2400, 150, 72, 100, 16 * 150 * 72, ws4, wsb) == -2                 # q batch stride
+    assert ab(1, 16, 2400, 0, 72, 16 * 2400 * 72, 0, ws4, wsb) == -2                    # no keys
+    assert ab(1, 16, 2400, 150, 72, 16 * 2400 * 72, 16 * 150 * 72, ws4, 64) == -6       # workspace
+    assert ab(1, 16, 2400, 150, 72, 16 * 2400 * 72, 16 * 150 * 72, ws4, wsb, dq=fake) == -8  # d_q over q
+    assert ab(1, 16, 0, 150, 72, 0, 16 * 150 * 72, None, 0) == 0                        # no queries
+    # backward: pooling
+    pb = lib.ptdit_proxy_pool_bwd
+    assert pb(fake, Grid(1, 1, 16, 16, 1150, 16), Win3(1, 4, 4), far, 0, None) == -2
+    assert pb(fake, g, Win3(1, 3, 3), far, 0, None) == -3
+    assert pb(None, g, Win3(1, 4, 4), far, 0, None) == -1
+    assert pb(fake, g, Win3(1, 4, 4), ctypes.c_void_p((1 << 20) + 256), 0, None) == -8
+    assert pb(None, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 4, 4), None, 0, None) == 0
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
     assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),
