@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU = 157.3      # MI355X fp32 vector ALUs (256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz)
 METRIC = "PT-block attention tokens/s + % MFMA-bf16 peak at 2048² (N=16384)"
 
 
@@ -91,6 +92,67 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     return out
 
 
+def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
+    """Attention-core backward at the workload's shapes, on synthetic resident
+    inputs: the shifted-window core, the cross-attention core (tokens x
+    proxies), the proxy self-attention core and the window-average backward.
+    Each kernel class is timed with the library's HIP-event trace. Rates: the
+    algorithmic FLOP of the five products of an attention backward (QK^T,
+    dO V^T, A^T dO, dS K, dS^T Q: 10 * Nq * Nk * d_h per head), against the fp32
+    vector peak (the kernels compute on the vector ALUs), and the HBM bytes
+    (inputs read once, fp32 gradients written once) against 8 TB/s."""
+    import torch
+    from diffusion_transformer_attention_pt_amd import _lib
+
+    B, N, M, D, heads = wl.B, wl.N, wl.M, wl.D, wl.heads
+    dh = D // heads
+    L = wl.win[0] * wl.win[1] * wl.win[2]
+    es = 2 if prec == torch.bfloat16 else 4
+    dev = "cuda"
+    torch.manual_seed(7)
+    qkv = torch.randn(B, 3, heads, N, dh, device=dev).to(prec)
+    do = torch.randn(B, N, D, device=dev).to(prec)
+    pkv = torch.randn(B, 3, heads, M, dh, device=dev).to(prec)
+    pdo = torch.randn(B, M, D, device=dev).to(prec)
+    dP = torch.randn(B, M, D, device=dev)
+    dbkv = torch.zeros(2, D, device=dev)
+    dqkv = torch.empty(B, 3, heads, N, dh, device=dev)
+    dx = torch.empty(B, N, D, device=dev)
+    grid = (B,) + tuple(wl.grid) + (D, heads)
+    cases = {
+        "window_bwd": (_lib.K_BWD_WINDOW,
+                       lambda: _lib.window_attn_bwd(qkv, do, grid, wl.win, wl.shift, d_qkv=dqkv, d_b_kv=dbkv),
+                       10 * B * heads * N * L * dh, 4 * B * N * D * es + 3 * B * N * D * 4),
+        "xattn_bwd": (_lib.K_BWD_DENSE,
+                      lambda: _lib.attn_bwd(qkv[:, 0], pkv[:, 1], pkv[:, 2], do),
+                      10 * B * heads * N * M * dh, 2 * B * N * D * es + 2 * B * M * D * es + B * N * D * 4
+                      + 2 * B * M * D * 4),
+        "proxy_sa_bwd": (_lib.K_BWD_DENSE,
+                         lambda: _lib.attn_bwd(pkv[:, 0], pkv[:, 1], pkv[:, 2], pdo),
+                         10 * B * heads * M * M * dh, 4 * B * M * D * es + 3 * B * M * D * 4),
+        "pool_bwd": (_lib.K_BWD_POOL, lambda: _lib.proxy_pool_bwd(dP, grid, wl.p, d_x=dx),
+                     0, B * M * D * 4 + B * N * D * 4),
+    }
+    res = {}
+    for name, (cls, fn, flop, nbytes) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        _lib.trace_enable(cls, 4 * reps)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        ms = _lib.trace_read(4 * reps)
+        _lib.trace_disable()
+        avg = statistics.mean(ms)
+        r = {"avg_ms": round(avg, 5), "gflop": round(flop / 1e9, 3), "mbytes": round(nbytes / 1e6, 1),
+             "hbm_gbs": round(nbytes / (avg * 1e-3) / 1e9, 1)}
+        if flop:
+            tf = flop / (avg * 1e-3) / 1e12
+            r.update({"tflops": round(tf, 2), "vs_fp32_vector_peak": round(tf / PEAK_FP32_VALU, 4)})
+        res[name] = r
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +167,8 @@ def main() -> int:
                          "caption tokens and the MLP (the default step is the attention core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the attention-core backward kernels at the workload's shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the run, copy a 256 MiB buffer once (a plain copy kernel of known "
                          "size, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -285,6 +349,8 @@ def main() -> int:
                            "peak_frac": round(roll_rate / PEAK_HBM_GBS, 4), "copies": ncopy}
         del xs, ys
         out["breakdown"] = br
+    if args.backward:
+        out["backward"] = backward_timings(wl, blk, prec)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
         out["cpu_baseline"]["gpu_speedup"] = round(tokens_per_s / out["cpu_baseline"]["value"], 1)
