@@ -245,6 +245,226 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
   }
 }
 
+// bf16 windows of at most 64 tokens on the matrix cores (v_mfma_f32_16x16x32_bf16,
+// fp32 accumulation; A = softmax weights and dS rounded to bf16 as operands).
+// Four waves; lane l: c = l % 16, g = l / 16.
+//  phase 1, wave w owns queries 16w..16w+15 (query 16w + c per lane):
+//    S^T = K Q^T and dP^T = V dO^T (key tile t: keys 16t + 4g + r, r < 4),
+//    softmax over the 64 keys (the 4 lane groups of a column share a query),
+//    D = sum A dP, dS = A (dP - D); dQ^T = K^T dS^T with dS^T packed from the
+//    registers (contraction order: keys 16t0 + 4g + e, then 16(t0+1) + 4g + e);
+//    A^T and dS^T go to LDS as [key][query].
+//  phase 2, wave w owns keys 16w..16w+15: dV^T = dO^T A and dK^T = Q^T dS, the
+//    contraction over the 64 queries read from the transposed LDS copies.
+template <int DH>
+__global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams p) {
+  constexpr int KEYS = 64;
+  constexpr int NKC = (DH + 31) / 32;  // 32-wide chunks of the head dim (rows padded with zeros)
+  constexpr int RP = NKC * 32 + 8;     // row pitch (elements) of the row-major K, V copies
+  constexpr int NDT = (DH + 15) / 16;  // 16-row tiles of the transposed copies / outputs
+  constexpr int TP = KEYS + 8;         // row pitch of the transposed copies
+  __shared__ __attribute__((aligned(16))) uint16_t kr[KEYS * RP], vr[KEYS * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t kT[NDT * 16 * TP], qT[NDT * 16 * TP], gT[NDT * 16 * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t pT[KEYS * TP], dsT[KEYS * TP];
+  __shared__ int tok_s[KEYS], lab_s[KEYS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int nWh = p.Hp / p.wh, nWw = p.Wp / p.ww;
+  const int Tw = blockIdx.x / (nWh * nWw), Iw = (blockIdx.x / nWw) % nWh, Jw = blockIdx.x % nWw;
+  const int wsz = p.wt * p.wh * p.ww;
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const bool masked = (p.st | p.sh | p.sw) != 0;
+
+  for (int s = tid; s < KEYS; s += BW_NT) {
+    int tok = -2, lab = 0;
+    if (s < wsz) {
+      const int a = s / (p.wh * p.ww), cc = (s / p.ww) % p.wh, e = s % p.ww;
+      const int rt = Tw * p.wt + a, ri = Iw * p.wh + cc, rj = Jw * p.ww + e;
+      int ot = rt + p.st; ot -= ot >= p.Fp ? p.Fp : 0;
+      int oi = ri + p.sh; oi -= oi >= p.Hp ? p.Hp : 0;
+      int oj = rj + p.sw; oj -= oj >= p.Wp ? p.Wp : 0;
+      tok = (ot < p.F && oi < p.H && oj < p.W) ? (ot * p.H + oi) * p.W + oj : -1;
+      lab = region_of(rt, p.Fp, p.wt, p.st) * 9 + region_of(ri, p.Hp, p.wh, p.sh) * 3 +
+            region_of(rj, p.Wp, p.ww, p.sw);
+    }
+    tok_s[s] = tok;
+    lab_s[s] = lab;
+  }
+  __syncthreads();
+
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(p.QKV);
+  const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
+  const uint16_t* Qb = base + (int64_t)b * 3 * gsz + h * hs;
+  const uint16_t* Kb = Qb + gsz;
+  const uint16_t* Vb = Qb + 2 * gsz;
+  const uint16_t* bias = reinterpret_cast<const uint16_t*>(p.bias_qkv);
+  const uint16_t* dOb = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * N * p.D + h * DH;
+
+  // staging: 16-byte chunks (8 dims) of every slot; row-major K, V (zero past
+  // DH), transposed K, Q, dO (rows DH.. of the transposed copies zero)
+  constexpr int CH = NKC * 4;  // chunks per padded row
+  for (int idx = tid; idx < KEYS * CH; idx += BW_NT) {
+    const int sl = idx / CH, ch = idx - sl * CH;
+    const int tok = tok_s[sl];
+    uint4 kq = {0, 0, 0, 0}, vq = {0, 0, 0, 0}, qq = {0, 0, 0, 0}, gq = {0, 0, 0, 0};
+    if (ch * 8 < DH) {
+      if (tok >= 0) {
+        kq = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
+        vq = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
+        qq = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
+        gq = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
+      } else if (tok == -1 && bias) {
+        kq = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
+        vq = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
+      }
+    }
+    *reinterpret_cast<uint4*>(&kr[sl * RP + ch * 8]) = kq;
+    *reinterpret_cast<uint4*>(&vr[sl * RP + ch * 8]) = vq;
+    if (ch * 8 < NDT * 16) {
+      const uint32_t ka[4] = {kq.x, kq.y, kq.z, kq.w}, qa[4] = {qq.x, qq.y, qq.z, qq.w},
+                     ga[4] = {gq.x, gq.y, gq.z, gq.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = (ch * 8 + e) * TP + sl, sh = (e & 1) * 16;
+        kT[row] = (uint16_t)(ka[e >> 1] >> sh);
+        qT[row] = (uint16_t)(qa[e >> 1] >> sh);
+        gT[row] = (uint16_t)(ga[e >> 1] >> sh);
+      }
+    }
+  }
+  __syncthreads();
+
+  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
+  float* dKb = dQb + gsz;
+  float* dVb = dQb + 2 * gsz;
+
+  // ---- phase 1: queries of wave w
+  {
+    const int qs = w * 16 + c;
+    const int qtok = tok_s[qs], qlab = lab_s[qs];
+    uint4 qf[NKC], gf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      // B operands: column = this lane's query, k = dims kc*32 + 8g .. +8
+      // (read back from the transposed copies would cost 8 LDS reads; the
+      // row-major source is the global row, zero past DH)
+      const int d = kc * 32 + 8 * g;
+      qf[kc] = (qtok >= 0 && d < DH) ? *reinterpret_cast<const uint4*>(Qb + (int64_t)qtok * DH + d) : uint4{0, 0, 0, 0};
+      gf[kc] = (qtok >= 0 && d < DH) ? *reinterpret_cast<const uint4*>(dOb + (int64_t)qtok * p.D + d)
+                                     : uint4{0, 0, 0, 0};
+    }
+    floatx4 sc[4], dp[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = zero4();
+      dp[t] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
+        const uint4 va = *reinterpret_cast<const uint4*>(&vr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
+        sc[t] = mfma_bf16(ka, qf[kc], sc[t]);
+        dp[t] = mfma_bf16(va, gf[kc], dp[t]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ks = t * 16 + 4 * g + r;
+        const bool ok = tok_s[ks] != -2 && (!masked || lab_s[ks] == qlab);
+        sc[t][r] = ok ? sc[t][r] * p.scale : -INFINITY;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx == -INFINITY) mx = 0.f;  // slot past the window: no allowed key
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] = expf(sc[t][r] - mx);
+        l += sc[t][r];
+      }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float rl = l > 0.f ? 1.f / l : 0.f;
+    float dd = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] *= rl;  // softmax weight A
+        dd += sc[t][r] * dp[t][r];
+      }
+    dd += __shfl_xor(dd, 16, 64);
+    dd += __shfl_xor(dd, 32, 64);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ks = t * 16 + 4 * g + r;
+        dp[t][r] = sc[t][r] * (dp[t][r] - dd);  // dS
+        pT[ks * TP + qs] = (uint16_t)(pack_bf2(sc[t][r], 0.f) & 0xffffu);
+        dsT[ks * TP + qs] = (uint16_t)(pack_bf2(dp[t][r], 0.f) & 0xffffu);
+      }
+    // dQ^T = K^T dS^T over the 64 keys (two MFMAs of 32 per dim tile)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int t0 = 0; t0 < 4; t0 += 2) {
+        const uint4 bf = uint4{pack_bf2(dp[t0][0], dp[t0][1]), pack_bf2(dp[t0][2], dp[t0][3]),
+                               pack_bf2(dp[t0 + 1][0], dp[t0 + 1][1]), pack_bf2(dp[t0 + 1][2], dp[t0 + 1][3])};
+        const int row = (dt * 16 + c) * TP, kb = t0 * 16 + 4 * g;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
+        acc = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc);
+      }
+      const int d = dt * 16 + 4 * g;
+      if (qtok >= 0 && d < DH)
+        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * DH + d) =
+            float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: keys of wave w
+  {
+    const int ks = w * 16 + c;
+    const int ktok = tok_s[ks];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      floatx4 av = zero4(), ak = zero4();
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int qo = kq * 32 + 8 * g;
+        const uint4 pa = *reinterpret_cast<const uint4*>(&pT[ks * TP + qo]);
+        const uint4 da = *reinterpret_cast<const uint4*>(&dsT[ks * TP + qo]);
+        const uint4 ga = *reinterpret_cast<const uint4*>(&gT[(dt * 16 + c) * TP + qo]);
+        const uint4 qa = *reinterpret_cast<const uint4*>(&qT[(dt * 16 + c) * TP + qo]);
+        av = mfma_bf16(ga, pa, av);
+        ak = mfma_bf16(qa, da, ak);
+      }
+      const int d = dt * 16 + 4 * g;
+      if (d >= DH) continue;
+      const float4 kv = float4{ak[0] * p.scale, ak[1] * p.scale, ak[2] * p.scale, ak[3] * p.scale};
+      const float4 vv = float4{av[0], av[1], av[2], av[3]};
+      if (ktok >= 0) {
+        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
+        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
+      } else if (ktok == -1 && p.dbias_kv) {
+        float* bk = p.dbias_kv + h * DH + d;
+        float* bv = p.dbias_kv + p.D + h * DH + d;
+        atomicAdd(bk + 0, kv.x); atomicAdd(bk + 1, kv.y); atomicAdd(bk + 2, kv.z); atomicAdd(bk + 3, kv.w);
+        atomicAdd(bv + 0, vv.x); atomicAdd(bv + 1, vv.y); atomicAdd(bv + 2, vv.z); atomicAdd(bv + 3, vv.w);
+      }
+    }
+  }
+}
+
 template <typename T, int DH>
 static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   WindowBwdParams p;
@@ -257,7 +477,8 @@ static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   const int nwin = (d.Fp / d.wt) * (d.Hp / d.wh) * (d.Wp / d.ww);
   const dim3 grid(nwin, d.heads, d.B);
   const int wsz = d.wt * d.wh * d.ww;
-  if (wsz <= 64) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 64>), grid, dim3(BW_NT), 0, s, p);
+  if (sizeof(T) == 2 && wsz <= 64) hipLaunchKernelGGL((window_bwd_mfma_kernel<DH>), grid, dim3(BW_NT), 0, s, p);
+  else if (wsz <= 64) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 64>), grid, dim3(BW_NT), 0, s, p);
   else if (wsz <= 128) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 128>), grid, dim3(BW_NT), 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
