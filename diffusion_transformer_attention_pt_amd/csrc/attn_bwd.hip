@@ -680,6 +680,241 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_reduce_kernel(DenseBwdParams 
   p.dv[b * p.dkv_bs + rest * DH + d] = sv;
 }
 
+// ---- matrix-core forms (bf16): lane l of a wave: c = l % 16, g = l / 16.
+constexpr int DM_MAXK = 256;  // keys resident in LDS in the query-major kernel
+
+// Stage rows r0 .. r0+ROWS-1 of a [rows][DH] bf16 head block (row stride
+// `rs` elements) as a row-major copy (pitch RP, zero past DH) and, when tr,
+// a transposed copy (pitch TP, rows DH.. zero); rows past `nrows` are zero.
+template <int DH, int ROWS, int RP, int TP>
+__device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t rs, int r0, int nrows, uint16_t* rowm,
+                                           uint16_t* tr, int tid) {
+  constexpr int NKC = (DH + 31) / 32, CH = NKC * 4, NDT = (DH + 15) / 16;
+  for (int idx = tid; idx < ROWS * CH; idx += BW_NT) {
+    const int r = idx / CH, ch = idx - r * CH;
+    uint4 v = {0, 0, 0, 0};
+    if (ch * 8 < DH && r0 + r < nrows) v = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * rs + ch * 8);
+    *reinterpret_cast<uint4*>(&rowm[r * RP + ch * 8]) = v;
+    if (tr && ch * 8 < NDT * 16) {
+      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * TP + r] = (uint16_t)(a[e >> 1] >> ((e & 1) * 16));
+    }
+  }
+}
+
+// Query-major: 64 queries per workgroup (16 per wave), every key of the head
+// (Nk <= 256) resident in LDS. Pass 1: row max and sum; pass 2: D = sum A dP;
+// pass 3: dS = A (dP - D) and dQ^T = K^T dS^T. Statistics to the workspace.
+template <int DH>
+__global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams p) {
+  constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16;
+  constexpr int TP = DM_MAXK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t kr[DM_MAXK * RP], vr[DM_MAXK * RP], kT[NDT * 16 * TP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int qi = blockIdx.x * DB_Q + w * 16 + c;
+  const bool live = qi < p.Nq;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
+  const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
+  stage_rows<DH, DM_MAXK, RP, TP>(K, DH, 0, p.Nk, kr, kT, tid);
+  stage_rows<DH, DM_MAXK, RP, TP>(V, DH, 0, p.Nk, vr, nullptr, tid);
+  uint4 qf[NKC], gf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int d = kc * 32 + 8 * g;
+    qf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(Q + (int64_t)qi * DH + d) : uint4{0, 0, 0, 0};
+    gf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(G0 + (int64_t)qi * p.D + d) : uint4{0, 0, 0, 0};
+  }
+  __syncthreads();
+  const int ntiles = (p.Nk + 15) / 16;
+  auto scores = [&](int t, floatx4& sc, floatx4* dp) {
+    sc = zero4();
+    if (dp) *dp = zero4();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
+      sc = mfma_bf16(ka, qf[kc], sc);
+      if (dp) {
+        const uint4 va = *reinterpret_cast<const uint4*>(&vr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
+        *dp = mfma_bf16(va, gf[kc], *dp);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = t * 16 + 4 * g + r < p.Nk ? sc[r] * p.scale : -INFINITY;
+  };
+  // pass 1
+  float mx = -INFINITY, l = 0.f;
+  for (int t = 0; t < ntiles; ++t) {
+    floatx4 sc;
+    scores(t, sc, nullptr);
+    const float m2 = fmaxf(mx, fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    if (m2 != -INFINITY) {
+      l = (mx == -INFINITY ? 0.f : l * expf(mx - m2)) + expf(sc[0] - m2) + expf(sc[1] - m2) + expf(sc[2] - m2) +
+          expf(sc[3] - m2);
+      mx = m2;
+    }
+  }
+  {
+    float M = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    float lp = mx == -INFINITY ? 0.f : l * expf(mx - M);
+    lp += __shfl_xor(lp, 16, 64);
+    lp += __shfl_xor(lp, 32, 64);
+    mx = M;
+    l = lp;
+  }
+  const float rl = 1.f / l;
+  // pass 2
+  float dd = 0.f;
+  for (int t = 0; t < ntiles; ++t) {
+    floatx4 sc, dp;
+    scores(t, sc, &dp);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dd += expf(sc[r] - mx) * rl * dp[r];
+  }
+  dd += __shfl_xor(dd, 16, 64);
+  dd += __shfl_xor(dd, 32, 64);
+  // pass 3
+  floatx4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero4();
+  for (int t0 = 0; t0 < ntiles; t0 += 2) {
+    floatx4 ds[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      floatx4 sc, dp;
+      if (t0 + u < ntiles) {
+        scores(t0 + u, sc, &dp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[u][r] = expf(sc[r] - mx) * rl * (dp[r] - dd);
+      } else {
+        ds[u] = zero4();
+      }
+    }
+    const uint4 bf = uint4{pack_bf2(ds[0][0], ds[0][1]), pack_bf2(ds[0][2], ds[0][3]),
+                           pack_bf2(ds[1][0], ds[1][1]), pack_bf2(ds[1][2], ds[1][3])};
+    const int kb = t0 * 16 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int row = (dt * 16 + c) * TP;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
+      acc[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc[dt]);
+    }
+  }
+  if (!live) return;
+  float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int d = dt * 16 + 4 * g;
+    if (d < DH)
+      *reinterpret_cast<float4*>(dq + d) =
+          float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+  }
+  if (g == 0) {
+    float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
+    st[0] = mx; st[1] = l; st[2] = dd;
+  }
+}
+
+// Key-major: 64 keys per workgroup (16 per wave) over one chunk of the
+// queries, 64-query tiles staged row-major (Q, dO: A operands of S = Q K^T,
+// dP = dO V^T) and transposed (Q^T, dO^T: A operands of dK^T = Q^T dS,
+// dV^T = dO^T A, contraction in the permuted query order of the registers).
+template <int DH>
+__global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams p) {
+  constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16, TP = DB_Q + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t qr[DB_Q * RP], gr[DB_Q * RP], qT[NDT * 16 * TP],
+      gT[NDT * 16 * TP];
+  __shared__ float st[DB_Q * 3];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int chunk = blockIdx.y, bh = blockIdx.z, b = bh / p.heads, h = bh - b * p.heads;
+  const int kj = blockIdx.x * DB_K + w * 16 + c;
+  const bool live = kj < p.Nk;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
+  const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
+  const float* S = p.stats + ((int64_t)b * p.heads + h) * p.Nq * 3;
+  uint4 kf[NKC], vf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int d = kc * 32 + 8 * g;
+    kf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(K + (int64_t)kj * DH + d) : uint4{0, 0, 0, 0};
+    vf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(V + (int64_t)kj * DH + d) : uint4{0, 0, 0, 0};
+  }
+  floatx4 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
+  const int q0 = chunk * p.qchunk, q1 = min(p.Nq, q0 + p.qchunk);
+  for (int t0 = q0; t0 < q1; t0 += DB_Q) {
+    __syncthreads();
+    stage_rows<DH, DB_Q, RP, TP>(Q, DH, t0, q1, qr, qT, tid);
+    stage_rows<DH, DB_Q, RP, TP>(G0, p.D, t0, q1, gr, gT, tid);
+    for (int idx = tid; idx < DB_Q * 3; idx += BW_NT) st[idx] = t0 + idx / 3 < q1 ? S[(int64_t)t0 * 3 + idx] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int qt0 = 0; qt0 < 4; qt0 += 2) {
+      floatx4 pa[2], da[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qt = qt0 + u;
+        floatx4 sc = zero4(), dp = zero4();
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const uint4 qa = *reinterpret_cast<const uint4*>(&qr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
+          const uint4 ga = *reinterpret_cast<const uint4*>(&gr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
+          sc = mfma_bf16(qa, kf[kc], sc);
+          dp = mfma_bf16(ga, vf[kc], dp);
+        }
+        // S[query qt*16 + 4g + r][key c]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qrow = qt * 16 + 4 * g + r;
+          const float a = t0 + qrow < q1 ? expf(sc[r] * p.scale - st[qrow * 3]) / st[qrow * 3 + 1] : 0.f;
+          pa[u][r] = a;
+          da[u][r] = a * (dp[r] - st[qrow * 3 + 2]);
+        }
+      }
+      const uint4 pf = uint4{pack_bf2(pa[0][0], pa[0][1]), pack_bf2(pa[0][2], pa[0][3]),
+                             pack_bf2(pa[1][0], pa[1][1]), pack_bf2(pa[1][2], pa[1][3])};
+      const uint4 df = uint4{pack_bf2(da[0][0], da[0][1]), pack_bf2(da[0][2], da[0][3]),
+                             pack_bf2(da[1][0], da[1][1]), pack_bf2(da[1][2], da[1][3])};
+      const int kb = qt0 * 16 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int row = (dt * 16 + c) * TP;
+        const uint2 glo = *reinterpret_cast<const uint2*>(&gT[row + kb]);
+        const uint2 ghi = *reinterpret_cast<const uint2*>(&gT[row + kb + 16]);
+        const uint2 qlo = *reinterpret_cast<const uint2*>(&qT[row + kb]);
+        const uint2 qhi = *reinterpret_cast<const uint2*>(&qT[row + kb + 16]);
+        dv[dt] = mfma_bf16(uint4{glo.x, glo.y, ghi.x, ghi.y}, pf, dv[dt]);
+        dk[dt] = mfma_bf16(uint4{qlo.x, qlo.y, qhi.x, qhi.y}, df, dk[dt]);
+      }
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int d = dt * 16 + 4 * g;
+    if (d >= DH) continue;
+    const float4 kk = float4{dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]};
+    const float4 vv = float4{dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
+    if (p.chunks == 1) {
+      *reinterpret_cast<float4*>(p.dk + b * p.dkv_bs + ((int64_t)h * p.Nk + kj) * DH + d) =
+          float4{kk.x * p.scale, kk.y * p.scale, kk.z * p.scale, kk.w * p.scale};
+      *reinterpret_cast<float4*>(p.dv + b * p.dkv_bs + ((int64_t)h * p.Nk + kj) * DH + d) = vv;
+    } else {
+      float* pt = p.part + ((((int64_t)chunk * p.B + b) * p.heads + h) * p.Nk + kj) * 2 * DH;
+      *reinterpret_cast<float4*>(pt + d) = kk;
+      *reinterpret_cast<float4*>(pt + DH + d) = vv;
+    }
+  }
+}
+
 template <typename T, int DH>
 static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   DenseBwdParams p;
@@ -690,12 +925,14 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   p.B = d.B; p.heads = d.heads; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
   p.qchunk = d.qchunk; p.chunks = d.chunks;
   p.scale = d.scale;
-  hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), dim3((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), dim3(BW_NT), 0, s,
-                     p);
+  constexpr bool BF = sizeof(T) == 2;
+  const dim3 gq((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), gk((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads);
+  if (BF && d.Nk <= DM_MAXK) hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gq, dim3(BW_NT), 0, s, p);
+  else hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), gq, dim3(BW_NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dense_bwd_kv_kernel<T, DH>), dim3((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads),
-                     dim3(BW_NT), 0, s, p);
+  if (BF) hipLaunchKernelGGL((dense_bwd_kv_mfma_kernel<DH>), gk, dim3(BW_NT), 0, s, p);
+  else hipLaunchKernelGGL((dense_bwd_kv_kernel<T, DH>), gk, dim3(BW_NT), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || d.chunks == 1) return e;
   const int64_t n = (int64_t)d.B * d.heads * d.Nk * DH;
