@@ -502,6 +502,7 @@ struct DenseBwdParams {
   float* stats;          // [B][heads][Nq][3]: row max, row sum, D = rowsum(A * dA)
   float* part;           // [chunks][B][heads][Nk][2][dh] when the queries are split
   int B, heads, Nq, Nk, D, qchunk, chunks;
+  int qtiles;            // 64-query tiles per workgroup of the matrix-core query-major kernel
   float scale;
 };
 
@@ -682,6 +683,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_reduce_kernel(DenseBwdParams 
 
 // ---- matrix-core forms (bf16): lane l of a wave: c = l % 16, g = l / 16.
 constexpr int DM_MAXK = 256;  // keys resident in LDS in the query-major kernel
+constexpr int DM_QT = 4;      // most 64-query tiles per workgroup of the query-major kernel
 
 // Stage rows r0 .. r0+ROWS-1 of a [rows][DH] bf16 head block (row stride
 // `rs` elements) as a row-major copy (pitch RP, zero past DH) and, when tr,
@@ -703,6 +705,42 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t rs, int 
   }
 }
 
+// The same staging in two steps (loads into registers, then LDS writes), so a
+// tile's loads can be in flight while the previous tile is computed.
+template <int DH, int ROWS>
+struct RowChunks {
+  static constexpr int CH = ((DH + 31) / 32) * 4, PER = (ROWS * CH + BW_NT - 1) / BW_NT;
+  uint4 v[PER];
+};
+template <int DH, int ROWS>
+__device__ __forceinline__ void load_rows(const uint16_t* src, int64_t rs, int r0, int nrows, int tid,
+                                          RowChunks<DH, ROWS>& rc) {
+  constexpr int CH = RowChunks<DH, ROWS>::CH;
+#pragma unroll
+  for (int i = 0; i < RowChunks<DH, ROWS>::PER; ++i) {
+    const int idx = tid + i * BW_NT, r = idx / CH, ch = idx - r * CH;
+    rc.v[i] = (idx < ROWS * CH && ch * 8 < DH && r0 + r < nrows)
+                  ? *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * rs + ch * 8)
+                  : uint4{0, 0, 0, 0};
+  }
+}
+template <int DH, int ROWS, int RP, int TP>
+__device__ __forceinline__ void put_rows(const RowChunks<DH, ROWS>& rc, uint16_t* rowm, uint16_t* tr, int tid) {
+  constexpr int CH = RowChunks<DH, ROWS>::CH, NDT = (DH + 15) / 16;
+#pragma unroll
+  for (int i = 0; i < RowChunks<DH, ROWS>::PER; ++i) {
+    const int idx = tid + i * BW_NT, r = idx / CH, ch = idx - r * CH;
+    if (idx >= ROWS * CH) continue;
+    const uint4 v = rc.v[i];
+    *reinterpret_cast<uint4*>(&rowm[r * RP + ch * 8]) = v;
+    if (ch * 8 < NDT * 16) {
+      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * TP + r] = (uint16_t)(a[e >> 1] >> ((e & 1) * 16));
+    }
+  }
+}
+
 // Query-major: 64 queries per workgroup (16 per wave), every key of the head
 // (Nk <= 256) resident in LDS. Pass 1: row max and sum; pass 2: D = sum A dP;
 // pass 3: dS = A (dP - D) and dQ^T = K^T dS^T. Statistics to the workspace.
@@ -713,14 +751,17 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   __shared__ __attribute__((aligned(16))) uint16_t kr[DM_MAXK * RP], vr[DM_MAXK * RP], kT[NDT * 16 * TP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int qi = blockIdx.x * DB_Q + w * 16 + c;
-  const bool live = qi < p.Nq;
   const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
   const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
   stage_rows<DH, DM_MAXK, RP, TP>(K, DH, 0, p.Nk, kr, kT, tid);
   stage_rows<DH, DM_MAXK, RP, TP>(V, DH, 0, p.Nk, vr, nullptr, tid);
+  __syncthreads();
+  // the staged keys serve DM_QT query tiles of 64
+  for (int qt = 0; qt < p.qtiles; ++qt) {
+  const int qi = (blockIdx.x * p.qtiles + qt) * DB_Q + w * 16 + c;
+  const bool live = qi < p.Nq;
   uint4 qf[NKC], gf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
@@ -728,7 +769,6 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
     qf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(Q + (int64_t)qi * DH + d) : uint4{0, 0, 0, 0};
     gf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(G0 + (int64_t)qi * p.D + d) : uint4{0, 0, 0, 0};
   }
-  __syncthreads();
   const int ntiles = (p.Nk + 15) / 16;
   auto scores = [&](int t, floatx4& sc, floatx4* dp) {
     sc = zero4();
@@ -752,15 +792,15 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
     scores(t, sc, nullptr);
     const float m2 = fmaxf(mx, fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (m2 != -INFINITY) {
-      l = (mx == -INFINITY ? 0.f : l * expf(mx - m2)) + expf(sc[0] - m2) + expf(sc[1] - m2) + expf(sc[2] - m2) +
-          expf(sc[3] - m2);
+      l = (mx == -INFINITY ? 0.f : l * __expf(mx - m2)) + __expf(sc[0] - m2) + __expf(sc[1] - m2) + __expf(sc[2] - m2) +
+          __expf(sc[3] - m2);
       mx = m2;
     }
   }
   {
     float M = fmaxf(mx, __shfl_xor(mx, 16, 64));
     M = fmaxf(M, __shfl_xor(M, 32, 64));
-    float lp = mx == -INFINITY ? 0.f : l * expf(mx - M);
+    float lp = mx == -INFINITY ? 0.f : l * __expf(mx - M);
     lp += __shfl_xor(lp, 16, 64);
     lp += __shfl_xor(lp, 32, 64);
     mx = M;
@@ -773,7 +813,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
     floatx4 sc, dp;
     scores(t, sc, &dp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dd += expf(sc[r] - mx) * rl * dp[r];
+    for (int r = 0; r < 4; ++r) dd += __expf(sc[r] - mx) * rl * dp[r];
   }
   dd += __shfl_xor(dd, 16, 64);
   dd += __shfl_xor(dd, 32, 64);
@@ -789,7 +829,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
       if (t0 + u < ntiles) {
         scores(t0 + u, sc, &dp);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[u][r] = expf(sc[r] - mx) * rl * (dp[r] - dd);
+        for (int r = 0; r < 4; ++r) ds[u][r] = __expf(sc[r] - mx) * rl * (dp[r] - dd);
       } else {
         ds[u] = zero4();
       }
@@ -805,18 +845,20 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
       acc[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc[dt]);
     }
   }
-  if (!live) return;
-  float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
+  if (live) {
+    float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const int d = dt * 16 + 4 * g;
-    if (d < DH)
-      *reinterpret_cast<float4*>(dq + d) =
-          float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = dt * 16 + 4 * g;
+      if (d < DH)
+        *reinterpret_cast<float4*>(dq + d) =
+            float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+    }
+    if (g == 0) {
+      float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
+      st[0] = mx; st[1] = l; st[2] = dd;
+    }
   }
-  if (g == 0) {
-    float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
-    st[0] = mx; st[1] = l; st[2] = dd;
   }
 }
 
@@ -850,12 +892,23 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
   const int q0 = chunk * p.qchunk, q1 = min(p.Nq, q0 + p.qchunk);
+  // the next tile's global loads are issued before the current tile's
+  // products and written to LDS after them
+  RowChunks<DH, DB_Q> qa, ga;
+  float sv = 0.f;
+  auto fetch = [&](int t0) {
+    load_rows<DH, DB_Q>(Q, DH, t0, q1, tid, qa);
+    load_rows<DH, DB_Q>(G0, p.D, t0, q1, tid, ga);
+    if (tid < DB_Q * 3) sv = t0 + tid / 3 < q1 ? S[(int64_t)t0 * 3 + tid] : 0.f;
+  };
+  if (q0 < q1) fetch(q0);
   for (int t0 = q0; t0 < q1; t0 += DB_Q) {
     __syncthreads();
-    stage_rows<DH, DB_Q, RP, TP>(Q, DH, t0, q1, qr, qT, tid);
-    stage_rows<DH, DB_Q, RP, TP>(G0, p.D, t0, q1, gr, gT, tid);
-    for (int idx = tid; idx < DB_Q * 3; idx += BW_NT) st[idx] = t0 + idx / 3 < q1 ? S[(int64_t)t0 * 3 + idx] : 0.f;
+    put_rows<DH, DB_Q, RP, TP>(qa, qr, qT, tid);
+    put_rows<DH, DB_Q, RP, TP>(ga, gr, gT, tid);
+    if (tid < DB_Q * 3) st[tid] = tid % 3 == 1 ? (sv > 0.f ? 1.f / sv : 0.f) : sv;  // row sum -> its reciprocal
     __syncthreads();
+    if (t0 + DB_Q < q1) fetch(t0 + DB_Q);
 #pragma unroll
     for (int qt0 = 0; qt0 < 4; qt0 += 2) {
       floatx4 pa[2], da[2];
@@ -874,7 +927,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qrow = qt * 16 + 4 * g + r;
-          const float a = t0 + qrow < q1 ? expf(sc[r] * p.scale - st[qrow * 3]) / st[qrow * 3 + 1] : 0.f;
+          const float a = t0 + qrow < q1 ? __expf(sc[r] * p.scale - st[qrow * 3]) * st[qrow * 3 + 1] : 0.f;
           pa[u][r] = a;
           da[u][r] = a * (dp[r] - st[qrow * 3 + 2]);
         }
@@ -927,7 +980,11 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   p.scale = d.scale;
   constexpr bool BF = sizeof(T) == 2;
   const dim3 gq((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), gk((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads);
-  if (BF && d.Nk <= DM_MAXK) hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gq, dim3(BW_NT), 0, s, p);
+  // several query tiles per workgroup (the staged keys serve them all) while
+  // that still leaves at least 1024 workgroups
+  p.qtiles = (int64_t)((d.Nq + DB_Q * DM_QT - 1) / (DB_Q * DM_QT)) * d.heads * d.B >= 1024 ? DM_QT : 1;
+  const dim3 gq4((d.Nq + DB_Q * p.qtiles - 1) / (DB_Q * p.qtiles), d.heads, d.B);
+  if (BF && d.Nk <= DM_MAXK) hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gq4, dim3(BW_NT), 0, s, p);
   else hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), gq, dim3(BW_NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
