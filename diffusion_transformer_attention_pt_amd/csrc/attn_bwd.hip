@@ -741,14 +741,16 @@ __device__ __forceinline__ void put_rows(const RowChunks<DH, ROWS>& rc, uint16_t
   }
 }
 
-// Query-major: every key of the head (Nk <= 256) resident in LDS; each wave
-// takes QS sub-tiles of 16 queries at once, so every K / V fragment read from
-// LDS feeds QS products. Pass 1: row max and sum; pass 2: D = sum A dP;
-// pass 3: dS = A (dP - D) and dQ^T = K^T dS^T. Statistics to the workspace.
-template <int DH, int QS>
+// Query-major: every key of the head (Nk <= 256) resident in LDS, 16 queries
+// a wave. One pass: all Nk scores and dP values of the lane's query column
+// stay in registers (16 tiles of 4), so the softmax is exact without a
+// second look at the keys; then D = sum A dP, dS = A (dP - D) and
+// dQ^T = K^T dS^T with dS^T packed from the registers. Statistics to the
+// workspace.
+template <int DH>
 __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams p) {
   constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16;
-  constexpr int TP = DM_MAXK + 8;
+  constexpr int TP = DM_MAXK + 8, MT = DM_MAXK / 16;
   __shared__ __attribute__((aligned(16))) uint16_t kr[DM_MAXK * RP], vr[DM_MAXK * RP], kT[NDT * 16 * TP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -760,141 +762,96 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   stage_rows<DH, DM_MAXK, RP, TP>(V, DH, 0, p.Nk, vr, nullptr, tid);
   __syncthreads();
   const int ntiles = (p.Nk + 15) / 16;
-  // the staged keys serve p.qtiles tiles of QS * 64 queries
+  // the staged keys serve p.qtiles tiles of 64 queries
   for (int qt = 0; qt < p.qtiles; ++qt) {
-    int qi[QS];
-    bool live[QS];
-    uint4 qf[QS][NKC], gf[QS][NKC];
+    const int qi = (blockIdx.x * p.qtiles + qt) * DB_Q + w * 16 + c;
+    const bool live = qi < p.Nq;
+    uint4 qf[NKC], gf[NKC];
 #pragma unroll
-    for (int u = 0; u < QS; ++u) {
-      qi[u] = ((blockIdx.x * p.qtiles + qt) * QS + u) * DB_Q + w * 16 + c;
-      live[u] = qi[u] < p.Nq;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const int d = kc * 32 + 8 * g;
-        qf[u][kc] = (live[u] && d < DH) ? *reinterpret_cast<const uint4*>(Q + (int64_t)qi[u] * DH + d)
-                                        : uint4{0, 0, 0, 0};
-        gf[u][kc] = (live[u] && d < DH) ? *reinterpret_cast<const uint4*>(G0 + (int64_t)qi[u] * p.D + d)
-                                        : uint4{0, 0, 0, 0};
-      }
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = kc * 32 + 8 * g;
+      qf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(Q + (int64_t)qi * DH + d) : uint4{0, 0, 0, 0};
+      gf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(G0 + (int64_t)qi * p.D + d) : uint4{0, 0, 0, 0};
     }
-    // S^T (and dP^T) of key tile t for the QS sub-tiles
-    auto scores = [&](int t, floatx4 (&sc)[QS], floatx4* dp) {
+    floatx4 sc[MT], dp[MT];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < QS; ++u) {
-        sc[u] = zero4();
-        if (dp) dp[u] = zero4();
-      }
+    for (int t = 0; t < MT; ++t) {
+      sc[t] = zero4();
+      dp[t] = zero4();
+      if (t < ntiles) {
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
-#pragma unroll
-        for (int u = 0; u < QS; ++u) sc[u] = mfma_bf16(ka, qf[u][kc], sc[u]);
-        if (dp) {
+        for (int kc = 0; kc < NKC; ++kc) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
           const uint4 va = *reinterpret_cast<const uint4*>(&vr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
-#pragma unroll
-          for (int u = 0; u < QS; ++u) dp[u] = mfma_bf16(va, gf[u][kc], dp[u]);
+          sc[t] = mfma_bf16(ka, qf[kc], sc[t]);
+          dp[t] = mfma_bf16(va, gf[kc], dp[t]);
         }
       }
 #pragma unroll
-      for (int u = 0; u < QS; ++u)
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] = t * 16 + 4 * g + r < p.Nk ? sc[t][r] * p.scale : -INFINITY;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float l = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[u][r] = t * 16 + 4 * g + r < p.Nk ? sc[u][r] * p.scale : -INFINITY;
-    };
-    // pass 1
-    float mx[QS], l[QS], rl[QS], dd[QS];
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int u = 0; u < QS; ++u) { mx[u] = -INFINITY; l[u] = 0.f; dd[u] = 0.f; }
-    for (int t = 0; t < ntiles; ++t) {
-      floatx4 sc[QS];
-      scores(t, sc, nullptr);
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] = __expf(sc[t][r] - mx);  // keys past Nk: exp(-inf) = 0
+        l += sc[t][r];
+      }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float rl = 1.f / l;
+    float dd = 0.f;
 #pragma unroll
-      for (int u = 0; u < QS; ++u) {
-        const float m2 = fmaxf(mx[u], fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
-        if (m2 != -INFINITY) {
-          l[u] = (mx[u] == -INFINITY ? 0.f : l[u] * __expf(mx[u] - m2)) + __expf(sc[u][0] - m2) +
-                 __expf(sc[u][1] - m2) + __expf(sc[u][2] - m2) + __expf(sc[u][3] - m2);
-          mx[u] = m2;
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] *= rl;
+        dd += sc[t][r] * dp[t][r];
+      }
+    dd += __shfl_xor(dd, 16, 64);
+    dd += __shfl_xor(dd, 32, 64);
+    floatx4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero4();
+#pragma unroll
+    for (int t0 = 0; t0 < MT; t0 += 2) {
+      if (t0 < ntiles) {
+        floatx4 ds[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[v][r] = sc[t0 + v][r] * (dp[t0 + v][r] - dd);
+        const uint4 bf = uint4{pack_bf2(ds[0][0], ds[0][1]), pack_bf2(ds[0][2], ds[0][3]),
+                               pack_bf2(ds[1][0], ds[1][1]), pack_bf2(ds[1][2], ds[1][3])};
+        const int kb = t0 * 16 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int row = (dt * 16 + c) * TP;
+          const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
+          acc[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc[dt]);
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < QS; ++u) {
-      float M = fmaxf(mx[u], __shfl_xor(mx[u], 16, 64));
-      M = fmaxf(M, __shfl_xor(M, 32, 64));
-      float lp = mx[u] == -INFINITY ? 0.f : l[u] * __expf(mx[u] - M);
-      lp += __shfl_xor(lp, 16, 64);
-      lp += __shfl_xor(lp, 32, 64);
-      mx[u] = M;
-      l[u] = lp;
-      rl[u] = 1.f / lp;
-    }
-    // pass 2
-    for (int t = 0; t < ntiles; ++t) {
-      floatx4 sc[QS], dp[QS];
-      scores(t, sc, dp);
-#pragma unroll
-      for (int u = 0; u < QS; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dd[u] += __expf(sc[u][r] - mx[u]) * rl[u] * dp[u][r];
-    }
-#pragma unroll
-    for (int u = 0; u < QS; ++u) {
-      dd[u] += __shfl_xor(dd[u], 16, 64);
-      dd[u] += __shfl_xor(dd[u], 32, 64);
-    }
-    // pass 3
-    floatx4 acc[QS][NDT];
-#pragma unroll
-    for (int u = 0; u < QS; ++u)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = zero4();
-    for (int t0 = 0; t0 < ntiles; t0 += 2) {
-      uint4 bf[QS];
-      floatx4 ds[2][QS];
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        floatx4 sc[QS], dp[QS];
-        if (t0 + v < ntiles) {
-          scores(t0 + v, sc, dp);
-#pragma unroll
-          for (int u = 0; u < QS; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ds[v][u][r] = __expf(sc[u][r] - mx[u]) * rl[u] * (dp[u][r] - dd[u]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < QS; ++u) ds[v][u] = zero4();
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < QS; ++u)
-        bf[u] = uint4{pack_bf2(ds[0][u][0], ds[0][u][1]), pack_bf2(ds[0][u][2], ds[0][u][3]),
-                      pack_bf2(ds[1][u][0], ds[1][u][1]), pack_bf2(ds[1][u][2], ds[1][u][3])};
-      const int kb = t0 * 16 + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int row = (dt * 16 + c) * TP;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
-        const uint4 ka = uint4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-        for (int u = 0; u < QS; ++u) acc[u][dt] = mfma_bf16(ka, bf[u], acc[u][dt]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < QS; ++u) {
-      if (!live[u]) continue;
-      float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi[u]) * DH;
+    if (live) {
+      float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int d = dt * 16 + 4 * g;
         if (d < DH)
-          *reinterpret_cast<float4*>(dq + d) = float4{acc[u][dt][0] * p.scale, acc[u][dt][1] * p.scale,
-                                                      acc[u][dt][2] * p.scale, acc[u][dt][3] * p.scale};
+          *reinterpret_cast<float4*>(dq + d) =
+              float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
       }
       if (g == 0) {
-        float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi[u]) * 3;
-        st[0] = mx[u]; st[1] = l[u]; st[2] = dd[u];
+        float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
+        st[0] = mx; st[1] = l; st[2] = dd;
       }
     }
   }
@@ -1018,21 +975,16 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   p.scale = d.scale;
   constexpr bool BF = sizeof(T) == 2;
   const dim3 gq((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), gk((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads);
-  // matrix-core query-major kernel: two 16-query sub-tiles a wave and
-  // several 128-query tiles a workgroup (the staged keys serve them all)
-  // while that still leaves at least 1024 workgroups; one sub-tile a wave
-  // and one tile a workgroup for small query counts
+  // matrix-core query-major kernel: several 64-query tiles a workgroup (the
+  // staged keys serve them all) while that still leaves >= 1024 workgroups
   const int64_t bh = (int64_t)d.heads * d.B;
-  const bool wide = (int64_t)((d.Nq + 2 * DB_Q - 1) / (2 * DB_Q)) * bh >= 1024;
   p.qtiles = 1;
-  while (wide && p.qtiles < DM_QT &&
-         (int64_t)((d.Nq + 4 * DB_Q * p.qtiles - 1) / (4 * DB_Q * p.qtiles)) * bh >= 1024)
+  while (p.qtiles < DM_QT && (int64_t)((d.Nq + 2 * DB_Q * p.qtiles - 1) / (2 * DB_Q * p.qtiles)) * bh >= 1024)
     p.qtiles *= 2;
-  const int qpw = (wide ? 2 : 1) * DB_Q * p.qtiles;  // queries a workgroup
+  const int qpw = DB_Q * p.qtiles;  // queries a workgroup
   const dim3 gqm((d.Nq + qpw - 1) / qpw, d.heads, d.B);
   if (BF && d.Nk <= DM_MAXK) {
-    if (wide) hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH, 2>), gqm, dim3(BW_NT), 0, s, p);
-    else hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH, 1>), gqm, dim3(BW_NT), 0, s, p);
+    hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gqm, dim3(BW_NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), gq, dim3(BW_NT), 0, s, p);
   }
