@@ -857,11 +857,12 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   }
 }
 
-// Key-major: 64 keys per workgroup (16 per wave) over one chunk of the
-// queries, 64-query tiles staged row-major (Q, dO: A operands of S = Q K^T,
-// dP = dO V^T) and transposed (Q^T, dO^T: A operands of dK^T = Q^T dS,
-// dV^T = dO^T A, contraction in the permuted query order of the registers).
-template <int DH>
+// Key-major: KS * 64 keys per workgroup (KS sub-tiles of 16 a wave) over one
+// chunk of the queries, 64-query tiles staged row-major (Q, dO: A operands of
+// S = Q K^T, dP = dO V^T) and transposed (Q^T, dO^T: A operands of
+// dK^T = Q^T dS, dV^T = dO^T A, contraction in the permuted query order of
+// the registers). Every fragment read from LDS feeds KS products.
+template <int DH, int KS>
 __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams p) {
   constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16, TP = DB_Q + 8;
   __shared__ __attribute__((aligned(16))) uint16_t qr[DB_Q * RP], gr[DB_Q * RP], qT[NDT * 16 * TP],
@@ -869,23 +870,30 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
   __shared__ float st[DB_Q * 3];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.y, bh = blockIdx.z, b = bh / p.heads, h = bh - b * p.heads;
-  const int kj = blockIdx.x * DB_K + w * 16 + c;
-  const bool live = kj < p.Nk;
   const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
   const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
   const float* S = p.stats + ((int64_t)b * p.heads + h) * p.Nq * 3;
-  uint4 kf[NKC], vf[NKC];
+  int kj[KS];
+  bool live[KS];
+  uint4 kf[KS][NKC], vf[KS][NKC];
+  floatx4 dk[KS][NDT], dv[KS][NDT];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) {
-    const int d = kc * 32 + 8 * g;
-    kf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(K + (int64_t)kj * DH + d) : uint4{0, 0, 0, 0};
-    vf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(V + (int64_t)kj * DH + d) : uint4{0, 0, 0, 0};
+  for (int u = 0; u < KS; ++u) {
+    kj[u] = blockIdx.x * (DB_K * KS) + u * DB_K + w * 16 + c;
+    live[u] = kj[u] < p.Nk;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = kc * 32 + 8 * g;
+      kf[u][kc] = (live[u] && d < DH) ? *reinterpret_cast<const uint4*>(K + (int64_t)kj[u] * DH + d)
+                                      : uint4{0, 0, 0, 0};
+      vf[u][kc] = (live[u] && d < DH) ? *reinterpret_cast<const uint4*>(V + (int64_t)kj[u] * DH + d)
+                                      : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) { dk[u][dt] = zero4(); dv[u][dt] = zero4(); }
   }
-  floatx4 dk[NDT], dv[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
   const int q0 = chunk * p.qchunk, q1 = min(p.Nq, q0 + p.qchunk);
   // the next tile's global loads are issued before the current tile's
   // products and written to LDS after them
@@ -906,31 +914,45 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
     if (t0 + DB_Q < q1) fetch(t0 + DB_Q);
 #pragma unroll
     for (int qt0 = 0; qt0 < 4; qt0 += 2) {
-      floatx4 pa[2], da[2];
+      floatx4 pa[KS][2], da[KS][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qt = qt0 + u;
-        floatx4 sc = zero4(), dp = zero4();
+      for (int v = 0; v < 2; ++v) {
+        const int qt = qt0 + v;
+        floatx4 sc[KS], dp[KS];
+#pragma unroll
+        for (int u = 0; u < KS; ++u) { sc[u] = zero4(); dp[u] = zero4(); }
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          const uint4 qa = *reinterpret_cast<const uint4*>(&qr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
-          const uint4 ga = *reinterpret_cast<const uint4*>(&gr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
-          sc = mfma_bf16(qa, kf[kc], sc);
-          dp = mfma_bf16(ga, vf[kc], dp);
+          const uint4 qa4 = *reinterpret_cast<const uint4*>(&qr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
+          const uint4 ga4 = *reinterpret_cast<const uint4*>(&gr[(qt * 16 + c) * RP + kc * 32 + 8 * g]);
+#pragma unroll
+          for (int u = 0; u < KS; ++u) {
+            sc[u] = mfma_bf16(qa4, kf[u][kc], sc[u]);
+            dp[u] = mfma_bf16(ga4, vf[u][kc], dp[u]);
+          }
         }
-        // S[query qt*16 + 4g + r][key c]
+        // S[query qt*16 + 4g + r][key of sub-tile u, column c]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qrow = qt * 16 + 4 * g + r;
-          const float a = t0 + qrow < q1 ? __expf(sc[r] * p.scale - st[qrow * 3]) * st[qrow * 3 + 1] : 0.f;
-          pa[u][r] = a;
-          da[u][r] = a * (dp[r] - st[qrow * 3 + 2]);
+          const bool qok = t0 + qrow < q1;
+          const float m = st[qrow * 3], rl = st[qrow * 3 + 1], dd = st[qrow * 3 + 2];
+#pragma unroll
+          for (int u = 0; u < KS; ++u) {
+            const float a = qok ? __expf(sc[u][r] * p.scale - m) * rl : 0.f;
+            pa[u][v][r] = a;
+            da[u][v][r] = a * (dp[u][r] - dd);
+          }
         }
       }
-      const uint4 pf = uint4{pack_bf2(pa[0][0], pa[0][1]), pack_bf2(pa[0][2], pa[0][3]),
-                             pack_bf2(pa[1][0], pa[1][1]), pack_bf2(pa[1][2], pa[1][3])};
-      const uint4 df = uint4{pack_bf2(da[0][0], da[0][1]), pack_bf2(da[0][2], da[0][3]),
-                             pack_bf2(da[1][0], da[1][1]), pack_bf2(da[1][2], da[1][3])};
+      uint4 pf[KS], df[KS];
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        pf[u] = uint4{pack_bf2(pa[u][0][0], pa[u][0][1]), pack_bf2(pa[u][0][2], pa[u][0][3]),
+                      pack_bf2(pa[u][1][0], pa[u][1][1]), pack_bf2(pa[u][1][2], pa[u][1][3])};
+        df[u] = uint4{pack_bf2(da[u][0][0], da[u][0][1]), pack_bf2(da[u][0][2], da[u][0][3]),
+                      pack_bf2(da[u][1][0], da[u][1][1]), pack_bf2(da[u][1][2], da[u][1][3])};
+      }
       const int kb = qt0 * 16 + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -939,26 +961,33 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
         const uint2 ghi = *reinterpret_cast<const uint2*>(&gT[row + kb + 16]);
         const uint2 qlo = *reinterpret_cast<const uint2*>(&qT[row + kb]);
         const uint2 qhi = *reinterpret_cast<const uint2*>(&qT[row + kb + 16]);
-        dv[dt] = mfma_bf16(uint4{glo.x, glo.y, ghi.x, ghi.y}, pf, dv[dt]);
-        dk[dt] = mfma_bf16(uint4{qlo.x, qlo.y, qhi.x, qhi.y}, df, dk[dt]);
+        const uint4 gA = uint4{glo.x, glo.y, ghi.x, ghi.y}, qA = uint4{qlo.x, qlo.y, qhi.x, qhi.y};
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          dv[u][dt] = mfma_bf16(gA, pf[u], dv[u][dt]);
+          dk[u][dt] = mfma_bf16(qA, df[u], dk[u][dt]);
+        }
       }
     }
   }
-  if (!live) return;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const int d = dt * 16 + 4 * g;
-    if (d >= DH) continue;
-    const float4 kk = float4{dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]};
-    const float4 vv = float4{dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
-    if (p.chunks == 1) {
-      *reinterpret_cast<float4*>(p.dk + b * p.dkv_bs + ((int64_t)h * p.Nk + kj) * DH + d) =
-          float4{kk.x * p.scale, kk.y * p.scale, kk.z * p.scale, kk.w * p.scale};
-      *reinterpret_cast<float4*>(p.dv + b * p.dkv_bs + ((int64_t)h * p.Nk + kj) * DH + d) = vv;
-    } else {
-      float* pt = p.part + ((((int64_t)chunk * p.B + b) * p.heads + h) * p.Nk + kj) * 2 * DH;
-      *reinterpret_cast<float4*>(pt + d) = kk;
-      *reinterpret_cast<float4*>(pt + DH + d) = vv;
+  for (int u = 0; u < KS; ++u) {
+    if (!live[u]) continue;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = dt * 16 + 4 * g;
+      if (d >= DH) continue;
+      const float4 kk = float4{dk[u][dt][0], dk[u][dt][1], dk[u][dt][2], dk[u][dt][3]};
+      const float4 vv = float4{dv[u][dt][0], dv[u][dt][1], dv[u][dt][2], dv[u][dt][3]};
+      if (p.chunks == 1) {
+        *reinterpret_cast<float4*>(p.dk + b * p.dkv_bs + ((int64_t)h * p.Nk + kj[u]) * DH + d) =
+            float4{kk.x * p.scale, kk.y * p.scale, kk.z * p.scale, kk.w * p.scale};
+        *reinterpret_cast<float4*>(p.dv + b * p.dkv_bs + ((int64_t)h * p.Nk + kj[u]) * DH + d) = vv;
+      } else {
+        float* pt = p.part + ((((int64_t)chunk * p.B + b) * p.heads + h) * p.Nk + kj[u]) * 2 * DH;
+        *reinterpret_cast<float4*>(pt + d) = kk;
+        *reinterpret_cast<float4*>(pt + DH + d) = vv;
+      }
     }
   }
 }
@@ -990,7 +1019,12 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (BF) hipLaunchKernelGGL((dense_bwd_kv_mfma_kernel<DH>), gk, dim3(BW_NT), 0, s, p);
+  // two 16-key sub-tiles a wave when there are at least 128 keys and the grid
+  // keeps at least one workgroup per CU
+  const dim3 gk2((d.Nk + 2 * DB_K - 1) / (2 * DB_K), d.chunks, d.B * d.heads);
+  const bool ks2 = d.Nk >= 2 * DB_K && (int64_t)gk2.x * gk2.y * gk2.z >= 256;
+  if (BF && ks2) hipLaunchKernelGGL((dense_bwd_kv_mfma_kernel<DH, 2>), gk2, dim3(BW_NT), 0, s, p);
+  else if (BF) hipLaunchKernelGGL((dense_bwd_kv_mfma_kernel<DH, 1>), gk, dim3(BW_NT), 0, s, p);
   else hipLaunchKernelGGL((dense_bwd_kv_kernel<T, DH>), gk, dim3(BW_NT), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || d.chunks == 1) return e;
