@@ -52,6 +52,20 @@ __device__ __forceinline__ int region_of(int k, int L, int w, int s) {
   return k < L - w ? 0 : (k < L - s ? 1 : 2);
 }
 
+// Transposed write of chunk ch (8 elements) of the four rows s0 .. s0+3:
+// t[(8 ch + e) * pitch + s0 + j] = element e of v[j], one 8-byte write per e.
+__device__ __forceinline__ void put_quad_t(uint16_t* t, int pitch, int ch, int s0, const uint4 (&v)[4]) {
+  const uint32_t a0[4] = {v[0].x, v[0].y, v[0].z, v[0].w}, a1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+  const uint32_t a2[4] = {v[2].x, v[2].y, v[2].z, v[2].w}, a3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = (e & 1) * 16;
+    const uint32_t lo = ((a0[e >> 1] >> sh) & 0xffffu) | (((a1[e >> 1] >> sh) & 0xffffu) << 16);
+    const uint32_t hi = ((a2[e >> 1] >> sh) & 0xffffu) | (((a3[e >> 1] >> sh) & 0xffffu) << 16);
+    *reinterpret_cast<uint2*>(&t[(ch * 8 + e) * pitch + s0]) = uint2{lo, hi};
+  }
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -303,34 +317,38 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
 
   // staging: 16-byte chunks (8 dims) of every slot; row-major K, V (zero past
   // DH), transposed K, Q, dO (rows DH.. of the transposed copies zero)
-  constexpr int CH = NKC * 4;  // chunks per padded row
-  for (int idx = tid; idx < KEYS * CH; idx += BW_NT) {
-    const int sl = idx / CH, ch = idx - sl * CH;
-    const int tok = tok_s[sl];
-    uint4 kq = {0, 0, 0, 0}, vq = {0, 0, 0, 0}, qq = {0, 0, 0, 0}, gq = {0, 0, 0, 0};
-    if (ch * 8 < DH) {
-      if (tok >= 0) {
-        kq = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
-        vq = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
-        qq = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
-        gq = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
-      } else if (tok == -1 && bias) {
-        kq = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
-        vq = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
+  // one thread per (8-dim chunk, quad of slots), quads fastest: the four
+  // slots' chunks are transposed in registers, so each transposed row gets
+  // one 8-byte write (and a wave's writes fall in distinct banks)
+  constexpr int CH = NKC * 4, QUADS = KEYS / 4;  // chunks per padded row, slot quads
+  for (int idx = tid; idx < CH * QUADS; idx += BW_NT) {
+    const int ch = idx / QUADS, kq = idx - ch * QUADS;
+    uint4 k4[4], v4[4], q4[4], g4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = tok_s[kq * 4 + j];
+      k4[j] = v4[j] = q4[j] = g4[j] = uint4{0, 0, 0, 0};
+      if (ch * 8 < DH) {
+        if (tok >= 0) {
+          k4[j] = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
+          v4[j] = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
+          q4[j] = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
+          g4[j] = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
+        } else if (tok == -1 && bias) {
+          k4[j] = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
+          v4[j] = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
+        }
       }
     }
-    *reinterpret_cast<uint4*>(&kr[sl * RP + ch * 8]) = kq;
-    *reinterpret_cast<uint4*>(&vr[sl * RP + ch * 8]) = vq;
-    if (ch * 8 < NDT * 16) {
-      const uint32_t ka[4] = {kq.x, kq.y, kq.z, kq.w}, qa[4] = {qq.x, qq.y, qq.z, qq.w},
-                     ga[4] = {gq.x, gq.y, gq.z, gq.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = (ch * 8 + e) * TP + sl, sh = (e & 1) * 16;
-        kT[row] = (uint16_t)(ka[e >> 1] >> sh);
-        qT[row] = (uint16_t)(qa[e >> 1] >> sh);
-        gT[row] = (uint16_t)(ga[e >> 1] >> sh);
-      }
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint4*>(&kr[(kq * 4 + j) * RP + ch * 8]) = k4[j];
+      *reinterpret_cast<uint4*>(&vr[(kq * 4 + j) * RP + ch * 8]) = v4[j];
+    }
+    if (ch * 8 < NDT * 16) {
+      put_quad_t(kT, TP, ch, kq * 4, k4);
+      put_quad_t(qT, TP, ch, kq * 4, q4);
+      put_quad_t(gT, TP, ch, kq * 4, g4);
     }
   }
   __syncthreads();
@@ -705,40 +723,38 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t rs, int 
   }
 }
 
-// The same staging in two steps (loads into registers, then LDS writes), so a
-// tile's loads can be in flight while the previous tile is computed.
+// Staging in two steps (loads into registers, then LDS writes), so a tile's
+// loads can be in flight while the previous tile is computed: one thread per
+// (8-dim chunk, quad of rows), quads fastest; the row-major copy gets four
+// 16-byte writes and the transposed copy one 8-byte write per transposed row
+// (put_quad_t).
 template <int DH, int ROWS>
-struct RowChunks {
-  static constexpr int CH = ((DH + 31) / 32) * 4, PER = (ROWS * CH + BW_NT - 1) / BW_NT;
-  uint4 v[PER];
+struct QuadChunks {
+  static constexpr int CH = ((DH + 31) / 32) * 4, QUADS = ROWS / 4, ITEMS = CH * QUADS;
+  static_assert(ITEMS <= BW_NT, "one item a thread");
+  uint4 v[4];
 };
 template <int DH, int ROWS>
-__device__ __forceinline__ void load_rows(const uint16_t* src, int64_t rs, int r0, int nrows, int tid,
-                                          RowChunks<DH, ROWS>& rc) {
-  constexpr int CH = RowChunks<DH, ROWS>::CH;
+__device__ __forceinline__ void load_quads(const uint16_t* src, int64_t rs, int r0, int nrows, int tid,
+                                           QuadChunks<DH, ROWS>& qc) {
+  constexpr int QUADS = QuadChunks<DH, ROWS>::QUADS;
+  const int ch = tid / QUADS, kq = tid - ch * QUADS;
 #pragma unroll
-  for (int i = 0; i < RowChunks<DH, ROWS>::PER; ++i) {
-    const int idx = tid + i * BW_NT, r = idx / CH, ch = idx - r * CH;
-    rc.v[i] = (idx < ROWS * CH && ch * 8 < DH && r0 + r < nrows)
+  for (int j = 0; j < 4; ++j) {
+    const int r = kq * 4 + j;
+    qc.v[j] = (tid < QuadChunks<DH, ROWS>::ITEMS && ch * 8 < DH && r0 + r < nrows)
                   ? *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * rs + ch * 8)
                   : uint4{0, 0, 0, 0};
   }
 }
 template <int DH, int ROWS, int RP, int TP>
-__device__ __forceinline__ void put_rows(const RowChunks<DH, ROWS>& rc, uint16_t* rowm, uint16_t* tr, int tid) {
-  constexpr int CH = RowChunks<DH, ROWS>::CH, NDT = (DH + 15) / 16;
+__device__ __forceinline__ void put_quads(const QuadChunks<DH, ROWS>& qc, uint16_t* rowm, uint16_t* tr, int tid) {
+  constexpr int QUADS = QuadChunks<DH, ROWS>::QUADS, NDT = (DH + 15) / 16;
+  if (tid >= QuadChunks<DH, ROWS>::ITEMS) return;
+  const int ch = tid / QUADS, kq = tid - ch * QUADS;
 #pragma unroll
-  for (int i = 0; i < RowChunks<DH, ROWS>::PER; ++i) {
-    const int idx = tid + i * BW_NT, r = idx / CH, ch = idx - r * CH;
-    if (idx >= ROWS * CH) continue;
-    const uint4 v = rc.v[i];
-    *reinterpret_cast<uint4*>(&rowm[r * RP + ch * 8]) = v;
-    if (ch * 8 < NDT * 16) {
-      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * TP + r] = (uint16_t)(a[e >> 1] >> ((e & 1) * 16));
-    }
-  }
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&rowm[(kq * 4 + j) * RP + ch * 8]) = qc.v[j];
+  if (ch * 8 < NDT * 16) put_quad_t(tr, TP, ch, kq * 4, qc.v);
 }
 
 // Query-major: every key of the head (Nk <= 256) resident in LDS, 16 queries
@@ -897,18 +913,18 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams
   const int q0 = chunk * p.qchunk, q1 = min(p.Nq, q0 + p.qchunk);
   // the next tile's global loads are issued before the current tile's
   // products and written to LDS after them
-  RowChunks<DH, DB_Q> qa, ga;
+  QuadChunks<DH, DB_Q> qa, ga;
   float sv = 0.f;
   auto fetch = [&](int t0) {
-    load_rows<DH, DB_Q>(Q, DH, t0, q1, tid, qa);
-    load_rows<DH, DB_Q>(G0, p.D, t0, q1, tid, ga);
+    load_quads<DH, DB_Q>(Q, DH, t0, q1, tid, qa);
+    load_quads<DH, DB_Q>(G0, p.D, t0, q1, tid, ga);
     if (tid < DB_Q * 3) sv = t0 + tid / 3 < q1 ? S[(int64_t)t0 * 3 + tid] : 0.f;
   };
   if (q0 < q1) fetch(q0);
   for (int t0 = q0; t0 < q1; t0 += DB_Q) {
     __syncthreads();
-    put_rows<DH, DB_Q, RP, TP>(qa, qr, qT, tid);
-    put_rows<DH, DB_Q, RP, TP>(ga, gr, gT, tid);
+    put_quads<DH, DB_Q, RP, TP>(qa, qr, qT, tid);
+    put_quads<DH, DB_Q, RP, TP>(ga, gr, gT, tid);
     if (tid < DB_Q * 3) st[tid] = tid % 3 == 1 ? (sv > 0.f ? 1.f / sv : 0.f) : sv;  // row sum -> its reciprocal
     __syncthreads();
     if (t0 + DB_Q < q1) fetch(t0 + DB_Q);
