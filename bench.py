@@ -98,9 +98,10 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
     proxies), the proxy self-attention core and the window-average backward.
     Each kernel class is timed with the library's HIP-event trace. Rates: the
     algorithmic FLOP of the five products of an attention backward (QK^T,
-    dO V^T, A^T dO, dS K, dS^T Q: 10 * Nq * Nk * d_h per head), against the fp32
-    vector peak (the kernels compute on the vector ALUs), and the HBM bytes
-    (inputs read once, fp32 gradients written once) against 8 TB/s."""
+    dO V^T, A^T dO, dS K, dS^T Q: 10 * Nq * Nk * d_h per head), against the
+    bf16 MFMA peak for bf16 inputs (the matrix-core kernels) and the fp32
+    vector peak for fp32 (the vector-ALU kernels), and the HBM bytes (inputs
+    read once, fp32 gradients written once) against 8 TB/s."""
     import torch
     from diffusion_transformer_attention_pt_amd import _lib
 
@@ -146,9 +147,11 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
         avg = statistics.mean(ms)
         r = {"avg_ms": round(avg, 5), "gflop": round(flop / 1e9, 3), "mbytes": round(nbytes / 1e6, 1),
              "hbm_gbs": round(nbytes / (avg * 1e-3) / 1e9, 1)}
+        r["hbm_frac"] = round(r["hbm_gbs"] / PEAK_HBM_GBS, 4)
         if flop:
             tf = flop / (avg * 1e-3) / 1e12
-            r.update({"tflops": round(tf, 2), "vs_fp32_vector_peak": round(tf / PEAK_FP32_VALU, 4)})
+            pk, pk_name = (PEAK_BF16_TFLOPS, "mfma_bf16") if prec == torch.bfloat16 else (PEAK_FP32_VALU, "fp32_vector")
+            r.update({"tflops": round(tf, 2), "peak": pk_name, "peak_frac": round(tf / pk, 4)})
         res[name] = r
     return res
 

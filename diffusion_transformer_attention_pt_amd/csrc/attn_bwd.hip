@@ -703,26 +703,6 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_reduce_kernel(DenseBwdParams 
 constexpr int DM_MAXK = 256;  // keys resident in LDS in the query-major kernel
 constexpr int DM_QT = 4;      // most 64-query tiles per workgroup of the query-major kernel
 
-// Stage rows r0 .. r0+ROWS-1 of a [rows][DH] bf16 head block (row stride
-// `rs` elements) as a row-major copy (pitch RP, zero past DH) and, when tr,
-// a transposed copy (pitch TP, rows DH.. zero); rows past `nrows` are zero.
-template <int DH, int ROWS, int RP, int TP>
-__device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t rs, int r0, int nrows, uint16_t* rowm,
-                                           uint16_t* tr, int tid) {
-  constexpr int NKC = (DH + 31) / 32, CH = NKC * 4, NDT = (DH + 15) / 16;
-  for (int idx = tid; idx < ROWS * CH; idx += BW_NT) {
-    const int r = idx / CH, ch = idx - r * CH;
-    uint4 v = {0, 0, 0, 0};
-    if (ch * 8 < DH && r0 + r < nrows) v = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * rs + ch * 8);
-    *reinterpret_cast<uint4*>(&rowm[r * RP + ch * 8]) = v;
-    if (tr && ch * 8 < NDT * 16) {
-      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tr[(ch * 8 + e) * TP + r] = (uint16_t)(a[e >> 1] >> ((e & 1) * 16));
-    }
-  }
-}
-
 // Staging in two steps (loads into registers, then LDS writes), so a tile's
 // loads can be in flight while the previous tile is computed: one thread per
 // (8-dim chunk, quad of rows), quads fastest; the row-major copy gets four
@@ -774,8 +754,29 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
   const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
-  stage_rows<DH, DM_MAXK, RP, TP>(K, DH, 0, p.Nk, kr, kT, tid);
-  stage_rows<DH, DM_MAXK, RP, TP>(V, DH, 0, p.Nk, vr, nullptr, tid);
+  {
+    // all keys: K row-major and transposed, V row-major; one item per
+    // (8-dim chunk, quad of keys), quads fastest, all loads of an item
+    // before its writes
+    constexpr int CH = NKC * 4, QUADS = DM_MAXK / 4;
+    for (int idx = tid; idx < CH * QUADS; idx += BW_NT) {
+      const int ch = idx / QUADS, kq = idx - ch * QUADS;
+      uint4 k4[4], v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = kq * 4 + j;
+        const bool ok = ch * 8 < DH && r < p.Nk;
+        k4[j] = ok ? *reinterpret_cast<const uint4*>(K + (int64_t)r * DH + ch * 8) : uint4{0, 0, 0, 0};
+        v4[j] = ok ? *reinterpret_cast<const uint4*>(V + (int64_t)r * DH + ch * 8) : uint4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint4*>(&kr[(kq * 4 + j) * RP + ch * 8]) = k4[j];
+        *reinterpret_cast<uint4*>(&vr[(kq * 4 + j) * RP + ch * 8]) = v4[j];
+      }
+      if (ch * 8 < NDT * 16) put_quad_t(kT, TP, ch, kq * 4, k4);
+    }
+  }
   __syncthreads();
   const int ntiles = (p.Nk + 15) / 16;
   // the staged keys serve p.qtiles tiles of 64 queries
