@@ -23,8 +23,8 @@ Readings (in addition to the forward readings of ptdit_oracle):
              queries are cropped, so they receive no gradient.
   R-bwd-core the backward of the window attention is taken at the attention
              core: from (Q, K, V, dO) of the real tokens to (dQ, dK, dV) and
-             the pad-slot sums; the projections' gradients are ordinary
-             linear-map gradients (dX = dY W, dW = dY^T X, db = sum dY).
+             the pad-slot sums; the projections' gradients are the linear-map
+             gradients of linear_bwd (dX = dY W, dW = dY^T X, db = sum dY).
 """
 from __future__ import annotations
 
@@ -34,7 +34,7 @@ import numpy as np
 
 from .ptdit_oracle import Grid, _f64, _padded, pad_grid, partition, proxy_grid, region_labels, roll3d, unpartition
 
-__all__ = ["attention_bwd", "window_core", "window_core_bwd", "proxy_pool_bwd", "roll3d_bwd"]
+__all__ = ["attention_bwd", "window_core", "window_core_bwd", "proxy_pool_bwd", "roll3d_bwd", "linear_bwd"]
 
 
 def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, heads: int,
@@ -163,3 +163,14 @@ def roll3d_bwd(g: np.ndarray, shift: Sequence[int]) -> np.ndarray:
     """Gradient of the forward roll: the roll is a permutation, so its
     gradient is the inverse permutation, the roll by +s."""
     return roll3d(_f64(g), shift, inverse=True)
+
+
+def linear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray):
+    """Gradient of ptdit_oracle.linear, Y = X W^T + b (the Q/K/V/O projections
+    of every attention module). x [..., d_in], w [d_out, d_in], dy [..., d_out].
+    Returns dx = dY W [..., d_in], dw = dY^T X [d_out, d_in], db = sum dY [d_out]."""
+    x, w, dy = _f64(x), _f64(w), _f64(dy)
+    x2 = x.reshape(-1, x.shape[-1])
+    dy2 = dy.reshape(-1, dy.shape[-1])
+    dx = (dy2 @ w).reshape(*x.shape[:-1], w.shape[1])
+    return dx, dy2.T @ x2, dy2.sum(axis=0)

@@ -4,8 +4,8 @@ CPU only. The backward oracle (oracle/ptdit_backward.py) is checked against:
   * central finite differences of the (separately pinned) forward oracle, one
     directional derivative per argument, so a wrong sign, a dropped term or a
     transposed operand in any one gradient fails;
-  * torch's autograd through scaled_dot_product_attention in float64 (a library
-    routine with its own backward);
+  * torch's autograd through scaled_dot_product_attention and linear in
+    float64 (library routines with their own backward);
   * closed forms: uniform attention (Q = 0) and the window average's adjoint;
   * adjoint identities <f(x), y> = <x, f^T(y)> for the pooling and the roll,
     and numpy.roll for the roll's inverse.
@@ -152,3 +152,19 @@ def test_roll_bwd_is_the_adjoint_and_numpy_roll():
     rhs = (x * O.roll3d_bwd(y, shift)).sum()
     assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
     np.testing.assert_array_equal(O.roll3d_bwd(y, shift), np.roll(y, shift, axis=(1, 2, 3)))
+
+
+def test_linear_bwd_matches_torch_autograd_and_finite_differences():
+    g = _rng(81)
+    x, w, dy = g.standard_normal((2, 5, 6)), g.standard_normal((4, 6)), g.standard_normal((2, 5, 4))
+    b = g.standard_normal(4)
+    tx, tw, tb = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, w, b))
+    torch.nn.functional.linear(tx, tw, tb).backward(torch.tensor(dy))
+    dx, dw, db = O.linear_bwd(x, w, dy)
+    for mine, ref in ((dx, tx.grad), (dw, tw.grad), (db, tb.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-12, atol=1e-12)
+    loss = lambda x_, w_, b_: float((O.linear(x_, w_, b_) * dy).sum())
+    for i, gr in enumerate((dx, dw, db)):
+        d = g.standard_normal(gr.shape)
+        fd = _fd(loss, (x, w, b), i, d)
+        assert abs(fd - (gr * d).sum()) <= 1e-7 * max(1.0, abs(fd))
