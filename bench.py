@@ -101,7 +101,8 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
     dO V^T, A^T dO, dS K, dS^T Q: 10 * Nq * Nk * d_h per head), against the
     bf16 MFMA peak for bf16 inputs (the matrix-core kernels) and the fp32
     vector peak for fp32 (the vector-ALU kernels), and the HBM bytes (inputs
-    read once, fp32 gradients written once) against 8 TB/s."""
+    read once, fp32 gradients written once) against 8 TB/s. The projection
+    gradients count their two products (dX, dW: 4 * rows * d_in * d_out FLOP)."""
     import torch
     from diffusion_transformer_attention_pt_amd import _lib
 
@@ -120,6 +121,12 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
     dqkv = torch.empty(B, 3, heads, N, dh, device=dev)
     dx = torch.empty(B, N, D, device=dev)
     grid = (B,) + tuple(wl.grid) + (D, heads)
+    xl = torch.randn(B * N, D, device=dev).to(prec)
+    w_o = (torch.randn(D, D, device=dev) * 0.02).to(torch.bfloat16)
+    w_qkv = (torch.randn(3 * D, D, device=dev) * 0.02).to(torch.bfloat16)
+    dy_o = torch.randn(B * N, D, device=dev)
+    dy_qkv = torch.randn(B * N, 3 * D, device=dev)
+    lws = torch.empty(_lib.load().ptdit_linear_bwd_workspace_bytes(B * N, D, 3 * D), dtype=torch.uint8, device=dev)
     cases = {
         "window_bwd": (_lib.K_BWD_WINDOW,
                        lambda: _lib.window_attn_bwd(qkv, do, grid, wl.win, wl.shift, d_qkv=dqkv, d_b_kv=dbkv),
@@ -133,6 +140,14 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
                          10 * B * heads * M * M * dh, 4 * B * M * D * es + 3 * B * M * D * 4),
         "pool_bwd": (_lib.K_BWD_POOL, lambda: _lib.proxy_pool_bwd(dP, grid, wl.p, d_x=dx),
                      0, B * M * D * 4 + B * N * D * 4),
+        # projection gradients (dX, dW, db) of the output map and of the Q/K/V
+        # map of the token rows; d_y fp32 as the core backward produces it
+        "linear_bwd_out": (_lib.K_BWD_LINEAR, lambda: _lib.linear_bwd(xl, w_o, dy_o, ws=lws),
+                           2 * 2 * B * N * D * D, B * N * D * 2 + D * D * 2 + B * N * D * 4 + B * N * D * 4
+                           + D * D * 4),
+        "linear_bwd_qkv": (_lib.K_BWD_LINEAR, lambda: _lib.linear_bwd(xl, w_qkv, dy_qkv, ws=lws),
+                           2 * 2 * B * N * D * 3 * D, B * N * D * 2 + 3 * D * D * 2 + 3 * B * N * D * 4
+                           + B * N * D * 4 + 3 * D * D * 4),
     }
     res = {}
     for name, (cls, fn, flop, nbytes) in cases.items():

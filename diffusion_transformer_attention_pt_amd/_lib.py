@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libptdit.so")
 PTDIT_BF16, PTDIT_F32 = 0, 1
 OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA, OP_MLP = 0, 1, 2, 3, 4
 (K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY, K_GEMM_MLP,
- K_BWD_WINDOW, K_BWD_DENSE, K_BWD_POOL) = range(12)
+ K_BWD_WINDOW, K_BWD_DENSE, K_BWD_POOL, K_BWD_LINEAR) = range(13)
 
 STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT_ERR_DIVISIBILITY",
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",
@@ -30,7 +30,7 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
             "ptdit_trace_disable", "ptdit_window_attn_bwd", "ptdit_attn_bwd", "ptdit_attn_bwd_workspace_bytes",
-            "ptdit_proxy_pool_bwd"]
+            "ptdit_proxy_pool_bwd", "ptdit_linear_bwd", "ptdit_linear_bwd_workspace_bytes"]
 
 
 class Grid(ctypes.Structure):
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
         "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
         "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
         "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
+        "ptdit_linear_bwd": [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "ptdit_linear_bwd_workspace_bytes": [i64, i32, i32],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -98,6 +100,7 @@ def load() -> ctypes.CDLL:
         f.restype = i32
     lib.ptdit_workspace_bytes.restype = sz
     lib.ptdit_attn_bwd_workspace_bytes.restype = sz
+    lib.ptdit_linear_bwd_workspace_bytes.restype = sz
     lib.ptdit_status_str.restype = ctypes.c_char_p
     lib.ptdit_version.restype = ctypes.c_char_p
     lib.ptdit_trace_disable.restype = None
@@ -421,6 +424,25 @@ def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int
     st = lib.ptdit_proxy_pool_bwd(_ptr(d_proxies), Grid(*grid), Win3(*p), _ptr(d_x), int(accumulate), _stream())
     _check("ptdit_proxy_pool_bwd", st)
     return d_x
+
+
+def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: bool = True, want_dw: bool = True,
+               want_db: bool = True, ws: Optional[torch.Tensor] = None):
+    """Gradients of Y = X W^T + b: x [..., d_in], w [d_out, d_in] bf16, d_y [..., d_out].
+    Returns fp32 (d_x or None, d_w or None, d_b or None)."""
+    lib = load()
+    d_in, d_out = x.shape[-1], w.shape[0]
+    rows = x.numel() // d_in
+    dev = x.device
+    dx = torch.empty(*x.shape[:-1], d_in, dtype=torch.float32, device=dev) if want_dx else None
+    dw = torch.empty(d_out, d_in, dtype=torch.float32, device=dev) if want_dw else None
+    db = torch.empty(d_out, dtype=torch.float32, device=dev) if want_db else None
+    need = int(lib.ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out))
+    ws = _ws(need, ws, dev)
+    st = lib.ptdit_linear_bwd(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(d_y), _dt(d_y.dtype),
+                              _ptr(dx), _ptr(dw), _ptr(db), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _check("ptdit_linear_bwd", st)
+    return dx, dw, db
 
 
 def trace_enable(kernel_class: int, capacity: int) -> None:

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libptdit.so")
-SOURCES = ["gemm.hip", "attn.hip", "attn_bwd.hip", "pool.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attn.hip", "attn_bwd.hip", "linear_bwd.hip", "pool.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -584,6 +584,68 @@ ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_wi
   return hip_status(launch_pool_bwd(d, stream));
 }
 
+size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out) {
+  if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return 0;
+  const int splits = wgrad_splits(rows, d_in, d_out);
+  return align_up((size_t)d_in * d_out * 2) + align_up((size_t)splits * d_out * d_in * 4) +
+         align_up((size_t)splits * d_out * 4);
+}
+
+ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
+                              const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
+                              float* d_b, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dt) || !valid_dtype(dy_dt)) return PTDIT_ERR_DTYPE;
+  if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return PTDIT_ERR_SHAPE;
+  if (rows > ((int64_t)1 << 31) / 8 * 8 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
+  if (rows == 0 || (!d_x && !d_w && !d_b)) return PTDIT_OK;
+  if (!d_y || (d_w && !x) || (d_x && !w)) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(d_y) || !aligned16(d_x) || !aligned16(d_w) || !aligned16(d_b) ||
+      !aligned16(ws))
+    return PTDIT_ERR_ALIGN;
+  const size_t need = ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  const size_t xb = (size_t)rows * d_in * esize(x_dt), yb = (size_t)rows * d_out * esize(dy_dt);
+  const size_t wb = (size_t)d_out * d_in * 2;
+  const void* outs[4] = {d_x, d_w, d_b, ws};
+  const size_t osz[4] = {(size_t)rows * d_in * 4, (size_t)d_out * d_in * 4, (size_t)d_out * 4, need};
+  for (int a = 0; a < 4; ++a) {
+    if (overlaps(outs[a], osz[a], x, xb) || overlaps(outs[a], osz[a], d_y, yb) || overlaps(outs[a], osz[a], w, wb))
+      return PTDIT_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], osz[a], outs[b], osz[b])) return PTDIT_ERR_ALIAS;
+  }
+  TraceScope ts(PTDIT_K_BWD_LINEAR, stream);
+  char* wsp = (char*)ws;
+  void* wt = wsp;
+  float* part = (float*)(wsp + align_up((size_t)d_in * d_out * 2));
+  const int splits = wgrad_splits(rows, d_in, d_out);
+  float* dbp = (float*)((char*)part + align_up((size_t)splits * d_out * d_in * 4));
+  if (d_x) {
+    // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight
+    hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
+    if (e != hipSuccess) return PTDIT_ERR_HIP;
+    GemmDesc g;
+    g.A = d_y; g.a_f32 = dy_dt == PTDIT_F32;
+    g.W = wt; g.bias = nullptr;
+    g.R = nullptr; g.r_f32 = 1;
+    g.Y = d_x; g.y_f32 = 1;
+    g.Y2 = nullptr;
+    g.M = rows; g.N = d_in; g.K = d_out;
+    g.head_major = false; g.Ntok = rows; g.heads = 0; g.dh = 0; g.D = d_in;
+    g.act = 0;
+    if (launch_gemm_bf16(g, stream) != hipSuccess) return PTDIT_ERR_HIP;
+  }
+  if (d_w || d_b) {
+    WgradDesc d;
+    d.dy = d_y; d.dy_f32 = dy_dt == PTDIT_F32;
+    d.x = x; d.x_f32 = x_dt == PTDIT_F32;
+    d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
+    d.rows = rows; d.d_in = d_in; d.d_out = d_out; d.splits = splits;
+    if (launch_wgrad(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
+  }
+  return PTDIT_OK;
+}
+
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity) {
   ptdit_trace_disable();
   if (capacity <= 0 || kernel_class < 0) return PTDIT_ERR_SHAPE;

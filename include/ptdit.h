@@ -315,6 +315,27 @@ size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int3
 ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,
                                   int32_t accumulate, hipStream_t stream);
 
+/*
+ * ptdit_linear_bwd -- gradients of a projection Y = X W^T + b (the Q/K/V/O
+ * maps of every attention module; note, code-correspondence module table):
+ * d_x = dY W, d_w = dY^T X, d_b = sum over rows of dY (all fp32, written).
+ *   x     [rows][d_in] device, x_dt (the forward's input of the map)
+ *   w     [d_out][d_in] device, bf16 (the forward's weight)
+ *   d_y   [rows][d_out] device, dy_dt (gradient of the map's output)
+ *   d_x   [rows][d_in] fp32 or NULL (skipped); d_w [d_out][d_in] fp32 or NULL;
+ *   d_b   [d_out] fp32 or NULL
+ *   ws    ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out) bytes
+ * The products run on bf16 matrix cores with fp32 accumulation (fp32 x or
+ * d_y are rounded to bf16 as operands; d_b sums d_y in fp32); the token axis
+ * of d_w is split over workgroups and the parts summed in a fixed order.
+ * d_in, d_out multiples of 8; every pointer 16-byte aligned; outputs overlap
+ * neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS).
+ */
+ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
+                              const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
+                              float* d_b, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out);
+
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
  * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*
  * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments. */
@@ -347,7 +368,8 @@ typedef enum {
   PTDIT_K_GEMM_MLP = 8,      /* both linear maps of the MLP */
   PTDIT_K_BWD_WINDOW = 9,    /* window attention backward */
   PTDIT_K_BWD_DENSE = 10,    /* proxy / cross-attention backward (all three kernels) */
-  PTDIT_K_BWD_POOL = 11      /* window-average backward */
+  PTDIT_K_BWD_POOL = 11,     /* window-average backward */
+  PTDIT_K_BWD_LINEAR = 12    /* projection gradients (all kernels of ptdit_linear_bwd) */
 } ptdit_kernel_class;
 
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity);

@@ -190,6 +190,19 @@ def test_host_validation_rejects_before_launch(lib):
     assert pb(None, g, Win3(1, 4, 4), far, 0, None) == -1
     assert pb(fake, g, Win3(1, 4, 4), ctypes.c_void_p((1 << 20) + 256), 0, None) == -8
     assert pb(None, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 4, 4), None, 0, None) == 0
+    # backward: projections (widths, nulls, workspace, aliasing, nothing wanted)
+    lb = lambda x, rows, di, do_, w_, dy, dx, dw, db, ws, wsb: lib.ptdit_linear_bwd(
+        x, 0, rows, di, do_, w_, dy, 1, dx, dw, db, ws, wsb, None)
+    lws = lib.ptdit_linear_bwd_workspace_bytes(2400, 1152, 1152)
+    assert lws >= 1152 * 1152 * 2 and lib.ptdit_linear_bwd_workspace_bytes(10, 12, 16) == 0
+    o1, o2, o3, o4 = (ctypes.c_void_p(1 << k) for k in (41, 42, 43, 44))
+    assert lb(fake, 2400, 1150, 1152, fake, far, o1, o2, o3, o4, lws) == -2
+    assert lb(fake, 2400, 1152, 1152, fake, None, o1, o2, o3, o4, lws) == -1
+    assert lb(None, 2400, 1152, 1152, fake, far, None, o2, None, o4, lws) == -1      # d_w needs x
+    assert lb(fake, 2400, 1152, 1152, fake, far, o1, o2, o3, o4, 64) == -6
+    assert lb(fake, 2400, 1152, 1152, fake, far, fake, o2, o3, o4, lws) == -8       # d_x over x
+    assert lb(fake, 2400, 1152, 1152, fake, far, o1, o1, o3, o4, lws) == -8         # d_x over d_w
+    assert lb(fake, 2400, 1152, 1152, fake, far, None, None, None, None, 0) == 0     # nothing wanted
     # empty inputs are a successful no-op
     assert lib.ptdit_proxy_pool(None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 2, 2), None, 0, None) == 0
     assert lib.ptdit_window_sa(None, None, 0, Grid(0, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),

@@ -197,3 +197,42 @@ def test_roll_bwd_is_the_inverse_roll(P):
     x = dev(g.standard_normal((2, 360, 64)).astype(np.float32), F32)
     y = P.roll3d(P.roll3d(x, grid, (1, 4, 4)), grid, (1, 4, 4), inverse=True)
     assert torch.equal(x, y)
+
+
+# ----------------------------------------------------------------------------- projections
+
+LIN_CASES = [
+    # rows, d_in, d_out, x dtype, d_y dtype
+    (2400, 1152, 1152, "bf16", "bf16"),
+    (2400, 1152, 1152, "bf16", "f32"),
+    (300, 1152, 3456, "bf16", "bf16"),
+    (1, 8, 16, "bf16", "f32"),
+    (777, 64, 200, "f32", "f32"),
+    (16384, 1152, 1152, "bf16", "f32"),   # the 2048^2 output projection
+]
+
+
+@pytest.mark.parametrize("case", LIN_CASES)
+def test_linear_bwd_vs_oracle(P, case):
+    rows, d_in, d_out, xdt, ydt = case
+    announce(f"linear bwd rows={rows} d_in={d_in} d_out={d_out} x {xdt} dy {ydt}")
+    g = np.random.Generator(np.random.PCG64(700 + rows + d_out))
+    x = g.standard_normal((rows, d_in)).astype(np.float32)
+    w = round_bf16(g.standard_normal((d_out, d_in)).astype(np.float32) * 0.02)
+    dy = g.standard_normal((rows, d_out)).astype(np.float32)
+    if xdt == "bf16":
+        x = round_bf16(x)
+    if ydt == "bf16":
+        dy = round_bf16(dy)
+    dx, dw, db = P.linear_bwd(dev(x, BF16 if xdt == "bf16" else F32), dev(w, BF16),
+                              dev(dy, BF16 if ydt == "bf16" else F32))
+    torch.cuda.synchronize()
+    rx, rw, rb = O.linear_bwd(x, w, dy)
+    # the products take bf16 operands (an fp32 d_y or x is rounded, relative
+    # error 2^-9 per term): d_x sums d_out terms of size |w| ~ 0.02; d_w and d_b
+    # sum `rows` terms of size ~1 and grow as sqrt(rows), so they are compared
+    # after division by sqrt(rows)
+    assert_close(host(dx), rx, "dX")
+    n = np.sqrt(rows)
+    assert_close(host(dw) / n, rw / n, "dW / sqrt(rows)")
+    assert_close(host(db) / n, rb / n, "db / sqrt(rows)")
