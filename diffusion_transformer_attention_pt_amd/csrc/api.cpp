@@ -588,7 +588,7 @@ size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_ou
   if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return 0;
   const int splits = wgrad_splits(rows, d_in, d_out);
   return align_up((size_t)d_in * d_out * 2) + align_up((size_t)splits * d_out * d_in * 4) +
-         align_up((size_t)splits * d_out * 4);
+         align_up((size_t)colsum_splits(rows) * d_out * 4);
 }
 
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
@@ -596,7 +596,7 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(x_dt) || !valid_dtype(dy_dt)) return PTDIT_ERR_DTYPE;
   if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return PTDIT_ERR_SHAPE;
-  if (rows > ((int64_t)1 << 31) / 8 * 8 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
+  if (rows > (int64_t)65535 * 256 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
   if (rows == 0 || (!d_x && !d_w && !d_b)) return PTDIT_OK;
   if (!d_y || (d_w && !x) || (d_x && !w)) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(d_y) || !aligned16(d_x) || !aligned16(d_w) || !aligned16(d_b) ||

@@ -107,13 +107,14 @@ struct WgradDesc {
   const void* dy; int dy_f32;
   const void* x; int x_f32;
   float* part;  // [splits][d_out][d_in] (needed when dw is set)
-  float* dbp;   // [splits][d_out] (needed when db is set)
+  float* dbp;   // [colsum_splits(rows)][d_out] (needed when db is set)
   float* dw;    // [d_out][d_in] or null
   float* db;    // [d_out] or null
   int64_t rows;
   int d_in, d_out, splits;
 };
 int wgrad_splits(int64_t rows, int d_in, int d_out);
+int colsum_splits(int64_t rows);
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s);
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s);
 

@@ -5,10 +5,10 @@
 //   transpose_kernel  W [d_out][d_in] -> W^T [d_in][d_out] (bf16), so dX is
 //                     an ordinary projection (the token-row GEMM kernels)
 //   wgrad_kernel      dW = dY^T X on the matrix cores: 128 x 128 tiles of dW,
-//                     the token axis split over workgroups; 32-token steps of
+//                     the token axis split over workgroups; 64-token steps of
 //                     dY and X are staged transposed ([column][token]) so both
 //                     MFMA operands are contiguous 16-byte LDS reads
-//   colsum_kernel     partial column sums of dY over the same token splits
+//   colsum_kernel     partial column sums of dY over 256-row blocks
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
 #include <hip/hip_runtime.h>
 
@@ -22,7 +22,7 @@ namespace ptdit {
 namespace {
 
 constexpr int LB_NT = 256;
-constexpr int WG_BM = 128, WG_BN = 128, WG_KT = 32, WG_TP = WG_KT + 8;
+constexpr int WG_BM = 128, WG_BN = 128, WG_KT = 64, WG_TP = WG_KT + 8;
 
 // 8 consecutive elements as bf16 (fp32 sources rounded to nearest even)
 __device__ __forceinline__ uint4 ld8_bf16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -71,9 +71,10 @@ struct WgradParams {
 };
 
 // 4 waves in 2 x 2, each a 64 x 64 block of the 128 x 128 tile (4 x 4 MFMA
-// tiles). Threads 0..127 stage dY, 128..255 stage X: one (8-column chunk,
-// 4-token quad) item each, quads fastest; the next step's loads are in flight
-// during the current step's products (two LDS buffers, one barrier a step).
+// tiles, two 32-token halves a step). Threads 0..127 stage dY, 128..255 stage
+// X: two (8-column chunk, 4-token quad) items each, quads fastest; the next
+// step's loads are in flight during the current step's products (two LDS
+// buffers, one barrier a step).
 template <typename TA, typename TB>
 __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t aT[2][WG_BM * WG_TP], bT[2][WG_BN * WG_TP];
@@ -84,17 +85,21 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   const int o0 = tm * WG_BM, i0 = tn * WG_BN;
   const int64_t t_begin = (int64_t)split * p.tch, t_end = min(p.rows, t_begin + p.tch);
   const bool isA = tid < 128;
-  const int it = tid & 127, ch = it >> 3, kq = it & 7;
+  const int it = tid & 127, ch = it >> 3, kq0 = it & 7;
   const int col = (isA ? o0 : i0) + ch * 8, ncols = isA ? p.d_out : p.d_in;
-  uint4 v[4];
+  uint4 v[2][4];
   auto load = [&](int64_t t0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + kq * 4 + j;
-      const bool ok = t < t_end && col < ncols;
-      if (isA) v[j] = ok ? ld8_bf16(reinterpret_cast<const TA*>(p.dy) + t * p.d_out + col) : uint4{0, 0, 0, 0};
-      else v[j] = ok ? ld8_bf16(reinterpret_cast<const TB*>(p.x) + t * p.d_in + col) : uint4{0, 0, 0, 0};
-    }
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + (kq0 + 8 * q) * 4 + j;
+        const bool ok = t < t_end && col < ncols;
+        if (isA)
+          v[q][j] = ok ? ld8_bf16(reinterpret_cast<const TA*>(p.dy) + t * p.d_out + col) : uint4{0, 0, 0, 0};
+        else
+          v[q][j] = ok ? ld8_bf16(reinterpret_cast<const TB*>(p.x) + t * p.d_in + col) : uint4{0, 0, 0, 0};
+      }
   };
   floatx4 acc[4][4];
 #pragma unroll
@@ -104,19 +109,23 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   if (t_begin < t_end) load(t_begin);
   int buf = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += WG_KT, buf ^= 1) {
-    put_quad_cols(isA ? aT[buf] : bT[buf], WG_TP, ch, kq * 4, v);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) put_quad_cols(isA ? aT[buf] : bT[buf], WG_TP, ch, (kq0 + 8 * q) * 4, v[q]);
     __syncthreads();
     if (t0 + WG_KT < t_end) load(t0 + WG_KT);
-    uint4 af[4], bf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      af[j] = *reinterpret_cast<const uint4*>(&aT[buf][(wm * 64 + j * 16 + c) * WG_TP + 8 * g]);
-      bf[j] = *reinterpret_cast<const uint4*>(&bT[buf][(wn * 64 + j * 16 + c) * WG_TP + 8 * g]);
+    for (int kh = 0; kh < 2; ++kh) {
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        af[j] = *reinterpret_cast<const uint4*>(&aT[buf][(wm * 64 + j * 16 + c) * WG_TP + kh * 32 + 8 * g]);
+        bf[j] = *reinterpret_cast<const uint4*>(&bT[buf][(wn * 64 + j * 16 + c) * WG_TP + kh * 32 + 8 * g]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
   }
   // D[m = 4g + r][n = c] of block (a, b): dW[o][i]
   float* out = p.part + (int64_t)split * p.d_out * p.d_in;
@@ -134,13 +143,14 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
     }
 }
 
-// partial column sums of dY over token split blockIdx.y
+// partial column sums of dY over token block blockIdx.y (CS_ROWS rows)
+constexpr int CS_ROWS = 256;
 template <typename TA>
 __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy, float* __restrict__ dbp,
-                                                       int64_t rows, int d_out, int64_t tch) {
+                                                       int64_t rows, int d_out) {
   const int o = blockIdx.x * LB_NT + threadIdx.x;
   if (o >= d_out) return;
-  const int64_t t0 = (int64_t)blockIdx.y * tch, t1 = min(rows, t0 + tch);
+  const int64_t t0 = (int64_t)blockIdx.y * CS_ROWS, t1 = min(rows, t0 + CS_ROWS);
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;  // four chains, combined in a fixed order
   int64_t t = t0;
   for (; t + 4 <= t1; t += 4) {
@@ -155,8 +165,8 @@ __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy
 
 __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ dbp, float* __restrict__ dw,
-                                                             float* __restrict__ db, int splits, int64_t nw,
-                                                             int d_out) {
+                                                             float* __restrict__ db, int splits, int csplits,
+                                                             int64_t nw, int d_out) {
   const int64_t e = (int64_t)blockIdx.x * LB_NT + threadIdx.x;
   if (e < nw && dw) {
     float s = 0.f;
@@ -165,16 +175,18 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
   }
   if (e < d_out && db) {
     float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += dbp[(int64_t)k * d_out + e];
+    for (int k = 0; k < csplits; ++k) s += dbp[(int64_t)k * d_out + e];
     db[e] = s;
   }
 }
 
 // ----------------------------------------------------------------------------
+int colsum_splits(int64_t rows) { return (int)((rows + CS_ROWS - 1) / CS_ROWS); }
+
 int wgrad_splits(int64_t rows, int d_in, int d_out) {
   const int64_t tiles = (int64_t)((d_out + WG_BM - 1) / WG_BM) * ((d_in + WG_BN - 1) / WG_BN);
-  int64_t s = (512 + tiles - 1) / tiles;              // >= 512 workgroups
-  const int64_t most = (rows + 255) / 256;            // >= 256 tokens a split
+  int64_t s = (1024 + tiles - 1) / tiles;             // >= 1024 workgroups
+  const int64_t most = (rows + 511) / 512;            // >= 512 tokens a split
   if (s > most) s = most;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
@@ -206,20 +218,21 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int csplits = colsum_splits(d.rows);
   if (d.db) {
-    const dim3 grid((d.d_out + LB_NT - 1) / LB_NT, splits);
+    const dim3 grid((d.d_out + LB_NT - 1) / LB_NT, csplits);
     if (d.dy_f32)
       hipLaunchKernelGGL((colsum_kernel<float>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
-                         d.dbp, d.rows, d.d_out, tch);
+                         d.dbp, d.rows, d.d_out);
     else
       hipLaunchKernelGGL((colsum_kernel<uint16_t>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const uint16_t*>(d.dy),
-                         d.dbp, d.rows, d.d_out, tch);
+                         d.dbp, d.rows, d.d_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t n = nw > d.d_out ? nw : d.d_out;
   hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s, d.part,
-                     d.dbp, d.dw, d.db, splits, nw, d.d_out);
+                     d.dbp, d.dw, d.db, splits, csplits, nw, d.d_out);
   return hipGetLastError();
 }
 

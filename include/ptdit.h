@@ -328,7 +328,7 @@ ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_wi
  * The products run on bf16 matrix cores with fp32 accumulation (fp32 x or
  * d_y are rounded to bf16 as operands; d_b sums d_y in fp32); the token axis
  * of d_w is split over workgroups and the parts summed in a fixed order.
- * d_in, d_out multiples of 8; every pointer 16-byte aligned; outputs overlap
+ * d_in, d_out multiples of 8, rows <= 65535*256; every pointer 16-byte aligned; outputs overlap
  * neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS).
  */
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
