@@ -32,7 +32,14 @@ __device__ __forceinline__ uint4 ld8_bf16(const float* p) {
   return uint4{pack_bf2(a.x, a.y), pack_bf2(a.z, a.w), pack_bf2(b.x, b.y), pack_bf2(b.z, b.w)};
 }
 
-// t[(8 ch + e) * pitch + s0 + j] = element e of v[j]: one 8-byte write per e
+// Column (token) index of element (row r, column k) in the transposed tiles:
+// 16-byte groups of the row XOR-swizzled by the row's 8-row group, so that
+// writes from 16 consecutive column chunks spread over the banks; reads of 8
+// consecutive tokens stay one aligned 16-byte read.
+__device__ __forceinline__ int swz(int r, int k) { return k ^ (((r >> 3) & 7) << 3); }
+
+// t[(8 ch + e) * pitch + swz(8 ch + e, s0 + j)] = element e of v[j]: one
+// 8-byte write per e (s0 % 4 == 0)
 __device__ __forceinline__ void put_quad_cols(uint16_t* t, int pitch, int ch, int s0, const uint4 (&v)[4]) {
   const uint32_t a0[4] = {v[0].x, v[0].y, v[0].z, v[0].w}, a1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
   const uint32_t a2[4] = {v[2].x, v[2].y, v[2].z, v[2].w}, a3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
@@ -41,7 +48,8 @@ __device__ __forceinline__ void put_quad_cols(uint16_t* t, int pitch, int ch, in
     const int sh = (e & 1) * 16;
     const uint32_t lo = ((a0[e >> 1] >> sh) & 0xffffu) | (((a1[e >> 1] >> sh) & 0xffffu) << 16);
     const uint32_t hi = ((a2[e >> 1] >> sh) & 0xffffu) | (((a3[e >> 1] >> sh) & 0xffffu) << 16);
-    *reinterpret_cast<uint2*>(&t[(ch * 8 + e) * pitch + s0]) = uint2{lo, hi};
+    const int r = ch * 8 + e;
+    *reinterpret_cast<uint2*>(&t[r * pitch + swz(r, s0)]) = uint2{lo, hi};
   }
 }
 
@@ -72,9 +80,10 @@ struct WgradParams {
 
 // 4 waves in 2 x 2, each a 64 x 64 block of the 128 x 128 tile (4 x 4 MFMA
 // tiles, two 32-token halves a step). Threads 0..127 stage dY, 128..255 stage
-// X: two (8-column chunk, 4-token quad) items each, quads fastest; the next
-// step's loads are in flight during the current step's products (two LDS
-// buffers, one barrier a step).
+// X: two (8-column chunk, 4-token quad) items each, chunks fastest (16 lanes
+// read one token row's 16 chunks: coalesced); the next step's loads are in
+// flight during the current step's products (two LDS buffers, one barrier a
+// step).
 template <typename TA, typename TB>
 __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t aT[2][WG_BM * WG_TP], bT[2][WG_BN * WG_TP];
@@ -85,7 +94,7 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   const int o0 = tm * WG_BM, i0 = tn * WG_BN;
   const int64_t t_begin = (int64_t)split * p.tch, t_end = min(p.rows, t_begin + p.tch);
   const bool isA = tid < 128;
-  const int it = tid & 127, ch = it >> 3, kq0 = it & 7;
+  const int it = tid & 127, ch = it & 15, kq0 = it >> 4;
   const int col = (isA ? o0 : i0) + ch * 8, ncols = isA ? p.d_out : p.d_in;
   uint4 v[2][4];
   auto load = [&](int64_t t0) {
@@ -118,8 +127,9 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
       uint4 af[4], bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        af[j] = *reinterpret_cast<const uint4*>(&aT[buf][(wm * 64 + j * 16 + c) * WG_TP + kh * 32 + 8 * g]);
-        bf[j] = *reinterpret_cast<const uint4*>(&bT[buf][(wn * 64 + j * 16 + c) * WG_TP + kh * 32 + 8 * g]);
+        const int ra = wm * 64 + j * 16 + c, rb = wn * 64 + j * 16 + c;
+        af[j] = *reinterpret_cast<const uint4*>(&aT[buf][ra * WG_TP + swz(ra, kh * 32 + 8 * g)]);
+        bf[j] = *reinterpret_cast<const uint4*>(&bT[buf][rb * WG_TP + swz(rb, kh * 32 + 8 * g)]);
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
