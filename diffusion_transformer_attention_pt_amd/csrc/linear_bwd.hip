@@ -22,7 +22,8 @@ namespace ptdit {
 namespace {
 
 constexpr int LB_NT = 256;
-constexpr int WG_BM = 128, WG_BN = 128, WG_KT = 64, WG_TP = WG_KT + 8;
+constexpr int WG_BM = 128, WG_BN = 128, WG_KT = 32, WG_TP = WG_KT + 8;
+constexpr int WG_QPT = WG_KT / 32;  // 4-token quads a staging thread takes per step
 
 // 8 consecutive elements as bf16 (fp32 sources rounded to nearest even)
 __device__ __forceinline__ uint4 ld8_bf16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -32,11 +33,12 @@ __device__ __forceinline__ uint4 ld8_bf16(const float* p) {
   return uint4{pack_bf2(a.x, a.y), pack_bf2(a.z, a.w), pack_bf2(b.x, b.y), pack_bf2(b.z, b.w)};
 }
 
-// Column (token) index of element (row r, column k) in the transposed tiles:
-// 16-byte groups of the row XOR-swizzled by the row's 8-row group, so that
+// Column (token) index of element (row r, column k < WG_KT) in the transposed
+// tiles: 16-byte groups of the row XOR-swizzled by the row's 8-row group
+// (within the WG_KT columns), so that
 // writes from 16 consecutive column chunks spread over the banks; reads of 8
 // consecutive tokens stay one aligned 16-byte read.
-__device__ __forceinline__ int swz(int r, int k) { return k ^ (((r >> 3) & 7) << 3); }
+__device__ __forceinline__ int swz(int r, int k) { return k ^ (((r >> 3) & (WG_KT / 8 - 1)) << 3); }
 
 // t[(8 ch + e) * pitch + swz(8 ch + e, s0 + j)] = element e of v[j]: one
 // 8-byte write per e (s0 % 4 == 0)
@@ -96,10 +98,10 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   const bool isA = tid < 128;
   const int it = tid & 127, ch = it & 15, kq0 = it >> 4;
   const int col = (isA ? o0 : i0) + ch * 8, ncols = isA ? p.d_out : p.d_in;
-  uint4 v[2][4];
+  uint4 v[WG_QPT][4];
   auto load = [&](int64_t t0) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < WG_QPT; ++q)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t t = t0 + (kq0 + 8 * q) * 4 + j;
@@ -119,11 +121,11 @@ __global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
   int buf = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += WG_KT, buf ^= 1) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) put_quad_cols(isA ? aT[buf] : bT[buf], WG_TP, ch, (kq0 + 8 * q) * 4, v[q]);
+    for (int q = 0; q < WG_QPT; ++q) put_quad_cols(isA ? aT[buf] : bT[buf], WG_TP, ch, (kq0 + 8 * q) * 4, v[q]);
     __syncthreads();
     if (t0 + WG_KT < t_end) load(t0 + WG_KT);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < WG_KT / 32; ++kh) {
       uint4 af[4], bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
