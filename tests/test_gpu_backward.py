@@ -1,6 +1,7 @@
-"""GPU parity of the attention-core backward (through the C ABI) against the
-float64 backward oracle (oracle/ptdit_backward.py, itself pinned to finite
-differences, torch autograd and adjoint identities).
+"""GPU parity of the backward pass (through the C ABI) against the float64
+backward oracle (oracle/ptdit_backward.py, itself pinned to finite
+differences, torch autograd and adjoint identities): the attention cores, the
+window average, the roll and the projections' gradients.
 
 Bar: max-abs 2e-2 and relative-L2 1e-2 for every gradient (tests/gpu_util.py);
 the non-accumulating pooling backward is an IEEE division by P and is compared
