@@ -743,8 +743,9 @@ __device__ __forceinline__ void put_quads(const QuadChunks<DH, ROWS>& qc, uint16
 // second look at the keys; then D = sum A dP, dS = A (dP - D) and
 // dQ^T = K^T dS^T with dS^T packed from the registers. Statistics to the
 // workspace.
+constexpr int DQ_NT = 512;  // 8 waves: two waves a SIMD share the staged keys
 template <int DH>
-__global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams p) {
+__global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_kernel(DenseBwdParams p) {
   constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16;
   constexpr int TP = DM_MAXK + 8, MT = DM_MAXK / 16;
   __shared__ __attribute__((aligned(16))) uint16_t kr[DM_MAXK * RP], vr[DM_MAXK * RP], kT[NDT * 16 * TP];
@@ -759,7 +760,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
     // (8-dim chunk, quad of keys), quads fastest, all loads of an item
     // before its writes
     constexpr int CH = NKC * 4, QUADS = DM_MAXK / 4;
-    for (int idx = tid; idx < CH * QUADS; idx += BW_NT) {
+    for (int idx = tid; idx < CH * QUADS; idx += DQ_NT) {
       const int ch = idx / QUADS, kq = idx - ch * QUADS;
       uint4 k4[4], v4[4];
 #pragma unroll
@@ -779,9 +780,9 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   }
   __syncthreads();
   const int ntiles = (p.Nk + 15) / 16;
-  // the staged keys serve p.qtiles tiles of 64 queries
+  // the staged keys serve p.qtiles tiles of 128 queries (16 a wave)
   for (int qt = 0; qt < p.qtiles; ++qt) {
-    const int qi = (blockIdx.x * p.qtiles + qt) * DB_Q + w * 16 + c;
+    const int qi = (blockIdx.x * p.qtiles + qt) * (DQ_NT / 4) + w * 16 + c;
     const bool live = qi < p.Nq;
     uint4 qf[NKC], gf[NKC];
 #pragma unroll
@@ -1021,16 +1022,17 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   p.scale = d.scale;
   constexpr bool BF = sizeof(T) == 2;
   const dim3 gq((d.Nq + DB_Q - 1) / DB_Q, d.heads, d.B), gk((d.Nk + DB_K - 1) / DB_K, d.chunks, d.B * d.heads);
-  // matrix-core query-major kernel: several 64-query tiles a workgroup (the
-  // staged keys serve them all) while that still leaves >= 1024 workgroups
+  // matrix-core query-major kernel: several 128-query tiles a workgroup (the
+  // staged keys serve them all) while that still leaves >= 512 workgroups
   const int64_t bh = (int64_t)d.heads * d.B;
+  constexpr int QT = DQ_NT / 4;  // queries a tile (16 a wave)
   p.qtiles = 1;
-  while (p.qtiles < DM_QT && (int64_t)((d.Nq + 2 * DB_Q * p.qtiles - 1) / (2 * DB_Q * p.qtiles)) * bh >= 1024)
+  while (p.qtiles < DM_QT && (int64_t)((d.Nq + 2 * QT * p.qtiles - 1) / (2 * QT * p.qtiles)) * bh >= 512)
     p.qtiles *= 2;
-  const int qpw = DB_Q * p.qtiles;  // queries a workgroup
+  const int qpw = QT * p.qtiles;  // queries a workgroup
   const dim3 gqm((d.Nq + qpw - 1) / qpw, d.heads, d.B);
   if (BF && d.Nk <= DM_MAXK) {
-    hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gqm, dim3(BW_NT), 0, s, p);
+    hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gqm, dim3(DQ_NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), gq, dim3(BW_NT), 0, s, p);
   }
