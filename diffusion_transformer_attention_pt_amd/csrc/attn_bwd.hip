@@ -881,7 +881,7 @@ __global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
 // dK^T = Q^T dS, dV^T = dO^T A, contraction in the permuted query order of
 // the registers). Every fragment read from LDS feeds KS products.
 template <int DH, int KS>
-__global__ void __launch_bounds__(BW_NT) dense_bwd_kv_mfma_kernel(DenseBwdParams p) {
+__global__ void __launch_bounds__(BW_NT, 2) dense_bwd_kv_mfma_kernel(DenseBwdParams p) {
   constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16, TP = DB_Q + 8;
   __shared__ __attribute__((aligned(16))) uint16_t qr[DB_Q * RP], gr[DB_Q * RP], qT[NDT * 16 * TP],
       gT[NDT * 16 * TP];
