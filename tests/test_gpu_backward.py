@@ -116,6 +116,10 @@ DENSE_CASES = {
     "dh64": (2, 16, 300, 64, 64, "q+kv", "bf16", 1.0),
     "f32": (1, 8, 1500, 96, 72, "q+kv", "f32", 1.0),
     "one_key": (1, 4, 70, 1, 72, "q+kv", "bf16", 1.0),
+    # more than 256 keys: the vector-ALU query-major kernel with the
+    # matrix-core key-major kernel (statistics handed between them)
+    "many_keys": (1, 16, 1100, 600, 72, "q+kv", "bf16", 1.0),
+    "batch2_chunks": (2, 16, 2100, 256, 72, "q+kv", "bf16", 1.0),
 }
 
 
