@@ -586,9 +586,12 @@ ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_wi
 
 size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out) {
   if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return 0;
-  const int splits = wgrad_splits(rows, d_in, d_out);
+  int splits;
+  int64_t tch;
+  wgrad_plan(rows, d_in, d_out, splits, tch);
+  const size_t ld = (size_t)splits * tch;
   return align_up((size_t)d_in * d_out * 2) + align_up((size_t)splits * d_out * d_in * 4) +
-         align_up((size_t)colsum_splits(rows) * d_out * 4);
+         align_up((size_t)colsum_splits(rows) * d_out * 4) + align_up(ld * d_out * 2) + align_up(ld * d_in * 2);
 }
 
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
@@ -596,7 +599,7 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(x_dt) || !valid_dtype(dy_dt)) return PTDIT_ERR_DTYPE;
   if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return PTDIT_ERR_SHAPE;
-  if (rows > (int64_t)65535 * 256 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
+  if (rows > (int64_t)65535 * 32 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
   if (rows == 0 || (!d_x && !d_w && !d_b)) return PTDIT_OK;
   if (!d_y || (d_w && !x) || (d_x && !w)) return PTDIT_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(d_y) || !aligned16(d_x) || !aligned16(d_w) || !aligned16(d_b) ||
@@ -618,8 +621,13 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
   char* wsp = (char*)ws;
   void* wt = wsp;
   float* part = (float*)(wsp + align_up((size_t)d_in * d_out * 2));
-  const int splits = wgrad_splits(rows, d_in, d_out);
+  int splits;
+  int64_t tch;
+  wgrad_plan(rows, d_in, d_out, splits, tch);
+  const size_t ld = (size_t)splits * tch;
   float* dbp = (float*)((char*)part + align_up((size_t)splits * d_out * d_in * 4));
+  uint16_t* dyt = (uint16_t*)((char*)dbp + align_up((size_t)colsum_splits(rows) * d_out * 4));
+  uint16_t* xt = (uint16_t*)((char*)dyt + align_up(ld * d_out * 2));
   if (d_x) {
     // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight
     hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
@@ -639,8 +647,9 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
     WgradDesc d;
     d.dy = d_y; d.dy_f32 = dy_dt == PTDIT_F32;
     d.x = x; d.x_f32 = x_dt == PTDIT_F32;
+    d.dyt = dyt; d.xt = xt;
     d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
-    d.rows = rows; d.d_in = d_in; d.d_out = d_out; d.splits = splits;
+    d.rows = rows; d.d_in = d_in; d.d_out = d_out;
     if (launch_wgrad(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
   }
   return PTDIT_OK;

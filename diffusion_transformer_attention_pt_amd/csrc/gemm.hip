@@ -31,6 +31,11 @@ struct GemmParams {
   int64_t Ntok;
   int heads, dh, D;
   int act;  // 1: GELU after the bias (token-major, no residual)
+  // row strides of A and W (elements; K for dense operands) and, for a
+  // contraction split over blockIdx.y, the per-split offsets of A, W (along
+  // their rows) and Y (elements); splits = gridDim.y. The DMA kernels only.
+  int64_t lda, ldw, ks_a, ks_w, ks_y;
+  int splits;
 };
 
 // XCD-aware tile order: hardware hands block i to XCD (i % 8); re-number so
@@ -325,9 +330,9 @@ struct DmaPlan {
   int dst[MAXI];
 
   __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
-    const int K = p.K;
-    a_base = reinterpret_cast<const char*>(reinterpret_cast<const TA*>(p.A) + m0 * K);
-    w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * K);
+    const int64_t lda = p.lda, ldw = p.ldw, split = blockIdx.y;
+    a_base = reinterpret_cast<const char*>(reinterpret_cast<const TA*>(p.A) + m0 * lda + split * p.ks_a);
+    w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * ldw + split * p.ks_w);
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int j0 = wave + i * NW;
@@ -336,13 +341,13 @@ struct DmaPlan {
       if (j < IA) {
         const int sl = j * 64 + lane, row = sl / CA, pp = sl % CA;
         const int r = m0 + row < p.M ? row : (int)(p.M - 1 - m0);
-        voff[i] = (uint32_t)(((int64_t)r * K + DmaA<TA>::chunk(row, pp) * (16 / (int)sizeof(TA))) *
+        voff[i] = (uint32_t)(((int64_t)r * lda + DmaA<TA>::chunk(row, pp) * (16 / (int)sizeof(TA))) *
                              (int)sizeof(TA));
         dst[i] = j * 64;
       } else {
         const int sl = (j - IA) * 64 + lane, row = sl / 4, pp = sl % 4;
         const int r = n0 + row < p.N ? row : p.N - 1 - n0;
-        voff[i] = (uint32_t)(((int64_t)r * K + (pp ^ ((row >> 1) & 3)) * 8) * 2);
+        voff[i] = (uint32_t)(((int64_t)r * ldw + (pp ^ ((row >> 1) & 3)) * 8) * 2);
         dst[i] = SA + (j - IA) * 64;
       }
     }
@@ -387,7 +392,7 @@ __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4
   constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int BPP = ES::BPP;
-  TY* Y = reinterpret_cast<TY*>(p.Y);
+  TY* Y = reinterpret_cast<TY*>(p.Y) + (int64_t)blockIdx.y * p.ks_y;
   const TR* R = reinterpret_cast<const TR*>(p.R);
   constexpr int E = 16 / (int)sizeof(TY);          // elements per 16-byte chunk
   constexpr int CPRO = BN / E;                     // chunks per staged row
@@ -1015,7 +1020,7 @@ template <typename TA, typename TR, typename TY, int BM, int BN, int WM, int WN,
 static hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * (int64_t)((p.N + BN - 1) / BN);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<TA, TR, TY, BM, BN, WM, WN, S, HM>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_dma_kernel<TA, TR, TY, BM, BN, WM, WN, S, HM>), dim3((unsigned)tiles, (unsigned)p.splits),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -1029,11 +1034,13 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
     // the model width D = 1152 with whole column tiles: residual folded into
     // the main loop (rows past M of a ragged last row tile are clamped)
     if (p.R && p.K == 36 * 32 && p.N % 288 == 0) {
-      hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36>), dim3((unsigned)tiles), dim3(512), 0, s, p);
+      hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(512), 0,
+                         s, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0>), dim3((unsigned)tiles), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(512), 0, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -1046,6 +1053,20 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
 template <typename TA, typename TR, typename TY, bool HM>
 static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   constexpr int STAGES = sizeof(TA) == 2 ? 4 : 3;
+  // strided or split contractions (row strides other than K, splits over
+  // blockIdx.y) go to the DMA kernels only
+  if (p.lda != p.K || p.ldw != p.K || p.splits != 1) {
+    const int64_t ld = p.lda > p.ldw ? p.lda : p.ldw;
+    if (p.K % 32 != 0 || p.K / 32 < STAGES || (int64_t)288 * ld * (int64_t)sizeof(TA) >= (int64_t)1 << 31 ||
+        p.splits < 1 || p.splits > 65535)
+      return hipErrorInvalidValue;
+    if constexpr (sizeof(TA) == 2) {
+      if (p.M >= 2048 && p.K % 128 == 0 && p.K >= 256 && !p.R) return run_pp<TR, TY, HM>(p, s);
+    }
+    if (p.M >= 1024) return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
+    if (p.K / 32 < 4) return hipErrorInvalidValue;
+    return run_dma<TA, TR, TY, 32, 64, 2, 2, 4, HM>(p, s);
+  }
   // the DMA kernels address a tile's A / W rows with 32-bit byte offsets
   const bool off32 = (int64_t)288 * p.K * (int64_t)sizeof(TA) < (int64_t)1 << 31;
   if (!off32) return p.M >= 1024 ? run_bf16<TA, TR, TY, 128, 128, 2, 2, HM>(p, s)
@@ -1085,6 +1106,10 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.Ntok = d.Ntok > 0 ? d.Ntok : 1;
   p.heads = d.heads; p.dh = d.dh; p.D = d.D;
   p.act = d.act;
+  p.lda = d.lda > 0 ? d.lda : d.K;
+  p.ldw = d.ldw > 0 ? d.ldw : d.K;
+  p.ks_a = d.ks_a; p.ks_w = d.ks_w; p.ks_y = d.ks_y;
+  p.splits = d.splits > 0 ? d.splits : 1;
   if (d.a_f32) {
     if (d.y_f32) return pick_r<float, float>(d, p, s);
     return pick_r<float, uint16_t>(d, p, s);
@@ -1094,6 +1119,7 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
 }
 
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s) {
+  if (d.lda > 0 || d.ldw > 0 || d.splits > 1) return hipErrorInvalidValue;  // dense operands only
   GemmF32Params p;
   p.A = reinterpret_cast<const float*>(d.A);
   p.W = reinterpret_cast<const float*>(d.W);

@@ -19,6 +19,11 @@ struct GemmDesc {
   int64_t M; int N; int K;
   int head_major; int64_t Ntok; int heads; int dh; int D;
   int act = 0;  // 1: GELU (tanh form) after the bias; token-major output without residual only
+  // strided / split contraction (bf16 DMA kernels only): row strides of A and
+  // W (0: K), and splits over blockIdx.y with per-split element offsets of
+  // A, W (along their rows) and Y
+  int64_t lda = 0, ldw = 0, ks_a = 0, ks_w = 0, ks_y = 0;
+  int splits = 1;
 };
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32
@@ -106,14 +111,16 @@ hipError_t launch_pool_bwd(const PoolBwdDesc& d, hipStream_t s);
 struct WgradDesc {
   const void* dy; int dy_f32;
   const void* x; int x_f32;
+  uint16_t* dyt;  // [d_out][ld] bf16 (ld = splits * tch of wgrad_plan; needed when dw is set)
+  uint16_t* xt;   // [d_in][ld] bf16 (needed when dw is set)
   float* part;  // [splits][d_out][d_in] (needed when dw is set)
   float* dbp;   // [colsum_splits(rows)][d_out] (needed when db is set)
   float* dw;    // [d_out][d_in] or null
   float* db;    // [d_out] or null
   int64_t rows;
-  int d_in, d_out, splits;
+  int d_in, d_out;
 };
-int wgrad_splits(int64_t rows, int d_in, int d_out);
+void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch);
 int colsum_splits(int64_t rows);
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s);
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s);

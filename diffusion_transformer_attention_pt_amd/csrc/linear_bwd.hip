@@ -4,10 +4,11 @@
 //
 //   transpose_kernel  W [d_out][d_in] -> W^T [d_in][d_out] (bf16), so dX is
 //                     an ordinary projection (the token-row GEMM kernels)
-//   wgrad_kernel      dW = dY^T X on the matrix cores: 128 x 128 tiles of dW,
-//                     the token axis split over workgroups; 64-token steps of
-//                     dY and X are staged transposed ([column][token]) so both
-//                     MFMA operands are contiguous 16-byte LDS reads
+//   transpose_pad_kernel  dY and X to token-contiguous bf16 [column][token]
+//                     (zero past the last token), so dW = dY^T X is an ordinary
+//                     contraction over the token axis on the DMA GEMM kernels
+//                     (those of the token-row projections), the token axis
+//                     split over blockIdx.y into partials
 //   colsum_kernel     partial column sums of dY over 256-row blocks
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
 #include <hip/hip_runtime.h>
@@ -22,38 +23,6 @@ namespace ptdit {
 namespace {
 
 constexpr int LB_NT = 256;
-constexpr int WG_BM = 128, WG_BN = 128, WG_KT = 32, WG_TP = WG_KT + 8;
-constexpr int WG_QPT = WG_KT / 32;  // 4-token quads a staging thread takes per step
-
-// 8 consecutive elements as bf16 (fp32 sources rounded to nearest even)
-__device__ __forceinline__ uint4 ld8_bf16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint4 ld8_bf16(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  return uint4{pack_bf2(a.x, a.y), pack_bf2(a.z, a.w), pack_bf2(b.x, b.y), pack_bf2(b.z, b.w)};
-}
-
-// Column (token) index of element (row r, column k < WG_KT) in the transposed
-// tiles: 16-byte groups of the row XOR-swizzled by the row's 8-row group
-// (within the WG_KT columns), so that
-// writes from 16 consecutive column chunks spread over the banks; reads of 8
-// consecutive tokens stay one aligned 16-byte read.
-__device__ __forceinline__ int swz(int r, int k) { return k ^ (((r >> 3) & (WG_KT / 8 - 1)) << 3); }
-
-// t[(8 ch + e) * pitch + swz(8 ch + e, s0 + j)] = element e of v[j]: one
-// 8-byte write per e (s0 % 4 == 0)
-__device__ __forceinline__ void put_quad_cols(uint16_t* t, int pitch, int ch, int s0, const uint4 (&v)[4]) {
-  const uint32_t a0[4] = {v[0].x, v[0].y, v[0].z, v[0].w}, a1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-  const uint32_t a2[4] = {v[2].x, v[2].y, v[2].z, v[2].w}, a3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int sh = (e & 1) * 16;
-    const uint32_t lo = ((a0[e >> 1] >> sh) & 0xffffu) | (((a1[e >> 1] >> sh) & 0xffffu) << 16);
-    const uint32_t hi = ((a2[e >> 1] >> sh) & 0xffffu) | (((a3[e >> 1] >> sh) & 0xffffu) << 16);
-    const int r = ch * 8 + e;
-    *reinterpret_cast<uint2*>(&t[r * pitch + swz(r, s0)]) = uint2{lo, hi};
-  }
-}
 
 }  // namespace
 
@@ -70,89 +39,23 @@ __global__ void __launch_bounds__(LB_NT) transpose_kernel(const uint16_t* __rest
     if (c0 + c < cols && r0 + tx < rows) wt[(int64_t)(c0 + c) * rows + r0 + tx] = tile[tx][c];
 }
 
-// ----------------------------------------------------------------------------
-struct WgradParams {
-  const void* dy;
-  const void* x;
-  float* part;    // [splits][d_out][d_in]
-  int64_t rows;
-  int d_in, d_out;
-  int64_t tch;    // tokens per split (a multiple of WG_KT)
-};
-
-// 4 waves in 2 x 2, each a 64 x 64 block of the 128 x 128 tile (4 x 4 MFMA
-// tiles, two 32-token halves a step). Threads 0..127 stage dY, 128..255 stage
-// X: two (8-column chunk, 4-token quad) items each, chunks fastest (16 lanes
-// read one token row's 16 chunks: coalesced); the next step's loads are in
-// flight during the current step's products (two LDS buffers, one barrier a
-// step).
-template <typename TA, typename TB>
-__global__ void __launch_bounds__(LB_NT) wgrad_kernel(WgradParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t aT[2][WG_BM * WG_TP], bT[2][WG_BN * WG_TP];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int wm = w & 1, wn = w >> 1;
-  const int tiles_n = (p.d_in + WG_BN - 1) / WG_BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n, split = blockIdx.y;
-  const int o0 = tm * WG_BM, i0 = tn * WG_BN;
-  const int64_t t_begin = (int64_t)split * p.tch, t_end = min(p.rows, t_begin + p.tch);
-  const bool isA = tid < 128;
-  const int it = tid & 127, ch = it & 15, kq0 = it >> 4;
-  const int col = (isA ? o0 : i0) + ch * 8, ncols = isA ? p.d_out : p.d_in;
-  uint4 v[WG_QPT][4];
-  auto load = [&](int64_t t0) {
-#pragma unroll
-    for (int q = 0; q < WG_QPT; ++q)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + (kq0 + 8 * q) * 4 + j;
-        const bool ok = t < t_end && col < ncols;
-        if (isA)
-          v[q][j] = ok ? ld8_bf16(reinterpret_cast<const TA*>(p.dy) + t * p.d_out + col) : uint4{0, 0, 0, 0};
-        else
-          v[q][j] = ok ? ld8_bf16(reinterpret_cast<const TB*>(p.x) + t * p.d_in + col) : uint4{0, 0, 0, 0};
-      }
-  };
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
-  if (t_begin < t_end) load(t_begin);
-  int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += WG_KT, buf ^= 1) {
-#pragma unroll
-    for (int q = 0; q < WG_QPT; ++q) put_quad_cols(isA ? aT[buf] : bT[buf], WG_TP, ch, (kq0 + 8 * q) * 4, v[q]);
-    __syncthreads();
-    if (t0 + WG_KT < t_end) load(t0 + WG_KT);
-#pragma unroll
-    for (int kh = 0; kh < WG_KT / 32; ++kh) {
-      uint4 af[4], bf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ra = wm * 64 + j * 16 + c, rb = wn * 64 + j * 16 + c;
-        af[j] = *reinterpret_cast<const uint4*>(&aT[buf][ra * WG_TP + swz(ra, kh * 32 + 8 * g)]);
-        bf[j] = *reinterpret_cast<const uint4*>(&bT[buf][rb * WG_TP + swz(rb, kh * 32 + 8 * g)]);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
-    }
+// src [rows][cols] (bf16 or fp32) -> dst [cols][ld] bf16, columns rows .. ld-1
+// of dst zero (ld % 32 == 0): the token-contiguous operands of dW = dY^T X
+template <typename T>
+__global__ void __launch_bounds__(LB_NT) transpose_pad_kernel(const T* __restrict__ src, uint16_t* __restrict__ dst,
+                                                              int64_t rows, int cols, int64_t ld) {
+  __shared__ uint16_t tile[32][33];
+  const int c0 = blockIdx.y * 32;
+  const int64_t r0 = (int64_t)blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    float v = 0.f;
+    if (r0 + r < rows && c0 + tx < cols) v = ld1(src + (r0 + r) * cols + c0 + tx);
+    tile[r][tx] = (uint16_t)(pack_bf2(v, 0.f) & 0xffffu);
   }
-  // D[m = 4g + r][n = c] of block (a, b): dW[o][i]
-  float* out = p.part + (int64_t)split * p.d_out * p.d_in;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = i0 + wn * 64 + b * 16 + c;
-      if (i >= p.d_in) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int o = o0 + wm * 64 + a * 16 + 4 * g + r;
-        if (o < p.d_out) out[(int64_t)o * p.d_in + i] = acc[a][b][r];
-      }
-    }
+  __syncthreads();
+  for (int c = ty; c < 32; c += 8)
+    if (c0 + c < cols) dst[(int64_t)(c0 + c) * ld + r0 + tx] = tile[tx][c];
 }
 
 // partial column sums of dY over token block blockIdx.y (CS_ROWS rows)
@@ -195,14 +98,17 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
 // ----------------------------------------------------------------------------
 int colsum_splits(int64_t rows) { return (int)((rows + CS_ROWS - 1) / CS_ROWS); }
 
-int wgrad_splits(int64_t rows, int d_in, int d_out) {
-  const int64_t tiles = (int64_t)((d_out + WG_BM - 1) / WG_BM) * ((d_in + WG_BN - 1) / WG_BN);
-  int64_t s = (1024 + tiles - 1) / tiles;             // >= 1024 workgroups
-  const int64_t most = (rows + 511) / 512;            // >= 512 tokens a split
-  if (s > most) s = most;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return (int)s;
+void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch) {
+  // the DMA GEMM's tile for M = d_out rows of dW: 256 x 288 from 1024 rows,
+  // 32 x 64 below; about one workgroup per CU in total
+  const int64_t tiles = d_out >= 1024 ? (int64_t)((d_out + 255) / 256) * ((d_in + 287) / 288)
+                                      : (int64_t)((d_out + 31) / 32) * ((d_in + 63) / 64);
+  int64_t sp = 256 / tiles;
+  if (sp < 1) sp = 1;
+  tch = (rows + sp - 1) / sp;
+  tch = (tch + 127) / 128 * 128;  // whole 128-token k-slices (the ping-pong kernel's unit)
+  if (tch < 256) tch = 256;
+  splits = (int)((rows + tch - 1) / tch);
 }
 
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s) {
@@ -214,20 +120,39 @@ hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hi
 
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
-  const int splits = d.splits;
-  int64_t tch = (d.rows + splits - 1) / splits;
-  tch = (tch + WG_KT - 1) / WG_KT * WG_KT;
-  const int64_t nw = (int64_t)d.d_out * d.d_in;
+  int splits;
+  int64_t tch;
+  wgrad_plan(d.rows, d.d_in, d.d_out, splits, tch);
+  const int64_t ld = splits * tch, nw = (int64_t)d.d_out * d.d_in;
   if (d.dw) {
-    WgradParams p;
-    p.dy = d.dy; p.x = d.x; p.part = d.part; p.rows = d.rows; p.d_in = d.d_in; p.d_out = d.d_out; p.tch = tch;
-    const int tiles = ((d.d_out + WG_BM - 1) / WG_BM) * ((d.d_in + WG_BN - 1) / WG_BN);
-    const dim3 grid(tiles, splits);
-    if (d.dy_f32 && d.x_f32) hipLaunchKernelGGL((wgrad_kernel<float, float>), grid, dim3(LB_NT), 0, s, p);
-    else if (d.dy_f32) hipLaunchKernelGGL((wgrad_kernel<float, uint16_t>), grid, dim3(LB_NT), 0, s, p);
-    else if (d.x_f32) hipLaunchKernelGGL((wgrad_kernel<uint16_t, float>), grid, dim3(LB_NT), 0, s, p);
-    else hipLaunchKernelGGL((wgrad_kernel<uint16_t, uint16_t>), grid, dim3(LB_NT), 0, s, p);
+    // dY^T [d_out][ld] and X^T [d_in][ld] (bf16, zero past rows), then
+    // dW = dY^T (X^T)^T on the DMA GEMM kernels with the token axis as K,
+    // split over blockIdx.y into partials [splits][d_out][d_in]
+    const dim3 gy((unsigned)(ld / 32), (unsigned)((d.d_out + 31) / 32)), gx((unsigned)(ld / 32), (unsigned)((d.d_in + 31) / 32));
+    if (d.dy_f32)
+      hipLaunchKernelGGL((transpose_pad_kernel<float>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
+                         d.dyt, d.rows, d.d_out, ld);
+    else
+      hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gy, dim3(LB_NT), 0, s,
+                         reinterpret_cast<const uint16_t*>(d.dy), d.dyt, d.rows, d.d_out, ld);
+    if (d.x_f32)
+      hipLaunchKernelGGL((transpose_pad_kernel<float>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.x),
+                         d.xt, d.rows, d.d_in, ld);
+    else
+      hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gx, dim3(LB_NT), 0, s,
+                         reinterpret_cast<const uint16_t*>(d.x), d.xt, d.rows, d.d_in, ld);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmDesc g;
+    g.A = d.dyt; g.a_f32 = 0;
+    g.W = d.xt; g.bias = nullptr;
+    g.R = nullptr; g.r_f32 = 1;
+    g.Y = d.part; g.y_f32 = 1;
+    g.Y2 = nullptr;
+    g.M = d.d_out; g.N = d.d_in; g.K = (int)tch;
+    g.head_major = 0; g.Ntok = d.d_out; g.heads = 0; g.dh = 0; g.D = d.d_in;
+    g.lda = ld; g.ldw = ld; g.ks_a = tch; g.ks_w = tch; g.ks_y = nw; g.splits = splits;
+    e = launch_gemm_bf16(g, s);
     if (e != hipSuccess) return e;
   }
   const int csplits = colsum_splits(d.rows);

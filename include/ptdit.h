@@ -326,9 +326,11 @@ ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_wi
  *   d_b   [d_out] fp32 or NULL
  *   ws    ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out) bytes
  * The products run on bf16 matrix cores with fp32 accumulation (fp32 x or
- * d_y are rounded to bf16 as operands; d_b sums d_y in fp32); the token axis
- * of d_w is split over workgroups and the parts summed in a fixed order.
- * d_in, d_out multiples of 8, rows <= 65535*256; every pointer 16-byte aligned; outputs overlap
+ * d_y are rounded to bf16 as operands; d_b sums d_y in fp32): d_x on the
+ * projection kernels with a transposed copy of w, d_w on the same kernels
+ * with token-contiguous (transposed) copies of d_y and x, the token axis
+ * split over workgroups and the parts summed in a fixed order.
+ * d_in, d_out multiples of 8, rows <= 65535*32; every pointer 16-byte aligned; outputs overlap
  * neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS).
  */
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
