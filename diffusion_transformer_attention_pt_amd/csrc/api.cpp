@@ -591,7 +591,8 @@ size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_ou
   wgrad_plan(rows, d_in, d_out, splits, tch);
   const size_t ld = (size_t)splits * tch;
   return align_up((size_t)d_in * d_out * 2) + align_up((size_t)splits * d_out * d_in * 4) +
-         align_up((size_t)colsum_splits(rows) * d_out * 4) + align_up(ld * d_out * 2) + align_up(ld * d_in * 2);
+         align_up((size_t)colsum_splits(rows) * d_out * 4) + align_up(ld * d_out * 2) + align_up(ld * d_in * 2) +
+         align_up((size_t)rows * d_out * 2);
 }
 
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
@@ -628,12 +629,22 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
   float* dbp = (float*)((char*)part + align_up((size_t)splits * d_out * d_in * 4));
   uint16_t* dyt = (uint16_t*)((char*)dbp + align_up((size_t)colsum_splits(rows) * d_out * 4));
   uint16_t* xt = (uint16_t*)((char*)dyt + align_up(ld * d_out * 2));
+  uint16_t* dyb = (uint16_t*)((char*)xt + align_up(ld * d_in * 2));
+  WgradDesc d;
+  d.dy = d_y; d.dy_f32 = dy_dt == PTDIT_F32;
+  d.x = x; d.x_f32 = x_dt == PTDIT_F32;
+  d.dyt = dyt; d.xt = xt;
+  // with d_w, the transpose pass also leaves a bf16 copy of an fp32 d_y for d_x
+  d.dyb = (d_x && d_w && dy_dt == PTDIT_F32) ? dyb : nullptr;
+  d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
+  d.rows = rows; d.d_in = d_in; d.d_out = d_out;
+  if (d_w && launch_wgrad_operands(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
   if (d_x) {
     // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight
     hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
     if (e != hipSuccess) return PTDIT_ERR_HIP;
     GemmDesc g;
-    g.A = d_y; g.a_f32 = dy_dt == PTDIT_F32;
+    g.A = d.dyb ? (const void*)d.dyb : d_y; g.a_f32 = !d.dyb && dy_dt == PTDIT_F32;
     g.W = wt; g.bias = nullptr;
     g.R = nullptr; g.r_f32 = 1;
     g.Y = d_x; g.y_f32 = 1;
@@ -643,15 +654,7 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
     g.act = 0;
     if (launch_gemm_bf16(g, stream) != hipSuccess) return PTDIT_ERR_HIP;
   }
-  if (d_w || d_b) {
-    WgradDesc d;
-    d.dy = d_y; d.dy_f32 = dy_dt == PTDIT_F32;
-    d.x = x; d.x_f32 = x_dt == PTDIT_F32;
-    d.dyt = dyt; d.xt = xt;
-    d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
-    d.rows = rows; d.d_in = d_in; d.d_out = d_out;
-    if (launch_wgrad(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
-  }
+  if ((d_w || d_b) && launch_wgrad(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
   return PTDIT_OK;
 }
 

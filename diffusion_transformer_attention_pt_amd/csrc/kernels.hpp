@@ -113,6 +113,7 @@ struct WgradDesc {
   const void* x; int x_f32;
   uint16_t* dyt;  // [d_out][ld] bf16 (ld = splits * tch of wgrad_plan; needed when dw is set)
   uint16_t* xt;   // [d_in][ld] bf16 (needed when dw is set)
+  uint16_t* dyb;  // optional row-major bf16 copy of dY [rows][d_out], written with dyt
   float* part;  // [splits][d_out][d_in] (needed when dw is set)
   float* dbp;   // [colsum_splits(rows)][d_out] (needed when db is set)
   float* dw;    // [d_out][d_in] or null
@@ -123,6 +124,7 @@ struct WgradDesc {
 void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch);
 int colsum_splits(int64_t rows);
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s);
-hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s);
+hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s);  // the transposed copies (and dyb)
+hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s);           // then dW from them, and db
 
 }  // namespace ptdit

@@ -39,23 +39,52 @@ __global__ void __launch_bounds__(LB_NT) transpose_kernel(const uint16_t* __rest
     if (c0 + c < cols && r0 + tx < rows) wt[(int64_t)(c0 + c) * rows + r0 + tx] = tile[tx][c];
 }
 
-// src [rows][cols] (bf16 or fp32) -> dst [cols][ld] bf16, columns rows .. ld-1
-// of dst zero (ld % 32 == 0): the token-contiguous operands of dW = dY^T X
+// src [rows][cols] (bf16 or fp32) -> dst [cols][ld] bf16 (columns rows ..
+// ld-1 zero; ld % 64 == 0), and optionally a row-major bf16 copy [rows][cols]:
+// the token-contiguous operands of dW = dY^T X (and the bf16 A operand of
+// dX = dY W). 64 x 64 tiles: 16 lanes read one row's 64 columns (4 each), the
+// transposed writes are 8 consecutive tokens (16 bytes) of one column.
+constexpr int TPD = 64, TPP = TPD + 2;  // tile, LDS pitch (elements)
+__device__ __forceinline__ void ld4f(const float* p, float (&v)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void ld4f(const uint16_t* p, float (&v)[4]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(a.x << 16); v[1] = __uint_as_float(a.x & 0xffff0000u);
+  v[2] = __uint_as_float(a.y << 16); v[3] = __uint_as_float(a.y & 0xffff0000u);
+}
 template <typename T>
 __global__ void __launch_bounds__(LB_NT) transpose_pad_kernel(const T* __restrict__ src, uint16_t* __restrict__ dst,
-                                                              int64_t rows, int cols, int64_t ld) {
-  __shared__ uint16_t tile[32][33];
-  const int c0 = blockIdx.y * 32;
-  const int64_t r0 = (int64_t)blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int r = ty; r < 32; r += 8) {
-    float v = 0.f;
-    if (r0 + r < rows && c0 + tx < cols) v = ld1(src + (r0 + r) * cols + c0 + tx);
-    tile[r][tx] = (uint16_t)(pack_bf2(v, 0.f) & 0xffffu);
+                                                              uint16_t* __restrict__ copy, int64_t rows, int cols,
+                                                              int64_t ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TPD * TPP];
+  const int64_t r0 = (int64_t)blockIdx.x * TPD;
+  const int c0 = blockIdx.y * TPD;
+  const int tid = threadIdx.x, lc = (tid & 15) * 4, lr = tid >> 4;  // 16 lanes a row
+#pragma unroll
+  for (int i = 0; i < TPD / 16; ++i) {
+    const int r = lr + 16 * i;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool ok = r0 + r < rows && c0 + lc < cols;  // cols % 4 == 0: a group is in or out
+    if (ok) ld4f(src + (r0 + r) * cols + c0 + lc, v);
+    const uint32_t p0 = pack_bf2(v[0], v[1]), p1 = pack_bf2(v[2], v[3]);
+    *reinterpret_cast<uint32_t*>(&tile[r * TPP + lc]) = p0;
+    *reinterpret_cast<uint32_t*>(&tile[r * TPP + lc + 2]) = p1;
+    if (copy && ok) *reinterpret_cast<uint2*>(copy + (r0 + r) * cols + c0 + lc) = uint2{p0, p1};
   }
   __syncthreads();
-  for (int c = ty; c < 32; c += 8)
-    if (c0 + c < cols) dst[(int64_t)(c0 + c) * ld + r0 + tx] = tile[tx][c];
+  // 64 columns x 8 token groups = 512 writes of 16 bytes, two a thread
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int item = tid + i * LB_NT, c = item >> 3, tg = item & 7;
+    if (c0 + c >= cols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)tile[(tg * 8 + 2 * j) * TPP + c] | ((uint32_t)tile[(tg * 8 + 2 * j + 1) * TPP + c] << 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ld + r0 + tg * 8) = uint4{w[0], w[1], w[2], w[3]};
+  }
 }
 
 // partial column sums of dY over token block blockIdx.y (CS_ROWS rows)
@@ -118,6 +147,29 @@ hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hi
   return hipGetLastError();
 }
 
+hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s) {
+  if (d.rows == 0 || !d.dw) return hipSuccess;
+  int splits;
+  int64_t tch;
+  wgrad_plan(d.rows, d.d_in, d.d_out, splits, tch);
+  const int64_t ld = splits * tch;
+  const dim3 gy((unsigned)(ld / TPD), (unsigned)((d.d_out + TPD - 1) / TPD)),
+      gx((unsigned)(ld / TPD), (unsigned)((d.d_in + TPD - 1) / TPD));
+  if (d.dy_f32)
+    hipLaunchKernelGGL((transpose_pad_kernel<float>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
+                       d.dyt, d.dyb, d.rows, d.d_out, ld);
+  else
+    hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const uint16_t*>(d.dy),
+                       d.dyt, d.dyb, d.rows, d.d_out, ld);
+  if (d.x_f32)
+    hipLaunchKernelGGL((transpose_pad_kernel<float>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.x),
+                       d.xt, nullptr, d.rows, d.d_in, ld);
+  else
+    hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const uint16_t*>(d.x),
+                       d.xt, nullptr, d.rows, d.d_in, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
   int splits;
@@ -128,21 +180,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     // dY^T [d_out][ld] and X^T [d_in][ld] (bf16, zero past rows), then
     // dW = dY^T (X^T)^T on the DMA GEMM kernels with the token axis as K,
     // split over blockIdx.y into partials [splits][d_out][d_in]
-    const dim3 gy((unsigned)(ld / 32), (unsigned)((d.d_out + 31) / 32)), gx((unsigned)(ld / 32), (unsigned)((d.d_in + 31) / 32));
-    if (d.dy_f32)
-      hipLaunchKernelGGL((transpose_pad_kernel<float>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
-                         d.dyt, d.rows, d.d_out, ld);
-    else
-      hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gy, dim3(LB_NT), 0, s,
-                         reinterpret_cast<const uint16_t*>(d.dy), d.dyt, d.rows, d.d_out, ld);
-    if (d.x_f32)
-      hipLaunchKernelGGL((transpose_pad_kernel<float>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.x),
-                         d.xt, d.rows, d.d_in, ld);
-    else
-      hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gx, dim3(LB_NT), 0, s,
-                         reinterpret_cast<const uint16_t*>(d.x), d.xt, d.rows, d.d_in, ld);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the transposed copies were written by launch_wgrad_operands
     GemmDesc g;
     g.A = d.dyt; g.a_f32 = 0;
     g.W = d.xt; g.bias = nullptr;
@@ -152,7 +190,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     g.M = d.d_out; g.N = d.d_in; g.K = (int)tch;
     g.head_major = 0; g.Ntok = d.d_out; g.heads = 0; g.dh = 0; g.D = d.d_in;
     g.lda = ld; g.ldw = ld; g.ks_a = tch; g.ks_w = tch; g.ks_y = nw; g.splits = splits;
-    e = launch_gemm_bf16(g, s);
+    const hipError_t e = launch_gemm_bf16(g, s);
     if (e != hipSuccess) return e;
   }
   const int csplits = colsum_splits(d.rows);
