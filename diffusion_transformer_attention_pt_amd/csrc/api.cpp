@@ -569,7 +569,8 @@ ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_wi
   if (p.t <= 0 || p.h <= 0 || p.w <= 0) return PTDIT_ERR_SHAPE;
   if (g.F % p.t || g.H % p.h || g.W % p.w) return PTDIT_ERR_DIVISIBILITY;
   const int64_t N = (int64_t)g.F * g.H * g.W;
-  if (N > (int64_t)1 << 30 || (int64_t)g.B * N * (g.D / 4) > (int64_t)INT32_MAX * 256) return PTDIT_ERR_SHAPE;
+  // the kernel takes eight token rows per workgroup (a 32-bit grid)
+  if (N > (int64_t)1 << 30 || (int64_t)g.B * N > (int64_t)INT32_MAX) return PTDIT_ERR_SHAPE;
   if ((int64_t)g.B * N == 0) return PTDIT_OK;
   if (!d_proxies || !d_x) return PTDIT_ERR_NULL;
   if (!aligned16(d_proxies) || !aligned16(d_x)) return PTDIT_ERR_ALIGN;

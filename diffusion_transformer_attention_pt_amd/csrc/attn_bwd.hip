@@ -270,17 +270,35 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
 //    A^T and dS^T go to LDS as [key][query].
 //  phase 2, wave w owns keys 16w..16w+15: dV^T = dO^T A and dK^T = Q^T dS, the
 //    contraction over the 64 queries read from the transposed LDS copies.
+// LDS (54 KB at d_h = 72, so three workgroups share a CU): the transposed
+// copies hold the DH real rows only, back to back; a 16-row dim tile that
+// runs past DH reads the next copy's (or the K/V region's) first rows, whose
+// products land in output rows >= DH, which are never stored. A^T and dS^T
+// reuse the row-major K, V region once every wave's S^T, dP^T products have
+// read it.
 template <int DH>
 __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams p) {
+  static_assert(DH % 8 == 0, "head width a multiple of 8");
   constexpr int KEYS = 64;
-  constexpr int NKC = (DH + 31) / 32;  // 32-wide chunks of the head dim (rows padded with zeros)
-  constexpr int RP = NKC * 32 + 8;     // row pitch (elements) of the row-major K, V copies
+  constexpr int NKC = (DH + 31) / 32;  // 32-wide chunks of the head dim (dims past DH read as zero)
+  // row pitch (elements) of the row-major K, V copies: an odd number of
+  // 16-byte chunks, so the 16 rows of a fragment read start in distinct banks
+  constexpr int RP = 8 * (DH / 8 + ((DH / 8) % 2 == 0 ? 1 : 2));
   constexpr int NDT = (DH + 15) / 16;  // 16-row tiles of the transposed copies / outputs
   constexpr int TP = KEYS + 8;         // row pitch of the transposed copies
-  __shared__ __attribute__((aligned(16))) uint16_t kr[KEYS * RP], vr[KEYS * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t kT[NDT * 16 * TP], qT[NDT * 16 * TP], gT[NDT * 16 * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t pT[KEYS * TP], dsT[KEYS * TP];
+  constexpr int T_SZ = DH * TP;        // one transposed copy (elements)
+  constexpr int KV_SZ = KEYS * RP;     // one row-major copy
+  static_assert(KEYS * TP <= KV_SZ, "A^T / dS^T fit in the K / V copies they replace");
+  static_assert((NDT * 16 - DH) * TP <= 2 * KV_SZ, "overrun rows of the last transposed copy stay in LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * T_SZ + 2 * KV_SZ];
   __shared__ int tok_s[KEYS], lab_s[KEYS];
+  uint16_t* const kT = lds;
+  uint16_t* const qT = lds + T_SZ;
+  uint16_t* const gT = lds + 2 * T_SZ;
+  uint16_t* const kr = lds + 3 * T_SZ;
+  uint16_t* const vr = kr + KV_SZ;
+  uint16_t* const pT = kr;  // written after every wave's S^T, dP^T products
+  uint16_t* const dsT = vr;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -315,12 +333,12 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
   const uint16_t* bias = reinterpret_cast<const uint16_t*>(p.bias_qkv);
   const uint16_t* dOb = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * N * p.D + h * DH;
 
-  // staging: 16-byte chunks (8 dims) of every slot; row-major K, V (zero past
-  // DH), transposed K, Q, dO (rows DH.. of the transposed copies zero)
-  // one thread per (8-dim chunk, quad of slots), quads fastest: the four
+  // staging: 16-byte chunks (8 dims) of every slot; row-major K, V and
+  // transposed K, Q, dO (DH rows each).
+  // One thread per (8-dim chunk, quad of slots), quads fastest: the four
   // slots' chunks are transposed in registers, so each transposed row gets
   // one 8-byte write (and a wave's writes fall in distinct banks)
-  constexpr int CH = NKC * 4, QUADS = KEYS / 4;  // chunks per padded row, slot quads
+  constexpr int CH = DH / 8, QUADS = KEYS / 4;  // chunks per row, slot quads
   for (int idx = tid; idx < CH * QUADS; idx += BW_NT) {
     const int ch = idx / QUADS, kq = idx - ch * QUADS;
     uint4 k4[4], v4[4], q4[4], g4[4];
@@ -328,16 +346,14 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
     for (int j = 0; j < 4; ++j) {
       const int tok = tok_s[kq * 4 + j];
       k4[j] = v4[j] = q4[j] = g4[j] = uint4{0, 0, 0, 0};
-      if (ch * 8 < DH) {
-        if (tok >= 0) {
-          k4[j] = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
-          v4[j] = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
-          q4[j] = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
-          g4[j] = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
-        } else if (tok == -1 && bias) {
-          k4[j] = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
-          v4[j] = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
-        }
+      if (tok >= 0) {
+        k4[j] = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
+        v4[j] = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
+        q4[j] = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
+        g4[j] = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
+      } else if (tok == -1 && bias) {
+        k4[j] = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
+        v4[j] = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
       }
     }
 #pragma unroll
@@ -345,11 +361,9 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       *reinterpret_cast<uint4*>(&kr[(kq * 4 + j) * RP + ch * 8]) = k4[j];
       *reinterpret_cast<uint4*>(&vr[(kq * 4 + j) * RP + ch * 8]) = v4[j];
     }
-    if (ch * 8 < NDT * 16) {
-      put_quad_t(kT, TP, ch, kq * 4, k4);
-      put_quad_t(qT, TP, ch, kq * 4, q4);
-      put_quad_t(gT, TP, ch, kq * 4, g4);
-    }
+    put_quad_t(kT, TP, ch, kq * 4, k4);
+    put_quad_t(qT, TP, ch, kq * 4, q4);
+    put_quad_t(gT, TP, ch, kq * 4, g4);
   }
   __syncthreads();
 
@@ -379,8 +393,11 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       dp[t] = zero4();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
-        const uint4 va = *reinterpret_cast<const uint4*>(&vr[(t * 16 + c) * RP + kc * 32 + 8 * g]);
+        const bool in = kc * 32 + 8 * g < DH;
+        const uint4 ka = in ? *reinterpret_cast<const uint4*>(&kr[(t * 16 + c) * RP + kc * 32 + 8 * g])
+                            : uint4{0, 0, 0, 0};
+        const uint4 va = in ? *reinterpret_cast<const uint4*>(&vr[(t * 16 + c) * RP + kc * 32 + 8 * g])
+                            : uint4{0, 0, 0, 0};
         sc[t] = mfma_bf16(ka, qf[kc], sc[t]);
         dp[t] = mfma_bf16(va, gf[kc], dp[t]);
       }
@@ -419,6 +436,7 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       }
     dd += __shfl_xor(dd, 16, 64);
     dd += __shfl_xor(dd, 32, 64);
+    __syncthreads();  // every wave is done with kr / vr, which pT / dsT overwrite
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1073,26 +1091,70 @@ struct PoolBwdParams {
   float P;
 };
 
+// PB_ROWS consecutive token rows per workgroup. A row's proxy depends on
+// wave-uniform values only, so its index math runs once per row on the
+// scalar unit, and consecutive rows of one proxy (the tokens of a window row)
+// share its quotients. Lanes cover 2 * BW_NT float4 columns per
+// pass; every load of a pass (d_x too, when accumulating) is issued before its
+// first store, so no store waits for a load.
+constexpr int PB_ROWS = 8;
+template <bool ACC>
 __global__ void __launch_bounds__(BW_NT) pool_bwd_kernel(PoolBwdParams p) {
+  const float* __restrict__ dP = p.dP;
+  float* __restrict__ dx = p.dx;
   const int q4 = p.D / 4;
-  const int64_t e = (int64_t)blockIdx.x * BW_NT + threadIdx.x;
-  if (e >= p.rows * q4) return;
-  const int64_t row = e / q4;
-  const int c = (int)(e - row * q4);
-  const int64_t N = (int64_t)p.F * p.H * p.W;
-  const int64_t b = row / N;
-  const int tok = (int)(row - b * N);
-  const int t = tok / (p.H * p.W), i = (tok / p.W) % p.H, j = tok % p.W;
+  const int N = p.F * p.H * p.W;
   const int nh = p.H / p.ph, nw = p.W / p.pw, M = (p.F / p.pt) * nh * nw;
-  const int m = ((t / p.pt) * nh + i / p.ph) * nw + j / p.pw;
-  const float4 g = *reinterpret_cast<const float4*>(p.dP + ((b * M + m) * p.D) + 4 * c);
-  float4 o{g.x / p.P, g.y / p.P, g.z / p.P, g.w / p.P};
-  float4* dst = reinterpret_cast<float4*>(p.dx + row * p.D + 4 * c);
-  if (p.accumulate) {
-    const float4 a = *dst;
-    o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+  const int64_t r0 = (int64_t)blockIdx.x * PB_ROWS;
+  const int nr = (int)min((int64_t)PB_ROWS, p.rows - r0);
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  for (int cb = 0; cb < q4; cb += 2 * BW_NT) {
+    const int c0 = cb + threadIdx.x, c1 = c0 + BW_NT;
+    // columns past the row load its last vector (in bounds, never stored)
+    const int l0 = min(c0, q4 - 1), l1 = min(c1, q4 - 1);
+    f4 v[PB_ROWS][2], a[ACC ? PB_ROWS : 1][2];
+    // every row's proxy (batch-major index) before the first load: B*N and
+    // N fit in 32 bits
+    int64_t bm[PB_ROWS];
+#pragma unroll
+    for (int r = 0; r < PB_ROWS; ++r) {
+      if (r >= nr) break;
+      const int row = (int)(r0 + r), b = row / N, tok = row - b * N;
+      const int t = tok / (p.H * p.W), i = (tok / p.W) % p.H, j = tok % p.W;
+      bm[r] = (int64_t)b * M + ((t / p.pt) * nh + i / p.ph) * nw + j / p.pw;
+    }
+#pragma unroll
+    for (int r = 0; r < PB_ROWS; ++r) {
+      if (r >= nr) break;
+      const int64_t row = r0 + r;
+      const f4* src = reinterpret_cast<const f4*>(dP + bm[r] * p.D);
+      v[r][0] = src[l0];
+      v[r][1] = src[l1];
+      if constexpr (ACC) {
+        const f4* d4 = reinterpret_cast<const f4*>(dx + row * p.D);
+        a[r][0] = d4[l0];
+        a[r][1] = d4[l1];
+      }
+    }
+    f4 q[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int r = 0; r < PB_ROWS; ++r) {
+      if (r >= nr) break;
+      f4* dst = reinterpret_cast<f4*>(dx + (r0 + r) * p.D);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (r == 0 || bm[r] != bm[r - 1]) {  // the first row of a run of one proxy
+          const f4 g = v[r][h];
+          q[h] = f4{g.x / p.P, g.y / p.P, g.z / p.P, g.w / p.P};
+        }
+        const int c = h ? c1 : c0;
+        if (c >= q4) continue;
+        f4 o = q[h];
+        if constexpr (ACC) o = f4{o.x + a[r][h].x, o.y + a[r][h].y, o.z + a[r][h].z, o.w + a[r][h].w};
+        dst[c] = o;
+      }
+    }
   }
-  *dst = o;
 }
 
 hipError_t launch_pool_bwd(const PoolBwdDesc& d, hipStream_t s) {
@@ -1103,9 +1165,10 @@ hipError_t launch_pool_bwd(const PoolBwdDesc& d, hipStream_t s) {
   p.rows = (int64_t)d.B * d.F * d.H * d.W;
   p.accumulate = d.accumulate;
   p.P = (float)(d.pt * d.ph * d.pw);
-  const int64_t n = p.rows * (d.D / 4);
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_bwd_kernel, dim3((unsigned)((n + BW_NT - 1) / BW_NT)), dim3(BW_NT), 0, s, p);
+  if (p.rows == 0 || d.D == 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.rows + PB_ROWS - 1) / PB_ROWS));
+  if (p.accumulate) hipLaunchKernelGGL((pool_bwd_kernel<true>), grid, dim3(BW_NT), 0, s, p);
+  else hipLaunchKernelGGL((pool_bwd_kernel<false>), grid, dim3(BW_NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -113,8 +113,15 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
                                                              int64_t nw, int d_out) {
   const int64_t e = (int64_t)blockIdx.x * LB_NT + threadIdx.x;
   if (e < nw && dw) {
+    // four loads in flight, added in split order
     float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * nw + e];
+    int k = 0;
+    for (; k + 4 <= splits; k += 4) {
+      const float a0 = part[(int64_t)k * nw + e], a1 = part[(int64_t)(k + 1) * nw + e];
+      const float a2 = part[(int64_t)(k + 2) * nw + e], a3 = part[(int64_t)(k + 3) * nw + e];
+      s += a0; s += a1; s += a2; s += a3;
+    }
+    for (; k < splits; ++k) s += part[(int64_t)k * nw + e];
     dw[e] = s;
   }
   if (e < d_out && db) {

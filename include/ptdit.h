@@ -309,7 +309,9 @@ size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int3
  * ptdit_proxy_pool_bwd -- gradient of the window average (Eq. GIIM's
  * Averaging): every token of a proxy window receives d_proxies[proxy] / P,
  * P = p_t*p_h*p_w (IEEE fp32 division). d_proxies [B][M][D] fp32, d_x
- * [B][N][D] fp32 (written, or added to when accumulate != 0); D % 4 == 0.
+ * [B][N][D] fp32 (written, or added to when accumulate != 0); D % 4 == 0,
+ * N <= 2^30, B*N <= 2^31 - 1 (else PTDIT_ERR_SHAPE); both pointers 16-byte
+ * aligned; d_x must not overlap d_proxies (PTDIT_ERR_ALIAS).
  * The gradient of the roll is the inverse roll: ptdit_roll3d(inverse = 1).
  */
 ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,

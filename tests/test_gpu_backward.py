@@ -175,6 +175,8 @@ POOL_CASES = [
     ((1, 1, 16, 16), 1152, (1, 4, 4)),
     ((2, 4, 6, 9), 64, (2, 3, 3)),
     ((1, 1, 128, 128), 1152, (1, 8, 8)),
+    ((1, 3, 5, 7), 2400, (3, 5, 7)),   # 105 rows (a ragged 8-row group), two column passes
+    ((3, 1, 3, 5), 8, (1, 3, 5)),      # 45 rows over three batches, two columns
 ]
 
 
