@@ -9,7 +9,7 @@
 //                     contraction over the token axis on the DMA GEMM kernels
 //                     (those of the token-row projections), the token axis
 //                     split over blockIdx.y into partials
-//   colsum_kernel     partial column sums of dY over 256-row blocks
+//   colsum_kernel     partial column sums of dY over 128-row blocks
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
 #include <hip/hip_runtime.h>
 
@@ -87,24 +87,46 @@ __global__ void __launch_bounds__(LB_NT) transpose_pad_kernel(const T* __restric
   }
 }
 
-// partial column sums of dY over token block blockIdx.y (CS_ROWS rows)
-constexpr int CS_ROWS = 256;
+// partial column sums of dY over token block blockIdx.y (CS_ROWS rows): four
+// columns per lane (d_out % 8 == 0, 16-byte aligned rows), eight rows of
+// loads in flight, four chains (row t % 4) combined in a fixed order
+constexpr int CS_ROWS = 128;
+template <typename TA> struct Col4;
+template <> struct Col4<float> {
+  __device__ static float4 ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
+};
+template <> struct Col4<uint16_t> {
+  __device__ static float4 ld(const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                  __uint_as_float(v.y & 0xffff0000u)};
+  }
+};
 template <typename TA>
 __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy, float* __restrict__ dbp,
                                                        int64_t rows, int d_out) {
-  const int o = blockIdx.x * LB_NT + threadIdx.x;
+  const int o = 4 * (blockIdx.x * LB_NT + threadIdx.x);
   if (o >= d_out) return;
   const int64_t t0 = (int64_t)blockIdx.y * CS_ROWS, t1 = min(rows, t0 + CS_ROWS);
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;  // four chains, combined in a fixed order
+  float4 s[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s[c] = float4{0.f, 0.f, 0.f, 0.f};
+  auto add = [](float4& a, const float4& b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; };
   int64_t t = t0;
-  for (; t + 4 <= t1; t += 4) {
-    s0 += ld1(dy + t * d_out + o);
-    s1 += ld1(dy + (t + 1) * d_out + o);
-    s2 += ld1(dy + (t + 2) * d_out + o);
-    s3 += ld1(dy + (t + 3) * d_out + o);
+  for (; t + 8 <= t1; t += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = Col4<TA>::ld(dy + (t + u) * d_out + o);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(s[u & 3], v[u]);
   }
-  for (; t < t1; ++t) s0 += ld1(dy + t * d_out + o);
-  dbp[(int64_t)blockIdx.y * d_out + o] = (s0 + s1) + (s2 + s3);
+  for (; t < t1; ++t) add(s[(t - t0) & 3], Col4<TA>::ld(dy + t * d_out + o));
+  float4 r = s[0];
+  add(r, s[1]);
+  float4 r2 = s[2];
+  add(r2, s[3]);
+  add(r, r2);
+  *reinterpret_cast<float4*>(dbp + (int64_t)blockIdx.y * d_out + o) = r;
 }
 
 __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __restrict__ part,
@@ -126,7 +148,13 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
   }
   if (e < d_out && db) {
     float s = 0.f;
-    for (int k = 0; k < csplits; ++k) s += dbp[(int64_t)k * d_out + e];
+    int k = 0;
+    for (; k + 4 <= csplits; k += 4) {
+      const float a0 = dbp[(int64_t)k * d_out + e], a1 = dbp[(int64_t)(k + 1) * d_out + e];
+      const float a2 = dbp[(int64_t)(k + 2) * d_out + e], a3 = dbp[(int64_t)(k + 3) * d_out + e];
+      s += a0; s += a1; s += a2; s += a3;
+    }
+    for (; k < csplits; ++k) s += dbp[(int64_t)k * d_out + e];
     db[e] = s;
   }
 }
@@ -202,7 +230,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   }
   const int csplits = colsum_splits(d.rows);
   if (d.db) {
-    const dim3 grid((d.d_out + LB_NT - 1) / LB_NT, csplits);
+    const dim3 grid((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits);
     if (d.dy_f32)
       hipLaunchKernelGGL((colsum_kernel<float>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
                          d.dbp, d.rows, d.d_out);
