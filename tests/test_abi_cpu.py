@@ -186,6 +186,7 @@ def test_host_validation_rejects_before_launch(lib):
     # backward: pooling
     pb = lib.ptdit_proxy_pool_bwd
     assert pb(fake, Grid(1, 1, 16, 16, 1150, 16), Win3(1, 4, 4), far, 0, None) == -2
+    assert pb(fake, Grid(3, 1024, 1024, 1024, 8, 16), Win3(1, 4, 4), far, 0, None) == -2  # B*N > 2^31 - 1
     assert pb(fake, g, Win3(1, 3, 3), far, 0, None) == -3
     assert pb(None, g, Win3(1, 4, 4), far, 0, None) == -1
     assert pb(fake, g, Win3(1, 4, 4), ctypes.c_void_p((1 << 20) + 256), 0, None) == -8
