@@ -45,10 +45,11 @@ def source_hash(files) -> str:
 
 
 def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
-    """Time the float64 oracle (as it stands) on full blocks of the same
-    workload, on this host's cores: blocks are repeated until half the budget
-    is spent (at least three when they fit in it), and the median is taken."""
-    import numpy as np  # noqa: F401
+    """Time the oracle (as it stands, run in float32: the fp32 NumPy oracle
+    the target statement names) on full blocks of the same workload, on this
+    host's cores: blocks are repeated until half the budget is spent (at
+    least three when they fit in it), and the median is taken."""
+    import numpy as np
     import oracle as O
     from synth_inputs import make_all_weights, make_x
     blas = "unknown"
@@ -66,14 +67,15 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)
+        with O.precision(np.float32):
+            O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)
         times.append(time.perf_counter() - t0)
         elapsed = time.perf_counter() - t_start
         if elapsed >= budget_s or (elapsed >= budget_s / 2 and len(times) >= 3) or len(times) >= 25:
             break
     t = statistics.median(times)
     out = {"value": wl.B * wl.N / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"{len(times)} full {wl.name} block(s) ({wl.B}x{wl.N} tokens), float64 NumPy, "
+           "sample": f"{len(times)} full {wl.name} block(s) ({wl.B}x{wl.N} tokens), float32 NumPy, "
                      f"median {t:.2f} s",
            "blas": blas, "host_cpus": len(os.sched_getaffinity(0))}
     # the same oracle on one BLAS thread, on the small fp32 image block
@@ -83,7 +85,7 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
         from synth_inputs import WORKLOADS
         small = WORKLOADS["img256_f32"]
         xs, wss = make_x(small), make_all_weights(small)
-        with threadpool_limits(limits=1, user_api="blas"):
+        with threadpool_limits(limits=1, user_api="blas"), O.precision(np.float32):
             t0 = time.perf_counter()
             O.block(xs, small.grid, small.p, small.win, small.shift, wss, small.heads)
             t1 = time.perf_counter() - t0

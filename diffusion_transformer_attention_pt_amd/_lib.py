@@ -130,6 +130,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _numel(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """Raise before any launch when a tensor's element count differs from
+    what the grid says it holds (the kernels index by the grid)."""
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name}: {tuple(t.shape)} holds {t.numel()} elements, the grid needs {n}")
+
+
+def _weights(w: "AttnWeights", D: int) -> None:
+    if tuple(w.w_qkv.shape) != (3 * D, D) or tuple(w.w_o.shape) != (D, D):
+        raise ValueError(f"attention weights must be w_qkv [{3 * D}, {D}] and w_o [{D}, {D}]")
+    _numel(w.b_qkv, 3 * D, "b_qkv")
+    _numel(w.b_o, D, "b_o")
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -198,6 +212,10 @@ def mlp(x: torch.Tensor, w: MlpWeights, residual: bool = True, out_dtype: Option
     lib = load()
     D = x.shape[-1]
     rows = x.numel() // D
+    for t, name in ((out, "out"), (x_lowp, "x_lowp"), (out_lowp, "out_lowp")):
+        _numel(t, rows * D, name)
+    if tuple(w.w1.shape) != (w.hidden, D) or tuple(w.w2.shape) != (D, w.hidden):
+        raise ValueError(f"MLP weights must be w1 [H, {D}] and w2 [{D}, H]")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_MLP, (rows, 1, 1, 1, D, 1), w.hidden, (1, 1, 1), w.dtype)
@@ -229,6 +247,11 @@ def linear(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None,
     lib = load()
     rows = x.numel() // x.shape[-1]
     d_in, d_out = x.shape[-1], w.shape[0]
+    if tuple(w.shape) != (d_out, d_in):
+        raise ValueError(f"w must be [d_out, {d_in}]")
+    _numel(b, d_out, "b")
+    _numel(residual, rows * d_out, "residual")
+    _numel(out, rows * d_out, "out")
     if out is None:
         out = torch.empty(*x.shape[:-1], d_out, dtype=out_dtype or x.dtype, device=x.device)
     r_dt = _dt(residual.dtype) if residual is not None else _dt(out.dtype)
@@ -250,6 +273,8 @@ def proxy_select(x: torch.Tensor, grid: Sequence[int], p: Sequence[int],
     if offsets is not None:
         if offsets.dtype != torch.int32 or offsets.numel() != B * M:
             raise ValueError("offsets must be int32 [B, M]")
+    _numel(x, B * F * H * W * D, "x")
+    _numel(out, B * M * D, "out")
     if out is None:
         out = torch.empty(B, M, D, dtype=out_dtype or x.dtype, device=x.device)
     st = lib.ptdit_proxy_select(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*p), _ptr(offsets), _ptr(out),
@@ -264,6 +289,8 @@ def proxy_pool(x: torch.Tensor, grid: Sequence[int], p: Sequence[int],
     lib = load()
     B, F, H, W, D, _ = grid
     M = (F // p[0]) * (H // p[1]) * (W // p[2]) if all(p) else 0
+    _numel(x, B * F * H * W * D, "x")
+    _numel(out, B * M * D, "out")
     if out is None:
         out = torch.empty(B, M, D, dtype=out_dtype or x.dtype, device=x.device)
     st = lib.ptdit_proxy_pool(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*p), _ptr(out), _dt(out.dtype),
@@ -277,6 +304,8 @@ def proxy_sa(P: torch.Tensor, heads: int, w: AttnWeights, residual: bool = True,
              out: Optional[torch.Tensor] = None) -> torch.Tensor:
     lib = load()
     B, M, D = P.shape
+    _weights(w, D)
+    _numel(out, B * M * D, "out")
     if out is None:
         out = torch.empty(B, M, D, dtype=out_dtype or P.dtype, device=P.device)
     need = workspace_bytes(OP_PROXY_SA, (B, 1, 1, M, D, heads), M, (1, 1, 1), w.dtype)
@@ -295,7 +324,13 @@ def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnW
     """out_lowp: optional bf16 tensor of out's shape that receives bf16(out);
     x_lowp: optional bf16 copy of an fp32 x, read by the query projection."""
     lib = load()
+    B, F, H, W, D, _ = grid
+    if P2.dim() != 3 or P2.shape[0] != B or P2.shape[2] != D:
+        raise ValueError(f"keys/values must be [{B}, M, {D}]")
     M = P2.shape[1]
+    _weights(w, D)
+    for t, name in ((x, "x"), (out, "out"), (out_lowp, "out_lowp"), (x_lowp, "x_lowp")):
+        _numel(t, B * F * H * W * D, name)
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_PROXY_XATTN, grid, M, (1, 1, 1), w.dtype)
@@ -308,6 +343,13 @@ def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnW
     return out
 
 
+def _window_shapes(grid, w, x, out, x_lowp, out_lowp) -> None:
+    B, F, H, W, D, _ = grid
+    _weights(w, D)
+    for t, name in ((x, "x"), (out, "out"), (x_lowp, "x_lowp"), (out_lowp, "out_lowp")):
+        _numel(t, B * F * H * W * D, name)
+
+
 def window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], w: AttnWeights,
               residual: bool = True, out_dtype: Optional[torch.dtype] = None,
               ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -315,6 +357,7 @@ def window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], w: AttnW
     """x_lowp: optional bf16 copy of an fp32 x (read by the projection);
     out_lowp: optional bf16 tensor that receives bf16(out)."""
     lib = load()
+    _window_shapes(grid, w, x, out, x_lowp, out_lowp)
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_WINDOW_SA, grid, 0, win, w.dtype)
@@ -334,6 +377,7 @@ def shift_window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], sh
                     out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x_lowp / out_lowp as for window_sa."""
     lib = load()
+    _window_shapes(grid, w, x, out, x_lowp, out_lowp)
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_SHIFT_WINDOW_SA, grid, 0, win, w.dtype)
@@ -350,6 +394,9 @@ def shift_window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], sh
 def roll3d(x: torch.Tensor, grid: Sequence[int], shift: Sequence[int], inverse: bool = False,
            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     lib = load()
+    B, F, H, W, D, _ = grid
+    _numel(x, B * F * H * W * D, "x")
+    _numel(out, B * F * H * W * D, "out")
     if out is None:
         out = torch.empty_like(x)
     st = lib.ptdit_roll3d(_ptr(x), Grid(*grid), Win3(*shift), int(inverse), _ptr(out), _dt(x.dtype),
@@ -368,6 +415,12 @@ def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], w
     B, F, H, W, D, heads = grid
     if d_o.dtype != qkv.dtype or (b_qkv is not None and b_qkv.dtype != qkv.dtype):
         raise ValueError("qkv, d_o and b_qkv must share one dtype")
+    N = F * H * W
+    _numel(qkv, B * 3 * N * D, "qkv")
+    _numel(d_o, B * N * D, "d_o")
+    _numel(b_qkv, 3 * D, "b_qkv")
+    _numel(d_qkv, B * 3 * N * D, "d_qkv")
+    _numel(d_b_kv, 2 * D, "d_b_kv")
     if d_qkv is None:
         d_qkv = torch.empty(qkv.shape, dtype=torch.float32, device=qkv.device)
     if d_b_kv is None:
@@ -396,6 +449,9 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
     lib = load()
     B, heads, Nq, dh = q.shape
     Nk = k.shape[2]
+    if tuple(k.shape) != (B, heads, Nk, dh) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k and v must both be [{B}, {heads}, Nk, {dh}]")
+    _numel(d_o, B * Nq * heads * dh, "d_o")
     if k.stride(0) != v.stride(0):
         raise ValueError("k and v must share their batch stride")
     dq = torch.empty(B, heads, Nq, dh, dtype=torch.float32, device=q.device)
@@ -419,6 +475,9 @@ def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int
     """Backward of the window average: d_x[token] (+)= d_proxies[its proxy] / P (fp32)."""
     lib = load()
     B, F, H, W, D, _ = grid
+    M = (F // p[0]) * (H // p[1]) * (W // p[2]) if all(p) else 0
+    _numel(d_proxies, B * M * D, "d_proxies")
+    _numel(d_x, B * F * H * W * D, "d_x")
     if d_x is None:
         d_x = torch.empty(B, F * H * W, D, dtype=torch.float32, device=d_proxies.device)
     st = lib.ptdit_proxy_pool_bwd(_ptr(d_proxies), Grid(*grid), Win3(*p), _ptr(d_x), int(accumulate), _stream())
@@ -433,6 +492,11 @@ def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: boo
     lib = load()
     d_in, d_out = x.shape[-1], w.shape[0]
     rows = x.numel() // d_in
+    if w.dtype != torch.bfloat16:
+        raise ValueError("linear_bwd reads w as bf16 (the forward's weight dtype)")
+    if tuple(w.shape) != (d_out, d_in):
+        raise ValueError(f"w must be [d_out, {d_in}]")
+    _numel(d_y, rows * d_out, "d_y")
     dev = x.device
     dx = torch.empty(*x.shape[:-1], d_in, dtype=torch.float32, device=dev) if want_dx else None
     dw = torch.empty(d_out, d_in, dtype=torch.float32, device=dev) if want_dw else None

@@ -135,9 +135,12 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   const size_t need = ptdit_workspace_bytes(PTDIT_OP_WINDOW_SA, g, 0, win, prec);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
   const size_t xb = rows * g.D * esize(x_dt), ob = rows * g.D * esize(out_dt), lb = rows * g.D * 2;
+  // inputs must not sit in the workspace either: the Q/K/V projection writes
+  // it before the output projection reads x as the residual
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need) || overlaps(out, ob, x_lowp, lb) ||
       overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, x_lowp, lb) ||
-      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need))
+      overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need) || overlaps(x, xb, ws, need) ||
+      overlaps(x_lowp, lb, ws, need))
     return PTDIT_ERR_ALIAS;
 
   const int D = g.D;
@@ -278,7 +281,7 @@ ptdit_status ptdit_mlp(const void* x, const void* x_lowp, ptdit_dtype x_dt, int6
   const size_t xb = rows * D * esize(x_dt), ob = rows * D * esize(out_dt), lb = rows * D * 2;
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, ws, need) || overlaps(out, ob, x_lowp, lb) ||
       overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, x_lowp, lb) || overlaps(out_lowp, lb, out, ob) ||
-      overlaps(out_lowp, lb, ws, need))
+      overlaps(out_lowp, lb, ws, need) || overlaps(x, xb, ws, need) || overlaps(x_lowp, lb, ws, need))
     return PTDIT_ERR_ALIAS;
   // h = GELU(x W1^T + b1) into the workspace, then out = h W2^T + b2 (+ x)
   hipError_t e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, hidden, w->w1, w->b1,
@@ -333,7 +336,7 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
   const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_SA, g, M, ptdit_win3{1, 1, 1}, prec);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
   if (overlaps(out, rows * D * esize(out_dt), proxies, rows * D * esize(p_dt)) ||
-      overlaps(out, rows * D * esize(out_dt), ws, need))
+      overlaps(out, rows * D * esize(out_dt), ws, need) || overlaps(proxies, rows * D * esize(p_dt), ws, need))
     return PTDIT_ERR_ALIAS;
 
   const int dh = D / heads;
@@ -385,7 +388,8 @@ ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, proxies, pb) || overlaps(out, ob, ws, need) ||
       overlaps(out_lowp, lb, x, xb) || overlaps(out_lowp, lb, proxies, pb) ||
       overlaps(out_lowp, lb, out, ob) || overlaps(out_lowp, lb, ws, need) || overlaps(out, ob, x_lowp, lb) ||
-      overlaps(out_lowp, lb, x_lowp, lb))
+      overlaps(out_lowp, lb, x_lowp, lb) || overlaps(x, xb, ws, need) || overlaps(x_lowp, lb, ws, need) ||
+      overlaps(proxies, pb, ws, need))
     return PTDIT_ERR_ALIAS;
 
   const int D = g.D, heads = g.heads, dh = D / heads;

@@ -219,7 +219,8 @@ ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_
  * (pad tokens are zero vectors, so their keys/values are the biases; their
  * outputs are dropped):  out = WSA(x) (+ x when add_residual != 0).
  *   x, out   [B][N][D];  x_lowp, out_lowp: optional bf16 copies (see above)
- * Requires a window of at most 128 tokens, a multiple of 16.
+ * Requires a window of 1 to 128 tokens (win.t*win.h*win.w <= 128, else
+ * PTDIT_ERR_SHAPE); any such window is accepted.
  */
 ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                              ptdit_win3 win, const ptdit_attn_w* w, int32_t add_residual,
@@ -278,7 +279,10 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
  *   d_qkv    [B][3][heads][N][dh] device, fp32: dQ, dK, dV of the real tokens
  *   d_b_kv   [2][D] device, fp32, or NULL: the gradients that reach pad key /
  *            value slots are ADDED here (d b_k, d b_v); required (else
- *            PTDIT_ERR_NULL) when the window does not divide the grid
+ *            PTDIT_ERR_NULL) when the window does not divide the grid. The
+ *            additions are device atomics, so their order (and with it the
+ *            last bits of d_b_kv) can differ from run to run; d_qkv is
+ *            written without atomics and is the same in every run
  *   win, shift as for the forward call (window <= 128 tokens, shift < window).
  */
 ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,

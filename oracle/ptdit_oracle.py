@@ -60,7 +60,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "linear", "attention", "mha", "proxy_grid", "proxy_pool", "proxy_pool_f32", "proxy_select",
+    "precision", "linear", "attention", "mha", "proxy_grid", "proxy_pool", "proxy_pool_f32", "proxy_select",
     "round_bf16_rne", "proxy_sa", "proxy_xattn", "pad_grid", "partition",
     "unpartition", "roll3d", "region_labels", "window_sa", "shift_window_sa",
     "block", "count_core_macs", "count_projection_macs", "gelu_tanh", "mlp", "text_xattn",
@@ -70,8 +70,34 @@ Grid = Tuple[int, int, int]
 Weights = Dict[str, np.ndarray]
 
 
+# Working precision of every step: float64, except inside `precision()`.
+_DT = np.float64
+
+
+class precision:
+    """Context manager that runs the same arithmetic in another NumPy float
+    type, e.g. ``with precision(np.float32): block(...)``. Only the CPU
+    baseline uses it (the fp32 NumPy oracle the target statement names); every
+    pin and parity test uses the float64 default."""
+
+    def __init__(self, dtype):
+        self.dtype = np.dtype(dtype).type
+        self.saved = None
+
+    def __enter__(self):
+        global _DT
+        self.saved, _DT = _DT, self.dtype
+        return self
+
+    def __exit__(self, *exc):
+        global _DT
+        _DT = self.saved
+        return False
+
+
 def _f64(a) -> np.ndarray:
-    return np.asarray(a, dtype=np.float64)
+    """The working precision (float64 unless inside `precision`)."""
+    return np.asarray(a, dtype=_DT)
 
 
 # ----------------------------------------------------------------------------
@@ -104,10 +130,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, heads: int,
     q, k, v = _f64(q), _f64(k), _f64(v)
     D = q.shape[-1]
     dh = D // heads
-    out = np.empty(q.shape[:-1] + (D,), dtype=np.float64)
+    out = np.empty(q.shape[:-1] + (D,), dtype=_DT)
     for h in range(heads):
         sl = slice(h * dh, (h + 1) * dh)
-        s = (q[..., sl] @ np.swapaxes(k[..., sl], -1, -2)) / np.sqrt(dh)
+        s = (q[..., sl] @ np.swapaxes(k[..., sl], -1, -2)) / float(np.sqrt(dh))
         if allow is not None:
             s = np.where(allow, s, -np.inf)
         s = s - s.max(axis=-1, keepdims=True)
@@ -250,7 +276,7 @@ def gelu_tanh(x: np.ndarray) -> np.ndarray:
     """GELU in its tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
     (Hendrycks & Gimpel, the approximation DiT-style MLPs use)."""
     x = _f64(x)
-    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    return 0.5 * x * (1.0 + np.tanh(float(np.sqrt(2.0 / np.pi)) * (x + 0.044715 * x ** 3)))
 
 
 def mlp(x: np.ndarray, w: Weights, residual: bool = True) -> np.ndarray:
@@ -274,7 +300,7 @@ def pad_grid(x: np.ndarray, grid: Grid, win: Sequence[int]) -> np.ndarray:
     x = _f64(x)
     B, N, D = x.shape
     Fp, Hp, Wp = _padded(grid, win)
-    out = np.zeros((B, Fp, Hp, Wp, D), dtype=np.float64)
+    out = np.zeros((B, Fp, Hp, Wp, D), dtype=_DT)
     out[:, :grid[0], :grid[1], :grid[2]] = x.reshape(B, *grid, D)
     return out
 

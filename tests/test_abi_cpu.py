@@ -115,6 +115,22 @@ def test_host_validation_rejects_before_launch(lib):
                                  o32, None, 1, ws, 1 << 30, 0, None) == -5   # misaligned x_lowp
     assert lib.ptdit_proxy_xattn(x32, lo, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, lo, 1, ws, 1 << 30, 0,
                                  None) == -8                 # out_lowp is x_lowp
+    # inputs inside the workspace (the first projection writes it before the
+    # last one reads the input as its residual)
+    big = ctypes.c_void_p(1 << 45)
+    inws = ctypes.c_void_p((1 << 45) + 4096)
+    assert lib.ptdit_window_sa(inws, None, 0, g, Win3(1, 8, 8), ctypes.byref(w), 1, o32, None, 0, big, 1 << 30, 0,
+                               None) == -8                   # x inside ws
+    assert lib.ptdit_window_sa(x32, inws, 1, g, Win3(1, 8, 8), ctypes.byref(w), 1, o32, None, 1, big, 1 << 30, 0,
+                               None) == -8                   # x_lowp inside ws
+    assert lib.ptdit_proxy_xattn(inws, None, 0, g, fake, 0, 256, ctypes.byref(w), 1, o32, None, 0, big, 1 << 30, 0,
+                                 None) == -8                 # x inside ws
+    assert lib.ptdit_proxy_xattn(x32, inws, 1, g, fake, 0, 256, ctypes.byref(w), 1, o32, None, 1, big, 1 << 30, 0,
+                                 None) == -8                 # x_lowp inside ws
+    assert lib.ptdit_proxy_xattn(fake, None, 0, g, inws, 0, 256, ctypes.byref(w), 1, o32, None, 0, big, 1 << 30,
+                                 0, None) == -8              # proxies inside ws
+    assert lib.ptdit_proxy_sa(inws, 0, 1, 256, 1152, 16, ctypes.byref(w), 1, o32, 0, big, 1 << 30, 0,
+                              None) == -8                    # proxies inside ws
     # cross-attention with no proxies
     assert lib.ptdit_proxy_xattn(fake, None, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, None, 0, fake, 1 << 30, 0,
                                  None) == -2
@@ -146,6 +162,10 @@ def test_host_validation_rejects_before_launch(lib):
     assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41), 1 << 30, prec=1) == -4
     assert mlp(fake, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41), 1 << 30,
                xl=ctypes.c_void_p(1 << 42)) == -4    # x_lowp beside a bf16 x
+    assert mlp(ctypes.c_void_p((1 << 41) + 4096), 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 41),
+               1 << 30) == -8                                # x inside ws
+    assert mlp(x32, 64, 1152, 4608, ctypes.byref(mw), far, ctypes.c_void_p(1 << 44), 1 << 30, xdt=1,
+               xl=ctypes.c_void_p((1 << 44) + 4096)) == -8   # x_lowp inside ws
     assert mlp(None, 0, 1152, 4608, ctypes.byref(mw), None, None, 0) == 0
     assert lib.ptdit_workspace_bytes(4, Grid(100, 1, 1, 1, 1152, 1), 4608, Win3(1, 1, 1), 0) >= 100 * 4608 * 2
     # roll: negative shift, D % 8, a grid row of 2^31 16-byte vectors (32-bit in-row index),
@@ -243,3 +263,45 @@ def test_product_path_has_no_cpu_fallback():
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src.replace("oracle is", ""), fn
             assert "import numpy" not in src, fn
+
+
+def test_binding_rejects_mismatched_shapes_before_any_call(lib):
+    """The ctypes wrappers compare every tensor with the grid (and w's dtype
+    for the projection gradients) and raise ValueError before the library is
+    called, so a mismatch never reaches a kernel as an out-of-bounds index.
+    CPU tensors suffice: the shape checks come before the device checks."""
+    import torch
+    from diffusion_transformer_attention_pt_amd import _lib as L
+
+    D, heads = 64, 1
+    grid = (1, 1, 8, 8, D, heads)
+    x = torch.zeros(1, 64, D)
+    short = torch.zeros(1, 63, D)
+    w = L.AttnWeights(torch.zeros(3 * D, D), torch.zeros(3 * D), torch.zeros(D, D), torch.zeros(D))
+    bad_w = L.AttnWeights(torch.zeros(2 * D, D), None, torch.zeros(D, D), None)
+    cases = [
+        lambda: L.proxy_pool(short, grid, (1, 2, 2)),
+        lambda: L.proxy_pool(x, grid, (1, 2, 2), out=torch.zeros(1, 15, D)),
+        lambda: L.proxy_select(short, grid, (1, 2, 2)),
+        lambda: L.window_sa(short, grid, (1, 4, 4), w),
+        lambda: L.window_sa(x, grid, (1, 4, 4), bad_w),
+        lambda: L.window_sa(x, grid, (1, 4, 4), w, x_lowp=short),
+        lambda: L.shift_window_sa(x, grid, (1, 4, 4), (0, 2, 2), w, out=short),
+        lambda: L.proxy_xattn(short, grid, torch.zeros(1, 16, D), w),
+        lambda: L.proxy_xattn(x, grid, torch.zeros(1, 16, D + 8), w),
+        lambda: L.proxy_sa(torch.zeros(1, 16, D), heads, bad_w),
+        lambda: L.roll3d(short, grid, (0, 1, 1)),
+        lambda: L.window_attn_bwd(torch.zeros(1, 3, heads, 63, D), torch.zeros(1, 64, D), grid, (1, 4, 4)),
+        lambda: L.window_attn_bwd(torch.zeros(1, 3, heads, 64, D), short, grid, (1, 4, 4)),
+        lambda: L.attn_bwd(torch.zeros(1, 2, 10, 72), torch.zeros(1, 2, 5, 72), torch.zeros(1, 2, 6, 72),
+                           torch.zeros(1, 10, 144)),
+        lambda: L.attn_bwd(torch.zeros(1, 2, 10, 72), torch.zeros(1, 2, 5, 72), torch.zeros(1, 2, 5, 72),
+                           torch.zeros(1, 9, 144)),
+        lambda: L.proxy_pool_bwd(torch.zeros(1, 15, D), grid, (1, 2, 2)),
+        lambda: L.linear_bwd(torch.zeros(4, D), torch.zeros(D, D), torch.zeros(4, D)),            # fp32 w
+        lambda: L.linear_bwd(torch.zeros(4, D), torch.zeros(D, D, dtype=torch.bfloat16), torch.zeros(5, D)),
+        lambda: L.linear(torch.zeros(4, D), torch.zeros(D, D + 8)),
+    ]
+    for i, f in enumerate(cases):
+        with pytest.raises(ValueError):
+            f()

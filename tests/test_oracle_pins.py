@@ -468,6 +468,61 @@ def test_core_macs_match_pages_formula_and_2p3_percent():
     assert f"{math.floor(pct * 10) / 10:.1f}" == facts["complexity_share_2048_percent"]["value"]
 
 
+def test_core_macs_counted_from_the_oracles_own_products(monkeypatch):
+    """The complexity paragraph's formula (2N^2D/P^2 + 2N^2D/P for GIIM, plus
+    the two window terms) against multiply-accumulates counted from the
+    operand shapes of the attention products the oracle actually runs inside
+    block() on the 2048^2 grid (narrow D: the count is linear in D), and the
+    2.3% share computed from those counts."""
+    facts = json.load(open(GOLDEN))
+    from oracle import ptdit_oracle as PO
+    real = PO.attention
+    calls = []
+
+    def counting(q, k, v, heads, allow=None):
+        lq = int(np.prod(q.shape[:-1]))          # every query row of the call
+        lk = k.shape[-2]                         # keys per query row
+        calls.append(2 * lq * lk * q.shape[-1])  # Q K^T and A V
+        return real(q, k, v, heads, allow)
+
+    monkeypatch.setattr(PO, "attention", counting)
+    wl = WORKLOADS["img2048"]
+    D, heads = 16, 2
+    g = np.random.default_rng(5)
+    x = g.standard_normal((1, wl.N, D))
+    ws = [_w(D, 90 + a, scale=0.1) for a in range(4)]
+    O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, heads)
+    assert len(calls) == 4                      # proxy SA, cross, WSA, SWSA
+    N, P, L = wl.N, int(np.prod(wl.p)), int(np.prod(wl.win))
+    assert calls[0] == 2 * N * N * D // (P * P)
+    assert calls[1] == 2 * N * N * D // P
+    assert calls[2] == calls[3] == 2 * N * L * D
+    share = Fraction(sum(calls), 2 * N * N * D)
+    pct = float(share) * 100
+    assert abs(pct - 2.368) < 1e-3
+    assert f"{math.floor(pct * 10) / 10:.1f}" == facts["complexity_share_2048_percent"]["value"]
+    # a planted slip (the cross-attention counted with the queries and keys
+    # swapped, i.e. keys = tokens) moves the share far from the page's figure
+    assert abs(float(Fraction(calls[0] + 2 * N * N * D + calls[2] + calls[3], 2 * N * N * D)) * 100 - 2.3) > 50
+
+
+def test_oracle_float32_mode_tracks_float64():
+    """precision(np.float32) runs the same steps in float32 (the CPU baseline's
+    fp32 oracle): its block output is float32 and within float32 rounding of
+    the float64 oracle, which is pinned by every other test here."""
+    wl = WORKLOADS["img256_f32"]
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    ref = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)["x3"]
+    with O.precision(np.float32):
+        got = O.block(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads)["x3"]
+    assert got.dtype == np.float32
+    assert O.block(x[:, :64], (1, 8, 8), (1, 2, 2), (1, 8, 8), (0, 4, 4), ws, wl.heads)["x3"].dtype == np.float64
+    d = got.astype(np.float64) - ref
+    assert np.linalg.norm(d) / np.linalg.norm(ref) < 1e-5
+    assert np.abs(d).max() < 1e-4
+
+
 def test_compression_schedule_keeps_proxy_count():
     facts = json.load(open(GOLDEN))
     for down in (8, 16):  # any fixed total latent downsampling factor
