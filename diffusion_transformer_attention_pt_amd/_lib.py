@@ -137,6 +137,15 @@ def _numel(t: Optional[torch.Tensor], n: int, name: str) -> None:
         raise ValueError(f"{name}: {tuple(t.shape)} holds {t.numel()} elements, the grid needs {n}")
 
 
+def _proxy_count(grid: Sequence[int], p: Sequence[int]) -> Optional[int]:
+    """B*M*D elements of the proxies, or None when p does not divide the grid
+    (the library then reports PTDIT_ERR_DIVISIBILITY itself)."""
+    B, F, H, W, D, _ = grid
+    if not all(p) or F % p[0] or H % p[1] or W % p[2]:
+        return None
+    return B * (F // p[0]) * (H // p[1]) * (W // p[2]) * D
+
+
 def _weights(w: "AttnWeights", D: int) -> None:
     if tuple(w.w_qkv.shape) != (3 * D, D) or tuple(w.w_o.shape) != (D, D):
         raise ValueError(f"attention weights must be w_qkv [{3 * D}, {D}] and w_o [{D}, {D}]")
@@ -274,7 +283,8 @@ def proxy_select(x: torch.Tensor, grid: Sequence[int], p: Sequence[int],
         if offsets.dtype != torch.int32 or offsets.numel() != B * M:
             raise ValueError("offsets must be int32 [B, M]")
     _numel(x, B * F * H * W * D, "x")
-    _numel(out, B * M * D, "out")
+    if _proxy_count(grid, p) is not None:
+        _numel(out, _proxy_count(grid, p), "out")
     if out is None:
         out = torch.empty(B, M, D, dtype=out_dtype or x.dtype, device=x.device)
     st = lib.ptdit_proxy_select(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*p), _ptr(offsets), _ptr(out),
@@ -290,7 +300,8 @@ def proxy_pool(x: torch.Tensor, grid: Sequence[int], p: Sequence[int],
     B, F, H, W, D, _ = grid
     M = (F // p[0]) * (H // p[1]) * (W // p[2]) if all(p) else 0
     _numel(x, B * F * H * W * D, "x")
-    _numel(out, B * M * D, "out")
+    if _proxy_count(grid, p) is not None:
+        _numel(out, _proxy_count(grid, p), "out")
     if out is None:
         out = torch.empty(B, M, D, dtype=out_dtype or x.dtype, device=x.device)
     st = lib.ptdit_proxy_pool(_ptr(x), _dt(x.dtype), Grid(*grid), Win3(*p), _ptr(out), _dt(out.dtype),
@@ -475,8 +486,8 @@ def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int
     """Backward of the window average: d_x[token] (+)= d_proxies[its proxy] / P (fp32)."""
     lib = load()
     B, F, H, W, D, _ = grid
-    M = (F // p[0]) * (H // p[1]) * (W // p[2]) if all(p) else 0
-    _numel(d_proxies, B * M * D, "d_proxies")
+    if _proxy_count(grid, p) is not None:
+        _numel(d_proxies, _proxy_count(grid, p), "d_proxies")
     _numel(d_x, B * F * H * W * D, "d_x")
     if d_x is None:
         d_x = torch.empty(B, F * H * W, D, dtype=torch.float32, device=d_proxies.device)

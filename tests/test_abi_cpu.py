@@ -305,3 +305,13 @@ def test_binding_rejects_mismatched_shapes_before_any_call(lib):
     for i, f in enumerate(cases):
         with pytest.raises(ValueError):
             f()
+
+
+def test_binding_leaves_divisibility_to_the_library(lib):
+    """A proxy window that does not divide the grid is the library's error to
+    report (PTDIT_ERR_DIVISIBILITY, checked on the host before any launch);
+    the binding's shape checks do not pre-empt it."""
+    import torch
+    from diffusion_transformer_attention_pt_amd import _lib as L
+    assert L._proxy_count((1, 1, 16, 16, 64, 1), (1, 5, 5)) is None
+    assert L._proxy_count((2, 1, 16, 16, 64, 1), (1, 4, 4)) == 2 * 16 * 64
