@@ -24,9 +24,10 @@ OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA, OP_MLP = 0, 1, 2,
 
 STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT_ERR_DIVISIBILITY",
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",
-          -7: "PTDIT_ERR_HIP", -8: "PTDIT_ERR_ALIAS"}
+          -7: "PTDIT_ERR_HIP", -8: "PTDIT_ERR_ALIAS", -9: "PTDIT_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PTDIT_NOALLOC_SCRATCH_BYTES
 
-EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_xattn",
+EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select", "ptdit_proxy_sa", "ptdit_proxy_sa_noalloc", "ptdit_proxy_xattn",
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
             "ptdit_trace_disable", "ptdit_window_attn_bwd", "ptdit_attn_bwd", "ptdit_attn_bwd_workspace_bytes",
@@ -77,6 +78,7 @@ def load() -> ctypes.CDLL:
         "ptdit_proxy_select": [vp, i32, G, W3, vp, vp, i32, vp],
         "ptdit_mlp": [vp, vp, i32, i64, i32, i32, MW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_proxy_sa": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, vp, sz, i32, vp],
+        "ptdit_proxy_sa_noalloc": [vp, i32, i32, i32, i32, i32, AW, i32, vp, i32, i32, vp],
         "ptdit_proxy_xattn": [vp, vp, i32, G, vp, i32, i32, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_window_sa": [vp, vp, i32, G, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_shift_window_sa": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
@@ -325,6 +327,21 @@ def proxy_sa(P: torch.Tensor, heads: int, w: AttnWeights, residual: bool = True,
     st = lib.ptdit_proxy_sa(_ptr(P), _dt(P.dtype), B, M, D, heads, ctypes.byref(cw), int(residual),
                             _ptr(out), _dt(out.dtype), _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
     _check("ptdit_proxy_sa", st)
+    return out
+
+
+def proxy_sa_noalloc(P: torch.Tensor, heads: int, w: AttnWeights, out: torch.Tensor,
+                     residual: bool = True) -> torch.Tensor:
+    """proxy_sa on the library's static scratch (ptdit_proxy_sa_noalloc): no
+    workspace, and nothing allocated here either (the caller passes out)."""
+    lib = load()
+    B, M, D = P.shape
+    _weights(w, D)
+    _numel(out, B * M * D, "out")
+    cw = w.c()
+    st = lib.ptdit_proxy_sa_noalloc(_ptr(P), _dt(P.dtype), B, M, D, heads, ctypes.byref(cw), int(residual),
+                                    _ptr(out), _dt(out.dtype), _dt(w.dtype), _stream())
+    _check("ptdit_proxy_sa_noalloc", st)
     return out
 
 

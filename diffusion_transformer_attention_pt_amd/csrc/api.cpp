@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "../../include/ptdit.h"
@@ -187,6 +188,7 @@ const char* ptdit_status_str(ptdit_status st) {
     case PTDIT_ERR_WORKSPACE: return "workspace missing or too small";
     case PTDIT_ERR_HIP: return "HIP launch failed";
     case PTDIT_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case PTDIT_ERR_SCRATCH: return "problem too large for the static scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -361,6 +363,56 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
   e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? proxies : nullptr, p_dt, out,
            out_dt, false, M, heads, D, PTDIT_K_GEMM_PROXY, stream);
   return hip_status(e);
+}
+
+// ------------------------------------------------------------------ no-allocation proxy SA
+// Scratch of ptdit_proxy_sa_noalloc: the Q/K/V and attention-output
+// workspace of ptdit_proxy_sa, in a file-scope device array that every GPU
+// the library runs on holds until the process ends. Host code never passes
+// the array's name to a kernel or a copy (on the host it is only a stand-in
+// for the symbol): it uses the device address hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[PTDIT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's scratch (nullptr on failure)
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+ptdit_status ptdit_proxy_sa_noalloc(const void* proxies, ptdit_dtype p_dt, int32_t B, int32_t M,
+                                    int32_t D, int32_t heads, const ptdit_attn_w* w,
+                                    int32_t add_residual, void* out, ptdit_dtype out_dt,
+                                    ptdit_dtype prec, hipStream_t stream) {
+  ptdit_status st = check_common(B, D, heads);
+  if (st) return st;
+  if (M < 0) return PTDIT_ERR_SHAPE;
+  if (!valid_dtype(prec)) return PTDIT_ERR_DTYPE;
+  if ((int64_t)B * M == 0) return PTDIT_OK;
+  const ptdit_grid g{B, 1, 1, M, D, heads};
+  const size_t need = ptdit_workspace_bytes(PTDIT_OP_PROXY_SA, g, M, ptdit_win3{1, 1, 1}, prec);
+  if (need == 0 || need > (size_t)PTDIT_NOALLOC_SCRATCH_BYTES) return PTDIT_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PTDIT_ERR_HIP;
+  void* ws = scratch_address(dev);
+  if (!ws) return PTDIT_ERR_HIP;
+  // the same kernels as ptdit_proxy_sa: the projection writes every Q/K/V
+  // element and the attention core every output element before they are
+  // read, so nothing of a previous call's scratch contents is used
+  return ptdit_proxy_sa(proxies, p_dt, B, M, D, heads, w, add_residual, out, out_dt, ws,
+                        (size_t)PTDIT_NOALLOC_SCRATCH_BYTES, prec, stream);
 }
 
 ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,

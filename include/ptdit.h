@@ -79,7 +79,8 @@ typedef enum {
   PTDIT_ERR_ALIGN = -5,         /* a pointer is not 16-byte aligned */
   PTDIT_ERR_WORKSPACE = -6,     /* workspace missing or smaller than required */
   PTDIT_ERR_HIP = -7,           /* a kernel launch failed */
-  PTDIT_ERR_ALIAS = -8          /* output overlaps an input or the workspace */
+  PTDIT_ERR_ALIAS = -8,         /* output overlaps an input or the workspace */
+  PTDIT_ERR_SCRATCH = -9        /* the no-allocation entry point's static scratch is too small */
 } ptdit_status;
 
 /* Token grid of one call: batch B, frames F, height H, width W (N = F*H*W),
@@ -195,6 +196,28 @@ ptdit_status ptdit_proxy_sa(const void* proxies, ptdit_dtype p_dt, int32_t B, in
                             int32_t D, int32_t heads, const ptdit_attn_w* w,
                             int32_t add_residual, void* out, ptdit_dtype out_dt,
                             void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_proxy_sa_noalloc -- ptdit_proxy_sa without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as ptdit_proxy_sa; its
+ * workspace is a static device array of PTDIT_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends (its device
+ * address is looked up on the first call on a device). Requires
+ * ptdit_workspace_bytes(PTDIT_OP_PROXY_SA, {B,1,1,M,D,heads}, M, ...) <=
+ * PTDIT_NOALLOC_SCRATCH_BYTES, else PTDIT_ERR_SCRATCH (before any launch):
+ * 32 MiB holds, e.g., B*M up to 3640 proxies of D = 1152 in bf16, 1820 in
+ * fp32. Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must be ordered by
+ * the caller. No scratch contents carry over between calls (every element
+ * is written before it is read), so nothing is cleared.
+ */
+#define PTDIT_NOALLOC_SCRATCH_BYTES (32 << 20)
+ptdit_status ptdit_proxy_sa_noalloc(const void* proxies, ptdit_dtype p_dt, int32_t B, int32_t M,
+                                    int32_t D, int32_t heads, const ptdit_attn_w* w,
+                                    int32_t add_residual, void* out, ptdit_dtype out_dt,
+                                    ptdit_dtype prec, hipStream_t stream);
 
 /*
  * ptdit_proxy_xattn -- CS(z_s, P') of Eq. GIIM (pvisual_attn2 followed by

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.ptdit_version()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = lib.ptdit_status_str(code)
         assert s and s != b"unknown status"
     assert lib.ptdit_status_str(-99) == b"unknown status"
@@ -131,6 +131,13 @@ def test_host_validation_rejects_before_launch(lib):
                                  0, None) == -8              # proxies inside ws
     assert lib.ptdit_proxy_sa(inws, 0, 1, 256, 1152, 16, ctypes.byref(w), 1, o32, 0, big, 1 << 30, 0,
                               None) == -8                    # proxies inside ws
+    # no-allocation proxy SA: a problem beyond the static scratch is refused
+    # on the host (3641 bf16 proxies of 1152 need more than 32 MiB)
+    na = lambda B, M, prec=0: lib.ptdit_proxy_sa_noalloc(fake, prec, B, M, 1152, 16, ctypes.byref(w), 1, far,
+                                                         prec, prec, None)
+    assert na(1, 3641) == -9 and na(2, 1821) == -9 and na(1, 1821, prec=1) == -9
+    assert na(0, 3641) == 0                                 # empty batch: nothing to do
+    assert lib.ptdit_proxy_sa_noalloc(fake, 0, 1, 256, 1152, 12, ctypes.byref(w), 1, far, 0, 0, None) == -2
     # cross-attention with no proxies
     assert lib.ptdit_proxy_xattn(fake, None, 0, g, fake, 0, 0, ctypes.byref(w), 1, fake, None, 0, fake, 1 << 30, 0,
                                  None) == -2
