@@ -44,6 +44,14 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
+def _padded_slots(wl) -> int:
+    """Window slots of one batch item: the grid padded up to whole TCM windows."""
+    n = 1
+    for g, w in zip(wl.grid, wl.win):
+        n *= -(-g // w) * w
+    return n
+
+
 def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     """Time the oracle (as it stands, run in float32: the fp32 NumPy oracle
     the target statement names) on full blocks of the same workload, on this
@@ -228,8 +236,15 @@ def main() -> int:
         blk.forward(x)
     torch.cuda.synchronize()
 
-    # dominant kernel: the Q/K/V projection of the token rows (2 launches per step)
-    dom_cls = _lib.K_GEMM_QKV
+    # dominant kernel: the Q/K/V projection of the token rows of the two window
+    # attentions (2 launches per step), fused with the window attention where
+    # the library takes that path (bf16, head width 72, 32/64/128-token windows)
+    _lib.trace_enable(_lib.K_WINDOW_FUSED, 8)
+    blk.forward(x)
+    torch.cuda.synchronize()
+    fused = len(_lib.trace_read(8)) > 0
+    _lib.trace_disable()
+    dom_cls = _lib.K_WINDOW_FUSED if fused else _lib.K_GEMM_QKV
     _lib.trace_enable(dom_cls, 2 * args.steps + 8)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -258,13 +273,18 @@ def main() -> int:
     peak = PEAK_BF16_TFLOPS if prec == torch.bfloat16 else PEAK_F32_TFLOPS
 
     rows = wl.B * wl.N
-    dom_flop = 2 * rows * wl.D * 3 * wl.D
+    L = wl.win[0] * wl.win[1] * wl.win[2]
+    # algorithmic FLOP per launch: the projection of the real token rows onto
+    # Q, K and V (2 * rows * D * 3D); fused, also the window core's two
+    # products counted dense over every (padded) window (2 * 2 * slots * L * D)
+    slots = wl.B * int(_padded_slots(wl))
+    dom_flop = 2 * rows * wl.D * 3 * wl.D + (4 * slots * L * wl.D if fused else 0)
     dom_avg_ms = statistics.mean(dom_ms) if dom_ms else float("nan")
     dom_tflops = dom_flop / (dom_avg_ms * 1e-3) / 1e12
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
-        rec = json.load(open(tpath)).get("gemm_qkv_" + wl.name)
+        rec = json.load(open(tpath)).get(("window_fused_" if fused else "gemm_qkv_") + wl.name)
         if rec and rec.get("source_sha") == source_hash(rec.get("sources", [])):
             traffic = rec.get("bytes_per_launch")
 
@@ -290,8 +310,11 @@ def main() -> int:
         "step_ms_p10_p50_p90": [round(quant(0.1), 4), round(quant(0.5), 4), round(quant(0.9), 4)],
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
-        "roofline": {"kernel": "gemm_pp_kernel: Q/K/V projection of the token rows "
-                               f"[{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] bf16 -> head-major bf16",
+        "roofline": {"kernel": (f"wfused_kernel: Q/K/V projection [{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] "
+                                f"bf16 fused with {L}-token window attention -> attention output bf16"
+                                if fused else
+                                "gemm_pp_kernel: Q/K/V projection of the token rows "
+                                f"[{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] bf16 -> head-major bf16"),
                      "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(dom_avg_ms, 5), "launches": len(dom_ms)},
@@ -299,7 +322,8 @@ def main() -> int:
     if args.breakdown:
         names = {_lib.K_POOL: "pool", _lib.K_GEMM_PROXY: "gemm_proxy", _lib.K_GEMM_Q: "gemm_q",
                  _lib.K_ATTN_FLASH: "attn_flash", _lib.K_GEMM_OUT: "gemm_out",
-                 _lib.K_GEMM_QKV: "gemm_qkv", _lib.K_ATTN_WINDOW: "attn_window"}
+                 _lib.K_GEMM_QKV: "gemm_qkv", _lib.K_ATTN_WINDOW: "attn_window",
+                 _lib.K_WINDOW_FUSED: "window_fused"}
         # algorithmic work per step of each class: FLOP (MFMA-bound classes) or
         # HBM bytes (pool, window cores: reads of x / Q,K,V and writes of the result)
         B, N, M, D = wl.B, wl.N, wl.M, wl.D
@@ -313,7 +337,8 @@ def main() -> int:
                 "attn_flash": ("TFLOP/s", 2 * B * D * (2 * M * M + 2 * N * M)),
                 "gemm_out": ("TFLOP/s", 3 * 2 * B * N * D * D),
                 "gemm_qkv": ("TFLOP/s", 2 * 2 * B * N * D * 3 * D),
-                "attn_window": ("GB/s", 2 * 4 * B * N * D * es)}
+                "attn_window": ("GB/s", 2 * 4 * B * N * D * es),
+                "window_fused": ("TFLOP/s", 2 * dom_flop)}
         if args.full_block:  # the text cross-attention shares the GIIM classes; the MLP has its own
             T, Hm = blk.L, blk.hidden
             for k, extra in (("gemm_q", 2 * B * N * D * D), ("gemm_proxy", 2 * B * T * D * 2 * D),
@@ -329,6 +354,8 @@ def main() -> int:
             torch.cuda.synchronize()
             ms = _lib.trace_read(64)
             _lib.trace_disable()
+            if not ms:      # a class this path does not launch
+                continue
             step_s = sum(ms) / 10 * 1e-3
             unit, amount = work[nm]
             if unit == "GB/s":

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libptdit.so")
 PTDIT_BF16, PTDIT_F32 = 0, 1
 OP_PROXY_SA, OP_PROXY_XATTN, OP_WINDOW_SA, OP_SHIFT_WINDOW_SA, OP_MLP = 0, 1, 2, 3, 4
 (K_POOL, K_GEMM_QKV, K_GEMM_OUT, K_ATTN_FLASH, K_ATTN_WINDOW, K_ROLL, K_GEMM_Q, K_GEMM_PROXY, K_GEMM_MLP,
- K_BWD_WINDOW, K_BWD_DENSE, K_BWD_POOL, K_BWD_LINEAR) = range(13)
+ K_BWD_WINDOW, K_BWD_DENSE, K_BWD_POOL, K_BWD_LINEAR, K_WINDOW_FUSED) = range(14)
 
 STATUS = {0: "PTDIT_OK", -1: "PTDIT_ERR_NULL", -2: "PTDIT_ERR_SHAPE", -3: "PTDIT_ERR_DIVISIBILITY",
           -4: "PTDIT_ERR_DTYPE", -5: "PTDIT_ERR_ALIGN", -6: "PTDIT_ERR_WORKSPACE",

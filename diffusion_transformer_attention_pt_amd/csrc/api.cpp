@@ -148,9 +148,33 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   char* wsp = (char*)ws;
   void* qkv = wsp;
   void* o = wsp + align_up((size_t)rows * 3 * D * esize(prec));
+  hipError_t e;
+  // bf16 operands available as bf16 (x itself, or its copy x_lowp): the
+  // Q/K/V projection and the window attention run as one kernel that keeps
+  // Q/K/V on chip and writes only the attention output
+  const void* xa = x_lowp ? x_lowp : (x_dt == PTDIT_BF16 ? x : nullptr);
+  WFusedDesc fd;
+  fd.X = xa; fd.w_qkv = w->w_qkv; fd.b_qkv = w->b_qkv; fd.O = o;
+  fd.B = g.B; fd.F = g.F; fd.H = g.H; fd.W = g.W; fd.D = D; fd.heads = g.heads; fd.dh = D / g.heads;
+  fd.wt = win.t; fd.wh = win.h; fd.ww = win.w;
+  fd.st = shift.t; fd.sh = shift.h; fd.sw = shift.w;
+  fd.Fp = (g.F + win.t - 1) / win.t * win.t;
+  fd.Hp = (g.H + win.h - 1) / win.h * win.h;
+  fd.Wp = (g.W + win.w - 1) / win.w * win.w;
+  fd.scale = 1.0f / std::sqrt((float)fd.dh);
+  if (prec == PTDIT_BF16 && xa && wfused_supported(fd)) {
+    {
+      TraceScope ts(PTDIT_K_WINDOW_FUSED, stream);
+      e = launch_wfused(fd, stream);
+    }
+    if (e != hipSuccess) return PTDIT_ERR_HIP;
+    e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
+             false, N, g.heads, D, PTDIT_K_GEMM_OUT, stream, out_lowp);
+    return hip_status(e);
+  }
   // the projection reads bf16(x); x_lowp, when given, already holds it
-  hipError_t e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, 3 * D, w->w_qkv,
-                      w->b_qkv, nullptr, prec, qkv, prec, true, N, g.heads, D, PTDIT_K_GEMM_QKV, stream);
+  e = gemm(prec, x_lowp ? x_lowp : x, x_lowp ? PTDIT_BF16 : x_dt, rows, D, 3 * D, w->w_qkv,
+           w->b_qkv, nullptr, prec, qkv, prec, true, N, g.heads, D, PTDIT_K_GEMM_QKV, stream);
   if (e != hipSuccess) return PTDIT_ERR_HIP;
   WindowDesc wd;
   wd.QKV = qkv; wd.bias_qkv = w->b_qkv; wd.O = o;
@@ -194,7 +218,6 @@ const char* ptdit_status_str(ptdit_status st) {
 }
 
 size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 win, ptdit_dtype prec) {
-  (void)win;
   if (!valid_dtype(prec) || g.B < 0 || g.D <= 0 || g.F < 0 || g.H < 0 || g.W < 0) return 0;
   const size_t es = esize(prec);
   const size_t B = (size_t)g.B, D = (size_t)g.D;
@@ -210,6 +233,9 @@ size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 wi
              (prec == PTDIT_BF16 && g.heads > 0 ? align_up(ptdit::flash_vt_bytes(g.B, g.heads, M)) : 0);
     case PTDIT_OP_WINDOW_SA:
     case PTDIT_OP_SHIFT_WINDOW_SA:
+      // windows the calls reject need no workspace: 0 (invalid arguments)
+      if (win.t <= 0 || win.h <= 0 || win.w <= 0 || (int64_t)win.t * win.h * win.w > 128) return 0;
+      // Q/K/V and the attention output (the fused kernel uses only the latter)
       return align_up(B * 3 * N * D * es) + align_up(B * N * D * es);
     case PTDIT_OP_MLP:
       if (M <= 0) return 0;

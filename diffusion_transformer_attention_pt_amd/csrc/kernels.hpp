@@ -75,6 +75,22 @@ struct WindowDesc {
 };
 hipError_t launch_window(const WindowDesc& d, int f32, hipStream_t s);
 
+// Window / shifted-window attention with the Q/K/V projection fused in
+// (wfused.hip): X [B][N][D] bf16 -> attention output O [B][N][D] bf16, the
+// same windows, roll, padding and mask as launch_window. bf16 only, dh = 72,
+// an even head count, windows of 32, 64 or 128 tokens, D % 128 == 0.
+struct WFusedDesc {
+  const void* X; const void* w_qkv; const void* b_qkv;
+  void* O;
+  int B, F, H, W, D, heads, dh;
+  int wt, wh, ww;
+  int st, sh, sw;
+  int Fp, Hp, Wp;
+  float scale;
+};
+bool wfused_supported(const WFusedDesc& d);
+hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s);
+
 // Backward pass of the attention core (fp32 gradients).
 struct WindowBwdDesc {
   const void* QKV; const void* bias_qkv; const void* dO;

@@ -1,0 +1,435 @@
+// Window and shifted-window self-attention with the Q/K/V projection fused
+// in (bf16, head width 72): the TCM attentions of the Qihoo-T2X reading note,
+// section 3 "Method", Eq. TCM, and the module table's attn1 on window-grouped
+// tokens with window_shift / window_Ishift around it.
+//
+// One workgroup takes 128 window slots (128 / L whole windows of L tokens of
+// the zero-padded, rolled grid) and one pair of heads.
+//
+// Phase 1 projects the slots' tokens onto the Q, K and V columns of both
+// heads: 3 x 144 = 432 output columns, 27 column blocks of 16. It is the
+// ping-pong DMA-ring GEMM of gemm_pp_kernel (8 waves in two groups one phase
+// apart, a 4-slot ring of 32-wide k-slices fed by global_load_lds) on a
+// 128 x 448 tile: waves of 64 rows x 7 blocks, the 28th block a copy of the
+// first whose result is never used. The A rows are gathered through the
+// window map (roll and zero padding applied per row), so nothing is
+// materialised; rows of pad slots load any real row and are zeroed after the
+// contraction, which leaves their K and V equal to the biases.
+//
+// Phase 2 writes Q and K row-major and V transposed (bf16) into the drained
+// ring, then every wave computes 32 queries of one (window, head): S^T = K Q^T
+// on the matrix cores, the boundary mask from per-slot region labels, an exact
+// one-pass softmax over the window's L keys held in registers, O^T = V^T P^T,
+// and writes O (token-major bf16) for the output projection. Q, K and V never
+// reach HBM. The arithmetic is that of the unfused path (same k order in the
+// projection, same rounding to bf16, same attention steps), so both give the
+// same attention output.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "ring.hpp"
+
+namespace ptdit {
+
+namespace {
+
+constexpr int WF_BM = 128;           // window slots per workgroup
+constexpr int WF_DH = 72;            // head width
+constexpr int WF_CPH = 2 * WF_DH;    // columns of one of Q/K/V for the head pair
+constexpr int WF_NWR = 3 * WF_CPH;   // W rows per tile (432)
+constexpr int WF_NBLK = WF_NWR / 16; // real column blocks (27)
+constexpr int WF_WM = 2, WF_WN = 4, WF_NW = 8;
+constexpr int WF_FM = WF_BM / WF_WM / 16;  // 4 row blocks per wave
+constexpr int WF_FN = 7;                   // column blocks per wave (4 x 7 = 28)
+constexpr int WF_SA = WF_BM * 4;           // 16-byte LDS slots of A per k-slice
+constexpr int WF_SB = WF_NWR * 4;          // ... of W
+constexpr int WF_IA = WF_SA / 64, WF_IT = WF_IA + WF_SB / 64;  // DMA instructions per slice
+constexpr int WF_MAXI = (WF_IT + WF_NW - 1) / WF_NW;
+static_assert(WF_WN * WF_FN == WF_NBLK + 1, "one spare column block");
+
+// staging of one (window, head) pair in the drained ring (bytes)
+template <int L>
+struct WfStage {
+  static constexpr int QB = L * WF_DH * 2;            // Q [L][72]
+  static constexpr int KB = QB;                       // K [L][72]
+  static constexpr int VTP = L + 4;                   // V^T row pitch (elements)
+  static constexpr int VB = 80 * VTP * 2;             // V^T [80][L+4], rows 72..79 zero
+  static constexpr int PAIRS = 2 * WF_BM / L;         // (window, head) pairs per tile
+  // bytes per ring slot: L = 32 two pairs a slot, L = 64 one, L = 128 Q + K in
+  // one slot and V^T in the next
+  static constexpr int SLOT_BYTES = L == 32 ? 2 * (QB + KB + VB) : (L == 64 ? QB + KB + VB : QB + KB);
+  static_assert(L == 32 || L == 64 || L == 128, "window sizes with a fused kernel");
+};
+
+}  // namespace
+
+struct WFusedParams {
+  const uint16_t* X;     // [B][N][D] bf16
+  const uint16_t* W;     // w_qkv [3D][D] bf16
+  const uint16_t* bias;  // b_qkv [3D] bf16 or null
+  uint16_t* O;           // [B][N][D] bf16
+  int N, D;
+  int F, H, Wd;
+  int wt, wh, ww;
+  int st, sh, sw;
+  int Fp, Hp, Wp;
+  int slots;       // B * Fp * Hp * Wp
+  int row_tiles;   // ceil(slots / 128)
+  int head_pairs;  // heads / 2
+  float sl2;       // 1/sqrt(dh) * log2(e)
+};
+
+__device__ __forceinline__ int wf_region(int k, int L, int w, int s) {
+  return k < L - w ? 0 : (k < L - s ? 1 : 2);
+}
+
+template <int L, bool MASKED>
+__global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
+  using SG = WfStage<L>;
+  constexpr int SLOT = (WF_SA + WF_SB) * 16 > SG::SLOT_BYTES ? (WF_SA + WF_SB) : (SG::SLOT_BYTES + 15) / 16;
+  __shared__ uint4 ring0[SLOT];
+  __shared__ uint4 ring1[SLOT];
+  __shared__ uint4 ring2[SLOT];
+  __shared__ uint4 ring3[SLOT];
+  __shared__ int grow_s[WF_BM];  // global token row b*N + tok, or -1 (pad slot / past the grid)
+  __shared__ __attribute__((aligned(16))) int lab_s[WF_BM];
+  auto slot = [&](auto sI) -> uint4* {
+    constexpr int sl = (decltype(sI)::value % 4 + 4) % 4;
+    if constexpr (sl == 0) return ring0;
+    else if constexpr (sl == 1) return ring1;
+    else if constexpr (sl == 2) return ring2;
+    else return ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;  // wm is the ping-pong group; SIMD wave % 4 holds one of each
+  const int g = lane >> 4, lr = lane & 15;
+
+  // XCD-aware tile order: block i runs on XCD i % 8; each XCD walks a
+  // contiguous range of logical tiles, head pair major, so with 8 head pairs
+  // every XCD keeps one pair's 432 weight rows in its L2.
+  const int ntiles = p.row_tiles * p.head_pairs;
+  if ((int)blockIdx.x >= ntiles) return;
+  int hp, rt;
+  {
+    const int bid = blockIdx.x, q = ntiles >> 3, rem = ntiles & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    hp = logical / p.row_tiles;
+    rt = logical - hp * p.row_tiles;
+  }
+
+  // slot -> token map of the tile's rows (roll by -shift on the padded grid)
+  if (tid < WF_BM) {
+    const int s = rt * WF_BM + tid;
+    int grow = -1, lab = -1;
+    if (s < p.slots) {
+      const int padN = p.Fp * p.Hp * p.Wp;
+      const int b = s / padN, rem = s - b * padN;
+      const int win = rem / L, e = rem - win * L;
+      const int nWh = p.Hp / p.wh, nWw = p.Wp / p.ww;
+      const int Tw = win / (nWh * nWw), Iw = (win / nWw) % nWh, Jw = win % nWw;
+      const int a = e / (p.wh * p.ww), c = (e / p.ww) % p.wh, f = e % p.ww;
+      const int rt_ = Tw * p.wt + a, ri = Iw * p.wh + c, rj = Jw * p.ww + f;
+      int ot = rt_ + p.st; ot -= ot >= p.Fp ? p.Fp : 0;
+      int oi = ri + p.sh; oi -= oi >= p.Hp ? p.Hp : 0;
+      int oj = rj + p.sw; oj -= oj >= p.Wp ? p.Wp : 0;
+      if (ot < p.F && oi < p.H && oj < p.Wd) grow = b * p.N + (ot * p.H + oi) * p.Wd + oj;
+      lab = wf_region(rt_, p.Fp, p.wt, p.st) * 9 + wf_region(ri, p.Hp, p.wh, p.sh) * 3 +
+            wf_region(rj, p.Wp, p.ww, p.sw);
+    }
+    grow_s[tid] = grow;
+    lab_s[tid] = lab;
+  }
+  __syncthreads();
+
+  // DMA plan: instruction j of a slice moves 64 16-byte chunks, A rows for
+  // j < WF_IA (4 chunks a row, swizzled as DmaA<bf16>), W rows after; wave w
+  // owns j = w + i*8 and repeats its first instruction to make WF_MAXI.
+  const char* const a_base = reinterpret_cast<const char*>(p.X);
+  const char* const w_base = reinterpret_cast<const char*>(p.W);
+  bool is_a[WF_MAXI];
+  uint32_t voff[WF_MAXI];
+  int dst[WF_MAXI];
+#pragma unroll
+  for (int i = 0; i < WF_MAXI; ++i) {
+    const int j0 = wave + i * WF_NW;
+    const int j = j0 < WF_IT ? j0 : wave;
+    is_a[i] = j < WF_IA;
+    if (j < WF_IA) {
+      const int sl = j * 64 + lane, row = sl >> 2, pp = sl & 3;
+      const int gr = max(grow_s[row], 0);  // pad slots load row 0 (zeroed later)
+      voff[i] = (uint32_t)gr * (uint32_t)(p.D * 2) + (uint32_t)((pp ^ ((row >> 1) & 3)) * 16);
+      dst[i] = j * 64;
+    } else {
+      const int sl = (j - WF_IA) * 64 + lane, row = sl >> 2, pp = sl & 3;
+      const int gq = row / WF_CPH, cc = row - gq * WF_CPH;
+      const int wrow = gq * p.D + hp * WF_CPH + cc;
+      voff[i] = (uint32_t)wrow * (uint32_t)(p.D * 2) + (uint32_t)((pp ^ ((row >> 1) & 3)) * 16);
+      dst[i] = WF_SA + (j - WF_IA) * 64;
+    }
+  }
+  auto issue = [&](int kt, uint4* st) {
+    const char* const ak = a_base + kt * 64;
+    const char* const wk = w_base + kt * 64;
+#pragma unroll
+    for (int i = 0; i < WF_MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
+  };
+
+  floatx4 acc[WF_FN][WF_FM];
+#pragma unroll
+  for (int i = 0; i < WF_FN; ++i)
+#pragma unroll
+    for (int j = 0; j < WF_FM; ++j) acc[i][j] = zero4();
+
+  const int lofs_a = DmaA<uint16_t>::lofs(wm * 64 + lr, g);
+  const int lofs_w = WF_SA + DmaA<uint16_t>::lofs(wn * (WF_FN * 16) + lr, g);
+  // the spare block (wave column 3, block 6) reads block 0's rows
+  const int lofs_w6 = wn == 3 ? WF_SA + DmaA<uint16_t>::lofs(lr, g) : lofs_w + 6 * 64;
+  uint4 wf[WF_FN], xf[WF_FM];
+  auto read_frags = [&](const uint4* st) {
+#pragma unroll
+    for (int i = 0; i < WF_FN - 1; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
+    wf[WF_FN - 1] = st[lofs_w6];
+#pragma unroll
+    for (int j = 0; j < WF_FM; ++j) xf[j] = DmaA<uint16_t>::frag(st, lofs_a, j);
+  };
+  auto mfmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < WF_FN; ++i)
+#pragma unroll
+      for (int j = 0; j < WF_FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+  };
+  // body of slice k (slot t = k % 4), as gemm_pp_kernel: refill slot t-1 with
+  // slice k+3, read slice k's fragments, wait for slice k+1, barrier, MFMAs,
+  // wait, barrier
+  auto body = [&](auto tI, auto issueI, auto wI, int k) {
+    constexpr int t = decltype(tI)::value;
+    if constexpr (decltype(issueI)::value) issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
+    read_frags(slot(std::integral_constant<int, t>{}));
+    wait_vm_lgkm0<decltype(wI)::value>();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas();
+    wait_vm_lgkm0<decltype(wI)::value>();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int KT = p.D / 32;  // multiple of 4, >= 8 (host check)
+  issue(0, slot(std::integral_constant<int, 0>{}));
+  issue(1, slot(std::integral_constant<int, 1>{}));
+  issue(2, slot(std::integral_constant<int, 2>{}));
+  wait_vm_lgkm0<2 * WF_MAXI>();
+  ring_barrier();
+  if (wm == 1) ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  using WS = std::integral_constant<int, 2 * WF_MAXI>;
+  for (int k0 = 0; k0 < KT - 4; k0 += 4) {
+    static_for<0, 4>([&](auto tI) { body(tI, std::true_type{}, WS{}, k0 + decltype(tI)::value); });
+  }
+  body(std::integral_constant<int, 0>{}, std::true_type{}, WS{}, KT - 4);
+  body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, WF_MAXI>{}, KT - 3);
+  body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 2);
+  body(std::integral_constant<int, 3>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 1);
+  if (wm == 0) ring_barrier();
+  wait_vm_lgkm0<0>();
+  ring_barrier();  // ring drained: every DMA landed, every fragment read retired
+
+  // ------------------------------------------------------------ phase 2
+  // LDS addresses of pair pr's Q, K and V^T (pair = window * 2 + head)
+  auto ring_at = [&](int s) -> char* {
+    return s == 0 ? reinterpret_cast<char*>(ring0)
+                  : (s == 1 ? reinterpret_cast<char*>(ring1)
+                            : (s == 2 ? reinterpret_cast<char*>(ring2) : reinterpret_cast<char*>(ring3)));
+  };
+  auto q_at = [&](int pr) -> char* {
+    if constexpr (L == 32) return ring_at(pr >> 1) + (pr & 1) * (SG::QB + SG::KB + SG::VB);
+    else if constexpr (L == 64) return ring_at(pr);
+    else return ring_at(2 * pr);
+  };
+  auto k_at = [&](int pr) -> char* { return q_at(pr) + SG::QB; };
+  auto vt_at = [&](int pr) -> uint16_t* {
+    if constexpr (L == 128) return reinterpret_cast<uint16_t*>(ring_at(2 * pr + 1));
+    else return reinterpret_cast<uint16_t*>(q_at(pr) + SG::QB + SG::KB);
+  };
+
+  // accumulators (+ bias; pad rows zeroed first) -> bf16 staging
+#pragma unroll
+  for (int i = 0; i < WF_FN; ++i) {
+    const int b = wn * WF_FN + i;  // wave-uniform
+    if (b >= WF_NBLK) continue;
+    const int gq = b / 9;          // 0 Q, 1 K, 2 V
+    const int c = (b - gq * 9) * 16 + 4 * g;
+    const int hh = c >= WF_DH ? 1 : 0, d = c - hh * WF_DH;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p.bias) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gq * p.D + hp * WF_CPH + c);
+      bv[0] = __uint_as_float(bb.x << 16); bv[1] = __uint_as_float(bb.x & 0xffff0000u);
+      bv[2] = __uint_as_float(bb.y << 16); bv[3] = __uint_as_float(bb.y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < WF_FM; ++j) {
+      const int r = wm * 64 + j * 16 + lr;
+      const bool real = grow_s[r] >= 0;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (real ? acc[i][j][e] : 0.f) + bv[e];
+      const int pr = (r / L) * 2 + hh, e_ = r % L;
+      if (gq < 2) {
+        char* base = gq == 0 ? q_at(pr) : k_at(pr);
+        *reinterpret_cast<uint2*>(base + (e_ * WF_DH + d) * 2) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      } else {
+        uint16_t* vt = vt_at(pr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[(d + e) * SG::VTP + e_] = (uint16_t)(pack_bf2(v[e], 0.f) & 0xffffu);
+      }
+    }
+  }
+  // V^T rows 72..79 of every pair are zero (the last 16-row tile of O^T)
+  for (int idx = tid; idx < SG::PAIRS * 8 * SG::VTP; idx += 512) {
+    const int pr = idx / (8 * SG::VTP), rem = idx - pr * 8 * SG::VTP;
+    vt_at(pr)[(WF_DH + rem / SG::VTP) * SG::VTP + rem % SG::VTP] = 0;
+  }
+  ring_barrier();
+
+  // attention: wave -> 32 queries of one (window, head) pair
+  constexpr int WPP = L / 32;  // waves per pair
+  constexpr int NKT = L / 16;  // key tiles
+  const int pr = wave / WPP, qb = (wave - pr * WPP) * 32;
+  const int wi = pr >> 1, hh = pr & 1;
+  const char* const qs = q_at(pr);
+  const char* const ks = k_at(pr);
+  const uint16_t* const vts = vt_at(pr);
+  floatx4 sc[2][NKT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) sc[qt][t] = zero4();
+#pragma unroll
+  for (int kc = 0; kc < 3; ++kc) {
+    const int dd = kc * 32 + 8 * g;
+    uint4 qf[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      qf[qt] = dd < WF_DH ? *reinterpret_cast<const uint4*>(qs + ((qb + qt * 16 + lr) * WF_DH + dd) * 2)
+                          : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+      const uint4 kf = dd < WF_DH ? *reinterpret_cast<const uint4*>(ks + ((t * 16 + lr) * WF_DH + dd) * 2)
+                                  : uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) sc[qt][t] = mfma_bf16(kf, qf[qt], sc[qt][t]);
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = wi * L + qb + qt * 16 + lr;
+    const int qlab = lab_s[qrow];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+      const int ks0 = wi * L + t * 16 + 4 * g;
+      const int4 lab4 = *reinterpret_cast<const int4*>(&lab_s[ks0]);
+      const int labs[4] = {lab4.x, lab4.y, lab4.z, lab4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = !MASKED || labs[r] == qlab;
+        const float v = ok ? sc[qt][t][r] * p.sl2 : -INFINITY;
+        sc[qt][t][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));  // the four lane groups hold a query's keys
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx == -INFINITY) mx = 0.f;
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = fast_exp2(sc[qt][t][r] - mx);
+        sc[qt][t][r] = e;
+        rs += e;
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    floatx4 o[5];
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt) o[dt] = zero4();
+#pragma unroll
+    for (int t0 = 0; t0 < NKT; t0 += 2) {
+      const uint4 pf = uint4{pack_bf2(sc[qt][t0][0], sc[qt][t0][1]), pack_bf2(sc[qt][t0][2], sc[qt][t0][3]),
+                             pack_bf2(sc[qt][t0 + 1][0], sc[qt][t0 + 1][1]),
+                             pack_bf2(sc[qt][t0 + 1][2], sc[qt][t0 + 1][3])};
+      const int kb = t0 * 16 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 5; ++dt) {
+        const uint16_t* row = vts + (dt * 16 + lr) * SG::VTP;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 16);
+        o[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
+      }
+    }
+    const int grow = grow_s[qrow];
+    if (grow >= 0) {
+      const float inv = 1.f / rs;
+      uint16_t* Ob = p.O + (int64_t)grow * p.D + (hp * 2 + hh) * WF_DH;
+#pragma unroll
+      for (int dt = 0; dt < 5; ++dt) {
+        const int dd = dt * 16 + 4 * g;
+        if (dd < WF_DH) store4(Ob + dd, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+      }
+    }
+  }
+}
+
+bool wfused_supported(const WFusedDesc& d) {
+  const int L = d.wt * d.wh * d.ww;
+  if (L != 32 && L != 64 && L != 128) return false;
+  if (d.dh != WF_DH || d.heads % 2 != 0 || d.D != d.heads * WF_DH) return false;
+  if (d.D % 128 != 0 || d.D < 256) return false;                  // 4 | D/32 >= 8 slices
+  const int64_t padN = (int64_t)d.Fp * d.Hp * d.Wp;
+  const int64_t N = (int64_t)d.F * d.H * d.W;
+  if ((int64_t)d.B * padN > INT32_MAX - WF_BM) return false;      // slot indices in 32 bits
+  // 32-bit byte offsets of X rows and of W rows from their bases
+  if ((int64_t)d.B * N * d.D * 2 >= ((int64_t)1 << 31)) return false;
+  if ((int64_t)3 * d.D * d.D * 2 >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+template <int L, bool M>
+static hipError_t run_wfused(const WFusedParams& p, hipStream_t s) {
+  const int ntiles = p.row_tiles * p.head_pairs;
+  hipLaunchKernelGGL((wfused_kernel<L, M>), dim3((unsigned)ntiles), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s) {
+  if (!wfused_supported(d)) return hipErrorInvalidValue;
+  if (d.B == 0) return hipSuccess;
+  WFusedParams p;
+  p.X = reinterpret_cast<const uint16_t*>(d.X);
+  p.W = reinterpret_cast<const uint16_t*>(d.w_qkv);
+  p.bias = reinterpret_cast<const uint16_t*>(d.b_qkv);
+  p.O = reinterpret_cast<uint16_t*>(d.O);
+  p.N = d.F * d.H * d.W;
+  p.D = d.D;
+  p.F = d.F; p.H = d.H; p.Wd = d.W;
+  p.wt = d.wt; p.wh = d.wh; p.ww = d.ww;
+  p.st = d.st; p.sh = d.sh; p.sw = d.sw;
+  p.Fp = d.Fp; p.Hp = d.Hp; p.Wp = d.Wp;
+  p.slots = d.B * d.Fp * d.Hp * d.Wp;
+  p.row_tiles = (p.slots + WF_BM - 1) / WF_BM;
+  p.head_pairs = d.heads / 2;
+  p.sl2 = d.scale * 1.4426950408889634f;
+  const bool masked = (d.st | d.sh | d.sw) != 0;
+  const int L = d.wt * d.wh * d.ww;
+  if (L == 32) return masked ? run_wfused<32, true>(p, s) : run_wfused<32, false>(p, s);
+  if (L == 64) return masked ? run_wfused<64, true>(p, s) : run_wfused<64, false>(p, s);
+  return masked ? run_wfused<128, true>(p, s) : run_wfused<128, false>(p, s);
+}
+
+}  // namespace ptdit

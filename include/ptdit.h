@@ -369,7 +369,12 @@ size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_ou
 
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
  * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*
- * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments. */
+ * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments, including a
+ * TCM window the window calls reject (a non-positive extent or more than 128
+ * tokens). The window calls' workspace holds the head-major Q/K/V and the
+ * attention output; when the fused kernel runs (bf16 precision, bf16 x or
+ * x_lowp, head width 72, an even head count, windows of 32, 64 or 128
+ * tokens) only the attention-output part is used. */
 size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 win,
                              ptdit_dtype prec);
 
@@ -400,7 +405,8 @@ typedef enum {
   PTDIT_K_BWD_WINDOW = 9,    /* window attention backward */
   PTDIT_K_BWD_DENSE = 10,    /* proxy / cross-attention backward (all three kernels) */
   PTDIT_K_BWD_POOL = 11,     /* window-average backward */
-  PTDIT_K_BWD_LINEAR = 12    /* projection gradients (all kernels of ptdit_linear_bwd) */
+  PTDIT_K_BWD_LINEAR = 12,   /* projection gradients (all kernels of ptdit_linear_bwd) */
+  PTDIT_K_WINDOW_FUSED = 13  /* Q/K/V projection fused with window / shifted-window attention */
 } ptdit_kernel_class;
 
 ptdit_status ptdit_trace_enable(int32_t kernel_class, int32_t capacity);
