@@ -19,8 +19,9 @@
 // Phase 2 writes Q and K row-major and V transposed (bf16) into the drained
 // ring, then every wave computes 32 queries of one (window, head): S^T = K Q^T
 // on the matrix cores, the boundary mask from per-slot region labels, an exact
-// one-pass softmax over the window's L keys held in registers, O^T = V^T P^T,
-// and writes O (token-major bf16) for the output projection. Q, K and V never
+// one-pass softmax over the window's L keys held in registers, O^T = V^T P^T.
+// O goes back over the wave's own Q rows and leaves as whole 288-byte token
+// rows (token-major bf16, the output projection's operand). Q, K and V never
 // reach HBM. The arithmetic is that of the unfused path (same k order in the
 // projection, same rounding to bf16, same attention steps), so both give the
 // same attention output.
@@ -46,17 +47,17 @@ constexpr int WF_IA = WF_SA / 64, WF_IT = WF_IA + WF_SB / 64;  // DMA instructio
 constexpr int WF_MAXI = (WF_IT + WF_NW - 1) / WF_NW;
 static_assert(WF_WN * WF_FN == WF_NBLK + 1, "one spare column block");
 
-// staging of one (window, head) pair in the drained ring (bytes)
+// staging of one window (both heads of the pair) in the drained ring (bytes)
 template <int L>
 struct WfStage {
-  static constexpr int QB = L * WF_DH * 2;            // Q [L][72]
-  static constexpr int KB = QB;                       // K [L][72]
+  static constexpr int QB = L * WF_CPH * 2;           // Q or K [L][144]
   static constexpr int VTP = L + 4;                   // V^T row pitch (elements)
-  static constexpr int VB = 80 * VTP * 2;             // V^T [80][L+4], rows 72..79 zero
-  static constexpr int PAIRS = 2 * WF_BM / L;         // (window, head) pairs per tile
-  // bytes per ring slot: L = 32 two pairs a slot, L = 64 one, L = 128 Q + K in
-  // one slot and V^T in the next
-  static constexpr int SLOT_BYTES = L == 32 ? 2 * (QB + KB + VB) : (L == 64 ? QB + KB + VB : QB + KB);
+  static constexpr int VB = WF_CPH * VTP * 2;         // V^T [144][L+4]
+  // bytes per ring slot: Q and K of one window (L = 64) or two (L = 32), Q or
+  // K alone (L = 128); V^T of one or two windows
+  static constexpr int QK_SLOT = L == 128 ? QB : (L == 64 ? 2 * QB : 4 * QB);
+  static constexpr int VT_SLOT = L == 32 ? 2 * VB : VB;
+  static constexpr int SLOT_BYTES = QK_SLOT > VT_SLOT ? QK_SLOT : VT_SLOT;
   static_assert(L == 32 || L == 64 || L == 128, "window sizes with a fused kernel");
 };
 
@@ -239,21 +240,24 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   ring_barrier();  // ring drained: every DMA landed, every fragment read retired
 
   // ------------------------------------------------------------ phase 2
-  // LDS addresses of pair pr's Q, K and V^T (pair = window * 2 + head)
-  auto ring_at = [&](int s) -> char* {
-    return s == 0 ? reinterpret_cast<char*>(ring0)
-                  : (s == 1 ? reinterpret_cast<char*>(ring1)
-                            : (s == 2 ? reinterpret_cast<char*>(ring2) : reinterpret_cast<char*>(ring3)));
+  // Staging in the drained ring (bf16), per window w of the tile with its two
+  // heads side by side: Q_w, K_w [L][144] row-major and V^T_w [144][L+4]
+  // (row = head * 72 + d). Every lane's window is wave-uniform, so slot
+  // bases are scalar and only offsets vary per lane.
+  const auto qk_base = [&](int w) -> char* {   // Q_w (K_w follows, except L = 128)
+    if constexpr (L == 32) return reinterpret_cast<char*>(w >> 1 ? ring1 : ring0) + (w & 1) * 2 * SG::QB;
+    else if constexpr (L == 64) return reinterpret_cast<char*>(w ? ring1 : ring0);
+    else return reinterpret_cast<char*>(ring0);
   };
-  auto q_at = [&](int pr) -> char* {
-    if constexpr (L == 32) return ring_at(pr >> 1) + (pr & 1) * (SG::QB + SG::KB + SG::VB);
-    else if constexpr (L == 64) return ring_at(pr);
-    else return ring_at(2 * pr);
+  const auto k_base = [&](int w) -> char* {
+    if constexpr (L == 128) return reinterpret_cast<char*>(ring1);
+    else return qk_base(w) + SG::QB;
   };
-  auto k_at = [&](int pr) -> char* { return q_at(pr) + SG::QB; };
-  auto vt_at = [&](int pr) -> uint16_t* {
-    if constexpr (L == 128) return reinterpret_cast<uint16_t*>(ring_at(2 * pr + 1));
-    else return reinterpret_cast<uint16_t*>(q_at(pr) + SG::QB + SG::KB);
+  const auto vt_base = [&](int w) -> uint16_t* {
+    if constexpr (L == 32)
+      return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(w >> 1 ? ring3 : ring2) + (w & 1) * SG::VB);
+    else if constexpr (L == 64) return reinterpret_cast<uint16_t*>(w ? ring3 : ring2);
+    else return reinterpret_cast<uint16_t*>(ring2);
   };
 
   // accumulators (+ bias; pad rows zeroed first) -> bf16 staging
@@ -262,8 +266,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     const int b = wn * WF_FN + i;  // wave-uniform
     if (b >= WF_NBLK) continue;
     const int gq = b / 9;          // 0 Q, 1 K, 2 V
-    const int c = (b - gq * 9) * 16 + 4 * g;
-    const int hh = c >= WF_DH ? 1 : 0, d = c - hh * WF_DH;
+    const int c = (b - gq * 9) * 16 + 4 * g;  // column within the head pair (0..143)
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
     if (p.bias) {
       const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gq * p.D + hp * WF_CPH + c);
@@ -272,26 +275,22 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     }
 #pragma unroll
     for (int j = 0; j < WF_FM; ++j) {
-      const int r = wm * 64 + j * 16 + lr;
-      const bool real = grow_s[r] >= 0;
+      const int r0 = wm * 64 + j * 16;       // wave-uniform first row of the block
+      const int w = r0 / L;                  // its window (uniform: 16 | L)
+      const int e_ = r0 - w * L + lr;        // slot within the window
+      const bool real = grow_s[r0 + lr] >= 0;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (real ? acc[i][j][e] : 0.f) + bv[e];
-      const int pr = (r / L) * 2 + hh, e_ = r % L;
       if (gq < 2) {
-        char* base = gq == 0 ? q_at(pr) : k_at(pr);
-        *reinterpret_cast<uint2*>(base + (e_ * WF_DH + d) * 2) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+        char* base = gq == 0 ? qk_base(w) : k_base(w);
+        *reinterpret_cast<uint2*>(base + (e_ * WF_CPH + c) * 2) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
       } else {
-        uint16_t* vt = vt_at(pr);
+        uint16_t* vt = vt_base(w) + c * SG::VTP + e_;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vt[(d + e) * SG::VTP + e_] = (uint16_t)(pack_bf2(v[e], 0.f) & 0xffffu);
+        for (int e = 0; e < 4; ++e) vt[e * SG::VTP] = (uint16_t)(pack_bf2(v[e], 0.f) & 0xffffu);
       }
     }
-  }
-  // V^T rows 72..79 of every pair are zero (the last 16-row tile of O^T)
-  for (int idx = tid; idx < SG::PAIRS * 8 * SG::VTP; idx += 512) {
-    const int pr = idx / (8 * SG::VTP), rem = idx - pr * 8 * SG::VTP;
-    vt_at(pr)[(WF_DH + rem / SG::VTP) * SG::VTP + rem % SG::VTP] = 0;
   }
   ring_barrier();
 
@@ -300,30 +299,37 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   constexpr int NKT = L / 16;  // key tiles
   const int pr = wave / WPP, qb = (wave - pr * WPP) * 32;
   const int wi = pr >> 1, hh = pr & 1;
-  const char* const qs = q_at(pr);
-  const char* const ks = k_at(pr);
-  const uint16_t* const vts = vt_at(pr);
+  char* const qs = qk_base(wi) + hh * WF_DH * 2;
+  const char* const ks = k_base(wi) + hh * WF_DH * 2;
+  const uint16_t* const vts = vt_base(wi);
   floatx4 sc[2][NKT];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int t = 0; t < NKT; ++t) sc[qt][t] = zero4();
+  // S^T = K Q^T over the head's 72 dims in three 32-wide steps; dims past 72
+  // (the other head's columns, or past the row) are masked to zero
 #pragma unroll
   for (int kc = 0; kc < 3; ++kc) {
     const int dd = kc * 32 + 8 * g;
+    const bool dok = dd < WF_DH;
+    const int ddc = dok ? dd : 0;
     uint4 qf[2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-      qf[qt] = dd < WF_DH ? *reinterpret_cast<const uint4*>(qs + ((qb + qt * 16 + lr) * WF_DH + dd) * 2)
-                          : uint4{0, 0, 0, 0};
+    for (int qt = 0; qt < 2; ++qt) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + ((qb + qt * 16 + lr) * WF_CPH + ddc) * 2);
+      qf[qt] = dok ? v : uint4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const uint4 kf = dd < WF_DH ? *reinterpret_cast<const uint4*>(ks + ((t * 16 + lr) * WF_DH + dd) * 2)
-                                  : uint4{0, 0, 0, 0};
+      const uint4 kv = *reinterpret_cast<const uint4*>(ks + ((t * 16 + lr) * WF_CPH + ddc) * 2);
+      const uint4 kf = dok ? kv : uint4{0, 0, 0, 0};
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) sc[qt][t] = mfma_bf16(kf, qf[qt], sc[qt][t]);
     }
   }
+  float inv[2];
+  floatx4 o[2][5];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qrow = wi * L + qb + qt * 16 + lr;
@@ -331,8 +337,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const int ks0 = wi * L + t * 16 + 4 * g;
-      const int4 lab4 = *reinterpret_cast<const int4*>(&lab_s[ks0]);
+      const int4 lab4 = *reinterpret_cast<const int4*>(&lab_s[wi * L + t * 16 + 4 * g]);
       const int labs[4] = {lab4.x, lab4.y, lab4.z, lab4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -356,9 +361,11 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
       }
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
-    floatx4 o[5];
+    inv[qt] = 1.f / rs;
 #pragma unroll
-    for (int dt = 0; dt < 5; ++dt) o[dt] = zero4();
+    for (int dt = 0; dt < 5; ++dt) o[qt][dt] = zero4();
+    // O^T = V^T P^T; rows past the head's 72 dims are computed on other data
+    // (or clamped rows) and never stored
 #pragma unroll
     for (int t0 = 0; t0 < NKT; t0 += 2) {
       const uint4 pf = uint4{pack_bf2(sc[qt][t0][0], sc[qt][t0][1]), pack_bf2(sc[qt][t0][2], sc[qt][t0][3]),
@@ -367,20 +374,43 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
       const int kb = t0 * 16 + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 5; ++dt) {
-        const uint16_t* row = vts + (dt * 16 + lr) * SG::VTP;
+        const int vrow = min(hh * WF_DH + dt * 16 + lr, WF_CPH - 1);
+        const uint16_t* row = vts + vrow * SG::VTP;
         const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
         const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 16);
-        o[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
+        o[qt][dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, pf, o[qt][dt]);
       }
     }
-    const int grow = grow_s[qrow];
-    if (grow >= 0) {
-      const float inv = 1.f / rs;
-      uint16_t* Ob = p.O + (int64_t)grow * p.D + (hp * 2 + hh) * WF_DH;
+  }
+  // O (bf16) over this wave's own Q rows: no other wave reads them (the other
+  // head's waves read the other 72 columns)
 #pragma unroll
-      for (int dt = 0; dt < 5; ++dt) {
-        const int dd = dt * 16 + 4 * g;
-        if (dd < WF_DH) store4(Ob + dd, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+  for (int qt = 0; qt < 2; ++qt) {
+    char* orow = qs + (qb + qt * 16 + lr) * WF_CPH * 2;
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt) {
+      const int dd = dt * 16 + 4 * g;
+      if (dd < WF_DH)
+        *reinterpret_cast<uint2*>(orow + dd * 2) =
+            uint2{pack_bf2(o[qt][dt][0] * inv[qt], o[qt][dt][1] * inv[qt]),
+                  pack_bf2(o[qt][dt][2] * inv[qt], o[qt][dt][3] * inv[qt])};
+    }
+  }
+  ring_barrier();
+  // O rows to HBM: wave v writes tile rows 16v .. 16v+15 (one window), each
+  // row the pair's 144 channels = 18 chunks of 16 bytes
+  {
+    const int r0 = wave * 16, w = r0 / L;
+    const char* ob = qk_base(w) + (r0 - w * L) * WF_CPH * 2;
+#pragma unroll
+    for (int it = 0; it < (16 * 18 + 63) / 64; ++it) {
+      const int idx = it * 64 + lane;
+      if (idx < 16 * 18) {
+        const int rr = idx / 18, ch = idx - rr * 18;
+        const int grow = grow_s[r0 + rr];
+        if (grow >= 0)
+          *reinterpret_cast<uint4*>(p.O + (int64_t)grow * p.D + hp * WF_CPH + ch * 8) =
+              *reinterpret_cast<const uint4*>(ob + (rr * WF_CPH + ch * 8) * 2);
       }
     }
   }
