@@ -25,6 +25,13 @@ Readings (in addition to the forward readings of ptdit_oracle):
              core: from (Q, K, V, dO) of the real tokens to (dQ, dK, dV) and
              the pad-slot sums; the projections' gradients are the linear-map
              gradients of linear_bwd (dX = dY W, dW = dY^T X, db = sum dY).
+  R-bwd-block the block's gradient (block_bwd) is that of <x3, dout> with
+             respect to x and all 32 weight and bias tensors, through the
+             chain of excerpt 2's order: SWSA, WSA, cross-attention, proxy
+             self-attention, window average; the residuals pass the gradient
+             through unchanged, and P' feeds both the cross-attention's keys
+             and values and (through its residual) back into the window
+             average's gradient.
 """
 from __future__ import annotations
 
@@ -34,7 +41,8 @@ import numpy as np
 
 from .ptdit_oracle import Grid, _f64, _padded, pad_grid, partition, proxy_grid, region_labels, roll3d, unpartition
 
-__all__ = ["attention_bwd", "window_core", "window_core_bwd", "proxy_pool_bwd", "roll3d_bwd", "linear_bwd"]
+__all__ = ["attention_bwd", "window_core", "window_core_bwd", "proxy_pool_bwd", "roll3d_bwd", "linear_bwd",
+           "mha_bwd", "window_mha_bwd", "block_bwd"]
 
 
 def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, heads: int,
@@ -174,3 +182,80 @@ def linear_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray):
     dy2 = dy.reshape(-1, dy.shape[-1])
     dx = (dy2 @ w).reshape(*x.shape[:-1], w.shape[1])
     return dx, dy2.T @ x2, dy2.sum(axis=0)
+
+
+_NAMES = ("q", "k", "v", "o")
+
+
+def _grads(d):
+    """{"wq": .., "bq": .., ...} from {"q": (dW, db), ...}."""
+    out = {}
+    for n in _NAMES:
+        out["w" + n], out["b" + n] = d[n]
+    return out
+
+
+def mha_bwd(xq: np.ndarray, xkv: np.ndarray, w, heads: int, dy: np.ndarray,
+            allow: Optional[np.ndarray] = None):
+    """Gradient of ptdit_oracle.mha(xq, xkv, w, heads, allow) for the output
+    gradient dy: the output projection's linear-map gradient, the attention
+    core's (attention_bwd), then the three input projections'. Returns
+    (dxq, dxkv, grads) with grads = {"wq", "bq", ..., "wo", "bo"}."""
+    from .ptdit_oracle import attention, linear
+    q = linear(xq, w["wq"], w.get("bq"))
+    k = linear(xkv, w["wk"], w.get("bk"))
+    v = linear(xkv, w["wv"], w.get("bv"))
+    o = attention(q, k, v, heads, allow)
+    do, dwo, dbo = linear_bwd(o, w["wo"], dy)
+    dq, dk, dv = attention_bwd(q, k, v, do, heads, allow)
+    dxq, dwq, dbq = linear_bwd(xq, w["wq"], dq)
+    dxk, dwk, dbk = linear_bwd(xkv, w["wk"], dk)
+    dxv, dwv, dbv = linear_bwd(xkv, w["wv"], dv)
+    return dxq, dxk + dxv, _grads({"q": (dwq, dbq), "k": (dwk, dbk), "v": (dwv, dbv), "o": (dwo, dbo)})
+
+
+def window_mha_bwd(x: np.ndarray, grid: Grid, win: Sequence[int], shift: Sequence[int], w, heads: int,
+                   dy: np.ndarray):
+    """Gradient of the WSA (shift 0) / SWSA branch without its residual,
+    Lin(window_core(Lin_q(x), Lin_k(x), Lin_v(x)); W_o, b_o), for the output
+    gradient dy. Pad keys/values are the biases (reading R-bwd-pad): their
+    slots' gradient sums add to d b_k, d b_v. Returns (dx, grads)."""
+    from .ptdit_oracle import linear
+    D = _f64(x).shape[-1]
+    zero = np.zeros(D)
+    bk = w.get("bk") if w.get("bk") is not None else zero
+    bv = w.get("bv") if w.get("bv") is not None else zero
+    q = linear(x, w["wq"], w.get("bq"))
+    k = linear(x, w["wk"], w.get("bk"))
+    v = linear(x, w["wv"], w.get("bv"))
+    o = window_core(q, k, v, grid, win, shift, heads, bk, bv)
+    do, dwo, dbo = linear_bwd(o, w["wo"], dy)
+    dq, dk, dv, dkpad, dvpad = window_core_bwd(q, k, v, do, grid, win, shift, heads, bk, bv)
+    dxq, dwq, dbq = linear_bwd(x, w["wq"], dq)
+    dxk, dwk, dbk = linear_bwd(x, w["wk"], dk)
+    dxv, dwv, dbv = linear_bwd(x, w["wv"], dv)
+    return dxq + dxk + dxv, _grads({"q": (dwq, dbq), "k": (dwk, dbk + dkpad), "v": (dwv, dbv + dvpad),
+                                    "o": (dwo, dbo)})
+
+
+def block_bwd(x: np.ndarray, grid: Grid, p: Sequence[int], win: Sequence[int], shift: Sequence[int],
+              weights, heads: int, dout: np.ndarray, pool: str = "f64"):
+    """Gradient of <block(x, ...)["x3"], dout> (reading R-bwd-block).
+
+    weights = [proxy SA, cross-attention, WSA, SWSA] as for block(); the
+    forward is recomputed with the same `pool` choice. Returns {"dx": [B, N, D],
+    "weights": [grads of the proxy SA, cross-attention, WSA, SWSA]}, each a
+    dict of "wq", "bq", "wk", "bk", "wv", "bv", "wo", "bo"; plus the
+    intermediate gradients "dx2", "dx1", "dP2", "dP" (of x2, x1, P', P)."""
+    from .ptdit_oracle import block
+    f = block(x, grid, p, win, shift, weights, heads, pool=pool)
+    dx3 = _f64(dout)
+    dsw, g_swsa = window_mha_bwd(f["x2"], grid, win, shift, weights[3], heads, dx3)
+    dx2 = dx3 + dsw                                   # x3 = x2 + SWSA(x2)
+    dw, g_wsa = window_mha_bwd(f["x1"], grid, win, (0, 0, 0), weights[2], heads, dx2)
+    dx1 = dx2 + dw                                    # x2 = x1 + WSA(x1)
+    dxq, dP2, g_cross = mha_bwd(x, f["P2"], weights[1], heads, dx1)   # x1 = x + CS(x, P')
+    dPq, dPkv, g_sa = mha_bwd(f["P"], f["P"], weights[0], heads, dP2)  # P' = P + SA(P)
+    dP = dP2 + dPq + dPkv
+    dx = dx1 + dxq + proxy_pool_bwd(dP, grid, p)      # P = Averaging(x)
+    return {"dx": dx, "weights": [g_sa, g_cross, g_wsa, g_swsa], "dx2": dx2, "dx1": dx1, "dP2": dP2, "dP": dP}
