@@ -31,7 +31,9 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_window_sa", "ptdit_shift_window_sa", "ptdit_roll3d", "ptdit_workspace_bytes",
             "ptdit_status_str", "ptdit_version", "ptdit_trace_enable", "ptdit_trace_read",
             "ptdit_trace_disable", "ptdit_window_attn_bwd", "ptdit_attn_bwd", "ptdit_attn_bwd_workspace_bytes",
-            "ptdit_proxy_pool_bwd", "ptdit_linear_bwd", "ptdit_linear_bwd_workspace_bytes"]
+            "ptdit_proxy_pool_bwd", "ptdit_linear_bwd", "ptdit_linear_bwd_workspace_bytes",
+            "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
+            "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32"]
 
 
 class Grid(ctypes.Structure):
@@ -95,6 +97,13 @@ def load() -> ctypes.CDLL:
         "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
         "ptdit_linear_bwd": [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp],
         "ptdit_linear_bwd_workspace_bytes": [i64, i32, i32],
+        "ptdit_linear_heads": [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp],
+        "ptdit_window_attn": [vp, vp, i32, G, W3, W3, vp, vp],
+        "ptdit_attn": [vp, i64, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp],
+        "ptdit_attn_workspace_bytes": [i32, i32, i32, i32],
+        "ptdit_heads_to_tokens": [vp, i32, i32, i32, i32, i32, vp, vp],
+        "ptdit_f32_to_bf16": [vp, i64, vp, vp],
+        "ptdit_add_f32": [vp, vp, i64, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -103,6 +112,7 @@ def load() -> ctypes.CDLL:
     lib.ptdit_workspace_bytes.restype = sz
     lib.ptdit_attn_bwd_workspace_bytes.restype = sz
     lib.ptdit_linear_bwd_workspace_bytes.restype = sz
+    lib.ptdit_attn_workspace_bytes.restype = sz
     lib.ptdit_status_str.restype = ctypes.c_char_p
     lib.ptdit_version.restype = ctypes.c_char_p
     lib.ptdit_trace_disable.restype = None
@@ -470,10 +480,13 @@ def _bhld(t: torch.Tensor, name: str) -> int:
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
-             ws: Optional[torch.Tensor] = None):
+             ws: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
     """Backward of the unmasked attention core (proxy SA, cross-attention).
     q [B, heads, Nq, dh], k / v [B, heads, Nk, dh] (views into fused buffers
-    allowed), d_o [B, Nq, heads*dh]. Returns fp32 (dq, dk, dv), contiguous."""
+    allowed), d_o [B, Nq, heads*dh]. Returns fp32 (dq, dk, dv): new contiguous
+    tensors, or the given fp32 views (each batch item a contiguous [heads, L,
+    dh] block; dk and dv with one batch stride)."""
     lib = load()
     B, heads, Nq, dh = q.shape
     Nk = k.shape[2]
@@ -482,9 +495,18 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
     _numel(d_o, B * Nq * heads * dh, "d_o")
     if k.stride(0) != v.stride(0):
         raise ValueError("k and v must share their batch stride")
-    dq = torch.empty(B, heads, Nq, dh, dtype=torch.float32, device=q.device)
-    dk = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
-    dv = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
+    for t, n, name in ((dq, Nq, "dq"), (dk, Nk, "dk"), (dv, Nk, "dv")):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, heads, n, dh)):
+            raise ValueError(f"{name} must be fp32 [{B}, {heads}, {n}, {dh}]")
+    if dq is None:
+        dq = torch.empty(B, heads, Nq, dh, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
+    dq_bs, dk_bs, dv_bs = _bhld(dq, "dq"), _bhld(dk, "dk"), _bhld(dv, "dv")
+    if dk_bs != dv_bs:
+        raise ValueError("dk and dv must share their batch stride")
     need = int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh))
     ws = _ws(need, ws, q.device)
     if len({q.dtype, k.dtype, v.dtype, d_o.dtype}) != 1:
@@ -492,7 +514,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
     q_bs, kv_bs = _bhld(q, "q"), _bhld(k, "k")
     _bhld(v, "v")
     st = lib.ptdit_attn_bwd(q.data_ptr(), q_bs, k.data_ptr(), v.data_ptr(), kv_bs, _ptr(d_o), _dt(q.dtype),
-                            B, heads, Nq, Nk, dh, _ptr(dq), heads * Nq * dh, _ptr(dk), _ptr(dv), heads * Nk * dh,
+                            B, heads, Nq, Nk, dh, dq.data_ptr(), dq_bs, dk.data_ptr(), dv.data_ptr(), dk_bs,
                             _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check("ptdit_attn_bwd", st)
     return dq, dk, dv
@@ -514,9 +536,11 @@ def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int
 
 
 def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: bool = True, want_dw: bool = True,
-               want_db: bool = True, ws: Optional[torch.Tensor] = None):
+               want_db: bool = True, ws: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+               dw: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None):
     """Gradients of Y = X W^T + b: x [..., d_in], w [d_out, d_in] bf16, d_y [..., d_out].
-    Returns fp32 (d_x or None, d_w or None, d_b or None)."""
+    Returns fp32 (d_x or None, d_w or None, d_b or None): new tensors, or the
+    given contiguous fp32 ones (e.g. row blocks of a larger gradient)."""
     lib = load()
     d_in, d_out = x.shape[-1], w.shape[0]
     rows = x.numel() // d_in
@@ -526,9 +550,16 @@ def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: boo
         raise ValueError(f"w must be [d_out, {d_in}]")
     _numel(d_y, rows * d_out, "d_y")
     dev = x.device
-    dx = torch.empty(*x.shape[:-1], d_in, dtype=torch.float32, device=dev) if want_dx else None
-    dw = torch.empty(d_out, d_in, dtype=torch.float32, device=dev) if want_dw else None
-    db = torch.empty(d_out, dtype=torch.float32, device=dev) if want_db else None
+    for t, n, name in ((dx, rows * d_in, "dx"), (dw, d_out * d_in, "dw"), (db, d_out, "db")):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be fp32")
+        _numel(t, n, name)
+    if dx is None and want_dx:
+        dx = torch.empty(*x.shape[:-1], d_in, dtype=torch.float32, device=dev)
+    if dw is None and want_dw:
+        dw = torch.empty(d_out, d_in, dtype=torch.float32, device=dev)
+    if db is None and want_db:
+        db = torch.empty(d_out, dtype=torch.float32, device=dev)
     need = int(lib.ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out))
     ws = _ws(need, ws, dev)
     st = lib.ptdit_linear_bwd(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(d_y), _dt(d_y.dtype),
@@ -549,3 +580,103 @@ def trace_read(max_n: int) -> list:
 
 def trace_disable() -> None:
     load().ptdit_trace_disable()
+
+
+# ----------------------------------------------------------------------------- recompute / chaining
+
+def linear_heads(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], B: int, Ntok: int, heads: int,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B*Ntok, D] -> y = x W^T + b head-major [B, G, heads, Ntok, D/heads] (G = rows(w) / D)."""
+    lib = load()
+    D = x.shape[-1]
+    if w.shape[1] != D or w.shape[0] % D:
+        raise ValueError(f"w must be [G*{D}, {D}]")
+    G = w.shape[0] // D
+    _numel(x, B * Ntok * D, "x")
+    _numel(b, G * D, "b")
+    _numel(out, B * Ntok * G * D, "out")
+    if out is None:
+        out = torch.empty(B, G, heads, Ntok, D // heads, dtype=w.dtype, device=x.device)
+    st = lib.ptdit_linear_heads(_ptr(x), _dt(x.dtype), B, Ntok, D, G, heads, _ptr(w), _ptr(b), _ptr(out),
+                                _dt(w.dtype), _stream())
+    _check("ptdit_linear_heads", st)
+    return out
+
+
+def window_attn(qkv: torch.Tensor, b_qkv: Optional[torch.Tensor], grid: Sequence[int], win: Sequence[int],
+                shift: Sequence[int] = (0, 0, 0), out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Window / shifted-window attention core on head-major qkv [B, 3, heads, N, dh] -> O [B, N, D]."""
+    lib = load()
+    B, F, H, W, D, heads = grid
+    N = F * H * W
+    _numel(qkv, B * 3 * N * D, "qkv")
+    _numel(b_qkv, 3 * D, "b_qkv")
+    _numel(out, B * N * D, "out")
+    if out is None:
+        out = torch.empty(B, N, D, dtype=qkv.dtype, device=qkv.device)
+    st = lib.ptdit_window_attn(_ptr(qkv), _ptr(b_qkv), _dt(qkv.dtype), Grid(*grid), Win3(*win), Win3(*shift),
+                               _ptr(out), _stream())
+    _check("ptdit_window_attn", st)
+    return out
+
+
+def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unmasked attention core: q [B, heads, Nq, dh], k / v [B, heads, Nk, dh] (views into
+    fused buffers allowed) -> O [B, Nq, heads*dh]."""
+    lib = load()
+    B, heads, Nq, dh = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, heads, Nk, dh) or tuple(v.shape) != tuple(k.shape) or k.stride(0) != v.stride(0):
+        raise ValueError("k and v must both be [B, heads, Nk, dh] with one batch stride")
+    if len({q.dtype, k.dtype, v.dtype}) != 1:
+        raise ValueError("q, k and v must share one dtype")
+    q_bs, kv_bs = _bhld(q, "q"), _bhld(k, "k")
+    _bhld(v, "v")
+    _numel(out, B * Nq * heads * dh, "out")
+    if out is None:
+        out = torch.empty(B, Nq, heads * dh, dtype=q.dtype, device=q.device)
+    need = int(lib.ptdit_attn_workspace_bytes(B, heads, Nk, _dt(q.dtype)))
+    ws = _ws(need, ws, q.device) if need else None
+    st = lib.ptdit_attn(q.data_ptr(), q_bs, k.data_ptr(), v.data_ptr(), kv_bs, _dt(q.dtype), B, heads, Nq, Nk, dh,
+                        _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check("ptdit_attn", st)
+    return out
+
+
+def heads_to_tokens(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 [B, G, heads, Ntok, dh] -> [B, Ntok, G*heads*dh]."""
+    lib = load()
+    B, G, heads, Ntok, dh = src.shape
+    if src.dtype != torch.float32:
+        raise ValueError("heads_to_tokens moves fp32 gradients")
+    _numel(out, src.numel(), "out")
+    if out is None:
+        out = torch.empty(B, Ntok, G * heads * dh, dtype=torch.float32, device=src.device)
+    _check("ptdit_heads_to_tokens",
+           lib.ptdit_heads_to_tokens(_ptr(src), B, G, heads, Ntok, dh, _ptr(out), _stream()))
+    return out
+
+
+def f32_to_bf16(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load()
+    if src.dtype != torch.float32:
+        raise ValueError("f32_to_bf16 reads fp32")
+    _numel(out, src.numel(), "out")
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    _check("ptdit_f32_to_bf16", lib.ptdit_f32_to_bf16(_ptr(src), src.numel(), _ptr(out), _stream()))
+    return out
+
+
+def add_f32(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = a + b (fp32, element-wise; out may be a or b)."""
+    lib = load()
+    if a.dtype != torch.float32 or b.dtype != torch.float32:
+        raise ValueError("add_f32 adds fp32 tensors")
+    _numel(b, a.numel(), "b")
+    _numel(out, a.numel(), "out")
+    if out is None:
+        out = torch.empty_like(a)
+    _check("ptdit_add_f32", lib.ptdit_add_f32(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream()))
+    return out

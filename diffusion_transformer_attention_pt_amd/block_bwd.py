@@ -1,0 +1,144 @@
+"""Backward of the PT-block attention core as a chain of C-ABI calls.
+
+The gradient of <x3, dout> with respect to the block input x and the 32
+weight and bias tensors of its four attentions (Qihoo-T2X reading note,
+section 3, Eq. GIIM and Eq. TCM, in the order of the code-correspondence
+excerpt of the PT-Block forward; the pages train at 2048^2, section 4). The
+calls run in reverse order of the forward:
+
+    x3 = x2 + SWSA(x2)   ->  dx2 = dout + dSWSA/dx2^T dout
+    x2 = x1 + WSA(x1)    ->  dx1 = dx2 + dWSA/dx1^T dx2
+    x1 = x + CS(x, P')   ->  dx  = dx1 + dCS/dx^T dx1,   dP' = dCS/dP'^T dx1
+    P' = P + SA(P)       ->  dP  = dP' + dSA/dP^T dP'
+    P  = Averaging(x)    ->  dx += Averaging^T dP
+
+Each attention's backward recomputes its head-major Q/K/V
+(ptdit_linear_heads) and attention output (ptdit_window_attn / ptdit_attn)
+from the block's stored inputs, then takes the output projection's gradient
+(ptdit_linear_bwd), the core's (ptdit_window_attn_bwd / ptdit_attn_bwd, on a
+bf16 dO from ptdit_f32_to_bf16), and the input projections' (ptdit_linear_bwd
+on the token-major dQ/dK/dV from ptdit_heads_to_tokens); residual branches
+join with ptdit_add_f32 and the window average's gradient accumulates into dx
+(ptdit_proxy_pool_bwd). Every step runs in the library's kernels; torch only
+holds the buffers. bf16 precision blocks with window-average proxies.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import torch
+
+from . import _lib
+from .block import PTBlockAttention
+
+
+class PTBlockBackward:
+    def __init__(self, blk: PTBlockAttention):
+        if blk.prec != torch.bfloat16:
+            raise ValueError("the block backward runs on bf16 blocks (bf16 matrix-core gradient kernels)")
+        if blk.proxy_mode != "mean" or blk.full:
+            raise ValueError("the block backward covers the attention core with window-average proxies")
+        self.blk = blk
+        B, N, M, D, heads = blk.B, blk.N, blk.M, blk.D, blk.heads
+        dh = D // heads
+        dev = blk.device
+        bf, f32 = torch.bfloat16, torch.float32
+        e = lambda *s, dt=f32: torch.empty(*s, dtype=dt, device=dev)
+        self.pads = any(g % w for g, w in zip((blk.F, blk.H, blk.W), blk.win))
+        # token-row buffers (shared by both window attentions)
+        self.qkv = e(B, 3, heads, N, dh, dt=bf)
+        self.o = e(B, N, D, dt=bf)
+        self.do16 = e(B, N, D, dt=bf)
+        self.dqkv_h = e(B, 3, heads, N, dh)
+        self.dqkv_t = e(B, N, 3 * D)
+        self.dbkv = e(2, D)
+        self.dx2, self.dx1, self.dx = e(B, N, D), e(B, N, D), e(B, N, D)
+        # cross-attention and proxy buffers
+        self.q = e(B, 1, heads, N, dh, dt=bf)
+        self.kv = e(B, 2, heads, M, dh, dt=bf)
+        self.dkv_h = e(B, 2, heads, M, dh)
+        self.dkv_t = e(B, M, 2 * D)
+        self.qkvp = e(B, 3, heads, M, dh, dt=bf)
+        self.op = e(B, M, D, dt=bf)
+        self.dop16 = e(B, M, D, dt=bf)
+        self.dqkvp_h = e(B, 3, heads, M, dh)
+        self.dqkvp_t = e(B, M, 3 * D)
+        self.dP = e(B, M, D)
+        lib = _lib.load()
+        need = max(int(lib.ptdit_linear_bwd_workspace_bytes(B * N, D, 3 * D)),
+                   int(lib.ptdit_linear_bwd_workspace_bytes(B * M, D, 3 * D)),
+                   int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, N, M, dh)),
+                   int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, M, M, dh)))
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def _window(self, xl: torch.Tensor, w: _lib.AttnWeights, shift, dy: torch.Tensor, dx_out: torch.Tensor):
+        """One window attention's backward: returns its weight gradients and
+        writes dx_out = dy + d(branch)/dx^T dy."""
+        blk = self.blk
+        B, N, D, heads = blk.B, blk.N, blk.D, blk.heads
+        _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=self.qkv)
+        _lib.window_attn(self.qkv, w.b_qkv, blk.g, blk.win, shift, out=self.o)
+        do32, dwo, dbo = _lib.linear_bwd(self.o, w.w_o, dy, ws=self.ws)
+        _lib.f32_to_bf16(do32, out=self.do16)
+        if self.pads:
+            self.dbkv.zero_()
+        _lib.window_attn_bwd(self.qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_h,
+                             d_b_kv=self.dbkv if self.pads else None)
+        _lib.heads_to_tokens(self.dqkv_h, out=self.dqkv_t)
+        dxb, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t, ws=self.ws)
+        if self.pads:   # pad slots' key/value gradients reach b_k, b_v
+            _lib.add_f32(dbqkv[D:], self.dbkv.view(-1), out=dbqkv[D:])
+        _lib.add_f32(dy, dxb, out=dx_out)
+        return {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor) -> Dict[str, object]:
+        """Gradients after blk.forward(x) (whose intermediates it reads).
+        dout: fp32 [B, N, D]. Returns {"dx": fp32 [B, N, D], "weights": [per
+        attention (proxy SA, cross, WSA, SWSA) {"w_qkv", "b_qkv", "w_o",
+        "b_o"}]} (all fp32)."""
+        blk = self.blk
+        B, N, M, D, heads = blk.B, blk.N, blk.M, blk.D, blk.heads
+        w = blk.weights
+        if dout.dtype != torch.float32 or not dout.is_contiguous():
+            raise ValueError("dout must be a contiguous fp32 tensor")
+        grads: List[dict] = [None] * 4
+        grads[3] = self._window(blk.x2_lowp, w[3], blk.shift, dout, self.dx2)
+        grads[2] = self._window(blk.x1_lowp, w[2], (0, 0, 0), self.dx2, self.dx1)
+        # cross-attention: tokens are queries, the attended proxies P' keys/values
+        wc = w[1]
+        _lib.linear_heads(x.view(B * N, D), wc.w_qkv[:D], wc.b_qkv[:D] if wc.b_qkv is not None else None,
+                          B, N, heads, out=self.q)
+        _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
+                          B, M, heads, out=self.kv)
+        _lib.attn(self.q[:, 0], self.kv[:, 0], self.kv[:, 1], out=self.o)
+        do32, dwo, dbo = _lib.linear_bwd(self.o, wc.w_o, self.dx1, ws=self.ws)
+        _lib.f32_to_bf16(do32, out=self.do16)
+        # dQ into the (now free) window buffers: [B, 1, heads, N, dh] and its
+        # token-major [B, N, D]
+        dq_h = self.dqkv_h.view(-1)[:B * N * D].view(B, 1, heads, N, D // heads)
+        dq_t = self.dqkv_t.view(-1)[:B * N * D].view(B, N, D)
+        _lib.attn_bwd(self.q[:, 0], self.kv[:, 0], self.kv[:, 1], self.do16, ws=self.ws,
+                      dq=dq_h[:, 0], dk=self.dkv_h[:, 0], dv=self.dkv_h[:, 1])
+        _lib.heads_to_tokens(dq_h, out=dq_t)
+        dwqkv = torch.empty(3 * D, D, dtype=torch.float32, device=x.device)
+        dbqkv = torch.empty(3 * D, dtype=torch.float32, device=x.device)
+        dxq, _, _ = _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dw=dwqkv[:D], db=dbqkv[:D])
+        _lib.heads_to_tokens(self.dkv_h, out=self.dkv_t)
+        dP2, _, _ = _lib.linear_bwd(blk.P2, wc.w_qkv[D:], self.dkv_t, ws=self.ws, dw=dwqkv[D:], db=dbqkv[D:])
+        grads[1] = {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
+        _lib.add_f32(self.dx1, dxq, out=self.dx)
+        # proxy self-attention on P (queries = keys = proxies)
+        wp = w[0]
+        _lib.linear_heads(blk.P.view(B * M, D), wp.w_qkv, wp.b_qkv, B, M, heads, out=self.qkvp)
+        _lib.attn(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], out=self.op)
+        dop32, dwo0, dbo0 = _lib.linear_bwd(self.op, wp.w_o, dP2, ws=self.ws)
+        _lib.f32_to_bf16(dop32, out=self.dop16)
+        _lib.attn_bwd(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], self.dop16, ws=self.ws,
+                      dq=self.dqkvp_h[:, 0], dk=self.dqkvp_h[:, 1], dv=self.dqkvp_h[:, 2])
+        _lib.heads_to_tokens(self.dqkvp_h, out=self.dqkvp_t)
+        dPx, dwqkv0, dbqkv0 = _lib.linear_bwd(blk.P, wp.w_qkv, self.dqkvp_t, ws=self.ws)
+        grads[0] = {"w_qkv": dwqkv0, "b_qkv": dbqkv0, "w_o": dwo0, "b_o": dbo0}
+        _lib.add_f32(dP2, dPx, out=self.dP)
+        # window average: every token of a window receives dP / P
+        _lib.proxy_pool_bwd(self.dP, blk.g, blk.p, d_x=self.dx, accumulate=True)
+        return {"dx": self.dx, "weights": grads}

@@ -55,6 +55,25 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Do n batch blocks {a + i*sa, la bytes} and n blocks {b + j*sb, lb bytes}
+// (i, j < n) share a byte? Exact for equal strides no shorter than the
+// blocks (views of one fused [B][G][...] buffer interleave without
+// overlapping); otherwise the whole extents are compared.
+bool overlaps_strided(const void* a, int64_t sa, int64_t la, const void* b, int64_t sb, int64_t lb, int64_t n) {
+  if (!a || !b || la <= 0 || lb <= 0 || n <= 0) return false;
+  if (sa != sb || sa < la || sa < lb || n == 1)
+    return overlaps(a, (size_t)((n - 1) * sa + la), b, (size_t)((n - 1) * sb + lb));
+  const int64_t s = sa, d = (int64_t)((intptr_t)b - (intptr_t)a);
+  // block j of b meets block i of a iff -lb < d + (j - i) s < la
+  const int64_t kmin = std::max<int64_t>(floor_div(-lb - d, s) + 1, -(n - 1));
+  const int64_t kmax = std::min<int64_t>(floor_div(la - d - 1, s), n - 1);
+  return kmin <= kmax;
+}
+
 ptdit_status check_common(int64_t B, int64_t D, int64_t heads) {
   if (B < 0 || B > 65535 || D <= 0 || heads <= 0 || heads > 65535) return PTDIT_ERR_SHAPE;
   if (D % heads != 0) return PTDIT_ERR_SHAPE;
@@ -618,18 +637,22 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
     return PTDIT_ERR_ALIGN;
   const size_t need = ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
-  const size_t es = esize(dt);
-  const size_t qb = ((B - 1) * q_bstride + hq) * es, kb = ((B - 1) * kv_bstride + hk) * es;
-  const size_t ob = (size_t)B * Nq * heads * dh * es;
-  const size_t dqb = ((B - 1) * dq_bstride + hq) * 4, dkb = ((B - 1) * dkv_bstride + hk) * 4;
-  const void* outs[4] = {d_q, d_k, d_v, ws};
-  const size_t osz[4] = {dqb, dkb, dkb, need};
+  // every operand as B batch blocks (stride, bytes); d_o and ws are one block
+  const int64_t es = (int64_t)esize(dt);
+  struct Blk { const void* p; int64_t stride, len, n; };
+  const Blk ins[4] = {{q, q_bstride * es, hq * es, B}, {k, kv_bstride * es, hk * es, B},
+                      {v, kv_bstride * es, hk * es, B}, {d_o, 0, (int64_t)B * Nq * heads * dh * es, 1}};
+  const Blk outs[4] = {{d_q, dq_bstride * 4, hq * 4, B}, {d_k, dkv_bstride * 4, hk * 4, B},
+                       {d_v, dkv_bstride * 4, hk * 4, B}, {ws, 0, (int64_t)need, 1}};
+  auto meet = [](const Blk& x, const Blk& y) {
+    if (x.n == y.n) return overlaps_strided(x.p, x.stride, x.len, y.p, y.stride, y.len, x.n);
+    return overlaps(x.p, (size_t)((x.n - 1) * x.stride + x.len), y.p, (size_t)((y.n - 1) * y.stride + y.len));
+  };
   for (int a = 0; a < 4; ++a) {
-    if (overlaps(outs[a], osz[a], q, qb) || overlaps(outs[a], osz[a], k, kb) || overlaps(outs[a], osz[a], v, kb) ||
-        overlaps(outs[a], osz[a], d_o, ob))
-      return PTDIT_ERR_ALIAS;
+    for (int c = 0; c < 4; ++c)
+      if (meet(outs[a], ins[c])) return PTDIT_ERR_ALIAS;
     for (int c = a + 1; c < 4; ++c)
-      if (overlaps(outs[a], osz[a], outs[c], osz[c])) return PTDIT_ERR_ALIAS;
+      if (meet(outs[a], outs[c])) return PTDIT_ERR_ALIAS;
   }
   DenseBwdDesc d;
   d.q = q; d.k = k; d.v = v; d.dO = d_o;
@@ -643,6 +666,119 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
   d.scale = 1.0f / std::sqrt((float)dh);
   TraceScope ts(PTDIT_K_BWD_DENSE, stream);
   return hip_status(launch_dense_bwd(d, dt == PTDIT_F32, stream));
+}
+
+// ------------------------------------------------------------------ recompute and chaining calls
+ptdit_status ptdit_linear_heads(const void* x, ptdit_dtype x_dt, int32_t B, int32_t Ntok, int32_t D,
+                                int32_t groups, int32_t heads, const void* w, const void* b, void* y,
+                                ptdit_dtype prec, hipStream_t stream) {
+  if (!valid_dtype(prec) || !valid_dtype(x_dt)) return PTDIT_ERR_DTYPE;
+  if (prec == PTDIT_F32 && x_dt != PTDIT_F32) return PTDIT_ERR_DTYPE;
+  ptdit_status st = check_common(B, D, heads);
+  if (st) return st;
+  if (Ntok < 0 || groups < 1 || groups > 3) return PTDIT_ERR_SHAPE;
+  const int64_t rows = (int64_t)B * Ntok;
+  if (rows == 0) return PTDIT_OK;
+  if (!x || !w || !y) return PTDIT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(b) || !aligned16(y)) return PTDIT_ERR_ALIGN;
+  if (overlaps(y, rows * groups * D * esize(prec), x, rows * D * esize(x_dt))) return PTDIT_ERR_ALIAS;
+  return hip_status(gemm(prec, x, x_dt, rows, D, groups * D, w, b, nullptr, prec, y, prec, true, Ntok, heads, D,
+                         PTDIT_K_GEMM_QKV, stream));
+}
+
+ptdit_status ptdit_window_attn(const void* qkv, const void* b_qkv, ptdit_dtype dt, ptdit_grid g, ptdit_win3 win,
+                               ptdit_win3 shift, void* o, hipStream_t stream) {
+  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+  ptdit_status st = check_grid(g);
+  if (st) return st;
+  if (win.t <= 0 || win.h <= 0 || win.w <= 0 || (int64_t)win.t * win.h * win.w > 128) return PTDIT_ERR_SHAPE;
+  if (shift.t < 0 || shift.h < 0 || shift.w < 0 || shift.t >= win.t || shift.h >= win.h || shift.w >= win.w)
+    return PTDIT_ERR_SHAPE;
+  const int64_t N = (int64_t)g.F * g.H * g.W, rows = (int64_t)g.B * N;
+  if (rows == 0) return PTDIT_OK;
+  if (!qkv || !o) return PTDIT_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(b_qkv) || !aligned16(o)) return PTDIT_ERR_ALIGN;
+  const size_t es = esize(dt);
+  if (overlaps(o, rows * g.D * es, qkv, rows * 3 * g.D * es) || overlaps(o, rows * g.D * es, b_qkv, 3 * g.D * es))
+    return PTDIT_ERR_ALIAS;
+  WindowDesc wd;
+  wd.QKV = qkv; wd.bias_qkv = b_qkv; wd.O = o;
+  wd.B = g.B; wd.F = g.F; wd.H = g.H; wd.W = g.W; wd.D = g.D; wd.heads = g.heads; wd.dh = g.D / g.heads;
+  wd.wt = win.t; wd.wh = win.h; wd.ww = win.w;
+  wd.st = shift.t; wd.sh = shift.h; wd.sw = shift.w;
+  wd.Fp = (g.F + win.t - 1) / win.t * win.t;
+  wd.Hp = (g.H + win.h - 1) / win.h * win.h;
+  wd.Wp = (g.W + win.w - 1) / win.w * win.w;
+  wd.scale = 1.0f / std::sqrt((float)wd.dh);
+  TraceScope ts(PTDIT_K_ATTN_WINDOW, stream);
+  return hip_status(launch_window(wd, dt == PTDIT_F32, stream));
+}
+
+size_t ptdit_attn_workspace_bytes(int32_t B, int32_t heads, int32_t Nk, ptdit_dtype dt) {
+  if (B < 0 || heads <= 0 || Nk < 0 || !valid_dtype(dt)) return 0;
+  return dt == PTDIT_BF16 ? flash_vt_bytes(B, heads, Nk) : 0;
+}
+
+ptdit_status ptdit_attn(const void* q, int64_t q_bstride, const void* k, const void* v, int64_t kv_bstride,
+                        ptdit_dtype dt, int32_t B, int32_t heads, int32_t Nq, int32_t Nk, int32_t dh, void* o,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+  if (B < 0 || heads <= 0 || Nq < 0 || Nk < 0 || (dh != 64 && dh != 72)) return PTDIT_ERR_SHAPE;
+  if ((int64_t)B * heads > 65535 || Nq > (1 << 30) || (Nq > 0 && Nk == 0)) return PTDIT_ERR_SHAPE;
+  if ((int64_t)B * Nq == 0) return PTDIT_OK;
+  const int64_t hq = (int64_t)heads * Nq * dh, hk = (int64_t)heads * Nk * dh;
+  if (q_bstride < hq || kv_bstride < hk) return PTDIT_ERR_SHAPE;
+  if (!q || !k || !v || !o) return PTDIT_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(ws)) return PTDIT_ERR_ALIGN;
+  const size_t need = ptdit_attn_workspace_bytes(B, heads, Nk, dt);
+  if (need && (!ws || ws_bytes < need)) return PTDIT_ERR_WORKSPACE;
+  const size_t es = esize(dt);
+  const size_t qb = ((B - 1) * q_bstride + hq) * es, kb = ((B - 1) * kv_bstride + hk) * es;
+  const size_t ob = (size_t)B * Nq * heads * dh * es;
+  if (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, kb) || overlaps(o, ob, ws, need) ||
+      overlaps(ws, need, q, qb) || overlaps(ws, need, k, kb) || overlaps(ws, need, v, kb))
+    return PTDIT_ERR_ALIAS;
+  FlashDesc f;
+  f.Q = q; f.q_bs = q_bstride; f.q_hs = (int64_t)Nq * dh;
+  f.K = k; f.k_bs = kv_bstride; f.k_hs = (int64_t)Nk * dh;
+  f.V = v; f.v_bs = kv_bstride; f.v_hs = (int64_t)Nk * dh;
+  f.O = o; f.B = B; f.heads = heads; f.Nq = Nq; f.Nk = Nk; f.dh = dh; f.D = heads * dh;
+  f.scale = 1.0f / std::sqrt((float)dh);
+  if (need) { f.vt = ws; f.vt_bytes = need; }
+  TraceScope ts(PTDIT_K_ATTN_FLASH, stream);
+  return hip_status(launch_flash(f, dt == PTDIT_F32, stream));
+}
+
+ptdit_status ptdit_heads_to_tokens(const float* src, int32_t B, int32_t groups, int32_t heads, int32_t Ntok,
+                                   int32_t dh, float* dst, hipStream_t stream) {
+  if (B < 0 || groups < 1 || heads <= 0 || Ntok < 0 || dh <= 0 || dh % 4) return PTDIT_ERR_SHAPE;
+  const int64_t n = (int64_t)B * groups * heads * Ntok * dh;
+  if (n == 0) return PTDIT_OK;
+  if ((int64_t)B * Ntok * groups * heads * dh / 4 > ((int64_t)1 << 40)) return PTDIT_ERR_SHAPE;
+  if (!src || !dst) return PTDIT_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return PTDIT_ERR_ALIGN;
+  if (overlaps(src, n * 4, dst, n * 4)) return PTDIT_ERR_ALIAS;
+  return hip_status(launch_heads_to_tokens(src, dst, B, groups, heads, Ntok, dh, stream));
+}
+
+ptdit_status ptdit_f32_to_bf16(const float* src, int64_t n, void* dst, hipStream_t stream) {
+  if (n < 0 || n % 8) return PTDIT_ERR_SHAPE;
+  if (n == 0) return PTDIT_OK;
+  if (!src || !dst) return PTDIT_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return PTDIT_ERR_ALIGN;
+  if (overlaps(src, n * 4, dst, n * 2)) return PTDIT_ERR_ALIAS;
+  return hip_status(launch_f32_to_bf16(src, (uint16_t*)dst, n, stream));
+}
+
+ptdit_status ptdit_add_f32(const float* a, const float* b, int64_t n, float* out, hipStream_t stream) {
+  if (n < 0 || n % 4) return PTDIT_ERR_SHAPE;
+  if (n == 0) return PTDIT_OK;
+  if (!a || !b || !out) return PTDIT_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return PTDIT_ERR_ALIGN;
+  // out may be a or b exactly (element-wise), but not a shifted view of either
+  const size_t nb = n * 4;
+  if ((out != a && overlaps(out, nb, a, nb)) || (out != b && overlaps(out, nb, b, nb))) return PTDIT_ERR_ALIAS;
+  return hip_status(launch_add_f32(a, b, out, n, stream));
 }
 
 ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,

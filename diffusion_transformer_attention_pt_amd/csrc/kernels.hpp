@@ -91,6 +91,12 @@ struct WFusedDesc {
 bool wfused_supported(const WFusedDesc& d);
 hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s);
 
+// util.hip: chaining the backward calls
+hipError_t launch_heads_to_tokens(const float* src, float* dst, int B, int G, int heads, int Ntok, int dh,
+                                  hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);  // n % 8 == 0
+hipError_t launch_add_f32(const float* a, const float* b, float* out, int64_t n, hipStream_t s);  // n % 4 == 0
+
 // Backward pass of the attention core (fp32 gradients).
 struct WindowBwdDesc {
   const void* QKV; const void* bias_qkv; const void* dO;

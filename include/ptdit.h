@@ -324,7 +324,9 @@ ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const voi
  *   d_k, d_v batch b at + b*dkv_bstride: [heads][Nk][dh], fp32
  *   ws       ptdit_attn_bwd_workspace_bytes(...) bytes of device memory
  *   dh 64 or 72; B*heads <= 65535; every pointer 16-byte aligned; the
- *   outputs overlap neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS).
+ *   outputs overlap neither the inputs nor each other nor ws (PTDIT_ERR_ALIAS;
+ *   batch blocks with one stride are compared block by block, so d_q, d_k,
+ *   d_v may be interleaved views of one [B][3][heads][L][dh] gradient buffer).
  */
 ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
                             int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
@@ -366,6 +368,63 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
                               const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out);
+
+/*
+ * Calls that recompute forward intermediates and chain the backward calls
+ * into the gradient of a whole block (section 3, Eq. GIIM and Eq. TCM; the
+ * pages train at 2048^2, section 4). Errors as everywhere: host checks
+ * before any launch, outputs untouched on failure.
+ *
+ * ptdit_linear_heads -- y = x W^T + b with the output head-major: the Q, K
+ * and V maps of an attention module (module table) as the attention cores
+ * read them. x [B*Ntok][D] (x_dt); w [groups*D][D], b [groups*D] or NULL
+ * (prec); y [B][groups][heads][Ntok][D/heads] (prec). groups 1..3 (Q; K,V;
+ * Q,K,V); D/heads 64 or 72.
+ */
+ptdit_status ptdit_linear_heads(const void* x, ptdit_dtype x_dt, int32_t B, int32_t Ntok, int32_t D,
+                                int32_t groups, int32_t heads, const void* w, const void* b, void* y,
+                                ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_window_attn -- the attention core of ptdit_window_sa (shift 0) or
+ * ptdit_shift_window_sa on given head-major Q/K/V (Eq. TCM): the same
+ * padding (pad keys/values = b_k/b_v), roll and boundary mask.
+ *   qkv   [B][3][heads][N][dh] (dt);  b_qkv [3D] (dt) or NULL
+ *   o     [B][N][D] (dt): the attention output, the output projection's input
+ * Window 1..128 tokens, 0 <= shift < window per axis.
+ */
+ptdit_status ptdit_window_attn(const void* qkv, const void* b_qkv, ptdit_dtype dt, ptdit_grid g, ptdit_win3 win,
+                               ptdit_win3 shift, void* o, hipStream_t stream);
+
+/*
+ * ptdit_attn -- the unmasked attention core of ptdit_proxy_sa / ptdit_proxy_xattn
+ * (Eq. GIIM's SA and CS) on given head-major Q/K/V, addressed as for
+ * ptdit_attn_bwd (q + b*q_bstride: [heads][Nq][dh]; k, v + b*kv_bstride:
+ * [heads][Nk][dh]); o [B][Nq][heads*dh] (dt). ws: ptdit_attn_workspace_bytes
+ * bytes (bf16 with more than 512 keys; else 0 and ws may be NULL).
+ */
+ptdit_status ptdit_attn(const void* q, int64_t q_bstride, const void* k, const void* v, int64_t kv_bstride,
+                        ptdit_dtype dt, int32_t B, int32_t heads, int32_t Nq, int32_t Nk, int32_t dh, void* o,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+size_t ptdit_attn_workspace_bytes(int32_t B, int32_t heads, int32_t Nk, ptdit_dtype dt);
+
+/*
+ * ptdit_heads_to_tokens -- fp32 layout change dst[b][t][(g*heads + h)*dh + d]
+ * = src[b][g][h][t][d]: the attention backward's dQ/dK/dV as the
+ * token-major output gradient of a Q/K/V projection (ptdit_linear_bwd's d_y).
+ * dh % 4 == 0; src and dst 16-byte aligned and disjoint.
+ */
+ptdit_status ptdit_heads_to_tokens(const float* src, int32_t B, int32_t groups, int32_t heads, int32_t Ntok,
+                                   int32_t dh, float* dst, hipStream_t stream);
+
+/* ptdit_f32_to_bf16 -- dst[i] = bf16(src[i]), round to nearest even (the
+ * operand precision of the bf16 backward kernels); n % 8 == 0, disjoint. */
+ptdit_status ptdit_f32_to_bf16(const float* src, int64_t n, void* dst, hipStream_t stream);
+
+/* ptdit_add_f32 -- out[i] = a[i] + b[i] (fp32): a residual's gradient
+ * joining its branch's; n % 4 == 0; out may be a or b itself, not a shifted
+ * view of either (PTDIT_ERR_ALIAS). */
+ptdit_status ptdit_add_f32(const float* a, const float* b, int64_t n, float* out, hipStream_t stream);
 
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
  * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*

@@ -322,3 +322,52 @@ def test_binding_leaves_divisibility_to_the_library(lib):
     from diffusion_transformer_attention_pt_amd import _lib as L
     assert L._proxy_count((1, 1, 16, 16, 64, 1), (1, 5, 5)) is None
     assert L._proxy_count((2, 1, 16, 16, 64, 1), (1, 4, 4)) == 2 * 16 * 64
+
+
+def test_chaining_calls_validate_on_the_host(lib):
+    """Host checks of the recompute / chaining calls (nothing launched)."""
+    import ctypes
+    from diffusion_transformer_attention_pt_amd._lib import Grid, Win3
+    a, b = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 34)
+    assert lib.ptdit_add_f32(a, b, 6, a, None) == -2                          # n % 4
+    assert lib.ptdit_add_f32(a, b, 64, ctypes.c_void_p((1 << 30) + 16), None) == -8   # shifted view of a
+    assert lib.ptdit_add_f32(a, b, 64, ctypes.c_void_p((1 << 30) + 4), None) == -5    # misaligned
+    assert lib.ptdit_add_f32(None, b, 64, a, None) == -1
+    assert lib.ptdit_add_f32(a, b, 0, a, None) == 0
+    assert lib.ptdit_f32_to_bf16(a, 12, b, None) == -2                        # n % 8
+    assert lib.ptdit_f32_to_bf16(a, 64, ctypes.c_void_p((1 << 30) + 64), None) == -8
+    assert lib.ptdit_heads_to_tokens(a, 1, 3, 16, 100, 70, b, None) == -2    # dh % 4
+    assert lib.ptdit_heads_to_tokens(a, 1, 3, 16, 100, 72, a, None) == -8
+    g = Grid(1, 1, 16, 16, 1152, 16)
+    assert lib.ptdit_window_attn(a, None, 0, g, Win3(1, 8, 8), Win3(0, 8, 0), b, None) == -2   # shift >= window
+    assert lib.ptdit_window_attn(a, None, 0, g, Win3(1, 16, 16), Win3(0, 0, 0), b, None) == -2  # 256 tokens
+    assert lib.ptdit_window_attn(a, None, 0, g, Win3(1, 8, 8), Win3(0, 4, 4), a, None) == -8
+    assert lib.ptdit_attn(a, 16 * 100 * 80, a, a, 16 * 50 * 80, 0, 1, 16, 100, 50, 80, b, None, 0, None) == -2
+    assert lib.ptdit_attn(a, 16 * 100 * 72, a, a, 16 * 50 * 72, 0, 1, 16, 100, 0, 72, b, None, 0, None) == -2
+    assert lib.ptdit_attn(a, 16 * 2048 * 72, a, a, 16 * 600 * 72, 0, 1, 16, 2048, 600, 72, b, None, 0, None) == -6
+    assert lib.ptdit_attn_workspace_bytes(1, 16, 600, 0) > 0 and lib.ptdit_attn_workspace_bytes(1, 16, 600, 1) == 0
+    assert lib.ptdit_linear_heads(a, 0, 1, 100, 1152, 4, 16, b, None, ctypes.c_void_p(1 << 38), 0, None) == -2
+    assert lib.ptdit_linear_heads(a, 0, 1, 100, 1152, 3, 16, b, None, a, 0, None) == -8
+
+
+def test_attn_bwd_alias_check_is_exact_for_interleaved_batches(lib):
+    """d_q, d_k, d_v as interleaved views of one [B][3][heads][L][dh] fp32
+    buffer (batch stride 3*heads*L*dh) are accepted for B > 1; a d_k view
+    shifted by one element into d_q's block is refused (nothing launched:
+    the workspace is too small, which is checked after the alias rule only
+    when the rule passes)."""
+    import ctypes
+    B, heads, L, dh = 2, 16, 256, 72
+    hk = heads * L * dh
+    q = ctypes.c_void_p(1 << 30)
+    kv = ctypes.c_void_p(1 << 32)
+    base = 1 << 36
+    args = lambda dq, dk, dv: lib.ptdit_attn_bwd(q, hk, kv, ctypes.c_void_p((1 << 32) + hk * 2), 2 * hk,
+                                                 ctypes.c_void_p(1 << 34), 0, B, heads, L, L, dh,
+                                                 ctypes.c_void_p(dq), 3 * hk, ctypes.c_void_p(dk),
+                                                 ctypes.c_void_p(dv), 3 * hk, ctypes.c_void_p(1 << 40), 1 << 30,
+                                                 None)
+    # interleaved views: accepted by the alias rule; the call then needs a GPU,
+    # so only the refusals are exercised here
+    assert args(base, base + 4 * hk + 16, base + 8 * hk) == -8   # d_k overlaps d_v's block
+    assert args(base, base + 4 * hk - 16, base + 8 * hk) == -8   # d_k overlaps d_q's block

@@ -4,7 +4,7 @@ differences, torch autograd and adjoint identities): the attention cores, the
 window average, the roll and the projections' gradients.
 
 Bar (tests/gpu_util.py, grad_bar): relative-L2 1e-2 and max-abs 2e-2 scaled by
-max(1, RMS of the reference gradient) for every gradient;
+max(1, largest magnitude of the reference gradient) for every gradient;
 the non-accumulating pooling backward is an IEEE division by P and is compared
 bit for bit with the float64 result rounded to float32 (exact: a float64
 quotient rounded to float32 is the correctly rounded float32 quotient).
@@ -256,7 +256,7 @@ def test_linear_bwd_vs_oracle(P, case):
     rx, rw, rb = O.linear_bwd(x, w, dy)
     # the products take bf16 operands (an fp32 d_y or x is rounded, relative
     # error 2^-9 per term); d_w and d_b sum `rows` terms of size ~1, so their
-    # max-abs bar scales with their RMS (grad_bar)
+    # max-abs bar scales with their largest element (grad_bar)
     assert_grad_close(host(dx), rx, "dX")
     assert_grad_close(host(dw), rw, "dW")
     assert_grad_close(host(db), rb, "db")
