@@ -12,7 +12,10 @@ Prints ONE JSON line.
 
 The dominant kernel's roofline entry times every launch of that kernel inside
 the timed region with HIP events recorded on the launch stream (the library's
-kernel trace). Its HBM traffic comes from rocprofv3 counters stored in
+kernel trace). "ceilings" holds what this machine sustains (the library's
+calibration kernels: back-to-back bf16 MFMAs on registers, a streaming HBM
+read of 2 GiB and of 38 MB), and the *_measured_frac fields price against
+them beside the published peaks. Its HBM traffic comes from rocprofv3 counters stored in
 profiles/traffic.json, and is reported only while the kernel source still
 hashes to the value recorded with the counters.
 """
@@ -162,6 +165,32 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
                            + B * N * D * 4 + 3 * D * D * 4),
     }
     res = {}
+    # the whole block's backward (PTBlockBackward: every gradient of <x3,
+    # dout>), timed with events on the launch stream after one forward
+    if prec == torch.bfloat16:
+        from diffusion_transformer_attention_pt_amd import PTBlockBackward
+        from synth_inputs import make_x
+        xb = torch.from_numpy(make_x(wl)).to(prec).to(dev)
+        blk.forward(xb)
+        bwd = PTBlockBackward(blk)
+        dout = torch.randn(B, N, D, device=dev)
+        bwd.backward(xb, dout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            bwd.backward(xb, dout)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = blk.flops()
+        # algorithmic backward FLOP: every projection twice (dX, dW), every
+        # attention core's five products (2.5 times its two forward products);
+        # the recomputed forward projections and cores are not counted
+        bflop = 2 * fl["projection"] + 2.5 * fl["core"]
+        res["block_backward"] = {"avg_ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+                                 "gflop": round(bflop / 1e9, 2), "tflops": round(bflop / (ms * 1e-3) / 1e12, 2),
+                                 "peak_frac": round(bflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     for name, (cls, fn, flop, nbytes) in cases.items():
         fn()
         torch.cuda.synchronize()
@@ -200,8 +229,9 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="also time the attention-core backward kernels at the workload's shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="before the run, copy a 256 MiB buffer once (a plain copy kernel of known "
-                         "size, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+                    help="before the run, copy a 256 MiB buffer once with the library's plain copy "
+                         "kernel (copy_kernel: known size, used to scale rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE readings), then once with torch's copy for comparison")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this attention core is built and timed on a single "
@@ -219,7 +249,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
-        dst = torch.empty_like(src)
+        dst = torch.zeros_like(src)
+        _lib.calibrate_copy(src, dst)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
@@ -281,6 +312,7 @@ def main() -> int:
     dom_flop = 2 * rows * wl.D * 3 * wl.D + (4 * slots * L * wl.D if fused else 0)
     dom_avg_ms = statistics.mean(dom_ms) if dom_ms else float("nan")
     dom_tflops = dom_flop / (dom_avg_ms * 1e-3) / 1e12
+    es_name = "bf16" if prec == torch.bfloat16 else "fp32"
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
@@ -313,12 +345,19 @@ def main() -> int:
         "roofline": {"kernel": (f"wfused_kernel: Q/K/V projection [{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] "
                                 f"bf16 fused with {L}-token window attention -> attention output bf16"
                                 if fused else
-                                "gemm_pp_kernel: Q/K/V projection of the token rows "
-                                f"[{rows}x{wl.D}] bf16 x [{wl.D}x{3 * wl.D}] bf16 -> head-major bf16"),
+                                f"{'gemm_pp_kernel' if prec == torch.bfloat16 else 'gemm_f32_kernel'}: Q/K/V "
+                                f"projection of the token rows [{rows}x{wl.D}] {es_name} x [{wl.D}x{3 * wl.D}] "
+                                f"{es_name} -> head-major {es_name}"),
                      "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(dom_avg_ms, 5), "launches": len(dom_ms)},
     }
+    # on-box ceilings (calibration kernels), beside the published peaks
+    ceil = _lib.calibrate()
+    out["ceilings"] = ceil
+    if prec == torch.bfloat16:
+        out["roofline"]["frac_of_measured"] = round(dom_tflops / ceil["mfma_bf16_tflops"], 4)
+        out["mfma_measured_frac"] = round(tflops / ceil["mfma_bf16_tflops"], 4)
     if args.breakdown:
         names = {_lib.K_POOL: "pool", _lib.K_GEMM_PROXY: "gemm_proxy", _lib.K_GEMM_Q: "gemm_q",
                  _lib.K_ATTN_FLASH: "attn_flash", _lib.K_GEMM_OUT: "gemm_out",
@@ -365,6 +404,10 @@ def main() -> int:
             br[nm] = {"launches_per_step": len(ms) // 10, "avg_ms": round(statistics.mean(ms), 5) if ms else None,
                       "ms_per_step": round(sum(ms) / 10, 5), "achieved": round(rate, 1), "unit": unit,
                       "peak_frac": round(rate / pk, 4)}
+            mc = ceil["hbm_read_gbs"] if unit == "GB/s" else (ceil["mfma_bf16_tflops"] if prec == torch.bfloat16
+                                                               else None)
+            if mc:
+                br[nm]["measured_frac"] = round(rate / mc, 4)
         # cold pooling: rotate copies of x whose total exceeds the 256 MB
         # last-level cache, so every launch reads x from HBM
         xbytes = x.numel() * x.element_size()

@@ -33,7 +33,8 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_trace_disable", "ptdit_window_attn_bwd", "ptdit_attn_bwd", "ptdit_attn_bwd_workspace_bytes",
             "ptdit_proxy_pool_bwd", "ptdit_linear_bwd", "ptdit_linear_bwd_workspace_bytes",
             "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
-            "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32"]
+            "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
+            "ptdit_calibrate_read", "ptdit_calibrate_copy"]
 
 
 class Grid(ctypes.Structure):
@@ -104,6 +105,9 @@ def load() -> ctypes.CDLL:
         "ptdit_heads_to_tokens": [vp, i32, i32, i32, i32, i32, vp, vp],
         "ptdit_f32_to_bf16": [vp, i64, vp, vp],
         "ptdit_add_f32": [vp, vp, i64, vp, vp],
+        "ptdit_calibrate_mfma": [i32, i32, vp, ctypes.POINTER(ctypes.c_int64), vp],
+        "ptdit_calibrate_read": [vp, i64, i32, vp, vp],
+        "ptdit_calibrate_copy": [vp, vp, i64, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -680,3 +684,54 @@ def add_f32(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None
         out = torch.empty_like(a)
     _check("ptdit_add_f32", lib.ptdit_add_f32(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream()))
     return out
+
+
+def calibrate_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """dst <- src byte for byte with the library's plain copy kernel (the
+    known-size reference for hardware byte counters)."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("calibrate_copy takes contiguous device tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("calibrate_copy: src and dst sizes differ")
+    _check("ptdit_calibrate_copy", load().ptdit_calibrate_copy(_ptr(src), _ptr(dst), nbytes, _stream()))
+    return dst
+
+
+def calibrate(reps: int = 5) -> dict:
+    """On-box ceilings: the sustained bf16 MFMA rate (back-to-back MFMAs on
+    register operands over 1024 workgroups) and the streaming HBM read rate
+    of a 2 GiB buffer (beyond the 256 MB last-level cache) and of a 38 MB
+    one (the pooling kernel's size), each the best of `reps` event-timed runs
+    (the 38 MB one also over workgroup counts). The 38 MB reads rotate over
+    16 buffers written beforehand in the same order (613 MB in all), so each
+    timed read finds its buffer mapped but evicted from the last-level cache."""
+    lib = load()
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    flop = ctypes.c_int64(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    ms = best(lambda: _check("ptdit_calibrate_mfma",
+                             lib.ptdit_calibrate_mfma(1024, 20000, _ptr(out), ctypes.byref(flop), _stream())))
+    res = {"mfma_bf16_tflops": round(flop.value / (ms * 1e-3) / 1e12, 1)}
+    for name, nbytes, grids in (("hbm_read_gbs", 2 << 30, (2048,)), ("hbm_read_gbs_38mb", 38_338_560, (512, 1024, 2048))):
+        bufs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(1 if nbytes > (1 << 30) else 16)]
+        it = iter(range(1 << 30))
+        ms = min(best(lambda: _check("ptdit_calibrate_read",
+                                     lib.ptdit_calibrate_read(_ptr(bufs[next(it) % len(bufs)]), nbytes, nb, _ptr(out),
+                                                              _stream())))
+                 for nb in grids)
+        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        del bufs
+    return res

@@ -781,6 +781,32 @@ ptdit_status ptdit_add_f32(const float* a, const float* b, int64_t n, float* out
   return hip_status(launch_add_f32(a, b, out, n, stream));
 }
 
+// ------------------------------------------------------------------ calibration
+ptdit_status ptdit_calibrate_mfma(int32_t blocks, int32_t iters, float* out, int64_t* flop, hipStream_t stream) {
+  if (blocks <= 0 || blocks > 65535 || iters <= 0) return PTDIT_ERR_SHAPE;
+  if (!out || !flop) return PTDIT_ERR_NULL;
+  if (!aligned16(out)) return PTDIT_ERR_ALIGN;
+  *flop = calib_mfma_flop(blocks, iters);
+  return hip_status(launch_calib_mfma(blocks, iters, out, stream));
+}
+
+ptdit_status ptdit_calibrate_read(const void* buf, int64_t bytes, int32_t blocks, float* out, hipStream_t stream) {
+  if (bytes <= 0 || bytes % 16 || blocks <= 0 || blocks > 65535) return PTDIT_ERR_SHAPE;
+  if (!buf || !out) return PTDIT_ERR_NULL;
+  if (!aligned16(buf) || !aligned16(out)) return PTDIT_ERR_ALIGN;
+  if (overlaps(out, (size_t)blocks * 256 * 4, buf, (size_t)bytes)) return PTDIT_ERR_ALIAS;
+  return hip_status(launch_calib_read(buf, bytes, blocks, out, stream));
+}
+
+ptdit_status ptdit_calibrate_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16) return PTDIT_ERR_SHAPE;
+  if (bytes == 0) return PTDIT_OK;
+  if (!src || !dst) return PTDIT_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return PTDIT_ERR_ALIGN;
+  if (overlaps(dst, (size_t)bytes, src, (size_t)bytes)) return PTDIT_ERR_ALIAS;
+  return hip_status(launch_calib_copy(src, dst, bytes, stream));
+}
+
 ptdit_status ptdit_proxy_pool_bwd(const float* d_proxies, ptdit_grid g, ptdit_win3 p, float* d_x,
                                   int32_t accumulate, hipStream_t stream) {
   if (g.B < 0 || g.F < 0 || g.H < 0 || g.W < 0 || g.D <= 0 || g.D % 4) return PTDIT_ERR_SHAPE;

@@ -97,6 +97,12 @@ hipError_t launch_heads_to_tokens(const float* src, float* dst, int B, int G, in
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);  // n % 8 == 0
 hipError_t launch_add_f32(const float* a, const float* b, float* out, int64_t n, hipStream_t s);  // n % 4 == 0
 
+// calib.hip: on-box ceilings for the benchmark
+int64_t calib_mfma_flop(int blocks, int iters);
+hipError_t launch_calib_mfma(int blocks, int iters, float* out, hipStream_t s);
+hipError_t launch_calib_read(const void* buf, int64_t bytes, int blocks, float* out, hipStream_t s);
+hipError_t launch_calib_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 // Backward pass of the attention core (fp32 gradients).
 struct WindowBwdDesc {
   const void* QKV; const void* bias_qkv; const void* dO;

@@ -7,11 +7,13 @@
 // the zero-padded, rolled grid) and one pair of heads.
 //
 // Phase 1 projects the slots' tokens onto the Q, K and V columns of both
-// heads: 3 x 144 = 432 output columns, 27 column blocks of 16. It is the
-// ping-pong DMA-ring GEMM of gemm_pp_kernel (8 waves in two groups one phase
-// apart, a 4-slot ring of 32-wide k-slices fed by global_load_lds) on a
-// 128 x 448 tile: waves of 64 rows x 7 blocks, the 28th block a copy of the
-// first whose result is never used. The A rows are gathered through the
+// heads: 3 x 144 = 432 output columns, 27 column blocks of 16 (V's first,
+// then Q's and K's). It is the ping-pong DMA-ring GEMM of gemm_pp_kernel (8
+// waves in two groups one phase apart, a 4-slot ring of 32-wide k-slices fed
+// by global_load_lds) on a 128 x 448 tile: waves of 64 rows x 7 blocks, the
+// 28th block a copy of the first whose result is never used. V's blocks are
+// computed transposed (tokens as the first MFMA operand), which leaves each
+// lane 4 consecutive tokens of one channel, as the V^T staging wants them. The A rows are gathered through the
 // window map (roll and zero padding applied per row), so nothing is
 // materialised; rows of pad slots load any real row and are zeroed after the
 // contraction, which leaves their K and V equal to the biases.
@@ -25,6 +27,8 @@
 // reach HBM. The arithmetic is that of the unfused path (same k order in the
 // projection, same rounding to bf16, same attention steps), so both give the
 // same attention output.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -37,6 +41,10 @@ constexpr int WF_BM = 128;           // window slots per workgroup
 constexpr int WF_DH = 72;            // head width
 constexpr int WF_CPH = 2 * WF_DH;    // columns of one of Q/K/V for the head pair
 constexpr int WF_NWR = 3 * WF_CPH;   // W rows per tile (432)
+// LDS row pitch of staged Q / K / O (elements): 152 = 76 dwords, 12 mod 32
+// banks, so the 16 rows of a 16-byte fragment read fall in distinct banks
+// (a pitch of 144, 8 mod 32, repeats every 4 rows)
+constexpr int WF_QP = WF_CPH + 8;
 constexpr int WF_NBLK = WF_NWR / 16; // real column blocks (27)
 constexpr int WF_WM = 2, WF_WN = 4, WF_NW = 8;
 constexpr int WF_FM = WF_BM / WF_WM / 16;  // 4 row blocks per wave
@@ -50,7 +58,7 @@ static_assert(WF_WN * WF_FN == WF_NBLK + 1, "one spare column block");
 // staging of one window (both heads of the pair) in the drained ring (bytes)
 template <int L>
 struct WfStage {
-  static constexpr int QB = L * WF_CPH * 2;           // Q or K [L][144]
+  static constexpr int QB = L * WF_QP * 2;            // Q or K [L][144 + 8]
   static constexpr int VTP = L + 4;                   // V^T row pitch (elements)
   static constexpr int VB = WF_CPH * VTP * 2;         // V^T [144][L+4]
   // bytes per ring slot: Q and K of one window (L = 64) or two (L = 32), Q or
@@ -91,7 +99,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   __shared__ uint4 ring1[SLOT];
   __shared__ uint4 ring2[SLOT];
   __shared__ uint4 ring3[SLOT];
-  __shared__ int grow_s[WF_BM];  // global token row b*N + tok, or -1 (pad slot / past the grid)
+  __shared__ __attribute__((aligned(16))) int grow_s[WF_BM];  // global token row b*N + tok, or -1 (pad / past the grid)
   __shared__ __attribute__((aligned(16))) int lab_s[WF_BM];
   auto slot = [&](auto sI) -> uint4* {
     constexpr int sl = (decltype(sI)::value % 4 + 4) % 4;
@@ -101,25 +109,42 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     else return ring3;
   };
 
-  const int tid = threadIdx.x, lane = tid & 63;
+
+  // XCD-aware tile order: block i runs on XCD i % 8; each XCD walks a
+  // contiguous range of logical tiles. Logical tiles group GP head pairs
+  // (2 when the pair count is even) with every row tile, the pair index
+  // fastest: with 8 head pairs, two XCDs share a group, each takes half the
+  // row tiles, keeps the group's 864 weight rows (2 MB) in its L2 and reads
+  // each of its token rows once (the two pairs' workgroups of a row tile run
+  // side by side).
+  const int ntiles = p.row_tiles * p.head_pairs;
+  // persistent: workgroup b takes tiles b, b + grid, ... (one workgroup per
+  // CU, so a tile's output stores drain while the next tile's first slices
+  // load); b + k*grid keeps b's XCD (grid % 8 == 0)
+  for (int bid = blockIdx.x; bid < ntiles; bid += gridDim.x) {
+  // thread indices re-derived per tile from an opaque copy of the thread id:
+  // nothing tile-invariant is hoisted out of the loop and kept live across
+  // the main loop (which would spill)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // wm is the ping-pong group; SIMD wave % 4 holds one of each
   const int g = lane >> 4, lr = lane & 15;
-
-  // XCD-aware tile order: block i runs on XCD i % 8; each XCD walks a
-  // contiguous range of logical tiles, head pair major, so with 8 head pairs
-  // every XCD keeps one pair's 432 weight rows in its L2.
-  const int ntiles = p.row_tiles * p.head_pairs;
-  if ((int)blockIdx.x >= ntiles) return;
   int hp, rt;
   {
-    const int bid = blockIdx.x, q = ntiles >> 3, rem = ntiles & 7;
+    const int q = ntiles >> 3, rem = ntiles & 7;
     const int xcd = bid & 7, idx = bid >> 3;
     const int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-    hp = logical / p.row_tiles;
-    rt = logical - hp * p.row_tiles;
+    const int GP = (p.head_pairs & 1) ? 1 : 2;
+    const int grp = logical / (p.row_tiles * GP), in = logical - grp * p.row_tiles * GP;
+    rt = in / GP;
+    hp = grp * GP + (in - rt * GP);
   }
 
+  // the previous tile's last LDS reads (the output copy) are done before its
+  // maps and ring are overwritten
+  if (bid != (int)blockIdx.x) __syncthreads();
   // slot -> token map of the tile's rows (roll by -shift on the padded grid)
   if (tid < WF_BM) {
     const int s = rt * WF_BM + tid;
@@ -164,7 +189,8 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
       dst[i] = j * 64;
     } else {
       const int sl = (j - WF_IA) * 64 + lane, row = sl >> 2, pp = sl & 3;
-      const int gq = row / WF_CPH, cc = row - gq * WF_CPH;
+      const int tg = row / WF_CPH, cc = row - tg * WF_CPH;  // tile column groups: V, Q, K
+      const int gq = tg == 0 ? 2 : tg - 1;                    // row group of w_qkv
       const int wrow = gq * p.D + hp * WF_CPH + cc;
       voff[i] = (uint32_t)wrow * (uint32_t)(p.D * 2) + (uint32_t)((pp ^ ((row >> 1) & 3)) * 16);
       dst[i] = WF_SA + (j - WF_IA) * 64;
@@ -182,6 +208,19 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   for (int i = 0; i < WF_FN; ++i)
 #pragma unroll
     for (int j = 0; j < WF_FM; ++j) acc[i][j] = zero4();
+  // biases of this lane's columns, loaded before the main loop (the staging
+  // would otherwise wait on one global round trip per column block): V blocks
+  // hold one channel per lane (cb + lr), Q/K blocks four (cb + 4g .. +3)
+  uint2 biasp[WF_FN];
+#pragma unroll
+  for (int i = 0; i < WF_FN; ++i) {
+    const int b = wn * WF_FN + i, tg = b / 9, cb = (b - tg * 9) * 16;
+    biasp[i] = uint2{0u, 0u};
+    if (p.bias && b < WF_NBLK) {
+      if (tg == 0) biasp[i].x = p.bias[2 * p.D + hp * WF_CPH + cb + lr];
+      else biasp[i] = *reinterpret_cast<const uint2*>(p.bias + (tg - 1) * p.D + hp * WF_CPH + cb + 4 * g);
+    }
+  }
 
   const int lofs_a = DmaA<uint16_t>::lofs(wm * 64 + lr, g);
   const int lofs_w = WF_SA + DmaA<uint16_t>::lofs(wn * (WF_FN * 16) + lr, g);
@@ -195,16 +234,23 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
 #pragma unroll
     for (int j = 0; j < WF_FM; ++j) xf[j] = DmaA<uint16_t>::frag(st, lofs_a, j);
   };
-  auto mfmas = [&]() {
+  // V's column blocks (the first 9 of the tile: all 7 of wave column 0, the
+  // first 2 of wave column 1) are computed transposed, tokens as the first
+  // operand, so a lane holds 4 consecutive tokens of one channel: the V^T
+  // staging is then one 8-byte write per accumulator block
+  const int nsw = wn == 0 ? WF_FN : (wn == 1 ? 2 : 0);
+  auto mfmas = [&](auto nswI) {
+    constexpr int NSW = decltype(nswI)::value;
 #pragma unroll
     for (int i = 0; i < WF_FN; ++i)
 #pragma unroll
-      for (int j = 0; j < WF_FM; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+      for (int j = 0; j < WF_FM; ++j)
+        acc[i][j] = i < NSW ? mfma_bf16(xf[j], wf[i], acc[i][j]) : mfma_bf16(wf[i], xf[j], acc[i][j]);
   };
   // body of slice k (slot t = k % 4), as gemm_pp_kernel: refill slot t-1 with
   // slice k+3, read slice k's fragments, wait for slice k+1, barrier, MFMAs,
   // wait, barrier
-  auto body = [&](auto tI, auto issueI, auto wI, int k) {
+  auto body = [&](auto tI, auto issueI, auto wI, int k, auto nswI) {
     constexpr int t = decltype(tI)::value;
     if constexpr (decltype(issueI)::value) issue(k + 3, slot(std::integral_constant<int, t - 1>{}));
     read_frags(slot(std::integral_constant<int, t>{}));
@@ -212,7 +258,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    mfmas();
+    mfmas(nswI);
     wait_vm_lgkm0<decltype(wI)::value>();
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
@@ -220,21 +266,28 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   };
 
   const int KT = p.D / 32;  // multiple of 4, >= 8 (host check)
-  issue(0, slot(std::integral_constant<int, 0>{}));
-  issue(1, slot(std::integral_constant<int, 1>{}));
-  issue(2, slot(std::integral_constant<int, 2>{}));
-  wait_vm_lgkm0<2 * WF_MAXI>();
-  ring_barrier();
-  if (wm == 1) ring_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  using WS = std::integral_constant<int, 2 * WF_MAXI>;
-  for (int k0 = 0; k0 < KT - 4; k0 += 4) {
-    static_for<0, 4>([&](auto tI) { body(tI, std::true_type{}, WS{}, k0 + decltype(tI)::value); });
-  }
-  body(std::integral_constant<int, 0>{}, std::true_type{}, WS{}, KT - 4);
-  body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, WF_MAXI>{}, KT - 3);
-  body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 2);
-  body(std::integral_constant<int, 3>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 1);
+  // the whole main loop is instantiated once per transposed-block count, so
+  // the choice is one uniform branch outside it
+  auto main_loop = [&](auto nswI) {
+    issue(0, slot(std::integral_constant<int, 0>{}));
+    issue(1, slot(std::integral_constant<int, 1>{}));
+    issue(2, slot(std::integral_constant<int, 2>{}));
+    wait_vm_lgkm0<2 * WF_MAXI>();
+    ring_barrier();
+    if (wm == 1) ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    using WS = std::integral_constant<int, 2 * WF_MAXI>;
+    for (int k0 = 0; k0 < KT - 4; k0 += 4) {
+      static_for<0, 4>([&](auto tI) { body(tI, std::true_type{}, WS{}, k0 + decltype(tI)::value, nswI); });
+    }
+    body(std::integral_constant<int, 0>{}, std::true_type{}, WS{}, KT - 4, nswI);
+    body(std::integral_constant<int, 1>{}, std::false_type{}, std::integral_constant<int, WF_MAXI>{}, KT - 3, nswI);
+    body(std::integral_constant<int, 2>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 2, nswI);
+    body(std::integral_constant<int, 3>{}, std::false_type{}, std::integral_constant<int, 0>{}, KT - 1, nswI);
+  };
+  if (nsw == WF_FN) main_loop(std::integral_constant<int, WF_FN>{});
+  else if (nsw == 2) main_loop(std::integral_constant<int, 2>{});
+  else main_loop(std::integral_constant<int, 0>{});
   if (wm == 0) ring_barrier();
   wait_vm_lgkm0<0>();
   ring_barrier();  // ring drained: every DMA landed, every fragment read retired
@@ -260,36 +313,57 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     else return reinterpret_cast<uint16_t*>(ring2);
   };
 
+  // which of this lane's rows are real tokens (pad slots and rows past the
+  // grid stage their bias only), read once: bit j for the Q/K layout (row
+  // r0 + lr), bits 4j + e for the transposed V layout (rows r0 + 4g + e)
+  uint32_t real_qk = 0, real_v = 0;
+#pragma unroll
+  for (int j = 0; j < WF_FM; ++j) {
+    const int r0 = wm * 64 + j * 16;
+    const int4 gr = *reinterpret_cast<const int4*>(&grow_s[r0 + 4 * g]);
+    real_qk |= (grow_s[r0 + lr] >= 0 ? 1u : 0u) << j;
+    real_v |= ((gr.x >= 0 ? 1u : 0u) | (gr.y >= 0 ? 2u : 0u) | (gr.z >= 0 ? 4u : 0u) | (gr.w >= 0 ? 8u : 0u))
+              << (4 * j);
+  }
   // accumulators (+ bias; pad rows zeroed first) -> bf16 staging
 #pragma unroll
   for (int i = 0; i < WF_FN; ++i) {
     const int b = wn * WF_FN + i;  // wave-uniform
     if (b >= WF_NBLK) continue;
-    const int gq = b / 9;          // 0 Q, 1 K, 2 V
-    const int c = (b - gq * 9) * 16 + 4 * g;  // column within the head pair (0..143)
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.bias) {
-      const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gq * p.D + hp * WF_CPH + c);
-      bv[0] = __uint_as_float(bb.x << 16); bv[1] = __uint_as_float(bb.x & 0xffff0000u);
-      bv[2] = __uint_as_float(bb.y << 16); bv[3] = __uint_as_float(bb.y & 0xffff0000u);
+    const int tg = b / 9;          // tile column group: 0 V (transposed), 1 Q, 2 K
+    const int cb = (b - tg * 9) * 16;
+    if (tg == 0) {
+      // lane: channel n of the pair's V, tokens r0 + 4g .. +3 of the block
+      const int n = cb + lr;
+      const float bvn = __uint_as_float((biasp[i].x & 0xffffu) << 16);
+#pragma unroll
+      for (int j = 0; j < WF_FM; ++j) {
+        const int r0 = wm * 64 + j * 16;
+        const int w = r0 / L;
+        const uint32_t rv = real_v >> (4 * j);
+        const float v0 = ((rv & 1u) ? acc[i][j][0] : 0.f) + bvn, v1 = ((rv & 2u) ? acc[i][j][1] : 0.f) + bvn;
+        const float v2 = ((rv & 4u) ? acc[i][j][2] : 0.f) + bvn, v3 = ((rv & 8u) ? acc[i][j][3] : 0.f) + bvn;
+        *reinterpret_cast<uint2*>(vt_base(w) + n * SG::VTP + (r0 - w * L + 4 * g)) =
+            uint2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
+      }
+      continue;
     }
+    const int gq = tg - 1;         // 0 Q, 1 K
+    const int c = cb + 4 * g;      // column within the head pair (0..143)
+    const uint2 bb = biasp[i];
+    const float bv[4] = {__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                         __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u)};
 #pragma unroll
     for (int j = 0; j < WF_FM; ++j) {
       const int r0 = wm * 64 + j * 16;       // wave-uniform first row of the block
       const int w = r0 / L;                  // its window (uniform: 16 | L)
       const int e_ = r0 - w * L + lr;        // slot within the window
-      const bool real = grow_s[r0 + lr] >= 0;
+      const bool real = (real_qk >> j) & 1u;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (real ? acc[i][j][e] : 0.f) + bv[e];
-      if (gq < 2) {
-        char* base = gq == 0 ? qk_base(w) : k_base(w);
-        *reinterpret_cast<uint2*>(base + (e_ * WF_CPH + c) * 2) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-      } else {
-        uint16_t* vt = vt_base(w) + c * SG::VTP + e_;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vt[e * SG::VTP] = (uint16_t)(pack_bf2(v[e], 0.f) & 0xffffu);
-      }
+      char* base = gq == 0 ? qk_base(w) : k_base(w);
+      *reinterpret_cast<uint2*>(base + (e_ * WF_QP + c) * 2) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
     }
   }
   ring_barrier();
@@ -317,12 +391,12 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     uint4 qf[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qs + ((qb + qt * 16 + lr) * WF_CPH + ddc) * 2);
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + ((qb + qt * 16 + lr) * WF_QP + ddc) * 2);
       qf[qt] = dok ? v : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(ks + ((t * 16 + lr) * WF_CPH + ddc) * 2);
+      const uint4 kv = *reinterpret_cast<const uint4*>(ks + ((t * 16 + lr) * WF_QP + ddc) * 2);
       const uint4 kf = dok ? kv : uint4{0, 0, 0, 0};
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) sc[qt][t] = mfma_bf16(kf, qf[qt], sc[qt][t]);
@@ -386,7 +460,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   // head's waves read the other 72 columns)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    char* orow = qs + (qb + qt * 16 + lr) * WF_CPH * 2;
+    char* orow = qs + (qb + qt * 16 + lr) * WF_QP * 2;
 #pragma unroll
     for (int dt = 0; dt < 5; ++dt) {
       const int dd = dt * 16 + 4 * g;
@@ -401,7 +475,7 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   // row the pair's 144 channels = 18 chunks of 16 bytes
   {
     const int r0 = wave * 16, w = r0 / L;
-    const char* ob = qk_base(w) + (r0 - w * L) * WF_CPH * 2;
+    const char* ob = qk_base(w) + (r0 - w * L) * WF_QP * 2;
 #pragma unroll
     for (int it = 0; it < (16 * 18 + 63) / 64; ++it) {
       const int idx = it * 64 + lane;
@@ -410,10 +484,11 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
         const int grow = grow_s[r0 + rr];
         if (grow >= 0)
           *reinterpret_cast<uint4*>(p.O + (int64_t)grow * p.D + hp * WF_CPH + ch * 8) =
-              *reinterpret_cast<const uint4*>(ob + (rr * WF_CPH + ch * 8) * 2);
+              *reinterpret_cast<const uint4*>(ob + (rr * WF_QP + ch * 8) * 2);
       }
     }
   }
+  }  // tiles
 }
 
 bool wfused_supported(const WFusedDesc& d) {
@@ -430,10 +505,27 @@ bool wfused_supported(const WFusedDesc& d) {
   return true;
 }
 
+// compute units of the current device (one persistent workgroup each)
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int L, bool M>
 static hipError_t run_wfused(const WFusedParams& p, hipStream_t s) {
   const int ntiles = p.row_tiles * p.head_pairs;
-  hipLaunchKernelGGL((wfused_kernel<L, M>), dim3((unsigned)ntiles), dim3(512), 0, s, p);
+  // a multiple of 8 workgroups (the XCD count), at most one per CU
+  int grid = device_cus() / 8 * 8;
+  if (grid < 8) grid = 8;
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL((wfused_kernel<L, M>), dim3((unsigned)grid), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -426,6 +426,25 @@ ptdit_status ptdit_f32_to_bf16(const float* src, int64_t n, void* dst, hipStream
  * view of either (PTDIT_ERR_ALIAS). */
 ptdit_status ptdit_add_f32(const float* a, const float* b, int64_t n, float* out, hipStream_t stream);
 
+/*
+ * Calibration (benchmark aid, no part of the method): the ceilings this box
+ * sustains, to price kernels beside the published peaks.
+ * ptdit_calibrate_mfma -- `blocks` workgroups of 4 waves issue `iters` x 8
+ * independent v_mfma_f32_16x16x32_bf16 on register operands; *flop receives
+ * the bf16 FLOP launched; out: blocks*256 floats (written, meaningless).
+ * ptdit_calibrate_read -- streams `bytes` (% 16 == 0) of buf with 16-byte
+ * loads over `blocks` workgroups of 256 threads; out: blocks*256 floats.
+ * ptdit_calibrate_copy -- dst[i] = src[i] over `bytes` (% 16 == 0), one
+ * 16-byte load and store per lane and step, consecutive lanes on consecutive
+ * 16 bytes: a copy of known size whose hardware counter readings (bytes
+ * fetched and written at the last-level cache) scale other kernels'
+ * readings; src and dst must not overlap (PTDIT_ERR_ALIAS).
+ * Time any of them with events on `stream`.
+ */
+ptdit_status ptdit_calibrate_mfma(int32_t blocks, int32_t iters, float* out, int64_t* flop, hipStream_t stream);
+ptdit_status ptdit_calibrate_read(const void* buf, int64_t bytes, int32_t blocks, float* out, hipStream_t stream);
+ptdit_status ptdit_calibrate_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 /* Workspace bytes needed by an attention call (M: proxies; win: the TCM window,
  * ignored for the GIIM ops) or by ptdit_mlp (op PTDIT_OP_MLP, rows = g.B*g.F*
  * g.H*g.W, M: the hidden width). Returns 0 for invalid arguments, including a

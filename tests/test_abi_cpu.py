@@ -371,3 +371,19 @@ def test_attn_bwd_alias_check_is_exact_for_interleaved_batches(lib):
     # so only the refusals are exercised here
     assert args(base, base + 4 * hk + 16, base + 8 * hk) == -8   # d_k overlaps d_v's block
     assert args(base, base + 4 * hk - 16, base + 8 * hk) == -8   # d_k overlaps d_q's block
+
+
+def test_calibration_calls_validate_on_the_host(lib):
+    """Host checks of the calibration calls (nothing launched)."""
+    import ctypes
+    a, b = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 34)
+    assert lib.ptdit_calibrate_copy(a, b, 24, None) == -2                      # bytes % 16
+    assert lib.ptdit_calibrate_copy(a, b, 0, None) == 0                        # nothing to copy
+    assert lib.ptdit_calibrate_copy(None, b, 64, None) == -1
+    assert lib.ptdit_calibrate_copy(ctypes.c_void_p((1 << 30) + 8), b, 64, None) == -5
+    assert lib.ptdit_calibrate_copy(a, ctypes.c_void_p((1 << 30) + 32), 64, None) == -8   # overlap
+    assert lib.ptdit_calibrate_read(a, 24, 64, b, None) == -2
+    assert lib.ptdit_calibrate_read(a, 1 << 20, 64, ctypes.c_void_p((1 << 30) + 4096), None) == -8
+    flop = ctypes.c_int64(0)
+    assert lib.ptdit_calibrate_mfma(0, 10, b, ctypes.byref(flop), None) == -2
+    assert lib.ptdit_calibrate_mfma(4, 10, None, ctypes.byref(flop), None) == -1
