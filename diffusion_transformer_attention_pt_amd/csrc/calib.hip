@@ -15,21 +15,29 @@
 
 namespace ptdit {
 
-__global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float* out) {
+__global__ void __launch_bounds__(512) mfma_loop_kernel(int iters, float* out) {
   const int lane = threadIdx.x & 63;
-  const uint4 a = uint4{0x3f803f80u + (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  const uint4 b = uint4{0x3c003c00u, 0x3c003c00u + (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
-  floatx4 acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = zero4();
+  // 8 accumulators in plain vector values and a 512-thread launch bound: the
+  // loop is then the 8 MFMAs alone on VGPR accumulators (under a 256-thread
+  // bound the compiler placed them in AGPRs and rotated them through moves
+  // every iteration, which halved the measured rate)
+  const uint4 ua = uint4{0x3f803f80u + (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const uint4 ub = uint4{0x3c003c00u, 0x3c003c00u + (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ua), b = __builtin_bit_cast(bf16x8_t, ub);
+  floatx4 acc0 = zero4(), acc1 = zero4(), acc2 = zero4(), acc3 = zero4();
+  floatx4 acc4 = zero4(), acc5 = zero4(), acc6 = zero4(), acc7 = zero4();
   for (int i = 0; i < iters; ++i) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = mfma_bf16(a, b, acc[c]);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc2, 0, 0, 0);
+    acc3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc3, 0, 0, 0);
+    acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc4, 0, 0, 0);
+    acc5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc5, 0, 0, 0);
+    acc6 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc6, 0, 0, 0);
+    acc7 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc7, 0, 0, 0);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
-  out[blockIdx.x * 256 + threadIdx.x] = s;
+  const floatx4 s4 = ((acc0 + acc1) + (acc2 + acc3)) + ((acc4 + acc5) + (acc6 + acc7));
+  out[blockIdx.x * 256 + threadIdx.x] = s4[0] + s4[1] + s4[2] + s4[3];
 }
 
 __global__ void __launch_bounds__(256) read_kernel(const uint4* __restrict__ buf, int64_t n16, float* out) {
