@@ -501,6 +501,282 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
   }
 }
 
+// bf16 windows of 65..128 tokens (the 2 x 8 x 8 video windows) on the matrix
+// cores. Eight waves, 16 queries (phase 1) and 16 keys (phase 2) a wave; Q,
+// K, V, dO staged row-major (A / B operands of S and dP) and K, Q, dO
+// transposed (A operands of dQ^T, dK^T, dV^T).
+//  phase 1 (query-major), as the 64-token kernel over 8 key tiles: S^T, dP^T,
+//    the exact softmax over the window's keys, D = sum A dP, dS = A (dP - D),
+//    dQ^T = K^T dS^T; the query's max, 1/rowsum and D go to LDS.
+//  phase 2 (key-major): S = Q K^T and dP = dO V^T recomputed for the wave's 16
+//    keys (lane: key 16w + c, queries 16qt + 4g + r), A = exp(S - max) / sum
+//    and dS = A (dP - D) from the stored statistics; dV^T = dO^T A and
+//    dK^T = Q^T dS with A, dS packed from the registers (contraction order:
+//    queries 16qt0 + 4g + e, then 16(qt0+1) + 4g + e). Nothing of size
+//    keys x queries is written to LDS.
+// LDS 148 KB at d_h = 72 (one workgroup per CU). A 16-row dim tile of a
+// transposed copy that runs past DH reads the next region's first rows, whose
+// products land in output rows >= DH, never stored.
+template <int DH>
+__global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams p) {
+  static_assert(DH % 8 == 0, "head width a multiple of 8");
+  constexpr int KEYS = 128, NW = 8, NT = KEYS / 16;
+  constexpr int NKC = (DH + 31) / 32;
+  constexpr int RP = 8 * (DH / 8 + ((DH / 8) % 2 == 0 ? 1 : 2));  // odd count of 16-byte chunks
+  constexpr int NDT = (DH + 15) / 16;
+  constexpr int TP = KEYS + 8;
+  constexpr int T_SZ = DH * TP, R_SZ = KEYS * RP;
+  static_assert((NDT * 16 - DH) * TP <= R_SZ, "overrun rows of the last transposed copy stay in LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * T_SZ + 4 * R_SZ];
+  __shared__ int tok_s[KEYS], lab_s[KEYS];
+  __shared__ float st_s[KEYS * 3];  // per query: max, 1 / rowsum, D
+  uint16_t* const kT = lds;
+  uint16_t* const qT = lds + T_SZ;
+  uint16_t* const gT = lds + 2 * T_SZ;
+  uint16_t* const kr = lds + 3 * T_SZ;
+  uint16_t* const vr = kr + R_SZ;
+  uint16_t* const qr = vr + R_SZ;
+  uint16_t* const gr = qr + R_SZ;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int nWh = p.Hp / p.wh, nWw = p.Wp / p.ww;
+  const int Tw = blockIdx.x / (nWh * nWw), Iw = (blockIdx.x / nWw) % nWh, Jw = blockIdx.x % nWw;
+  const int wsz = p.wt * p.wh * p.ww;
+  const int64_t N = (int64_t)p.F * p.H * p.W;
+  const bool masked = (p.st | p.sh | p.sw) != 0;
+
+  if (tid < KEYS) {
+    const int s = tid;
+    int tok = -2, lab = 0;
+    if (s < wsz) {
+      const int a = s / (p.wh * p.ww), cc = (s / p.ww) % p.wh, e = s % p.ww;
+      const int rt = Tw * p.wt + a, ri = Iw * p.wh + cc, rj = Jw * p.ww + e;
+      int ot = rt + p.st; ot -= ot >= p.Fp ? p.Fp : 0;
+      int oi = ri + p.sh; oi -= oi >= p.Hp ? p.Hp : 0;
+      int oj = rj + p.sw; oj -= oj >= p.Wp ? p.Wp : 0;
+      tok = (ot < p.F && oi < p.H && oj < p.W) ? (ot * p.H + oi) * p.W + oj : -1;
+      lab = region_of(rt, p.Fp, p.wt, p.st) * 9 + region_of(ri, p.Hp, p.wh, p.sh) * 3 +
+            region_of(rj, p.Wp, p.ww, p.sw);
+    }
+    tok_s[s] = tok;
+    lab_s[s] = lab;
+  }
+  __syncthreads();
+
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(p.QKV);
+  const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
+  const uint16_t* Qb = base + (int64_t)b * 3 * gsz + h * hs;
+  const uint16_t* Kb = Qb + gsz;
+  const uint16_t* Vb = Qb + 2 * gsz;
+  const uint16_t* bias = reinterpret_cast<const uint16_t*>(p.bias_qkv);
+  const uint16_t* dOb = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * N * p.D + h * DH;
+
+  // staging: one thread per (8-dim chunk, quad of slots), quads fastest
+  constexpr int CH = DH / 8, QUADS = KEYS / 4;
+  static_assert(CH * QUADS <= NW * 64, "one staging item a thread");
+  if (tid < CH * QUADS) {
+    const int ch = tid / QUADS, kq = tid - ch * QUADS;
+    uint4 k4[4], v4[4], q4[4], g4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = tok_s[kq * 4 + j];
+      k4[j] = v4[j] = q4[j] = g4[j] = uint4{0, 0, 0, 0};
+      if (tok >= 0) {
+        k4[j] = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * DH + ch * 8);
+        v4[j] = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * DH + ch * 8);
+        q4[j] = *reinterpret_cast<const uint4*>(Qb + (int64_t)tok * DH + ch * 8);
+        g4[j] = *reinterpret_cast<const uint4*>(dOb + (int64_t)tok * p.D + ch * 8);
+      } else if (tok == -1 && bias) {
+        k4[j] = *reinterpret_cast<const uint4*>(bias + p.D + h * DH + ch * 8);
+        v4[j] = *reinterpret_cast<const uint4*>(bias + 2 * p.D + h * DH + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (kq * 4 + j) * RP + ch * 8;
+      *reinterpret_cast<uint4*>(&kr[r]) = k4[j];
+      *reinterpret_cast<uint4*>(&vr[r]) = v4[j];
+      *reinterpret_cast<uint4*>(&qr[r]) = q4[j];
+      *reinterpret_cast<uint4*>(&gr[r]) = g4[j];
+    }
+    put_quad_t(kT, TP, ch, kq * 4, k4);
+    put_quad_t(qT, TP, ch, kq * 4, q4);
+    put_quad_t(gT, TP, ch, kq * 4, g4);
+  }
+  __syncthreads();
+
+  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
+  float* dKb = dQb + gsz;
+  float* dVb = dQb + 2 * gsz;
+
+  // ---- phase 1: queries of wave w
+  {
+    const int qs = w * 16 + c;
+    const int qtok = tok_s[qs], qlab = lab_s[qs];
+    uint4 qf[NKC], gf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = kc * 32 + 8 * g;
+      qf[kc] = d < DH ? *reinterpret_cast<const uint4*>(&qr[qs * RP + d]) : uint4{0, 0, 0, 0};
+      gf[kc] = d < DH ? *reinterpret_cast<const uint4*>(&gr[qs * RP + d]) : uint4{0, 0, 0, 0};
+    }
+    floatx4 sc[NT], dp[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sc[t] = zero4();
+      dp[t] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const bool in = kc * 32 + 8 * g < DH;
+        const int r = (t * 16 + c) * RP + kc * 32 + 8 * g;
+        const uint4 ka = in ? *reinterpret_cast<const uint4*>(&kr[r]) : uint4{0, 0, 0, 0};
+        const uint4 va = in ? *reinterpret_cast<const uint4*>(&vr[r]) : uint4{0, 0, 0, 0};
+        sc[t] = mfma_bf16(ka, qf[kc], sc[t]);
+        dp[t] = mfma_bf16(va, gf[kc], dp[t]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ks = t * 16 + 4 * g + r;
+        const bool ok = tok_s[ks] != -2 && (!masked || lab_s[ks] == qlab);
+        sc[t][r] = ok ? sc[t][r] * p.scale : -INFINITY;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx == -INFINITY) mx = 0.f;  // slot past the window: no allowed key
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] = expf(sc[t][r] - mx);
+        l += sc[t][r];
+      }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float rl = l > 0.f ? 1.f / l : 0.f;
+    float dd = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[t][r] *= rl;
+        dd += sc[t][r] * dp[t][r];
+      }
+    dd += __shfl_xor(dd, 16, 64);
+    dd += __shfl_xor(dd, 32, 64);
+    if (g == 0) {
+      st_s[qs * 3] = mx;
+      st_s[qs * 3 + 1] = rl;
+      st_s[qs * 3 + 2] = dd;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dp[t][r] = sc[t][r] * (dp[t][r] - dd);  // dS
+    // dQ^T = K^T dS^T over the keys (two key tiles per MFMA)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int t0 = 0; t0 < NT; t0 += 2) {
+        const uint4 bf = uint4{pack_bf2(dp[t0][0], dp[t0][1]), pack_bf2(dp[t0][2], dp[t0][3]),
+                               pack_bf2(dp[t0 + 1][0], dp[t0 + 1][1]), pack_bf2(dp[t0 + 1][2], dp[t0 + 1][3])};
+        const int row = (dt * 16 + c) * TP, kb = t0 * 16 + 4 * g;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
+        acc = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc);
+      }
+      const int d = dt * 16 + 4 * g;
+      if (qtok >= 0 && d < DH)
+        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * DH + d) =
+            float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
+    }
+  }
+  __syncthreads();  // statistics of every query in LDS
+
+  // ---- phase 2: keys of wave w
+  {
+    const int ks = w * 16 + c;
+    const int ktok = tok_s[ks], klab = lab_s[ks];
+    const bool kvalid = ktok != -2;
+    uint4 kf[NKC], vf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = kc * 32 + 8 * g;
+      kf[kc] = d < DH ? *reinterpret_cast<const uint4*>(&kr[ks * RP + d]) : uint4{0, 0, 0, 0};
+      vf[kc] = d < DH ? *reinterpret_cast<const uint4*>(&vr[ks * RP + d]) : uint4{0, 0, 0, 0};
+    }
+    floatx4 dk[NDT], dv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
+#pragma unroll
+    for (int qt0 = 0; qt0 < NT; qt0 += 2) {
+      floatx4 pa[2], da[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int qt = qt0 + v;
+        floatx4 sc = zero4(), dp = zero4();
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const bool in = kc * 32 + 8 * g < DH;
+          const int r = (qt * 16 + c) * RP + kc * 32 + 8 * g;
+          const uint4 qa = in ? *reinterpret_cast<const uint4*>(&qr[r]) : uint4{0, 0, 0, 0};
+          const uint4 ga = in ? *reinterpret_cast<const uint4*>(&gr[r]) : uint4{0, 0, 0, 0};
+          sc = mfma_bf16(qa, kf[kc], sc);
+          dp = mfma_bf16(ga, vf[kc], dp);
+        }
+        // S[query 16qt + 4g + r][key ks]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qrow = qt * 16 + 4 * g + r;
+          const bool ok = kvalid && tok_s[qrow] != -2 && (!masked || lab_s[qrow] == klab);
+          const float m = st_s[qrow * 3], rl = st_s[qrow * 3 + 1], dd = st_s[qrow * 3 + 2];
+          const float a = ok ? expf(sc[r] * p.scale - m) * rl : 0.f;
+          pa[v][r] = a;
+          da[v][r] = a * (dp[r] - dd);
+        }
+      }
+      const uint4 pf = uint4{pack_bf2(pa[0][0], pa[0][1]), pack_bf2(pa[0][2], pa[0][3]),
+                             pack_bf2(pa[1][0], pa[1][1]), pack_bf2(pa[1][2], pa[1][3])};
+      const uint4 df = uint4{pack_bf2(da[0][0], da[0][1]), pack_bf2(da[0][2], da[0][3]),
+                             pack_bf2(da[1][0], da[1][1]), pack_bf2(da[1][2], da[1][3])};
+      const int kb = qt0 * 16 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int row = (dt * 16 + c) * TP;
+        const uint2 glo = *reinterpret_cast<const uint2*>(&gT[row + kb]);
+        const uint2 ghi = *reinterpret_cast<const uint2*>(&gT[row + kb + 16]);
+        const uint2 qlo = *reinterpret_cast<const uint2*>(&qT[row + kb]);
+        const uint2 qhi = *reinterpret_cast<const uint2*>(&qT[row + kb + 16]);
+        dv[dt] = mfma_bf16(uint4{glo.x, glo.y, ghi.x, ghi.y}, pf, dv[dt]);
+        dk[dt] = mfma_bf16(uint4{qlo.x, qlo.y, qhi.x, qhi.y}, df, dk[dt]);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = dt * 16 + 4 * g;
+      if (d >= DH) continue;
+      const float4 kv = float4{dk[dt][0] * p.scale, dk[dt][1] * p.scale, dk[dt][2] * p.scale, dk[dt][3] * p.scale};
+      const float4 vv = float4{dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
+      if (ktok >= 0) {
+        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
+        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
+      } else if (ktok == -1 && p.dbias_kv) {
+        float* bk = p.dbias_kv + h * DH + d;
+        float* bv = p.dbias_kv + p.D + h * DH + d;
+        atomicAdd(bk + 0, kv.x); atomicAdd(bk + 1, kv.y); atomicAdd(bk + 2, kv.z); atomicAdd(bk + 3, kv.w);
+        atomicAdd(bv + 0, vv.x); atomicAdd(bv + 1, vv.y); atomicAdd(bv + 2, vv.z); atomicAdd(bv + 3, vv.w);
+      }
+    }
+  }
+}
+
 template <typename T, int DH>
 static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   WindowBwdParams p;
@@ -514,6 +790,8 @@ static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   const dim3 grid(nwin, d.heads, d.B);
   const int wsz = d.wt * d.wh * d.ww;
   if (sizeof(T) == 2 && wsz <= 64) hipLaunchKernelGGL((window_bwd_mfma_kernel<DH>), grid, dim3(BW_NT), 0, s, p);
+  else if (sizeof(T) == 2 && wsz <= 128)
+    hipLaunchKernelGGL((window_bwd_mfma128_kernel<DH>), grid, dim3(512), 0, s, p);
   else if (wsz <= 64) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 64>), grid, dim3(BW_NT), 0, s, p);
   else if (wsz <= 128) hipLaunchKernelGGL((window_bwd_kernel<T, DH, 128>), grid, dim3(BW_NT), 0, s, p);
   else return hipErrorInvalidValue;
@@ -893,6 +1171,162 @@ __global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
   }
 }
 
+// Query-major for more than 256 keys: the keys stream through the same LDS
+// layout in chunks of 256, twice. Pass 1 keeps, per query, the running
+// maximum m, sum l = sum exp(s - m) and U = sum exp(s - m) dP over the chunks
+// seen so far (both sums rescaled by exp(m_old - m_new) when the maximum
+// grows), so that after the last chunk D = sum A dP = U / l. Pass 2 restages
+// every chunk and forms the exact A = exp(s - m) / l and dS = A (dP - D),
+// accumulating dQ^T = K^T dS^T across the chunks. A chunk is contracted in
+// two halves of 128 keys (8 tiles of 16 scores and dP values a lane).
+// Statistics to the workspace as in the resident kernel.
+template <int DH>
+__global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_stream_kernel(DenseBwdParams p) {
+  constexpr int NKC = (DH + 31) / 32, RP = NKC * 32 + 8, NDT = (DH + 15) / 16;
+  constexpr int TP = DM_MAXK + 8, HT = DM_MAXK / 32;  // 16-key tiles in half a chunk
+  __shared__ __attribute__((aligned(16))) uint16_t kr[DM_MAXK * RP], vr[DM_MAXK * RP], kT[NDT * 16 * TP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + b * p.kv_bs + (int64_t)h * p.Nk * DH;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_bs + (int64_t)h * p.Nq * DH;
+  const uint16_t* G0 = reinterpret_cast<const uint16_t*>(p.dO) + (int64_t)b * p.Nq * p.D + h * DH;
+  const int qi = blockIdx.x * (DQ_NT / 4) + w * 16 + c;
+  const bool live = qi < p.Nq;
+  uint4 qf[NKC], gf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int d = kc * 32 + 8 * g;
+    qf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(Q + (int64_t)qi * DH + d) : uint4{0, 0, 0, 0};
+    gf[kc] = (live && d < DH) ? *reinterpret_cast<const uint4*>(G0 + (int64_t)qi * p.D + d) : uint4{0, 0, 0, 0};
+  }
+  // chunk k0..k0+255: K, V row-major and K transposed (keys past Nk zero)
+  auto stage = [&](int k0) {
+    constexpr int CH = NKC * 4, QUADS = DM_MAXK / 4;
+    __syncthreads();  // the previous chunk's reads are done
+    for (int idx = tid; idx < CH * QUADS; idx += DQ_NT) {
+      const int ch = idx / QUADS, kq = idx - ch * QUADS;
+      uint4 k4[4], v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = k0 + kq * 4 + j;
+        const bool ok = ch * 8 < DH && r < p.Nk;
+        k4[j] = ok ? *reinterpret_cast<const uint4*>(K + (int64_t)r * DH + ch * 8) : uint4{0, 0, 0, 0};
+        v4[j] = ok ? *reinterpret_cast<const uint4*>(V + (int64_t)r * DH + ch * 8) : uint4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint4*>(&kr[(kq * 4 + j) * RP + ch * 8]) = k4[j];
+        *reinterpret_cast<uint4*>(&vr[(kq * 4 + j) * RP + ch * 8]) = v4[j];
+      }
+      if (ch * 8 < NDT * 16) put_quad_t(kT, TP, ch, kq * 4, k4);
+    }
+    __syncthreads();
+  };
+  // scores (scaled; -inf past Nk) and dP of half hf of the staged chunk
+  auto half = [&](int k0, int hf, floatx4 (&sc)[HT], floatx4 (&dp)[HT]) {
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      const int tt = hf * HT + t;
+      sc[t] = zero4();
+      dp[t] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&kr[(tt * 16 + c) * RP + kc * 32 + 8 * g]);
+        const uint4 va = *reinterpret_cast<const uint4*>(&vr[(tt * 16 + c) * RP + kc * 32 + 8 * g]);
+        sc[t] = mfma_bf16(ka, qf[kc], sc[t]);
+        dp[t] = mfma_bf16(va, gf[kc], dp[t]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[t][r] = k0 + tt * 16 + 4 * g + r < p.Nk ? sc[t][r] * p.scale : -INFINITY;
+    }
+  };
+
+  // ---- pass 1: running statistics (the lane's partial sums over its keys;
+  // the maximum is shared by the four lane groups of the query)
+  float m = -INFINITY, l = 0.f, u = 0.f;
+  for (int k0 = 0; k0 < p.Nk; k0 += DM_MAXK) {
+    stage(k0);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (k0 + hf * HT * 16 >= p.Nk) break;  // uniform
+      floatx4 sc[HT], dp[HT];
+      half(k0, hf, sc, dp);
+      float cm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cm = fmaxf(cm, sc[t][r]);
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float mn = fmaxf(m, cm);           // finite: every half holds a key
+      const float al = __expf(m - mn);         // 0 on the first half (m = -inf)
+      l *= al;
+      u *= al;
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __expf(sc[t][r] - mn);
+          l += e;
+          u += e * dp[t][r];
+        }
+      m = mn;
+    }
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  u += __shfl_xor(u, 16, 64);
+  u += __shfl_xor(u, 32, 64);
+  const float rl = 1.f / l, dd = u * rl;
+
+  // ---- pass 2: dS and dQ
+  floatx4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero4();
+  for (int k0 = 0; k0 < p.Nk; k0 += DM_MAXK) {
+    stage(k0);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (k0 + hf * HT * 16 >= p.Nk) break;
+      floatx4 sc[HT], dp[HT];
+      half(k0, hf, sc, dp);
+#pragma unroll
+      for (int t0 = 0; t0 < HT; t0 += 2) {
+        floatx4 ds[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[v][r] = __expf(sc[t0 + v][r] - m) * rl * (dp[t0 + v][r] - dd);
+        const uint4 bf = uint4{pack_bf2(ds[0][0], ds[0][1]), pack_bf2(ds[0][2], ds[0][3]),
+                               pack_bf2(ds[1][0], ds[1][1]), pack_bf2(ds[1][2], ds[1][3])};
+        const int kb = (hf * HT + t0) * 16 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int row = (dt * 16 + c) * TP;
+          const uint2 lo = *reinterpret_cast<const uint2*>(&kT[row + kb]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&kT[row + kb + 16]);
+          acc[dt] = mfma_bf16(uint4{lo.x, lo.y, hi.x, hi.y}, bf, acc[dt]);
+        }
+      }
+    }
+  }
+  if (live) {
+    float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = dt * 16 + 4 * g;
+      if (d < DH)
+        *reinterpret_cast<float4*>(dq + d) =
+            float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+    }
+    if (g == 0) {
+      float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
+      st[0] = m; st[1] = l; st[2] = dd;
+    }
+  }
+}
+
 // Key-major: KS * 64 keys per workgroup (KS sub-tiles of 16 a wave) over one
 // chunk of the queries, 64-query tiles staged row-major (Q, dO: A operands of
 // S = Q K^T, dP = dO V^T) and transposed (Q^T, dO^T: A operands of
@@ -1051,6 +1485,9 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   const dim3 gqm((d.Nq + qpw - 1) / qpw, d.heads, d.B);
   if (BF && d.Nk <= DM_MAXK) {
     hipLaunchKernelGGL((dense_bwd_q_mfma_kernel<DH>), gqm, dim3(DQ_NT), 0, s, p);
+  } else if (BF) {
+    const dim3 gqs((d.Nq + QT - 1) / QT, d.heads, d.B);
+    hipLaunchKernelGGL((dense_bwd_q_mfma_stream_kernel<DH>), gqs, dim3(DQ_NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((dense_bwd_q_kernel<T, DH>), gq, dim3(BW_NT), 0, s, p);
   }

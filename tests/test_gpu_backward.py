@@ -57,12 +57,22 @@ WIN_CASES = {
     # the same over 20 padded windows of a 60 x 100 grid (the bias sums add
     # the pad slots of every one of them)
     "img_many_pad_windows": ((1, 1, 60, 100), 1152, 16, (1, 8, 8), (0, 2, 2), "bf16", 1.0),
+    # 128-token video windows (2 x 8 x 8) on the matrix-core kernel: head width
+    # 64; batch 2 without a shift; a pad (1 frame, 4 rows, 4 columns) that
+    # differs from the shift (1, 2, 2), so pad slots are visible
+    "video128_dh64": ((1, 4, 16, 16), 1024, 16, (2, 8, 8), (1, 4, 4), "bf16", 1.0),
+    "video128_batch2_noshift": ((2, 4, 16, 16), 1152, 16, (2, 8, 8), (0, 0, 0), "bf16", 1.0),
+    "video128_pad_ne_shift": ((1, 3, 20, 36), 1152, 16, (2, 8, 8), (1, 2, 2), "bf16", 1.0),
+    "video128_peaked": ((1, 4, 16, 16), 1152, 16, (2, 8, 8), (1, 4, 4), "bf16", 1.7),
+    # 96-token windows (1 x 8 x 12): slots 96..127 of the 128-slot kernel are
+    # empty
+    "window96_shift": ((1, 1, 16, 24), 1152, 16, (1, 8, 12), (0, 4, 6), "bf16", 1.0),
 }
 
 # cases whose pad slots are visible to real queries (their pad gradients must
 # be nonzero, so the bias-sum path is exercised)
 PAD_VISIBLE = {"img_pad_ne_shift", "img_many_pad_windows", "small_window_pad", "video_pad_shift",
-               "f32_video_pad"}
+               "f32_video_pad", "video128_pad_ne_shift"}
 
 
 @pytest.mark.parametrize("name", list(WIN_CASES))
@@ -120,6 +130,47 @@ def test_window_attn_bwd_full_size_sampled_windows(P):
         assert_grad_close(tok(dqkv[:, 2])[0][t], rv, f"dV window {w}")
 
 
+def test_window_attn_bwd_video_full_size_sampled_windows(P):
+    # the 16 x 30 x 45 video grid (padded to 16 x 32 x 48 for 2 x 8 x 8
+    # windows, 128 tokens) with the temporal shift (1, 4, 4): the whole backward
+    # on the matrix-core 128-token kernel, six windows by the oracle (the
+    # first, the wrap-around corner, four drawn)
+    B, F, H, W, D, heads = 1, 16, 30, 45, 1152, 16
+    win, shift = (2, 8, 8), (1, 4, 4)
+    dh, N = D // heads, F * H * W
+    announce("window bwd full size video 16x30x45 win (2,8,8) shift (1,4,4)")
+    q, k, v, do = make_attn_grad_inputs(B, heads, N, N, dh, seed=352)
+    g = np.random.Generator(np.random.PCG64(353))
+    bias = round_bf16(g.standard_normal(3 * D).astype(np.float32) * 0.5)
+    qkv = np.stack([q, k, v], axis=1)
+    dqkv, dbkv = P.window_attn_bwd(dev(qkv, BF16), dev(do, BF16), (B, F, H, W, D, heads), win, shift,
+                                   b_qkv=dev(bias, BF16))
+    torch.cuda.synchronize()
+    dqkv = host(dqkv)
+    grid_p = tuple(-(-n // w) * w for n, w in zip((F, H, W), win))
+    # slot -> token (or pad) of every window, from the oracle's own pad, roll and partition
+    ids = np.full((1,) + grid_p + (1,), -1.0)
+    ids[0, :F, :H, :W, 0] = np.arange(N, dtype=np.float64).reshape(F, H, W)
+    slots = O.partition(O.roll3d(ids, shift), win).reshape(-1, 128).astype(np.int64)
+    labs = O.partition(O.region_labels(grid_p, win, shift)[None, ..., None], win).reshape(-1, 128)
+    picks = [0, slots.shape[0] - 1] + list(g.choice(slots.shape[0], 4, replace=False))
+    qt, kt, vt = tok(q)[0], tok(k)[0], tok(v)[0]
+    bk, bv = bias[D:2 * D], bias[2 * D:]
+    for w in picks:
+        t = slots[w]
+        real = t >= 0
+        allow = labs[w][:, None] == labs[w][None, :]
+        kw = np.where(real[:, None], kt[np.maximum(t, 0)], bk[None, :])      # pad keys / values are the biases
+        vw = np.where(real[:, None], vt[np.maximum(t, 0)], bv[None, :])
+        qw = np.where(real[:, None], qt[np.maximum(t, 0)], 0.0)
+        dow = np.where(real[:, None], do[0][np.maximum(t, 0)], 0.0)
+        rq, rk, rv = O.attention_bwd(qw, kw, vw, dow, heads, allow)
+        tr = t[real]
+        assert_grad_close(tok(dqkv[:, 0])[0][tr], rq[real], f"dQ window {w}")
+        assert_grad_close(tok(dqkv[:, 1])[0][tr], rk[real], f"dK window {w}")
+        assert_grad_close(tok(dqkv[:, 2])[0][tr], rv[real], f"dV window {w}")
+
+
 # ----------------------------------------------------------------------------- dense core
 
 DENSE_CASES = {
@@ -131,9 +182,19 @@ DENSE_CASES = {
     "dh64": (2, 16, 300, 64, 64, "q+kv", "bf16", 1.0),
     "f32": (1, 8, 1500, 96, 72, "q+kv", "f32", 1.0),
     "one_key": (1, 4, 70, 1, 72, "q+kv", "bf16", 1.0),
-    # more than 256 keys: the vector-ALU query-major kernel with the
-    # matrix-core key-major kernel (statistics handed between them)
+    # more than 256 keys: the streamed query-major kernel (keys in chunks of
+    # 256, two passes) with the key-major kernel (statistics handed between
+    # them); 600 keys end in a ragged half chunk
     "many_keys": (1, 16, 1100, 600, 72, "q+kv", "bf16", 1.0),
+    # the 16 x 30 x 45 video's proxy self-attention (864 proxies) and its
+    # cross-attention on a slice of the queries; 1152 proxies of the long video
+    # (72 x 32 x 32, proxy window 2 x 4 x 4) with peaked scores; head width 64
+    "video_proxy_sa_864": (1, 16, 864, 864, 72, "qkv", "bf16", 1.0),
+    "video_xattn_864": (1, 16, 3000, 864, 72, "q+kv", "bf16", 1.0),
+    "long_video_1152_peaked": (1, 16, 1152, 1152, 72, "qkv", "bf16", 1.7),
+    "many_keys_dh64": (1, 16, 700, 300, 64, "q+kv", "bf16", 1.0),
+    # 257 keys: one key past a whole chunk (a second chunk of one key)
+    "keys_257": (1, 8, 500, 257, 72, "q+kv", "bf16", 1.0),
     "batch2_chunks": (2, 16, 2100, 256, 72, "q+kv", "bf16", 1.0),
     # few keys against thousands of queries: every dK / dV row sums
     # thousands of products (the randomized sweep's largest absolute errors)
@@ -176,6 +237,25 @@ def test_attn_bwd_full_size_cross_attention(P):
     B, heads, Nq, Nk, dh = 1, 16, 16384, 256, 72
     announce("dense bwd full size Nq=16384 Nk=256")
     q, k, v, do = make_attn_grad_inputs(B, heads, Nq, Nk, dh, seed=550)
+    kv = dev(np.stack([k, v], axis=1), BF16)
+    dq, dk, dv = P.attn_bwd(dev(q, BF16), kv[:, 0], kv[:, 1], dev(do, BF16))
+    torch.cuda.synchronize()
+    dq, dk, dv = host(dq), host(dk), host(dv)
+    for h in (0, heads - 1):
+        sl = slice(h * dh, (h + 1) * dh)
+        rq, rk, rv = O.attention_bwd(q[0, h], k[0, h], v[0, h], do[0][:, sl], 1)
+        assert_grad_close(dq[0, h], rq, f"dQ head {h}")
+        assert_grad_close(dk[0, h], rk, f"dK head {h}")
+        assert_grad_close(dv[0, h], rv, f"dV head {h}")
+
+
+def test_attn_bwd_full_size_video_cross_attention(P):
+    # cross-attention of the 16 x 30 x 45 video: 21600 token queries, 864
+    # proxies (streamed query-major kernel), 16 heads; the oracle takes two
+    # heads whole
+    B, heads, Nq, Nk, dh = 1, 16, 21600, 864, 72
+    announce("dense bwd full size video Nq=21600 Nk=864")
+    q, k, v, do = make_attn_grad_inputs(B, heads, Nq, Nk, dh, seed=551)
     kv = dev(np.stack([k, v], axis=1), BF16)
     dq, dk, dv = P.attn_bwd(dev(q, BF16), kv[:, 0], kv[:, 1], dev(do, BF16))
     torch.cuda.synchronize()

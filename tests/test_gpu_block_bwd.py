@@ -34,6 +34,11 @@ CASES = {
     # pad (4): pad keys are visible, on the 64-token matrix-core kernels
     "batch2_pad": tiny("bwd_b2", B=2, F=1, H=20, W=36, D=1152, heads=16, p=(1, 4, 4), win=(1, 8, 8),
                        shift=(0, 2, 2), dtype="bf16", index=62),
+    # half the 16 x 30 x 45 video: 432 proxies (more than 256 keys: the
+    # streamed query-major kernels) and 2 x 8 x 8 windows (the 128-token
+    # matrix-core window kernel), 30 x 45 padded to 32 x 48
+    "video_432_proxies": tiny("bwd_video432", B=1, F=8, H=30, W=45, D=1152, heads=16, p=(1, 5, 5),
+                              win=(2, 8, 8), shift=(1, 4, 4), dtype="bf16", index=64),
 }
 
 
