@@ -102,6 +102,9 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
   const bool masked = (p.st | p.sh | p.sw) != 0;
 
   // slot s of the window -> token (-1: pad, -2: past the window), region label
+  __shared__ float padg[2 * DH];  // pad keys' gradients: d b_k (0 .. DH-1), d b_v
+  for (int i = threadIdx.x; i < 2 * DH; i += blockDim.x) padg[i] = 0.f;
+  bool my_pad = false;
   for (int s = tid; s < KEYS; s += BW_NT) {
     int tok = -2, lab = 0;
     if (s < wsz) {
@@ -116,8 +119,11 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
     }
     tok_s[s] = tok;
     lab_s[s] = lab;
+    my_pad |= tok == -1;
   }
-  __syncthreads();
+  // pad slots' key / value gradients are summed per channel in LDS, then
+  // added to d_bias_kv once per workgroup (not once per pad key)
+  const bool any_pad = __syncthreads_or(my_pad) != 0;
 
   const T* base = reinterpret_cast<const T*>(p.QKV);
   const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
@@ -252,10 +258,15 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
         float k = 0.f, v = 0.f;
 #pragma unroll
         for (int e = 0; e < DH; ++e) { k = e == d ? dk[e] : k; v = e == d ? dv[e] : v; }
-        atomicAdd(p.dbias_kv + h * DH + d, k);
-        atomicAdd(p.dbias_kv + p.D + h * DH + d, v);
+        atomicAdd(&padg[d], k);
+        atomicAdd(&padg[DH + d], v);
       }
     }
+  }
+  if (any_pad && p.dbias_kv) {  // uniform
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * DH; i += blockDim.x)
+      atomicAdd(p.dbias_kv + (i < DH ? h * DH + i : p.D + h * DH + i - DH), padg[i]);
   }
 }
 
@@ -308,6 +319,7 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
   const int64_t N = (int64_t)p.F * p.H * p.W;
   const bool masked = (p.st | p.sh | p.sw) != 0;
 
+  bool my_pad = false;
   for (int s = tid; s < KEYS; s += BW_NT) {
     int tok = -2, lab = 0;
     if (s < wsz) {
@@ -322,8 +334,11 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
     }
     tok_s[s] = tok;
     lab_s[s] = lab;
+    my_pad |= tok == -1;
   }
-  __syncthreads();
+  // pad slots' key / value gradients are summed per channel in LDS, then
+  // added to d_bias_kv once per workgroup (not once per pad key)
+  const bool any_pad = __syncthreads_or(my_pad) != 0;
 
   const uint16_t* base = reinterpret_cast<const uint16_t*>(p.QKV);
   const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
@@ -466,6 +481,13 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
     }
   }
   __syncthreads();
+  // pad keys' gradients (d b_k at 0 .. DH-1, d b_v after) are summed in the
+  // transposed-K copy, which phase 2 no longer reads
+  float* const padg = reinterpret_cast<float*>(kT);
+  if (any_pad) {  // uniform
+    for (int i = tid; i < 2 * DH; i += BW_NT) padg[i] = 0.f;
+    __syncthreads();
+  }
 
   // ---- phase 2: keys of wave w
   {
@@ -492,12 +514,17 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
         *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
         *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
       } else if (ktok == -1 && p.dbias_kv) {
-        float* bk = p.dbias_kv + h * DH + d;
-        float* bv = p.dbias_kv + p.D + h * DH + d;
+        float* bk = &padg[d];
+        float* bv = &padg[DH + d];
         atomicAdd(bk + 0, kv.x); atomicAdd(bk + 1, kv.y); atomicAdd(bk + 2, kv.z); atomicAdd(bk + 3, kv.w);
         atomicAdd(bv + 0, vv.x); atomicAdd(bv + 1, vv.y); atomicAdd(bv + 2, vv.z); atomicAdd(bv + 3, vv.w);
       }
     }
+  }
+  if (any_pad && p.dbias_kv) {  // uniform
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * DH; i += blockDim.x)
+      atomicAdd(p.dbias_kv + (i < DH ? h * DH + i : p.D + h * DH + i - DH), padg[i]);
   }
 }
 
@@ -546,6 +573,9 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
   const int64_t N = (int64_t)p.F * p.H * p.W;
   const bool masked = (p.st | p.sh | p.sw) != 0;
 
+  __shared__ float padg[2 * DH];  // pad keys' gradients: d b_k (0 .. DH-1), d b_v
+  for (int i = threadIdx.x; i < 2 * DH; i += blockDim.x) padg[i] = 0.f;
+  bool my_pad = false;
   if (tid < KEYS) {
     const int s = tid;
     int tok = -2, lab = 0;
@@ -561,8 +591,11 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
     }
     tok_s[s] = tok;
     lab_s[s] = lab;
+    my_pad |= tok == -1;
   }
-  __syncthreads();
+  // pad slots' key / value gradients are summed per channel in LDS, then
+  // added to d_bias_kv once per workgroup (not once per pad key)
+  const bool any_pad = __syncthreads_or(my_pad) != 0;
 
   const uint16_t* base = reinterpret_cast<const uint16_t*>(p.QKV);
   const int64_t hs = N * DH, gsz = (int64_t)p.heads * hs;
@@ -768,12 +801,17 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
         *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
         *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
       } else if (ktok == -1 && p.dbias_kv) {
-        float* bk = p.dbias_kv + h * DH + d;
-        float* bv = p.dbias_kv + p.D + h * DH + d;
+        float* bk = &padg[d];
+        float* bv = &padg[DH + d];
         atomicAdd(bk + 0, kv.x); atomicAdd(bk + 1, kv.y); atomicAdd(bk + 2, kv.z); atomicAdd(bk + 3, kv.w);
         atomicAdd(bv + 0, vv.x); atomicAdd(bv + 1, vv.y); atomicAdd(bv + 2, vv.z); atomicAdd(bv + 3, vv.w);
       }
     }
+  }
+  if (any_pad && p.dbias_kv) {  // uniform
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * DH; i += blockDim.x)
+      atomicAdd(p.dbias_kv + (i < DH ? h * DH + i : p.D + h * DH + i - DH), padg[i]);
   }
 }
 

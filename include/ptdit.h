@@ -302,10 +302,12 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
  *   d_qkv    [B][3][heads][N][dh] device, fp32: dQ, dK, dV of the real tokens
  *   d_b_kv   [2][D] device, fp32, or NULL: the gradients that reach pad key /
  *            value slots are ADDED here (d b_k, d b_v); required (else
- *            PTDIT_ERR_NULL) when the window does not divide the grid. The
- *            additions are device atomics, so their order (and with it the
- *            last bits of d_b_kv) can differ from run to run; d_qkv is
- *            written without atomics and is the same in every run
+ *            PTDIT_ERR_NULL) when the window does not divide the grid. Each
+ *            (window, head) sums its pad slots' gradients on chip and adds
+ *            the sum with one device atomic per channel, so the order of the
+ *            additions across windows (and with it the last bits of d_b_kv)
+ *            can differ from run to run; d_qkv is written without atomics
+ *            and is the same in every run
  *   win, shift as for the forward call (window <= 128 tokens, shift < window).
  */
 ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
