@@ -34,7 +34,8 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_proxy_pool_bwd", "ptdit_linear_bwd", "ptdit_linear_bwd_workspace_bytes",
             "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
             "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
-            "ptdit_calibrate_read", "ptdit_calibrate_copy"]
+            "ptdit_calibrate_read", "ptdit_calibrate_copy", "ptdit_linear_bwd_ex",
+            "ptdit_window_attn_bwd_tokens"]
 
 
 class Grid(ctypes.Structure):
@@ -93,10 +94,12 @@ def load() -> ctypes.CDLL:
         "ptdit_trace_read": [ctypes.POINTER(ctypes.c_float), i32],
         "ptdit_trace_disable": [],
         "ptdit_window_attn_bwd": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
+        "ptdit_window_attn_bwd_tokens": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
         "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
         "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
         "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
         "ptdit_linear_bwd": [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "ptdit_linear_bwd_ex": [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "ptdit_linear_bwd_workspace_bytes": [i64, i32, i32],
         "ptdit_linear_heads": [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp],
         "ptdit_window_attn": [vp, vp, i32, G, W3, W3, vp, vp],
@@ -449,10 +452,12 @@ def roll3d(x: torch.Tensor, grid: Sequence[int], shift: Sequence[int], inverse: 
 
 def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], win: Sequence[int],
                     shift: Sequence[int] = (0, 0, 0), b_qkv: Optional[torch.Tensor] = None,
-                    d_qkv: Optional[torch.Tensor] = None, d_b_kv: Optional[torch.Tensor] = None):
+                    d_qkv: Optional[torch.Tensor] = None, d_b_kv: Optional[torch.Tensor] = None,
+                    tokens: bool = False):
     """Backward of the window / shifted-window attention core. qkv [B, 3, heads,
     N, dh] (the forward's Q/K/V), d_o [B, N, D]. Returns (d_qkv fp32 [B, 3, heads,
-    N, dh], d_b_kv fp32 [2, D]: pad-slot gradients, added to d_b_kv when given)."""
+    N, dh], or [B, N, 3D] with tokens=True (ptdit_window_attn_bwd_tokens), d_b_kv
+    fp32 [2, D]: pad-slot gradients, added to d_b_kv when given)."""
     lib = load()
     B, F, H, W, D, heads = grid
     if d_o.dtype != qkv.dtype or (b_qkv is not None and b_qkv.dtype != qkv.dtype):
@@ -464,12 +469,14 @@ def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], w
     _numel(d_qkv, B * 3 * N * D, "d_qkv")
     _numel(d_b_kv, 2 * D, "d_b_kv")
     if d_qkv is None:
-        d_qkv = torch.empty(qkv.shape, dtype=torch.float32, device=qkv.device)
+        shape = (B, N, 3 * D) if tokens else tuple(qkv.shape)
+        d_qkv = torch.empty(shape, dtype=torch.float32, device=qkv.device)
     if d_b_kv is None:
         d_b_kv = torch.zeros(2, D, dtype=torch.float32, device=qkv.device)
-    st = lib.ptdit_window_attn_bwd(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid), Win3(*win),
-                                   Win3(*shift), _ptr(d_qkv), _ptr(d_b_kv), _stream())
-    _check("ptdit_window_attn_bwd", st)
+    fn = lib.ptdit_window_attn_bwd_tokens if tokens else lib.ptdit_window_attn_bwd
+    st = fn(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid), Win3(*win), Win3(*shift), _ptr(d_qkv),
+            _ptr(d_b_kv), _stream())
+    _check("ptdit_window_attn_bwd_tokens" if tokens else "ptdit_window_attn_bwd", st)
     return d_qkv, d_b_kv
 
 
@@ -541,10 +548,14 @@ def proxy_pool_bwd(d_proxies: torch.Tensor, grid: Sequence[int], p: Sequence[int
 
 def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: bool = True, want_dw: bool = True,
                want_db: bool = True, ws: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
-               dw: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None):
+               dw: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+               dx_add: Optional[torch.Tensor] = None, dx_bf16: Optional[torch.Tensor] = None):
     """Gradients of Y = X W^T + b: x [..., d_in], w [d_out, d_in] bf16, d_y [..., d_out].
     Returns fp32 (d_x or None, d_w or None, d_b or None): new tensors, or the
-    given contiguous fp32 ones (e.g. row blocks of a larger gradient)."""
+    given contiguous fp32 ones (e.g. row blocks of a larger gradient).
+    dx_add (fp32, the shape of d_x; may be dx itself): added to d_x in the
+    product's epilogue (ptdit_linear_bwd_ex). dx_bf16 (bf16): d_x rounded to
+    bf16 as well; with want_dx False only the bf16 gradient is written."""
     lib = load()
     d_in, d_out = x.shape[-1], w.shape[0]
     rows = x.numel() // d_in
@@ -554,10 +565,17 @@ def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: boo
         raise ValueError(f"w must be [d_out, {d_in}]")
     _numel(d_y, rows * d_out, "d_y")
     dev = x.device
-    for t, n, name in ((dx, rows * d_in, "dx"), (dw, d_out * d_in, "dw"), (db, d_out, "db")):
+    for t, n, name in ((dx, rows * d_in, "dx"), (dw, d_out * d_in, "dw"), (db, d_out, "db"),
+                       (dx_add, rows * d_in, "dx_add")):
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be fp32")
         _numel(t, n, name)
+    if dx_bf16 is not None:
+        if dx_bf16.dtype != torch.bfloat16:
+            raise ValueError("dx_bf16 must be bf16")
+        _numel(dx_bf16, rows * d_in, "dx_bf16")
+    if dx_add is not None and not want_dx:
+        raise ValueError("dx_add needs the fp32 d_x (want_dx)")
     if dx is None and want_dx:
         dx = torch.empty(*x.shape[:-1], d_in, dtype=torch.float32, device=dev)
     if dw is None and want_dw:
@@ -566,9 +584,15 @@ def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: boo
         db = torch.empty(d_out, dtype=torch.float32, device=dev)
     need = int(lib.ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out))
     ws = _ws(need, ws, dev)
-    st = lib.ptdit_linear_bwd(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(d_y), _dt(d_y.dtype),
-                              _ptr(dx), _ptr(dw), _ptr(db), _ptr(ws), ws.numel() * ws.element_size(), _stream())
-    _check("ptdit_linear_bwd", st)
+    if dx_add is None and dx_bf16 is None:
+        st = lib.ptdit_linear_bwd(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(d_y), _dt(d_y.dtype),
+                                  _ptr(dx), _ptr(dw), _ptr(db), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+        _check("ptdit_linear_bwd", st)
+    else:
+        st = lib.ptdit_linear_bwd_ex(_ptr(x), _dt(x.dtype), rows, d_in, d_out, _ptr(w), _ptr(d_y), _dt(d_y.dtype),
+                                     _ptr(dx), _ptr(dx_add), _ptr(dx_bf16), _ptr(dw), _ptr(db), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream())
+        _check("ptdit_linear_bwd_ex", st)
     return dx, dw, db
 
 

@@ -15,10 +15,12 @@ calls run in reverse order of the forward:
 Each attention's backward recomputes its head-major Q/K/V
 (ptdit_linear_heads) and attention output (ptdit_window_attn / ptdit_attn)
 from the block's stored inputs, then takes the output projection's gradient
-(ptdit_linear_bwd), the core's (ptdit_window_attn_bwd / ptdit_attn_bwd, on a
-bf16 dO from ptdit_f32_to_bf16), and the input projections' (ptdit_linear_bwd
-on the token-major dQ/dK/dV from ptdit_heads_to_tokens); residual branches
-join with ptdit_add_f32 and the window average's gradient accumulates into dx
+(ptdit_linear_bwd_ex, whose d_x product writes the core's bf16 dO directly),
+the core's (ptdit_window_attn_bwd / ptdit_attn_bwd), and the input
+projections' (ptdit_linear_bwd_ex on the token-major dQ/dK/dV, which the
+window core's backward writes directly, ptdit_window_attn_bwd_tokens, and the
+dense cores' pass through ptdit_heads_to_tokens; the residual branch's
+gradient added in the d_x product's epilogue); the window average's gradient accumulates into dx
 (ptdit_proxy_pool_bwd). Every step runs in the library's kernels; torch only
 holds the buffers. bf16 precision blocks with window-average proxies.
 """
@@ -78,17 +80,16 @@ class PTBlockBackward:
         B, N, D, heads = blk.B, blk.N, blk.D, blk.heads
         _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=self.qkv)
         _lib.window_attn(self.qkv, w.b_qkv, blk.g, blk.win, shift, out=self.o)
-        do32, dwo, dbo = _lib.linear_bwd(self.o, w.w_o, dy, ws=self.ws)
-        _lib.f32_to_bf16(do32, out=self.do16)
+        _, dwo, dbo = _lib.linear_bwd(self.o, w.w_o, dy, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         if self.pads:
             self.dbkv.zero_()
-        _lib.window_attn_bwd(self.qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_h,
-                             d_b_kv=self.dbkv if self.pads else None)
-        _lib.heads_to_tokens(self.dqkv_h, out=self.dqkv_t)
-        dxb, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t, ws=self.ws)
+        # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
+        _lib.window_attn_bwd(self.qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t,
+                             d_b_kv=self.dbkv if self.pads else None, tokens=True)
+        # dx_out = dy (the residual) + d(branch)/dx^T dy, joined in the product
+        _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t, ws=self.ws, dx=dx_out, dx_add=dy)
         if self.pads:   # pad slots' key/value gradients reach b_k, b_v
             _lib.add_f32(dbqkv[D:], self.dbkv.view(-1), out=dbqkv[D:])
-        _lib.add_f32(dy, dxb, out=dx_out)
         return {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
 
     def backward(self, x: torch.Tensor, dout: torch.Tensor) -> Dict[str, object]:
@@ -111,8 +112,7 @@ class PTBlockBackward:
         _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
                           B, M, heads, out=self.kv)
         _lib.attn(self.q[:, 0], self.kv[:, 0], self.kv[:, 1], out=self.o)
-        do32, dwo, dbo = _lib.linear_bwd(self.o, wc.w_o, self.dx1, ws=self.ws)
-        _lib.f32_to_bf16(do32, out=self.do16)
+        _, dwo, dbo = _lib.linear_bwd(self.o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         # dQ into the (now free) window buffers: [B, 1, heads, N, dh] and its
         # token-major [B, N, D]
         dq_h = self.dqkv_h.view(-1)[:B * N * D].view(B, 1, heads, N, D // heads)
@@ -122,23 +122,22 @@ class PTBlockBackward:
         _lib.heads_to_tokens(dq_h, out=dq_t)
         dwqkv = torch.empty(3 * D, D, dtype=torch.float32, device=x.device)
         dbqkv = torch.empty(3 * D, dtype=torch.float32, device=x.device)
-        dxq, _, _ = _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dw=dwqkv[:D], db=dbqkv[:D])
+        # dx = dx1 (the residual) + the queries' gradient, joined in the product
+        _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dx=self.dx, dx_add=self.dx1, dw=dwqkv[:D], db=dbqkv[:D])
         _lib.heads_to_tokens(self.dkv_h, out=self.dkv_t)
         dP2, _, _ = _lib.linear_bwd(blk.P2, wc.w_qkv[D:], self.dkv_t, ws=self.ws, dw=dwqkv[D:], db=dbqkv[D:])
         grads[1] = {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
-        _lib.add_f32(self.dx1, dxq, out=self.dx)
         # proxy self-attention on P (queries = keys = proxies)
         wp = w[0]
         _lib.linear_heads(blk.P.view(B * M, D), wp.w_qkv, wp.b_qkv, B, M, heads, out=self.qkvp)
         _lib.attn(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], out=self.op)
-        dop32, dwo0, dbo0 = _lib.linear_bwd(self.op, wp.w_o, dP2, ws=self.ws)
-        _lib.f32_to_bf16(dop32, out=self.dop16)
+        _, dwo0, dbo0 = _lib.linear_bwd(self.op, wp.w_o, dP2, ws=self.ws, want_dx=False, dx_bf16=self.dop16)
         _lib.attn_bwd(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], self.dop16, ws=self.ws,
                       dq=self.dqkvp_h[:, 0], dk=self.dqkvp_h[:, 1], dv=self.dqkvp_h[:, 2])
         _lib.heads_to_tokens(self.dqkvp_h, out=self.dqkvp_t)
-        dPx, dwqkv0, dbqkv0 = _lib.linear_bwd(blk.P, wp.w_qkv, self.dqkvp_t, ws=self.ws)
+        # dP = dP' (the residual) + the proxy attention's gradient
+        _, dwqkv0, dbqkv0 = _lib.linear_bwd(blk.P, wp.w_qkv, self.dqkvp_t, ws=self.ws, dx=self.dP, dx_add=dP2)
         grads[0] = {"w_qkv": dwqkv0, "b_qkv": dbqkv0, "w_o": dwo0, "b_o": dbo0}
-        _lib.add_f32(dP2, dPx, out=self.dP)
         # window average: every token of a window receives dP / P
         _lib.proxy_pool_bwd(self.dP, blk.g, blk.p, d_x=self.dx, accumulate=True)
         return {"dx": self.dx, "weights": grads}

@@ -572,9 +572,9 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
   return hip_status(launch_roll(d, stream));
 }
 
-ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
-                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv,
-                                   float* d_b_kv, hipStream_t stream) {
+static ptdit_status window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                    ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv, float* d_b_kv,
+                                    int tokens_out, hipStream_t stream) {
   if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
   ptdit_status st = check_grid(g);
   if (st) return st;
@@ -596,6 +596,7 @@ ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const voi
     return PTDIT_ERR_ALIAS;
   WindowBwdDesc d;
   d.QKV = qkv; d.bias_qkv = b_qkv; d.dO = d_o; d.dQKV = d_qkv; d.dbias_kv = d_b_kv;
+  d.tokens_out = tokens_out;
   d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D; d.heads = g.heads; d.dh = g.D / g.heads;
   d.wt = win.t; d.wh = win.h; d.ww = win.w;
   d.st = shift.t; d.sh = shift.h; d.sw = shift.w;
@@ -605,6 +606,18 @@ ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const voi
   d.scale = 1.0f / std::sqrt((float)d.dh);
   TraceScope ts(PTDIT_K_BWD_WINDOW, stream);
   return hip_status(launch_window_bwd(d, dt == PTDIT_F32, stream));
+}
+
+ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                   ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv,
+                                   float* d_b_kv, hipStream_t stream) {
+  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv, d_b_kv, 0, stream);
+}
+
+ptdit_status ptdit_window_attn_bwd_tokens(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv_t,
+                                          float* d_b_kv, hipStream_t stream) {
+  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv_t, d_b_kv, 1, stream);
 }
 
 namespace {
@@ -843,24 +856,38 @@ size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_ou
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
                               const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ptdit_linear_bwd_ex(x, x_dt, rows, d_in, d_out, w, d_y, dy_dt, d_x, nullptr, nullptr, d_w, d_b, ws,
+                             ws_bytes, stream);
+}
+
+ptdit_status ptdit_linear_bwd_ex(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
+                                 const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x,
+                                 const float* d_x_add, uint16_t* d_x_bf16, float* d_w, float* d_b, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(x_dt) || !valid_dtype(dy_dt)) return PTDIT_ERR_DTYPE;
   if (rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8) return PTDIT_ERR_SHAPE;
   if (rows > (int64_t)65535 * 32 || (int64_t)d_in * d_out > ((int64_t)1 << 31)) return PTDIT_ERR_SHAPE;
-  if (rows == 0 || (!d_x && !d_w && !d_b)) return PTDIT_OK;
-  if (!d_y || (d_w && !x) || (d_x && !w)) return PTDIT_ERR_NULL;
+  const bool want_dx = d_x || d_x_bf16;
+  if (rows == 0 || (!want_dx && !d_w && !d_b)) return PTDIT_OK;
+  if (!d_y || (d_w && !x) || (want_dx && !w)) return PTDIT_ERR_NULL;
+  if (d_x_add && !d_x) return PTDIT_ERR_NULL;  // the sum is formed in fp32, so it needs d_x
   if (!aligned16(x) || !aligned16(w) || !aligned16(d_y) || !aligned16(d_x) || !aligned16(d_w) || !aligned16(d_b) ||
-      !aligned16(ws))
+      !aligned16(ws) || !aligned16(d_x_add) || !aligned16(d_x_bf16))
     return PTDIT_ERR_ALIGN;
   const size_t need = ptdit_linear_bwd_workspace_bytes(rows, d_in, d_out);
   if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
   const size_t xb = (size_t)rows * d_in * esize(x_dt), yb = (size_t)rows * d_out * esize(dy_dt);
-  const size_t wb = (size_t)d_out * d_in * 2;
-  const void* outs[4] = {d_x, d_w, d_b, ws};
-  const size_t osz[4] = {(size_t)rows * d_in * 4, (size_t)d_out * d_in * 4, (size_t)d_out * 4, need};
-  for (int a = 0; a < 4; ++a) {
+  const size_t wb = (size_t)d_out * d_in * 2, ab = (size_t)rows * d_in * 4;
+  const void* outs[5] = {d_x, d_w, d_b, ws, d_x_bf16};
+  const size_t osz[5] = {(size_t)rows * d_in * 4, (size_t)d_out * d_in * 4, (size_t)d_out * 4, need,
+                         (size_t)rows * d_in * 2};
+  for (int a = 0; a < 5; ++a) {
     if (overlaps(outs[a], osz[a], x, xb) || overlaps(outs[a], osz[a], d_y, yb) || overlaps(outs[a], osz[a], w, wb))
       return PTDIT_ERR_ALIAS;
-    for (int b = a + 1; b < 4; ++b)
+    // the added gradient may be d_x itself (each element read, then written,
+    // by the same lane of the same tile), else it overlaps no output
+    if (!(a == 0 && d_x_add == d_x) && overlaps(outs[a], osz[a], d_x_add, ab)) return PTDIT_ERR_ALIAS;
+    for (int b = a + 1; b < 5; ++b)
       if (overlaps(outs[a], osz[a], outs[b], osz[b])) return PTDIT_ERR_ALIAS;
   }
   TraceScope ts(PTDIT_K_BWD_LINEAR, stream);
@@ -880,20 +907,22 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
   d.x = x; d.x_f32 = x_dt == PTDIT_F32;
   d.dyt = dyt; d.xt = xt;
   // with d_w, the transpose pass also leaves a bf16 copy of an fp32 d_y for d_x
-  d.dyb = (d_x && d_w && dy_dt == PTDIT_F32) ? dyb : nullptr;
+  d.dyb = (want_dx && d_w && dy_dt == PTDIT_F32) ? dyb : nullptr;
   d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
   d.rows = rows; d.d_in = d_in; d.d_out = d_out;
   if (d_w && launch_wgrad_operands(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
-  if (d_x) {
-    // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight
+  if (want_dx) {
+    // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight;
+    // the added gradient is the GEMM's residual, the bf16 copy its second
+    // output (or its only output when d_x is NULL)
     hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
     if (e != hipSuccess) return PTDIT_ERR_HIP;
     GemmDesc g;
     g.A = d.dyb ? (const void*)d.dyb : d_y; g.a_f32 = !d.dyb && dy_dt == PTDIT_F32;
     g.W = wt; g.bias = nullptr;
-    g.R = nullptr; g.r_f32 = 1;
-    g.Y = d_x; g.y_f32 = 1;
-    g.Y2 = nullptr;
+    g.R = d_x_add; g.r_f32 = 1;
+    g.Y = d_x ? (void*)d_x : (void*)d_x_bf16; g.y_f32 = d_x ? 1 : 0;
+    g.Y2 = d_x ? d_x_bf16 : nullptr;
     g.M = rows; g.N = d_in; g.K = d_out;
     g.head_major = false; g.Ntok = rows; g.heads = 0; g.dh = 0; g.D = d_in;
     g.act = 0;

@@ -75,7 +75,9 @@ struct WindowBwdParams {
   const void* QKV;       // [B][3][heads][N][dh]
   const void* bias_qkv;  // [3D] or null (pad keys/values are b_k/b_v, else 0)
   const void* dO;        // [B][N][D]
-  float* dQKV;           // [B][3][heads][N][dh]
+  float* dQKV;           // dQ, dK, dV: element (b, g, h, token, d) at
+                         // b*o_bs + g*o_gs + h*o_hs + token*o_ts + d
+  int64_t o_bs, o_gs, o_hs, o_ts;  // head-major [B][3][heads][N][dh] or token-major [B][N][3D]
   float* dbias_kv;       // [2][D], accumulated into; null when nothing pads
   int F, H, W, D, heads;
   int wt, wh, ww;
@@ -149,9 +151,9 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
-  float* dKb = dQb + gsz;
-  float* dVb = dQb + 2 * gsz;
+  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
+  float* dKb = dQb + p.o_gs;
+  float* dVb = dQb + 2 * p.o_gs;
 
   // Phase 1 (query slot i, keys sub, sub+G, ...): statistics and dQ.
   {
@@ -209,7 +211,7 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
       float mine = 0.f;
 #pragma unroll
       for (int e = 0; e < G; ++e) mine = e == sub ? part[e] : mine;
-      if (tq >= 0 && d0 + sub < DH) dQb[(int64_t)tq * DH + d0 + sub] = mine * p.scale;
+      if (tq >= 0 && d0 + sub < DH) dQb[(int64_t)tq * p.o_ts + d0 + sub] = mine * p.scale;
     }
   }
   __syncthreads();
@@ -250,8 +252,8 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
         float k = 0.f, v = 0.f;
 #pragma unroll
         for (int e = 0; e < DH; ++e) { k = e == d ? dk[e] : k; v = e == d ? dv[e] : v; }
-        dKb[(int64_t)tk * DH + d] = k;
-        dVb[(int64_t)tk * DH + d] = v;
+        dKb[(int64_t)tk * p.o_ts + d] = k;
+        dVb[(int64_t)tk * p.o_ts + d] = v;
       }
     } else if (tk == -1 && p.dbias_kv) {
       for (int d = sub; d < DH; d += G) {
@@ -382,9 +384,9 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
-  float* dKb = dQb + gsz;
-  float* dVb = dQb + 2 * gsz;
+  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
+  float* dKb = dQb + p.o_gs;
+  float* dVb = dQb + 2 * p.o_gs;
 
   // ---- phase 1: queries of wave w
   {
@@ -476,7 +478,7 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       }
       const int d = dt * 16 + 4 * g;
       if (qtok >= 0 && d < DH)
-        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * DH + d) =
+        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * p.o_ts + d) =
             float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
     }
   }
@@ -511,8 +513,8 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       const float4 kv = float4{ak[0] * p.scale, ak[1] * p.scale, ak[2] * p.scale, ak[3] * p.scale};
       const float4 vv = float4{av[0], av[1], av[2], av[3]};
       if (ktok >= 0) {
-        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
-        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
+        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * p.o_ts + d) = kv;
+        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * p.o_ts + d) = vv;
       } else if (ktok == -1 && p.dbias_kv) {
         float* bk = &padg[d];
         float* bv = &padg[DH + d];
@@ -639,9 +641,9 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * 3 * gsz + h * hs;
-  float* dKb = dQb + gsz;
-  float* dVb = dQb + 2 * gsz;
+  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
+  float* dKb = dQb + p.o_gs;
+  float* dVb = dQb + 2 * p.o_gs;
 
   // ---- phase 1: queries of wave w
   {
@@ -727,7 +729,7 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
       }
       const int d = dt * 16 + 4 * g;
       if (qtok >= 0 && d < DH)
-        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * DH + d) =
+        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * p.o_ts + d) =
             float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
     }
   }
@@ -798,8 +800,8 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
       const float4 kv = float4{dk[dt][0] * p.scale, dk[dt][1] * p.scale, dk[dt][2] * p.scale, dk[dt][3] * p.scale};
       const float4 vv = float4{dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
       if (ktok >= 0) {
-        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * DH + d) = kv;
-        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * DH + d) = vv;
+        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * p.o_ts + d) = kv;
+        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * p.o_ts + d) = vv;
       } else if (ktok == -1 && p.dbias_kv) {
         float* bk = &padg[d];
         float* bv = &padg[DH + d];
@@ -820,6 +822,12 @@ static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   WindowBwdParams p;
   p.QKV = d.QKV; p.bias_qkv = d.bias_qkv; p.dO = d.dO; p.dQKV = d.dQKV; p.dbias_kv = d.dbias_kv;
   p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D; p.heads = d.heads;
+  const int64_t N = (int64_t)d.F * d.H * d.W;
+  if (d.tokens_out) {  // [B][N][3D]: the Q/K/V projection's output gradient
+    p.o_bs = N * 3 * d.D; p.o_gs = d.D; p.o_hs = DH; p.o_ts = 3 * (int64_t)d.D;
+  } else {             // [B][3][heads][N][dh]
+    p.o_hs = N * DH; p.o_gs = d.heads * p.o_hs; p.o_bs = 3 * p.o_gs; p.o_ts = DH;
+  }
   p.wt = d.wt; p.wh = d.wh; p.ww = d.ww;
   p.st = d.st; p.sh = d.sh; p.sw = d.sw;
   p.Fp = d.Fp; p.Hp = d.Hp; p.Wp = d.Wp;

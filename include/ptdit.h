@@ -315,6 +315,18 @@ ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const voi
                                    float* d_b_kv, hipStream_t stream);
 
 /*
+ * ptdit_window_attn_bwd_tokens -- ptdit_window_attn_bwd with dQ, dK, dV
+ * written token-major: d_qkv_t [B][N][3D] fp32, element [b][t][g*D + h*dh + d]
+ * for g = Q, K, V, the output gradient of the Q/K/V projection as
+ * ptdit_linear_bwd reads it (so no layout pass sits between the two).
+ * Everything else, the padding / bias gradients and the errors as
+ * ptdit_window_attn_bwd.
+ */
+ptdit_status ptdit_window_attn_bwd_tokens(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
+                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv_t,
+                                          float* d_b_kv, hipStream_t stream);
+
+/*
  * ptdit_attn_bwd -- the core of ptdit_proxy_sa (queries = keys = proxies) or
  * ptdit_proxy_xattn (queries = tokens, keys = proxies), unmasked.
  *   q        batch b at q + b*q_bstride elements: [heads][Nq][dh], dt
@@ -370,6 +382,25 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
                               const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out);
+
+/*
+ * ptdit_linear_bwd_ex -- ptdit_linear_bwd with the two steps that join a
+ * projection's input gradient into a block's backward folded into the d_x
+ * product (the residual branches of Eq. GIIM / Eq. TCM: x_out = x_in +
+ * branch(x_in), so d x_in = d x_out + d branch):
+ *   d_x_add  [rows][d_in] fp32 or NULL: added to d_x (d_x = d_y W + d_x_add);
+ *            may be d_x itself (in place), else disjoint from every output;
+ *            requires d_x (PTDIT_ERR_NULL), and d_x_bf16 is then the rounding
+ *            of the sum
+ *   d_x_bf16 [rows][d_in] bf16 or NULL: d_x rounded to bf16 (nearest even),
+ *            the operand precision of the matrix-core attention backward
+ * d_x may be NULL when d_x_bf16 is given (only the bf16 gradient is written).
+ * Everything else, the workspace and the errors as ptdit_linear_bwd.
+ */
+ptdit_status ptdit_linear_bwd_ex(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
+                                 const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x,
+                                 const float* d_x_add, uint16_t* d_x_bf16, float* d_w, float* d_b, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 /*
  * Calls that recompute forward intermediates and chain the backward calls

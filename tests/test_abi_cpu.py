@@ -387,3 +387,21 @@ def test_calibration_calls_validate_on_the_host(lib):
     flop = ctypes.c_int64(0)
     assert lib.ptdit_calibrate_mfma(0, 10, b, ctypes.byref(flop), None) == -2
     assert lib.ptdit_calibrate_mfma(4, 10, None, ctypes.byref(flop), None) == -1
+
+
+def test_linear_bwd_ex_validates_on_the_host(lib):
+    """ptdit_linear_bwd_ex refusals (nothing launched)."""
+    import ctypes
+    x, w, dy = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 32), ctypes.c_void_p(1 << 34)
+    dx, dw, db = ctypes.c_void_p(1 << 36), ctypes.c_void_p(1 << 38), ctypes.c_void_p(1 << 39)
+    add, b16, ws = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42)
+    rows, di, do = 256, 64, 128
+    need = lib.ptdit_linear_bwd_workspace_bytes(rows, di, do)
+    call = lambda dx_=dx, add_=add, b16_=b16, dw_=dw: lib.ptdit_linear_bwd_ex(
+        x, 1, rows, di, do, w, dy, 1, dx_, add_, b16_, dw_, db, ws, need, None)
+    assert call(dx_=None) == -1                                     # d_x_add needs the fp32 d_x
+    assert call(b16_=ctypes.c_void_p((1 << 41) + 8)) == -5          # misaligned bf16 copy
+    assert call(add_=ctypes.c_void_p((1 << 38) + 64)) == -8         # added gradient inside d_w
+    assert call(b16_=ctypes.c_void_p((1 << 36) + 64)) == -8         # bf16 copy inside d_x
+    assert call(add_=ctypes.c_void_p((1 << 36) + 16)) == -8         # a shifted view of d_x
+    assert lib.ptdit_linear_bwd_ex(x, 1, 0, di, do, w, dy, 1, dx, add, b16, dw, db, ws, need, None) == 0

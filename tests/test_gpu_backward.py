@@ -101,6 +101,32 @@ def test_window_attn_bwd_vs_oracle(P, name):
         assert np.abs(rkp).max() > 1e-3 and np.abs(rvp).max() > 1e-3, "pad gradients should be nonzero here"
 
 
+@pytest.mark.parametrize("name", ["img_pad_ne_shift", "video128_pad_ne_shift", "f32_video_pad", "dh64_shift"])
+def test_window_attn_bwd_tokens_layout(P, name):
+    """ptdit_window_attn_bwd_tokens writes the same values as
+    ptdit_window_attn_bwd, token-major: bit for bit equal to the head-major
+    result after the layout change; the pad-slot bias gradients agree to the
+    order of their atomic additions."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    (B, F, H, W), D, heads, win, shift, dt, scale = WIN_CASES[name]
+    dh, N = D // heads, F * H * W
+    announce(f"window bwd tokens layout {name}")
+    q, k, v, do = make_attn_grad_inputs(B, heads, N, N, dh, seed=320 + len(name), scale=scale, dtype=dt)
+    g = np.random.Generator(np.random.PCG64(420 + len(name)))
+    bias = g.standard_normal(3 * D).astype(np.float32) * 0.5
+    prec = BF16 if dt == "bf16" else F32
+    if dt == "bf16":
+        bias = round_bf16(bias)
+    qkv = dev(np.stack([q, k, v], axis=1), prec)
+    dqkv_h, db_h = P.window_attn_bwd(qkv, dev(do, prec), (B, F, H, W, D, heads), win, shift, b_qkv=dev(bias, prec))
+    dqkv_t, db_t = _lib.window_attn_bwd(qkv, dev(do, prec), (B, F, H, W, D, heads), win, shift,
+                                        b_qkv=dev(bias, prec), tokens=True)
+    torch.cuda.synchronize()
+    assert tuple(dqkv_t.shape) == (B, N, 3 * D)
+    assert torch.equal(dqkv_t, _lib.heads_to_tokens(dqkv_h))
+    np.testing.assert_allclose(host(db_t), host(db_h), rtol=1e-5, atol=1e-5)
+
+
 def test_window_attn_bwd_full_size_sampled_windows(P):
     # the 2048^2 image grid (128 x 128 tokens, 16 heads of 72) with the TCM
     # shift: the whole backward on the GPU, seven windows (the first, the
@@ -266,6 +292,41 @@ def test_attn_bwd_full_size_video_cross_attention(P):
         assert_grad_close(dq[0, h], rq, f"dQ head {h}")
         assert_grad_close(dk[0, h], rk, f"dK head {h}")
         assert_grad_close(dv[0, h], rv, f"dV head {h}")
+
+
+@pytest.mark.parametrize("d_in,d_out", [(1152, 1152), (1152, 3456), (64, 200)])
+def test_linear_bwd_ex_joins(P, d_in, d_out):
+    """ptdit_linear_bwd_ex against ptdit_linear_bwd: the bf16-only d_x is the
+    nearest-even rounding of the fp32 d_x, bit for bit; d_x with an added
+    gradient (out of place and in place) equals d_x + add to fp32 rounding
+    (the K = 1152 products fold the addend into the accumulators mid-loop, so
+    the order of the additions differs), and its bf16 copy rounds that sum."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    from gpu_util import dev
+    rows = 2400
+    announce(f"linear_bwd_ex rows={rows} {d_in}->{d_out}")
+    g = np.random.Generator(np.random.PCG64(700 + d_out))
+    x = dev(round_bf16(g.standard_normal((rows, d_in)).astype(np.float32)), BF16)
+    w = dev(round_bf16((g.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)), BF16)
+    dy = dev(g.standard_normal((rows, d_out)).astype(np.float32), F32)
+    add = dev(g.standard_normal((rows, d_in)).astype(np.float32), F32)
+    dx0, dw0, db0 = _lib.linear_bwd(x, w, dy)
+    b16 = torch.empty(rows, d_in, dtype=BF16, device="cuda")
+    _, dw1, db1 = _lib.linear_bwd(x, w, dy, want_dx=False, dx_bf16=b16)
+    torch.cuda.synchronize()
+    assert torch.equal(b16.view(torch.int16), dx0.to(BF16).view(torch.int16))
+    assert torch.equal(dw1, dw0) and torch.equal(db1, db0)
+    ref = host(dx0).astype(np.float64) + host(add)
+    tol = 1e-5 * max(1.0, float(np.abs(ref).max()))
+    dx2 = torch.empty(rows, d_in, dtype=F32, device="cuda")
+    b16b = torch.empty(rows, d_in, dtype=BF16, device="cuda")
+    _lib.linear_bwd(x, w, dy, dx=dx2, dx_add=add, dx_bf16=b16b, want_dw=False, want_db=False)
+    inplace = add.clone()
+    _lib.linear_bwd(x, w, dy, dx=inplace, dx_add=inplace, want_dw=False, want_db=False)
+    torch.cuda.synchronize()
+    assert np.abs(host(dx2) - ref).max() <= tol
+    assert np.abs(host(inplace) - ref).max() <= tol
+    assert torch.equal(b16b.view(torch.int16), dx2.to(BF16).view(torch.int16))
 
 
 # ----------------------------------------------------------------------------- pooling
