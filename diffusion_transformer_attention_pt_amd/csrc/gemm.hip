@@ -616,12 +616,13 @@ gemm_dma_kernel(GemmParams p) {
 // (k = -1: the prologue's load); -1: none
 constexpr int pp_rblock(int k, int nb) { return k < 0 ? nb + k : (k < nb - 1 ? k : -1); }
 
-template <typename TR, typename TY, bool HEADMAJOR, int RKT>
+template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   constexpr bool RIN = RKT > 0;
-  static_assert(!RIN || RKT == 36, "one k-slice per accumulator block of a 64 x 144 wave tile");
+  static_assert(!RIN || (RKT == 36 && BM == 256), "one k-slice per accumulator block of a 64 x 144 wave tile");
+  static_assert(BM == 256 || BM == 128, "wave tiles of 64 or 32 rows");
   using TA = uint16_t;
-  constexpr int BM = 256, BN = 288, WM = 4, WN = 2, NW = 8, STAGES = 4;
+  constexpr int BN = 288, WM = 4, WN = 2, NW = 8, STAGES = 4;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
   constexpr int NB = FN * FM;  // accumulator blocks per wave
   constexpr int RL = RIN ? 1 : 0;
@@ -971,6 +972,15 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 != 0 || p.K < 256) return hipErrorInvalidValue;  // KT % 4 == 0, KT >= 8
   const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
   if (tiles <= 0) return hipSuccess;
+  if (tiles < 256) {
+    // fewer 256-row tiles than CUs (the 1024^2 block's 8192-row projections
+    // onto D): 128-row tiles (waves of 32 x 144) keep every CU busy; the
+    // residual is added in the epilogue
+    const int64_t t128 = ((p.M + 127) / 128) * (int64_t)((p.N + 287) / 288);
+    hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0, 128>), dim3((unsigned)t128, (unsigned)p.splits), dim3(512),
+                       0, s, p);
+    return hipGetLastError();
+  }
   if constexpr (!HM) {
     // the model width D = 1152 with whole column tiles: residual folded into
     // the main loop (rows past M of a ragged last row tile are clamped)
