@@ -223,7 +223,10 @@ def test_roll_bit_exact(P, grid, shift, B, D, dt):
                                            # so three of its four row waves hold no real row)
                                            (2100, 1152, 1152), (2350, 1152, 2304),
                                            # few rows on 32-row tiles (ragged: 300 = 9 x 32 + 12)
-                                           (300, 1152, 2304)])
+                                           (300, 1152, 2304),
+                                           # 268 tiles of 256 rows: one whole round (16384 rows),
+                                           # then 616 rows on 128-row tiles (ragged: 104 in the last)
+                                           (17000, 1152, 1152)])
 @pytest.mark.parametrize("mode", ["bf16", "bf16_f32in_res", "bf16_res32", "bf16_res16", "f32"])
 def test_linear(P, rows, din, dout, mode):
     """bf16_res32 / bf16_res16: bf16 x with an fp32 / bf16 residual, the two
