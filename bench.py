@@ -171,26 +171,40 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
         from diffusion_transformer_attention_pt_amd import PTBlockBackward
         from synth_inputs import make_x
         xb = torch.from_numpy(make_x(wl)).to(prec).to(dev)
-        blk.forward(xb)
         bwd = PTBlockBackward(blk)
         dout = torch.randn(B, N, D, device=dev)
-        bwd.backward(xb, dout)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            bwd.backward(xb, dout)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
         fl = blk.flops()
         # algorithmic backward FLOP: every projection twice (dX, dW), every
         # attention core's five products (2.5 times its two forward products);
         # the recomputed forward projections and cores are not counted
         bflop = 2 * fl["projection"] + 2.5 * fl["core"]
-        res["block_backward"] = {"avg_ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
-                                 "gflop": round(bflop / 1e9, 2), "tflops": round(bflop / (ms * 1e-3) / 1e12, 2),
-                                 "peak_frac": round(bflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        rate = lambda ms: {"avg_ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+                           "gflop": round(bflop / 1e9, 2), "tflops": round(bflop / (ms * 1e-3) / 1e12, 2),
+                           "peak_frac": round(bflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # after an inference forward: Q/K/V and attention outputs recomputed
+        blk.forward(xb)
+        res["block_backward"] = rate(timed(lambda: bwd.backward(xb, dout)))
+        # after a keep-mode (training) forward: read back instead
+        blk.forward(xb, keep=True)
+        res["block_backward_kept"] = rate(timed(lambda: bwd.backward(xb, dout)))
+        # one training step of the block: keep-mode forward + backward
+        ms_f = timed(lambda: blk.forward(xb, keep=True))
+        ms_t = timed(lambda: (blk.forward(xb, keep=True), bwd.backward(xb, dout)))
+        res["train_step"] = {"forward_keep_ms": round(ms_f, 4), "step_ms": round(ms_t, 4),
+                             "tokens_per_s": round(B * N / (ms_t * 1e-3), 1),
+                             "tflops": round((fl["total"] + bflop) / (ms_t * 1e-3) / 1e12, 2)}
     for name, (cls, fn, flop, nbytes) in cases.items():
         fn()
         torch.cuda.synchronize()

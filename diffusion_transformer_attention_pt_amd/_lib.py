@@ -35,7 +35,7 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
             "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
             "ptdit_calibrate_read", "ptdit_calibrate_copy", "ptdit_linear_bwd_ex",
-            "ptdit_window_attn_bwd_tokens"]
+            "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep"]
 
 
 class Grid(ctypes.Structure):
@@ -95,6 +95,7 @@ def load() -> ctypes.CDLL:
         "ptdit_trace_disable": [],
         "ptdit_window_attn_bwd": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
         "ptdit_window_attn_bwd_tokens": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
+        "ptdit_window_sa_keep": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
         "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
         "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
@@ -434,6 +435,45 @@ def shift_window_sa(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], sh
                                    _stream())
     _check("ptdit_shift_window_sa", st)
     return out
+
+
+def window_sa_keep(x: torch.Tensor, grid: Sequence[int], win: Sequence[int], shift: Sequence[int],
+                   w: AttnWeights, ws: torch.Tensor, residual: bool = True, out_dtype: Optional[torch.dtype] = None,
+                   out: Optional[torch.Tensor] = None, x_lowp: Optional[torch.Tensor] = None,
+                   out_lowp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """window_sa (shift (0, 0, 0)) or shift_window_sa that leaves the head-major
+    Q/K/V and the attention output in ws (ptdit_window_sa_keep; window_ws_views
+    reads them)."""
+    lib = load()
+    _window_shapes(grid, w, x, out, x_lowp, out_lowp)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    need = workspace_bytes(OP_WINDOW_SA, grid, 0, win, w.dtype)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"window_sa_keep: the workspace needs {need} bytes")
+    cw = w.c()
+    st = lib.ptdit_window_sa_keep(_ptr(x), _ptr(x_lowp), _dt(x.dtype), Grid(*grid), Win3(*win), Win3(*shift),
+                                  ctypes.byref(cw), int(residual), _ptr(out), _ptr(out_lowp), _dt(out.dtype),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _dt(w.dtype), _stream())
+    _check("ptdit_window_sa_keep", st)
+    return out
+
+
+def _align(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+def window_ws_views(ws: torch.Tensor, grid: Sequence[int], prec: torch.dtype):
+    """(qkv [B, 3, heads, N, dh], o [B, N, D]) views of a window call's
+    workspace (the layout ptdit_window_sa_keep documents)."""
+    B, F, H, W, D, heads = grid
+    N = F * H * W
+    es = torch.tensor([], dtype=prec).element_size()
+    flat = ws.view(torch.uint8).view(-1)
+    qkv = flat[:B * 3 * N * D * es].view(prec).view(B, 3, heads, N, D // heads)
+    off = _align(B * 3 * N * D * es)
+    o = flat[off:off + B * N * D * es].view(prec).view(B, N, D)
+    return qkv, o
 
 
 def roll3d(x: torch.Tensor, grid: Sequence[int], shift: Sequence[int], inverse: bool = False,

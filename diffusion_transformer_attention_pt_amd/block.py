@@ -87,27 +87,70 @@ class PTBlockAttention:
             self.x4_lowp = torch.empty_like(self.x1_lowp) if lowp else None
             need += [_lib.workspace_bytes(_lib.OP_PROXY_XATTN, self.g, self.L, (1, 1, 1), prec),
                      _lib.workspace_bytes(_lib.OP_MLP, (B * self.N, 1, 1, 1, D, 1), self.hidden, (1, 1, 1), prec)]
+        self._ws_need = list(need[:3])
         need = max(need)
         self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        self._kws = None     # per-call workspaces of keep mode (allocated on first use)
+        self.kept = None     # views of what the last keep-mode forward left for the backward
 
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, keep: bool = False) -> torch.Tensor:
+        """One forward. keep=True (training): every attention call gets its own
+        workspace and the window attentions run as ptdit_window_sa_keep, so the
+        Q/K/V and attention outputs of all four attentions stay for the
+        backward (self.kept) instead of being recomputed."""
         g, w = self.g, self.weights
+        if keep:
+            if self._kws is None:
+                n_sa, n_x, n_w = self._ws_need
+                self._kws = [torch.empty(n, dtype=torch.uint8, device=self.device) for n in (n_sa, n_x, n_w, n_w)]
+            ws_sa, ws_x, ws_w, ws_s = self._kws
+        else:
+            ws_sa = ws_x = ws_w = ws_s = self.ws
         if self.proxy_mode == "mean":
             _lib.proxy_pool(x, g, self.p, out=self.P)
         else:
             _lib.proxy_select(x, g, self.p, self.proxy_offsets, out=self.P)
-        _lib.proxy_sa(self.P, self.heads, w[0], residual=True, ws=self.ws, out=self.P2)
-        _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=self.ws, out=self.x1, out_lowp=self.x1_lowp)
-        _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2,
-                       x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
-        _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3,
-                             x_lowp=self.x2_lowp, out_lowp=self.x3_lowp if self.full else None)
+        _lib.proxy_sa(self.P, self.heads, w[0], residual=True, ws=ws_sa, out=self.P2)
+        _lib.proxy_xattn(x, g, self.P2, w[1], residual=True, ws=ws_x, out=self.x1, out_lowp=self.x1_lowp)
+        if keep:
+            _lib.window_sa_keep(self.x1, g, self.win, (0, 0, 0), w[2], ws_w, residual=True, out=self.x2,
+                                x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
+            _lib.window_sa_keep(self.x2, g, self.win, self.shift, w[3], ws_s, residual=True, out=self.x3,
+                                x_lowp=self.x2_lowp, out_lowp=self.x3_lowp if self.full else None)
+            self.kept = self._kept_views()
+        else:
+            self.kept = None
+            _lib.window_sa(self.x1, g, self.win, w[2], residual=True, ws=self.ws, out=self.x2,
+                           x_lowp=self.x1_lowp, out_lowp=self.x2_lowp)
+            _lib.shift_window_sa(self.x2, g, self.win, self.shift, w[3], residual=True, ws=self.ws, out=self.x3,
+                                 x_lowp=self.x2_lowp, out_lowp=self.x3_lowp if self.full else None)
         if not self.full:
             return self.x3
         _lib.proxy_xattn(self.x3, g, self.text, self.w_text, residual=True, ws=self.ws, out=self.x4,
                          out_lowp=self.x4_lowp, x_lowp=self.x3_lowp)
         _lib.mlp(self.x4, self.w_mlp, residual=True, ws=self.ws, out=self.x5, x_lowp=self.x4_lowp)
         return self.x5
+
+    def _kept_views(self) -> Dict[str, torch.Tensor]:
+        """Views of the keep-mode workspaces in the layouts the calls document:
+        proxy SA [Q/K/V head-major | O], cross-attention [Q | K/V head-major |
+        O], window attentions [Q/K/V head-major | O], each part 256-byte
+        aligned."""
+        B, N, M, D, heads, prec = self.B, self.N, self.M, self.D, self.heads, self.prec
+        dh = D // heads
+        es = torch.tensor([], dtype=prec).element_size()
+        al = lambda n: (n + 255) // 256 * 256
+        part = lambda ws, off, n, shape: ws[off:off + n * es].view(prec).view(*shape)
+        ws_sa, ws_x, ws_w, ws_s = self._kws
+        out = {"sa_qkv": part(ws_sa, 0, B * 3 * M * D, (B, 3, heads, M, dh)),
+               "sa_o": part(ws_sa, al(B * 3 * M * D * es), B * M * D, (B, M, D)),
+               "x_q": part(ws_x, 0, B * N * D, (B, 1, heads, N, dh))}
+        kv_off = al(B * N * D * es)
+        out["x_kv"] = part(ws_x, kv_off, B * 2 * M * D, (B, 2, heads, M, dh))
+        out["x_o"] = part(ws_x, kv_off + al(B * 2 * M * D * es), B * N * D, (B, N, D))
+        out["wsa_qkv"], out["wsa_o"] = _lib.window_ws_views(ws_w, self.g, prec)
+        out["swsa_qkv"], out["swsa_o"] = _lib.window_ws_views(ws_s, self.g, prec)
+        return out
 
     def intermediates(self) -> Dict[str, torch.Tensor]:
         out = {"P": self.P, "P2": self.P2, "x1": self.x1, "x2": self.x2, "x3": self.x3}

@@ -12,9 +12,10 @@ calls run in reverse order of the forward:
     P' = P + SA(P)       ->  dP  = dP' + dSA/dP^T dP'
     P  = Averaging(x)    ->  dx += Averaging^T dP
 
-Each attention's backward recomputes its head-major Q/K/V
-(ptdit_linear_heads) and attention output (ptdit_window_attn / ptdit_attn)
-from the block's stored inputs, then takes the output projection's gradient
+Each attention's backward takes its head-major Q/K/V and attention output
+from the forward when it ran with keep=True (the calls' workspaces, kept
+apart), else recomputes them (ptdit_linear_heads, ptdit_window_attn /
+ptdit_attn) from the block's stored inputs; then it takes takes the output projection's gradient
 (ptdit_linear_bwd_ex, whose d_x product writes the core's bf16 dO directly),
 the core's (ptdit_window_attn_bwd / ptdit_attn_bwd), and the input
 projections' (ptdit_linear_bwd_ex on the token-major dQ/dK/dV, which the
@@ -73,18 +74,23 @@ class PTBlockBackward:
                    int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, M, M, dh)))
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
-    def _window(self, xl: torch.Tensor, w: _lib.AttnWeights, shift, dy: torch.Tensor, dx_out: torch.Tensor):
+    def _window(self, xl: torch.Tensor, w: _lib.AttnWeights, shift, dy: torch.Tensor, dx_out: torch.Tensor,
+                kept=None):
         """One window attention's backward: returns its weight gradients and
-        writes dx_out = dy + d(branch)/dx^T dy."""
+        writes dx_out = dy + d(branch)/dx^T dy. kept: (qkv, o) of the forward."""
         blk = self.blk
         B, N, D, heads = blk.B, blk.N, blk.D, blk.heads
-        _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=self.qkv)
-        _lib.window_attn(self.qkv, w.b_qkv, blk.g, blk.win, shift, out=self.o)
-        _, dwo, dbo = _lib.linear_bwd(self.o, w.w_o, dy, ws=self.ws, want_dx=False, dx_bf16=self.do16)
+        if kept is not None:
+            qkv, o = kept
+        else:
+            qkv, o = self.qkv, self.o
+            _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=qkv)
+            _lib.window_attn(qkv, w.b_qkv, blk.g, blk.win, shift, out=o)
+        _, dwo, dbo = _lib.linear_bwd(o, w.w_o, dy, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         if self.pads:
             self.dbkv.zero_()
         # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
-        _lib.window_attn_bwd(self.qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t,
+        _lib.window_attn_bwd(qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t,
                              d_b_kv=self.dbkv if self.pads else None, tokens=True)
         # dx_out = dy (the residual) + d(branch)/dx^T dy, joined in the product
         _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t, ws=self.ws, dx=dx_out, dx_add=dy)
@@ -93,7 +99,8 @@ class PTBlockBackward:
         return {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
 
     def backward(self, x: torch.Tensor, dout: torch.Tensor) -> Dict[str, object]:
-        """Gradients after blk.forward(x) (whose intermediates it reads).
+        """Gradients after blk.forward(x) or blk.forward(x, keep=True) (whose
+        intermediates it reads; with keep, also its Q/K/V and attention outputs).
         dout: fp32 [B, N, D]. Returns {"dx": fp32 [B, N, D], "weights": [per
         attention (proxy SA, cross, WSA, SWSA) {"w_qkv", "b_qkv", "w_o",
         "b_o"}]} (all fp32)."""
@@ -103,21 +110,28 @@ class PTBlockBackward:
         if dout.dtype != torch.float32 or not dout.is_contiguous():
             raise ValueError("dout must be a contiguous fp32 tensor")
         grads: List[dict] = [None] * 4
-        grads[3] = self._window(blk.x2_lowp, w[3], blk.shift, dout, self.dx2)
-        grads[2] = self._window(blk.x1_lowp, w[2], (0, 0, 0), self.dx2, self.dx1)
+        k = blk.kept
+        grads[3] = self._window(blk.x2_lowp, w[3], blk.shift, dout, self.dx2,
+                                kept=(k["swsa_qkv"], k["swsa_o"]) if k else None)
+        grads[2] = self._window(blk.x1_lowp, w[2], (0, 0, 0), self.dx2, self.dx1,
+                                kept=(k["wsa_qkv"], k["wsa_o"]) if k else None)
         # cross-attention: tokens are queries, the attended proxies P' keys/values
         wc = w[1]
-        _lib.linear_heads(x.view(B * N, D), wc.w_qkv[:D], wc.b_qkv[:D] if wc.b_qkv is not None else None,
-                          B, N, heads, out=self.q)
-        _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
-                          B, M, heads, out=self.kv)
-        _lib.attn(self.q[:, 0], self.kv[:, 0], self.kv[:, 1], out=self.o)
-        _, dwo, dbo = _lib.linear_bwd(self.o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
+        if k:
+            q, kv, o = k["x_q"], k["x_kv"], k["x_o"]
+        else:
+            q, kv, o = self.q, self.kv, self.o
+            _lib.linear_heads(x.view(B * N, D), wc.w_qkv[:D], wc.b_qkv[:D] if wc.b_qkv is not None else None,
+                              B, N, heads, out=q)
+            _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
+                              B, M, heads, out=kv)
+            _lib.attn(q[:, 0], kv[:, 0], kv[:, 1], out=o)
+        _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         # dQ into the (now free) window buffers: [B, 1, heads, N, dh] and its
         # token-major [B, N, D]
         dq_h = self.dqkv_h.view(-1)[:B * N * D].view(B, 1, heads, N, D // heads)
         dq_t = self.dqkv_t.view(-1)[:B * N * D].view(B, N, D)
-        _lib.attn_bwd(self.q[:, 0], self.kv[:, 0], self.kv[:, 1], self.do16, ws=self.ws,
+        _lib.attn_bwd(q[:, 0], kv[:, 0], kv[:, 1], self.do16, ws=self.ws,
                       dq=dq_h[:, 0], dk=self.dkv_h[:, 0], dv=self.dkv_h[:, 1])
         _lib.heads_to_tokens(dq_h, out=dq_t)
         dwqkv = torch.empty(3 * D, D, dtype=torch.float32, device=x.device)
@@ -129,10 +143,14 @@ class PTBlockBackward:
         grads[1] = {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
         # proxy self-attention on P (queries = keys = proxies)
         wp = w[0]
-        _lib.linear_heads(blk.P.view(B * M, D), wp.w_qkv, wp.b_qkv, B, M, heads, out=self.qkvp)
-        _lib.attn(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], out=self.op)
-        _, dwo0, dbo0 = _lib.linear_bwd(self.op, wp.w_o, dP2, ws=self.ws, want_dx=False, dx_bf16=self.dop16)
-        _lib.attn_bwd(self.qkvp[:, 0], self.qkvp[:, 1], self.qkvp[:, 2], self.dop16, ws=self.ws,
+        if k:
+            qkvp, op = k["sa_qkv"], k["sa_o"]
+        else:
+            qkvp, op = self.qkvp, self.op
+            _lib.linear_heads(blk.P.view(B * M, D), wp.w_qkv, wp.b_qkv, B, M, heads, out=qkvp)
+            _lib.attn(qkvp[:, 0], qkvp[:, 1], qkvp[:, 2], out=op)
+        _, dwo0, dbo0 = _lib.linear_bwd(op, wp.w_o, dP2, ws=self.ws, want_dx=False, dx_bf16=self.dop16)
+        _lib.attn_bwd(qkvp[:, 0], qkvp[:, 1], qkvp[:, 2], self.dop16, ws=self.ws,
                       dq=self.dqkvp_h[:, 0], dk=self.dqkvp_h[:, 1], dv=self.dqkvp_h[:, 2])
         _lib.heads_to_tokens(self.dqkvp_h, out=self.dqkvp_t)
         # dP = dP' (the residual) + the proxy attention's gradient

@@ -136,7 +136,7 @@ const void* offset_elems(const void* p, int64_t elems, ptdit_dtype dt) {
 ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                            ptdit_win3 win, ptdit_win3 shift, const ptdit_attn_w* w,
                            int32_t add_residual, void* out, void* out_lowp, ptdit_dtype out_dt,
-                           void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream) {
+                           void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream, bool keep = false) {
   ptdit_status st = check_grid(g);
   if (st) return st;
   if ((st = check_io_dtypes(prec, x_dt, out_dt))) return st;
@@ -174,6 +174,7 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   const void* xa = x_lowp ? x_lowp : (x_dt == PTDIT_BF16 ? x : nullptr);
   WFusedDesc fd;
   fd.X = xa; fd.w_qkv = w->w_qkv; fd.b_qkv = w->b_qkv; fd.O = o;
+  fd.qkv_out = keep ? qkv : nullptr;  // the unfused path writes Q/K/V there anyway
   fd.B = g.B; fd.F = g.F; fd.H = g.H; fd.W = g.W; fd.D = D; fd.heads = g.heads; fd.dh = D / g.heads;
   fd.wt = win.t; fd.wh = win.h; fd.ww = win.w;
   fd.st = shift.t; fd.sh = shift.h; fd.sw = shift.w;
@@ -542,6 +543,14 @@ ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtyp
                                    hipStream_t stream) {
   return window_common(x, x_lowp, x_dt, g, win, shift, w, add_residual, out, out_lowp, out_dt, ws,
                        ws_bytes, prec, stream);
+}
+
+ptdit_status ptdit_window_sa_keep(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
+                                  ptdit_win3 win, ptdit_win3 shift, const ptdit_attn_w* w, int32_t add_residual,
+                                  void* out, void* out_lowp, ptdit_dtype out_dt, void* ws, size_t ws_bytes,
+                                  ptdit_dtype prec, hipStream_t stream) {
+  return window_common(x, x_lowp, x_dt, g, win, shift, w, add_residual, out, out_lowp, out_dt, ws, ws_bytes, prec,
+                       stream, true);
 }
 
 ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t inverse,

@@ -82,6 +82,7 @@ hipError_t launch_window(const WindowDesc& d, int f32, hipStream_t s);
 struct WFusedDesc {
   const void* X; const void* w_qkv; const void* b_qkv;
   void* O;
+  void* qkv_out = nullptr;  // optional head-major Q/K/V [B][3][heads][N][dh] (the backward's copy)
   int B, F, H, W, D, heads, dh;
   int wt, wh, ww;
   int st, sh, sw;

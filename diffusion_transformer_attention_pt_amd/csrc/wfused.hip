@@ -24,7 +24,9 @@
 // one-pass softmax over the window's L keys held in registers, O^T = V^T P^T.
 // O goes back over the wave's own Q rows and leaves as whole 288-byte token
 // rows (token-major bf16, the output projection's operand). Q, K and V never
-// reach HBM. The arithmetic is that of the unfused path (same k order in the
+// reach HBM, except in the KEEP instance (training forward), which also
+// copies the staged Q/K/V of the real tokens out head-major for the backward.
+// The arithmetic is that of the unfused path (same k order in the
 // projection, same rounding to bf16, same attention steps), so both give the
 // same attention output.
 #include <atomic>
@@ -76,6 +78,7 @@ struct WFusedParams {
   const uint16_t* W;     // w_qkv [3D][D] bf16
   const uint16_t* bias;  // b_qkv [3D] bf16 or null
   uint16_t* O;           // [B][N][D] bf16
+  uint16_t* QKV;         // KEEP: head-major Q/K/V [B][3][heads][N][72] bf16 of the real tokens
   int N, D;
   int F, H, Wd;
   int wt, wh, ww;
@@ -91,7 +94,7 @@ __device__ __forceinline__ int wf_region(int k, int L, int w, int s) {
   return k < L - w ? 0 : (k < L - s ? 1 : 2);
 }
 
-template <int L, bool MASKED>
+template <int L, bool MASKED, bool KEEP>
 __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   using SG = WfStage<L>;
   constexpr int SLOT = (WF_SA + WF_SB) * 16 > SG::SLOT_BYTES ? (WF_SA + WF_SB) : (SG::SLOT_BYTES + 15) / 16;
@@ -343,8 +346,8 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
         const uint32_t rv = real_v >> (4 * j);
         const float v0 = ((rv & 1u) ? acc[i][j][0] : 0.f) + bvn, v1 = ((rv & 2u) ? acc[i][j][1] : 0.f) + bvn;
         const float v2 = ((rv & 4u) ? acc[i][j][2] : 0.f) + bvn, v3 = ((rv & 8u) ? acc[i][j][3] : 0.f) + bvn;
-        *reinterpret_cast<uint2*>(vt_base(w) + n * SG::VTP + (r0 - w * L + 4 * g)) =
-            uint2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
+        const uint2 pk = uint2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
+        *reinterpret_cast<uint2*>(vt_base(w) + n * SG::VTP + (r0 - w * L + 4 * g)) = pk;
       }
       continue;
     }
@@ -367,6 +370,34 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     }
   }
   ring_barrier();
+  if constexpr (KEEP) {
+    // Q, K and V of the real tokens, head-major, from the staging: per
+    // (slot, Q/K/V, head) 72 bf16 = 9 chunks of 16 bytes; a V chunk gathers 8
+    // channel rows of the transposed V (adjacent lanes read adjacent slots)
+    const int64_t heads = (int64_t)p.head_pairs * 2;
+    for (int idx = tid; idx < WF_BM * 3 * 2 * 9; idx += 512) {
+      const int sl = idx / 54, rem = idx - sl * 54;
+      const int gq = rem / 18, hh = (rem / 9) & 1, ch = rem % 9;
+      const int grow = grow_s[sl];
+      if (grow < 0) continue;
+      const int w = sl / L, e_ = sl - w * L;
+      uint4 val;
+      if (gq < 2) {
+        val = *reinterpret_cast<const uint4*>((gq == 0 ? qk_base(w) : k_base(w)) +
+                                              (e_ * WF_QP + hh * WF_DH + ch * 8) * 2);
+      } else {
+        const uint16_t* vs = vt_base(w) + (hh * WF_DH + ch * 8) * SG::VTP + e_;
+        uint32_t u[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u[k] = (uint32_t)vs[(2 * k) * SG::VTP] | ((uint32_t)vs[(2 * k + 1) * SG::VTP] << 16);
+        val = uint4{u[0], u[1], u[2], u[3]};
+      }
+      const int64_t bb = grow / p.N, tok = grow - bb * p.N;
+      *reinterpret_cast<uint4*>(p.QKV + (((bb * 3 + gq) * heads + hp * 2 + hh) * p.N + tok) * WF_DH + ch * 8) = val;
+    }
+    // every Q row read before a wave writes its O over its own Q rows
+    ring_barrier();
+  }
 
   // attention: wave -> 32 queries of one (window, head) pair
   constexpr int WPP = L / 32;  // waves per pair
@@ -518,14 +549,14 @@ static int device_cus() {
   return n;
 }
 
-template <int L, bool M>
+template <int L, bool M, bool K>
 static hipError_t run_wfused(const WFusedParams& p, hipStream_t s) {
   const int ntiles = p.row_tiles * p.head_pairs;
   // a multiple of 8 workgroups (the XCD count), at most one per CU
   int grid = device_cus() / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > ntiles) grid = ntiles;
-  hipLaunchKernelGGL((wfused_kernel<L, M>), dim3((unsigned)grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((wfused_kernel<L, M, K>), dim3((unsigned)grid), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -537,6 +568,7 @@ hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s) {
   p.W = reinterpret_cast<const uint16_t*>(d.w_qkv);
   p.bias = reinterpret_cast<const uint16_t*>(d.b_qkv);
   p.O = reinterpret_cast<uint16_t*>(d.O);
+  p.QKV = reinterpret_cast<uint16_t*>(d.qkv_out);
   p.N = d.F * d.H * d.W;
   p.D = d.D;
   p.F = d.F; p.H = d.H; p.Wd = d.W;
@@ -549,9 +581,14 @@ hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s) {
   p.sl2 = d.scale * 1.4426950408889634f;
   const bool masked = (d.st | d.sh | d.sw) != 0;
   const int L = d.wt * d.wh * d.ww;
-  if (L == 32) return masked ? run_wfused<32, true>(p, s) : run_wfused<32, false>(p, s);
-  if (L == 64) return masked ? run_wfused<64, true>(p, s) : run_wfused<64, false>(p, s);
-  return masked ? run_wfused<128, true>(p, s) : run_wfused<128, false>(p, s);
+  if (p.QKV) {  // the backward's copy of Q/K/V as well
+    if (L == 32) return masked ? run_wfused<32, true, true>(p, s) : run_wfused<32, false, true>(p, s);
+    if (L == 64) return masked ? run_wfused<64, true, true>(p, s) : run_wfused<64, false, true>(p, s);
+    return masked ? run_wfused<128, true, true>(p, s) : run_wfused<128, false, true>(p, s);
+  }
+  if (L == 32) return masked ? run_wfused<32, true, false>(p, s) : run_wfused<32, false, false>(p, s);
+  if (L == 64) return masked ? run_wfused<64, true, false>(p, s) : run_wfused<64, false, false>(p, s);
+  return masked ? run_wfused<128, true, false>(p, s) : run_wfused<128, false, false>(p, s);
 }
 
 }  // namespace ptdit

@@ -269,6 +269,22 @@ ptdit_status ptdit_shift_window_sa(const void* x, const void* x_lowp, ptdit_dtyp
                                    hipStream_t stream);
 
 /*
+ * ptdit_window_sa_keep -- ptdit_window_sa (shift 0) or ptdit_shift_window_sa
+ * that leaves in the workspace what the backward pass of Eq. TCM reads, so a
+ * training step need not recompute it: on return ws holds the head-major
+ * Q/K/V [B][3][heads][N][dh] (prec, biases added, the real tokens) at offset
+ * 0 and the attention output [B][N][D] (prec) at the next 256-byte boundary
+ * (each call needs its own workspace for them to survive), the layout
+ * ptdit_window_attn_bwd and ptdit_linear_bwd take. The same workspace size
+ * (ptdit_workspace_bytes) and errors as the plain calls; the fused path writes
+ * Q/K/V in addition to its output, the unfused one writes them anyway.
+ */
+ptdit_status ptdit_window_sa_keep(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
+                                  ptdit_win3 win, ptdit_win3 shift, const ptdit_attn_w* w, int32_t add_residual,
+                                  void* out, void* out_lowp, ptdit_dtype out_dt, void* ws, size_t ws_bytes,
+                                  ptdit_dtype prec, hipStream_t stream);
+
+/*
  * ptdit_roll3d -- the 3D cyclic shift of window_shift / window_Ishift as a
  * stand-alone copy (the attention calls never materialise it):
  * inverse == 0: y[t,i,j] = x[(t+s_t) mod F, (i+s_h) mod H, (j+s_w) mod W];

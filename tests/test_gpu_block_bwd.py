@@ -61,13 +61,20 @@ def test_block_backward_vs_oracle(P, name):
     dout = g.standard_normal((wl.B, wl.N, wl.D)).astype(np.float32)
     blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=torch.bfloat16)
     xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
-    blk.forward(xd)
     bwd = P.PTBlockBackward(blk)
-    got = bwd.backward(xd, torch.from_numpy(dout).cuda())
-    torch.cuda.synchronize()
     ref = O.block_bwd(x, wl.grid, wl.p, wl.win, wl.shift, ws, wl.heads, dout, pool="f32")
+    # recompute mode (forward for inference), then keep mode (the forward's
+    # Q/K/V and attention outputs read back instead of recomputed)
+    for keep in (False, True):
+        announce(f"  keep={keep}")
+        blk.forward(xd, keep=keep)
+        got = bwd.backward(xd, torch.from_numpy(dout).cuda())
+        torch.cuda.synchronize()
+        _check_block_grads(got, ref, wl.D)
+
+
+def _check_block_grads(got, ref, D):
     assert_grad_close(host(got["dx"]), ref["dx"], "dx")
-    D = wl.D
     for a, att in enumerate(("proxy SA", "cross", "WSA", "SWSA")):
         gw, rw = got["weights"][a], ref["weights"][a]
         wqkv, bqkv = host(gw["w_qkv"]), host(gw["b_qkv"])
@@ -83,6 +90,58 @@ def test_block_backward_vs_oracle(P, name):
         assert mk <= bar
         assert_grad_close(host(gw["w_o"]), rw["wo"], f"{att} dW_o")
         assert_grad_close(host(gw["b_o"]), rw["bo"], f"{att} db_o")
+
+
+@pytest.mark.parametrize("name,prec", [("batch2_pad", torch.bfloat16), ("video_pad", torch.bfloat16),
+                                       ("batch2_pad", torch.float32)])
+def test_keep_mode_tensors(P, name, prec):
+    """What a keep-mode forward leaves for the backward: the block output is
+    bit for bit the recompute-mode output (the same kernels; keep only adds
+    writes); the proxy SA and cross-attention Q/K/V and outputs are bit for
+    bit what the backward's recompute calls produce (the same projection and
+    attention kernels); so are the window attentions' Q/K/V and outputs,
+    which with bf16 come from the fused projection + attention kernel: it
+    takes the projection's k order, roundings and attention steps of the
+    separate calls."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    wl = CASES[name]
+    announce(f"keep tensors {name} {prec} grid={(wl.B,) + wl.grid} win={wl.win} shift={wl.shift}")
+    B, N, M, D, heads = wl.B, wl.N, wl.M, wl.D, wl.heads
+    x = make_x(wl)
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, make_all_weights(wl),
+                             prec=prec)
+    xd = torch.from_numpy(x).to(prec).cuda()
+    y0 = blk.forward(xd).clone()
+    y1 = blk.forward(xd, keep=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), "keep changed the block output"
+    k = blk.kept
+    w = blk.weights
+    xl = lambda t, lo: (lo if lo is not None else t.to(prec))
+    # proxy SA: Q/K/V of P, attention of them
+    qkvp = _lib.linear_heads(blk.P.view(B * M, D), w[0].w_qkv, w[0].b_qkv, B, M, heads)
+    op = _lib.attn(qkvp[:, 0], qkvp[:, 1], qkvp[:, 2])
+    torch.cuda.synchronize()
+    assert torch.equal(k["sa_qkv"], qkvp), "proxy SA Q/K/V"
+    assert torch.equal(k["sa_o"], op), "proxy SA output"
+    # cross-attention: Q of the tokens, K/V of P'
+    wc = w[1]
+    q = _lib.linear_heads(xd.view(B * N, D), wc.w_qkv[:D], wc.b_qkv[:D], B, N, heads)
+    kv = _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:], B, M, heads)
+    o = _lib.attn(q[:, 0], kv[:, 0], kv[:, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(k["x_q"], q), "cross-attention Q"
+    assert torch.equal(k["x_kv"], kv), "cross-attention K/V"
+    assert torch.equal(k["x_o"], o), "cross-attention output"
+    # window attentions
+    for nm, src, lo, wt, sh in (("wsa", blk.x1, blk.x1_lowp, w[2], (0, 0, 0)),
+                                ("swsa", blk.x2, blk.x2_lowp, w[3], wl.shift)):
+        a = xl(src, lo).view(B * N, D)
+        qkv = _lib.linear_heads(a, wt.w_qkv, wt.b_qkv, B, N, heads)
+        ow = _lib.window_attn(qkv, wt.b_qkv, blk.g, wl.win, sh)
+        torch.cuda.synchronize()
+        assert torch.equal(k[nm + "_qkv"], qkv), nm + " Q/K/V"
+        assert torch.equal(k[nm + "_o"], ow), nm + " output"
 
 
 def test_chaining_primitives(P):

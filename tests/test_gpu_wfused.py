@@ -9,7 +9,9 @@ Each case checks, through the C ABI:
   * equality, bit for bit, with the unfused path (projection GEMM to a
     head-major Q/K/V workspace, then the window kernel), which an fp32 input
     without a bf16 copy takes: both compute the same bf16 Q/K/V in the same
-    order and the same attention steps.
+    order and the same attention steps;
+  * the keep variant (ptdit_window_sa_keep): the same output, and the Q/K/V
+    it copies out equal, bit for bit, to the unfused path's.
 Cases span padded grids, shifts that differ from the pad, 3D 128-token
 windows, 32-token windows, row tiles that straddle a batch boundary, a head
 count other than 16, the full 2048^2 grid, and the shapes the fused kernel
@@ -80,6 +82,7 @@ def _fused_launches(P, fn):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_fused_window_calls(P, name):
+    from diffusion_transformer_attention_pt_amd import _lib
     wl = CASES[name]
     g = (wl.B, wl.F, wl.H, wl.W, wl.D, wl.heads)
     announce(f"fused window {name} grid={(wl.B,) + wl.grid} D={wl.D} heads={wl.heads} win={wl.win} "
@@ -110,6 +113,21 @@ def test_fused_window_calls(P, name):
         assert n1 == 1
         assert_close(host(res), O.shift_window_sa(x, wl.grid, wl.win, sh, w, wl.heads, True),
                      f"{'swsa' if shifted else 'wsa'} + residual")
+        # keep mode (ptdit_window_sa_keep): the same output, and the head-major
+        # Q/K/V and attention output it leaves in the workspace equal, bit for
+        # bit, what the unfused path leaves there (its projection GEMM's Q/K/V)
+        need = _lib.workspace_bytes(_lib.OP_WINDOW_SA, g, 0, wl.win, BF16)
+        ws_f = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+        ws_u = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        kept, nk = _fused_launches(P, lambda: _lib.window_sa_keep(xb, g, wl.win, sh, aw, ws_f, residual=False,
+                                                                  out_dtype=F32))
+        assert nk == 1
+        assert torch.equal(kept, got), "keep changed the output"
+        _lib.window_sa_keep(x32, g, wl.win, sh, aw, ws_u, residual=False, out_dtype=F32)
+        torch.cuda.synchronize()
+        (qf, of), (qu, ou) = _lib.window_ws_views(ws_f, g, BF16), _lib.window_ws_views(ws_u, g, BF16)
+        assert torch.equal(qf.view(torch.int16), qu.view(torch.int16)), "kept Q/K/V differ from the unfused path's"
+        assert torch.equal(of.view(torch.int16), ou.view(torch.int16)), "kept outputs differ"
 
 
 def test_fused_not_taken_where_unsupported(P):
