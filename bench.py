@@ -107,7 +107,7 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     return out
 
 
-def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
+def backward_timings(wl, blk, prec, reps: int = 10, per_call: bool = True) -> dict:
     """Attention-core backward at the workload's shapes, on synthetic resident
     inputs: the shifted-window core, the cross-attention core (tokens x
     proxies), the proxy self-attention core and the window-average backward.
@@ -205,7 +205,7 @@ def backward_timings(wl, blk, prec, reps: int = 10) -> dict:
         res["train_step"] = {"forward_keep_ms": round(ms_f, 4), "step_ms": round(ms_t, 4),
                              "tokens_per_s": round(B * N / (ms_t * 1e-3), 1),
                              "tflops": round((fl["total"] + bflop) / (ms_t * 1e-3) / 1e12, 2)}
-    for name, (cls, fn, flop, nbytes) in cases.items():
+    for name, (cls, fn, flop, nbytes) in (cases.items() if per_call else ()):
         fn()
         torch.cuda.synchronize()
         _lib.trace_enable(cls, 4 * reps)
@@ -242,6 +242,8 @@ def main() -> int:
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--backward", action="store_true",
                     help="also time the attention-core backward kernels at the workload's shapes")
+    ap.add_argument("--backward-block", action="store_true",
+                    help="also time the whole block's backward and training step only (no per-call cases)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the run, copy a 256 MiB buffer once with the library's plain copy "
                          "kernel (copy_kernel: known size, used to scale rocprofv3 FETCH_SIZE / "
@@ -455,8 +457,8 @@ def main() -> int:
                            "peak_frac": round(roll_rate / PEAK_HBM_GBS, 4), "copies": ncopy}
         del xs, ys
         out["breakdown"] = br
-    if args.backward:
-        out["backward"] = backward_timings(wl, blk, prec)
+    if args.backward or args.backward_block:
+        out["backward"] = backward_timings(wl, blk, prec, per_call=not args.backward_block)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
         out["cpu_baseline"]["gpu_speedup"] = round(tokens_per_s / out["cpu_baseline"]["value"], 1)

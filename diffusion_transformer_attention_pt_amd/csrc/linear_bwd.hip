@@ -9,7 +9,9 @@
 //                     contraction over the token axis on the DMA GEMM kernels
 //                     (those of the token-row projections), the token axis
 //                     split over blockIdx.y into partials
-//   colsum_kernel     partial column sums of dY over 128-row blocks
+//   colsum_kernel     partial column sums of dY over 64-row blocks (only
+//                     when dW is not wanted: otherwise the transpose pass,
+//                     which reads every element of dY anyway, writes them)
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
 #include <hip/hip_runtime.h>
 
@@ -43,7 +45,10 @@ __global__ void __launch_bounds__(LB_NT) transpose_kernel(const uint16_t* __rest
 // ld-1 zero; ld % 64 == 0), and optionally a row-major bf16 copy [rows][cols]:
 // the token-contiguous operands of dW = dY^T X (and the bf16 A operand of
 // dX = dY W). 64 x 64 tiles: 16 lanes read one row's 64 columns (4 each), the
-// transposed writes are 8 consecutive tokens (16 bytes) of one column.
+// transposed writes are 8 consecutive tokens (16 bytes) of one column. With
+// colp, the tile's column sums of src (fp32 values as read, the 16 row groups
+// added in order) go to colp[tile row][column]: the partials of db = sum_t dY
+// over 64-token blocks.
 constexpr int TPD = 64, TPP = TPD + 2;  // tile, LDS pitch (elements)
 __device__ __forceinline__ void ld4f(const float* p, float (&v)[4]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -56,24 +61,35 @@ __device__ __forceinline__ void ld4f(const uint16_t* p, float (&v)[4]) {
 }
 template <typename T>
 __global__ void __launch_bounds__(LB_NT) transpose_pad_kernel(const T* __restrict__ src, uint16_t* __restrict__ dst,
-                                                              uint16_t* __restrict__ copy, int64_t rows, int cols,
-                                                              int64_t ld) {
+                                                              uint16_t* __restrict__ copy, float* __restrict__ colp,
+                                                              int64_t rows, int cols, int64_t ld) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TPD * TPP];
+  __shared__ __attribute__((aligned(16))) float csum[16][TPD];
   const int64_t r0 = (int64_t)blockIdx.x * TPD;
   const int c0 = blockIdx.y * TPD;
   const int tid = threadIdx.x, lc = (tid & 15) * 4, lr = tid >> 4;  // 16 lanes a row
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < TPD / 16; ++i) {
     const int r = lr + 16 * i;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     const bool ok = r0 + r < rows && c0 + lc < cols;  // cols % 4 == 0: a group is in or out
     if (ok) ld4f(src + (r0 + r) * cols + c0 + lc, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs[j] += v[j];
     const uint32_t p0 = pack_bf2(v[0], v[1]), p1 = pack_bf2(v[2], v[3]);
     *reinterpret_cast<uint32_t*>(&tile[r * TPP + lc]) = p0;
     *reinterpret_cast<uint32_t*>(&tile[r * TPP + lc + 2]) = p1;
     if (copy && ok) *reinterpret_cast<uint2*>(copy + (r0 + r) * cols + c0 + lc) = uint2{p0, p1};
   }
+  if (colp) *reinterpret_cast<float4*>(&csum[lr][lc]) = float4{cs[0], cs[1], cs[2], cs[3]};
   __syncthreads();
+  if (colp && tid < TPD && r0 < rows && c0 + tid < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += csum[g][tid];
+    colp[blockIdx.x * (int64_t)cols + c0 + tid] = t;
+  }
   // 64 columns x 8 token groups = 512 writes of 16 bytes, two a thread
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -87,10 +103,11 @@ __global__ void __launch_bounds__(LB_NT) transpose_pad_kernel(const T* __restric
   }
 }
 
-// partial column sums of dY over token block blockIdx.y (CS_ROWS rows): four
+// partial column sums of dY over token block blockIdx.y (CS_ROWS rows, the
+// transpose tile's height, so both give the same partial layout): four
 // columns per lane (d_out % 8 == 0, 16-byte aligned rows), eight rows of
 // loads in flight, four chains (row t % 4) combined in a fixed order
-constexpr int CS_ROWS = 128;
+constexpr int CS_ROWS = TPD;
 template <typename TA> struct Col4;
 template <> struct Col4<float> {
   __device__ static float4 ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -190,18 +207,20 @@ hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s) {
   const int64_t ld = splits * tch;
   const dim3 gy((unsigned)(ld / TPD), (unsigned)((d.d_out + TPD - 1) / TPD)),
       gx((unsigned)(ld / TPD), (unsigned)((d.d_in + TPD - 1) / TPD));
+  // the dY pass also writes db's partials (colsum_kernel then is not run)
+  float* colp = d.db ? d.dbp : nullptr;
   if (d.dy_f32)
     hipLaunchKernelGGL((transpose_pad_kernel<float>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
-                       d.dyt, d.dyb, d.rows, d.d_out, ld);
+                       d.dyt, d.dyb, colp, d.rows, d.d_out, ld);
   else
     hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gy, dim3(LB_NT), 0, s, reinterpret_cast<const uint16_t*>(d.dy),
-                       d.dyt, d.dyb, d.rows, d.d_out, ld);
+                       d.dyt, d.dyb, colp, d.rows, d.d_out, ld);
   if (d.x_f32)
     hipLaunchKernelGGL((transpose_pad_kernel<float>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.x),
-                       d.xt, nullptr, d.rows, d.d_in, ld);
+                       d.xt, nullptr, nullptr, d.rows, d.d_in, ld);
   else
     hipLaunchKernelGGL((transpose_pad_kernel<uint16_t>), gx, dim3(LB_NT), 0, s, reinterpret_cast<const uint16_t*>(d.x),
-                       d.xt, nullptr, d.rows, d.d_in, ld);
+                       d.xt, nullptr, nullptr, d.rows, d.d_in, ld);
   return hipGetLastError();
 }
 
@@ -229,7 +248,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int csplits = colsum_splits(d.rows);
-  if (d.db) {
+  if (d.db && !d.dw) {  // with dW the transpose pass wrote the partials
     const dim3 grid((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits);
     if (d.dy_f32)
       hipLaunchKernelGGL((colsum_kernel<float>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
