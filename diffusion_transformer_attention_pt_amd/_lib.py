@@ -94,7 +94,7 @@ def load() -> ctypes.CDLL:
         "ptdit_trace_read": [ctypes.POINTER(ctypes.c_float), i32],
         "ptdit_trace_disable": [],
         "ptdit_window_attn_bwd": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
-        "ptdit_window_attn_bwd_tokens": [vp, vp, vp, i32, G, W3, W3, vp, vp, vp],
+        "ptdit_window_attn_bwd_tokens": [vp, vp, vp, i32, G, W3, W3, vp, i32, vp, vp],
         "ptdit_window_sa_keep": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
         "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
@@ -496,8 +496,9 @@ def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], w
                     tokens: bool = False):
     """Backward of the window / shifted-window attention core. qkv [B, 3, heads,
     N, dh] (the forward's Q/K/V), d_o [B, N, D]. Returns (d_qkv fp32 [B, 3, heads,
-    N, dh], or [B, N, 3D] with tokens=True (ptdit_window_attn_bwd_tokens), d_b_kv
-    fp32 [2, D]: pad-slot gradients, added to d_b_kv when given)."""
+    N, dh], or [B, N, 3D] with tokens=True (ptdit_window_attn_bwd_tokens; then a
+    given d_qkv may also be bf16, for bf16 inputs), d_b_kv fp32 [2, D]: pad-slot
+    gradients, added to d_b_kv when given)."""
     lib = load()
     B, F, H, W, D, heads = grid
     if d_o.dtype != qkv.dtype or (b_qkv is not None and b_qkv.dtype != qkv.dtype):
@@ -511,11 +512,17 @@ def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], w
     if d_qkv is None:
         shape = (B, N, 3 * D) if tokens else tuple(qkv.shape)
         d_qkv = torch.empty(shape, dtype=torch.float32, device=qkv.device)
+    if d_qkv.dtype != torch.float32 and not (tokens and d_qkv.dtype == torch.bfloat16):
+        raise ValueError("d_qkv must be float32 (or bfloat16 with tokens=True)")
     if d_b_kv is None:
         d_b_kv = torch.zeros(2, D, dtype=torch.float32, device=qkv.device)
-    fn = lib.ptdit_window_attn_bwd_tokens if tokens else lib.ptdit_window_attn_bwd
-    st = fn(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid), Win3(*win), Win3(*shift), _ptr(d_qkv),
-            _ptr(d_b_kv), _stream())
+    if tokens:
+        st = lib.ptdit_window_attn_bwd_tokens(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid),
+                                              Win3(*win), Win3(*shift), _ptr(d_qkv), _dt(d_qkv.dtype),
+                                              _ptr(d_b_kv), _stream())
+    else:
+        st = lib.ptdit_window_attn_bwd(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid), Win3(*win),
+                                       Win3(*shift), _ptr(d_qkv), _ptr(d_b_kv), _stream())
     _check("ptdit_window_attn_bwd_tokens" if tokens else "ptdit_window_attn_bwd", st)
     return d_qkv, d_b_kv
 

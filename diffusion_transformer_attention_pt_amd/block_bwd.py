@@ -15,13 +15,14 @@ calls run in reverse order of the forward:
 Each attention's backward takes its head-major Q/K/V and attention output
 from the forward when it ran with keep=True (the calls' workspaces, kept
 apart), else recomputes them (ptdit_linear_heads, ptdit_window_attn /
-ptdit_attn) from the block's stored inputs; then it takes takes the output projection's gradient
-(ptdit_linear_bwd_ex, whose d_x product writes the core's bf16 dO directly),
-the core's (ptdit_window_attn_bwd / ptdit_attn_bwd), and the input
-projections' (ptdit_linear_bwd_ex on the token-major dQ/dK/dV, which the
-window core's backward writes directly, ptdit_window_attn_bwd_tokens, and the
-dense cores' pass through ptdit_heads_to_tokens; the residual branch's
-gradient added in the d_x product's epilogue); the window average's gradient accumulates into dx
+ptdit_attn) from the block's stored inputs. Then come the output
+projection's gradient (ptdit_linear_bwd_ex, whose d_x product writes the
+core's bf16 dO directly), the core's (ptdit_window_attn_bwd_tokens /
+ptdit_attn_bwd) and the input projections' (ptdit_linear_bwd_ex on the
+token-major dQ/dK/dV: the window cores write them so, in bf16, the precision
+the projection's gradient products read them in; the dense cores' pass
+through ptdit_heads_to_tokens), the residual branch's gradient added in the
+d_x product's epilogue. The window average's gradient accumulates into dx
 (ptdit_proxy_pool_bwd). Every step runs in the library's kernels; torch only
 holds the buffers. bf16 precision blocks with window-average proxies.
 """
@@ -52,8 +53,8 @@ class PTBlockBackward:
         self.qkv = e(B, 3, heads, N, dh, dt=bf)
         self.o = e(B, N, D, dt=bf)
         self.do16 = e(B, N, D, dt=bf)
-        self.dqkv_h = e(B, 3, heads, N, dh)
-        self.dqkv_t = e(B, N, 3 * D)
+        self.dqkv_t16 = e(B, N, 3 * D, dt=bf)   # the window cores' gradient, token-major bf16
+        self.dq_h, self.dq_t = e(B, 1, heads, N, dh), e(B, N, D)   # the cross-attention's dQ
         self.dbkv = e(2, D)
         self.dx2, self.dx1, self.dx = e(B, N, D), e(B, N, D), e(B, N, D)
         # cross-attention and proxy buffers
@@ -90,10 +91,10 @@ class PTBlockBackward:
         if self.pads:
             self.dbkv.zero_()
         # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
-        _lib.window_attn_bwd(qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t,
+        _lib.window_attn_bwd(qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t16,
                              d_b_kv=self.dbkv if self.pads else None, tokens=True)
         # dx_out = dy (the residual) + d(branch)/dx^T dy, joined in the product
-        _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t, ws=self.ws, dx=dx_out, dx_add=dy)
+        _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t16, ws=self.ws, dx=dx_out, dx_add=dy)
         if self.pads:   # pad slots' key/value gradients reach b_k, b_v
             _lib.add_f32(dbqkv[D:], self.dbkv.view(-1), out=dbqkv[D:])
         return {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
@@ -127,10 +128,8 @@ class PTBlockBackward:
                               B, M, heads, out=kv)
             _lib.attn(q[:, 0], kv[:, 0], kv[:, 1], out=o)
         _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
-        # dQ into the (now free) window buffers: [B, 1, heads, N, dh] and its
-        # token-major [B, N, D]
-        dq_h = self.dqkv_h.view(-1)[:B * N * D].view(B, 1, heads, N, D // heads)
-        dq_t = self.dqkv_t.view(-1)[:B * N * D].view(B, N, D)
+        # dQ head-major [B, 1, heads, N, dh], then token-major [B, N, D]
+        dq_h, dq_t = self.dq_h, self.dq_t
         _lib.attn_bwd(q[:, 0], kv[:, 0], kv[:, 1], self.do16, ws=self.ws,
                       dq=dq_h[:, 0], dk=self.dkv_h[:, 0], dv=self.dkv_h[:, 1])
         _lib.heads_to_tokens(dq_h, out=dq_t)

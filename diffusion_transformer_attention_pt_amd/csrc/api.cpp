@@ -582,9 +582,10 @@ ptdit_status ptdit_roll3d(const void* x, ptdit_grid g, ptdit_win3 shift, int32_t
 }
 
 static ptdit_status window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
-                                    ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv, float* d_b_kv,
-                                    int tokens_out, hipStream_t stream) {
-  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+                                    ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, void* d_qkv,
+                                    ptdit_dtype out_dt, float* d_b_kv, int tokens_out, hipStream_t stream) {
+  if (!valid_dtype(dt) || !valid_dtype(out_dt)) return PTDIT_ERR_DTYPE;
+  if (out_dt == PTDIT_BF16 && dt != PTDIT_BF16) return PTDIT_ERR_DTYPE;  // bf16 gradients from bf16 inputs
   ptdit_status st = check_grid(g);
   if (st) return st;
   if (win.t <= 0 || win.h <= 0 || win.w <= 0) return PTDIT_ERR_SHAPE;
@@ -598,7 +599,7 @@ static ptdit_status window_attn_bwd(const void* qkv, const void* b_qkv, const vo
   if (!qkv || !d_o || !d_qkv || (pads && !d_b_kv)) return PTDIT_ERR_NULL;
   if (!aligned16(qkv) || !aligned16(d_o) || !aligned16(d_qkv) || !aligned16(b_qkv) || !aligned16(d_b_kv))
     return PTDIT_ERR_ALIGN;
-  const size_t gb = (size_t)rows * 3 * g.D * 4, bb = (size_t)2 * g.D * 4;
+  const size_t gb = (size_t)rows * 3 * g.D * esize(out_dt), bb = (size_t)2 * g.D * 4;
   if (overlaps(d_qkv, gb, qkv, rows * 3 * g.D * esize(dt)) || overlaps(d_qkv, gb, d_o, rows * g.D * esize(dt)) ||
       overlaps(d_qkv, gb, b_qkv, 3 * g.D * esize(dt)) || overlaps(d_b_kv, bb, d_qkv, gb) ||
       overlaps(d_b_kv, bb, qkv, rows * 3 * g.D * esize(dt)) || overlaps(d_b_kv, bb, d_o, rows * g.D * esize(dt)))
@@ -606,6 +607,7 @@ static ptdit_status window_attn_bwd(const void* qkv, const void* b_qkv, const vo
   WindowBwdDesc d;
   d.QKV = qkv; d.bias_qkv = b_qkv; d.dO = d_o; d.dQKV = d_qkv; d.dbias_kv = d_b_kv;
   d.tokens_out = tokens_out;
+  d.out_bf16 = out_dt == PTDIT_BF16;
   d.B = g.B; d.F = g.F; d.H = g.H; d.W = g.W; d.D = g.D; d.heads = g.heads; d.dh = g.D / g.heads;
   d.wt = win.t; d.wh = win.h; d.ww = win.w;
   d.st = shift.t; d.sh = shift.h; d.sw = shift.w;
@@ -620,13 +622,13 @@ static ptdit_status window_attn_bwd(const void* qkv, const void* b_qkv, const vo
 ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
                                    ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv,
                                    float* d_b_kv, hipStream_t stream) {
-  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv, d_b_kv, 0, stream);
+  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv, PTDIT_F32, d_b_kv, 0, stream);
 }
 
 ptdit_status ptdit_window_attn_bwd_tokens(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
-                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv_t,
-                                          float* d_b_kv, hipStream_t stream) {
-  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv_t, d_b_kv, 1, stream);
+                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, void* d_qkv_t,
+                                          ptdit_dtype d_qkv_dt, float* d_b_kv, hipStream_t stream) {
+  return window_attn_bwd(qkv, b_qkv, d_o, dt, g, win, shift, d_qkv_t, d_qkv_dt, d_b_kv, 1, stream);
 }
 
 namespace {

@@ -75,9 +75,10 @@ struct WindowBwdParams {
   const void* QKV;       // [B][3][heads][N][dh]
   const void* bias_qkv;  // [3D] or null (pad keys/values are b_k/b_v, else 0)
   const void* dO;        // [B][N][D]
-  float* dQKV;           // dQ, dK, dV: element (b, g, h, token, d) at
+  void* dQKV;            // dQ, dK, dV: element (b, g, h, token, d) at
                          // b*o_bs + g*o_gs + h*o_hs + token*o_ts + d
   int64_t o_bs, o_gs, o_hs, o_ts;  // head-major [B][3][heads][N][dh] or token-major [B][N][3D]
+  int out_bf16;          // dQKV elements bf16 (matrix-core kernels only), else fp32
   float* dbias_kv;       // [2][D], accumulated into; null when nothing pads
   int F, H, W, D, heads;
   int wt, wh, ww;
@@ -85,6 +86,15 @@ struct WindowBwdParams {
   int Fp, Hp, Wp;
   float scale;
 };
+
+// four consecutive gradient elements (e % 4 == 0) as fp32, or rounded to bf16
+// (round to nearest even) when the caller asked for bf16
+__device__ __forceinline__ void bwd_store4(const WindowBwdParams& p, int64_t e, float4 v) {
+  if (p.out_bf16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.dQKV) + e) = uint2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.dQKV) + e) = v;
+}
 
 template <typename T, int DH, int KEYS>
 __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
@@ -151,7 +161,7 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_kernel(WindowBwdParams p) {
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
+  float* dQb = reinterpret_cast<float*>(p.dQKV) + (int64_t)b * p.o_bs + h * p.o_hs;
   float* dKb = dQb + p.o_gs;
   float* dVb = dQb + 2 * p.o_gs;
 
@@ -384,9 +394,9 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
-  float* dKb = dQb + p.o_gs;
-  float* dVb = dQb + 2 * p.o_gs;
+  const int64_t dQb = (int64_t)b * p.o_bs + h * p.o_hs;  // element offsets in dQKV
+  const int64_t dKb = dQb + p.o_gs;
+  const int64_t dVb = dQb + 2 * p.o_gs;
 
   // ---- phase 1: queries of wave w
   {
@@ -478,8 +488,8 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       }
       const int d = dt * 16 + 4 * g;
       if (qtok >= 0 && d < DH)
-        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * p.o_ts + d) =
-            float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
+        bwd_store4(p, dQb + (int64_t)qtok * p.o_ts + d,
+                   float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale});
     }
   }
   __syncthreads();
@@ -513,8 +523,8 @@ __global__ void __launch_bounds__(BW_NT) window_bwd_mfma_kernel(WindowBwdParams 
       const float4 kv = float4{ak[0] * p.scale, ak[1] * p.scale, ak[2] * p.scale, ak[3] * p.scale};
       const float4 vv = float4{av[0], av[1], av[2], av[3]};
       if (ktok >= 0) {
-        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * p.o_ts + d) = kv;
-        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * p.o_ts + d) = vv;
+        bwd_store4(p, dKb + (int64_t)ktok * p.o_ts + d, kv);
+        bwd_store4(p, dVb + (int64_t)ktok * p.o_ts + d, vv);
       } else if (ktok == -1 && p.dbias_kv) {
         float* bk = &padg[d];
         float* bv = &padg[DH + d];
@@ -641,9 +651,9 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
   }
   __syncthreads();
 
-  float* dQb = p.dQKV + (int64_t)b * p.o_bs + h * p.o_hs;
-  float* dKb = dQb + p.o_gs;
-  float* dVb = dQb + 2 * p.o_gs;
+  const int64_t dQb = (int64_t)b * p.o_bs + h * p.o_hs;  // element offsets in dQKV
+  const int64_t dKb = dQb + p.o_gs;
+  const int64_t dVb = dQb + 2 * p.o_gs;
 
   // ---- phase 1: queries of wave w
   {
@@ -729,8 +739,8 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
       }
       const int d = dt * 16 + 4 * g;
       if (qtok >= 0 && d < DH)
-        *reinterpret_cast<float4*>(dQb + (int64_t)qtok * p.o_ts + d) =
-            float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale};
+        bwd_store4(p, dQb + (int64_t)qtok * p.o_ts + d,
+                   float4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale});
     }
   }
   __syncthreads();  // statistics of every query in LDS
@@ -800,8 +810,8 @@ __global__ void __launch_bounds__(512) window_bwd_mfma128_kernel(WindowBwdParams
       const float4 kv = float4{dk[dt][0] * p.scale, dk[dt][1] * p.scale, dk[dt][2] * p.scale, dk[dt][3] * p.scale};
       const float4 vv = float4{dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
       if (ktok >= 0) {
-        *reinterpret_cast<float4*>(dKb + (int64_t)ktok * p.o_ts + d) = kv;
-        *reinterpret_cast<float4*>(dVb + (int64_t)ktok * p.o_ts + d) = vv;
+        bwd_store4(p, dKb + (int64_t)ktok * p.o_ts + d, kv);
+        bwd_store4(p, dVb + (int64_t)ktok * p.o_ts + d, vv);
       } else if (ktok == -1 && p.dbias_kv) {
         float* bk = &padg[d];
         float* bv = &padg[DH + d];
@@ -821,6 +831,7 @@ template <typename T, int DH>
 static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   WindowBwdParams p;
   p.QKV = d.QKV; p.bias_qkv = d.bias_qkv; p.dO = d.dO; p.dQKV = d.dQKV; p.dbias_kv = d.dbias_kv;
+  p.out_bf16 = d.out_bf16;
   p.F = d.F; p.H = d.H; p.W = d.W; p.D = d.D; p.heads = d.heads;
   const int64_t N = (int64_t)d.F * d.H * d.W;
   if (d.tokens_out) {  // [B][N][3D]: the Q/K/V projection's output gradient
@@ -835,6 +846,7 @@ static hipError_t pick_window_bwd(const WindowBwdDesc& d, hipStream_t s) {
   const int nwin = (d.Fp / d.wt) * (d.Hp / d.wh) * (d.Wp / d.ww);
   const dim3 grid(nwin, d.heads, d.B);
   const int wsz = d.wt * d.wh * d.ww;
+  if (d.out_bf16 && (sizeof(T) != 2 || wsz > 128)) return hipErrorInvalidValue;  // fp32 out only there
   if (sizeof(T) == 2 && wsz <= 64) hipLaunchKernelGGL((window_bwd_mfma_kernel<DH>), grid, dim3(BW_NT), 0, s, p);
   else if (sizeof(T) == 2 && wsz <= 128)
     hipLaunchKernelGGL((window_bwd_mfma128_kernel<DH>), grid, dim3(512), 0, s, p);

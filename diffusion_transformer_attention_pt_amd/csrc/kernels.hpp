@@ -107,8 +107,9 @@ hipError_t launch_calib_copy(const void* src, void* dst, int64_t bytes, hipStrea
 // Backward pass of the attention core (fp32 gradients).
 struct WindowBwdDesc {
   const void* QKV; const void* bias_qkv; const void* dO;
-  float* dQKV; float* dbias_kv;
+  void* dQKV; float* dbias_kv;
   int tokens_out = 0;  // 0: dQKV head-major [B][3][heads][N][dh]; 1: token-major [B][N][3D]
+  int out_bf16 = 0;    // dQKV in bf16 (bf16 inputs only), else fp32
   int B, F, H, W, D, heads, dh;
   int wt, wh, ww;
   int st, sh, sw;

@@ -332,15 +332,18 @@ ptdit_status ptdit_window_attn_bwd(const void* qkv, const void* b_qkv, const voi
 
 /*
  * ptdit_window_attn_bwd_tokens -- ptdit_window_attn_bwd with dQ, dK, dV
- * written token-major: d_qkv_t [B][N][3D] fp32, element [b][t][g*D + h*dh + d]
+ * written token-major: d_qkv_t [B][N][3D], element [b][t][g*D + h*dh + d]
  * for g = Q, K, V, the output gradient of the Q/K/V projection as
- * ptdit_linear_bwd reads it (so no layout pass sits between the two).
- * Everything else, the padding / bias gradients and the errors as
- * ptdit_window_attn_bwd.
+ * ptdit_linear_bwd reads it (so no layout pass sits between the two), in
+ * d_qkv_dt: PTDIT_F32, or PTDIT_BF16 (round to nearest even; only with
+ * dt == PTDIT_BF16, else PTDIT_ERR_DTYPE), half the bytes to write and to
+ * read back, and the precision the projection's gradient products take their
+ * operands in anyway. Everything else, the padding / bias gradients (fp32)
+ * and the errors as ptdit_window_attn_bwd.
  */
 ptdit_status ptdit_window_attn_bwd_tokens(const void* qkv, const void* b_qkv, const void* d_o, ptdit_dtype dt,
-                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, float* d_qkv_t,
-                                          float* d_b_kv, hipStream_t stream);
+                                          ptdit_grid g, ptdit_win3 win, ptdit_win3 shift, void* d_qkv_t,
+                                          ptdit_dtype d_qkv_dt, float* d_b_kv, hipStream_t stream);
 
 /*
  * ptdit_attn_bwd -- the core of ptdit_proxy_sa (queries = keys = proxies) or

@@ -105,8 +105,9 @@ def test_window_attn_bwd_vs_oracle(P, name):
 def test_window_attn_bwd_tokens_layout(P, name):
     """ptdit_window_attn_bwd_tokens writes the same values as
     ptdit_window_attn_bwd, token-major: bit for bit equal to the head-major
-    result after the layout change; the pad-slot bias gradients agree to the
-    order of their atomic additions."""
+    result after the layout change, and with bf16 gradients, to that result
+    rounded to bf16; the pad-slot bias gradients agree to the order of their
+    atomic additions."""
     from diffusion_transformer_attention_pt_amd import _lib
     (B, F, H, W), D, heads, win, shift, dt, scale = WIN_CASES[name]
     dh, N = D // heads, F * H * W
@@ -125,6 +126,18 @@ def test_window_attn_bwd_tokens_layout(P, name):
     assert tuple(dqkv_t.shape) == (B, N, 3 * D)
     assert torch.equal(dqkv_t, _lib.heads_to_tokens(dqkv_h))
     np.testing.assert_allclose(host(db_t), host(db_h), rtol=1e-5, atol=1e-5)
+    if dt == "bf16":
+        # bf16 gradients: the fp32 values rounded to nearest even, bit for bit
+        d16 = torch.empty(B, N, 3 * D, dtype=BF16, device="cuda")
+        _, db16 = _lib.window_attn_bwd(qkv, dev(do, prec), (B, F, H, W, D, heads), win, shift,
+                                       b_qkv=dev(bias, prec), tokens=True, d_qkv=d16)
+        torch.cuda.synchronize()
+        assert torch.equal(d16.view(torch.int16), dqkv_t.to(BF16).view(torch.int16))
+        np.testing.assert_allclose(host(db16), host(db_h), rtol=1e-5, atol=1e-5)
+    else:
+        with pytest.raises(_lib.PtditError):   # bf16 gradients only from bf16 inputs
+            _lib.window_attn_bwd(qkv, dev(do, prec), (B, F, H, W, D, heads), win, shift, b_qkv=dev(bias, prec),
+                                 tokens=True, d_qkv=torch.empty(B, N, 3 * D, dtype=BF16, device="cuda"))
 
 
 def test_window_attn_bwd_full_size_sampled_windows(P):
