@@ -35,7 +35,7 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
             "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
             "ptdit_calibrate_read", "ptdit_calibrate_copy", "ptdit_linear_bwd_ex",
-            "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep"]
+            "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep", "ptdit_attn_bwd_tokens"]
 
 
 class Grid(ctypes.Structure):
@@ -97,6 +97,8 @@ def load() -> ctypes.CDLL:
         "ptdit_window_attn_bwd_tokens": [vp, vp, vp, i32, G, W3, W3, vp, i32, vp, vp],
         "ptdit_window_sa_keep": [vp, vp, i32, G, W3, W3, AW, i32, vp, vp, i32, vp, sz, i32, vp],
         "ptdit_attn_bwd": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, sz, vp],
+        "ptdit_attn_bwd_tokens": [vp, i64, vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, i64, vp,
+                                  sz, vp],
         "ptdit_attn_bwd_workspace_bytes": [i32, i32, i32, i32, i32],
         "ptdit_proxy_pool_bwd": [vp, G, W3, vp, i32, vp],
         "ptdit_linear_bwd": [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp],
@@ -539,12 +541,14 @@ def _bhld(t: torch.Tensor, name: str) -> int:
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
              ws: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
-             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, dq_tokens: bool = False):
     """Backward of the unmasked attention core (proxy SA, cross-attention).
     q [B, heads, Nq, dh], k / v [B, heads, Nk, dh] (views into fused buffers
     allowed), d_o [B, Nq, heads*dh]. Returns fp32 (dq, dk, dv): new contiguous
     tensors, or the given fp32 views (each batch item a contiguous [heads, L,
-    dh] block; dk and dv with one batch stride)."""
+    dh] block; dk and dv with one batch stride). dq_tokens: dq token-major
+    [B, Nq, heads*dh] (ptdit_attn_bwd_tokens), fp32 or, for bf16 inputs, a
+    given bf16 tensor."""
     lib = load()
     B, heads, Nq, dh = q.shape
     Nk = k.shape[2]
@@ -553,16 +557,22 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
     _numel(d_o, B * Nq * heads * dh, "d_o")
     if k.stride(0) != v.stride(0):
         raise ValueError("k and v must share their batch stride")
-    for t, n, name in ((dq, Nq, "dq"), (dk, Nk, "dk"), (dv, Nk, "dv")):
+    for t, n, name in (((None if dq_tokens else dq), Nq, "dq"), (dk, Nk, "dk"), (dv, Nk, "dv")):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, heads, n, dh)):
             raise ValueError(f"{name} must be fp32 [{B}, {heads}, {n}, {dh}]")
+    if dq_tokens and dq is not None:
+        if dq.dtype not in (torch.float32, torch.bfloat16) or not dq.is_contiguous():
+            raise ValueError("dq (token-major) must be a contiguous fp32 or bf16 tensor")
+        _numel(dq, B * Nq * heads * dh, "dq")
     if dq is None:
-        dq = torch.empty(B, heads, Nq, dh, dtype=torch.float32, device=q.device)
+        dq = torch.empty(*((B, Nq, heads * dh) if dq_tokens else (B, heads, Nq, dh)), dtype=torch.float32,
+                         device=q.device)
     if dk is None:
         dk = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
     if dv is None:
         dv = torch.empty(B, heads, Nk, dh, dtype=torch.float32, device=q.device)
-    dq_bs, dk_bs, dv_bs = _bhld(dq, "dq"), _bhld(dk, "dk"), _bhld(dv, "dv")
+    dq_bs = None if dq_tokens else _bhld(dq, "dq")
+    dk_bs, dv_bs = _bhld(dk, "dk"), _bhld(dv, "dv")
     if dk_bs != dv_bs:
         raise ValueError("dk and dv must share their batch stride")
     need = int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh))
@@ -571,6 +581,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
         raise ValueError("q, k, v and d_o must share one dtype")
     q_bs, kv_bs = _bhld(q, "q"), _bhld(k, "k")
     _bhld(v, "v")
+    if dq_tokens:
+        st = lib.ptdit_attn_bwd_tokens(q.data_ptr(), q_bs, k.data_ptr(), v.data_ptr(), kv_bs, _ptr(d_o),
+                                       _dt(q.dtype), B, heads, Nq, Nk, dh, dq.data_ptr(), _dt(dq.dtype),
+                                       dk.data_ptr(), dv.data_ptr(), dk_bs, _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream())
+        _check("ptdit_attn_bwd_tokens", st)
+        return dq, dk, dv
     st = lib.ptdit_attn_bwd(q.data_ptr(), q_bs, k.data_ptr(), v.data_ptr(), kv_bs, _ptr(d_o), _dt(q.dtype),
                             B, heads, Nq, Nk, dh, dq.data_ptr(), dq_bs, dk.data_ptr(), dv.data_ptr(), dk_bs,
                             _ptr(ws), ws.numel() * ws.element_size(), _stream())

@@ -20,8 +20,9 @@ projection's gradient (ptdit_linear_bwd_ex, whose d_x product writes the
 core's bf16 dO directly), the core's (ptdit_window_attn_bwd_tokens /
 ptdit_attn_bwd) and the input projections' (ptdit_linear_bwd_ex on the
 token-major dQ/dK/dV: the window cores write them so, in bf16, the precision
-the projection's gradient products read them in; the dense cores' pass
-through ptdit_heads_to_tokens), the residual branch's gradient added in the
+the projection's gradient products read them in; the cross-attention core
+writes its dQ so too, ptdit_attn_bwd_tokens; the proxy keys' and values'
+gradients pass through ptdit_heads_to_tokens), the residual branch's gradient added in the
 d_x product's epilogue. The window average's gradient accumulates into dx
 (ptdit_proxy_pool_bwd). Every step runs in the library's kernels; torch only
 holds the buffers. bf16 precision blocks with window-average proxies.
@@ -54,7 +55,6 @@ class PTBlockBackward:
         self.o = e(B, N, D, dt=bf)
         self.do16 = e(B, N, D, dt=bf)
         self.dqkv_t16 = e(B, N, 3 * D, dt=bf)   # the window cores' gradient, token-major bf16
-        self.dq_h, self.dq_t = e(B, 1, heads, N, dh), e(B, N, D)   # the cross-attention's dQ
         self.dbkv = e(2, D)
         self.dx2, self.dx1, self.dx = e(B, N, D), e(B, N, D), e(B, N, D)
         # cross-attention and proxy buffers
@@ -128,11 +128,10 @@ class PTBlockBackward:
                               B, M, heads, out=kv)
             _lib.attn(q[:, 0], kv[:, 0], kv[:, 1], out=o)
         _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
-        # dQ head-major [B, 1, heads, N, dh], then token-major [B, N, D]
-        dq_h, dq_t = self.dq_h, self.dq_t
+        # dQ token-major bf16 [B, N, D] into the (now free) window gradient buffer
+        dq_t = self.dqkv_t16.view(-1)[:B * N * D].view(B, N, D)
         _lib.attn_bwd(q[:, 0], kv[:, 0], kv[:, 1], self.do16, ws=self.ws,
-                      dq=dq_h[:, 0], dk=self.dkv_h[:, 0], dv=self.dkv_h[:, 1])
-        _lib.heads_to_tokens(dq_h, out=dq_t)
+                      dq=dq_t, dk=self.dkv_h[:, 0], dv=self.dkv_h[:, 1], dq_tokens=True)
         dwqkv = torch.empty(3 * D, D, dtype=torch.float32, device=x.device)
         dbqkv = torch.empty(3 * D, dtype=torch.float32, device=x.device)
         # dx = dx1 (the residual) + the queries' gradient, joined in the product

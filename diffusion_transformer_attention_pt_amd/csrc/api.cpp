@@ -644,11 +644,13 @@ size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int3
   return bytes < kAlign ? kAlign : bytes;
 }
 
-ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
-                            int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
-                            int32_t Nq, int32_t Nk, int32_t dh, float* d_q, int64_t dq_bstride, float* d_k,
-                            float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(dt)) return PTDIT_ERR_DTYPE;
+static ptdit_status attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
+                             int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                             int32_t Nq, int32_t Nk, int32_t dh, void* d_q, int64_t dq_bstride, int dq_tok,
+                             ptdit_dtype dq_dt, float* d_k, float* d_v, int64_t dkv_bstride, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dt) || !valid_dtype(dq_dt)) return PTDIT_ERR_DTYPE;
+  if (dq_dt == PTDIT_BF16 && dt != PTDIT_BF16) return PTDIT_ERR_DTYPE;  // bf16 gradients from bf16 inputs
   if (B < 0 || heads <= 0 || Nq < 0 || Nk < 0 || (dh != 64 && dh != 72)) return PTDIT_ERR_SHAPE;
   if ((int64_t)B * heads > 65535 || Nq > (1 << 30) || (Nq > 0 && Nk == 0) || bwd_chunks(Nq) > 65535)
     return PTDIT_ERR_SHAPE;
@@ -666,7 +668,8 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
   struct Blk { const void* p; int64_t stride, len, n; };
   const Blk ins[4] = {{q, q_bstride * es, hq * es, B}, {k, kv_bstride * es, hk * es, B},
                       {v, kv_bstride * es, hk * es, B}, {d_o, 0, (int64_t)B * Nq * heads * dh * es, 1}};
-  const Blk outs[4] = {{d_q, dq_bstride * 4, hq * 4, B}, {d_k, dkv_bstride * 4, hk * 4, B},
+  const int64_t qes = (int64_t)esize(dq_dt);
+  const Blk outs[4] = {{d_q, dq_bstride * qes, hq * qes, B}, {d_k, dkv_bstride * 4, hk * 4, B},
                        {d_v, dkv_bstride * 4, hk * 4, B}, {ws, 0, (int64_t)need, 1}};
   auto meet = [](const Blk& x, const Blk& y) {
     if (x.n == y.n) return overlaps_strided(x.p, x.stride, x.len, y.p, y.stride, y.len, x.n);
@@ -682,6 +685,7 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
   d.q = q; d.k = k; d.v = v; d.dO = d_o;
   d.q_bs = q_bstride; d.kv_bs = kv_bstride;
   d.dq = d_q; d.dk = d_k; d.dv = d_v; d.dq_bs = dq_bstride; d.dkv_bs = dkv_bstride;
+  d.dq_tok = dq_tok; d.dq_bf16 = dq_dt == PTDIT_BF16;
   d.stats = (float*)ws;
   d.part = (float*)((char*)ws + align_up((size_t)B * heads * Nq * 3 * 4));
   d.B = B; d.heads = heads; d.Nq = Nq; d.Nk = Nk; d.D = heads * dh; d.dh = dh;
@@ -690,6 +694,22 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
   d.scale = 1.0f / std::sqrt((float)dh);
   TraceScope ts(PTDIT_K_BWD_DENSE, stream);
   return hip_status(launch_dense_bwd(d, dt == PTDIT_F32, stream));
+}
+
+ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, const void* v,
+                            int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                            int32_t Nq, int32_t Nk, int32_t dh, float* d_q, int64_t dq_bstride, float* d_k,
+                            float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return attn_bwd(q, q_bstride, k, v, kv_bstride, d_o, dt, B, heads, Nq, Nk, dh, d_q, dq_bstride, 0, PTDIT_F32,
+                  d_k, d_v, dkv_bstride, ws, ws_bytes, stream);
+}
+
+ptdit_status ptdit_attn_bwd_tokens(const void* q, int64_t q_bstride, const void* k, const void* v,
+                                   int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                                   int32_t Nq, int32_t Nk, int32_t dh, void* d_q_t, ptdit_dtype d_q_dt, float* d_k,
+                                   float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return attn_bwd(q, q_bstride, k, v, kv_bstride, d_o, dt, B, heads, Nq, Nk, dh, d_q_t,
+                  (int64_t)Nq * heads * dh, 1, d_q_dt, d_k, d_v, dkv_bstride, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ recompute and chaining calls

@@ -869,14 +869,28 @@ hipError_t launch_window_bwd(const WindowBwdDesc& d, int f32, hipStream_t s) {
 struct DenseBwdParams {
   const void *q, *k, *v, *dO;
   int64_t q_bs, kv_bs;   // batch strides (elements) of q and of k / v
-  float *dq, *dk, *dv;
+  void* dq;              // head-major [heads][Nq][dh] or token-major [Nq][D] a batch item
+  float *dk, *dv;
   int64_t dq_bs, dkv_bs;
+  int dq_tok, dq_bf16;   // dQ token-major; dQ in bf16 (matrix-core kernels only), else fp32
   float* stats;          // [B][heads][Nq][3]: row max, row sum, D = rowsum(A * dA)
   float* part;           // [chunks][B][heads][Nk][2][dh] when the queries are split
   int B, heads, Nq, Nk, D, qchunk, chunks;
   int qtiles;            // 64-query tiles per workgroup of the matrix-core query-major kernel
   float scale;
 };
+
+// element offset of dQ[b][h][query qi][0]
+__device__ __forceinline__ int64_t dq_offset(const DenseBwdParams& p, int b, int h, int64_t qi, int dh) {
+  return b * p.dq_bs + (p.dq_tok ? qi * p.D + (int64_t)h * dh : ((int64_t)h * p.Nq + qi) * dh);
+}
+// four consecutive dQ elements (e % 4 == 0), fp32 or rounded to bf16
+__device__ __forceinline__ void dq_store4(const DenseBwdParams& p, int64_t e, float4 v) {
+  if (p.dq_bf16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.dq) + e) = uint2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.dq) + e) = v;
+}
 
 constexpr int DB_Q = 64;   // queries per workgroup (query-major kernel)
 constexpr int DB_K = 64;   // keys per LDS chunk / per workgroup (key-major kernel)
@@ -958,7 +972,7 @@ __global__ void __launch_bounds__(BW_NT) dense_bwd_q_kernel(DenseBwdParams p) {
 #pragma unroll
   for (int d = 0; d < DH; ++d) { X[d] = group_sum<G>(X[d]); Y[d] = group_sum<G>(Y[d]); }
   if (!live) return;
-  float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + i) * DH;
+  float* dq = reinterpret_cast<float*>(p.dq) + dq_offset(p, b, h, i, DH);  // fp32 inputs: fp32 dQ
   for (int d = sub; d < DH; d += G) {
     float x = 0.f, y = 0.f;
 #pragma unroll
@@ -1213,13 +1227,13 @@ __global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_kernel(DenseBwdParams 
       }
     }
     if (live) {
-      float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
+      const int64_t dq = dq_offset(p, b, h, qi, DH);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int d = dt * 16 + 4 * g;
         if (d < DH)
-          *reinterpret_cast<float4*>(dq + d) =
-              float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+          dq_store4(p, dq + d,
+                    float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale});
       }
       if (g == 0) {
         float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
@@ -1370,13 +1384,13 @@ __global__ void __launch_bounds__(DQ_NT) dense_bwd_q_mfma_stream_kernel(DenseBwd
     }
   }
   if (live) {
-    float* dq = p.dq + b * p.dq_bs + ((int64_t)h * p.Nq + qi) * DH;
+    const int64_t dq = dq_offset(p, b, h, qi, DH);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int d = dt * 16 + 4 * g;
       if (d < DH)
-        *reinterpret_cast<float4*>(dq + d) =
-            float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale};
+        dq_store4(p, dq + d,
+                  float4{acc[dt][0] * p.scale, acc[dt][1] * p.scale, acc[dt][2] * p.scale, acc[dt][3] * p.scale});
     }
     if (g == 0) {
       float* st = p.stats + (((int64_t)b * p.heads + h) * p.Nq + qi) * 3;
@@ -1526,6 +1540,8 @@ static hipError_t run_dense_bwd(const DenseBwdDesc& d, hipStream_t s) {
   p.q = d.q; p.k = d.k; p.v = d.v; p.dO = d.dO;
   p.q_bs = d.q_bs; p.kv_bs = d.kv_bs;
   p.dq = d.dq; p.dk = d.dk; p.dv = d.dv; p.dq_bs = d.dq_bs; p.dkv_bs = d.dkv_bs;
+  p.dq_tok = d.dq_tok; p.dq_bf16 = d.dq_bf16;
+  if (d.dq_bf16 && sizeof(T) != 2) return hipErrorInvalidValue;  // the fp32 kernels write fp32
   p.stats = d.stats; p.part = d.part;
   p.B = d.B; p.heads = d.heads; p.Nq = d.Nq; p.Nk = d.Nk; p.D = d.D;
   p.qchunk = d.qchunk; p.chunks = d.chunks;

@@ -972,11 +972,14 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 != 0 || p.K < 256) return hipErrorInvalidValue;  // KT % 4 == 0, KT >= 8
   const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
   if (tiles <= 0) return hipSuccess;
-  if (tiles < 256) {
+  const int64_t t128 = ((p.M + 127) / 128) * (int64_t)((p.N + 287) / 288);
+  if (tiles * p.splits < 256 && t128 * p.splits <= 256) {
     // fewer 256-row tiles than CUs (the 1024^2 block's 8192-row projections
-    // onto D): 128-row tiles (waves of 32 x 144) keep every CU busy; the
+    // onto D): 128-row tiles (waves of 32 x 144) keep more CUs busy, in one
+    // round still (a second, partial round would cost more than the idle
+    // CUs: the 3456 x 1152 weight gradient split 4 ways over the tokens of a
+    // 2048^2 block runs 142 us on 224 workgroups, 193 us on 432); the
     // residual is added in the epilogue
-    const int64_t t128 = ((p.M + 127) / 128) * (int64_t)((p.N + 287) / 288);
     hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0, 128>), dim3((unsigned)t128, (unsigned)p.splits), dim3(512),
                        0, s, p);
     return hipGetLastError();

@@ -121,8 +121,10 @@ hipError_t launch_window_bwd(const WindowBwdDesc& d, int f32, hipStream_t s);
 struct DenseBwdDesc {
   const void *q, *k, *v, *dO;
   int64_t q_bs, kv_bs;
-  float *dq, *dk, *dv;
+  void* dq; float *dk, *dv;
   int64_t dq_bs, dkv_bs;
+  int dq_tok = 0;   // dQ token-major [B][Nq][D] (else head-major [B][heads][Nq][dh])
+  int dq_bf16 = 0;  // dQ in bf16 (bf16 inputs only), else fp32
   float* stats;  // [B][heads][Nq][3]
   float* part;   // [chunks][B][heads][Nk][2][dh] (chunks > 1)
   int B, heads, Nq, Nk, D, dh, qchunk, chunks;

@@ -368,6 +368,19 @@ ptdit_status ptdit_attn_bwd(const void* q, int64_t q_bstride, const void* k, con
 size_t ptdit_attn_bwd_workspace_bytes(int32_t B, int32_t heads, int32_t Nq, int32_t Nk, int32_t dh);
 
 /*
+ * ptdit_attn_bwd_tokens -- ptdit_attn_bwd with dQ written token-major:
+ * d_q_t [B][Nq][heads*dh], element [b][q][h*dh + d], the output gradient of
+ * the query projection as ptdit_linear_bwd reads it (so no layout pass sits
+ * between the two), in d_q_dt: PTDIT_F32, or PTDIT_BF16 (round to nearest
+ * even; only with dt == PTDIT_BF16, else PTDIT_ERR_DTYPE). d_k, d_v, the
+ * workspace and the errors as ptdit_attn_bwd.
+ */
+ptdit_status ptdit_attn_bwd_tokens(const void* q, int64_t q_bstride, const void* k, const void* v,
+                                   int64_t kv_bstride, const void* d_o, ptdit_dtype dt, int32_t B, int32_t heads,
+                                   int32_t Nq, int32_t Nk, int32_t dh, void* d_q_t, ptdit_dtype d_q_dt, float* d_k,
+                                   float* d_v, int64_t dkv_bstride, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ptdit_proxy_pool_bwd -- gradient of the window average (Eq. GIIM's
  * Averaging): every token of a proxy window receives d_proxies[proxy] / P,
  * P = p_t*p_h*p_w (IEEE fp32 division). d_proxies [B][M][D] fp32, d_x

@@ -270,6 +270,36 @@ def test_attn_bwd_vs_oracle(P, name):
     assert_grad_close(tok(host(dv)), rv, "dV")
 
 
+@pytest.mark.parametrize("name", ["xattn_chunks_ragged", "many_keys", "dh64", "f32"])
+def test_attn_bwd_tokens_layout(P, name):
+    """ptdit_attn_bwd_tokens: dQ token-major, bit for bit the head-major dQ
+    of ptdit_attn_bwd after the layout change, and with bf16 gradients that
+    result rounded to bf16; dK and dV unchanged (fp32 inputs: bf16 gradients
+    are refused)."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    B, heads, Nq, Nk, dh, layout, dt, scale = DENSE_CASES[name]
+    announce(f"dense bwd tokens layout {name}")
+    q, k, v, do = make_attn_grad_inputs(B, heads, Nq, Nk, dh, seed=560 + len(name), scale=scale, dtype=dt)
+    prec = BF16 if dt == "bf16" else F32
+    qd = dev(q, prec)
+    kv = dev(np.stack([k, v], axis=1), prec)
+    dd = dev(do, prec)
+    dq, dk, dv = P.attn_bwd(qd, kv[:, 0], kv[:, 1], dd)
+    dq_t, dk_t, dv_t = _lib.attn_bwd(qd, kv[:, 0], kv[:, 1], dd, dq_tokens=True)
+    torch.cuda.synchronize()
+    assert tuple(dq_t.shape) == (B, Nq, heads * dh)
+    assert torch.equal(dq_t, dq.transpose(1, 2).reshape(B, Nq, heads * dh))
+    assert torch.equal(dk_t, dk) and torch.equal(dv_t, dv)
+    d16 = torch.empty(B, Nq, heads * dh, dtype=BF16, device="cuda")
+    if dt == "bf16":
+        _lib.attn_bwd(qd, kv[:, 0], kv[:, 1], dd, dq=d16, dq_tokens=True)
+        torch.cuda.synchronize()
+        assert torch.equal(d16.view(torch.int16), dq_t.to(BF16).view(torch.int16))
+    else:
+        with pytest.raises(_lib.PtditError):
+            _lib.attn_bwd(qd, kv[:, 0], kv[:, 1], dd, dq=d16, dq_tokens=True)
+
+
 def test_attn_bwd_full_size_cross_attention(P):
     # cross-attention at 2048^2: 16384 token queries, 256 proxies, 16 heads;
     # the oracle takes two heads whole (dK, dV sum over every query)
