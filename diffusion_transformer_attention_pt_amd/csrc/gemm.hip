@@ -1015,7 +1015,10 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
         p.splits < 1 || p.splits > 65535)
       return hipErrorInvalidValue;
     if constexpr (sizeof(TA) == 2) {
-      if (p.M >= 2048 && p.K % 128 == 0 && p.K >= 256 && !p.R) return run_pp<TR, TY, HM>(p, s);
+      // from 1024 rows: the weight gradients of the D x D output maps too
+      // (1152 rows, ragged in 256-row tiles; the ping-pong kernel clamps the
+      // rows past M on load and drops them on store)
+      if (p.M >= 1024 && p.K % 128 == 0 && p.K >= 256 && !p.R) return run_pp<TR, TY, HM>(p, s);
     }
     if (p.M >= 1024) return run_dma<TA, TR, TY, 256, 288, 4, 2, STAGES, HM>(p, s);
     if (p.K / 32 < 4) return hipErrorInvalidValue;
