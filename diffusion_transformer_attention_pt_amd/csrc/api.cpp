@@ -941,7 +941,8 @@ ptdit_status ptdit_linear_bwd_ex(const void* x, ptdit_dtype x_dt, int64_t rows, 
   d.dyb = (want_dx && d_w && dy_dt == PTDIT_F32) ? dyb : nullptr;
   d.part = part; d.dbp = dbp; d.dw = d_w; d.db = d_b;
   d.rows = rows; d.d_in = d_in; d.d_out = d_out;
-  if (d_w && launch_wgrad_operands(d, stream) != hipSuccess) return PTDIT_ERR_HIP;
+  if (d_w && !wgrad_token_major(rows, d_in, d_out, d.dy_f32, d.x_f32) && launch_wgrad_operands(d, stream) != hipSuccess)
+    return PTDIT_ERR_HIP;
   if (want_dx) {
     // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight;
     // the added gradient is the GEMM's residual, the bf16 copy its second

@@ -37,6 +37,9 @@ struct GemmParams {
   // their rows) and Y (elements); splits = gridDim.y. The DMA kernels only.
   int64_t lda, ldw, ks_a, ks_w, ks_y;
   int splits;
+  // token-major operands (gemm_pp_kernel TN instance): K of the last split
+  // when it differs from K (0: the same)
+  int k_last;
 };
 
 // XCD-aware tile order: hardware hands block i to XCD (i % 8); re-number so
@@ -300,6 +303,103 @@ struct DmaPlan {
     for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
   }
 };
+
+// Token-major operands: the weight gradient dW = dY^T X contracts over the
+// token index t, which is the row index of both dY [T][d_out] and X [T][d_in].
+// A k-slice is 32 token rows x the tile's columns, staged as it lies in
+// memory, in LDS rows of TN_CPR = 36 16-byte chunks (a 288-column W tile; a
+// 256-column A tile leaves 4 chunks of a row unused, loaded with a copy of a
+// real chunk). Token row r's chunk c sits at position c ^ (2 * ((r >> 3) & 1)):
+// with the 576-byte pitch rows r .. r+3 start 64 bytes apart in the banks and
+// the XOR moves rows 8 apart by 32 bytes, so the 8 rows x 32 bytes that a
+// half-wave of one transposing read touches fall in distinct banks.
+// Fragments are then read with ds_read_b64_tr_b16 (see tn_frag).
+constexpr int TN_CPR = 36;
+__device__ __forceinline__ int tn_pos(int row, int c) { return c ^ (2 * ((row >> 3) & 1)); }
+
+template <int BM, int BN, int NW>
+struct DmaPlanTN {
+  static_assert(BM <= 8 * TN_CPR && BN <= 8 * TN_CPR, "tile columns fit an LDS row");
+  static constexpr int SA = 32 * TN_CPR, SB = 32 * TN_CPR;  // 16-byte slots per stage
+  static constexpr int IA = SA / 64, IB = SB / 64, IT = IA + IB;
+  static constexpr int MAXI = (IT + NW - 1) / NW;
+
+  const char* a_base;
+  const char* w_base;
+  int64_t a_step, w_step;  // bytes per k-slice (32 token rows)
+  bool is_a[MAXI];
+  uint32_t voff[MAXI];
+  int dst[MAXI];
+
+  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
+    const int64_t lda = p.lda, ldw = p.ldw, split = blockIdx.y;
+    a_base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(p.A) + split * p.ks_a * lda + m0);
+    w_base = reinterpret_cast<const char*>(p.W + split * p.ks_w * ldw + n0);
+    a_step = 64 * lda;
+    w_step = 64 * ldw;
+    // real chunks of the tile's columns (M, N multiples of 8); positions past
+    // them (row padding, a ragged last tile) load the last real chunk
+    const int ca = (int)(p.M - m0 < BM ? (p.M - m0) / 8 : BM / 8);
+    const int cw = p.N - n0 < BN ? (p.N - n0) / 8 : BN / 8;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j0 = wave + i * NW;
+      const int j = j0 < IT ? j0 : wave;
+      is_a[i] = j < IA;
+      const int sl = (j < IA ? j : j - IA) * 64 + lane, row = sl / TN_CPR, pos = sl % TN_CPR;
+      int c = tn_pos(row, pos);  // the chunk stored at pos (the map is its own inverse)
+      const int cmax = j < IA ? ca : cw;
+      if (c >= cmax) c = cmax - 1;
+      voff[i] = (uint32_t)(((int64_t)row * (j < IA ? lda : ldw) + 8 * c) * 2);
+      dst[i] = j < IA ? j * 64 : SA + (j - IA) * 64;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint4* st) const {
+    const char* const ak = a_base + kt * a_step;
+    const char* const wk = w_base + kt * w_step;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
+  }
+};
+
+// Fragment of a token-major operand: lane (i = lane % 16, g = lane / 16)
+// needs fragment row col0 + 16 j + i at k = 8 g .. 8 g + 7, i.e. LDS token
+// rows 8 g .. 8 g + 7 of one column. A transposing read (ds_read_b64_tr_b16)
+// in which lane l of a 16-lane group points at token row R + (l >> 2),
+// columns C + 4 (l & 3) .. +3 returns to lane i the column C + i at token
+// rows R .. R + 3 (the lane layout measured on gfx950); two such reads
+// (R = 8 g and 8 g + 4) make the fragment. Byte address of the first read of
+// fragment j: base + 32 j, base = bE for even j, bO for odd j (the chunk XOR
+// moves a lane by +-32 bytes depending on the parity of the 16-column block);
+// the second read is 4 rows (2304 bytes) further.
+struct TnFragBase {
+  int bE, bO;
+  __device__ __forceinline__ void init(int region_bytes, int col0w, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const int krow = 8 * g + (i >> 2), b = g & 1;  // (krow >> 3) & 1 == g & 1
+    const int byte = region_bytes + krow * TN_CPR * 16 + ((col0w >> 3) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+    const int bp = byte + 32 * b, bm = byte - 32 * b;
+    // block j's chunk pair has bit 1 = ((col0w >> 4) + j) & 1; with it set the
+    // XOR moves the lane down by 32 bytes
+    const bool P = ((col0w >> 4) & 1) != 0;
+    bE = P ? bm : bp;
+    bO = P ? bp : bm;
+  }
+};
+__device__ __forceinline__ uint2 tn_read(const uint4* st, int byte) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  typedef __attribute__((address_space(3))) char* lds_char;
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)((lds_char)(st) + byte));
+  return __builtin_bit_cast(uint2, r);
+}
+template <int J>
+__device__ __forceinline__ uint4 tn_frag(const uint4* st, const TnFragBase& fb) {
+  const int base = (J & 1) ? fb.bO : fb.bE;
+  const uint2 lo = tn_read(st, base + 32 * J);
+  const uint2 hi = tn_read(st, base + 32 * J + 4 * TN_CPR * 16);
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
 
 // Epilogue staging through the ring: band j = tile rows {wm*TM + j*16 + r},
 // i.e. WM*16 rows x BN columns, row pitch padded by 16 bytes. A bf16 band
@@ -616,9 +716,10 @@ gemm_dma_kernel(GemmParams p) {
 // (k = -1: the prologue's load); -1: none
 constexpr int pp_rblock(int k, int nb) { return k < 0 ? nb + k : (k < nb - 1 ? k : -1); }
 
-template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256>
+template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256, bool TOKMAJ = false>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   constexpr bool RIN = RKT > 0;
+  static_assert(!TOKMAJ || (!RIN && !HEADMAJOR && BM == 256), "token-major operands: the weight gradient only");
   static_assert(!RIN || (RKT == 36 && BM == 256), "one k-slice per accumulator block of a 64 x 144 wave tile");
   static_assert(BM == 256 || BM == 128, "wave tiles of 64 or 32 rows");
   using TA = uint16_t;
@@ -627,7 +728,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   constexpr int NB = FN * FM;  // accumulator blocks per wave
   constexpr int RL = RIN ? 1 : 0;
   static_assert(!RIN || !HEADMAJOR, "residual only for token-major output");
-  using DP = DmaPlan<TA, BM, BN, NW>;
+  using DP = typename std::conditional<TOKMAJ, DmaPlanTN<BM, BN, NW>, DmaPlan<TA, BM, BN, NW>>::type;
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int SA = DP::SA, MAXI = DP::MAXI;
   constexpr int SLOT = (DP::SA + DP::SB) > ES::SLOT ? (DP::SA + DP::SB) : ES::SLOT;
@@ -652,7 +753,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  const int KT = RIN ? RKT : p.K / 32;
+  const int KT = RIN ? RKT : ((p.k_last > 0 && (int)blockIdx.y == p.splits - 1) ? p.k_last : p.K) / 32;
 
   DP dma;
   dma.init(p, m0, n0, wave, lane);
@@ -665,12 +766,22 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   const int g = lane >> 4, lr = lane & 15;
   const int lofs_w = SA + DmaA<uint16_t>::lofs(wn * TN + lr, g);
   const int lofs_a = DmaA<TA>::lofs(wm * TM + lr, g);
+  TnFragBase fbw, fba;
+  if constexpr (TOKMAJ) {
+    fbw.init(SA * 16, wn * TN, lane);
+    fba.init(0, wm * TM, lane);
+  }
   uint4 wf[FN], xf[FM];
   auto read_frags = [&](const uint4* st) {
+    if constexpr (TOKMAJ) {
+      static_for<0, FN>([&](auto iI) { wf[decltype(iI)::value] = tn_frag<decltype(iI)::value>(st, fbw); });
+      static_for<0, FM>([&](auto jI) { xf[decltype(jI)::value] = tn_frag<decltype(jI)::value>(st, fba); });
+    } else {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
+      for (int i = 0; i < FN; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, lofs_a, j);
+      for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, lofs_a, j);
+    }
   };
   auto mfmas = [&]() {
 #pragma unroll
@@ -1069,6 +1180,20 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.ldw = d.ldw > 0 ? d.ldw : d.K;
   p.ks_a = d.ks_a; p.ks_w = d.ks_w; p.ks_y = d.ks_y;
   p.splits = d.splits > 0 ? d.splits : 1;
+  p.k_last = d.k_last;
+  if (d.tn) {
+    // token-major bf16 operands (the weight gradient): the ping-pong kernel's
+    // TN instance, 256 x 288 tiles, fp32 output, no bias / residual
+    const int kl = d.k_last > 0 ? d.k_last : d.K;
+    if (d.a_f32 || !d.y_f32 || d.R || d.bias || d.head_major || d.Y2 || p.K % 128 || p.K < 256 || kl % 128 ||
+        kl < 256 || p.M % 8 || p.N % 8 || p.M <= 0 || p.N <= 0 || p.lda <= 0 || p.ldw <= 0 ||
+        p.lda * 64 * 32 >= ((int64_t)1 << 31) || p.ldw * 64 * 32 >= ((int64_t)1 << 31))
+      return hipErrorInvalidValue;
+    const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
+    hipLaunchKernelGGL((gemm_pp_kernel<float, float, false, 0, 256, true>), dim3((unsigned)tiles, (unsigned)p.splits),
+                       dim3(512), 0, s, p);
+    return hipGetLastError();
+  }
   if (d.a_f32) {
     if (d.y_f32) return pick_r<float, float>(d, p, s);
     return pick_r<float, uint16_t>(d, p, s);

@@ -24,6 +24,10 @@ struct GemmDesc {
   // A, W (along their rows) and Y
   int64_t lda = 0, ldw = 0, ks_a = 0, ks_w = 0, ks_y = 0;
   int splits = 1;
+  // token-major operands: A [K][lda] and W [K][ldw] with the contraction
+  // index as their row (ks_a, ks_w in rows), bf16, fp32 Y (the weight
+  // gradient dY^T X); k_last: K of the last split when it differs (0: K)
+  int tn = 0, k_last = 0;
 };
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32
@@ -156,6 +160,8 @@ struct WgradDesc {
 };
 void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch);
 int colsum_splits(int64_t rows);
+// dW from token-major bf16 dY and X directly (no transposed copies)
+bool wgrad_token_major(int64_t rows, int d_in, int d_out, int dy_f32, int x_f32);
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s);
 hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s);  // the transposed copies (and dyb)
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s);           // then dW from them, and db

@@ -9,10 +9,15 @@
 //                     contraction over the token axis on the DMA GEMM kernels
 //                     (those of the token-row projections), the token axis
 //                     split over blockIdx.y into partials
-//   colsum_kernel     partial column sums of dY over 64-row blocks (only
-//                     when dW is not wanted: otherwise the transpose pass,
-//                     which reads every element of dY anyway, writes them)
+//   colsum_kernel     partial column sums of dY over 64-row blocks (when
+//                     no transpose pass reads dY: otherwise that pass,
+//                     which reads every element anyway, writes them)
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
+//
+// With bf16 dY and X, d_out >= 1024 and a token count that is a multiple of
+// 128, dW = dY^T X runs on the ping-pong kernel's token-major instance
+// straight from dY and X (both with the token index as their row): no
+// transposed copies; the last split may be longer (k_last).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -224,13 +229,41 @@ hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool wgrad_token_major(int64_t rows, int d_in, int d_out, int dy_f32, int x_f32) {
+  return !dy_f32 && !x_f32 && d_out >= 1024 && rows % 128 == 0 && rows >= 256;
+}
+
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
   int splits;
   int64_t tch;
   wgrad_plan(d.rows, d.d_in, d.d_out, splits, tch);
   const int64_t ld = splits * tch, nw = (int64_t)d.d_out * d.d_in;
-  if (d.dw) {
+  const bool tn = wgrad_token_major(d.rows, d.d_in, d.d_out, d.dy_f32, d.x_f32);
+  if (d.dw && tn) {
+    // whole splits of tch tokens, the remainder joined to the last one when it
+    // is shorter than the kernel's 256-token minimum
+    int sp = (int)((d.rows + tch - 1) / tch);
+    int64_t kl = d.rows - (int64_t)(sp - 1) * tch;
+    if (kl < 256 && sp > 1) {
+      --sp;
+      kl += tch;
+    }
+    GemmDesc g;
+    g.A = d.dy; g.a_f32 = 0;
+    g.W = d.x; g.bias = nullptr;
+    g.R = nullptr; g.r_f32 = 1;
+    g.Y = d.part; g.y_f32 = 1;
+    g.Y2 = nullptr;
+    g.M = d.d_out; g.N = d.d_in; g.K = (int)tch;
+    g.head_major = 0; g.Ntok = d.d_out; g.heads = 0; g.dh = 0; g.D = d.d_in;
+    g.lda = d.d_out; g.ldw = d.d_in; g.ks_a = tch; g.ks_w = tch; g.ks_y = nw; g.splits = sp;
+    g.tn = 1; g.k_last = sp > 1 ? (int)kl : 0;
+    if (sp == 1) g.K = (int)kl;
+    const hipError_t e = launch_gemm_bf16(g, s);
+    if (e != hipSuccess) return e;
+    splits = sp;
+  } else if (d.dw) {
     // dY^T [d_out][ld] and X^T [d_in][ld] (bf16, zero past rows), then
     // dW = dY^T (X^T)^T on the DMA GEMM kernels with the token axis as K,
     // split over blockIdx.y into partials [splits][d_out][d_in]
@@ -248,7 +281,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int csplits = colsum_splits(d.rows);
-  if (d.db && !d.dw) {  // with dW the transpose pass wrote the partials
+  if (d.db && (!d.dw || tn)) {  // else the transpose pass wrote the partials
     const dim3 grid((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits);
     if (d.dy_f32)
       hipLaunchKernelGGL((colsum_kernel<float>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),

@@ -300,6 +300,23 @@ def test_attn_bwd_tokens_layout(P, name):
             _lib.attn_bwd(qd, kv[:, 0], kv[:, 1], dd, dq=d16, dq_tokens=True)
 
 
+def test_linear_bwd_token_major_matches_transposed(P):
+    """The weight gradient from token-major bf16 operands equals, bit for bit,
+    the one from transposed copies (an fp32 x holding the same bf16 values
+    takes that path): same splits, same k order within each split."""
+    rows, d_in, d_out = 16384, 1152, 3456
+    announce(f"linear bwd token-major vs transposed rows={rows} d_out={d_out}")
+    g = np.random.Generator(np.random.PCG64(790))
+    x = round_bf16(g.standard_normal((rows, d_in)).astype(np.float32))
+    w = round_bf16(g.standard_normal((d_out, d_in)).astype(np.float32) * 0.02)
+    dy = round_bf16(g.standard_normal((rows, d_out)).astype(np.float32))
+    _, dw_tn, db_tn = P.linear_bwd(dev(x, BF16), dev(w, BF16), dev(dy, BF16), want_dx=False)
+    _, dw_t, db_t = P.linear_bwd(dev(x, F32), dev(w, BF16), dev(dy, BF16), want_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw_tn, dw_t)
+    np.testing.assert_allclose(host(db_tn), host(db_t), rtol=1e-5, atol=1e-4)
+
+
 def test_attn_bwd_full_size_cross_attention(P):
     # cross-attention at 2048^2: 16384 token queries, 256 proxies, 16 heads;
     # the oracle takes two heads whole (dK, dV sum over every query)
@@ -419,6 +436,12 @@ LIN_CASES = [
     (1, 8, 16, "bf16", "f32"),
     (777, 64, 200, "f32", "f32"),
     (16384, 1152, 1152, "bf16", "f32"),   # the 2048^2 output projection
+    # bf16 d_y and x, token counts a multiple of 128: dW from the token-major
+    # operands directly (no transposed copies)
+    (16384, 1152, 3456, "bf16", "bf16"),  # the 2048^2 Q/K/V projection: 4 splits of 4096
+    (2432, 1152, 3456, "bf16", "bf16"),   # splits of 640 tokens, the last 512; 3456 rows of dW ragged in 256
+    (1408, 1152, 1152, "bf16", "bf16"),   # a 128-token remainder joined to the last split (384)
+    (256, 1152, 1152, "bf16", "bf16"),    # one split of 256 tokens
 ]
 
 
