@@ -15,17 +15,22 @@ calls run in reverse order of the forward:
 Each attention's backward takes its head-major Q/K/V and attention output
 from the forward when it ran with keep=True (the calls' workspaces, kept
 apart), else recomputes them (ptdit_linear_heads, ptdit_window_attn /
-ptdit_attn) from the block's stored inputs. Then come the output
-projection's gradient (ptdit_linear_bwd_ex, whose d_x product writes the
-core's bf16 dO directly), the core's (ptdit_window_attn_bwd_tokens /
-ptdit_attn_bwd) and the input projections' (ptdit_linear_bwd_ex on the
-token-major dQ/dK/dV: the window cores write them so, in bf16, the precision
-the projection's gradient products read them in; the cross-attention core
-writes its dQ so too, ptdit_attn_bwd_tokens; the proxy keys' and values'
-gradients pass through ptdit_heads_to_tokens), the residual branch's gradient added in the
-d_x product's epilogue. The window average's gradient accumulates into dx
-(ptdit_proxy_pool_bwd). Every step runs in the library's kernels; torch only
-holds the buffers. bf16 precision blocks with window-average proxies.
+ptdit_attn) from the block's stored inputs. Then come the output projection's
+gradient (ptdit_linear_bwd_ex, whose d_x product writes the core's bf16 dO
+directly), the core's (ptdit_window_attn_bwd_tokens / ptdit_attn_bwd) and the
+input projections' (ptdit_linear_bwd_ex on the token-major dQ/dK/dV: the
+window cores write them so, in bf16, the precision the projection's gradient
+products read them in; the cross-attention core writes its dQ so too,
+ptdit_attn_bwd_tokens; the proxy keys' and values' gradients pass through
+ptdit_heads_to_tokens), the residual branch's gradient added in the d_x
+product's epilogue. The output projections' gradient products read bf16 dY
+(the precision their operands take anyway): dout rounded by
+ptdit_f32_to_bf16, dx2 and dx1 written in bf16 beside fp32 by the products
+that form them; with bf16 operands and a token count that is a multiple of
+128 the weight gradients need no transposed copies. The window average's
+gradient accumulates into dx (ptdit_proxy_pool_bwd). Every step runs in the
+library's kernels; torch only holds the buffers. bf16 precision blocks with
+window-average proxies.
 """
 from __future__ import annotations
 
@@ -57,6 +62,9 @@ class PTBlockBackward:
         self.dqkv_t16 = e(B, N, 3 * D, dt=bf)   # the window cores' gradient, token-major bf16
         self.dbkv = e(2, D)
         self.dx2, self.dx1, self.dx = e(B, N, D), e(B, N, D), e(B, N, D)
+        # bf16 copies of the residual-stream gradients for the output
+        # projections' gradient products (dout's, then dx1's; dx2's)
+        self.g16a, self.g16b = e(B, N, D, dt=bf), e(B, N, D, dt=bf)
         # cross-attention and proxy buffers
         self.q = e(B, 1, heads, N, dh, dt=bf)
         self.kv = e(B, 2, heads, M, dh, dt=bf)
@@ -76,9 +84,11 @@ class PTBlockBackward:
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def _window(self, xl: torch.Tensor, w: _lib.AttnWeights, shift, dy: torch.Tensor, dx_out: torch.Tensor,
-                kept=None):
+                kept=None, dy16=None, dx_out16=None):
         """One window attention's backward: returns its weight gradients and
-        writes dx_out = dy + d(branch)/dx^T dy. kept: (qkv, o) of the forward."""
+        writes dx_out = dy + d(branch)/dx^T dy (and its bf16 copy into
+        dx_out16). kept: (qkv, o) of the forward; dy16: bf16(dy), which the
+        output projection's gradient products read."""
         blk = self.blk
         B, N, D, heads = blk.B, blk.N, blk.D, blk.heads
         if kept is not None:
@@ -87,14 +97,16 @@ class PTBlockBackward:
             qkv, o = self.qkv, self.o
             _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=qkv)
             _lib.window_attn(qkv, w.b_qkv, blk.g, blk.win, shift, out=o)
-        _, dwo, dbo = _lib.linear_bwd(o, w.w_o, dy, ws=self.ws, want_dx=False, dx_bf16=self.do16)
+        _, dwo, dbo = _lib.linear_bwd(o, w.w_o, dy16 if dy16 is not None else dy, ws=self.ws, want_dx=False,
+                                      dx_bf16=self.do16)
         if self.pads:
             self.dbkv.zero_()
         # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
         _lib.window_attn_bwd(qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t16,
                              d_b_kv=self.dbkv if self.pads else None, tokens=True)
         # dx_out = dy (the residual) + d(branch)/dx^T dy, joined in the product
-        _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t16, ws=self.ws, dx=dx_out, dx_add=dy)
+        _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t16, ws=self.ws, dx=dx_out, dx_add=dy,
+                                          dx_bf16=dx_out16)
         if self.pads:   # pad slots' key/value gradients reach b_k, b_v
             _lib.add_f32(dbqkv[D:], self.dbkv.view(-1), out=dbqkv[D:])
         return {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
@@ -112,10 +124,15 @@ class PTBlockBackward:
             raise ValueError("dout must be a contiguous fp32 tensor")
         grads: List[dict] = [None] * 4
         k = blk.kept
+        # the output projections' gradient products take bf16(dY): dout's
+        # rounded here, dx2's and dx1's written by the products that form them
+        _lib.f32_to_bf16(dout, out=self.g16a)
         grads[3] = self._window(blk.x2_lowp, w[3], blk.shift, dout, self.dx2,
-                                kept=(k["swsa_qkv"], k["swsa_o"]) if k else None)
+                                kept=(k["swsa_qkv"], k["swsa_o"]) if k else None, dy16=self.g16a,
+                                dx_out16=self.g16b)
         grads[2] = self._window(blk.x1_lowp, w[2], (0, 0, 0), self.dx2, self.dx1,
-                                kept=(k["wsa_qkv"], k["wsa_o"]) if k else None)
+                                kept=(k["wsa_qkv"], k["wsa_o"]) if k else None, dy16=self.g16b,
+                                dx_out16=self.g16a)
         # cross-attention: tokens are queries, the attended proxies P' keys/values
         wc = w[1]
         if k:
@@ -127,7 +144,7 @@ class PTBlockBackward:
             _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
                               B, M, heads, out=kv)
             _lib.attn(q[:, 0], kv[:, 0], kv[:, 1], out=o)
-        _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.dx1, ws=self.ws, want_dx=False, dx_bf16=self.do16)
+        _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.g16a, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         # dQ token-major bf16 [B, N, D] into the (now free) window gradient buffer
         dq_t = self.dqkv_t16.view(-1)[:B * N * D].view(B, N, D)
         _lib.attn_bwd(q[:, 0], kv[:, 0], kv[:, 1], self.do16, ws=self.ws,
