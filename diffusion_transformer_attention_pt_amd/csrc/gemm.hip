@@ -38,8 +38,10 @@ struct GemmParams {
   int64_t lda, ldw, ks_a, ks_w, ks_y;
   int splits;
   // token-major operands (gemm_pp_kernel TN instance): K of the last split
-  // when it differs from K (0: the same)
+  // when it differs from K (0: the same; a multiple of 128), and the tokens of
+  // that split that exist (0: all); the rows past them read as zero
   int k_last;
+  int k_valid;
 };
 
 // XCD-aware tile order: hardware hands block i to XCD (i % 8); re-number so
@@ -302,6 +304,7 @@ struct DmaPlan {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
   }
+  __device__ __forceinline__ void issue_head(int kt, uint4* st) const { issue(kt, st); }
 };
 
 // Token-major operands: the weight gradient dW = dY^T X contracts over the
@@ -316,6 +319,15 @@ struct DmaPlan {
 // Fragments are then read with ds_read_b64_tr_b16 (see tn_frag).
 constexpr int TN_CPR = 36;
 __device__ __forceinline__ int tn_pos(int row, int c) { return c ^ (2 * ((row >> 3) & 1)); }
+// zeros in device memory (static storage, never written): 32 rows of up to
+// TN_ZERO_LD elements (so a slice's per-lane offsets stay inside it). The
+// final split, when its real tokens (k_valid) are fewer than its K (k_last,
+// a multiple of 128), starts k_last - k_valid tokens early, so that it ends
+// at the last token, and its first (k_last - k_valid) / 32 <= 3 k-slices
+// (tokens of the split before it) read these zeros instead: they are issued
+// in the prologue only, so the main loop carries no check.
+constexpr int TN_ZERO_LD = 4096;
+__device__ __attribute__((aligned(16))) uint16_t tn_zero_slice[32 * TN_ZERO_LD];
 
 template <int BM, int BN, int NW>
 struct DmaPlanTN {
@@ -327,14 +339,19 @@ struct DmaPlanTN {
   const char* a_base;
   const char* w_base;
   int64_t a_step, w_step;  // bytes per k-slice (32 token rows)
+  int nz;                  // leading k-slices that read zeros (final split; <= 3)
   bool is_a[MAXI];
   uint32_t voff[MAXI];
   int dst[MAXI];
 
   __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
     const int64_t lda = p.lda, ldw = p.ldw, split = blockIdx.y;
-    a_base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(p.A) + split * p.ks_a * lda + m0);
-    w_base = reinterpret_cast<const char*>(p.W + split * p.ks_w * ldw + n0);
+    const bool last = (int)blockIdx.y == p.splits - 1 && p.k_valid > 0;
+    const int kl = p.k_last > 0 ? p.k_last : p.K;
+    nz = last ? (kl - p.k_valid) / 32 : 0;
+    const int64_t t0a = split * p.ks_a - 32 * nz, t0w = split * p.ks_w - 32 * nz;  // first token row
+    a_base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(p.A) + t0a * lda + m0);
+    w_base = reinterpret_cast<const char*>(p.W + t0w * ldw + n0);
     a_step = 64 * lda;
     w_step = 64 * ldw;
     // real chunks of the tile's columns (M, N multiples of 8); positions past
@@ -357,6 +374,16 @@ struct DmaPlanTN {
   __device__ __forceinline__ void issue(int kt, uint4* st) const {
     const char* const ak = a_base + kt * a_step;
     const char* const wk = w_base + kt * w_step;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
+  }
+  // the prologue's slices 0..2: the final split's leading nz slices read the
+  // zero region (offsets row * ld + column, ld <= TN_ZERO_LD, stay inside it)
+  __device__ __forceinline__ void issue_head(int kt, uint4* st) const {
+    const bool z = kt < nz;
+    const char* const zero = reinterpret_cast<const char*>(tn_zero_slice);
+    const char* const ak = z ? zero : a_base + kt * a_step;
+    const char* const wk = z ? zero : w_base + kt * w_step;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
   }
@@ -865,12 +892,12 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   // Prologue: slices 0..2 (and, with RIN, the residual of block NB-1 after
   // slice 1, into buffer 1), slice 0 landed (barrier #0); group 1 then takes
   // its extra barrier.
-  dma.issue(0, slot(std::integral_constant<int, 0>{}));
-  dma.issue(1, slot(std::integral_constant<int, 1>{}));
+  dma.issue_head(0, slot(std::integral_constant<int, 0>{}));
+  dma.issue_head(1, slot(std::integral_constant<int, 1>{}));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (RIN) rbuf[1] = rload(std::integral_constant<int, pp_rblock(-1, NB)>{});
   __builtin_amdgcn_sched_barrier(0);
-  dma.issue(2, slot(std::integral_constant<int, 2>{}));
+  dma.issue_head(2, slot(std::integral_constant<int, 2>{}));
   wait_vm_lgkm0<2 * MAXI + RL>();
   ring_barrier();
   if (wn == 1) ring_barrier();
@@ -1181,12 +1208,15 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.ks_a = d.ks_a; p.ks_w = d.ks_w; p.ks_y = d.ks_y;
   p.splits = d.splits > 0 ? d.splits : 1;
   p.k_last = d.k_last;
+  p.k_valid = d.k_valid;
   if (d.tn) {
     // token-major bf16 operands (the weight gradient): the ping-pong kernel's
     // TN instance, 256 x 288 tiles, fp32 output, no bias / residual
     const int kl = d.k_last > 0 ? d.k_last : d.K;
     if (d.a_f32 || !d.y_f32 || d.R || d.bias || d.head_major || d.Y2 || p.K % 128 || p.K < 256 || kl % 128 ||
-        kl < 256 || p.M % 8 || p.N % 8 || p.M <= 0 || p.N <= 0 || p.lda <= 0 || p.ldw <= 0 ||
+        kl < 256 || d.k_valid < 0 || d.k_valid > kl || d.k_valid % 32 ||
+        (d.k_valid > 0 && d.k_valid < kl && (p.lda > TN_ZERO_LD || p.ldw > TN_ZERO_LD)) || p.M % 8 || p.N % 8 ||
+        p.M <= 0 || p.N <= 0 || p.lda <= 0 || p.ldw <= 0 ||
         p.lda * 64 * 32 >= ((int64_t)1 << 31) || p.ldw * 64 * 32 >= ((int64_t)1 << 31))
       return hipErrorInvalidValue;
     const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);

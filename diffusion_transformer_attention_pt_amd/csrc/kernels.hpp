@@ -26,8 +26,9 @@ struct GemmDesc {
   int splits = 1;
   // token-major operands: A [K][lda] and W [K][ldw] with the contraction
   // index as their row (ks_a, ks_w in rows), bf16, fp32 Y (the weight
-  // gradient dY^T X); k_last: K of the last split when it differs (0: K)
-  int tn = 0, k_last = 0;
+  // gradient dY^T X); k_last: K of the last split when it differs (0: K);
+  // k_valid: the tokens of the last split that exist (0: all of its K)
+  int tn = 0, k_last = 0, k_valid = 0;
 };
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32

@@ -14,10 +14,11 @@
 //                     which reads every element anyway, writes them)
 //   wgrad_reduce      fixed-order sum of the partials (deterministic)
 //
-// With bf16 dY and X, d_out >= 1024 and a token count that is a multiple of
-// 128, dW = dY^T X runs on the ping-pong kernel's token-major instance
-// straight from dY and X (both with the token index as their row): no
-// transposed copies; the last split may be longer (k_last).
+// With bf16 dY and X, 1024 <= d_out <= 4096, d_in <= 4096 and a token count
+// that is a multiple of 32 (at least 256), dW = dY^T X runs on the ping-pong
+// kernel's token-major instance straight from dY and X (both with the token
+// index as their row): no transposed copies; the last split may be longer
+// (k_last) and end in whole 32-token slices that read as zero (k_valid).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -230,7 +231,7 @@ hipError_t launch_wgrad_operands(const WgradDesc& d, hipStream_t s) {
 }
 
 bool wgrad_token_major(int64_t rows, int d_in, int d_out, int dy_f32, int x_f32) {
-  return !dy_f32 && !x_f32 && d_out >= 1024 && rows % 128 == 0 && rows >= 256;
+  return !dy_f32 && !x_f32 && d_out >= 1024 && d_out <= 4096 && d_in <= 4096 && rows % 32 == 0 && rows >= 256;
 }
 
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
@@ -242,13 +243,15 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   const bool tn = wgrad_token_major(d.rows, d.d_in, d.d_out, d.dy_f32, d.x_f32);
   if (d.dw && tn) {
     // whole splits of tch tokens, the remainder joined to the last one when it
-    // is shorter than the kernel's 256-token minimum
+    // is shorter than the kernel's 256-token minimum; the last split's K is
+    // rounded up to 128 tokens, the rows past its kv real ones read as zero
     int sp = (int)((d.rows + tch - 1) / tch);
-    int64_t kl = d.rows - (int64_t)(sp - 1) * tch;
-    if (kl < 256 && sp > 1) {
+    int64_t kv = d.rows - (int64_t)(sp - 1) * tch;
+    if (kv < 256 && sp > 1) {
       --sp;
-      kl += tch;
+      kv += tch;
     }
+    const int64_t kl = (kv + 127) / 128 * 128 < 256 ? 256 : (kv + 127) / 128 * 128;
     GemmDesc g;
     g.A = d.dy; g.a_f32 = 0;
     g.W = d.x; g.bias = nullptr;
@@ -258,7 +261,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     g.M = d.d_out; g.N = d.d_in; g.K = (int)tch;
     g.head_major = 0; g.Ntok = d.d_out; g.heads = 0; g.dh = 0; g.D = d.d_in;
     g.lda = d.d_out; g.ldw = d.d_in; g.ks_a = tch; g.ks_w = tch; g.ks_y = nw; g.splits = sp;
-    g.tn = 1; g.k_last = sp > 1 ? (int)kl : 0;
+    g.tn = 1; g.k_last = (int)kl; g.k_valid = (int)kv;
     if (sp == 1) g.K = (int)kl;
     const hipError_t e = launch_gemm_bf16(g, s);
     if (e != hipSuccess) return e;

@@ -442,6 +442,11 @@ LIN_CASES = [
     (2432, 1152, 3456, "bf16", "bf16"),   # splits of 640 tokens, the last 512; 3456 rows of dW ragged in 256
     (1408, 1152, 1152, "bf16", "bf16"),   # a 128-token remainder joined to the last split (384)
     (256, 1152, 1152, "bf16", "bf16"),    # one split of 256 tokens
+    # token counts a multiple of 32 only: the last split starts early and its
+    # first slices read zeros
+    (21600, 1152, 3456, "bf16", "bf16"),  # the 16 x 30 x 45 video's Q/K/V projection
+    (1312, 1152, 1152, "bf16", "bf16"),   # splits of 256, the last 288 tokens in K 384: 3 zero slices
+    (288, 1152, 1152, "bf16", "bf16"),    # one split, 288 tokens in K 384 (it starts 96 tokens early)
 ]
 
 
