@@ -152,34 +152,32 @@ __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy
   *reinterpret_cast<float4*>(dbp + (int64_t)blockIdx.y * d_out + o) = r;
 }
 
+// four consecutive elements a thread (nw and d_out multiples of 4, 16-byte
+// aligned rows), eight partials in flight, each element summed in split
+// order (deterministic)
+__device__ __forceinline__ void add4(float4& s, const float4& v) {
+  s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+}
+__device__ __forceinline__ float4 sum_splits4(const float* __restrict__ part, int64_t stride, int n, int64_t e) {
+  float4 s = float4{0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(part + (int64_t)(k + u) * stride + e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add4(s, v[u]);
+  }
+  for (; k < n; ++k) add4(s, *reinterpret_cast<const float4*>(part + (int64_t)k * stride + e));
+  return s;
+}
 __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ dbp, float* __restrict__ dw,
                                                              float* __restrict__ db, int splits, int csplits,
                                                              int64_t nw, int d_out) {
-  const int64_t e = (int64_t)blockIdx.x * LB_NT + threadIdx.x;
-  if (e < nw && dw) {
-    // four loads in flight, added in split order
-    float s = 0.f;
-    int k = 0;
-    for (; k + 4 <= splits; k += 4) {
-      const float a0 = part[(int64_t)k * nw + e], a1 = part[(int64_t)(k + 1) * nw + e];
-      const float a2 = part[(int64_t)(k + 2) * nw + e], a3 = part[(int64_t)(k + 3) * nw + e];
-      s += a0; s += a1; s += a2; s += a3;
-    }
-    for (; k < splits; ++k) s += part[(int64_t)k * nw + e];
-    dw[e] = s;
-  }
-  if (e < d_out && db) {
-    float s = 0.f;
-    int k = 0;
-    for (; k + 4 <= csplits; k += 4) {
-      const float a0 = dbp[(int64_t)k * d_out + e], a1 = dbp[(int64_t)(k + 1) * d_out + e];
-      const float a2 = dbp[(int64_t)(k + 2) * d_out + e], a3 = dbp[(int64_t)(k + 3) * d_out + e];
-      s += a0; s += a1; s += a2; s += a3;
-    }
-    for (; k < csplits; ++k) s += dbp[(int64_t)k * d_out + e];
-    db[e] = s;
-  }
+  const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
+  if (e < nw && dw) *reinterpret_cast<float4*>(dw + e) = sum_splits4(part, nw, splits, e);
+  if (e < d_out && db) *reinterpret_cast<float4*>(db + e) = sum_splits4(dbp, d_out, csplits, e);
 }
 
 // ----------------------------------------------------------------------------
@@ -296,7 +294,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int64_t n = nw > d.d_out ? nw : d.d_out;
-  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s, d.part,
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s, d.part,
                      d.dbp, d.dw, d.db, splits, csplits, nw, d.d_out);
   return hipGetLastError();
 }
