@@ -139,8 +139,10 @@ def backward_timings(wl, blk, prec, reps: int = 10, per_call: bool = True) -> di
     xl = torch.randn(B * N, D, device=dev).to(prec)
     w_o = (torch.randn(D, D, device=dev) * 0.02).to(torch.bfloat16)
     w_qkv = (torch.randn(3 * D, D, device=dev) * 0.02).to(torch.bfloat16)
-    dy_o = torch.randn(B * N, D, device=dev)
-    dy_qkv = torch.randn(B * N, 3 * D, device=dev)
+    # d_y in bf16, as the block backward hands it over (the window cores'
+    # dQ/dK/dV, the residual-stream gradient's bf16 copy)
+    dy_o = torch.randn(B * N, D, device=dev).to(prec)
+    dy_qkv = torch.randn(B * N, 3 * D, device=dev).to(prec)
     lws = torch.empty(_lib.load().ptdit_linear_bwd_workspace_bytes(B * N, D, 3 * D), dtype=torch.uint8, device=dev)
     cases = {
         "window_bwd": (_lib.K_BWD_WINDOW,
@@ -156,12 +158,12 @@ def backward_timings(wl, blk, prec, reps: int = 10, per_call: bool = True) -> di
         "pool_bwd": (_lib.K_BWD_POOL, lambda: _lib.proxy_pool_bwd(dP, grid, wl.p, d_x=dx),
                      0, B * M * D * 4 + B * N * D * 4),
         # projection gradients (dX, dW, db) of the output map and of the Q/K/V
-        # map of the token rows; d_y fp32 as the core backward produces it
+        # map of the token rows (x and d_y read, fp32 dX, dW written)
         "linear_bwd_out": (_lib.K_BWD_LINEAR, lambda: _lib.linear_bwd(xl, w_o, dy_o, ws=lws),
-                           2 * 2 * B * N * D * D, B * N * D * 2 + D * D * 2 + B * N * D * 4 + B * N * D * 4
+                           2 * 2 * B * N * D * D, B * N * D * es + D * D * 2 + B * N * D * es + B * N * D * 4
                            + D * D * 4),
         "linear_bwd_qkv": (_lib.K_BWD_LINEAR, lambda: _lib.linear_bwd(xl, w_qkv, dy_qkv, ws=lws),
-                           2 * 2 * B * N * D * 3 * D, B * N * D * 2 + 3 * D * D * 2 + 3 * B * N * D * 4
+                           2 * 2 * B * N * D * 3 * D, B * N * D * es + 3 * D * D * 2 + 3 * B * N * D * es
                            + B * N * D * 4 + 3 * D * D * 4),
     }
     res = {}
