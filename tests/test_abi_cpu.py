@@ -405,3 +405,43 @@ def test_linear_bwd_ex_validates_on_the_host(lib):
     assert call(b16_=ctypes.c_void_p((1 << 36) + 64)) == -8         # bf16 copy inside d_x
     assert call(add_=ctypes.c_void_p((1 << 36) + 16)) == -8         # a shifted view of d_x
     assert lib.ptdit_linear_bwd_ex(x, 1, 0, di, do, w, dy, 1, dx, add, b16, dw, db, ws, need, None) == 0
+
+
+def test_keep_and_token_major_gradient_calls_validate_on_the_host(lib):
+    """ptdit_window_sa_keep, ptdit_window_attn_bwd_tokens and
+    ptdit_attn_bwd_tokens refusals (nothing launched): bf16 gradients only
+    from bf16 inputs, the window call's own checks for the keep variant."""
+    import ctypes
+    from diffusion_transformer_attention_pt_amd._lib import AttnW, Grid, Win3
+    fake = ctypes.c_void_p(1 << 20)
+    g = Grid(1, 1, 16, 16, 1152, 16)
+    w = AttnW(fake.value, None, fake.value, None)
+    far, ws = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 44)
+    # keep variant: same refusals as the window call
+    assert lib.ptdit_window_sa_keep(None, None, 0, g, Win3(1, 8, 8), Win3(0, 0, 0), ctypes.byref(w), 1, far,
+                                    None, 0, ws, 1 << 30, 0, None) == -1
+    assert lib.ptdit_window_sa_keep(fake, None, 0, g, Win3(1, 8, 8), Win3(0, 8, 4), ctypes.byref(w), 1, far,
+                                    None, 0, ws, 1 << 30, 0, None) == -2
+    assert lib.ptdit_window_sa_keep(fake, None, 0, g, Win3(1, 8, 8), Win3(0, 4, 4), ctypes.byref(w), 1, far,
+                                    None, 0, ws, 16, 0, None) == -6
+    assert lib.ptdit_window_sa_keep(fake, None, 0, Grid(1, 1, 0, 16, 1152, 16), Win3(1, 8, 8), Win3(0, 4, 4),
+                                    ctypes.byref(w), 1, far, None, 0, ws, 16, 0, None) == 0  # nothing to do
+    # window gradients: bf16 output from fp32 inputs is refused, a bad dtype too
+    qkv, do, dq = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 32), ctypes.c_void_p(1 << 34)
+    assert lib.ptdit_window_attn_bwd_tokens(qkv, None, do, 1, g, Win3(1, 8, 8), Win3(0, 4, 4), dq, 0, None,
+                                            None) == -4
+    assert lib.ptdit_window_attn_bwd_tokens(qkv, None, do, 0, g, Win3(1, 8, 8), Win3(0, 4, 4), dq, 7, None,
+                                            None) == -4
+    assert lib.ptdit_window_attn_bwd_tokens(qkv, None, do, 0, g, Win3(1, 8, 8), Win3(0, 4, 4),
+                                            ctypes.c_void_p((1 << 30) + 64), 0, None, None) == -8  # dq in qkv
+    # dense gradients with token-major dQ: the same dtype rule, the alias check
+    # against the token-major extent
+    k, v, dk, dv = (ctypes.c_void_p(1 << s) for s in (36, 37, 38, 39))
+    B, heads, Nq, Nk, dh = 1, 16, 1024, 256, 72
+    need = lib.ptdit_attn_bwd_workspace_bytes(B, heads, Nq, Nk, dh)
+    call = lambda dt, qdt, dq_=dq: lib.ptdit_attn_bwd_tokens(qkv, heads * Nq * dh, k, v, heads * Nk * dh, do, dt,
+                                                             B, heads, Nq, Nk, dh, dq_, qdt, dk, dv,
+                                                             heads * Nk * dh, ws, need, None)
+    assert call(1, 0) == -4                                         # bf16 dQ from fp32 inputs
+    assert call(0, 0, dq_=ctypes.c_void_p((1 << 32) + 1024)) == -8  # dQ inside d_o
+    assert call(0, 0, dq_=ctypes.c_void_p((1 << 34) + 8)) == -5     # misaligned
