@@ -275,8 +275,8 @@ struct DmaPlan {
   uint32_t voff[MAXI];
   int dst[MAXI];
 
-  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
-    const int64_t lda = p.lda, ldw = p.ldw, split = blockIdx.y;
+  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane, int split_) {
+    const int64_t lda = p.lda, ldw = p.ldw, split = split_;
     a_base = reinterpret_cast<const char*>(reinterpret_cast<const TA*>(p.A) + m0 * lda + split * p.ks_a);
     w_base = reinterpret_cast<const char*>(p.W + (int64_t)n0 * ldw + split * p.ks_w);
 #pragma unroll
@@ -344,9 +344,9 @@ struct DmaPlanTN {
   uint32_t voff[MAXI];
   int dst[MAXI];
 
-  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane) {
-    const int64_t lda = p.lda, ldw = p.ldw, split = blockIdx.y;
-    const bool last = (int)blockIdx.y == p.splits - 1 && p.k_valid > 0;
+  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane, int split_) {
+    const int64_t lda = p.lda, ldw = p.ldw, split = split_;
+    const bool last = split_ == p.splits - 1 && p.k_valid > 0;
     const int kl = p.k_last > 0 ? p.k_last : p.K;
     nz = last ? (kl - p.k_valid) / 32 : 0;
     const int64_t t0a = split * p.ks_a - 32 * nz, t0w = split * p.ks_w - 32 * nz;  // first token row
@@ -456,11 +456,11 @@ struct EpiShape {
 template <typename TR, typename TY, int BM, int BN, int WM, int WN, int STAGES, bool HEADMAJOR, class SlotFn>
 __device__ __forceinline__ void ring_epilogue(const GemmParams& p, const floatx4 (&acc)[BN / WN / 16][BM / WM / 16],
                                               const uint2 (&biasp)[BN / WN / 16], SlotFn&& slot, int tid,
-                                              int lane, int wm, int wn, int64_t m0, int n0) {
+                                              int lane, int wm, int wn, int64_t m0, int n0, int split) {
   constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int BPP = ES::BPP;
-  TY* Y = reinterpret_cast<TY*>(p.Y) + (int64_t)blockIdx.y * p.ks_y;
+  TY* Y = reinterpret_cast<TY*>(p.Y) + (int64_t)split * p.ks_y;
   const TR* R = reinterpret_cast<const TR*>(p.R);
   constexpr int E = 16 / (int)sizeof(TY);          // elements per 16-byte chunk
   constexpr int CPRO = BN / E;                     // chunks per staged row
@@ -646,7 +646,7 @@ gemm_dma_kernel(GemmParams p) {
   const int KT = p.K / 32;
 
   DP dma;
-  dma.init(p, m0, n0, wave, lane);
+  dma.init(p, m0, n0, wave, lane, blockIdx.y);
 
   floatx4 acc[FN][FM];
 #pragma unroll
@@ -703,7 +703,8 @@ gemm_dma_kernel(GemmParams p) {
 
   wait_vm_lgkm0<0>();
   ring_barrier();  // ring drained, every fragment read retired
-  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(p, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
+  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(p, acc, biasp, slot, tid, lane, wm, wn, m0, n0,
+                                                          blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -775,15 +776,32 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;  // wn is the group
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (p.N + BN - 1) / BN;
-  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
+  int tm, tn, split;
+  if constexpr (TOKMAJ) {
+    // one-dimensional grid over (split, tm, tn): XCD k (the hardware hands
+    // block i to XCD i % 8) walks a contiguous range of that order, tn
+    // fastest, so the workgroups of an XCD share the dY slabs of their row
+    // tiles and the X slabs of one split in its L2 (the row-major order of
+    // the other kernels would spread a dY slab over four XCDs)
+    const int nt = tiles_m * tiles_n, total = nt * p.splits;
+    if ((int)blockIdx.x >= total) return;
+    const int q = total >> 3, rem = total & 7, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    split = logical / nt;
+    const int in = logical - split * nt;
+    tm = in / tiles_n;
+    tn = in - tm * tiles_n;
+  } else {
+    if ((int)blockIdx.x >= tiles_m * tiles_n) return;
+    tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, tm, tn);
+    split = blockIdx.y;
+  }
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  const int KT = RIN ? RKT : ((p.k_last > 0 && (int)blockIdx.y == p.splits - 1) ? p.k_last : p.K) / 32;
+  const int KT = RIN ? RKT : ((p.k_last > 0 && split == p.splits - 1) ? p.k_last : p.K) / 32;
 
   DP dma;
-  dma.init(p, m0, n0, wave, lane);
+  dma.init(p, m0, n0, wave, lane, split);
   floatx4 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -936,7 +954,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   if constexpr (RIN) pe.R = nullptr;  // every block's residual is in the accumulators
   uint2 biasp[FN];
   load_bias<FN>(p, n0 + wn * TN, lane, biasp);
-  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(pe, acc, biasp, slot, tid, lane, wm, wn, m0, n0);
+  ring_epilogue<TR, TY, BM, BN, WM, WN, STAGES, HEADMAJOR>(pe, acc, biasp, slot, tid, lane, wm, wn, m0, n0, split);
 }
 
 // ----------------------------------------------------------------------------
@@ -1220,7 +1238,8 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
         p.lda * 64 * 32 >= ((int64_t)1 << 31) || p.ldw * 64 * 32 >= ((int64_t)1 << 31))
       return hipErrorInvalidValue;
     const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
-    hipLaunchKernelGGL((gemm_pp_kernel<float, float, false, 0, 256, true>), dim3((unsigned)tiles, (unsigned)p.splits),
+    // one-dimensional grid: the kernel maps it onto (split, row tile, column tile)
+    hipLaunchKernelGGL((gemm_pp_kernel<float, float, false, 0, 256, true>), dim3((unsigned)(tiles * p.splits)),
                        dim3(512), 0, s, p);
     return hipGetLastError();
   }
