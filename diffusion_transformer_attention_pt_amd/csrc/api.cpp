@@ -175,6 +175,8 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   WFusedDesc fd;
   fd.X = xa; fd.w_qkv = w->w_qkv; fd.b_qkv = w->b_qkv; fd.O = o;
   fd.qkv_out = keep ? qkv : nullptr;  // the unfused path writes Q/K/V there anyway
+  // the weights packed in the fused kernel's DMA order, after Q/K/V and O
+  fd.w_packed = (char*)o + align_up((size_t)rows * D * esize(prec));
   fd.B = g.B; fd.F = g.F; fd.H = g.H; fd.W = g.W; fd.D = D; fd.heads = g.heads; fd.dh = D / g.heads;
   fd.wt = win.t; fd.wh = win.h; fd.ww = win.w;
   fd.st = shift.t; fd.sh = shift.h; fd.sw = shift.w;
@@ -183,6 +185,8 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   fd.Wp = (g.W + win.w - 1) / win.w * win.w;
   fd.scale = 1.0f / std::sqrt((float)fd.dh);
   if (prec == PTDIT_BF16 && xa && wfused_supported(fd)) {
+    e = launch_wfused_pack(fd, stream);
+    if (e != hipSuccess) return PTDIT_ERR_HIP;
     {
       TraceScope ts(PTDIT_K_WINDOW_FUSED, stream);
       e = launch_wfused(fd, stream);
@@ -255,8 +259,10 @@ size_t ptdit_workspace_bytes(ptdit_op op, ptdit_grid g, int32_t M, ptdit_win3 wi
     case PTDIT_OP_SHIFT_WINDOW_SA:
       // windows the calls reject need no workspace: 0 (invalid arguments)
       if (win.t <= 0 || win.h <= 0 || win.w <= 0 || (int64_t)win.t * win.h * win.w > 128) return 0;
-      // Q/K/V and the attention output (the fused kernel uses only the latter)
-      return align_up(B * 3 * N * D * es) + align_up(B * N * D * es);
+      // Q/K/V and the attention output (the fused kernel uses only the
+      // latter), then (bf16) w_qkv packed for the fused kernel, 3 D^2 bf16
+      return align_up(B * 3 * N * D * es) + align_up(B * N * D * es) +
+             (prec == PTDIT_BF16 ? align_up(3 * D * D * 2) : 0);
     case PTDIT_OP_MLP:
       if (M <= 0) return 0;
       return align_up(B * N * (size_t)M * es);

@@ -88,6 +88,7 @@ struct WFusedDesc {
   const void* X; const void* w_qkv; const void* b_qkv;
   void* O;
   void* qkv_out = nullptr;  // optional head-major Q/K/V [B][3][heads][N][dh] (the backward's copy)
+  void* w_packed = nullptr; // wfused_packed_bytes(D) bytes: w_qkv in the kernel's DMA order (launch_wfused_pack)
   int B, F, H, W, D, heads, dh;
   int wt, wh, ww;
   int st, sh, sw;
@@ -95,6 +96,10 @@ struct WFusedDesc {
   float scale;
 };
 bool wfused_supported(const WFusedDesc& d);
+// packed weights: launch_wfused_pack writes them from w_qkv into w_packed,
+// launch_wfused reads them from there (stream order joins the two)
+size_t wfused_packed_bytes(int D);
+hipError_t launch_wfused_pack(const WFusedDesc& d, hipStream_t s);
 hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s);
 
 // util.hip: chaining the backward calls

@@ -55,6 +55,7 @@ constexpr int WF_SA = WF_BM * 4;           // 16-byte LDS slots of A per k-slice
 constexpr int WF_SB = WF_NWR * 4;          // ... of W
 constexpr int WF_IA = WF_SA / 64, WF_IT = WF_IA + WF_SB / 64;  // DMA instructions per slice
 constexpr int WF_MAXI = (WF_IT + WF_NW - 1) / WF_NW;
+constexpr int WF_PK_SLICE = WF_SB * 16;    // bytes of one packed weight k-slice (27 KB)
 static_assert(WF_WN * WF_FN == WF_NBLK + 1, "one spare column block");
 
 // staging of one window (both heads of the pair) in the drained ring (bytes)
@@ -75,7 +76,7 @@ struct WfStage {
 
 struct WFusedParams {
   const uint16_t* X;     // [B][N][D] bf16
-  const uint16_t* W;     // w_qkv [3D][D] bf16
+  const uint16_t* Wpk;   // w_qkv packed by wfused_pack_kernel: [head pair][k-slice][WF_SB 16-byte chunks]
   const uint16_t* bias;  // b_qkv [3D] bf16 or null
   uint16_t* O;           // [B][N][D] bf16
   uint16_t* QKV;         // KEEP: head-major Q/K/V [B][3][heads][N][72] bf16 of the real tokens
@@ -174,9 +175,15 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
 
   // DMA plan: instruction j of a slice moves 64 16-byte chunks, A rows for
   // j < WF_IA (4 chunks a row, swizzled as DmaA<bf16>), W rows after; wave w
-  // owns j = w + i*8 and repeats its first instruction to make WF_MAXI.
+  // owns j = w + i*8 and repeats its first instruction to make WF_MAXI. The
+  // weights come packed: the tile's k-slice of its 432 weight rows is one
+  // contiguous 27 KB run already in LDS order, so each W instruction reads
+  // 1 KB of whole cache lines (a row-major slice would fetch 64 bytes from
+  // each of 16 rows, half lines, which the L2 serves at about two thirds of
+  // the whole-line rate when every CU streams).
+  const int KT = p.D / 32;  // multiple of 4, >= 8 (host check)
   const char* const a_base = reinterpret_cast<const char*>(p.X);
-  const char* const w_base = reinterpret_cast<const char*>(p.W);
+  const char* const w_base = reinterpret_cast<const char*>(p.Wpk) + (size_t)hp * KT * WF_PK_SLICE;
   bool is_a[WF_MAXI];
   uint32_t voff[WF_MAXI];
   int dst[WF_MAXI];
@@ -191,17 +198,13 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
       voff[i] = (uint32_t)gr * (uint32_t)(p.D * 2) + (uint32_t)((pp ^ ((row >> 1) & 3)) * 16);
       dst[i] = j * 64;
     } else {
-      const int sl = (j - WF_IA) * 64 + lane, row = sl >> 2, pp = sl & 3;
-      const int tg = row / WF_CPH, cc = row - tg * WF_CPH;  // tile column groups: V, Q, K
-      const int gq = tg == 0 ? 2 : tg - 1;                    // row group of w_qkv
-      const int wrow = gq * p.D + hp * WF_CPH + cc;
-      voff[i] = (uint32_t)wrow * (uint32_t)(p.D * 2) + (uint32_t)((pp ^ ((row >> 1) & 3)) * 16);
+      voff[i] = (uint32_t)((j - WF_IA) * 1024 + lane * 16);
       dst[i] = WF_SA + (j - WF_IA) * 64;
     }
   }
   auto issue = [&](int kt, uint4* st) {
     const char* const ak = a_base + kt * 64;
-    const char* const wk = w_base + kt * 64;
+    const char* const wk = w_base + kt * WF_PK_SLICE;
 #pragma unroll
     for (int i = 0; i < WF_MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
   };
@@ -268,7 +271,6 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int KT = p.D / 32;  // multiple of 4, >= 8 (host check)
   // the whole main loop is instantiated once per transposed-block count, so
   // the choice is one uniform branch outside it
   auto main_loop = [&](auto nswI) {
@@ -522,6 +524,35 @@ __global__ void __launch_bounds__(512, 1) wfused_kernel(WFusedParams p) {
   }  // tiles
 }
 
+// w_qkv -> the DMA order of the tiles' weight slices. Chunk s of the run of
+// head pair hp and k-slice kt holds what the row-major plan would have placed
+// at the tile's LDS position s: weight row wrow of tile row s >> 2 (tile rows:
+// V's 144 columns of the pair, then Q's, then K's), 16-byte chunk
+// (s & 3) ^ (((s >> 2) >> 1) & 3) of the k-slice (the DmaA<bf16> swizzle).
+// One workgroup per (k-slice, head pair), k-slice fastest, so the two halves
+// of each 128-byte weight line are read by neighbouring workgroups.
+__global__ void __launch_bounds__(256) wfused_pack_kernel(const uint16_t* __restrict__ W, uint4* __restrict__ Wpk,
+                                                          int D) {
+  const int kt = blockIdx.x, hp = blockIdx.y, KT = gridDim.x;
+  uint4* dst = Wpk + ((size_t)hp * KT + kt) * WF_SB;
+  for (int s = threadIdx.x; s < WF_SB; s += 256) {
+    const int row = s >> 2, pp = s & 3;
+    const int tg = row / WF_CPH, cc = row - tg * WF_CPH;  // tile column groups: V, Q, K
+    const int gq = tg == 0 ? 2 : tg - 1;                    // row group of w_qkv
+    const int wrow = gq * D + hp * WF_CPH + cc;
+    dst[s] = *reinterpret_cast<const uint4*>(W + (size_t)wrow * D + kt * 32 + (pp ^ ((row >> 1) & 3)) * 8);
+  }
+}
+
+size_t wfused_packed_bytes(int D) { return (size_t)(D / WF_CPH) * (size_t)(D / 32) * WF_PK_SLICE; }
+
+hipError_t launch_wfused_pack(const WFusedDesc& d, hipStream_t s) {
+  if (!wfused_supported(d) || !d.w_packed) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wfused_pack_kernel, dim3((unsigned)(d.D / 32), (unsigned)(d.heads / 2)), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(d.w_qkv), reinterpret_cast<uint4*>(d.w_packed), d.D);
+  return hipGetLastError();
+}
+
 bool wfused_supported(const WFusedDesc& d) {
   const int L = d.wt * d.wh * d.ww;
   if (L != 32 && L != 64 && L != 128) return false;
@@ -561,11 +592,11 @@ static hipError_t run_wfused(const WFusedParams& p, hipStream_t s) {
 }
 
 hipError_t launch_wfused(const WFusedDesc& d, hipStream_t s) {
-  if (!wfused_supported(d)) return hipErrorInvalidValue;
+  if (!wfused_supported(d) || !d.w_packed) return hipErrorInvalidValue;
   if (d.B == 0) return hipSuccess;
   WFusedParams p;
   p.X = reinterpret_cast<const uint16_t*>(d.X);
-  p.W = reinterpret_cast<const uint16_t*>(d.w_qkv);
+  p.Wpk = reinterpret_cast<const uint16_t*>(d.w_packed);
   p.bias = reinterpret_cast<const uint16_t*>(d.b_qkv);
   p.O = reinterpret_cast<uint16_t*>(d.O);
   p.QKV = reinterpret_cast<uint16_t*>(d.qkv_out);

@@ -244,6 +244,11 @@ ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_
  *   x, out   [B][N][D];  x_lowp, out_lowp: optional bf16 copies (see above)
  * Requires a window of 1 to 128 tokens (win.t*win.h*win.w <= 128, else
  * PTDIT_ERR_SHAPE); any such window is accepted.
+ *   ws       ptdit_workspace_bytes(PTDIT_OP_WINDOW_SA, g, 0, win, prec) bytes:
+ *            Q/K/V [B][3][heads][N][dh] and the attention output [B][N][D]
+ *            (prec, each at a 256-byte boundary), then, for bf16, 3 D^2 bf16
+ *            of scratch where the fused path packs w_qkv in its kernel's
+ *            load order at every call (nothing is cached between calls).
  */
 ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                              ptdit_win3 win, const ptdit_attn_w* w, int32_t add_residual,

@@ -50,7 +50,8 @@ def test_workspace_bytes(lib):
     from diffusion_transformer_attention_pt_amd._lib import Grid, Win3, OP_WINDOW_SA, OP_PROXY_XATTN, OP_PROXY_SA
     g = Grid(1, 1, 128, 128, 1152, 16)
     n = lib.ptdit_workspace_bytes(OP_WINDOW_SA, g, 0, Win3(1, 8, 8), 0)
-    assert n == 4 * 16384 * 1152 * 2
+    assert n == 4 * 16384 * 1152 * 2 + 3 * 1152 * 1152 * 2   # Q/K/V, O, packed w_qkv (bf16)
+    assert lib.ptdit_workspace_bytes(OP_WINDOW_SA, g, 0, Win3(1, 8, 8), 1) == 4 * 16384 * 1152 * 4
     n = lib.ptdit_workspace_bytes(OP_PROXY_XATTN, g, 256, Win3(1, 1, 1), 1)
     assert n == (2 * 16384 * 1152 + 2 * 256 * 1152) * 4
     n = lib.ptdit_workspace_bytes(OP_PROXY_SA, Grid(2, 1, 1, 256, 1152, 16), 256, Win3(1, 1, 1), 0)
