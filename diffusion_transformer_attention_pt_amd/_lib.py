@@ -35,7 +35,8 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_linear_heads", "ptdit_window_attn", "ptdit_attn", "ptdit_attn_workspace_bytes",
             "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
             "ptdit_calibrate_read", "ptdit_calibrate_copy", "ptdit_linear_bwd_ex",
-            "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep", "ptdit_attn_bwd_tokens"]
+            "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep", "ptdit_attn_bwd_tokens",
+            "ptdit_window_packed_bytes", "ptdit_pack_window_weights"]
 
 
 class Grid(ctypes.Structure):
@@ -49,7 +50,7 @@ class Win3(ctypes.Structure):
 
 class AttnW(ctypes.Structure):
     _fields_ = [("w_qkv", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p),
-                ("w_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p)]
+                ("w_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p), ("w_qkv_packed", ctypes.c_void_p)]
 
 
 class MlpW(ctypes.Structure):
@@ -114,6 +115,8 @@ def load() -> ctypes.CDLL:
         "ptdit_calibrate_mfma": [i32, i32, vp, ctypes.POINTER(ctypes.c_int64), vp],
         "ptdit_calibrate_read": [vp, i64, i32, vp, vp],
         "ptdit_calibrate_copy": [vp, vp, i64, vp],
+        "ptdit_window_packed_bytes": [i32, i32],
+        "ptdit_pack_window_weights": [vp, i32, i32, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -123,6 +126,7 @@ def load() -> ctypes.CDLL:
     lib.ptdit_attn_bwd_workspace_bytes.restype = sz
     lib.ptdit_linear_bwd_workspace_bytes.restype = sz
     lib.ptdit_attn_workspace_bytes.restype = sz
+    lib.ptdit_window_packed_bytes.restype = sz
     lib.ptdit_status_str.restype = ctypes.c_char_p
     lib.ptdit_version.restype = ctypes.c_char_p
     lib.ptdit_trace_disable.restype = None
@@ -192,6 +196,9 @@ class AttnWeights:
     b_qkv: Optional[torch.Tensor]
     w_o: torch.Tensor
     b_o: Optional[torch.Tensor]
+    # optional: w_qkv packed for the window calls' fused kernel
+    # (pack_window_weights); must be repacked whenever w_qkv changes
+    w_qkv_packed: Optional[torch.Tensor] = None
 
     @staticmethod
     def from_dict(w: dict, dtype: torch.dtype, device) -> "AttnWeights":
@@ -207,7 +214,7 @@ class AttnWeights:
         return self.w_qkv.dtype
 
     def c(self) -> AttnW:
-        return AttnW(_ptr(self.w_qkv), _ptr(self.b_qkv), _ptr(self.w_o), _ptr(self.b_o))
+        return AttnW(_ptr(self.w_qkv), _ptr(self.b_qkv), _ptr(self.w_o), _ptr(self.b_o), _ptr(self.w_qkv_packed))
 
 
 @dataclass
@@ -388,6 +395,22 @@ def proxy_xattn(x: torch.Tensor, grid: Sequence[int], P2: torch.Tensor, w: AttnW
                                ctypes.byref(cw), int(residual), _ptr(out), _ptr(out_lowp), _dt(out.dtype),
                                _ptr(ws), ws.numel(), _dt(w.dtype), _stream())
     _check("ptdit_proxy_xattn", st)
+    return out
+
+
+def pack_window_weights(w: AttnWeights, heads: int) -> Optional[torch.Tensor]:
+    """w_qkv packed in the window calls' fused-kernel load order
+    (ptdit_pack_window_weights), or None where that kernel does not apply
+    (fp32 weights, head width other than 72, ...). Attach the result as
+    w.w_qkv_packed so the window calls skip their per-call packing."""
+    lib = load()
+    D = w.w_qkv.shape[1]
+    nb = int(lib.ptdit_window_packed_bytes(D, heads)) if w.dtype == torch.bfloat16 else 0
+    if nb == 0:
+        return None
+    out = torch.empty(nb // 2, dtype=torch.bfloat16, device=w.w_qkv.device)
+    st = lib.ptdit_pack_window_weights(_ptr(w.w_qkv), D, heads, _ptr(out), _stream())
+    _check("ptdit_pack_window_weights", st)
     return out
 
 

@@ -58,6 +58,10 @@ class PTBlockAttention:
         self.M = (self.F // p[0]) * (self.H // p[1]) * (self.W // p[2])
         self.g = (B, self.F, self.H, self.W, D, heads)
         self.weights = [AttnWeights.from_dict(w, prec, self.device) for w in weights]
+        # the window attentions' w_qkv packed once for their fused kernel, so
+        # a forward launches no packing (weights are fixed for the block's life)
+        for w in self.weights[2:4]:
+            w.w_qkv_packed = _lib.pack_window_weights(w, heads)
         stream_dt = torch.float32
         self.P = torch.empty(B, self.M, D, dtype=stream_dt, device=self.device)
         self.P2 = torch.empty_like(self.P)

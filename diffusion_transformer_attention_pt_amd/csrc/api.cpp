@@ -90,7 +90,8 @@ ptdit_status check_io_dtypes(ptdit_dtype prec, ptdit_dtype in_dt, ptdit_dtype ou
 
 ptdit_status check_weights(const ptdit_attn_w* w) {
   if (!w || !w->w_qkv || !w->w_o) return PTDIT_ERR_NULL;
-  if (!aligned16(w->w_qkv) || !aligned16(w->w_o) || !aligned16(w->b_qkv) || !aligned16(w->b_o))
+  if (!aligned16(w->w_qkv) || !aligned16(w->w_o) || !aligned16(w->b_qkv) || !aligned16(w->b_o) ||
+      !aligned16(w->w_qkv_packed))
     return PTDIT_ERR_ALIGN;
   return PTDIT_OK;
 }
@@ -185,8 +186,12 @@ ptdit_status window_common(const void* x, const void* x_lowp, ptdit_dtype x_dt, 
   fd.Wp = (g.W + win.w - 1) / win.w * win.w;
   fd.scale = 1.0f / std::sqrt((float)fd.dh);
   if (prec == PTDIT_BF16 && xa && wfused_supported(fd)) {
-    e = launch_wfused_pack(fd, stream);
-    if (e != hipSuccess) return PTDIT_ERR_HIP;
+    if (w->w_qkv_packed) {
+      fd.w_packed = const_cast<void*>(w->w_qkv_packed);  // read only
+    } else {
+      e = launch_wfused_pack(fd, stream);
+      if (e != hipSuccess) return PTDIT_ERR_HIP;
+    }
     {
       TraceScope ts(PTDIT_K_WINDOW_FUSED, stream);
       e = launch_wfused(fd, stream);
@@ -531,6 +536,34 @@ ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_
   e = gemm(prec, o, prec, rows, D, D, w->w_o, w->b_o, add_residual ? x : nullptr, x_dt, out, out_dt,
            false, N, heads, D, PTDIT_K_GEMM_OUT, stream, out_lowp);
   return hip_status(e);
+}
+
+// the fused kernel's weight layout for (D, heads): the descriptor fields the
+// packing and wfused_supported read (one 64-token window, one token)
+static WFusedDesc pack_desc(int32_t D, int32_t heads) {
+  WFusedDesc fd{};
+  fd.B = 1; fd.F = 1; fd.H = 8; fd.W = 8; fd.D = D; fd.heads = heads; fd.dh = heads > 0 ? D / heads : 0;
+  fd.wt = 1; fd.wh = 8; fd.ww = 8;
+  fd.Fp = 1; fd.Hp = 8; fd.Wp = 8;
+  return fd;
+}
+
+size_t ptdit_window_packed_bytes(int32_t D, int32_t heads) {
+  if (D <= 0 || heads <= 0 || D % heads) return 0;
+  return wfused_supported(pack_desc(D, heads)) ? wfused_packed_bytes(D) : 0;
+}
+
+ptdit_status ptdit_pack_window_weights(const void* w_qkv, int32_t D, int32_t heads, void* packed,
+                                       hipStream_t stream) {
+  if (!w_qkv || !packed) return PTDIT_ERR_NULL;
+  if (!aligned16(w_qkv) || !aligned16(packed)) return PTDIT_ERR_ALIGN;
+  const size_t nb = ptdit_window_packed_bytes(D, heads);
+  if (nb == 0) return PTDIT_ERR_SHAPE;
+  if (overlaps(packed, nb, w_qkv, (size_t)3 * D * D * 2)) return PTDIT_ERR_ALIAS;
+  WFusedDesc fd = pack_desc(D, heads);
+  fd.w_qkv = w_qkv;
+  fd.w_packed = packed;
+  return hip_status(launch_wfused_pack(fd, stream));
 }
 
 ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,

@@ -90,12 +90,19 @@ typedef struct { int32_t B, F, H, W, D, heads; } ptdit_grid;
 /* A 3D extent (proxy window, TCM window or shift) along (t, h, w). */
 typedef struct { int32_t t, h, w; } ptdit_win3;
 
-/* Weights of one attention module (layout in the header comment). */
+/* Weights of one attention module (layout in the header comment).
+ * w_qkv_packed is optional (NULL: none): a copy of w_qkv that
+ * ptdit_pack_window_weights wrote. The window calls (ptdit_window_sa,
+ * ptdit_shift_window_sa, ptdit_window_sa_keep) then read it instead of
+ * packing w_qkv into their workspace at every call; it must be the packing
+ * of this very w_qkv (not checked: repack after changing the weights). The
+ * other calls ignore it. */
 typedef struct {
   const void* w_qkv;
   const void* b_qkv;
   const void* w_o;
   const void* b_o;
+  const void* w_qkv_packed;
 } ptdit_attn_w;
 
 /* Operation codes for ptdit_workspace_bytes. */
@@ -248,12 +255,29 @@ ptdit_status ptdit_proxy_xattn(const void* x, const void* x_lowp, ptdit_dtype x_
  *            Q/K/V [B][3][heads][N][dh] and the attention output [B][N][D]
  *            (prec, each at a 256-byte boundary), then, for bf16, 3 D^2 bf16
  *            of scratch where the fused path packs w_qkv in its kernel's
- *            load order at every call (nothing is cached between calls).
+ *            load order when w->w_qkv_packed is NULL (nothing is cached
+ *            between calls; see ptdit_pack_window_weights).
  */
 ptdit_status ptdit_window_sa(const void* x, const void* x_lowp, ptdit_dtype x_dt, ptdit_grid g,
                              ptdit_win3 win, const ptdit_attn_w* w, int32_t add_residual,
                              void* out, void* out_lowp, ptdit_dtype out_dt,
                              void* ws, size_t ws_bytes, ptdit_dtype prec, hipStream_t stream);
+
+/*
+ * ptdit_pack_window_weights -- w_qkv [3D][D] (bf16) rewritten in the load
+ * order of the window calls' fused Q/K/V-projection + attention kernel (the
+ * module table's attn1, Eq. TCM): for each pair of heads and each 32-wide
+ * slice of the contraction, the pair's 432 Q/K/V weight rows as one
+ * contiguous run, so the kernel reads whole cache lines. The packed copy
+ * (ptdit_window_packed_bytes(D, heads) bytes, caller-owned, 16-byte
+ * aligned) goes into ptdit_attn_w.w_qkv_packed. PTDIT_ERR_SHAPE where the
+ * fused kernel does not apply (head width other than 72, an odd head count,
+ * D % 128 != 0); ptdit_window_packed_bytes then returns 0. Same values as
+ * the packing each window call does in its workspace when no copy is given.
+ */
+size_t ptdit_window_packed_bytes(int32_t D, int32_t heads);
+ptdit_status ptdit_pack_window_weights(const void* w_qkv, int32_t D, int32_t heads, void* packed,
+                                       hipStream_t stream);
 
 /*
  * ptdit_shift_window_sa -- SWSA of Eq. TCM (window_shift, window attention,

@@ -446,3 +446,25 @@ def test_keep_and_token_major_gradient_calls_validate_on_the_host(lib):
     assert call(1, 0) == -4                                         # bf16 dQ from fp32 inputs
     assert call(0, 0, dq_=ctypes.c_void_p((1 << 32) + 1024)) == -8  # dQ inside d_o
     assert call(0, 0, dq_=ctypes.c_void_p((1 << 34) + 8)) == -5     # misaligned
+
+
+def test_window_weight_packing_validates_on_the_host(lib):
+    """ptdit_window_packed_bytes / ptdit_pack_window_weights: the size is
+    3 D^2 bf16 where the fused kernel applies, 0 elsewhere; refusals before
+    any launch (null, misaligned, unsupported shape, packed copy over w_qkv);
+    a misaligned packed copy in ptdit_attn_w is refused by the window call."""
+    import ctypes
+    from diffusion_transformer_attention_pt_amd._lib import AttnW, Grid, Win3
+    assert lib.ptdit_window_packed_bytes(1152, 16) == 3 * 1152 * 1152 * 2
+    assert lib.ptdit_window_packed_bytes(2304, 32) == 3 * 2304 * 2304 * 2
+    for D, heads in ((1024, 16), (576, 8), (1152, 0), (0, 16), (1152, 15), (1152, 12)):
+        assert lib.ptdit_window_packed_bytes(D, heads) == 0, (D, heads)
+    fake, far = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 40)
+    assert lib.ptdit_pack_window_weights(None, 1152, 16, far, None) == -1
+    assert lib.ptdit_pack_window_weights(fake, 1152, 16, None, None) == -1
+    assert lib.ptdit_pack_window_weights(fake, 1152, 16, ctypes.c_void_p((1 << 40) + 8), None) == -5
+    assert lib.ptdit_pack_window_weights(fake, 1024, 16, far, None) == -2
+    assert lib.ptdit_pack_window_weights(fake, 1152, 16, ctypes.c_void_p((1 << 20) + 4096), None) == -8
+    w = AttnW(fake.value, None, fake.value, None, (1 << 40) + 8)
+    assert lib.ptdit_window_sa(fake, None, 0, Grid(1, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),
+                               1, far, None, 0, ctypes.c_void_p(1 << 44), 1 << 30, 0, None) == -5

@@ -103,6 +103,15 @@ def test_fused_window_calls(P, name):
         assert n == 1, f"fused kernel launches: {n}"
         ref = O.shift_window_sa(x, wl.grid, wl.win, sh, w, wl.heads, False)
         assert_close(host(got), ref, f"{'swsa' if shifted else 'wsa'} branch")
+        # with w_qkv packed once by ptdit_pack_window_weights (no per-call
+        # packing): the same bits
+        aw_p = P.AttnWeights(aw.w_qkv, aw.b_qkv, aw.w_o, aw.b_o, _lib.pack_window_weights(aw, wl.heads))
+        assert aw_p.w_qkv_packed is not None
+        got_p, n_p = _fused_launches(P, lambda: (P.shift_window_sa(xb, g, wl.win, sh, aw_p, residual=False,
+                                                                   out_dtype=F32) if shifted else
+                                                 P.window_sa(xb, g, wl.win, aw_p, residual=False, out_dtype=F32)))
+        assert n_p == 1
+        assert torch.equal(got_p, got), "prepacked weights changed the output"
         # the unfused path (fp32 input, no bf16 copy) gives the same bits
         x32 = dev(x, F32)
         plain, n0 = _fused_launches(P, lambda: call(x32, False))
@@ -145,3 +154,29 @@ def test_fused_not_taken_where_unsupported(P):
         assert n == 0
         assert_close(host(got), O.shift_window_sa(x, wl.grid, wl.win, wl.shift, w, wl.heads, False),
                      f"unfused {kw}")
+
+
+def test_packed_window_weights_layout(P):
+    """ptdit_pack_window_weights is a pure permutation of w_qkv, pinned here
+    by rebuilding it on the host: for head pair hp and k-slice kt, tile row r
+    (V's 144 rows of the pair, then Q's, then K's) and 16-byte position q,
+    the chunk (q ^ ((r >> 1) & 3)) of that weight row's k-slice."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    for D, heads in ((1152, 16), (2304, 32)):
+        announce(f"packed window weights D={D} heads={heads}")
+        g = torch.Generator().manual_seed(D)
+        w = (torch.randn(3 * D, D, generator=g) * 0.02).to(BF16)
+        aw = P.AttnWeights(w.cuda(), None, torch.zeros(D, D, dtype=BF16, device="cuda"), None)
+        got = _lib.pack_window_weights(aw, heads)
+        torch.cuda.synchronize()
+        hp_n, kt_n = heads // 2, D // 32
+        hp = np.arange(hp_n)[:, None, None, None, None]
+        kt = np.arange(kt_n)[None, :, None, None, None]
+        r = np.arange(432)[None, None, :, None, None]
+        q = np.arange(4)[None, None, None, :, None]
+        e = np.arange(8)[None, None, None, None, :]
+        tg, cc = r // 144, r % 144
+        wrow = np.where(tg == 0, 2, tg - 1) * D + hp * 144 + cc
+        col = kt * 32 + (q ^ ((r >> 1) & 3)) * 8 + e
+        ref = w.view(torch.int16).numpy()[wrow, col]
+        assert np.array_equal(got.view(torch.int16).cpu().numpy().reshape(ref.shape), ref)
