@@ -36,7 +36,8 @@ EXPORTED = ["ptdit_linear", "ptdit_mlp", "ptdit_proxy_pool", "ptdit_proxy_select
             "ptdit_heads_to_tokens", "ptdit_f32_to_bf16", "ptdit_add_f32", "ptdit_calibrate_mfma",
             "ptdit_calibrate_read", "ptdit_calibrate_copy", "ptdit_linear_bwd_ex",
             "ptdit_window_attn_bwd_tokens", "ptdit_window_sa_keep", "ptdit_attn_bwd_tokens",
-            "ptdit_window_packed_bytes", "ptdit_pack_window_weights"]
+            "ptdit_window_packed_bytes", "ptdit_pack_window_weights", "ptdit_linear_bwd_dw_group",
+            "ptdit_linear_bwd_dw_group_workspace_bytes"]
 
 
 class Grid(ctypes.Structure):
@@ -117,6 +118,9 @@ def load() -> ctypes.CDLL:
         "ptdit_calibrate_copy": [vp, vp, i64, vp],
         "ptdit_window_packed_bytes": [i32, i32],
         "ptdit_pack_window_weights": [vp, i32, i32, vp, vp],
+        "ptdit_linear_bwd_dw_group": [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, i32,
+                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp],
+        "ptdit_linear_bwd_dw_group_workspace_bytes": [i32, i64, i32, i32],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -127,6 +131,7 @@ def load() -> ctypes.CDLL:
     lib.ptdit_linear_bwd_workspace_bytes.restype = sz
     lib.ptdit_attn_workspace_bytes.restype = sz
     lib.ptdit_window_packed_bytes.restype = sz
+    lib.ptdit_linear_bwd_dw_group_workspace_bytes.restype = sz
     lib.ptdit_status_str.restype = ctypes.c_char_p
     lib.ptdit_version.restype = ctypes.c_char_p
     lib.ptdit_trace_disable.restype = None
@@ -681,6 +686,47 @@ def linear_bwd(x: torch.Tensor, w: torch.Tensor, d_y: torch.Tensor, want_dx: boo
                                      ws.numel() * ws.element_size(), _stream())
         _check("ptdit_linear_bwd_ex", st)
     return dx, dw, db
+
+
+MAX_DW_GROUP = 4   # PTDIT_MAX_DW_GROUP
+
+
+def linear_bwd_dw_group(xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor],
+                        dws: Optional[Sequence[torch.Tensor]] = None, dbs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                        want_db: bool = True, ws: Optional[torch.Tensor] = None):
+    """Weight (and bias) gradients of up to MAX_DW_GROUP projections of one
+    shape in one launch (ptdit_linear_bwd_dw_group): xs[i] [rows, d_in],
+    dys[i] [rows, d_out], bf16 token-major. Returns (dws, dbs), fp32: the
+    given tensors or new ones (dbs entries None without want_db)."""
+    lib = load()
+    n = len(xs)
+    if n < 1 or n > MAX_DW_GROUP or len(dys) != n:
+        raise ValueError(f"1..{MAX_DW_GROUP} products, as many dY as X")
+    d_in, d_out = xs[0].shape[-1], dys[0].shape[-1]
+    rows = xs[0].numel() // d_in
+    for x, dy in zip(xs, dys):
+        if x.dtype != torch.bfloat16 or dy.dtype != torch.bfloat16:
+            raise ValueError("X and dY are bf16")
+        _numel(x, rows * d_in, "x")
+        _numel(dy, rows * d_out, "d_y")
+    dev = xs[0].device
+    if dws is None:
+        dws = [torch.empty(d_out, d_in, dtype=torch.float32, device=dev) for _ in range(n)]
+    if dbs is None:
+        dbs = [torch.empty(d_out, dtype=torch.float32, device=dev) if want_db else None for _ in range(n)]
+    for t, cnt, name in [(t, d_out * d_in, "dw") for t in dws] + [(t, d_out, "db") for t in dbs]:
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be fp32")
+        _numel(t, cnt, name)
+    need = int(lib.ptdit_linear_bwd_dw_group_workspace_bytes(n, rows, d_in, d_out))
+    if need == 0:
+        raise ValueError("shape outside the grouped weight gradient (rows % 32, 256 <= rows, 1024 <= d_out <= 4096)")
+    ws = _ws(need, ws, dev)
+    arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+    st = lib.ptdit_linear_bwd_dw_group(n, arr(xs), arr(dys), rows, d_in, d_out, arr(dws), arr(dbs), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream())
+    _check("ptdit_linear_bwd_dw_group", st)
+    return dws, dbs
 
 
 def trace_enable(kernel_class: int, capacity: int) -> None:

@@ -43,7 +43,15 @@ from .block import PTBlockAttention
 
 
 class PTBlockBackward:
-    def __init__(self, blk: PTBlockAttention):
+    def __init__(self, blk: PTBlockAttention, group_dw: bool = True):
+        """group_dw: leave the weight and bias gradients of the four N-row
+        D x D maps (the three output projections of the token rows and the
+        cross-attention's query projection) to the end of the pass, where one
+        ptdit_linear_bwd_dw_group launch forms all four (fewer token splits
+        and partial sums than four calls); the chain then forms only their
+        d_x products. Where that call's shape rules do not hold (fewer than
+        256 or a count of tokens not a multiple of 32, D < 1024) the
+        gradients stay in the chain."""
         if blk.prec != torch.bfloat16:
             raise ValueError("the block backward runs on bf16 blocks (bf16 matrix-core gradient kernels)")
         if blk.proxy_mode != "mean" or blk.full:
@@ -77,14 +85,21 @@ class PTBlockBackward:
         self.dqkvp_t = e(B, M, 3 * D)
         self.dP = e(B, M, D)
         lib = _lib.load()
-        need = max(int(lib.ptdit_linear_bwd_workspace_bytes(B * N, D, 3 * D)),
+        gneed = int(lib.ptdit_linear_bwd_dw_group_workspace_bytes(4, B * N, D, D))
+        self.group = group_dw and gneed > 0
+        if self.group:
+            # operands kept for the deferred products: bf16(dout) (g16a is
+            # reused for dx1), and the recompute path's attention outputs
+            self.g16c = e(B, N, D, dt=bf)
+            self.o_w2, self.o_x = e(B, N, D, dt=bf), e(B, N, D, dt=bf)
+        need = max(gneed, int(lib.ptdit_linear_bwd_workspace_bytes(B * N, D, 3 * D)),
                    int(lib.ptdit_linear_bwd_workspace_bytes(B * M, D, 3 * D)),
                    int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, N, M, dh)),
                    int(lib.ptdit_attn_bwd_workspace_bytes(B, heads, M, M, dh)))
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def _window(self, xl: torch.Tensor, w: _lib.AttnWeights, shift, dy: torch.Tensor, dx_out: torch.Tensor,
-                kept=None, dy16=None, dx_out16=None):
+                kept=None, dy16=None, dx_out16=None, o_buf=None):
         """One window attention's backward: returns its weight gradients and
         writes dx_out = dy + d(branch)/dx^T dy (and its bf16 copy into
         dx_out16). kept: (qkv, o) of the forward; dy16: bf16(dy), which the
@@ -94,11 +109,18 @@ class PTBlockBackward:
         if kept is not None:
             qkv, o = kept
         else:
-            qkv, o = self.qkv, self.o
+            qkv, o = self.qkv, (o_buf if o_buf is not None else self.o)
             _lib.linear_heads(xl.view(B * N, D), w.w_qkv, w.b_qkv, B, N, heads, out=qkv)
             _lib.window_attn(qkv, w.b_qkv, blk.g, blk.win, shift, out=o)
-        _, dwo, dbo = _lib.linear_bwd(o, w.w_o, dy16 if dy16 is not None else dy, ws=self.ws, want_dx=False,
-                                      dx_bf16=self.do16)
+        dyo = dy16 if dy16 is not None else dy
+        if self.group:   # dW, db of w_o at the end of the pass
+            _lib.linear_bwd(o, w.w_o, dyo, ws=self.ws, want_dx=False, want_dw=False, want_db=False,
+                            dx_bf16=self.do16)
+            dwo = torch.empty(D, D, dtype=torch.float32, device=o.device)
+            dbo = torch.empty(D, dtype=torch.float32, device=o.device)
+            self._deferred.append((o, dyo, dwo, dbo))
+        else:
+            _, dwo, dbo = _lib.linear_bwd(o, w.w_o, dyo, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         if self.pads:
             self.dbkv.zero_()
         # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
@@ -124,27 +146,36 @@ class PTBlockBackward:
             raise ValueError("dout must be a contiguous fp32 tensor")
         grads: List[dict] = [None] * 4
         k = blk.kept
+        self._deferred = []   # (X, dY, dW, db) of the grouped D x D products
         # the output projections' gradient products take bf16(dY): dout's
         # rounded here, dx2's and dx1's written by the products that form them
-        _lib.f32_to_bf16(dout, out=self.g16a)
+        dout16 = self.g16c if self.group else self.g16a
+        _lib.f32_to_bf16(dout, out=dout16)
         grads[3] = self._window(blk.x2_lowp, w[3], blk.shift, dout, self.dx2,
-                                kept=(k["swsa_qkv"], k["swsa_o"]) if k else None, dy16=self.g16a,
+                                kept=(k["swsa_qkv"], k["swsa_o"]) if k else None, dy16=dout16,
                                 dx_out16=self.g16b)
         grads[2] = self._window(blk.x1_lowp, w[2], (0, 0, 0), self.dx2, self.dx1,
                                 kept=(k["wsa_qkv"], k["wsa_o"]) if k else None, dy16=self.g16b,
-                                dx_out16=self.g16a)
+                                dx_out16=self.g16a, o_buf=self.o_w2 if self.group else None)
         # cross-attention: tokens are queries, the attended proxies P' keys/values
         wc = w[1]
         if k:
             q, kv, o = k["x_q"], k["x_kv"], k["x_o"]
         else:
-            q, kv, o = self.q, self.kv, self.o
+            q, kv, o = self.q, self.kv, (self.o_x if self.group else self.o)
             _lib.linear_heads(x.view(B * N, D), wc.w_qkv[:D], wc.b_qkv[:D] if wc.b_qkv is not None else None,
                               B, N, heads, out=q)
             _lib.linear_heads(blk.P2.view(B * M, D), wc.w_qkv[D:], wc.b_qkv[D:] if wc.b_qkv is not None else None,
                               B, M, heads, out=kv)
             _lib.attn(q[:, 0], kv[:, 0], kv[:, 1], out=o)
-        _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.g16a, ws=self.ws, want_dx=False, dx_bf16=self.do16)
+        if self.group:
+            _lib.linear_bwd(o, wc.w_o, self.g16a, ws=self.ws, want_dx=False, want_dw=False, want_db=False,
+                            dx_bf16=self.do16)
+            dwo = torch.empty(D, D, dtype=torch.float32, device=x.device)
+            dbo = torch.empty(D, dtype=torch.float32, device=x.device)
+            self._deferred.append((o, self.g16a, dwo, dbo))
+        else:
+            _, dwo, dbo = _lib.linear_bwd(o, wc.w_o, self.g16a, ws=self.ws, want_dx=False, dx_bf16=self.do16)
         # dQ token-major bf16 [B, N, D] into the (now free) window gradient buffer
         dq_t = self.dqkv_t16.view(-1)[:B * N * D].view(B, N, D)
         _lib.attn_bwd(q[:, 0], kv[:, 0], kv[:, 1], self.do16, ws=self.ws,
@@ -152,7 +183,13 @@ class PTBlockBackward:
         dwqkv = torch.empty(3 * D, D, dtype=torch.float32, device=x.device)
         dbqkv = torch.empty(3 * D, dtype=torch.float32, device=x.device)
         # dx = dx1 (the residual) + the queries' gradient, joined in the product
-        _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dx=self.dx, dx_add=self.dx1, dw=dwqkv[:D], db=dbqkv[:D])
+        if self.group:
+            _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dx=self.dx, dx_add=self.dx1, want_dw=False,
+                            want_db=False)
+            self._deferred.append((x, dq_t, dwqkv[:D], dbqkv[:D]))
+        else:
+            _lib.linear_bwd(x, wc.w_qkv[:D], dq_t, ws=self.ws, dx=self.dx, dx_add=self.dx1, dw=dwqkv[:D],
+                            db=dbqkv[:D])
         _lib.heads_to_tokens(self.dkv_h, out=self.dkv_t)
         dP2, _, _ = _lib.linear_bwd(blk.P2, wc.w_qkv[D:], self.dkv_t, ws=self.ws, dw=dwqkv[D:], db=dbqkv[D:])
         grads[1] = {"w_qkv": dwqkv, "b_qkv": dbqkv, "w_o": dwo, "b_o": dbo}
@@ -173,4 +210,9 @@ class PTBlockBackward:
         grads[0] = {"w_qkv": dwqkv0, "b_qkv": dbqkv0, "w_o": dwo0, "b_o": dbo0}
         # window average: every token of a window receives dP / P
         _lib.proxy_pool_bwd(self.dP, blk.g, blk.p, d_x=self.dx, accumulate=True)
+        if self._deferred:   # the four D x D maps' dW, db in one launch
+            xs, dys, dws, dbs = (list(t) for t in zip(*self._deferred))
+            _lib.linear_bwd_dw_group([a.reshape(B * N, D) for a in xs], [a.reshape(B * N, D) for a in dys], dws,
+                                     dbs, ws=self.ws)
+            self._deferred = []
         return {"dx": self.dx, "weights": grads}

@@ -923,6 +923,62 @@ size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_ou
          align_up((size_t)rows * d_out * 2);
 }
 
+static_assert(PTDIT_MAX_DW_GROUP <= GEMM_MAX_GROUPS, "one launch holds every product");
+
+size_t ptdit_linear_bwd_dw_group_workspace_bytes(int32_t n, int64_t rows, int32_t d_in, int32_t d_out) {
+  if (n < 1 || n > PTDIT_MAX_DW_GROUP || rows <= 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8 ||
+      !wgrad_token_major(rows, d_in, d_out, 0, 0))
+    return 0;
+  return wgrad_group_ws_bytes(n, rows, d_in, d_out);
+}
+
+ptdit_status ptdit_linear_bwd_dw_group(int32_t n, const void* const* x, const void* const* d_y, int64_t rows,
+                                       int32_t d_in, int32_t d_out, float* const* d_w, float* const* d_b, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  if (n < 1 || n > PTDIT_MAX_DW_GROUP || rows < 0 || d_in <= 0 || d_out <= 0 || d_in % 8 || d_out % 8)
+    return PTDIT_ERR_SHAPE;
+  if (!x || !d_y || !d_w) return PTDIT_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!x[i] || !d_y[i] || !d_w[i]) return PTDIT_ERR_NULL;
+  if (rows == 0) return PTDIT_OK;
+  if (rows > (int64_t)65535 * 32 || !wgrad_token_major(rows, d_in, d_out, 0, 0)) return PTDIT_ERR_SHAPE;
+  const size_t need = wgrad_group_ws_bytes(n, rows, d_in, d_out);
+  if (!ws || ws_bytes < need) return PTDIT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return PTDIT_ERR_ALIGN;
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(x[i]) || !aligned16(d_y[i]) || !aligned16(d_w[i]) || (d_b && !aligned16(d_b[i])))
+      return PTDIT_ERR_ALIGN;
+  const size_t xb = (size_t)rows * d_in * 2, yb = (size_t)rows * d_out * 2;
+  const size_t wb = (size_t)d_out * d_in * 4, bb = (size_t)d_out * 4;
+  for (int i = 0; i < n; ++i) {
+    const void* outs[2] = {d_w[i], d_b ? d_b[i] : nullptr};
+    const size_t osz[2] = {wb, bb};
+    for (int o = 0; o < 2; ++o) {
+      if (!outs[o]) continue;
+      if (overlaps(outs[o], osz[o], ws, need)) return PTDIT_ERR_ALIAS;
+      for (int j = 0; j < n; ++j) {
+        if (overlaps(outs[o], osz[o], x[j], xb) || overlaps(outs[o], osz[o], d_y[j], yb)) return PTDIT_ERR_ALIAS;
+        if (j != i && (overlaps(outs[o], osz[o], d_w[j], wb) || (d_b && overlaps(outs[o], osz[o], d_b[j], bb))))
+          return PTDIT_ERR_ALIAS;
+      }
+    }
+    if (d_b && overlaps(d_w[i], wb, d_b[i], bb)) return PTDIT_ERR_ALIAS;
+    if (overlaps(ws, need, x[i], xb) || overlaps(ws, need, d_y[i], yb)) return PTDIT_ERR_ALIAS;
+  }
+  WgradGroupDesc d;
+  d.n = n;
+  for (int i = 0; i < n; ++i) {
+    d.dy[i] = d_y[i];
+    d.x[i] = x[i];
+    d.dw[i] = d_w[i];
+    d.db[i] = d_b ? d_b[i] : nullptr;
+  }
+  d.ws = ws;
+  d.rows = rows; d.d_in = d_in; d.d_out = d_out;
+  TraceScope ts(PTDIT_K_BWD_LINEAR, stream);
+  return hip_status(launch_wgrad_group(d, stream));
+}
+
 ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int32_t d_in, int32_t d_out,
                               const void* w, const void* d_y, ptdit_dtype dy_dt, float* d_x, float* d_w,
                               float* d_b, void* ws, size_t ws_bytes, hipStream_t stream) {

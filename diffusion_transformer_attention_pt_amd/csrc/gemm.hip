@@ -42,6 +42,12 @@ struct GemmParams {
   // that split that exist (0: all); the rows past them read as zero
   int k_last;
   int k_valid;
+  // token-major instance only: `groups` products of one shape whose A, W
+  // and Y bases are gA[g], gW[g], gY[g] (groups == 1: A, W, Y)
+  int groups;
+  const void* gA[GEMM_MAX_GROUPS];
+  const void* gW[GEMM_MAX_GROUPS];
+  void* gY[GEMM_MAX_GROUPS];
 };
 
 // XCD-aware tile order: hardware hands block i to XCD (i % 8); re-number so
@@ -745,7 +751,8 @@ gemm_dma_kernel(GemmParams p) {
 constexpr int pp_rblock(int k, int nb) { return k < 0 ? nb + k : (k < nb - 1 ? k : -1); }
 
 template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256, bool TOKMAJ = false>
-__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p_in) {
+  GemmParams p = p_in;
   constexpr bool RIN = RKT > 0;
   static_assert(!TOKMAJ || (!RIN && !HEADMAJOR && BM == 256), "token-major operands: the weight gradient only");
   static_assert(!RIN || (RKT == 36 && BM == 256), "one k-slice per accumulator block of a 64 x 144 wave tile");
@@ -783,10 +790,19 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
     // fastest, so the workgroups of an XCD share the dY slabs of their row
     // tiles and the X slabs of one split in its L2 (the row-major order of
     // the other kernels would spread a dY slab over four XCDs)
-    const int nt = tiles_m * tiles_n, total = nt * p.splits;
+    // groups of one shape: the order is (group, split, tm, tn), tn fastest
+    const int nt = tiles_m * tiles_n, per = nt * p.splits, total = per * p.groups;
     if ((int)blockIdx.x >= total) return;
     const int q = total >> 3, rem = total & 7, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-    const int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    if (p.groups > 1) {
+      const int gi = logical / per;
+      logical -= gi * per;
+      // read from the kernel argument (a uniform scalar load), not the copy
+      p.A = p_in.gA[gi];
+      p.W = reinterpret_cast<const uint16_t*>(p_in.gW[gi]);
+      p.Y = p_in.gY[gi];
+    }
     split = logical / nt;
     const int in = logical - split * nt;
     tm = in / tiles_n;
@@ -1227,6 +1243,12 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
   p.splits = d.splits > 0 ? d.splits : 1;
   p.k_last = d.k_last;
   p.k_valid = d.k_valid;
+  p.groups = 1;
+  for (int i = 0; i < GEMM_MAX_GROUPS; ++i) {
+    p.gA[i] = i < d.groups ? d.gA[i] : nullptr;
+    p.gW[i] = i < d.groups ? d.gW[i] : nullptr;
+    p.gY[i] = i < d.groups ? d.gY[i] : nullptr;
+  }
   if (d.tn) {
     // token-major bf16 operands (the weight gradient): the ping-pong kernel's
     // TN instance, 256 x 288 tiles, fp32 output, no bias / residual
@@ -1238,9 +1260,15 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
         p.lda * 64 * 32 >= ((int64_t)1 << 31) || p.ldw * 64 * 32 >= ((int64_t)1 << 31))
       return hipErrorInvalidValue;
     const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
-    // one-dimensional grid: the kernel maps it onto (split, row tile, column tile)
-    hipLaunchKernelGGL((gemm_pp_kernel<float, float, false, 0, 256, true>), dim3((unsigned)(tiles * p.splits)),
-                       dim3(512), 0, s, p);
+    if (d.groups > 1) {  // products of this shape at gA/gW/gY (A, W, Y unused)
+      if (d.groups > GEMM_MAX_GROUPS) return hipErrorInvalidValue;
+      for (int i = 0; i < d.groups; ++i)
+        if (!d.gA[i] || !d.gW[i] || !d.gY[i]) return hipErrorInvalidValue;
+      p.groups = d.groups;
+    }
+    // one-dimensional grid: the kernel maps it onto (group, split, row tile, column tile)
+    hipLaunchKernelGGL((gemm_pp_kernel<float, float, false, 0, 256, true>),
+                       dim3((unsigned)(tiles * p.splits * p.groups)), dim3(512), 0, s, p);
     return hipGetLastError();
   }
   if (d.a_f32) {

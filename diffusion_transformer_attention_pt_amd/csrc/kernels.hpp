@@ -10,6 +10,8 @@ namespace ptdit {
 // Y = A W^T + bias (+ R). A: [M][K], W: [N][K], bias: [N], R/Y: [M][N].
 // head_major: Y is instead written as [b][N/D groups][heads][Ntok][dh] with
 // row m = b*Ntok + tok and column n = g*D + h*dh + d (no residual then).
+constexpr int GEMM_MAX_GROUPS = 4;
+
 struct GemmDesc {
   const void* A; int a_f32;
   const void* W; const void* bias;
@@ -29,6 +31,12 @@ struct GemmDesc {
   // gradient dY^T X); k_last: K of the last split when it differs (0: K);
   // k_valid: the tokens of the last split that exist (0: all of its K)
   int tn = 0, k_last = 0, k_valid = 0;
+  // token-major only: groups > 1 products of this shape, operands and
+  // outputs at gA[g], gW[g], gY[g] (A, W, Y are then not read)
+  int groups = 1;
+  const void* gA[GEMM_MAX_GROUPS] = {};
+  const void* gW[GEMM_MAX_GROUPS] = {};
+  void* gY[GEMM_MAX_GROUPS] = {};
 };
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s);  // W, bias bf16
 hipError_t launch_gemm_f32(const GemmDesc& d, hipStream_t s);   // everything fp32
@@ -164,7 +172,22 @@ struct WgradDesc {
   int64_t rows;
   int d_in, d_out;
 };
-void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch);
+void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch, int groups = 1);
+// dW (and db) of n <= GEMM_MAX_GROUPS products of one shape, token-major bf16
+// dY and X (wgrad_token_major), in one GEMM launch split over the tokens for
+// all of them, then per product the column sums and the split-order reduction
+struct WgradGroupDesc {
+  int n;
+  const void* dy[GEMM_MAX_GROUPS];  // bf16 [rows][d_out]
+  const void* x[GEMM_MAX_GROUPS];   // bf16 [rows][d_in]
+  float* dw[GEMM_MAX_GROUPS];       // [d_out][d_in]
+  float* db[GEMM_MAX_GROUPS];       // [d_out] or null
+  void* ws;                         // wgrad_group_ws_bytes
+  int64_t rows;
+  int d_in, d_out;
+};
+size_t wgrad_group_ws_bytes(int n, int64_t rows, int d_in, int d_out);
+hipError_t launch_wgrad_group(const WgradGroupDesc& d, hipStream_t s);
 int colsum_splits(int64_t rows);
 // dW from token-major bf16 dY and X directly (no transposed copies)
 bool wgrad_token_major(int64_t rows, int d_in, int d_out, int dy_f32, int x_f32);

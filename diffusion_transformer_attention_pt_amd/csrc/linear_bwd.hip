@@ -183,11 +183,12 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
 // ----------------------------------------------------------------------------
 int colsum_splits(int64_t rows) { return (int)((rows + CS_ROWS - 1) / CS_ROWS); }
 
-void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch) {
+void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch, int groups) {
   // the DMA GEMM's tile for M = d_out rows of dW: 256 x 288 from 1024 rows,
-  // 32 x 64 below; about one workgroup per CU in total
-  const int64_t tiles = d_out >= 1024 ? (int64_t)((d_out + 255) / 256) * ((d_in + 287) / 288)
-                                      : (int64_t)((d_out + 31) / 32) * ((d_in + 63) / 64);
+  // 32 x 64 below; about one workgroup per CU in total, over all `groups`
+  // products of this shape that one launch computes
+  const int64_t tiles = (int64_t)groups * (d_out >= 1024 ? (int64_t)((d_out + 255) / 256) * ((d_in + 287) / 288)
+                                                         : (int64_t)((d_out + 31) / 32) * ((d_in + 63) / 64));
   int64_t sp = 256 / tiles;
   if (sp < 1) sp = 1;
   tch = (rows + sp - 1) / sp;
@@ -232,6 +233,77 @@ bool wgrad_token_major(int64_t rows, int d_in, int d_out, int dy_f32, int x_f32)
   return !dy_f32 && !x_f32 && d_out >= 1024 && d_out <= 4096 && d_in <= 4096 && rows % 32 == 0 && rows >= 256;
 }
 
+// whole splits of tch tokens, the remainder joined to the last one when it is
+// shorter than the kernel's 256-token minimum; the last split's K is rounded
+// up to 128 tokens, the rows past its kv real ones read as zero
+static void wgrad_tn_splits(int64_t rows, int64_t tch, int& sp, int64_t& kv, int64_t& kl) {
+  sp = (int)((rows + tch - 1) / tch);
+  kv = rows - (int64_t)(sp - 1) * tch;
+  if (kv < 256 && sp > 1) {
+    --sp;
+    kv += tch;
+  }
+  kl = (kv + 127) / 128 * 128 < 256 ? 256 : (kv + 127) / 128 * 128;
+}
+
+size_t wgrad_group_ws_bytes(int n, int64_t rows, int d_in, int d_out) {
+  int splits, sp;
+  int64_t tch, kv, kl;
+  wgrad_plan(rows, d_in, d_out, splits, tch, n);
+  wgrad_tn_splits(rows, tch, sp, kv, kl);
+  const size_t a = 255;
+  const size_t pb = ((size_t)sp * d_out * d_in * 4 + a) & ~a, cb = ((size_t)colsum_splits(rows) * d_out * 4 + a) & ~a;
+  return (size_t)n * (pb + cb);
+}
+
+hipError_t launch_wgrad_group(const WgradGroupDesc& d, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  if (d.n < 1 || d.n > GEMM_MAX_GROUPS || !wgrad_token_major(d.rows, d.d_in, d.d_out, 0, 0))
+    return hipErrorInvalidValue;
+  int splits, sp;
+  int64_t tch, kv, kl;
+  wgrad_plan(d.rows, d.d_in, d.d_out, splits, tch, d.n);
+  wgrad_tn_splits(d.rows, tch, sp, kv, kl);
+  const int64_t nw = (int64_t)d.d_out * d.d_in;
+  const int csplits = colsum_splits(d.rows);
+  const size_t a = 255;
+  const size_t pb = ((size_t)sp * nw * 4 + a) & ~a, cb = ((size_t)csplits * d.d_out * 4 + a) & ~a;
+  char* const ws = reinterpret_cast<char*>(d.ws);
+  auto part = [&](int i) { return reinterpret_cast<float*>(ws + (size_t)i * pb); };
+  auto dbp = [&](int i) { return reinterpret_cast<float*>(ws + (size_t)d.n * pb + (size_t)i * cb); };
+  // one launch: the n products' splits, (group, split, row tile, column tile)
+  GemmDesc g;
+  g.A = d.dy[0]; g.a_f32 = 0;
+  g.W = d.x[0]; g.bias = nullptr;
+  g.R = nullptr; g.r_f32 = 1;
+  g.Y = part(0); g.y_f32 = 1;
+  g.Y2 = nullptr;
+  g.M = d.d_out; g.N = d.d_in; g.K = sp == 1 ? (int)kl : (int)tch;
+  g.head_major = 0; g.Ntok = d.d_out; g.heads = 0; g.dh = 0; g.D = d.d_in;
+  g.lda = d.d_out; g.ldw = d.d_in; g.ks_a = tch; g.ks_w = tch; g.ks_y = nw; g.splits = sp;
+  g.tn = 1; g.k_last = (int)kl; g.k_valid = (int)kv;
+  g.groups = d.n;
+  for (int i = 0; i < d.n; ++i) {
+    g.gA[i] = d.dy[i];
+    g.gW[i] = d.x[i];
+    g.gY[i] = part(i);
+  }
+  hipError_t e = launch_gemm_bf16(g, s);
+  if (e != hipSuccess) return e;
+  const int64_t n4 = nw > d.d_out ? nw : d.d_out;
+  for (int i = 0; i < d.n; ++i) {
+    if (d.db[i]) {
+      hipLaunchKernelGGL((colsum_kernel<uint16_t>), dim3((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits), dim3(LB_NT), 0,
+                         s, reinterpret_cast<const uint16_t*>(d.dy[i]), dbp(i), d.rows, d.d_out);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n4 / 4 + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s,
+                       part(i), dbp(i), d.dw[i], d.db[i], sp, csplits, nw, d.d_out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
   int splits;
@@ -240,16 +312,9 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   const int64_t ld = splits * tch, nw = (int64_t)d.d_out * d.d_in;
   const bool tn = wgrad_token_major(d.rows, d.d_in, d.d_out, d.dy_f32, d.x_f32);
   if (d.dw && tn) {
-    // whole splits of tch tokens, the remainder joined to the last one when it
-    // is shorter than the kernel's 256-token minimum; the last split's K is
-    // rounded up to 128 tokens, the rows past its kv real ones read as zero
-    int sp = (int)((d.rows + tch - 1) / tch);
-    int64_t kv = d.rows - (int64_t)(sp - 1) * tch;
-    if (kv < 256 && sp > 1) {
-      --sp;
-      kv += tch;
-    }
-    const int64_t kl = (kv + 127) / 128 * 128 < 256 ? 256 : (kv + 127) / 128 * 128;
+    int sp;
+    int64_t kv, kl;
+    wgrad_tn_splits(d.rows, tch, sp, kv, kl);
     GemmDesc g;
     g.A = d.dy; g.a_f32 = 0;
     g.W = d.x; g.bias = nullptr;

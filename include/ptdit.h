@@ -445,6 +445,32 @@ ptdit_status ptdit_linear_bwd(const void* x, ptdit_dtype x_dt, int64_t rows, int
 size_t ptdit_linear_bwd_workspace_bytes(int64_t rows, int32_t d_in, int32_t d_out);
 
 /*
+ * ptdit_linear_bwd_dw_group -- the weight and bias gradients of n (1 to
+ * PTDIT_MAX_DW_GROUP) projections of one shape (module table: the Q/K/V/O
+ * maps; training at 2048^2, section 4), dW_i = dY_i^T X_i, db_i = sum of
+ * the rows of dY_i, in one GEMM launch whose token splits cover all n
+ * products, so each product needs fewer splits (and partial sums) than a
+ * ptdit_linear_bwd call of its own; the splits of each product are summed in
+ * split order (deterministic). For the gradients a backward pass can leave
+ * to its end, as the block backward does with its four D x D maps.
+ *   x, d_y  host arrays of n device pointers: X_i [rows][d_in], dY_i
+ *           [rows][d_out], bf16, token-major (row r = token r)
+ *   d_w     host array of n device pointers, fp32 [d_out][d_in] each
+ *   d_b     NULL, or a host array of n device pointers (fp32 [d_out], an
+ *           entry may be NULL: that db is not formed)
+ *   ws      ptdit_linear_bwd_dw_group_workspace_bytes(n, rows, d_in, d_out)
+ * Requires rows % 32 == 0, 256 <= rows <= 65535*32, 1024 <= d_out <= 4096,
+ * d_in <= 4096, both multiples of 8 (else PTDIT_ERR_SHAPE; the workspace
+ * size is then 0); outputs overlapping an input, the workspace or another
+ * output: PTDIT_ERR_ALIAS.
+ */
+#define PTDIT_MAX_DW_GROUP 4
+size_t ptdit_linear_bwd_dw_group_workspace_bytes(int32_t n, int64_t rows, int32_t d_in, int32_t d_out);
+ptdit_status ptdit_linear_bwd_dw_group(int32_t n, const void* const* x, const void* const* d_y, int64_t rows,
+                                       int32_t d_in, int32_t d_out, float* const* d_w, float* const* d_b, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/*
  * ptdit_linear_bwd_ex -- ptdit_linear_bwd with the two steps that join a
  * projection's input gradient into a block's backward folded into the d_x
  * product (the residual branches of Eq. GIIM / Eq. TCM: x_out = x_in +

@@ -468,3 +468,30 @@ def test_window_weight_packing_validates_on_the_host(lib):
     w = AttnW(fake.value, None, fake.value, None, (1 << 40) + 8)
     assert lib.ptdit_window_sa(fake, None, 0, Grid(1, 1, 16, 16, 1152, 16), Win3(1, 8, 8), ctypes.byref(w),
                                1, far, None, 0, ctypes.c_void_p(1 << 44), 1 << 30, 0, None) == -5
+
+
+def test_grouped_weight_gradient_validates_on_the_host(lib):
+    """ptdit_linear_bwd_dw_group refusals before any launch, and its
+    workspace size (0 outside the shape rules)."""
+    import ctypes
+    vp = ctypes.c_void_p
+    assert lib.ptdit_linear_bwd_dw_group_workspace_bytes(4, 16384, 1152, 1152) > 0
+    for n, rows, di, do in ((0, 16384, 1152, 1152), (5, 16384, 1152, 1152), (2, 16400, 1152, 1152),
+                            (2, 128, 1152, 1152), (2, 16384, 1152, 512), (2, 16384, 8192, 1152)):
+        assert lib.ptdit_linear_bwd_dw_group_workspace_bytes(n, rows, di, do) == 0, (n, rows, di, do)
+    base = 1 << 32
+    arr = lambda *p: (vp * len(p))(*p)
+    x, dy, dw = arr(base, base + (1 << 28)), arr(base + (2 << 28), base + (3 << 28)), arr(1 << 40, (1 << 40) + (1 << 24))
+    ws, need = vp(1 << 44), lib.ptdit_linear_bwd_dw_group_workspace_bytes(2, 16384, 1152, 1152)
+    call = lambda n=2, x_=x, dy_=dy, dw_=dw, db_=None, rows=16384, ws_=ws, nb=need: \
+        lib.ptdit_linear_bwd_dw_group(n, x_, dy_, rows, 1152, 1152, dw_, db_, ws_, nb, None)
+    assert call(n=5) == -2
+    assert call(x_=None) == -1
+    assert call(dw_=arr(1 << 40, None)) == -1
+    assert call(rows=16400) == -2                      # not a multiple of 32
+    assert call(nb=need - 1) == -6
+    assert call(ws_=vp((1 << 44) + 4)) == -5
+    assert call(dw_=arr(1 << 40, (1 << 40) + 8)) == -5  # misaligned second output
+    assert call(dw_=arr(1 << 40, (1 << 40) + 4096)) == -8  # the outputs overlap
+    assert call(dw_=arr(base + 64, 1 << 42)) == -8     # an output inside X_0
+    assert call(rows=0) == 0

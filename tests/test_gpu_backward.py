@@ -472,3 +472,30 @@ def test_linear_bwd_vs_oracle(P, case):
     assert_grad_close(host(dx), rx, "dX")
     assert_grad_close(host(dw), rw, "dW")
     assert_grad_close(host(db), rb, "db")
+
+
+@pytest.mark.parametrize("rows,d_in,d_out,n", [(16384, 1152, 1152, 4), (21600, 1152, 1152, 3),
+                                               (4096, 1152, 3456, 2), (2400, 1152, 1152, 1)])
+def test_linear_bwd_dw_group(P, rows, d_in, d_out, n):
+    """ptdit_linear_bwd_dw_group: each product's dW against the float64
+    oracle (gradient bar) and against its own ptdit_linear_bwd call (the same
+    bf16 products summed in fp32 over other token splits: within fp32
+    rounding); db bit for bit (the same column sums and split order)."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    announce(f"grouped dW rows={rows} {d_in}->{d_out} n={n}")
+    g = np.random.Generator(np.random.PCG64(900 + n + rows % 97))
+    xs = [round_bf16(g.standard_normal((rows, d_in)).astype(np.float32)) for _ in range(n)]
+    dys = [round_bf16(g.standard_normal((rows, d_out)).astype(np.float32)) for _ in range(n)]
+    w = dev(round_bf16(g.standard_normal((d_out, d_in)).astype(np.float32) * 0.02), BF16)
+    xd, dyd = [dev(a, BF16) for a in xs], [dev(a, BF16) for a in dys]
+    dws, dbs = _lib.linear_bwd_dw_group(xd, dyd)
+    torch.cuda.synchronize()
+    for i in range(n):
+        _, dw1, db1 = _lib.linear_bwd(xd[i], w, dyd[i], want_dx=False)
+        torch.cuda.synchronize()
+        got, one = host(dws[i]), host(dw1)
+        assert np.abs(got - one).max() <= 2e-6 * max(1.0, float(np.abs(one).max())) * np.sqrt(rows), f"dW {i}"
+        assert torch.equal(dbs[i], db1), f"db {i}"
+    _, rw, rb = O.linear_bwd(xs[0], host(w), dys[0])
+    assert_grad_close(host(dws[0]), rw, "grouped dW 0")
+    assert_grad_close(host(dbs[0]), rb, "grouped db 0")

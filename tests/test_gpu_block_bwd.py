@@ -92,6 +92,51 @@ def _check_block_grads(got, ref, D):
         assert_grad_close(host(gw["b_o"]), rw["bo"], f"{att} db_o")
 
 
+@pytest.mark.parametrize("name", ["batch2_pad", "img2048"])
+def test_grouped_weight_gradients_match_the_chain(P, name):
+    """PTBlockBackward with the four D x D weight gradients grouped at the end
+    (ptdit_linear_bwd_dw_group, the default) against the chain that forms
+    them in place: d_x and every other gradient bit for bit (the same calls),
+    the grouped d_W within fp32 rounding of the chain's (the same bf16
+    products summed over other token splits), their d_b bit for bit."""
+    wl = CASES[name]
+    announce(f"grouped vs in-chain weight gradients {name}")
+    x = make_x(wl)
+    ws = make_all_weights(wl)
+    g = np.random.Generator(np.random.PCG64(950 + wl.index))
+    dout = torch.from_numpy(g.standard_normal((wl.B, wl.N, wl.D)).astype(np.float32)).cuda()
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=torch.bfloat16)
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    b_grp, b_chain = P.PTBlockBackward(blk), P.PTBlockBackward(blk, group_dw=False)
+    assert b_grp.group and not b_chain.group
+    for keep in (False, True):
+        blk.forward(xd, keep=keep)
+        a = b_grp.backward(xd, dout)
+        a = {"dx": a["dx"].clone(), "weights": [{k: v.clone() for k, v in w.items()} for w in a["weights"]]}
+        c = b_chain.backward(xd, dout)
+        torch.cuda.synchronize()
+        assert torch.equal(a["dx"], c["dx"]), "dx"
+        D = wl.D
+        grouped = {(1, "w_o"), (2, "w_o"), (3, "w_o")}
+        for i in range(4):
+            for k in ("w_qkv", "b_qkv", "w_o", "b_o"):
+                ga, gc = a["weights"][i][k], c["weights"][i][k]
+                if (i, k) in grouped or (i == 1 and k == "w_qkv"):
+                    rows = slice(0, D) if k == "w_qkv" else slice(None)
+                    if k == "w_qkv":   # only the query rows are grouped
+                        assert torch.equal(ga[D:], gc[D:]), f"{i} {k} K/V rows"
+                    da, dc = host(ga[rows]), host(gc[rows])
+                    assert np.abs(da - dc).max() <= 1e-5 * max(1.0, float(np.abs(dc).max())), f"{i} {k}"
+                elif k == "b_qkv" and i >= 2:
+                    # the window attentions' pad-slot key/value bias gradients
+                    # are added with atomics (order of arrival): K/V rows close
+                    assert torch.equal(ga[:D], gc[:D]), f"{i} {k} Q rows"
+                    da, dc = host(ga[D:]), host(gc[D:])
+                    assert np.abs(da - dc).max() <= 1e-5 * max(1.0, float(np.abs(dc).max())), f"{i} {k} K/V rows"
+                else:
+                    assert torch.equal(ga, gc), f"{i} {k}"
+
+
 @pytest.mark.parametrize("name,prec", [("batch2_pad", torch.bfloat16), ("video_pad", torch.bfloat16),
                                        ("batch2_pad", torch.float32)])
 def test_keep_mode_tensors(P, name, prec):
