@@ -126,8 +126,8 @@ template <> struct Col4<uint16_t> {
   }
 };
 template <typename TA>
-__global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy, float* __restrict__ dbp,
-                                                       int64_t rows, int d_out) {
+__device__ __forceinline__ void colsum_body(const TA* __restrict__ dy, float* __restrict__ dbp, int64_t rows,
+                                            int d_out) {
   const int o = 4 * (blockIdx.x * LB_NT + threadIdx.x);
   if (o >= d_out) return;
   const int64_t t0 = (int64_t)blockIdx.y * CS_ROWS, t1 = min(rows, t0 + CS_ROWS);
@@ -150,6 +150,25 @@ __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy
   add(r2, s[3]);
   add(r, r2);
   *reinterpret_cast<float4*>(dbp + (int64_t)blockIdx.y * d_out + o) = r;
+}
+template <typename TA>
+__global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy, float* __restrict__ dbp,
+                                                       int64_t rows, int d_out) {
+  colsum_body<TA>(dy, dbp, rows, d_out);
+}
+
+// the products of one grouped weight-gradient launch, indexed by blockIdx.z
+// (column sums) or blockIdx.y (reduction); a null dy / dw skips a product
+struct WgradGroupPtrs {
+  const uint16_t* dy[GEMM_MAX_GROUPS];
+  float* dbp[GEMM_MAX_GROUPS];
+  const float* part[GEMM_MAX_GROUPS];
+  float* dw[GEMM_MAX_GROUPS];
+  float* db[GEMM_MAX_GROUPS];
+};
+__global__ void __launch_bounds__(LB_NT) colsum_group_kernel(WgradGroupPtrs g, int64_t rows, int d_out) {
+  const uint16_t* dy = g.dy[blockIdx.z];
+  if (dy) colsum_body<uint16_t>(dy, g.dbp[blockIdx.z], rows, d_out);
 }
 
 // four consecutive elements a thread (nw and d_out multiples of 4, 16-byte
@@ -178,6 +197,15 @@ __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __rest
   const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
   if (e < nw && dw) *reinterpret_cast<float4*>(dw + e) = sum_splits4(part, nw, splits, e);
   if (e < d_out && db) *reinterpret_cast<float4*>(db + e) = sum_splits4(dbp, d_out, csplits, e);
+}
+__global__ void __launch_bounds__(LB_NT) wgrad_reduce_group_kernel(WgradGroupPtrs g, int splits, int csplits,
+                                                                   int64_t nw, int d_out) {
+  const int p = blockIdx.y;
+  const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
+  float* const dw = g.dw[p];
+  float* const db = g.db[p];
+  if (e < nw && dw) *reinterpret_cast<float4*>(dw + e) = sum_splits4(g.part[p], nw, splits, e);
+  if (e < d_out && db) *reinterpret_cast<float4*>(db + e) = sum_splits4(g.dbp[p], d_out, csplits, e);
 }
 
 // ----------------------------------------------------------------------------
@@ -290,18 +318,27 @@ hipError_t launch_wgrad_group(const WgradGroupDesc& d, hipStream_t s) {
   }
   hipError_t e = launch_gemm_bf16(g, s);
   if (e != hipSuccess) return e;
-  const int64_t n4 = nw > d.d_out ? nw : d.d_out;
+  // every product's column sums in one launch, then every product's
+  // split-order reduction in one launch (the same sums as the per-call path)
+  WgradGroupPtrs gp{};
+  bool any_db = false;
   for (int i = 0; i < d.n; ++i) {
-    if (d.db[i]) {
-      hipLaunchKernelGGL((colsum_kernel<uint16_t>), dim3((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits), dim3(LB_NT), 0,
-                         s, reinterpret_cast<const uint16_t*>(d.dy[i]), dbp(i), d.rows, d.d_out);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n4 / 4 + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s,
-                       part(i), dbp(i), d.dw[i], d.db[i], sp, csplits, nw, d.d_out);
+    gp.dy[i] = d.db[i] ? reinterpret_cast<const uint16_t*>(d.dy[i]) : nullptr;
+    gp.dbp[i] = dbp(i);
+    gp.part[i] = part(i);
+    gp.dw[i] = d.dw[i];
+    gp.db[i] = d.db[i];
+    any_db = any_db || d.db[i];
+  }
+  if (any_db) {
+    hipLaunchKernelGGL(colsum_group_kernel, dim3((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits, d.n), dim3(LB_NT), 0, s,
+                       gp, d.rows, d.d_out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  const int64_t n4 = nw > d.d_out ? nw : d.d_out;
+  hipLaunchKernelGGL(wgrad_reduce_group_kernel, dim3((unsigned)((n4 / 4 + LB_NT - 1) / LB_NT), d.n), dim3(LB_NT), 0,
+                     s, gp, sp, csplits, nw, d.d_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
