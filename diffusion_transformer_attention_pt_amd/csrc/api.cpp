@@ -1039,14 +1039,22 @@ ptdit_status ptdit_linear_bwd_ex(const void* x, ptdit_dtype x_dt, int64_t rows, 
   if (d_w && !wgrad_token_major(rows, d_in, d_out, d.dy_f32, d.x_f32) && launch_wgrad_operands(d, stream) != hipSuccess)
     return PTDIT_ERR_HIP;
   if (want_dx) {
-    // dX = dY W = dY (W^T)^T: the projection kernels with the transposed weight;
-    // the added gradient is the GEMM's residual, the bf16 copy its second
-    // output (or its only output when d_x is NULL)
-    hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
-    if (e != hipSuccess) return PTDIT_ERR_HIP;
+    // dX = dY W: with bf16 dY and d_out % 128 == 0 the ping-pong kernel reads
+    // the weight as it lies (k-major: row o of W is k-slice row o); else the
+    // projection kernels take a transposed copy. The added gradient is the
+    // GEMM's residual, the bf16 copy its second output (or its only output
+    // when d_x is NULL)
     GemmDesc g;
     g.A = d.dyb ? (const void*)d.dyb : d_y; g.a_f32 = !d.dyb && dy_dt == PTDIT_F32;
-    g.W = wt; g.bias = nullptr;
+    const bool kmajor = !g.a_f32 && d_out % 128 == 0 && d_out >= 256 && rows >= 1024;
+    if (kmajor) {
+      g.w_kmajor = 1;
+      g.ldw = d_in;
+    } else {
+      hipError_t e = launch_transpose_bf16(w, wt, d_out, d_in, stream);
+      if (e != hipSuccess) return PTDIT_ERR_HIP;
+    }
+    g.W = kmajor ? w : wt; g.bias = nullptr;
     g.R = d_x_add; g.r_f32 = 1;
     g.Y = d_x ? (void*)d_x : (void*)d_x_bf16; g.y_f32 = d_x ? 1 : 0;
     g.Y2 = d_x ? d_x_bf16 : nullptr;

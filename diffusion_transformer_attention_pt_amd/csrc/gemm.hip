@@ -395,6 +395,60 @@ struct DmaPlanTN {
   }
 };
 
+// Row-major bf16 A (as DmaPlan) with a k-major W: W [K][ldw] stored with the
+// contraction index as its row, the way a weight [d_out][d_in] lies for
+// dX = dY W (K = d_out). W's k-slice is 32 rows x the tile's columns, staged
+// as it lies (the token-major layout of DmaPlanTN, read with tn_frag), so the
+// product needs no transposed copy of the weight.
+template <int BM, int BN, int NW>
+struct DmaPlanMix {
+  static_assert(BN <= 8 * TN_CPR, "tile columns fit an LDS row");
+  static constexpr int SA = BM * 4, SB = 32 * TN_CPR;  // 16-byte slots per stage
+  static constexpr int IA = SA / 64, IB = SB / 64, IT = IA + IB;
+  static constexpr int MAXI = (IT + NW - 1) / NW;
+  static_assert(SA % 64 == 0 && SB % 64 == 0, "stage must be whole DMA instructions");
+
+  const char* a_base;
+  const char* w_base;
+  int w_step;  // bytes per 32 rows of W
+  bool is_a[MAXI];
+  uint32_t voff[MAXI];
+  int dst[MAXI];
+
+  __device__ __forceinline__ void init(const GemmParams& p, int64_t m0, int n0, int wave, int lane, int) {
+    const int64_t lda = p.lda, ldw = p.ldw;
+    a_base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(p.A) + m0 * lda);
+    w_base = reinterpret_cast<const char*>(p.W + n0);
+    w_step = (int)(64 * ldw);
+    const int cw = p.N - n0 < BN ? (p.N - n0) / 8 : BN / 8;  // real 8-column chunks of the tile
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j0 = wave + i * NW;
+      const int j = j0 < IT ? j0 : wave;
+      is_a[i] = j < IA;
+      if (j < IA) {
+        const int sl = j * 64 + lane, row = sl / 4, pp = sl % 4;
+        const int r = m0 + row < p.M ? row : (int)(p.M - 1 - m0);
+        voff[i] = (uint32_t)(((int64_t)r * lda + DmaA<uint16_t>::chunk(row, pp) * 8) * 2);
+        dst[i] = j * 64;
+      } else {
+        const int sl = (j - IA) * 64 + lane, row = sl / TN_CPR, pos = sl % TN_CPR;
+        int c = tn_pos(row, pos);  // the chunk stored at pos (the map is its own inverse)
+        if (c >= cw) c = cw - 1;   // row padding / a ragged last tile: a real chunk, never stored
+        voff[i] = (uint32_t)(((int64_t)row * ldw + 8 * c) * 2);
+        dst[i] = SA + (j - IA) * 64;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint4* st) const {
+    const char* const ak = a_base + kt * 64;
+    const char* const wk = w_base + kt * w_step;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) PTDIT_GLDS16((is_a[i] ? ak : wk) + voff[i], st + dst[i]);
+  }
+  __device__ __forceinline__ void issue_head(int kt, uint4* st) const { issue(kt, st); }
+};
+
 // Fragment of a token-major operand: lane (i = lane % 16, g = lane / 16)
 // needs fragment row col0 + 16 j + i at k = 8 g .. 8 g + 7, i.e. LDS token
 // rows 8 g .. 8 g + 7 of one column. A transposing read (ds_read_b64_tr_b16)
@@ -750,11 +804,12 @@ gemm_dma_kernel(GemmParams p) {
 // (k = -1: the prologue's load); -1: none
 constexpr int pp_rblock(int k, int nb) { return k < 0 ? nb + k : (k < nb - 1 ? k : -1); }
 
-template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256, bool TOKMAJ = false>
+template <typename TR, typename TY, bool HEADMAJOR, int RKT, int BM = 256, bool TOKMAJ = false, bool WKM = false>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p_in) {
   GemmParams p = p_in;
   constexpr bool RIN = RKT > 0;
   static_assert(!TOKMAJ || (!RIN && !HEADMAJOR && BM == 256), "token-major operands: the weight gradient only");
+  static_assert(!WKM || (!TOKMAJ && !HEADMAJOR), "k-major W: token-major output (dX = dY W)");
   static_assert(!RIN || (RKT == 36 && BM == 256), "one k-slice per accumulator block of a 64 x 144 wave tile");
   static_assert(BM == 256 || BM == 128, "wave tiles of 64 or 32 rows");
   using TA = uint16_t;
@@ -763,7 +818,9 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p_in) {
   constexpr int NB = FN * FM;  // accumulator blocks per wave
   constexpr int RL = RIN ? 1 : 0;
   static_assert(!RIN || !HEADMAJOR, "residual only for token-major output");
-  using DP = typename std::conditional<TOKMAJ, DmaPlanTN<BM, BN, NW>, DmaPlan<TA, BM, BN, NW>>::type;
+  using DP = typename std::conditional<
+      TOKMAJ, DmaPlanTN<BM, BN, NW>,
+      typename std::conditional<WKM, DmaPlanMix<BM, BN, NW>, DmaPlan<TA, BM, BN, NW>>::type>::type;
   using ES = EpiShape<TY, BN, WM, STAGES>;
   constexpr int SA = DP::SA, MAXI = DP::MAXI;
   constexpr int SLOT = (DP::SA + DP::SB) > ES::SLOT ? (DP::SA + DP::SB) : ES::SLOT;
@@ -828,15 +885,17 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p_in) {
   const int lofs_w = SA + DmaA<uint16_t>::lofs(wn * TN + lr, g);
   const int lofs_a = DmaA<TA>::lofs(wm * TM + lr, g);
   TnFragBase fbw, fba;
-  if constexpr (TOKMAJ) {
-    fbw.init(SA * 16, wn * TN, lane);
-    fba.init(0, wm * TM, lane);
-  }
+  if constexpr (TOKMAJ || WKM) fbw.init(SA * 16, wn * TN, lane);
+  if constexpr (TOKMAJ) fba.init(0, wm * TM, lane);
   uint4 wf[FN], xf[FM];
   auto read_frags = [&](const uint4* st) {
     if constexpr (TOKMAJ) {
       static_for<0, FN>([&](auto iI) { wf[decltype(iI)::value] = tn_frag<decltype(iI)::value>(st, fbw); });
       static_for<0, FM>([&](auto jI) { xf[decltype(jI)::value] = tn_frag<decltype(jI)::value>(st, fba); });
+    } else if constexpr (WKM) {
+      static_for<0, FN>([&](auto iI) { wf[decltype(iI)::value] = tn_frag<decltype(iI)::value>(st, fbw); });
+#pragma unroll
+      for (int j = 0; j < FM; ++j) xf[j] = DmaA<TA>::frag(st, lofs_a, j);
     } else {
 #pragma unroll
       for (int i = 0; i < FN; ++i) wf[i] = DmaA<uint16_t>::frag(st, lofs_w, i);
@@ -1139,7 +1198,7 @@ static hipError_t run_dma(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename TR, typename TY, bool HM>
+template <typename TR, typename TY, bool HM, bool WKM = false>
 static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 != 0 || p.K < 256) return hipErrorInvalidValue;  // KT % 4 == 0, KT >= 8
   const int64_t tiles = ((p.M + 255) / 256) * (int64_t)((p.N + 287) / 288);
@@ -1152,21 +1211,21 @@ static hipError_t run_pp(const GemmParams& p, hipStream_t s) {
     // CUs: the 3456 x 1152 weight gradient split 4 ways over the tokens of a
     // 2048^2 block runs 142 us on 224 workgroups, 193 us on 432); the
     // residual is added in the epilogue
-    hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0, 128>), dim3((unsigned)t128, (unsigned)p.splits), dim3(512),
-                       0, s, p);
+    hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0, 128, false, WKM>), dim3((unsigned)t128, (unsigned)p.splits),
+                       dim3(512), 0, s, p);
     return hipGetLastError();
   }
   if constexpr (!HM) {
     // the model width D = 1152 with whole column tiles: residual folded into
     // the main loop (rows past M of a ragged last row tile are clamped)
     if (p.R && p.K == 36 * 32 && p.N % 288 == 0) {
-      hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(512), 0,
-                         s, p);
+      hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 36, 256, false, WKM>), dim3((unsigned)tiles, (unsigned)p.splits),
+                         dim3(512), 0, s, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(512), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_pp_kernel<TR, TY, HM, 0, 256, false, WKM>), dim3((unsigned)tiles, (unsigned)p.splits),
+                     dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1248,6 +1307,16 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t s) {
     p.gA[i] = i < d.groups ? d.gA[i] : nullptr;
     p.gW[i] = i < d.groups ? d.gW[i] : nullptr;
     p.gY[i] = i < d.groups ? d.gY[i] : nullptr;
+  }
+  if (d.w_kmajor) {
+    // k-major W [K][ldw] (dX = dY W with the weight as it lies): the
+    // ping-pong kernel's mixed instance; bf16 A, token-major output, an fp32
+    // residual or none, no bias
+    if (d.a_f32 || d.head_major || d.splits > 1 || d.act || d.bias || (d.R && !d.r_f32) || p.K % 128 || p.K < 256 ||
+        p.N % 8 || p.N <= 0 || p.M <= 0 || p.lda != p.K || p.ldw < p.N || p.ldw % 8 ||
+        (int64_t)2 * p.K * p.ldw >= ((int64_t)1 << 31) || (int64_t)512 * p.K >= ((int64_t)1 << 31))
+      return hipErrorInvalidValue;
+    return d.y_f32 ? run_pp<float, float, false, true>(p, s) : run_pp<float, uint16_t, false, true>(p, s);
   }
   if (d.tn) {
     // token-major bf16 operands (the weight gradient): the ping-pong kernel's

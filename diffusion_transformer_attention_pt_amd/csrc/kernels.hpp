@@ -33,6 +33,9 @@ struct GemmDesc {
   int tn = 0, k_last = 0, k_valid = 0;
   // token-major only: groups > 1 products of this shape, operands and
   // outputs at gA[g], gW[g], gY[g] (A, W, Y are then not read)
+  // w_kmajor: W is [K][ldw] with the contraction index as its row (a weight
+  // [d_out][d_in] for dX = dY W), read without a transposed copy
+  int w_kmajor = 0;
   int groups = 1;
   const void* gA[GEMM_MAX_GROUPS] = {};
   const void* gW[GEMM_MAX_GROUPS] = {};

@@ -499,3 +499,33 @@ def test_linear_bwd_dw_group(P, rows, d_in, d_out, n):
     _, rw, rb = O.linear_bwd(xs[0], host(w), dys[0])
     assert_grad_close(host(dws[0]), rw, "grouped dW 0")
     assert_grad_close(host(dbs[0]), rb, "grouped db 0")
+
+
+@pytest.mark.parametrize("rows,d_in,d_out,add", [(16384, 1152, 3456, True), (2400, 1152, 1152, True),
+                                                 (4096, 1152, 1152, False), (1200, 1152, 2304, False)])
+def test_linear_bwd_dx_weight_as_it_lies(P, rows, d_in, d_out, add):
+    """d_x = dY W from bf16 dY reads W [d_out][d_in] as it lies (the k-major
+    instance of the ping-pong GEMM, no transposed copy): against the same
+    product from an fp32 dY holding the same values (which takes the
+    transposed copy) to fp32 summation order, with and without an added
+    gradient (the residual in the main loop when d_out = 1152), ragged row
+    tiles included; and against the float64 oracle."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    announce(f"dX k-major W rows={rows} {d_out}->{d_in} add={add}")
+    g = np.random.Generator(np.random.PCG64(960 + rows % 89 + d_out))
+    x = round_bf16(g.standard_normal((rows, d_in)).astype(np.float32))
+    w = round_bf16((g.standard_normal((d_out, d_in)) * 0.05).astype(np.float32))
+    dy = round_bf16(g.standard_normal((rows, d_out)).astype(np.float32))
+    ad = dev(g.standard_normal((rows, d_in)).astype(np.float32), F32) if add else None
+    wd = dev(w, BF16)
+    dx_k, _, _ = _lib.linear_bwd(dev(x, BF16), wd, dev(dy, BF16), want_dw=False, want_db=False,
+                                 dx_add=ad, dx=torch.empty(rows, d_in, dtype=F32, device="cuda") if add else None)
+    dx_t, _, _ = _lib.linear_bwd(dev(x, BF16), wd, dev(dy, F32), want_dw=False, want_db=False,
+                                 dx_add=ad, dx=torch.empty(rows, d_in, dtype=F32, device="cuda") if add else None)
+    torch.cuda.synchronize()
+    k, t = host(dx_k), host(dx_t)
+    assert np.abs(k - t).max() <= 1e-5 * max(1.0, float(np.abs(t).max())), "k-major vs transposed"
+    ref = dy.astype(np.float64) @ w.astype(np.float64)
+    if add:
+        ref = ref + host(ad)
+    assert_grad_close(k, ref, "dX k-major")
