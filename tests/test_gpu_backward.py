@@ -501,8 +501,9 @@ def test_linear_bwd_dw_group(P, rows, d_in, d_out, n):
     assert_grad_close(host(dbs[0]), rb, "grouped db 0")
 
 
-@pytest.mark.parametrize("rows,d_in,d_out,add", [(16384, 1152, 3456, True), (2400, 1152, 1152, True),
-                                                 (4096, 1152, 1152, False), (1200, 1152, 2304, False)])
+@pytest.mark.parametrize("rows,d_in,d_out,add", [(16384, 1152, 1152, True), (2400, 1152, 1152, True),
+                                                 (4096, 1152, 1152, False), (1200, 1152, 1024, False),
+                                                 (16384, 1152, 3456, True)])
 def test_linear_bwd_dx_weight_as_it_lies(P, rows, d_in, d_out, add):
     """d_x = dY W from bf16 dY reads W [d_out][d_in] as it lies (the k-major
     instance of the ping-pong GEMM, no transposed copy): against the same
