@@ -38,9 +38,11 @@ def test_noalloc_proxy_sa_matches_workspace_call_twice(P):
     ws_np = make_all_weights(wl)[0]                 # the proxy self-attention's weights
     w = _lib.AttnWeights.from_dict(ws_np, torch.bfloat16, "cuda")
     D, heads = wl.D, wl.heads
-    # first call: two batches of the 2048^2 block's 256 proxies (fp32 stream,
-    # as in the block); second call: a smaller problem, 1 x 100 bf16 proxies
-    for (B, M, pdt), seed in (((2, 256, torch.float32), 71), ((1, 100, torch.bfloat16), 72)):
+    # first call: the video's 864 proxies (bf16); then two batches of the
+    # 2048^2 block's 256 proxies (fp32 stream, as in the block); then a
+    # smaller problem, 1 x 100 bf16 proxies (each call smaller than the last)
+    for (B, M, pdt), seed in (((1, 864, torch.bfloat16), 70), ((2, 256, torch.float32), 71),
+                              ((1, 100, torch.bfloat16), 72)):
         announce(f"proxy_sa_noalloc B={B} M={M} {pdt}")
         x = _proxies(B, M, D, seed)
         if pdt == torch.bfloat16:
