@@ -59,9 +59,9 @@ class PTBlockAttention:
         self.g = (B, self.F, self.H, self.W, D, heads)
         self.weights = [AttnWeights.from_dict(w, prec, self.device) for w in weights]
         # the window attentions' w_qkv packed once for their fused kernel, so
-        # a forward launches no packing (weights are fixed for the block's life)
-        for w in self.weights[2:4]:
-            w.w_qkv_packed = _lib.pack_window_weights(w, heads)
+        # a forward launches no packing; after changing the weights in place
+        # (an optimizer step), call repack_weights()
+        self.repack_weights()
         stream_dt = torch.float32
         self.P = torch.empty(B, self.M, D, dtype=stream_dt, device=self.device)
         self.P2 = torch.empty_like(self.P)
@@ -96,6 +96,14 @@ class PTBlockAttention:
         self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         self._kws = None     # per-call workspaces of keep mode (allocated on first use)
         self.kept = None     # views of what the last keep-mode forward left for the backward
+
+    def repack_weights(self) -> None:
+        """Rewrite the packed copies of the two window attentions' w_qkv
+        (ptdit_pack_window_weights) from the current weights. The window calls
+        read the packed copy, not w_qkv, so it must follow every in-place
+        change of the weights."""
+        for w in self.weights[2:4]:
+            w.w_qkv_packed = _lib.pack_window_weights(w, self.heads)
 
     def forward(self, x: torch.Tensor, keep: bool = False) -> torch.Tensor:
         """One forward. keep=True (training): every attention call gets its own

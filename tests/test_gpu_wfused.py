@@ -180,3 +180,24 @@ def test_packed_window_weights_layout(P):
         col = kt * 32 + (q ^ ((r >> 1) & 3)) * 8 + e
         ref = w.view(torch.int16).numpy()[wrow, col]
         assert np.array_equal(got.view(torch.int16).cpu().numpy().reshape(ref.shape), ref)
+
+
+def test_block_repacks_changed_window_weights(P):
+    """PTBlockAttention reads its window attentions' packed w_qkv: after an
+    in-place change of the weights, repack_weights() makes the forward follow
+    it (equal, bit for bit, to a block built on the changed weights)."""
+    wl = _wl(H=16, W=24)
+    announce("block repack after an in-place weight change")
+    from synth_inputs import make_all_weights
+    ws = make_all_weights(wl)
+    x = dev(make_x(wl, seed=870), BF16)
+    blk = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws, prec=BF16)
+    ws2 = [dict(w) for w in ws]
+    ws2[3] = dict(ws[3], wq=ws[3]["wq"] * 1.5)
+    ref = P.PTBlockAttention(wl.B, wl.grid, wl.D, wl.heads, wl.p, wl.win, wl.shift, ws2, prec=BF16).forward(x).clone()
+    D = wl.D
+    blk.weights[3].w_qkv[:D].copy_(torch.as_tensor(ws2[3]["wq"]).to(BF16))
+    blk.repack_weights()
+    got = blk.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
