@@ -1267,9 +1267,18 @@ static hipError_t pick_tile(const GemmParams& p, hipStream_t s) {
   // few rows (proxies): a small tile for parallelism; a 4-slot ring measured
   // faster than 8 or 12 slots here (shorter prologue, same streaming rate)
   if (p.M < 1024 && p.K % 32 == 0 && p.K / 32 >= 4) {
-    // 32-row tiles when 64-row tiles would leave CUs idle (the 256 proxies of
-    // an image block); 64-row tiles from one workgroup a CU on (measured: 512
-    // proxies, 432 tiles, 5 us faster a step than 864 32-row tiles)
+    // From 512 rows (the video block's 864 proxies): 64-row tiles, 128
+    // columns wide when that still gives about a workgroup a CU (fewer
+    // re-reads of each A and W slab; measured at 864 x 3456, K = 1152:
+    // 18.9 us against 22.3 on 64 x 64 tiles, 864 x 2304: 13.2 against
+    // 16.0), else 64 wide (864 x 1152: 7.7 us against 9.1 on 32 x 64).
+    if (p.M >= 512) {
+      if (((p.M + 63) / 64) * (int64_t)((p.N + 127) / 128) >= 216)
+        return run_dma<TA, TR, TY, 64, 128, 2, 2, 4, HM>(p, s);
+      return run_dma<TA, TR, TY, 64, 64, 2, 2, 4, HM>(p, s);
+    }
+    // fewer rows (the 256 proxies of an image block): 32-row tiles when
+    // 64-row tiles would leave CUs idle
     if (((p.M + 63) / 64) * (int64_t)((p.N + 63) / 64) < 256) return run_dma<TA, TR, TY, 32, 64, 2, 2, 4, HM>(p, s);
     return run_dma<TA, TR, TY, 64, 64, 2, 2, 4, HM>(p, s);
   }

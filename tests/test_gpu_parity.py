@@ -224,6 +224,10 @@ def test_roll_bit_exact(P, grid, shift, B, D, dt):
                                            (2100, 1152, 1152), (2350, 1152, 2304),
                                            # few rows on 32-row tiles (ragged: 300 = 9 x 32 + 12)
                                            (300, 1152, 2304),
+                                           # proxy rows from 512 on: 64 x 64 tiles (864 x 1152)
+                                           # and 64 x 128 tiles (864 x 2304; ragged: 864 = 13 x 64
+                                           # + 32, 1000 above = 15 x 64 + 40)
+                                           (864, 1152, 1152), (864, 1152, 2304),
                                            # 268 tiles of 256 rows: one whole round (16384 rows),
                                            # then 616 rows on 128-row tiles (ragged: 104 in the last)
                                            (17000, 1152, 1152)])
