@@ -47,6 +47,42 @@ __global__ void __launch_bounds__(LB_NT) transpose_kernel(const uint16_t* __rest
     if (c0 + c < cols && r0 + tx < rows) wt[(int64_t)(c0 + c) * rows + r0 + tx] = tile[tx][c];
 }
 
+// The same for rows and cols that are multiples of 8 (every weight the
+// projections take): 64 x 64 tiles moved in 16-byte pieces. Lane (t, q)
+// reads 8 columns of W rows t and t + 32, and writes 8 consecutive entries
+// (W rows 8q .. 8q + 7) of W^T rows t and t + 32; the LDS tile is 64 rows of
+// 33 dwords (66 elements), so the 8 rows one transposed read walks are not
+// all in one bank.
+__global__ void __launch_bounds__(LB_NT) transpose16_kernel(const uint16_t* __restrict__ w,
+                                                            uint16_t* __restrict__ wt, int rows, int cols) {
+  __shared__ uint32_t tile[64 * 33];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int q = threadIdx.x & 7, t = threadIdx.x >> 3;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = t + 32 * h;
+    if (r0 + r < rows && c0 + 8 * q < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(w + (int64_t)(r0 + r) * cols + c0 + 8 * q);
+      uint32_t* d = tile + r * 33 + 4 * q;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+  }
+  __syncthreads();
+  const uint16_t* ts = reinterpret_cast<const uint16_t*>(tile);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = t + 32 * h;
+    // rows and cols are multiples of 8: a chunk lies wholly inside or outside
+    if (c0 + c < cols && r0 + 8 * q < rows) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)ts[(8 * q + 2 * e) * 66 + c] | ((uint32_t)ts[(8 * q + 2 * e + 1) * 66 + c] << 16);
+      *reinterpret_cast<uint4*>(wt + (int64_t)(c0 + c) * rows + r0 + 8 * q) = uint4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
+
 // src [rows][cols] (bf16 or fp32) -> dst [cols][ld] bf16 (columns rows ..
 // ld-1 zero; ld % 64 == 0), and optionally a row-major bf16 copy [rows][cols]:
 // the token-contiguous operands of dW = dY^T X (and the bf16 A operand of
@@ -227,6 +263,11 @@ void wgrad_plan(int64_t rows, int d_in, int d_out, int& splits, int64_t& tch, in
 
 hipError_t launch_transpose_bf16(const void* w, void* wt, int rows, int cols, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  if (rows % 8 == 0 && cols % 8 == 0) {
+    hipLaunchKernelGGL(transpose16_kernel, dim3((cols + 63) / 64, (rows + 63) / 64), dim3(LB_NT), 0, s,
+                       reinterpret_cast<const uint16_t*>(w), reinterpret_cast<uint16_t*>(wt), rows, cols);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(transpose_kernel, dim3((cols + 31) / 32, (rows + 31) / 32), dim3(LB_NT), 0, s,
                      reinterpret_cast<const uint16_t*>(w), reinterpret_cast<uint16_t*>(wt), rows, cols);
   return hipGetLastError();

@@ -435,6 +435,7 @@ LIN_CASES = [
     (300, 1152, 3456, "bf16", "bf16"),
     (1, 8, 16, "bf16", "f32"),
     (777, 64, 200, "f32", "f32"),
+    (130, 72, 200, "bf16", "bf16"),       # the weight's transposed copy ragged in both 64-wide tile axes
     (16384, 1152, 1152, "bf16", "f32"),   # the 2048^2 output projection
     # bf16 d_y and x, token counts a multiple of 128: dW from the token-major
     # operands directly (no transposed copies)
