@@ -223,25 +223,76 @@ __device__ __forceinline__ float4 sum_splits4(const float* __restrict__ part, in
 #pragma unroll
     for (int u = 0; u < 8; ++u) add4(s, v[u]);
   }
-  for (; k < n; ++k) add4(s, *reinterpret_cast<const float4*>(part + (int64_t)k * stride + e));
+  if (k < n) {  // the last (< 8) partials, loaded together, added in order
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = k + u < n ? *reinterpret_cast<const float4*>(part + (int64_t)(k + u) * stride + e)
+                       : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k + u < n) add4(s, v[u]);
+  }
   return s;
 }
+
+// db from the column-sum partials [csplits][d_out] (one per 64-row block,
+// hundreds of them): a workgroup takes 64 columns; lane (c, r) sums the
+// partials r, r + 16, r + 32, ... of columns 4c .. 4c + 3 in that order, and
+// the 16 subtotals of a column are then added in the order r = 0 .. 15
+// (fixed, so the result does not depend on scheduling)
+constexpr int DB_COLS = 64;
+__device__ __forceinline__ void db_reduce_block(const float* __restrict__ dbp, float* __restrict__ db, int csplits,
+                                                int d_out, int blk) {
+  __shared__ float4 sub[16][16];
+  const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const int e = blk * DB_COLS + 4 * c;
+  float4 s = float4{0.f, 0.f, 0.f, 0.f};
+  if (e < d_out) {
+    int k = r;
+    for (; k + 48 < csplits; k += 64) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(dbp + (int64_t)(k + 16 * u) * d_out + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add4(s, v[u]);
+    }
+    for (; k < csplits; k += 16) add4(s, *reinterpret_cast<const float4*>(dbp + (int64_t)k * d_out + e));
+  }
+  sub[r][c] = s;
+  __syncthreads();
+  if (r == 0 && e < d_out) {
+    float4 t = sub[0][c];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) add4(t, sub[i][c]);
+    *reinterpret_cast<float4*>(db + e) = t;
+  }
+}
+static int db_reduce_blocks(int d_out) { return (d_out + DB_COLS - 1) / DB_COLS; }
+
+// blocks [0, nwb): dW, four elements a thread; blocks from nwb on: db
 __global__ void __launch_bounds__(LB_NT) wgrad_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ dbp, float* __restrict__ dw,
                                                              float* __restrict__ db, int splits, int csplits,
-                                                             int64_t nw, int d_out) {
+                                                             int64_t nw, int d_out, int nwb) {
+  if ((int)blockIdx.x >= nwb) {
+    if (db) db_reduce_block(dbp, db, csplits, d_out, blockIdx.x - nwb);
+    return;
+  }
   const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
   if (e < nw && dw) *reinterpret_cast<float4*>(dw + e) = sum_splits4(part, nw, splits, e);
-  if (e < d_out && db) *reinterpret_cast<float4*>(db + e) = sum_splits4(dbp, d_out, csplits, e);
 }
 __global__ void __launch_bounds__(LB_NT) wgrad_reduce_group_kernel(WgradGroupPtrs g, int splits, int csplits,
-                                                                   int64_t nw, int d_out) {
+                                                                   int64_t nw, int d_out, int nwb) {
   const int p = blockIdx.y;
-  const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
   float* const dw = g.dw[p];
   float* const db = g.db[p];
+  if ((int)blockIdx.x >= nwb) {
+    if (db) db_reduce_block(g.dbp[p], db, csplits, d_out, blockIdx.x - nwb);
+    return;
+  }
+  const int64_t e = 4 * ((int64_t)blockIdx.x * LB_NT + threadIdx.x);
   if (e < nw && dw) *reinterpret_cast<float4*>(dw + e) = sum_splits4(g.part[p], nw, splits, e);
-  if (e < d_out && db) *reinterpret_cast<float4*>(db + e) = sum_splits4(g.dbp[p], d_out, csplits, e);
 }
 
 // ----------------------------------------------------------------------------
@@ -376,9 +427,9 @@ hipError_t launch_wgrad_group(const WgradGroupDesc& d, hipStream_t s) {
                        gp, d.rows, d.d_out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t n4 = nw > d.d_out ? nw : d.d_out;
-  hipLaunchKernelGGL(wgrad_reduce_group_kernel, dim3((unsigned)((n4 / 4 + LB_NT - 1) / LB_NT), d.n), dim3(LB_NT), 0,
-                     s, gp, sp, csplits, nw, d.d_out);
+  const int nwb = (int)((nw / 4 + LB_NT - 1) / LB_NT);
+  hipLaunchKernelGGL(wgrad_reduce_group_kernel, dim3((unsigned)(nwb + (any_db ? db_reduce_blocks(d.d_out) : 0)), d.n),
+                     dim3(LB_NT), 0, s, gp, sp, csplits, nw, d.d_out, nwb);
   return hipGetLastError();
 }
 
@@ -436,9 +487,9 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t n = nw > d.d_out ? nw : d.d_out;
-  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + LB_NT - 1) / LB_NT)), dim3(LB_NT), 0, s, d.part,
-                     d.dbp, d.dw, d.db, splits, csplits, nw, d.d_out);
+  const int nwb = d.dw ? (int)((nw / 4 + LB_NT - 1) / LB_NT) : 0;
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)(nwb + (d.db ? db_reduce_blocks(d.d_out) : 0))),
+                     dim3(LB_NT), 0, s, d.part, d.dbp, d.dw, d.db, splits, csplits, nw, d.d_out, nwb);
   return hipGetLastError();
 }
 
