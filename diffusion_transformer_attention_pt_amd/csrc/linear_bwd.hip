@@ -161,32 +161,41 @@ template <> struct Col4<uint16_t> {
                   __uint_as_float(v.y & 0xffff0000u)};
   }
 };
+// A workgroup: 64 four-column groups x 4 row chains; chain c (one wave)
+// sums the rows t0 + c, t0 + c + 4, ... of its block in increasing order,
+// eight loads in flight, and the chains are combined as (c0 + c1) + (c2 + c3)
 template <typename TA>
 __device__ __forceinline__ void colsum_body(const TA* __restrict__ dy, float* __restrict__ dbp, int64_t rows,
                                             int d_out) {
-  const int o = 4 * (blockIdx.x * LB_NT + threadIdx.x);
-  if (o >= d_out) return;
+  __shared__ float4 chain[4][64];
+  const int cq = threadIdx.x & 63, c = threadIdx.x >> 6;
+  const int o = 4 * (blockIdx.x * 64 + cq);
   const int64_t t0 = (int64_t)blockIdx.y * CS_ROWS, t1 = min(rows, t0 + CS_ROWS);
-  float4 s[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s[c] = float4{0.f, 0.f, 0.f, 0.f};
   auto add = [](float4& a, const float4& b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; };
-  int64_t t = t0;
-  for (; t + 8 <= t1; t += 8) {
-    float4 v[8];
+  float4 s = float4{0.f, 0.f, 0.f, 0.f};
+  if (o < d_out) {
+    int64_t t = t0 + c;
+    for (; t + 28 < t1; t += 32) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = Col4<TA>::ld(dy + (t + u) * d_out + o);
+      for (int u = 0; u < 8; ++u) v[u] = Col4<TA>::ld(dy + (t + 4 * u) * d_out + o);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(s[u & 3], v[u]);
+      for (int u = 0; u < 8; ++u) add(s, v[u]);
+    }
+    for (; t < t1; t += 4) add(s, Col4<TA>::ld(dy + t * d_out + o));
   }
-  for (; t < t1; ++t) add(s[(t - t0) & 3], Col4<TA>::ld(dy + t * d_out + o));
-  float4 r = s[0];
-  add(r, s[1]);
-  float4 r2 = s[2];
-  add(r2, s[3]);
-  add(r, r2);
-  *reinterpret_cast<float4*>(dbp + (int64_t)blockIdx.y * d_out + o) = r;
+  chain[c][cq] = s;
+  __syncthreads();
+  if (c == 0 && o < d_out) {
+    float4 r = chain[0][cq];
+    add(r, chain[1][cq]);
+    float4 r2 = chain[2][cq];
+    add(r2, chain[3][cq]);
+    add(r, r2);
+    *reinterpret_cast<float4*>(dbp + (int64_t)blockIdx.y * d_out + o) = r;
+  }
 }
+static int colsum_blocks(int d_out) { return (d_out / 4 + 63) / 64; }
 template <typename TA>
 __global__ void __launch_bounds__(LB_NT) colsum_kernel(const TA* __restrict__ dy, float* __restrict__ dbp,
                                                        int64_t rows, int d_out) {
@@ -423,7 +432,7 @@ hipError_t launch_wgrad_group(const WgradGroupDesc& d, hipStream_t s) {
     any_db = any_db || d.db[i];
   }
   if (any_db) {
-    hipLaunchKernelGGL(colsum_group_kernel, dim3((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits, d.n), dim3(LB_NT), 0, s,
+    hipLaunchKernelGGL(colsum_group_kernel, dim3(colsum_blocks(d.d_out), csplits, d.n), dim3(LB_NT), 0, s,
                        gp, d.rows, d.d_out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -477,7 +486,7 @@ hipError_t launch_wgrad(const WgradDesc& d, hipStream_t s) {
   }
   const int csplits = colsum_splits(d.rows);
   if (d.db && (!d.dw || tn)) {  // else the transpose pass wrote the partials
-    const dim3 grid((d.d_out / 4 + LB_NT - 1) / LB_NT, csplits);
+    const dim3 grid(colsum_blocks(d.d_out), csplits);
     if (d.dy_f32)
       hipLaunchKernelGGL((colsum_kernel<float>), grid, dim3(LB_NT), 0, s, reinterpret_cast<const float*>(d.dy),
                          d.dbp, d.rows, d.d_out);
