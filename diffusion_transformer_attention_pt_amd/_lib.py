@@ -523,12 +523,15 @@ def roll3d(x: torch.Tensor, grid: Sequence[int], shift: Sequence[int], inverse: 
 def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], win: Sequence[int],
                     shift: Sequence[int] = (0, 0, 0), b_qkv: Optional[torch.Tensor] = None,
                     d_qkv: Optional[torch.Tensor] = None, d_b_kv: Optional[torch.Tensor] = None,
-                    tokens: bool = False):
+                    tokens: bool = False, pad_grad: bool = True):
     """Backward of the window / shifted-window attention core. qkv [B, 3, heads,
     N, dh] (the forward's Q/K/V), d_o [B, N, D]. Returns (d_qkv fp32 [B, 3, heads,
     N, dh], or [B, N, 3D] with tokens=True (ptdit_window_attn_bwd_tokens; then a
     given d_qkv may also be bf16, for bf16 inputs), d_b_kv fp32 [2, D]: pad-slot
-    gradients, added to d_b_kv when given)."""
+    gradients, added to d_b_kv when given). With pad_grad=False and no d_b_kv,
+    no pad-slot buffer is made (None is returned in its place): for grids the
+    window divides, where the library then reads and writes none (it refuses
+    the call otherwise)."""
     lib = load()
     B, F, H, W, D, heads = grid
     if d_o.dtype != qkv.dtype or (b_qkv is not None and b_qkv.dtype != qkv.dtype):
@@ -544,7 +547,7 @@ def window_attn_bwd(qkv: torch.Tensor, d_o: torch.Tensor, grid: Sequence[int], w
         d_qkv = torch.empty(shape, dtype=torch.float32, device=qkv.device)
     if d_qkv.dtype != torch.float32 and not (tokens and d_qkv.dtype == torch.bfloat16):
         raise ValueError("d_qkv must be float32 (or bfloat16 with tokens=True)")
-    if d_b_kv is None:
+    if d_b_kv is None and pad_grad:
         d_b_kv = torch.zeros(2, D, dtype=torch.float32, device=qkv.device)
     if tokens:
         st = lib.ptdit_window_attn_bwd_tokens(_ptr(qkv), _ptr(b_qkv), _ptr(d_o), _dt(qkv.dtype), Grid(*grid),

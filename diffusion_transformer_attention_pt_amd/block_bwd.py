@@ -125,7 +125,7 @@ class PTBlockBackward:
             self.dbkv.zero_()
         # dQ/dK/dV written token-major: the Q/K/V projection's d_y as it is read
         _lib.window_attn_bwd(qkv, self.do16, blk.g, blk.win, shift, b_qkv=w.b_qkv, d_qkv=self.dqkv_t16,
-                             d_b_kv=self.dbkv if self.pads else None, tokens=True)
+                             d_b_kv=self.dbkv if self.pads else None, tokens=True, pad_grad=self.pads)
         # dx_out = dy (the residual) + d(branch)/dx^T dy, joined in the product
         _, dwqkv, dbqkv = _lib.linear_bwd(xl, w.w_qkv, self.dqkv_t16, ws=self.ws, dx=dx_out, dx_add=dy,
                                           dx_bf16=dx_out16)

@@ -101,6 +101,31 @@ def test_window_attn_bwd_vs_oracle(P, name):
         assert np.abs(rkp).max() > 1e-3 and np.abs(rvp).max() > 1e-3, "pad gradients should be nonzero here"
 
 
+@pytest.mark.parametrize("name", ["img_batch2_noshift", "dh64_shift", "img_pad_shift"])
+def test_window_attn_bwd_without_pad_buffer(P, name):
+    """pad_grad=False passes no pad-slot buffer: where the window divides the
+    grid the gradients equal those of a call with one, bit for bit, and no
+    buffer comes back; where it does not, the library refuses the call."""
+    from diffusion_transformer_attention_pt_amd import _lib
+    (B, F, H, W), D, heads, win, shift, dt, scale = WIN_CASES[name]
+    dh, N = D // heads, F * H * W
+    announce(f"window bwd without pad buffer {name}")
+    q, k, v, do = make_attn_grad_inputs(B, heads, N, N, dh, seed=350 + len(name), scale=scale, dtype=dt)
+    qkv = dev(np.stack([q, k, v], axis=1), BF16)
+    grid = (B, F, H, W, D, heads)
+    divides = all(gs % ws == 0 for gs, ws in zip((F, H, W), win))
+    if not divides:
+        with pytest.raises(_lib.PtditError):
+            _lib.window_attn_bwd(qkv, dev(do, BF16), grid, win, shift, tokens=True, pad_grad=False)
+        return
+    d_ref, db_ref = _lib.window_attn_bwd(qkv, dev(do, BF16), grid, win, shift, tokens=True)
+    d_new, db_new = _lib.window_attn_bwd(qkv, dev(do, BF16), grid, win, shift, tokens=True, pad_grad=False)
+    torch.cuda.synchronize()
+    assert db_new is None
+    assert torch.equal(d_new, d_ref)
+    assert not host(db_ref).any()
+
+
 @pytest.mark.parametrize("name", ["img_pad_ne_shift", "video128_pad_ne_shift", "f32_video_pad", "dh64_shift"])
 def test_window_attn_bwd_tokens_layout(P, name):
     """ptdit_window_attn_bwd_tokens writes the same values as
